@@ -1,0 +1,310 @@
+"""Seeded synthetic workloads for routed block-sparse attention.
+
+This module only draws inputs.  It holds none of the method's arithmetic (no
+curve, no pooling, no routing, no attention): the oracle and the HIP path
+both take what it returns, and each computes everything else on its own.
+
+The workloads stand in for per-layer attention shapes of a chunked, Wan-style
+video DiT with a 3 x 30 x 52 latent chunk (4680 tokens) and 48-chunk
+rollouts, as in Velox's runtime traces [Velox: Spatial Memory Makes World
+Models Efficient -- Main Findings; Methodology, closing paragraph].  No
+dataset is used or reproduced.
+
+Every random piece is drawn from its own PCG64 stream keyed by
+``(seed, tag, head, chunk)``, so a piece (one head of one chunk) can be
+regenerated on its own and is identical to the same piece of a full draw.
+Normal draws are float32; sums with offsets are formed in float32 and then
+rounded to bf16 (round to nearest even) for bf16 workloads.  Padded rows
+(past a chunk's last valid token) are exact zeros.
+"""
+
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+# stream tags
+T_QNOISE, T_KNOISE, T_V, T_QOFF, T_KOFF, T_OVERLAP, T_ZROWS, T_KROW, T_FIELD, T_MIXQ, T_MIXK = range(11)
+
+CHUNK_GRID = (3, 30, 52)           # latent frames x height x width of one chunk
+CHUNK_TOKENS = 3 * 30 * 52         # 4680
+
+
+def _rng(*key) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(k) for k in key])))
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _parallel(fn, items):
+    items = list(items)
+    if len(items) <= 1:
+        return [fn(x) for x in items]
+    with ThreadPoolExecutor(_threads()) as ex:
+        return list(ex.map(fn, items))
+
+
+def block_lengths(tokens: int, bs: int) -> np.ndarray:
+    """Valid tokens of each ``bs``-token block holding ``tokens`` tokens
+    (input structure: the last block of a chunk is partly padding)."""
+    nb = -(-tokens // bs)
+    return np.array([min(bs, tokens - b * bs) for b in range(nb)], dtype=np.int32)
+
+
+@dataclass
+class Workload:
+    """Inputs of one configuration.
+
+    Blocked tensors are head-major ``[heads][n_blocks*bs][d]`` (``torch``, CPU,
+    ``dtype``).  For raster workloads ``q``/``k``/``v`` are None and
+    ``q_raster[L][heads][d]``, ``k_raster``/``v_raster[n_chunks][L][heads][d]``
+    are given instead, with ``grid`` the chunk's latent grid."""
+    name: str
+    dtype: torch.dtype
+    heads: int
+    d: int
+    bs: int
+    q_len: np.ndarray
+    k_len: np.ndarray
+    k_per_row: np.ndarray                 # [heads*nqb] int32 budgets
+    scale: float
+    q: Optional[torch.Tensor] = None
+    k: Optional[torch.Tensor] = None
+    v: Optional[torch.Tensor] = None
+    overlap: Optional[np.ndarray] = None  # [nqb][n_candidates] float32
+    lam: float = 2.0
+    g_ref: float = 0.2
+    tau: float = 0.1
+    n_dense_tail: int = 0
+    grid: Optional[tuple] = None
+    q_raster: Optional[torch.Tensor] = None
+    k_raster: Optional[torch.Tensor] = None
+    v_raster: Optional[torch.Tensor] = None
+    head_ids: list = field(default_factory=list)
+    notes: str = ""
+
+    @property
+    def nqb(self) -> int:
+        return len(self.q_len)
+
+    @property
+    def nkb(self) -> int:
+        return len(self.k_len)
+
+    @property
+    def n_candidates(self) -> int:
+        return self.nkb - self.n_dense_tail
+
+
+def _to_dtype(x32: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
+    return t.to(dtype) if dtype != torch.float32 else t.clone()
+
+
+def _blocked_tensor(seed, noise_tag, off_tag, heads, head_ids, n_chunks, lens, bs, d,
+                    dtype, offset_sd):
+    """``[len(head_ids)][n_chunks*len(lens)*bs][d]`` with N(0,1) noise plus a
+    per-(head, block) N(0, offset_sd^2) offset vector, zero padded rows."""
+    nbc = len(lens)
+    rows_c = nbc * bs
+    out = torch.zeros((len(head_ids), n_chunks * rows_c, d), dtype=dtype)
+    valid = np.zeros(rows_c, dtype=bool)
+    for b, n in enumerate(lens):
+        valid[b * bs: b * bs + n] = True
+
+    def piece(job):
+        hi, c = job
+        h = head_ids[hi]
+        x = np.zeros((rows_c, d), dtype=np.float32)
+        noise = _rng(seed, noise_tag, h, c).standard_normal((int(valid.sum()), d), dtype=np.float32)
+        x[valid] = noise
+        if off_tag is not None and offset_sd > 0:
+            off = _rng(seed, off_tag, h, c).standard_normal((nbc, d), dtype=np.float32) * np.float32(offset_sd)
+            x += np.repeat(off, bs, axis=0) * valid[:, None]
+        out[hi, c * rows_c:(c + 1) * rows_c, :] = _to_dtype(x, dtype)
+        return None
+
+    _parallel(piece, [(hi, c) for hi in range(len(head_ids)) for c in range(n_chunks)])
+    return out
+
+
+def c1() -> Workload:
+    """Tiny fp32 routed attention: 1 head, d 64, 4 query blocks and 16 KV
+    blocks of 64 tokens, top-K 4, no bias, N(0,1) plus N(0, 0.5^2) per-block
+    offsets on Q and K, scale 1/8."""
+    seed, H, d, bs = 1001, 1, 64, 64
+    qlen = np.full(4, 64, dtype=np.int32)
+    klen = np.full(16, 64, dtype=np.int32)
+    heads = [0]
+    q = _blocked_tensor(seed, T_QNOISE, T_QOFF, H, heads, 1, qlen, bs, d, torch.float32, 0.5)
+    k = _blocked_tensor(seed, T_KNOISE, T_KOFF, H, heads, 1, klen, bs, d, torch.float32, 0.5)
+    v = _blocked_tensor(seed, T_V, None, H, heads, 1, klen, bs, d, torch.float32, 0.0)
+    return Workload("C1-tiny-fp32", torch.float32, H, d, bs, qlen, klen,
+                    np.full(H * 4, 4, dtype=np.int32), 1.0 / math.sqrt(d), q, k, v,
+                    head_ids=heads)
+
+
+def c2(heads=None) -> Workload:
+    """Wan-1.3B-like layer, bf16: 12 heads, d 128, a 4680-token query chunk in
+    37 blocks of 128 (the last holds 72 tokens), 143 full history blocks,
+    top-K 50, N(0,1) plus N(0, 0.5^2) per-block offsets, no bias."""
+    seed, H, d, bs = 1002, 12, 128, 128
+    head_ids = list(range(H)) if heads is None else list(heads)
+    qlen = block_lengths(CHUNK_TOKENS, bs)
+    klen = np.full(143, bs, dtype=np.int32)
+    q = _blocked_tensor(seed, T_QNOISE, T_QOFF, H, head_ids, 1, qlen, bs, d, torch.bfloat16, 0.5)
+    k = _blocked_tensor(seed, T_KNOISE, T_KOFF, H, head_ids, 1, klen, bs, d, torch.bfloat16, 0.5)
+    v = _blocked_tensor(seed, T_V, None, H, head_ids, 1, klen, bs, d, torch.bfloat16, 0.0)
+    return Workload("C2-wan1.3b-bf16", torch.bfloat16, len(head_ids), d, bs, qlen, klen,
+                    np.full(len(head_ids) * len(qlen), 50, dtype=np.int32), 1.0 / math.sqrt(d),
+                    q, k, v, head_ids=head_ids)
+
+
+def c3(heads=None) -> Workload:
+    """C2's tensors plus a per-(query block, KV block) overlap ~ Beta(0.5, 2)
+    drawn in float64 and stored as float32, with 11 of the 37 query-block
+    rows set to zero (forcing the unbiased fallback); lambda 2, g_ref 0.2,
+    tau 0.1, top-K 50."""
+    w = c2(heads)
+    rng = _rng(1003, T_OVERLAP, 0, 0)
+    g = rng.beta(0.5, 2.0, size=(w.nqb, w.nkb)).astype(np.float32)
+    zero_rows = _rng(1003, T_ZROWS, 0, 0).choice(w.nqb, 11, replace=False)
+    g[zero_rows, :] = 0.0
+    w.name = "C3-geometric-bias-bf16"
+    w.overlap = g
+    w.notes = "zero rows: " + ",".join(str(int(i)) for i in sorted(zero_rows))
+    return w
+
+
+def c4(c: int = 48, heads=None, n_store_chunks: Optional[int] = None) -> Workload:
+    """Growing-context 14B-like layer, bf16: 40 heads, d 128, a 4680-token
+    query chunk (37 blocks of 128), KV history of ``c`` chunks of 4680 tokens
+    (37 blocks each, the last of each chunk holds 72 tokens); N(0,1) plus
+    N(0, 0.5^2) per-block offsets on Q and K; fixed top-K 50.
+
+    The KV store is drawn chunk by chunk, so the history at ``c`` is the
+    prefix of the history at any larger ``c`` (the store grows by appending).
+    ``n_store_chunks`` (default ``c``) sets how many chunks are allocated."""
+    seed, H, d, bs = 1004, 40, 128, 128
+    head_ids = list(range(H)) if heads is None else list(heads)
+    n_store = c if n_store_chunks is None else max(c, n_store_chunks)
+    qlen = block_lengths(CHUNK_TOKENS, bs)
+    klen_chunk = block_lengths(CHUNK_TOKENS, bs)
+    q = _blocked_tensor(seed, T_QNOISE, T_QOFF, H, head_ids, 1, qlen, bs, d, torch.bfloat16, 0.5)
+    k = _blocked_tensor(seed, T_KNOISE, T_KOFF, H, head_ids, n_store, klen_chunk, bs, d, torch.bfloat16, 0.5)
+    v = _blocked_tensor(seed, T_V, None, H, head_ids, n_store, klen_chunk, bs, d, torch.bfloat16, 0.0)
+    klen = np.tile(klen_chunk, c).astype(np.int32)
+    rows = c * len(klen_chunk) * bs
+    return Workload(f"C4-growing-context-c{c}-bf16", torch.bfloat16, len(head_ids), d, bs, qlen, klen,
+                    np.full(len(head_ids) * len(qlen), 50, dtype=np.int32), 1.0 / math.sqrt(d),
+                    q, k[:, :rows, :], v[:, :rows, :], head_ids=head_ids,
+                    notes=f"store chunks allocated: {n_store}")
+
+
+def _field_params(seed):
+    """Rank-8 smooth field: each component is a sum of 4 cosines with integer
+    wave numbers in {0,1,2}^3 (not all zero) over (frame/144, y/30, x/52)
+    and uniform random phases."""
+    rng = _rng(seed, T_FIELD, 0, 0)
+    waves = []
+    for _r in range(8):
+        comps = []
+        for _m in range(4):
+            while True:
+                kk = rng.integers(0, 3, size=3)
+                if kk.any():
+                    break
+            phase = rng.uniform(0.0, 2.0 * math.pi)
+            comps.append((int(kk[0]), int(kk[1]), int(kk[2]), float(phase)))
+        waves.append(comps)
+    return waves
+
+
+def _field_values(waves, frames, n_frames_total, Hh, Ww):
+    """Field components ``[len(frames)*Hh*Ww][8]`` (float64, raster order)
+    at the given global frame indices, normalised to unit variance over the
+    whole rollout grid."""
+    tt = np.asarray(frames, dtype=np.float64)[:, None, None] / n_frames_total
+    yy = np.arange(Hh, dtype=np.float64)[None, :, None] / Hh
+    xx = np.arange(Ww, dtype=np.float64)[None, None, :] / Ww
+    out = np.zeros((len(frames), Hh, Ww, 8))
+    for r, comps in enumerate(waves):
+        f = np.zeros((len(frames), Hh, Ww))
+        for (kt, ky, kx, ph) in comps:
+            f = f + np.cos(2.0 * math.pi * (kt * tt + ky * yy + kx * xx) + ph)
+        out[..., r] = f
+    return out.reshape(-1, 8)
+
+
+def c5(heads=None, n_chunks: int = 48) -> Workload:
+    """Ragged routes, bf16: 40 heads, d 128, 64-token blocks, 48 chunks of a
+    3 x 30 x 52 grid (47 history chunks + the current one).  Q and K are a
+    rank-8 spatially smooth field over the rollout's latent grid mixed per
+    head (mixing ~ N(0, 1/8)) plus N(0, 0.3^2) noise; V ~ N(0,1).  Tensors are
+    raster token-major per chunk.  Budgets K ~ uniform integer in [8, 143]
+    per (head, query block) over the history; the current chunk's 74 blocks
+    are attended densely."""
+    seed, H, d, bs = 1005, 40, 128, 64
+    head_ids = list(range(H)) if heads is None else list(heads)
+    T, Hh, Ww = CHUNK_GRID
+    L = CHUNK_TOKENS
+    n_frames_total = T * 48
+    waves = _field_params(seed)
+    # normalisation over the whole 48-chunk rollout grid
+    all_f = _field_values(waves, range(n_frames_total), n_frames_total, Hh, Ww)
+    norm = all_f.std(axis=0)
+    mix_q = np.stack([_rng(seed, T_MIXQ, h, 0).standard_normal((8, d)) / math.sqrt(8.0) for h in range(H)])
+    mix_k = np.stack([_rng(seed, T_MIXK, h, 0).standard_normal((8, d)) / math.sqrt(8.0) for h in range(H)])
+    mix_q = mix_q[head_ids]
+    mix_k = mix_k[head_ids]
+    nh = len(head_ids)
+
+    def field_chunk(c):
+        f = _field_values(waves, range(T * c, T * c + T), n_frames_total, Hh, Ww) / norm
+        return f.astype(np.float32)
+
+    def make(mix, noise_tag, chunks, noise_sd):
+        out = torch.empty((len(chunks), L, nh, d), dtype=torch.bfloat16)
+
+        def piece(job):
+            ci, hi = job
+            c = chunks[ci]
+            base = field_chunk(c) @ mix[hi].astype(np.float32) if mix is not None else 0.0
+            noise = _rng(seed, noise_tag, head_ids[hi], c).standard_normal((L, d), dtype=np.float32)
+            x = base + noise * np.float32(noise_sd)
+            out[ci, :, hi, :] = _to_dtype(x, torch.bfloat16)
+            return None
+
+        _parallel(piece, [(ci, hi) for ci in range(len(chunks)) for hi in range(nh)])
+        return out
+
+    cur = n_chunks - 1
+    q_r = make(mix_q, T_QNOISE, [cur], 0.3)[0]
+    k_r = make(mix_k, T_KNOISE, list(range(n_chunks)), 0.3)
+    v_r = make(None, T_V, list(range(n_chunks)), 1.0)
+    nbc = -(-L // bs)
+    qlen = block_lengths(L, bs)
+    klen = np.tile(block_lengths(L, bs), n_chunks).astype(np.int32)
+    kr = _rng(seed, T_KROW, 0, 0).integers(8, 144, size=(H, nbc)).astype(np.int32)[head_ids]
+    return Workload("C5-ragged-structured-bf16", torch.bfloat16, nh, d, bs, qlen, klen,
+                    kr.reshape(-1), 1.0 / math.sqrt(d), n_dense_tail=nbc, grid=CHUNK_GRID,
+                    q_raster=q_r, k_raster=k_r, v_raster=v_r, head_ids=head_ids)
+
+
+REGISTRY = {"C1": c1, "C2": c2, "C3": c3, "C4": c4, "C5": c5}
+
+
+def get(name: str, **kw) -> Workload:
+    return REGISTRY[name](**kw)
