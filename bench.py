@@ -1,0 +1,284 @@
+"""Benchmark: routed block-sparse attention over a growing KV history at chunk
+48 on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk C]
+                    [--no-cpu-baseline] [--dense] [--sweep FILE]
+
+Workload: the 14B-like growing-context layer -- 40 heads, head dim 128, a
+3 x 30 x 52 latent chunk (4680 tokens, 37 blocks of 128), a KV history of C
+chunks (default 48: 224,640 tokens, 1776 blocks), fixed top-K 50, bf16.
+Inputs are seeded synthetic tensors (``workloads.c4``), resident in HBM
+before timing starts.
+
+One step is one attention call of the chunked model, the whole hot path:
+Gilbert index of the chunk grid; permutation of the current chunk's raster
+Q, K, V into Gilbert head-major blocks (K, V into the store's newest slot);
+routing (mean-pool Q and all history K, score, top-K, CSR); block-sparse
+attention; inverse permutation of O.
+
+Printed: one JSON line.  ``value`` = effective TFLOP/s of the step (valid
+selected (query, key) pairs x 4 d FLOP, divided by the step time).  The
+attention kernel alone is timed with events on its stream inside the timed
+region; ``roofline`` prices it against HBM bandwidth with its algorithmic
+bytes (each distinct selected K/V block once, plus Q, O and the lists).
+``cpu_baseline`` times the float64 oracle on a bounded sample on the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "block-sparse attn effective TFLOP/s + ms/call at chunk 48; % bf16 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_c4_chunk48_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_gilbert_amd", "csrc", "attn.hip")
+
+
+def attn_source_hash() -> str:
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def setup_c4(chunk: int = 48, heads=None, device="cuda:0"):
+    """C4 at history length ``chunk``: the store holds chunks 0..chunk-1 in
+    Gilbert block layout; the current chunk (index chunk-1) is also given in
+    raster layout, obtained with the library's inverse permutation, so the
+    step's forward permutation rewrites the slot with identical bits."""
+    import torch
+
+    import workloads
+    from block_sparse_attention_gilbert_amd import gilbert_perm
+    from block_sparse_attention_gilbert_amd.pipeline import RoutedAttention
+
+    w = workloads.c4(c=chunk, heads=heads)
+    k_store = w.k.contiguous().to(device)
+    v_store = w.v.contiguous().to(device)
+    ra = RoutedAttention((3, 30, 52), w.heads, w.d, w.bs, chunk, device=device, k_cap=50,
+                         k_store=k_store, v_store=v_store)
+    cur = chunk - 1
+    ks, vs = ra.slot(cur)
+    q_raster = gilbert_perm(w.q.to(device), ra.perm, block=w.bs, inverse=True)
+    k_raster = gilbert_perm(ks, ra.perm, block=w.bs, inverse=True)
+    v_raster = gilbert_perm(vs, ra.perm, block=w.bs, inverse=True)
+    torch.cuda.synchronize()
+    return dict(w=w, ra=ra, q_raster=q_raster, k_raster=k_raster, v_raster=v_raster, cur=cur)
+
+
+def run_step(st, attn_events=None):
+    return st["ra"].step(st["q_raster"], st["k_raster"], st["v_raster"], st["cur"], attn_events=attn_events)
+
+
+def work_counts(row_ptr, col_idx, q_len, k_len, heads, nqb, bs, d):
+    """Exact effective FLOP, tile FLOP, distinct (head, block) pairs and the
+    algorithmic bytes of one attention launch, from the CSR lists."""
+    import numpy as np
+    rp = row_ptr.cpu().numpy().astype(np.int64)
+    ci = col_idx.cpu().numpy().astype(np.int64)
+    k_len = np.asarray(k_len, dtype=np.int64)
+    q_len = np.asarray(q_len, dtype=np.int64)
+    eff = 0
+    pairs = 0
+    uniq_rows = 0
+    for h in range(heads):
+        seg = ci[rp[h * nqb]:rp[(h + 1) * nqb]]
+        for i in range(nqb):
+            lst = ci[rp[h * nqb + i]:rp[h * nqb + i + 1]]
+            eff += int(q_len[i]) * int(k_len[lst].sum())
+            pairs += len(lst)
+        u = np.unique(seg)
+        uniq_rows += int(k_len[u].sum())
+    flop = 4 * d * eff
+    tile_flop = 4 * d * bs * bs * pairs
+    kv_bytes = 2 * uniq_rows * d * 2                   # K and V rows of the distinct selected blocks
+    qo_bytes = 2 * heads * int(q_len.sum()) * d * 2    # Q in, O out
+    list_bytes = 4 * (len(rp) + int(rp[-1]))
+    return dict(flop=flop, tile_flop=tile_flop, pairs=pairs, uniq_rows=uniq_rows,
+                alg_bytes=kv_bytes + qo_bytes + list_bytes, visits=pairs)
+
+
+def cpu_baseline(st, n_heads=2):
+    """Time the float64 oracle (route + attention) on ``n_heads`` heads of the
+    same workload; report effective TFLOP/s on that sample."""
+    import numpy as np
+
+    from oracle import attention as oatt
+    from oracle import route as oroute
+    from oracle.numerics import bf16_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    w = st["w"]
+    flop = 0
+    t0 = time.perf_counter()
+    for h in range(n_heads):
+        q = bf16_bits_to_f64(w.q[h].contiguous().view(__import__("torch").int16).numpy())
+        k = bf16_bits_to_f64(w.k[h].contiguous().view(__import__("torch").int16).numpy())
+        v = bf16_bits_to_f64(w.v[h].contiguous().view(__import__("torch").int16).numpy())
+        r = oroute.route_head(q, k, w.q_len, w.k_len, w.bs, scale=w.scale, k_per_row=w.k_per_row[:w.nqb])
+        oatt.block_sparse_head(q, k, v, w.q_len, w.k_len, w.bs, r["lists"], w.scale)
+        for i, lst in enumerate(r["lists"]):
+            flop += 4 * w.d * int(w.q_len[i]) * int(np.asarray(w.k_len)[lst].sum())
+    dt = time.perf_counter() - t0
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "float64 oracle route + attention for %d of %d heads at chunk %d (%.1f s, %.3g FLOP)"
+                      % (n_heads, w.heads, w.nkb // 37, dt, flop)}
+
+
+def read_traffic(per_launch_bytes):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("attn_source_sha256_16") != attn_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--chunk", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--dense", action="store_true", help="also time dense attention at the same chunk")
+    ap.add_argument("--sweep", default=None, help="write a chunk 1..C sparse/dense sweep to this JSONL file")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode (see the sharding notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_gilbert_amd as bsa  # fails loudly if libbsa.so is missing
+
+    dev = "cuda:0"
+    t_setup = time.perf_counter()
+    st = setup_c4(args.chunk, device=dev)
+    w, ra = st["w"], st["ra"]
+    print("setup %.1f s (generate + upload + raster inputs)" % (time.perf_counter() - t_setup), file=sys.stderr,
+          flush=True)
+
+    # correctness guard of the step: the slot rewritten by the forward
+    # permutation must equal the generated store bits
+    ks_before = ra.slot(st["cur"])[0].clone()
+    for _ in range(args.warmup):
+        run_step(st)
+    torch.cuda.synchronize()
+    assert torch.equal(ks_before, ra.slot(st["cur"])[0]), "forward permutation did not reproduce the store slot"
+    del ks_before
+
+    events = []
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        _, r = run_step(st, attn_events=events)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    attn_ms = sum(a.elapsed_time(b) for a, b in events) / len(events)
+
+    wc = work_counts(r["row_ptr"], r["col_idx"], w.q_len, w.k_len, w.heads, w.nqb, w.bs, w.d)
+    value = wc["flop"] / (ms_step * 1e-3) / 1e12
+    attn_tflops = wc["flop"] / (attn_ms * 1e-3) / 1e12
+    achieved_gbs = wc["alg_bytes"] / (attn_ms * 1e-3) / 1e9
+    traffic = read_traffic(wc["alg_bytes"])
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) + per-block offsets; no dataset, no weights)",
+        "config": {"workload": "C4 growing-context 14B-like layer at chunk %d" % args.chunk,
+                   "heads": w.heads, "head_dim": w.d, "block": w.bs, "query_tokens": 4680,
+                   "kv_tokens": 4680 * args.chunk, "kv_blocks": w.nkb, "top_k": 50,
+                   "step": "gilbert_index + 3 forward permutes + route (full K pool) + block-sparse attention "
+                           "+ inverse permute", "parallelism": "single GPU"},
+        "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "attn": {"ms_per_call": round(attn_ms, 4), "effective_tflops": round(attn_tflops, 2),
+                 "pct_bf16_mfma_peak": round(100.0 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+                 "tile_tflops": round(wc["tile_flop"] / (attn_ms * 1e-3) / 1e12, 2),
+                 "effective_flop": wc["flop"], "listed_blocks": wc["pairs"],
+                 "distinct_kv_rows": wc["uniq_rows"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "kernel": "attn_bf16_kernel<128,128,sparse>",
+                     "alg_bytes_per_launch": wc["alg_bytes"]},
+    }
+    if args.dense:
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        ra.dense(st["cur"])
+        torch.cuda.synchronize()
+        ev[0].record()
+        n_dense = max(1, min(args.steps, 5))
+        for _ in range(n_dense):
+            ra.dense(st["cur"])
+        ev[1].record()
+        torch.cuda.synchronize()
+        dms = ev[0].elapsed_time(ev[1]) / n_dense
+        dflop = 4 * w.d * int(w.q_len.sum()) * int(w.k_len.sum()) * w.heads
+        out["dense"] = {"ms_per_call": round(dms, 3), "effective_tflops": round(dflop / (dms * 1e-3) / 1e12, 2),
+                        "speedup_sparse_vs_dense": round(dms / attn_ms, 2)}
+    if args.sweep:
+        sweep(st, args.sweep)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(st, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+def sweep(st, path):
+    """History-length sweep (chunk 1..C) of the routed call (route + sparse
+    attention) and of dense attention, on the resident store; the queries
+    stay those of the last chunk."""
+    import torch
+    ra = st["ra"]
+    with open(path, "w") as f:
+        for c in range(1, ra.store_chunks + 1):
+            cur = c - 1
+            ra.route_and_attend(cur)
+            torch.cuda.synchronize()
+            ev = []
+            for _ in range(5):
+                ra.route_and_attend(cur, attn_events=ev)
+            torch.cuda.synchronize()
+            sparse_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                ra.dense(cur)
+            e1.record()
+            torch.cuda.synchronize()
+            f.write(json.dumps({"chunk": c, "sparse_attn_ms": round(sparse_ms, 4),
+                                "dense_attn_ms": round(e0.elapsed_time(e1) / 3, 4)}) + "\n")
+            f.flush()
+            print("sweep chunk %d done" % c, file=sys.stderr, flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,329 @@
+"""Routed, indexed block-sparse attention over a Gilbert-ordered KV history,
+for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding of ``libbsa.so`` (C ABI in ``include/bsa.h``).  The
+functions here only marshal arguments: every step of the path runs in the
+library's HIP kernels, on ``torch.cuda.current_stream()`` unless a stream is
+given.  PyTorch provides device memory and streams.  If the library has not
+been built, importing this package raises ImportError; there is no fallback.
+
+Entry points (same names as the C ABI, without the ``bsa_`` prefix):
+``gilbert_index``, ``gilbert_perm``, ``route_topk`` (with
+``route_workspace_size``), ``block_sparse_attn``, ``dense_attn``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsa.so")
+
+BSA_OK, BSA_EINVAL, BSA_EUNSUPPORTED, BSA_EWORKSPACE, BSA_EHIP = range(5)
+BSA_BF16, BSA_F32 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libbsa.so is not built: run `python block_sparse_attention_gilbert_amd/build.py` "
+        "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+_f = ctypes.c_float
+
+
+class RouteArgs(ctypes.Structure):
+    """Mirror of ``bsa_route_args``."""
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", _p), ("k", _p), ("dtype", _i),
+        ("heads", _i), ("d", _i), ("block", _i), ("nqb", _i), ("nkb", _i),
+        ("q_head_stride", _i64), ("k_head_stride", _i64),
+        ("q_block_len", _p), ("kv_block_len", _p),
+        ("scale", ctypes.c_double),
+        ("overlap", _p), ("overlap_row_stride", _i64),
+        ("lam", ctypes.c_double), ("g_ref", ctypes.c_double), ("tau", ctypes.c_double),
+        ("k_fixed", _i), ("k_per_row", _p), ("k_max", _i),
+        ("n_dense_tail_blocks", _i),
+        ("kpool", _p), ("kpool_valid_blocks", _i),
+        ("row_ptr", _p), ("col_idx", _p), ("col_capacity", _i64),
+        ("fallback_counts", _p), ("sel_keys", _p),
+    ]
+
+
+_lib.bsa_version.restype = _i
+_lib.bsa_strerror.restype = ctypes.c_char_p
+_lib.bsa_strerror.argtypes = [_i]
+_lib.bsa_last_error_detail.restype = ctypes.c_char_p
+_lib.bsa_gilbert_index.restype = _i
+_lib.bsa_gilbert_index.argtypes = [_i, _i, _i, _p, _p, _p]
+_lib.bsa_gilbert_perm.restype = _i
+_lib.bsa_gilbert_perm.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i64, _i64, _i, _i, _p]
+_lib.bsa_route_workspace_size.restype = ctypes.c_size_t
+_lib.bsa_route_workspace_size.argtypes = [ctypes.POINTER(RouteArgs)]
+_lib.bsa_route_topk.restype = _i
+_lib.bsa_route_topk.argtypes = [ctypes.POINTER(RouteArgs), _p, ctypes.c_size_t, _p]
+_ATTN_COMMON = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p]
+_lib.bsa_block_sparse_attn.restype = _i
+_lib.bsa_block_sparse_attn.argtypes = _ATTN_COMMON + [_p, _p, _i64, _f, _p]
+_lib.bsa_dense_attn.restype = _i
+_lib.bsa_dense_attn.argtypes = _ATTN_COMMON + [_f, _p]
+
+EXPORTED = ("bsa_version", "bsa_strerror", "bsa_last_error_detail", "bsa_gilbert_index",
+            "bsa_gilbert_perm", "bsa_route_workspace_size", "bsa_route_topk",
+            "bsa_block_sparse_attn", "bsa_dense_attn")
+
+
+class BsaError(RuntimeError):
+    def __init__(self, code: int, detail: str):
+        self.code = code
+        self.detail = detail
+        super().__init__("%s: %s" % (_lib.bsa_strerror(code).decode(), detail))
+
+
+def _check(code: int) -> None:
+    if code != BSA_OK:
+        raise BsaError(code, _lib.bsa_last_error_detail().decode())
+
+
+def version() -> int:
+    return _lib.bsa_version()
+
+
+def library():
+    """The loaded ctypes library (for direct C-ABI calls)."""
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BSA_BF16
+    if t.dtype == torch.float32:
+        return BSA_F32
+    raise TypeError("dtype %s: bfloat16 or float32 expected" % t.dtype)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on a GPU device")
+
+
+def _heads_rows(t: torch.Tensor, d: int):
+    if t.dim() != 3 or t.shape[2] != d or t.stride(2) != 1 or t.stride(1) != d:
+        raise ValueError("expected a [heads][rows][d] tensor with contiguous rows, got shape %s strides %s"
+                         % (tuple(t.shape), t.stride()))
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _i32(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous int32 tensor" % name)
+    return t
+
+
+# --------------------------------------------------------------------- curve
+
+def gilbert_index(T: int, H: int, W: int, device="cuda", stream=None, with_inverse=True):
+    """Gilbert order of a T x H x W grid: ``(perm, inv)`` int32 tensors."""
+    n = T * H * W
+    perm = torch.empty(n, dtype=torch.int32, device=device)
+    inv = torch.empty(n, dtype=torch.int32, device=device) if with_inverse else None
+    _check(_lib.bsa_gilbert_index(T, H, W, _ptr(perm), _ptr(inv), _stream(stream)))
+    return perm, inv
+
+
+def gilbert_perm(src: torch.Tensor, perm: torch.Tensor, *, block: int, inverse: bool = False,
+                 dst: Optional[torch.Tensor] = None, L: Optional[int] = None, stream=None):
+    """Raster ``[L][heads][d]`` -> Gilbert ``[heads][n_blocks*block][d]``
+    (``inverse=False``) or back.  ``dst`` may be a head-strided view (e.g. a
+    chunk slot of a KV store); it is allocated when omitted."""
+    _need_gpu(src, perm, dst)
+    perm = _i32(perm, "perm")
+    if not inverse:
+        L_, heads, d = src.shape
+        if src.stride(2) != 1 or src.stride(1) != d:
+            raise ValueError("raster src must have contiguous [heads][d] per token")
+        rows = -(-L_ // block) * block
+        if dst is None:
+            dst = torch.empty((heads, rows, d), dtype=src.dtype, device=src.device)
+        _, drows, ghs = _heads_rows(dst, d)
+        if drows < rows:
+            raise ValueError("dst holds %d rows per head, %d needed" % (drows, rows))
+        rts = src.stride(0)
+        _check(_lib.bsa_gilbert_perm(_ptr(src), _ptr(dst), _ptr(perm), L_, heads, d, block, rts, ghs, 0,
+                                     _dtype_code(src), _stream(stream)))
+        return dst
+    heads, rows, ghs = _heads_rows(src, src.shape[2])
+    d = src.shape[2]
+    L_ = perm.numel() if L is None else L
+    if dst is None:
+        dst = torch.empty((L_, heads, d), dtype=src.dtype, device=src.device)
+    if dst.stride(2) != 1 or dst.stride(1) != d:
+        raise ValueError("raster dst must have contiguous [heads][d] per token")
+    _check(_lib.bsa_gilbert_perm(_ptr(src), _ptr(dst), _ptr(perm), L_, heads, d, block, dst.stride(0), ghs, 1,
+                                 _dtype_code(src), _stream(stream)))
+    return dst
+
+
+# --------------------------------------------------------------------- router
+
+def _route_args(q, k, *, block, nqb, nkb, q_block_len, kv_block_len, scale, overlap, lam, g_ref, tau,
+                k_fixed, k_per_row, k_max, n_dense_tail_blocks, kpool, kpool_valid_blocks,
+                row_ptr, col_idx, fallback_counts, sel_keys):
+    d = q.shape[2]
+    heads, _, qhs = _heads_rows(q, d)
+    _, _, khs = _heads_rows(k, d)
+    a = RouteArgs()
+    a.struct_size = ctypes.sizeof(RouteArgs)
+    a.q, a.k, a.dtype = q.data_ptr(), k.data_ptr(), _dtype_code(q)
+    a.heads, a.d, a.block, a.nqb, a.nkb = heads, d, block, nqb, nkb
+    a.q_head_stride, a.k_head_stride = qhs, khs
+    a.q_block_len = None if q_block_len is None else q_block_len.data_ptr()
+    a.kv_block_len = None if kv_block_len is None else kv_block_len.data_ptr()
+    a.scale = float(scale)
+    if overlap is not None:
+        if overlap.dtype != torch.float32 or overlap.stride(1) != 1:
+            raise ValueError("overlap must be float32 with contiguous rows")
+        a.overlap, a.overlap_row_stride = overlap.data_ptr(), overlap.stride(0)
+    a.lam, a.g_ref, a.tau = float(lam), float(g_ref), float(tau)
+    a.k_fixed = int(k_fixed)
+    a.k_per_row = None if k_per_row is None else k_per_row.data_ptr()
+    a.k_max = int(k_max) if k_max is not None else int(k_fixed)
+    a.n_dense_tail_blocks = int(n_dense_tail_blocks)
+    a.kpool = None if kpool is None else kpool.data_ptr()
+    a.kpool_valid_blocks = int(kpool_valid_blocks)
+    if row_ptr is not None:
+        a.row_ptr, a.col_idx, a.col_capacity = row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel()
+    a.fallback_counts = None if fallback_counts is None else fallback_counts.data_ptr()
+    a.sel_keys = None if sel_keys is None else sel_keys.data_ptr()
+    return a
+
+
+def route_capacity(heads: int, nqb: int, nkb: int, k_cap: int, n_dense_tail_blocks: int = 0) -> int:
+    """Entries ``col_idx`` must hold."""
+    n_cand = nkb - n_dense_tail_blocks
+    return heads * nqb * (min(k_cap, n_cand) + n_dense_tail_blocks)
+
+
+def route_topk(q: torch.Tensor, k: torch.Tensor, *, block: int, nqb: int, nkb: int, scale: float,
+               q_block_len=None, kv_block_len=None, overlap=None, lam: float = 2.0, g_ref: float = 0.2,
+               tau: float = 0.1, k_fixed: int = 50, k_per_row=None, k_max: Optional[int] = None,
+               n_dense_tail_blocks: int = 0, kpool=None, kpool_valid_blocks: int = 0,
+               want_keys: bool = False, out: Optional[dict] = None, workspace=None, stream=None):
+    """Pool, score, fuse and select.  Returns a dict with ``row_ptr``,
+    ``col_idx`` (capacity-sized; the first ``row_ptr[-1]`` entries are the
+    lists), ``fallback_counts`` and optionally ``sel_keys``.  ``out`` and
+    ``workspace`` may be passed in to avoid allocations."""
+    _need_gpu(q, k, q_block_len, kv_block_len, overlap, k_per_row, kpool)
+    heads = q.shape[0]
+    n_cand = nkb - n_dense_tail_blocks
+    k_cap = k_max if k_per_row is not None else k_fixed
+    if k_per_row is not None and k_max is None:
+        raise ValueError("k_max is required with k_per_row")
+    dev = q.device
+    if out is None:
+        out = {
+            "row_ptr": torch.empty(heads * nqb + 1, dtype=torch.int32, device=dev),
+            "col_idx": torch.empty(max(1, route_capacity(heads, nqb, nkb, k_cap, n_dense_tail_blocks)),
+                                   dtype=torch.int32, device=dev),
+            "fallback_counts": torch.zeros(2, dtype=torch.int32, device=dev),
+            "sel_keys": torch.empty((heads, nqb, n_cand), dtype=torch.float64, device=dev) if want_keys else None,
+        }
+    a = _route_args(q, k, block=block, nqb=nqb, nkb=nkb, q_block_len=_i32(q_block_len, "q_block_len"),
+                    kv_block_len=_i32(kv_block_len, "kv_block_len"), scale=scale, overlap=overlap, lam=lam,
+                    g_ref=g_ref, tau=tau, k_fixed=k_fixed, k_per_row=_i32(k_per_row, "k_per_row"), k_max=k_max,
+                    n_dense_tail_blocks=n_dense_tail_blocks, kpool=kpool, kpool_valid_blocks=kpool_valid_blocks,
+                    row_ptr=out["row_ptr"], col_idx=out["col_idx"], fallback_counts=out["fallback_counts"],
+                    sel_keys=out.get("sel_keys"))
+    need = _lib.bsa_route_workspace_size(ctypes.byref(a))
+    if need == 0:
+        _check(_lib.bsa_route_topk(ctypes.byref(a), None, 0, _stream(stream)))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    out["workspace"] = workspace
+    _check(_lib.bsa_route_topk(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def route_workspace_size(q, k, **kw) -> int:
+    """Workspace bytes ``route_topk`` needs for these arguments."""
+    a = _route_args(q, k, row_ptr=None, col_idx=None, fallback_counts=None, sel_keys=None, **kw)
+    return _lib.bsa_route_workspace_size(ctypes.byref(a))
+
+
+# --------------------------------------------------------------------- attention
+
+def _attn_prep(q, k, v, out, lse, block):
+    _need_gpu(q, k, v, out, lse)
+    d = q.shape[2]
+    heads, qrows, qhs = _heads_rows(q, d)
+    _, krows, khs = _heads_rows(k, d)
+    _, vrows, vhs = _heads_rows(v, d)
+    if k.shape[0] != heads or v.shape[0] != heads or vrows < krows:
+        raise ValueError("q, k, v head counts / rows disagree")
+    if qrows % block or krows % block:
+        raise ValueError("row counts must be multiples of the block size")
+    if out is None:
+        out = torch.empty((heads, qrows, d), dtype=q.dtype, device=q.device)
+    _, _, ohs = _heads_rows(out, d)
+    if lse is True:
+        lse = torch.empty((heads, qrows), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor")
+    return d, heads, qrows // block, krows // block, qhs, khs, vhs, out, ohs, lse
+
+
+def block_sparse_attn(q, k, v, row_ptr, col_idx, *, block: int, scale: Optional[float] = None,
+                      q_block_len=None, kv_block_len=None, out=None, lse=None, nkb: Optional[int] = None,
+                      stream=None):
+    """Attention of every (head, query block) over its listed KV blocks.
+    ``lse=True`` allocates and returns the log-sum-exp.  Returns ``(O, LSE)``."""
+    _need_gpu(row_ptr, col_idx)
+    d, heads, nqb, nkb_, qhs, khs, vhs, out, ohs, lse = _attn_prep(q, k, v, out, lse, block)
+    nkb = nkb_ if nkb is None else nkb
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(_lib.bsa_block_sparse_attn(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), heads, d, block, nqb, nkb, qhs, khs,
+        vhs, ohs, _ptr(_i32(q_block_len, "q_block_len")), _ptr(_i32(kv_block_len, "kv_block_len")),
+        _ptr(_i32(row_ptr, "row_ptr")), _ptr(_i32(col_idx, "col_idx")), col_idx.numel(), scale,
+        _stream(stream)))
+    return out, lse
+
+
+def dense_attn(q, k, v, *, block: int, scale: Optional[float] = None, q_block_len=None, kv_block_len=None,
+               out=None, lse=None, nkb: Optional[int] = None, stream=None):
+    """Dense attention over every KV block, through the same kernel."""
+    d, heads, nqb, nkb_, qhs, khs, vhs, out, ohs, lse = _attn_prep(q, k, v, out, lse, block)
+    nkb = nkb_ if nkb is None else nkb
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(_lib.bsa_dense_attn(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), heads, d, block, nqb, nkb, qhs, khs,
+        vhs, ohs, _ptr(_i32(q_block_len, "q_block_len")), _ptr(_i32(kv_block_len, "kv_block_len")), scale,
+        _stream(stream)))
+    return out, lse
+
+
+__all__ = ["gilbert_index", "gilbert_perm", "route_topk", "route_workspace_size", "route_capacity",
+           "block_sparse_attn", "dense_attn", "version", "library", "BsaError", "RouteArgs", "EXPORTED",
+           "BSA_OK", "BSA_EINVAL", "BSA_EUNSUPPORTED", "BSA_EWORKSPACE", "BSA_EHIP", "BSA_BF16", "BSA_F32"]

@@ -1,0 +1,77 @@
+// C ABI entry points: validate on the host, then enqueue on the caller's
+// stream.  See include/bsa.h for the contract of each function.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace {
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return BSA_OK;
+    return bsa::fail(BSA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsa_gilbert_index(int T, int H, int W, int32_t* perm, int32_t* inv, hipStream_t stream) {
+    bsa::clear_error();
+    const int st = bsa::validate_gilbert_index(T, H, W, perm);
+    if (st != BSA_OK) return st;
+    return hip_status(bsa::launch_gilbert_index(T, H, W, perm, inv, stream), "gilbert_index launch");
+}
+
+int bsa_gilbert_perm(const void* src, void* dst, const int32_t* perm, int L, int heads, int d, int block,
+                     int64_t raster_token_stride, int64_t gilbert_head_stride, int inverse, int dtype,
+                     hipStream_t stream) {
+    bsa::clear_error();
+    const int st = bsa::validate_gilbert_perm(src, dst, perm, L, heads, d, block, raster_token_stride,
+                                              gilbert_head_stride, inverse, dtype);
+    if (st != BSA_OK) return st;
+    return hip_status(bsa::launch_gilbert_perm(src, dst, perm, L, heads, d, block, raster_token_stride,
+                                               gilbert_head_stride, inverse, dtype, stream),
+                      "gilbert_perm launch");
+}
+
+int bsa_route_topk(const bsa_route_args* args, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    bsa::clear_error();
+    bsa::RouteLayout lay;
+    const int st = bsa::validate_route(args, &lay);
+    if (st != BSA_OK) return st;
+    if (!workspace) return bsa::fail(BSA_EWORKSPACE, "workspace is NULL (%zu bytes needed)", lay.total);
+    if (workspace_bytes < lay.total)
+        return bsa::fail(BSA_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, lay.total);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return bsa::fail(BSA_EWORKSPACE, "workspace must be 256-byte aligned");
+    return hip_status(bsa::launch_route(args, lay, workspace, stream), "route launch");
+}
+
+int bsa_block_sparse_attn(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int heads,
+                          int d, int block, int nqb, int nkb, int64_t q_head_stride, int64_t k_head_stride,
+                          int64_t v_head_stride, int64_t o_head_stride, const int32_t* q_block_len,
+                          const int32_t* kv_block_len, const int32_t* row_ptr, const int32_t* col_idx,
+                          int64_t col_len, float scale, hipStream_t stream) {
+    bsa::clear_error();
+    bsa::AttnProblem p{q,      k,     v,    o,       lse,          dtype,        heads,   d,       block,
+                       nqb,    nkb,   q_head_stride, k_head_stride, v_head_stride, o_head_stride,
+                       q_block_len, kv_block_len, row_ptr, col_idx, col_len, scale};
+    const int st = bsa::validate_attn(p, false);
+    if (st != BSA_OK) return st;
+    return hip_status(bsa::launch_attn(p, false, stream), "block_sparse_attn launch");
+}
+
+int bsa_dense_attn(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int heads, int d,
+                   int block, int nqb, int nkb, int64_t q_head_stride, int64_t k_head_stride,
+                   int64_t v_head_stride, int64_t o_head_stride, const int32_t* q_block_len,
+                   const int32_t* kv_block_len, float scale, hipStream_t stream) {
+    bsa::clear_error();
+    bsa::AttnProblem p{q,      k,     v,    o,       lse,          dtype,        heads,   d,       block,
+                       nqb,    nkb,   q_head_stride, k_head_stride, v_head_stride, o_head_stride,
+                       q_block_len, kv_block_len, nullptr, nullptr, 0, scale};
+    const int st = bsa::validate_attn(p, true);
+    if (st != BSA_OK) return st;
+    return hip_status(bsa::launch_attn(p, true, stream), "dense_attn launch");
+}
+
+}  // extern "C"

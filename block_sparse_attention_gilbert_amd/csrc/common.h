@@ -1,0 +1,57 @@
+// Shared host-side helpers of the bsa library: status reporting and the
+// argument records that the validation layer fills and the launchers read.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "bsa.h"
+
+namespace bsa {
+
+// Record a formatted detail for the calling thread and return `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+const char* last_detail();
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int dtype_bytes(int dtype) { return dtype == BSA_BF16 ? 2 : 4; }
+
+// Validated attention problem (shared by the sparse and dense entry points).
+struct AttnProblem {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int dtype;
+    int heads, d, block, nqb, nkb;
+    int64_t q_hs, k_hs, v_hs, o_hs;
+    const int32_t* q_len;
+    const int32_t* kv_len;
+    const int32_t* row_ptr;  // NULL for dense
+    const int32_t* col_idx;  // NULL for dense
+    int64_t col_len;
+    float scale;
+};
+
+// Workspace layout of the router (byte offsets, 256-byte aligned).
+struct RouteLayout {
+    size_t qbar, kbar, keys, keff, flags, total;
+    int n_cand;
+    bool kbar_in_ws, keys_in_ws;
+};
+
+int validate_gilbert_index(int T, int H, int W, const int32_t* perm);
+int validate_gilbert_perm(const void* src, const void* dst, const int32_t* perm, int L, int heads,
+                          int d, int block, int64_t raster_token_stride,
+                          int64_t gilbert_head_stride, int inverse, int dtype);
+int validate_attn(const AttnProblem& p, bool dense);
+int validate_route(const bsa_route_args* a, RouteLayout* lay);
+size_t route_layout(const bsa_route_args* a, RouteLayout* lay);
+
+// Largest candidate count the in-LDS top-K sort handles.
+constexpr int kMaxCandidates = 4096;
+
+}  // namespace bsa

@@ -1,0 +1,121 @@
+// Generalized-Hilbert ("Gilbert") order of a latent chunk and the
+// raster <-> Gilbert permutation of token tensors.
+//
+// [Velox: Spatial Memory Makes World Models Efficient -- Key Contributions 3
+//  ("global-aligned Gilbert KV storage"); Methodology, Step 6 (the order keeps
+//  neighbouring image regions contiguous, so local neighbourhoods and
+//  block-contiguous KV storage share one coordinate frame)]
+// [Light Interaction -- abstract ("3D block sparse attention")]
+//
+// The pages name the curve but do not define it.  The definition used here:
+// a cuboid is filled from corner p along a travel axis a (ending one cell
+// short of p + a when parity allows), with two further axes b and c.
+// Halving an axis rounds its half up to even when the half is odd and the
+// axis is longer than 2.  Rules, in order:
+//   |b| = |c| = 1          straight run along a
+//   |c| = 1 (or |b| = 1)   the 2-D rule in the plane (a, b) (or (a, c))
+//   |a| = 1                the 2-D rule on the (b, c) face along the longer
+//   |b| = |c| = 2          |a| = 2: face a=0 by the 2-D rule along b, then
+//                          face a=1 from its b-far corner along -b;
+//                          otherwise split a at its even half
+//   2|a| > 3 max(|b|,|c|)  split a at its even half, both parts along a
+//   otherwise              U-turn in the plane of a and the longer L of b, c
+//                          (b on ties), the remaining axis O carried whole:
+//                          (p, L/2, a/2, O), (p + L/2, a, L - L/2, O),
+//                          (p + a - unit(a) + L/2 - unit(L), -L/2, -(a - a/2), O)
+// 2-D rule on (a, b): |b| = 1 run along a; |a| = 1 run along b; 2|a| > 3|b|
+// split a; otherwise (p, b/2, a/2), (p + b/2, a, b - b/2),
+// (p + a - unit(a) + b/2 - unit(b), -b/2, -(a - a/2)).
+// Top level: travel axis = longest of (w, h, t), ties in that order, the
+// next longest second, start (0, 0, 0).
+//
+// Each GPU thread finds the cell at one curve position by descending this
+// subdivision: at every level it computes the children's cell counts and
+// steps into the child that holds its position.
+#include <hip/hip_runtime.h>
+
+#include "gilbert_curve.h"
+#include "kernels.h"
+
+namespace bsa {
+namespace {
+
+using curve::V3;
+using curve::gilbert_cell;
+
+__global__ void gilbert_index_kernel(int T, int H, int W, int32_t* __restrict__ perm,
+                                     int32_t* __restrict__ inv) {
+    const int64_t n = (int64_t)T * H * W;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const V3 cell = gilbert_cell(T, H, W, i);
+    const int32_t r = (int32_t)(((int64_t)cell.t * H + cell.h) * W + cell.w);
+    perm[i] = r;
+    if (inv) inv[r] = (int32_t)i;
+}
+
+// One thread moves one 16-byte chunk of one (row, head).  Threads walk the
+// chunks of a row fastest, then heads, then rows, so raster reads cover a
+// token's heads contiguously and Gilbert writes cover whole rows.
+template <bool INVERSE>
+__global__ void gilbert_perm_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                    const int32_t* __restrict__ perm, int L, int heads,
+                                    int chunks_per_row, int64_t rows_total,
+                                    int64_t raster_token_stride_c, int64_t gilbert_head_stride_c) {
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = rows_total * heads * chunks_per_row;
+    if (tid >= total) return;
+    const int ch = (int)(tid % chunks_per_row);
+    const int64_t rest = tid / chunks_per_row;
+    const int h = (int)(rest % heads);
+    const int64_t i = rest / heads;
+    const int64_t g = h * gilbert_head_stride_c + i * chunks_per_row + ch;
+    if (!INVERSE) {
+        if (i < L) {
+            const int64_t r = (int64_t)perm[i] * raster_token_stride_c + (int64_t)h * chunks_per_row + ch;
+            dst[g] = src[r];
+        } else {
+            dst[g] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    } else {
+        if (i < L) {
+            const int64_t r = (int64_t)perm[i] * raster_token_stride_c + (int64_t)h * chunks_per_row + ch;
+            dst[r] = src[g];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gilbert_index(int T, int H, int W, int32_t* perm, int32_t* inv, hipStream_t stream) {
+    const int64_t n = (int64_t)T * H * W;
+    const int threads = 256;
+    const unsigned blocks = (unsigned)((n + threads - 1) / threads);
+    hipLaunchKernelGGL(gilbert_index_kernel, dim3(blocks), dim3(threads), 0, stream, T, H, W, perm, inv);
+    return hipGetLastError();
+}
+
+hipError_t launch_gilbert_perm(const void* src, void* dst, const int32_t* perm, int L, int heads, int d,
+                               int block, int64_t raster_token_stride, int64_t gilbert_head_stride,
+                               int inverse, int dtype, hipStream_t stream) {
+    const int eb = dtype == BSA_BF16 ? 2 : 4;
+    const int chunk_elems = 16 / eb;
+    const int chunks_per_row = d / chunk_elems;
+    const int64_t rows_total = inverse ? (int64_t)L : ((int64_t)L + block - 1) / block * block;
+    const int64_t total = rows_total * heads * chunks_per_row;
+    const int threads = 256;
+    const unsigned blocks = (unsigned)((total + threads - 1) / threads);
+    const int64_t rts_c = raster_token_stride / chunk_elems;
+    const int64_t ghs_c = gilbert_head_stride / chunk_elems;
+    if (inverse)
+        hipLaunchKernelGGL(gilbert_perm_kernel<true>, dim3(blocks), dim3(threads), 0, stream,
+                           static_cast<const uint4*>(src), static_cast<uint4*>(dst), perm, L, heads,
+                           chunks_per_row, rows_total, rts_c, ghs_c);
+    else
+        hipLaunchKernelGGL(gilbert_perm_kernel<false>, dim3(blocks), dim3(threads), 0, stream,
+                           static_cast<const uint4*>(src), static_cast<uint4*>(dst), perm, L, heads,
+                           chunks_per_row, rows_total, rts_c, ghs_c);
+    return hipGetLastError();
+}
+
+}  // namespace bsa

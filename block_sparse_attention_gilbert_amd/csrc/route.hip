@@ -1,0 +1,397 @@
+// Block router: mean pooling of Q and K per block, pair scores with the soft
+// geometric bias, and top-K selection into ascending CSR lists.
+//
+// [Velox: Spatial Memory Makes World Models Efficient -- Methodology, Step 4:
+//  a per-layer importance distribution over the visible KV blocks from mean
+//  query and mean key vectors; vetted overlap (above tau) is rescaled to
+//  g_hat and multiplies the distribution by (1 + lambda g_hat), then
+//  renormalised (at most a 1 + lambda boost); Key Contributions 2: uncovered
+//  regions keep the model-derived route; Methodology, Step 5: the
+//  top-scoring blocks up to a budget]
+//
+// Arithmetic is float64 throughout.  A block mean of <= 128 bf16 values is
+// an exact float64 sum divided once, so it does not depend on summation
+// order.  The fused distribution softmax(s) * (1 + lambda g_hat) / Z orders
+// a row exactly as kappa = s + log1p(lambda g_hat) does (Z is a positive
+// per-row constant, log is increasing), so kappa is what gets ranked; a row
+// whose overlap is all zero has g_hat = 0 everywhere and so keeps kappa = s,
+// the unbiased route.  Ranking is the total order (kappa descending, block
+// index ascending).
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace bsa {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ double bf16_to_f64(uint32_t bits16) {
+    return (double)__uint_as_float(bits16 << 16);
+}
+
+// Mean of the valid rows of each block.  grid = (blocks to pool, heads).
+// Thread t owns one 16-byte chunk of a row and a stride of rows.
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads)
+pool_kernel(const void* __restrict__ x, int64_t head_stride, int d, int block,
+            const int32_t* __restrict__ lens, int b_begin, double* __restrict__ out,
+            int64_t out_head_blocks) {
+    __shared__ double part[2048];
+    constexpr int CE = BF16 ? 8 : 4;  // elements per 16-byte chunk
+    const int b = b_begin + blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+    int valid = lens ? lens[b] : block;
+    valid = valid < 0 ? 0 : (valid > block ? block : valid);
+    const int chunks = d / CE, groups = kThreads / chunks;
+    const int ch = t % chunks, g = t / chunks;
+    double acc[CE];
+#pragma unroll
+    for (int e = 0; e < CE; ++e) acc[e] = 0.0;
+    const int64_t base = h * head_stride + (int64_t)b * block * d + ch * CE;
+    for (int row = g; row < valid; row += groups) {
+        if (BF16) {
+            const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + base + (int64_t)row * d);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += bf16_to_f64(w[e] & 0xFFFFu);
+                acc[2 * e + 1] += bf16_to_f64(w[e] >> 16);
+            }
+        } else {
+            const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + base + (int64_t)row * d);
+            acc[0] += (double)f.x;
+            acc[1] += (double)f.y;
+            acc[2] += (double)f.z;
+            acc[3] += (double)f.w;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < CE; ++e) part[g * d + ch * CE + e] = acc[e];
+    __syncthreads();
+    if (t < d) {
+        double s = 0.0;
+        for (int gg = 0; gg < groups; ++gg) s += part[gg * d + t];
+        out[(h * out_head_blocks + b) * d + t] = valid > 0 ? s / (double)valid : 0.0;
+    }
+}
+
+// Which query-block rows of the overlap are all zero (flag bit 0) or never
+// above tau (flag bit 1).  grid = nqb.
+__global__ void __launch_bounds__(kThreads)
+overlap_flags_kernel(const float* __restrict__ overlap, int64_t ors, int n_cand, double tau,
+                     int32_t* __restrict__ flags) {
+    __shared__ int any_nz[kThreads / 64], any_vet[kThreads / 64];
+    const int i = blockIdx.x, t = threadIdx.x;
+    int nz = 0, vet = 0;
+    for (int j = t; j < n_cand; j += kThreads) {
+        const float g = overlap[(int64_t)i * ors + j];
+        nz |= g != 0.0f;
+        vet |= ((double)g > tau) && g > 0.0f;
+    }
+    nz = __any(nz);
+    vet = __any(vet);
+    if ((t & 63) == 0) {
+        any_nz[t >> 6] = nz;
+        any_vet[t >> 6] = vet;
+    }
+    __syncthreads();
+    if (t == 0) {
+        int a = 0, v = 0;
+        for (int w = 0; w < kThreads / 64; ++w) {
+            a |= any_nz[w];
+            v |= any_vet[w];
+        }
+        flags[i] = (a ? 0 : 1) | (v ? 0 : 2);
+    }
+}
+
+// kappa[h][i][j] = (qbar_i . kbar_j) * scale + log1p(lambda * g_hat_ij).
+// grid = (ceil(n_cand / 64), heads).  Thread (jl, rs) = (t % 64, t / 64)
+// scores candidate j0 + jl against rows r0 + rs + 4m; pooled vectors are
+// staged through LDS 32 channels at a time.
+constexpr int kScoreJ = 64, kScoreDC = 32, kScoreRG = 32;
+
+__global__ void __launch_bounds__(kThreads)
+score_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar, int64_t kbar_head_blocks,
+             int nqb, int n_cand, int d, double scale, const float* __restrict__ overlap, int64_t ors,
+             double lambda, double g_ref, double tau, double* __restrict__ keys) {
+    __shared__ double kt[kScoreJ][kScoreDC + 1];
+    __shared__ double qt[kScoreRG][kScoreDC];
+    const int h = blockIdx.y, j0 = blockIdx.x * kScoreJ, t = threadIdx.x;
+    const int jl = t % kScoreJ, rs = t / kScoreJ;
+    const int j = j0 + jl;
+    constexpr int RPT = kScoreRG / (kThreads / kScoreJ);  // rows per thread
+    for (int r0 = 0; r0 < nqb; r0 += kScoreRG) {
+        double acc[RPT];
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) acc[m] = 0.0;
+        for (int dc = 0; dc < d; dc += kScoreDC) {
+            __syncthreads();
+            for (int x = t; x < kScoreJ * kScoreDC; x += kThreads) {
+                const int jj = x / kScoreDC, dd = x % kScoreDC, jg = j0 + jj;
+                kt[jj][dd] = jg < n_cand ? kbar[(h * kbar_head_blocks + jg) * d + dc + dd] : 0.0;
+            }
+            for (int x = t; x < kScoreRG * kScoreDC; x += kThreads) {
+                const int rr = x / kScoreDC, dd = x % kScoreDC, ig = r0 + rr;
+                qt[rr][dd] = ig < nqb ? qbar[((int64_t)h * nqb + ig) * d + dc + dd] : 0.0;
+            }
+            __syncthreads();
+#pragma unroll 8
+            for (int dd = 0; dd < kScoreDC; ++dd) {
+                const double kv = kt[jl][dd];
+#pragma unroll
+                for (int m = 0; m < RPT; ++m) acc[m] = fma(qt[rs + 4 * m][dd], kv, acc[m]);
+            }
+        }
+        if (j < n_cand) {
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                const int i = r0 + rs + 4 * m;
+                if (i >= nqb) continue;
+                double kappa = acc[m] * scale;
+                if (overlap) {
+                    const double g = (double)overlap[(int64_t)i * ors + j];
+                    const double gh = g <= tau ? 0.0 : fmin(1.0, g / g_ref);
+                    kappa += log1p(lambda * gh);
+                }
+                keys[((int64_t)h * nqb + i) * n_cand + j] = kappa;
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ int block_sum_1024(int v, int* sh) {
+    const int t = threadIdx.x;
+    __syncthreads();
+    sh[t] = v;
+    __syncthreads();
+    for (int off = 512; off > 0; off >>= 1) {
+        if (t < off) sh[t] += sh[t + off];
+        __syncthreads();
+    }
+    const int r = sh[0];
+    __syncthreads();
+    return r;
+}
+
+// Single workgroup: per-row list lengths, the exclusive prefix sum into
+// row_ptr, and the fallback counts.
+__global__ void __launch_bounds__(1024)
+rowptr_kernel(int heads, int nqb, int nkb, int n_cand, int block, const int32_t* __restrict__ q_len,
+              const int32_t* __restrict__ kv_len, int k_fixed, const int32_t* __restrict__ k_per_row,
+              int k_max, const int32_t* __restrict__ flags, int32_t* __restrict__ row_ptr,
+              int32_t* __restrict__ keff, int32_t* __restrict__ fallback_counts) {
+    __shared__ int sh[1024];
+    const int t = threadIdx.x;
+    int c_vis = 0, c_tail = 0;
+    for (int j = t; j < nkb; j += 1024) {
+        const int v = kv_len ? kv_len[j] : block;
+        if (v > 0) {
+            if (j < n_cand)
+                ++c_vis;
+            else
+                ++c_tail;
+        }
+    }
+    const int n_vis = block_sum_1024(c_vis, sh);
+    const int n_tail = block_sum_1024(c_tail, sh);
+    const int rows = heads * nqb;
+    int carry = 0;
+    for (int base = 0; base < rows; base += 1024) {
+        const int r = base + t;
+        int tot = 0;
+        if (r < rows) {
+            const int i = r % nqb;
+            const int vq = q_len ? q_len[i] : block;
+            int kr = k_fixed;
+            if (k_per_row) {
+                kr = k_per_row[r];
+                kr = kr < 0 ? 0 : (kr > k_max ? k_max : kr);
+            }
+            const int ke = vq > 0 ? (kr < n_vis ? kr : n_vis) : 0;
+            keff[r] = ke;
+            tot = vq > 0 ? ke + n_tail : 0;
+        }
+        __syncthreads();
+        sh[t] = tot;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int add = t >= off ? sh[t - off] : 0;
+            __syncthreads();
+            sh[t] += add;
+            __syncthreads();
+        }
+        if (r < rows) row_ptr[r] = carry + sh[t] - tot;
+        carry += sh[1023];
+    }
+    if (t == 0) row_ptr[rows] = carry;
+    if (fallback_counts) {
+        int z = 0, u = 0;
+        if (flags) {
+            for (int i = t; i < nqb; i += 1024) {
+                z += flags[i] & 1;
+                u += (flags[i] >> 1) & 1;
+            }
+        }
+        z = block_sum_1024(z, sh);
+        u = block_sum_1024(u, sh);
+        if (t == 0) {
+            fallback_counts[0] = z;
+            fallback_counts[1] = u;
+        }
+    }
+}
+
+// Order-preserving map of a double to an unsigned integer (larger double,
+// larger key); -0 and +0 map to the same key.
+__device__ __forceinline__ unsigned long long order_key(double v) {
+    if (v == 0.0) v = 0.0;
+    const long long b = __double_as_longlong(v);
+    return b < 0 ? ~(unsigned long long)b : ((unsigned long long)b | 0x8000000000000000ull);
+}
+
+// "a before b" under (key descending, index ascending).
+__device__ __forceinline__ bool before(unsigned long long ka, int ia, unsigned long long kb, int ib) {
+    return ka > kb || (ka == kb && ia < ib);
+}
+
+// Per (query block, head): bitonic sort of the candidate keys in LDS, flag
+// the first K_eff, and write the flagged block indices in ascending order,
+// followed by the dense tail.  grid = (nqb, heads).
+__global__ void __launch_bounds__(kThreads)
+topk_kernel(const double* __restrict__ keys, int nqb, int n_cand, int nkb, int log2n, int block,
+            const int32_t* __restrict__ q_len, const int32_t* __restrict__ kv_len,
+            const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ keff,
+            int32_t* __restrict__ col_idx) {
+    __shared__ unsigned long long sk[kMaxCandidates];
+    __shared__ int si[kMaxCandidates];
+    __shared__ unsigned char flag[kMaxCandidates];
+    __shared__ int scan[kThreads];
+    const int i = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+    const int r = h * nqb + i;
+    const int vq = q_len ? q_len[i] : block;
+    if (vq <= 0) return;
+    const int start = row_ptr[r];
+    const int ke = keff[r];
+    const int N = 1 << log2n;
+    const double* row = keys + (int64_t)r * n_cand;
+    for (int x = t; x < N; x += kThreads) {
+        unsigned long long key = 0;
+        int idx = 0x7fffffff;
+        if (x < n_cand) {
+            idx = x;
+            const int v = kv_len ? kv_len[x] : block;
+            if (v > 0) {
+                key = order_key(row[x]);
+            }
+            flag[x] = 0;
+        }
+        sk[x] = key;
+        si[x] = idx;
+    }
+    __syncthreads();
+    for (int k = 2; k <= N; k <<= 1) {
+        for (int jj = k >> 1; jj > 0; jj >>= 1) {
+            for (int p = t; p < (N >> 1); p += kThreads) {
+                const int x = 2 * jj * (p / jj) + (p % jj);
+                const int y = x + jj;
+                const unsigned long long kx = sk[x], ky = sk[y];
+                const int ix = si[x], iy = si[y];
+                const bool up = (x & k) == 0;
+                const bool xb = before(kx, ix, ky, iy);
+                if (up != xb) {
+                    sk[x] = ky;
+                    sk[y] = kx;
+                    si[x] = iy;
+                    si[y] = ix;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int x = t; x < ke; x += kThreads)
+        if (si[x] < n_cand) flag[si[x]] = 1;
+    __syncthreads();
+    const int seg = (n_cand + kThreads - 1) / kThreads;
+    const int lo = t * seg < n_cand ? t * seg : n_cand;
+    const int hi = lo + seg < n_cand ? lo + seg : n_cand;
+    int cnt = 0;
+    for (int x = lo; x < hi; ++x) cnt += flag[x];
+    scan[t] = cnt;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+        const int add = t >= off ? scan[t - off] : 0;
+        __syncthreads();
+        scan[t] += add;
+        __syncthreads();
+    }
+    int pos = start + scan[t] - cnt;
+    for (int x = lo; x < hi; ++x)
+        if (flag[x]) col_idx[pos++] = x;
+    if (t == 0) {
+        int p = start + ke;
+        for (int jb = n_cand; jb < nkb; ++jb) {
+            const int v = kv_len ? kv_len[jb] : block;
+            if (v > 0) col_idx[p++] = jb;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* ws, hipStream_t stream) {
+    char* w = static_cast<char*>(ws);
+    double* qbar = reinterpret_cast<double*>(w + lay.qbar);
+    const int n_cand = lay.n_cand;
+    double* kbar = lay.kbar_in_ws ? reinterpret_cast<double*>(w + lay.kbar) : a->kpool;
+    double* keys = lay.keys_in_ws ? reinterpret_cast<double*>(w + lay.keys) : a->sel_keys;
+    int32_t* keff = reinterpret_cast<int32_t*>(w + lay.keff);
+    int32_t* flags = reinterpret_cast<int32_t*>(w + lay.flags);
+    const bool bf16 = a->dtype == BSA_BF16;
+
+    // 1. pooled queries
+    {
+        dim3 grid(a->nqb, a->heads);
+        if (bf16)
+            hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kThreads), 0, stream, a->q, a->q_head_stride, a->d,
+                               a->block, a->q_block_len, 0, qbar, (int64_t)a->nqb);
+        else
+            hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kThreads), 0, stream, a->q, a->q_head_stride, a->d,
+                               a->block, a->q_block_len, 0, qbar, (int64_t)a->nqb);
+    }
+    // 2. pooled keys of the candidates not yet in the cache
+    const int kb0 = a->kpool ? a->kpool_valid_blocks : 0;
+    if (n_cand > kb0) {
+        dim3 grid(n_cand - kb0, a->heads);
+        if (bf16)
+            hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kThreads), 0, stream, a->k, a->k_head_stride, a->d,
+                               a->block, a->kv_block_len, kb0, kbar, (int64_t)n_cand);
+        else
+            hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kThreads), 0, stream, a->k, a->k_head_stride, a->d,
+                               a->block, a->kv_block_len, kb0, kbar, (int64_t)n_cand);
+    }
+    // 3. overlap row flags (for the fallback counts)
+    const bool want_flags = a->overlap && a->fallback_counts && n_cand > 0;
+    if (want_flags)
+        hipLaunchKernelGGL(overlap_flags_kernel, dim3(a->nqb), dim3(kThreads), 0, stream, a->overlap,
+                           a->overlap_row_stride, n_cand, a->tau, flags);
+    // 4. selection keys
+    if (n_cand > 0) {
+        dim3 grid((n_cand + kScoreJ - 1) / kScoreJ, a->heads);
+        hipLaunchKernelGGL(score_kernel, grid, dim3(kThreads), 0, stream, qbar, kbar, (int64_t)n_cand, a->nqb,
+                           n_cand, a->d, a->scale, a->overlap, a->overlap_row_stride, a->lambda, a->g_ref, a->tau,
+                           keys);
+    }
+    // 5. list lengths and row pointers
+    hipLaunchKernelGGL(rowptr_kernel, dim3(1), dim3(1024), 0, stream, a->heads, a->nqb, a->nkb, n_cand, a->block,
+                       a->q_block_len, a->kv_block_len, a->k_per_row ? 0 : a->k_fixed, a->k_per_row,
+                       a->k_max, want_flags ? flags : nullptr, a->row_ptr, keff, a->fallback_counts);
+    // 6. selection
+    int log2n = 1;
+    while ((1 << log2n) < n_cand) ++log2n;
+    hipLaunchKernelGGL(topk_kernel, dim3(a->nqb, a->heads), dim3(kThreads), 0, stream, keys, a->nqb, n_cand, a->nkb,
+                       log2n, a->block, a->q_block_len, a->kv_block_len, a->row_ptr, keff, a->col_idx);
+    return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,189 @@
+// Host-side argument validation and error reporting of the bsa C ABI.
+//
+// This file makes no HIP runtime call, so it builds with a plain host
+// compiler and every error path can be exercised without a GPU.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+
+namespace bsa {
+
+namespace {
+thread_local char g_detail[512] = {0};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_dim(int x) { return x == 64 || x == 128; }
+}  // namespace
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_detail[0] = 0; }
+
+const char* last_detail() { return g_detail; }
+
+int validate_gilbert_index(int T, int H, int W, const int32_t* perm) {
+    if (T < 1 || H < 1 || W < 1) return fail(BSA_EINVAL, "grid %d x %d x %d: dimensions must be >= 1", T, H, W);
+    if ((int64_t)T * H * W > INT32_MAX) return fail(BSA_EINVAL, "grid %d x %d x %d exceeds 2^31-1 cells", T, H, W);
+    if (!perm) return fail(BSA_EINVAL, "perm is NULL");
+    return BSA_OK;
+}
+
+int validate_gilbert_perm(const void* src, const void* dst, const int32_t* perm, int L, int heads,
+                          int d, int block, int64_t raster_token_stride,
+                          int64_t gilbert_head_stride, int inverse, int dtype) {
+    if (!src || !dst || !perm) return fail(BSA_EINVAL, "src, dst and perm must be non-NULL");
+    if (dtype != BSA_BF16 && dtype != BSA_F32) return fail(BSA_EUNSUPPORTED, "dtype %d", dtype);
+    if (!supported_dim(d)) return fail(BSA_EUNSUPPORTED, "d = %d (64 or 128)", d);
+    if (!supported_dim(block)) return fail(BSA_EUNSUPPORTED, "block = %d (64 or 128)", block);
+    if (L < 1 || heads < 1) return fail(BSA_EINVAL, "L = %d, heads = %d must be >= 1", L, heads);
+    if (inverse != 0 && inverse != 1) return fail(BSA_EINVAL, "inverse = %d (0 or 1)", inverse);
+    if (raster_token_stride < (int64_t)heads * d)
+        return fail(BSA_EINVAL, "raster_token_stride %lld < heads*d = %lld", (long long)raster_token_stride,
+                    (long long)heads * d);
+    const int64_t rows = ceil_div(L, block) * block;
+    if (gilbert_head_stride < rows * d)
+        return fail(BSA_EINVAL, "gilbert_head_stride %lld < n_blocks*block*d = %lld",
+                    (long long)gilbert_head_stride, (long long)(rows * d));
+    const int eb = dtype_bytes(dtype);
+    if (!aligned16(src) || !aligned16(dst) || (raster_token_stride * eb) % 16 || (gilbert_head_stride * eb) % 16)
+        return fail(BSA_EINVAL, "pointers and strides must be 16-byte aligned");
+    const char* s = static_cast<const char*>(src);
+    const char* t = static_cast<const char*>(dst);
+    const int64_t raster_bytes = ((int64_t)(L - 1) * raster_token_stride + (int64_t)heads * d) * eb;
+    const int64_t gil_bytes = ((int64_t)(heads - 1) * gilbert_head_stride + rows * d) * eb;
+    const int64_t sb = inverse ? gil_bytes : raster_bytes, tb = inverse ? raster_bytes : gil_bytes;
+    if (s < t + tb && t < s + sb) return fail(BSA_EINVAL, "src and dst overlap");
+    return BSA_OK;
+}
+
+int validate_attn(const AttnProblem& p, bool dense) {
+    if (!p.q || !p.k || !p.v || !p.o) return fail(BSA_EINVAL, "q, k, v and o must be non-NULL");
+    if (!dense && (!p.row_ptr || !p.col_idx)) return fail(BSA_EINVAL, "row_ptr and col_idx must be non-NULL");
+    if (p.dtype != BSA_BF16 && p.dtype != BSA_F32) return fail(BSA_EUNSUPPORTED, "dtype %d", p.dtype);
+    if (!supported_dim(p.d)) return fail(BSA_EUNSUPPORTED, "d = %d (64 or 128)", p.d);
+    if (!supported_dim(p.block)) return fail(BSA_EUNSUPPORTED, "block = %d (64 or 128)", p.block);
+    if (p.heads < 1 || p.nqb < 1 || p.nkb < 1)
+        return fail(BSA_EINVAL, "heads %d, nqb %d, nkb %d must be >= 1", p.heads, p.nqb, p.nkb);
+    if ((int64_t)p.heads * p.nqb > INT32_MAX / 2) return fail(BSA_EINVAL, "heads*nqb too large");
+    if (!dense && p.col_len < 0) return fail(BSA_EINVAL, "col_len %lld < 0", (long long)p.col_len);
+    const int64_t qrows = (int64_t)p.nqb * p.block, krows = (int64_t)p.nkb * p.block;
+    if (p.q_hs < qrows * p.d || p.o_hs < qrows * p.d)
+        return fail(BSA_EINVAL, "q/o head stride below nqb*block*d = %lld", (long long)(qrows * p.d));
+    if (p.k_hs < krows * p.d || p.v_hs < krows * p.d)
+        return fail(BSA_EINVAL, "k/v head stride below nkb*block*d = %lld", (long long)(krows * p.d));
+    const int eb = dtype_bytes(p.dtype);
+    if (!aligned16(p.q) || !aligned16(p.k) || !aligned16(p.v) || !aligned16(p.o) || (p.q_hs * eb) % 16 ||
+        (p.k_hs * eb) % 16 || (p.v_hs * eb) % 16 || (p.o_hs * eb) % 16)
+        return fail(BSA_EINVAL, "tensor pointers and head strides must be 16-byte aligned");
+    if (!(p.scale > 0.0f) || p.scale > 3.0e38f) return fail(BSA_EINVAL, "scale must be finite and > 0");
+    return BSA_OK;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t route_layout(const bsa_route_args* a, RouteLayout* lay) {
+    const int n_cand = a->nkb - a->n_dense_tail_blocks;
+    size_t off = 0;
+    lay->n_cand = n_cand;
+    lay->qbar = off;
+    off = align256(off + sizeof(double) * (size_t)a->heads * a->nqb * a->d);
+    lay->kbar_in_ws = a->kpool == nullptr;
+    lay->kbar = off;
+    if (lay->kbar_in_ws) off = align256(off + sizeof(double) * (size_t)a->heads * n_cand * a->d);
+    lay->keys_in_ws = a->sel_keys == nullptr;
+    lay->keys = off;
+    if (lay->keys_in_ws) off = align256(off + sizeof(double) * (size_t)a->heads * a->nqb * n_cand);
+    lay->keff = off;
+    off = align256(off + sizeof(int32_t) * ((size_t)a->heads * a->nqb + 8));
+    lay->flags = off;
+    off = align256(off + sizeof(int32_t) * ((size_t)a->nqb + 8));
+    lay->total = off;
+    return off;
+}
+
+int validate_route(const bsa_route_args* a, RouteLayout* lay) {
+    if (!a) return fail(BSA_EINVAL, "args is NULL");
+    if (a->struct_size != sizeof(bsa_route_args))
+        return fail(BSA_EINVAL, "struct_size %zu != sizeof(bsa_route_args) %zu", a->struct_size,
+                    sizeof(bsa_route_args));
+    if (!a->q || !a->k) return fail(BSA_EINVAL, "q and k must be non-NULL");
+    if (!a->row_ptr || !a->col_idx) return fail(BSA_EINVAL, "row_ptr and col_idx must be non-NULL");
+    if (a->dtype != BSA_BF16 && a->dtype != BSA_F32) return fail(BSA_EUNSUPPORTED, "dtype %d", a->dtype);
+    if (!supported_dim(a->d)) return fail(BSA_EUNSUPPORTED, "d = %d (64 or 128)", a->d);
+    if (!supported_dim(a->block)) return fail(BSA_EUNSUPPORTED, "block = %d (64 or 128)", a->block);
+    if (a->heads < 1 || a->nqb < 1 || a->nkb < 1)
+        return fail(BSA_EINVAL, "heads %d, nqb %d, nkb %d must be >= 1", a->heads, a->nqb, a->nkb);
+    if (a->n_dense_tail_blocks < 0 || a->n_dense_tail_blocks > a->nkb)
+        return fail(BSA_EINVAL, "n_dense_tail_blocks %d outside [0, nkb]", a->n_dense_tail_blocks);
+    const int n_cand = a->nkb - a->n_dense_tail_blocks;
+    if (n_cand > kMaxCandidates)
+        return fail(BSA_EUNSUPPORTED, "%d candidate blocks exceed the in-LDS selection limit %d", n_cand,
+                    kMaxCandidates);
+    if ((int64_t)a->heads * a->nqb > (1 << 24)) return fail(BSA_EINVAL, "heads*nqb too large");
+    const int64_t qrows = (int64_t)a->nqb * a->block, krows = (int64_t)a->nkb * a->block;
+    if (a->q_head_stride < qrows * a->d) return fail(BSA_EINVAL, "q_head_stride below nqb*block*d");
+    if (a->k_head_stride < krows * a->d) return fail(BSA_EINVAL, "k_head_stride below nkb*block*d");
+    const int eb = dtype_bytes(a->dtype);
+    if (!aligned16(a->q) || !aligned16(a->k) || (a->q_head_stride * eb) % 16 || (a->k_head_stride * eb) % 16)
+        return fail(BSA_EINVAL, "q/k pointers and head strides must be 16-byte aligned");
+    if (!(a->scale > 0.0) || a->scale > 1.0e300) return fail(BSA_EINVAL, "scale must be finite and > 0");
+    if (a->overlap) {
+        if (a->overlap_row_stride < n_cand) return fail(BSA_EINVAL, "overlap_row_stride below the candidate count");
+        if (!(a->g_ref > 0.0)) return fail(BSA_EINVAL, "g_ref must be > 0");
+        if (!(a->lambda >= 0.0)) return fail(BSA_EINVAL, "lambda must be >= 0");
+        if (!(a->tau == a->tau)) return fail(BSA_EINVAL, "tau is NaN");
+    }
+    int kcap;
+    if (a->k_per_row) {
+        if (a->k_max < 0) return fail(BSA_EINVAL, "k_max %d < 0", a->k_max);
+        kcap = a->k_max;
+    } else {
+        if (a->k_fixed < 0) return fail(BSA_EINVAL, "k_fixed %d < 0", a->k_fixed);
+        kcap = a->k_fixed;
+    }
+    if (kcap > n_cand) kcap = n_cand;
+    if (a->kpool && (a->kpool_valid_blocks < 0 || a->kpool_valid_blocks > n_cand))
+        return fail(BSA_EINVAL, "kpool_valid_blocks %d outside [0, %d]", a->kpool_valid_blocks, n_cand);
+    const int64_t need = (int64_t)a->heads * a->nqb * ((int64_t)kcap + a->n_dense_tail_blocks);
+    if (a->col_capacity < need)
+        return fail(BSA_EINVAL, "col_capacity %lld < heads*nqb*(k cap + dense tail) = %lld",
+                    (long long)a->col_capacity, (long long)need);
+    route_layout(a, lay);
+    return BSA_OK;
+}
+
+}  // namespace bsa
+
+extern "C" {
+
+int bsa_version(void) { return 100; }  // 0.1.0
+
+const char* bsa_strerror(int status) {
+    switch (status) {
+        case BSA_OK: return "ok";
+        case BSA_EINVAL: return "invalid argument";
+        case BSA_EUNSUPPORTED: return "unsupported configuration";
+        case BSA_EWORKSPACE: return "workspace missing or too small";
+        case BSA_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* bsa_last_error_detail(void) { return bsa::last_detail(); }
+
+size_t bsa_route_workspace_size(const bsa_route_args* args) {
+    bsa::RouteLayout lay;
+    if (bsa::validate_route(args, &lay) != BSA_OK) return 0;
+    return lay.total;
+}
+
+}  // extern "C"

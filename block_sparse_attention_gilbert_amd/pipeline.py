@@ -1,0 +1,141 @@
+"""One attention call of a chunked model over its growing KV history, as a
+chain of the library's entry points with every buffer allocated up front.
+
+[Velox: Spatial Memory Makes World Models Efficient -- Methodology (the model
+generates one chunk at a time and keeps every previous chunk in a KV cache;
+only the set of historical KV blocks each region may look at changes),
+Steps 4-6; Key Contributions 3]
+
+Per call (``RoutedAttention.step``):
+
+1. the chunk's Gilbert order (computed once per grid and cached);
+2. Q, K, V of the current chunk, raster token-major ``[L][heads][d]``, are
+   permuted into Gilbert head-major block-padded layout; K and V land in the
+   current chunk's slot of the KV store (the store grows by appending);
+3. the router pools, scores, fuses and selects over the visible history;
+4. block-sparse attention over the selected blocks;
+5. O is permuted back to raster order.
+
+Nothing here computes on the host: each step is one or more HIP kernels of
+``libbsa.so`` on the current stream.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from . import (_check, _lib, _ptr, _stream, block_sparse_attn, dense_attn, gilbert_index, gilbert_perm,
+               route_capacity, route_topk)
+
+
+def block_lengths(tokens: int, block: int, n_chunks: int = 1, device="cuda") -> torch.Tensor:
+    nb = -(-tokens // block)
+    one = [min(block, tokens - b * block) for b in range(nb)]
+    return torch.tensor(one * n_chunks, dtype=torch.int32, device=device)
+
+
+class RoutedAttention:
+    """Buffers and state for routed attention over a KV store of
+    ``store_chunks`` chunks of a ``grid`` = (T, H, W) latent chunk."""
+
+    def __init__(self, grid, heads: int, d: int, block: int, store_chunks: int, dtype=torch.bfloat16,
+                 device="cuda", k_cap: int = 50, n_dense_tail_chunks: int = 0,
+                 k_store: Optional[torch.Tensor] = None, v_store: Optional[torch.Tensor] = None):
+        self.grid = tuple(grid)
+        self.L = grid[0] * grid[1] * grid[2]
+        self.heads, self.d, self.block, self.dtype, self.device = heads, d, block, dtype, device
+        self.nbc = -(-self.L // block)              # blocks per chunk
+        self.rows_c = self.nbc * block
+        self.store_chunks = store_chunks
+        self.k_cap = k_cap
+        self.n_dense_tail_chunks = n_dense_tail_chunks
+        self.scale = 1.0 / math.sqrt(d)
+        shape = (heads, store_chunks * self.rows_c, d)
+        self.k_store = torch.zeros(shape, dtype=dtype, device=device) if k_store is None else k_store
+        self.v_store = torch.zeros(shape, dtype=dtype, device=device) if v_store is None else v_store
+        self.q_blk = torch.empty((heads, self.rows_c, d), dtype=dtype, device=device)
+        self.o_blk = torch.empty((heads, self.rows_c, d), dtype=dtype, device=device)
+        self.o_raster = torch.empty((self.L, heads, d), dtype=dtype, device=device)
+        self.lse = torch.empty((heads, self.rows_c), dtype=torch.float32, device=device)
+        self.q_len = block_lengths(self.L, block, 1, device)
+        self.kv_len = block_lengths(self.L, block, store_chunks, device)
+        self.perm, self.inv = gilbert_index(*self.grid, device=device)
+        nkb_max = store_chunks * self.nbc
+        tail = n_dense_tail_chunks * self.nbc
+        self.route_out = {
+            "row_ptr": torch.empty(heads * self.nbc + 1, dtype=torch.int32, device=device),
+            "col_idx": torch.empty(max(1, route_capacity(heads, self.nbc, nkb_max, k_cap, tail)),
+                                   dtype=torch.int32, device=device),
+            "fallback_counts": torch.zeros(2, dtype=torch.int32, device=device),
+            "sel_keys": None,
+        }
+        self.workspace = None
+
+    def slot(self, c: int):
+        """K and V views of chunk ``c``'s slot of the store."""
+        r0, r1 = c * self.rows_c, (c + 1) * self.rows_c
+        return self.k_store[:, r0:r1, :], self.v_store[:, r0:r1, :]
+
+    def append(self, k_raster, v_raster, c: int, stream=None):
+        """Permute a chunk's raster K and V into slot ``c`` of the store."""
+        ks, vs = self.slot(c)
+        gilbert_perm(k_raster, self.perm, block=self.block, dst=ks, stream=stream)
+        gilbert_perm(v_raster, self.perm, block=self.block, dst=vs, stream=stream)
+
+    def step(self, q_raster, k_raster, v_raster, c: int, *, k_fixed: Optional[int] = None,
+             k_per_row: Optional[torch.Tensor] = None, overlap: Optional[torch.Tensor] = None,
+             lam=2.0, g_ref=0.2, tau=0.1, refresh_index: bool = True, stream=None, attn_events=None):
+        """One attention call for chunk ``c`` (0-based) over chunks 0..c.
+        Returns ``(o_raster, route_out)``.  ``attn_events``: optional list
+        that receives a (start, end) pair of timing events recorded around
+        the attention kernel on the stream it runs on."""
+        if refresh_index:
+            self._index(stream)
+        self.append(k_raster, v_raster, c, stream)
+        gilbert_perm(q_raster, self.perm, block=self.block, dst=self.q_blk, stream=stream)
+        r = self.route_and_attend(c, k_fixed=k_fixed, k_per_row=k_per_row, overlap=overlap, lam=lam, g_ref=g_ref,
+                                  tau=tau, stream=stream, attn_events=attn_events)
+        gilbert_perm(self.o_blk, self.perm, block=self.block, inverse=True, dst=self.o_raster, stream=stream)
+        return self.o_raster, r
+
+    def route_and_attend(self, c: int, *, k_fixed: Optional[int] = None, k_per_row: Optional[torch.Tensor] = None,
+                         overlap: Optional[torch.Tensor] = None, lam=2.0, g_ref=0.2, tau=0.1, stream=None,
+                         attn_events=None):
+        """Route the already permuted queries over chunks 0..c of the store
+        and attend; the result stays in Gilbert layout (``o_blk``, ``lse``)."""
+        nkb = (c + 1) * self.nbc
+        k_hist, v_hist = self.k_store[:, : nkb * self.block], self.v_store[:, : nkb * self.block]
+        tail = self.n_dense_tail_chunks * self.nbc
+        kf = self.k_cap if k_fixed is None else k_fixed
+        r = route_topk(self.q_blk, k_hist, block=self.block, nqb=self.nbc, nkb=nkb, scale=self.scale,
+                       q_block_len=self.q_len, kv_block_len=self.kv_len[:nkb], overlap=overlap, lam=lam,
+                       g_ref=g_ref, tau=tau, k_fixed=kf, k_per_row=k_per_row,
+                       k_max=self.k_cap if k_per_row is not None else None, n_dense_tail_blocks=tail,
+                       out=self.route_out, workspace=self.workspace, stream=stream)
+        self.workspace = r["workspace"]
+        if attn_events is not None:
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            ev[0].record(stream)
+        block_sparse_attn(self.q_blk, k_hist, v_hist, r["row_ptr"], r["col_idx"], block=self.block,
+                          scale=self.scale, q_block_len=self.q_len, kv_block_len=self.kv_len[:nkb],
+                          out=self.o_blk, lse=self.lse, stream=stream)
+        if attn_events is not None:
+            ev[1].record(stream)
+            attn_events.append(ev)
+        return r
+
+    def _index(self, stream=None):
+        """Recompute the chunk's Gilbert order into the preallocated buffers."""
+        _check(_lib.bsa_gilbert_index(self.grid[0], self.grid[1], self.grid[2], _ptr(self.perm), _ptr(self.inv),
+                                      _stream(stream)))
+
+    def dense(self, c: int, stream=None):
+        """Dense attention of the current (already permuted) queries over
+        chunks 0..c, through the same kernel."""
+        nkb = (c + 1) * self.nbc
+        return dense_attn(self.q_blk, self.k_store[:, : nkb * self.block], self.v_store[:, : nkb * self.block],
+                          block=self.block, scale=self.scale, q_block_len=self.q_len,
+                          kv_block_len=self.kv_len[:nkb], out=self.o_blk, lse=self.lse, stream=stream)

@@ -1,0 +1,264 @@
+/*
+ * bsa.h -- C ABI of the routed, indexed block-sparse attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library implements one hot path of chunked video world models whose
+ * new chunk attends to a growing KV history:
+ *
+ *   1. a generalized-Hilbert ("Gilbert") token order of a latent chunk, so a
+ *      run of consecutive tokens (a KV block) is a compact 3-D tile, and the
+ *      permutation of raster tensors into that order
+ *      [Velox: Spatial Memory Makes World Models Efficient -- Key
+ *      Contributions 3; Methodology, Step 6] [Light Interaction -- abstract];
+ *   2. a router: mean-pooled Q and K per block, a score for every
+ *      (query block, KV block) pair, an optional soft geometric bias with
+ *      unbiased fallback, and a top-K list per (head, query block)
+ *      [Velox -- Key Contributions 1-2; Methodology, Steps 4-5];
+ *   3. attention that visits only the listed KV blocks with an online
+ *      softmax, and the dense case through the same kernel
+ *      [Velox -- Methodology, Step 6; Main Findings].
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Every function returns an int status (BSA_OK on success).  Arguments are
+ *   validated on the host, synchronously, before anything is enqueued; on
+ *   error nothing is enqueued and bsa_last_error_detail() describes the
+ *   problem.  Kernel launch failures return BSA_EHIP.  Execution is
+ *   asynchronous on the caller's stream; no entry point synchronises the
+ *   host.
+ * - Every data pointer is caller-owned DEVICE memory unless stated
+ *   otherwise.  The library never allocates or frees; scratch memory is a
+ *   caller buffer sized by the matching *_workspace_size function.  The
+ *   library holds no mutable global state and is safe to call from several
+ *   threads on different streams.
+ * - Tensor pointers must be 16-byte aligned and head strides must keep every
+ *   row 16-byte aligned.
+ * - Results are deterministic: identical inputs give bitwise identical
+ *   outputs (no atomics).
+ * - dtype is BSA_BF16 (bfloat16 storage, fp32 accumulation) or BSA_F32.
+ * - d (head dim) and block (tokens per block) are 64 or 128.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define BSA_OK 0
+#define BSA_EINVAL 1        /* null, negative or inconsistent arguments */
+#define BSA_EUNSUPPORTED 2  /* d, block or dtype outside what the kernels build for */
+#define BSA_EWORKSPACE 3    /* workspace missing or too small */
+#define BSA_EHIP 4          /* a HIP launch or runtime call failed */
+
+/* dtypes */
+#define BSA_BF16 0
+#define BSA_F32 1
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int bsa_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* bsa_strerror(int status);
+
+/* Detail of the last error reported on the calling thread (never NULL;
+ * empty after a successful call). */
+const char* bsa_last_error_detail(void);
+
+/*
+ * bsa_gilbert_index -- generalized-Hilbert order of a T x H x W grid.
+ * [Velox -- Key Contributions 3 ("global-aligned Gilbert KV storage");
+ *  Methodology, Step 6 (neighbouring regions contiguous in memory)]
+ *
+ * perm[i] (int32, T*H*W entries) receives the raster index t*H*W + h*W + w of
+ * the i-th cell on the curve; inv (nullable, T*H*W entries) receives the
+ * inverse, inv[perm[i]] = i.  The curve starts at (0,0,0) and travels along
+ * the longest axis (ties: w, then h); it takes unit steps whenever the
+ * grid's parity allows a corner-to-corner path.  One thread per index
+ * descends the curve's recursive subdivision.
+ * Errors: BSA_EINVAL if a dimension is < 1, T*H*W exceeds 2^31-1, or perm is
+ * NULL.
+ */
+int bsa_gilbert_index(int T, int H, int W, int32_t* perm, int32_t* inv, hipStream_t stream);
+
+/*
+ * bsa_gilbert_perm -- permute one chunk between raster token-major layout
+ * and Gilbert-ordered, head-major, block-padded layout.
+ * [Velox -- Key Contributions 3; Methodology, Step 6]
+ *
+ * Raster layout: element (token t, head h, channel c) at
+ *   raster[t * raster_token_stride + h * d + c],   t < L.
+ * Gilbert layout: element (head h, row i, channel c) at
+ *   gil[h * gilbert_head_stride + i * d + c],      i < n_blocks * block,
+ * with n_blocks = ceil(L / block).
+ * inverse = 0: src is raster, dst is Gilbert; gil row i < L takes raster
+ *   token perm[i]; rows L .. n_blocks*block-1 are written as zeros.
+ * inverse = 1: src is Gilbert, dst is raster; raster token perm[i] takes
+ *   gil row i (padded rows are not read).
+ * The copy is bitwise.  dst may be a slice of a larger KV store (set
+ * gilbert_head_stride to the store's head stride).  src and dst must not
+ * overlap.  perm is device int32[L] (a permutation of 0..L-1).
+ * Errors: BSA_EINVAL (null pointers, L < 1, heads < 1, strides too small,
+ * misalignment), BSA_EUNSUPPORTED (d, block or dtype).
+ */
+int bsa_gilbert_perm(const void* src, void* dst, const int32_t* perm, int L, int heads, int d,
+                     int block, int64_t raster_token_stride, int64_t gilbert_head_stride,
+                     int inverse, int dtype, hipStream_t stream);
+
+/*
+ * Router arguments.  Set struct_size = sizeof(bsa_route_args).
+ * [Velox -- Methodology, Step 4 (importance from mean query and mean key
+ *  vectors; overlap above tau rescaled and applied as (1 + lambda * g_hat),
+ *  then renormalised; at most a 1 + lambda boost); Key Contributions 2
+ *  (uncovered regions keep the model-derived route); Methodology, Step 5
+ *  (top-scoring blocks up to a budget)]
+ *
+ * Inputs (device unless noted):
+ *  q, k           [heads][rows][d] in dtype, rows contiguous; q rows =
+ *                 nqb*block, k rows = nkb*block; head strides in elements.
+ *  q_block_len    int32[nqb] valid tokens per query block (NULL: all full).
+ *  kv_block_len   int32[nkb] valid tokens per KV block (NULL: all full).
+ *                 Padded rows must be finite; they are never read by the
+ *                 pooling.
+ *  scale          score scale (normally 1/sqrt(d)).
+ *  overlap        float32[nqb][overlap_row_stride] (NULL: no bias); entry
+ *                 (i, j) is the geometric overlap of query block i with
+ *                 candidate KV block j, shared by all heads.
+ *  lambda, g_ref, tau   fusion constants (g_ref > 0).
+ *  k_fixed        budget of every row, used when k_per_row is NULL.
+ *  k_per_row      int32[heads*nqb] per-row budgets (NULL: k_fixed); values
+ *                 are clamped to [0, k_max].
+ *  k_max          upper bound of the per-row budgets (sizes col_idx).
+ *  n_dense_tail_blocks  the last n_dense_tail_blocks KV blocks are not
+ *                 candidates; every non-empty list ends with those of them
+ *                 that hold a valid token (the current chunk, attended
+ *                 densely).  Candidates are blocks 0 .. nkb-n_dense_tail-1.
+ *  kpool          float64[heads][n_candidates][d] pooled-key cache (NULL:
+ *                 pool every candidate into the workspace).  Blocks
+ *                 < kpool_valid_blocks are taken from the cache as they
+ *                 are; blocks >= kpool_valid_blocks are pooled and written
+ *                 into it.
+ * Outputs (device):
+ *  row_ptr        int32[heads*nqb + 1]; row r = h*nqb + i.
+ *  col_idx        int32[col_capacity]; row r's list is col_idx[row_ptr[r] ..
+ *                 row_ptr[r+1]-1], ascending block indices.
+ *  fallback_counts int32[2] (nullable): [0] query blocks whose overlap row is
+ *                 all zero (unbiased fallback), [1] query blocks with no
+ *                 overlap above tau (includes [0]).  Both 0 without overlap.
+ *  sel_keys       float64[heads][nqb][n_candidates] (nullable): the
+ *                 selection keys kappa = s + log1p(lambda * g_hat).
+ *
+ * Semantics: qbar, kbar = means over valid rows in float64 (exact sums);
+ * s_ij = (qbar_i . kbar_j) * scale in float64; g_hat = 0 if g <= tau else
+ * min(1, g / g_ref); the fused importance softmax(s)_j * (1 + lambda g_hat_j)
+ * renormalised has the same order within a row as kappa_ij = s_ij +
+ * log1p(lambda g_hat_ij), which is what is ranked.  A row keeps
+ * K_eff = min(K_r, candidates with a valid token) blocks: the largest kappa,
+ * ties to the lower block index; a query block with no valid token gets an
+ * empty list.
+ */
+typedef struct bsa_route_args {
+    size_t struct_size;
+    const void* q;
+    const void* k;
+    int dtype;
+    int heads;
+    int d;
+    int block;
+    int nqb;
+    int nkb;
+    int64_t q_head_stride;
+    int64_t k_head_stride;
+    const int32_t* q_block_len;
+    const int32_t* kv_block_len;
+    double scale;
+    const float* overlap;
+    int64_t overlap_row_stride;
+    double lambda;
+    double g_ref;
+    double tau;
+    int k_fixed;
+    const int32_t* k_per_row;
+    int k_max;
+    int n_dense_tail_blocks;
+    double* kpool;
+    int kpool_valid_blocks;
+    int32_t* row_ptr;
+    int32_t* col_idx;
+    int64_t col_capacity;
+    int32_t* fallback_counts;
+    double* sel_keys;
+} bsa_route_args;
+
+/* Bytes of workspace bsa_route_topk needs for these arguments (0 if the
+ * arguments are invalid). */
+size_t bsa_route_workspace_size(const bsa_route_args* args);
+
+/*
+ * bsa_route_topk -- pool, score, fuse and select; see bsa_route_args.
+ * workspace: device memory of at least bsa_route_workspace_size(args) bytes,
+ * 256-byte aligned, owned by the caller, not read before it is written.
+ * Errors: BSA_EINVAL (arguments; col_capacity below
+ * heads*nqb*(min(k cap, candidates) + n_dense_tail_blocks)),
+ * BSA_EUNSUPPORTED, BSA_EWORKSPACE.
+ */
+int bsa_route_topk(const bsa_route_args* args, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/*
+ * bsa_block_sparse_attn -- attention of every query block over its listed
+ * KV blocks.
+ * [Velox -- Methodology, Step 6: an indexed block-sparse kernel, not a dense
+ *  call with a mask; a skipped block costs neither its QK^T tile nor its KV
+ *  load; the block size is the attention tile] [Light Interaction --
+ *  abstract: 3-D block-sparse attention]
+ *
+ *  q              [heads][nqb*block][d], head stride q_head_stride.
+ *  k, v           [heads][nkb*block][d], head strides k/v_head_stride.
+ *  o              [heads][nqb*block][d] output in dtype, head stride
+ *                 o_head_stride.
+ *  lse            float32[heads][nqb*block] (nullable): natural-log
+ *                 log-sum-exp of the scaled scores per query row.
+ *  q_block_len, kv_block_len  as for the router (NULL: all full).
+ *  row_ptr        int32[heads*nqb + 1], col_idx int32[col_len]: the lists
+ *                 (row r = h*nqb + i).  Entries outside [0, nkb) and ranges
+ *                 outside [0, col_len) are ignored.
+ *  scale          score scale (normally 1/sqrt(d)).
+ * For each head h and valid query row t of block i:
+ *   O = sum_u softmax_u(scale * q_t . k_u) v_u over the valid keys u of the
+ *   listed blocks (no causal mask).  Padded query rows are written as 0 (LSE
+ *   -inf); an empty list gives O = 0, LSE = -inf.  bf16: QK^T and PV are bf16
+ *   MFMA products with fp32 accumulation and an fp32 online softmax; P is
+ *   rounded to bf16 before the PV product; O is rounded to bf16 once.
+ * Errors: BSA_EINVAL, BSA_EUNSUPPORTED.
+ */
+int bsa_block_sparse_attn(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int dtype, int heads, int d, int block, int nqb, int nkb,
+                          int64_t q_head_stride, int64_t k_head_stride, int64_t v_head_stride,
+                          int64_t o_head_stride, const int32_t* q_block_len,
+                          const int32_t* kv_block_len, const int32_t* row_ptr,
+                          const int32_t* col_idx, int64_t col_len, float scale,
+                          hipStream_t stream);
+
+/*
+ * bsa_dense_attn -- the dense baseline: bsa_block_sparse_attn with every KV
+ * block listed in ascending order, through the same kernel.
+ * [Velox -- Main Findings: dense attention over all retained context]
+ */
+int bsa_dense_attn(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
+                   int heads, int d, int block, int nqb, int nkb, int64_t q_head_stride,
+                   int64_t k_head_stride, int64_t v_head_stride, int64_t o_head_stride,
+                   const int32_t* q_block_len, const int32_t* kv_block_len, float scale,
+                   hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

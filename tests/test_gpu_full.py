@@ -1,0 +1,102 @@
+"""Full-size parity in the benchmark's launch configuration: C4 at chunk 48
+(the headline workload) and C5 (48 ragged chunks), checked on sampled heads
+(every route of those heads bit-exact) and sampled query rows (attention),
+plus size-independent properties on every head."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import attention as oatt
+from oracle import layout as olay
+from oracle import route as oroute
+from oracle.gilbert import gilbert_order
+
+from helpers import BF16_MAX_ABS, BF16_MEAN_ABS, assert_lists_equal, csr_lists, f64, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE_HEADS = [0, 17, 39]
+
+
+def _sample_rows(rng, q_len, bs, n=48):
+    valid = np.concatenate([np.arange(i * bs, i * bs + int(n_)) for i, n_ in enumerate(q_len)])
+    pick = rng.choice(valid, size=n, replace=False)
+    last = (len(q_len) - 1) * bs + int(q_len[-1]) - 1
+    return np.unique(np.concatenate([pick, [0, last]]))
+
+
+def test_c4_chunk48_bench_configuration():
+    dev = need_gpu()
+    import bench
+    st = bench.setup_c4(48, device=dev)
+    w, ra = st["w"], st["ra"]
+    slot_before = ra.slot(st["cur"])[0].clone()
+    o_raster, r = bench.run_step(st)
+    torch.cuda.synchronize()
+    print("C4 chunk 48: step ran", flush=True)
+    assert torch.equal(slot_before, ra.slot(st["cur"])[0])
+    perm = gilbert_order(3, 30, 52)[0]
+    assert np.array_equal(ra.perm.cpu().numpy(), perm)
+    lists = csr_lists(r["row_ptr"], r["col_idx"], w.heads, w.nqb)
+    # every row: 50 distinct ascending in-range blocks
+    for h in range(w.heads):
+        for l in lists[h]:
+            assert len(l) == 50 and np.all(np.diff(l) > 0) and l[0] >= 0 and l[-1] < w.nkb
+    # padded query rows of the Gilbert-layout output are zero
+    assert torch.all(ra.o_blk[:, 36 * 128 + 72:, :] == 0)
+    rng = np.random.default_rng(48)
+    for h in SAMPLE_HEADS:
+        q, k, v = f64(w.q[h]), f64(w.k[h]), f64(w.v[h])
+        ref = oroute.route_head(q, k, w.q_len, w.k_len, w.bs, scale=w.scale, k_per_row=w.k_per_row[:w.nqb])
+        assert_lists_equal(lists[h], ref["lists"], "C4 c=48 head %d" % h)
+        rows = _sample_rows(rng, w.q_len, w.bs)
+        o_ref, _ = oatt.block_sparse_head(q, k, v, w.q_len, w.k_len, w.bs, ref["lists"], w.scale, rows=rows)
+        o_gpu = f64(o_raster[:, h, :])[perm[rows]]      # Gilbert row i is raster token perm[i]
+        err = np.abs(o_gpu - o_ref[rows])
+        print("head", h, "max", err.max(), "mean", err.mean(), flush=True)
+        assert err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS
+
+
+def test_c5_ragged_full():
+    dev = need_gpu()
+    from block_sparse_attention_gilbert_amd.pipeline import RoutedAttention
+    w = workloads.c5()
+    n_chunks = 48
+    ra = RoutedAttention(w.grid, w.heads, w.d, w.bs, n_chunks, device=dev, k_cap=143, n_dense_tail_chunks=1)
+    for c in range(n_chunks - 1):
+        ra.append(w.k_raster[c].to(dev), w.v_raster[c].to(dev), c)
+    kpr = torch.from_numpy(w.k_per_row).to(dev)
+    o_raster, r = ra.step(w.q_raster.to(dev), w.k_raster[-1].to(dev), w.v_raster[-1].to(dev), n_chunks - 1,
+                          k_per_row=kpr)
+    torch.cuda.synchronize()
+    print("C5: step ran", flush=True)
+    T, H, W = w.grid
+    L = T * H * W
+    perm = gilbert_order(T, H, W)[0]
+    ql = olay.chunk_block_lengths(L, w.bs)
+    kl = olay.chunk_block_lengths(L, w.bs, n_chunks)
+    nbc = len(ql)
+    lists = csr_lists(r["row_ptr"], r["col_idx"], w.heads, nbc)
+    for h in range(w.heads):
+        for i, l in enumerate(lists[h]):
+            kr = int(w.k_per_row[h * nbc + i])
+            assert len(l) == kr + nbc and np.all(np.diff(l) > 0)
+            assert np.array_equal(l[kr:], np.arange((n_chunks - 1) * nbc, n_chunks * nbc))
+    rng = np.random.default_rng(5)
+    for h in SAMPLE_HEADS:
+        q = olay.permute_forward(f64(w.q_raster[:, h:h + 1]), perm, w.bs)[0]
+        k = np.concatenate([olay.permute_forward(f64(w.k_raster[c][:, h:h + 1]), perm, w.bs)[0]
+                            for c in range(n_chunks)])
+        v = np.concatenate([olay.permute_forward(f64(w.v_raster[c][:, h:h + 1]), perm, w.bs)[0]
+                            for c in range(n_chunks)])
+        ref = oroute.route_head(q, k, ql, kl, w.bs, scale=w.scale, k_per_row=w.k_per_row[h * nbc:(h + 1) * nbc],
+                                n_dense_tail=nbc)
+        assert_lists_equal(lists[h], ref["lists"], "C5 head %d" % h)
+        rows = _sample_rows(rng, ql, w.bs)
+        o_ref, _ = oatt.block_sparse_head(q, k, v, ql, kl, w.bs, ref["lists"], w.scale, rows=rows)
+        o_gpu = f64(o_raster[:, h, :])[perm[rows]]
+        err = np.abs(o_gpu - o_ref[rows])
+        print("C5 head", h, "max", err.max(), "mean", err.mean(), flush=True)
+        assert err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS

@@ -1,0 +1,72 @@
+"""GPU parity of the Gilbert order (bit-exact against the oracle's
+enumeration) and of the raster <-> Gilbert permutation (bitwise)."""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import layout as olay
+from oracle.gilbert import gilbert_order
+
+from helpers import f64, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def test_index_config_shapes():
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    for shape in [(3, 30, 52), (1, 30, 52), (21, 30, 52), (3, 60, 104), (1, 1, 1), (1, 1, 37), (2, 2, 2)]:
+        perm, inv = bsa.gilbert_index(*shape, device=dev)
+        ref, ref_inv = gilbert_order(*shape)
+        assert np.array_equal(perm.cpu().numpy(), ref), shape
+        assert np.array_equal(inv.cpu().numpy(), ref_inv), shape
+
+
+def test_index_small_shape_sweep():
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    for shape in itertools.product(range(1, 7), repeat=3):
+        perm, _ = bsa.gilbert_index(*shape, device=dev, with_inverse=False)
+        assert np.array_equal(perm.cpu().numpy(), gilbert_order(*shape)[0]), shape
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("block,d", [(128, 128), (64, 128), (64, 64), (128, 64)])
+def test_permute_bitwise(dtype, block, d):
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    T, H, W = 3, 30, 52
+    L, heads = T * H * W, 3
+    g = torch.Generator().manual_seed(11)
+    src = torch.randn((L, heads, d), generator=g).to(dtype)
+    perm, _ = bsa.gilbert_index(T, H, W, device=dev)
+    dst = bsa.gilbert_perm(src.to(dev), perm, block=block)
+    ref = olay.permute_forward(f64(src), gilbert_order(T, H, W)[0], block)
+    assert np.array_equal(f64(dst), ref)              # bitwise (values exact in float64)
+    assert torch.all(dst[:, L:, :] == 0)
+    back = bsa.gilbert_perm(dst, perm, block=block, inverse=True)
+    assert torch.equal(back.cpu(), src)
+
+
+def test_permute_into_store_slot_and_token_stride():
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    T, H, W = 3, 30, 52
+    L, heads, d, block = T * H * W, 4, 128, 128
+    nbc = -(-L // block)
+    # raster rows carry q, k, v side by side: token stride 3*heads*d
+    fused = torch.randn((L, 3, heads, d), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).to(dev)
+    k_raster = fused[:, 1]
+    store = torch.full((heads, 3 * nbc * block, d), 7.0, dtype=torch.bfloat16, device=dev)
+    perm, _ = bsa.gilbert_index(T, H, W, device=dev)
+    slot = store[:, nbc * block: 2 * nbc * block]
+    bsa.gilbert_perm(k_raster, perm, block=block, dst=slot)
+    ref = olay.permute_forward(f64(k_raster), gilbert_order(T, H, W)[0], block)
+    assert np.array_equal(f64(slot), ref)
+    assert torch.all(store[:, : nbc * block] == 7.0) and torch.all(store[:, 2 * nbc * block:] == 7.0)
+    out = torch.zeros((L, 2, heads, d), dtype=torch.bfloat16, device=dev)
+    bsa.gilbert_perm(slot, perm, block=block, inverse=True, dst=out[:, 1])
+    assert torch.equal(out[:, 1], k_raster) and torch.all(out[:, 0] == 0)

@@ -1,0 +1,150 @@
+"""GPU parity of the router: CSR lists bit-exact against the oracle on the
+configurations (C1-C5 at sizes the oracle finishes in seconds), fallback
+counts, selection keys, the pooled-key cache, and edge cases."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import layout as olay
+from oracle import route as oroute
+from oracle.gilbert import gilbert_order
+
+from helpers import assert_lists_equal, csr_lists, f64, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_route(w, dev, **kw):
+    import block_sparse_attention_gilbert_amd as bsa
+    q, k = w.q.to(dev), w.k.to(dev)
+    ql = torch.from_numpy(w.q_len.astype(np.int32)).to(dev)
+    kl = torch.from_numpy(w.k_len.astype(np.int32)).to(dev)
+    ov = None if w.overlap is None else torch.from_numpy(w.overlap).to(dev)
+    r = bsa.route_topk(q, k, block=w.bs, nqb=w.nqb, nkb=w.nkb, scale=w.scale, q_block_len=ql, kv_block_len=kl,
+                       overlap=ov, lam=w.lam, g_ref=w.g_ref, tau=w.tau, k_fixed=int(w.k_per_row[0]),
+                       n_dense_tail_blocks=w.n_dense_tail, **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def _oracle_head(w, h, **kw):
+    q, k = f64(w.q[h]), f64(w.k[h])
+    return oroute.route_head(q, k, w.q_len, w.k_len, w.bs, scale=w.scale,
+                             k_per_row=w.k_per_row[h * w.nqb:(h + 1) * w.nqb], overlap=w.overlap,
+                             lam=w.lam, tau=w.tau, g_ref=w.g_ref, n_dense_tail=w.n_dense_tail, **kw)
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3"])
+def test_routes_bit_exact(name):
+    dev = need_gpu()
+    w = workloads.get(name)
+    r = _gpu_route(w, dev, want_keys=True)
+    got = csr_lists(r["row_ptr"], r["col_idx"], w.heads, w.nqb)
+    keys = r["sel_keys"].cpu().numpy()
+    for h in range(w.heads):
+        ref = _oracle_head(w, h)
+        assert_lists_equal(got[h], ref["lists"], "%s head %d" % (name, h))
+        # selection keys agree with the oracle's kappa to rounding
+        kap = ref["kappa"]
+        assert np.max(np.abs(keys[h] - kap)) <= 1e-12 * max(1.0, np.max(np.abs(kap)))
+    fb = r["fallback_counts"].cpu().numpy()
+    if w.overlap is None:
+        assert fb.tolist() == [0, 0]
+    else:
+        ref = _oracle_head(w, 0)
+        assert fb[0] == int(ref["zero_rows"].sum()) == 11
+        assert fb[1] == int(ref["unvetted_rows"].sum())
+
+
+@pytest.mark.parametrize("c", [1, 2, 5])
+def test_routes_growing_context(c):
+    dev = need_gpu()
+    w = workloads.c4(c=c, heads=[0, 7, 21, 39])
+    r = _gpu_route(w, dev)
+    got = csr_lists(r["row_ptr"], r["col_idx"], w.heads, w.nqb)
+    for h in range(w.heads):
+        ref = _oracle_head(w, h)
+        assert_lists_equal(got[h], ref["lists"], "C4 c=%d head %d" % (c, h))
+        if c == 1:  # K >= candidates: every block, i.e. dense
+            assert all(len(l) == 37 for l in got[h])
+
+
+def _c5_blocked(w, n_chunks):
+    """Gilbert-permuted C5 tensors (oracle's own permutation), per head."""
+    T, H, W = w.grid
+    L = T * H * W
+    perm, _ = gilbert_order(T, H, W)
+    q = olay.permute_forward(f64(w.q_raster), perm, w.bs)
+    k = np.concatenate([olay.permute_forward(f64(w.k_raster[c]), perm, w.bs) for c in range(n_chunks)], axis=1)
+    v = np.concatenate([olay.permute_forward(f64(w.v_raster[c]), perm, w.bs) for c in range(n_chunks)], axis=1)
+    return q, k, v, olay.chunk_block_lengths(L, w.bs), olay.chunk_block_lengths(L, w.bs, n_chunks)
+
+
+def test_routes_ragged_dense_tail():
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    from block_sparse_attention_gilbert_amd.pipeline import RoutedAttention
+    n_chunks = 4
+    w = workloads.c5(heads=[0, 1, 2], n_chunks=n_chunks)
+    ra = RoutedAttention(w.grid, w.heads, w.d, w.bs, n_chunks, device=dev, k_cap=143, n_dense_tail_chunks=1)
+    for c in range(n_chunks - 1):
+        ra.append(w.k_raster[c].to(dev), w.v_raster[c].to(dev), c)
+    kpr = torch.from_numpy(w.k_per_row).to(dev)
+    _, r = ra.step(w.q_raster.to(dev), w.k_raster[-1].to(dev), w.v_raster[-1].to(dev), n_chunks - 1,
+                   k_per_row=kpr)
+    torch.cuda.synchronize()
+    q, k, _v, ql, kl = _c5_blocked(w, n_chunks)
+    nbc = len(ql)
+    got = csr_lists(r["row_ptr"], r["col_idx"], w.heads, nbc)
+    for h in range(w.heads):
+        ref = oroute.route_head(q[h], k[h], ql, kl, w.bs, scale=w.scale,
+                                k_per_row=w.k_per_row[h * nbc:(h + 1) * nbc], n_dense_tail=nbc)
+        assert_lists_equal(got[h], ref["lists"], "C5 head %d" % h)
+    assert bsa is not None
+
+
+def test_pooled_key_cache_incremental():
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    w = workloads.c4(c=3, heads=[0, 1])
+    ql = torch.from_numpy(w.q_len).to(dev)
+    kl = torch.from_numpy(w.k_len).to(dev)
+    q, k = w.q.to(dev), w.k.to(dev)
+    cache = torch.zeros((w.heads, w.nkb, w.d), dtype=torch.float64, device=dev)
+    kw = dict(block=128, nqb=37, nkb=w.nkb, scale=w.scale, q_block_len=ql, kv_block_len=kl, k_fixed=50)
+    r_full = bsa.route_topk(q, k, kpool=cache, kpool_valid_blocks=0, **kw)   # pools every block
+    lists_full = csr_lists(r_full["row_ptr"], r_full["col_idx"], w.heads, 37)
+    cache[:, 74:] = float("nan")            # forget the newest chunk's means ...
+    r_inc = bsa.route_topk(q, k, kpool=cache, kpool_valid_blocks=74, **kw)  # ... and pool only it
+    lists_inc = csr_lists(r_inc["row_ptr"], r_inc["col_idx"], w.heads, 37)
+    for h in range(w.heads):
+        assert_lists_equal(lists_inc[h], lists_full[h], "incremental head %d" % h)
+        ref = _oracle_head(w, h)
+        assert_lists_equal(lists_inc[h], ref["lists"], "cache head %d" % h)
+        assert np.array_equal(cache[h].cpu().numpy(), ref["kbar"])   # exact block means
+
+
+def test_route_edge_cases():
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    rng = np.random.default_rng(5)
+    heads, d, bs, nqb, nkb = 2, 64, 64, 3, 12
+    q = torch.from_numpy(rng.standard_normal((heads, nqb * bs, d)).astype(np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy(rng.standard_normal((heads, nkb * bs, d)).astype(np.float32)).to(torch.bfloat16)
+    k[:, 9 * bs:10 * bs] = k[:, 4 * bs:5 * bs]            # duplicate block -> exact tie
+    q_len = np.array([bs, 0, 17], dtype=np.int32)         # an empty query block, a ragged one
+    k_len = np.array([bs] * 6 + [0] + [bs] * 3 + [5, bs], dtype=np.int32)  # an empty KV block
+    k[:, 6 * bs:7 * bs] = 1.0e4                           # junk in the empty block's rows
+    for K, tail in [(0, 0), (3, 0), (4, 2), (50, 0), (5, 2)]:
+        r = bsa.route_topk(q.to(dev), k.to(dev), block=bs, nqb=nqb, nkb=nkb, scale=0.125,
+                           q_block_len=torch.from_numpy(q_len).to(dev), kv_block_len=torch.from_numpy(k_len).to(dev),
+                           k_fixed=K, n_dense_tail_blocks=tail)
+        got = csr_lists(r["row_ptr"], r["col_idx"], heads, nqb)
+        for h in range(heads):
+            ref = oroute.route_head(f64(q[h]), f64(k[h]), q_len, k_len, bs, scale=0.125,
+                                    k_per_row=[K] * nqb, n_dense_tail=tail)
+            assert_lists_equal(got[h], ref["lists"], "K=%d tail=%d head %d" % (K, tail, h))
+            assert len(got[h][1]) == 0
+            assert all(6 not in l.tolist() for l in got[h])
