@@ -157,7 +157,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--chunk", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--dense", action="store_true", help="also time dense attention at the same chunk")
     ap.add_argument("--sweep", default=None, help="write a chunk 1..C sparse/dense sweep to this JSONL file")
     args = ap.parse_args()

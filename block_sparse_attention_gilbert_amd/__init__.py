@@ -123,7 +123,7 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 def _need_gpu(*ts):
     for t in ts:
-        if t is not None and not t.is_cuda:
+        if isinstance(t, torch.Tensor) and not t.is_cuda:
             raise ValueError("tensors must be on a GPU device")
 
 
