@@ -77,20 +77,64 @@ __device__ __forceinline__ int key_of_row(int m) {
     return 16 * (g >> 1) + 8 * hh + 4 * (g & 1) + ii;
 }
 
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+
+// LDS tile layout: rows of D bf16 (no padding), 16-byte chunks XOR-swizzled
+// by row so that the 32 rows an MFMA operand read touches fall in distinct
+// banks.  Byte offset of (row, 16-byte chunk c) inside a tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int c) {
+    constexpr int CPR = D / 8;  // chunks per row
+    return row * (D * 2) + ((c ^ (row & (CPR - 1))) << 4);
+}
+
+// Direct global -> LDS copy of one BLK x D bf16 tile into the swizzled
+// layout.  One 16-byte load per lane lands at lds_base + 16 * lane, so lane
+// l of wave-instruction I fills row r = I * RPI + l / CPR, physical chunk
+// l % CPR, and fetches the logical chunk that belongs there.
+template <int BLK, int D, int NW>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ g, uint16_t* lds_tile, int wave, int lane) {
+    constexpr int CPR = D / 8;
+    constexpr int RPI = 64 / CPR;                  // rows per wave-instruction (1 KB)
+    constexpr int NI = BLK * D * 2 / 1024 / NW;    // instructions per wave
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+        const int I = n * NW + wave;
+        const int row = I * RPI + lane / CPR;
+        const int pc = lane % CPR;
+        const int c = pc ^ (row & (CPR - 1));
+        const uint16_t* src = g + row * D + c * 8;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                         (__attribute__((address_space(3))) void*)((lds_u16_t*)lds_tile + I * 512),
+                                         16, 0, 0);
+    }
+}
+
+// Transposing LDS read of V: in each 16-lane group, lane i returns
+// V[kb + j][dv0 + i] for j = 0..3 (four consecutive keys of one channel);
+// lane a = 4j + r of the group addresses V[kb + j][dv0 + 4r .. 4r+3].
+template <int D>
+__device__ __forceinline__ s16x4_t v_tr_read(const uint16_t* v_tile, int kb, int dv0, int i) {
+    const int j = i >> 2, r = i & 3;
+    const int row = kb + j;
+    const int col = dv0 + 4 * r;  // 4-element piece: chunk col/8, half (col/4)%2
+    const int off = tile_off<D>(row, col >> 3) + ((col >> 2) & 1) * 8;
+    lds_s16x4_t* p = (lds_s16x4_t*)((__attribute__((address_space(3))) char*)v_tile + off);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+}
 
 template <int BLK, int D, bool DENSE>
 __global__ void __launch_bounds__(BLK * 2) attn_bf16_kernel(AttnArgs a) {
-    constexpr int NT = BLK * 2;  // BLK/32 waves of 64
-    constexpr int KS = D + 8;    // LDS row stride of K (elements)
-    constexpr int VS = BLK + 8;  // LDS row stride of V^T (elements)
+    constexpr int NW = BLK / 32;           // waves; each owns 32 query rows
     constexpr int KT = BLK / 32, DT = D / 32, KK = D / 16;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[BLK * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+    constexpr int TILE = BLK * D;          // elements per K or V tile
+    // two stages of (K tile, V tile)
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int hi = lane >> 5, l32 = lane & 31;
+    const int hi = lane >> 5, l32 = lane & 31, g16 = lane & 15;
     int h, i;
     map_item(a.heads * a.nqb, a.nqb, h, i);
     int vq = a.q_len ? a.q_len[i] : BLK;
@@ -101,6 +145,36 @@ __global__ void __launch_bounds__(BLK * 2) attn_bf16_kernel(AttnArgs a) {
     const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + h * a.q_hs + (int64_t)i * BLK * D;
     const uint16_t* Kh = static_cast<const uint16_t*>(a.k) + h * a.k_hs;
     const uint16_t* Vh = static_cast<const uint16_t*>(a.v) + h * a.v_hs;
+
+    int e0, e1;
+    if (DENSE) {
+        e0 = 0;
+        e1 = a.nkb;
+    } else {
+        const int row = h * a.nqb + i;
+        e0 = a.row_ptr[row];
+        e1 = a.row_ptr[row + 1];
+        e0 = e0 < 0 ? 0 : e0;
+        e1 = e1 > a.col_len ? (int)a.col_len : e1;
+    }
+    // next listed block at or after e with at least one valid key, or -1
+    auto next_valid = [&](int& e, int& j, int& vk) {
+        for (; e < e1; ++e) {
+            j = DENSE ? e : a.col_idx[e];
+            if (j < 0 || j >= a.nkb) continue;
+            vk = a.kv_len ? a.kv_len[j] : BLK;
+            vk = vk > BLK ? BLK : vk;
+            if (vk > 0) return true;
+        }
+        return false;
+    };
+
+    int e = e0, j = 0, vk = 0;
+    bool have = next_valid(e, j, vk);
+    if (have) {
+        dma_tile<BLK, D, NW>(Kh + (int64_t)j * TILE, lds, wave, lane);
+        dma_tile<BLK, D, NW>(Vh + (int64_t)j * TILE, lds + TILE, wave, lane);
+    }
 
     bf16x8_t qf[KK];
     {
@@ -114,128 +188,98 @@ __global__ void __launch_bounds__(BLK * 2) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
     float m = -INFINITY, l = 0.f;
-
-    int e0, e1;
-    if (DENSE) {
-        e0 = 0;
-        e1 = a.nkb;
-    } else {
-        const int row = h * a.nqb + i;
-        e0 = a.row_ptr[row];
-        e1 = a.row_ptr[row + 1];
-        e0 = e0 < 0 ? 0 : e0;
-        e1 = e1 > a.col_len ? (int)a.col_len : e1;
-    }
     const int kr = key_of_row(l32);
+    int stage = 0;
 
-    for (int e = e0; e < e1; ++e) {
-        const int j = DENSE ? e : a.col_idx[e];
-        if (j < 0 || j >= a.nkb) continue;
-        int vk = a.kv_len ? a.kv_len[j] : BLK;
-        vk = vk > BLK ? BLK : vk;
-        if (vk <= 0) continue;
+    while (have) {
+        // this stage's tile has landed (every wave waited on its own copies)
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        {
-            const uint16_t* Kb = Kh + (int64_t)j * BLK * D;
+        const int vk_cur = vk;
+        int en = e + 1, jn = 0, vkn = 0;
+        const bool have_next = next_valid(en, jn, vkn);
+        if (have_next) {
+            uint16_t* nxt = lds + (stage ^ 1) * 2 * TILE;
+            dma_tile<BLK, D, NW>(Kh + (int64_t)jn * TILE, nxt, wave, lane);
+            dma_tile<BLK, D, NW>(Vh + (int64_t)jn * TILE, nxt + TILE, wave, lane);
+        }
+        const uint16_t* Kt = lds + stage * 2 * TILE;
+        const uint16_t* Vt = Kt + TILE;
+
+        if (active) {
+            // S^T = K Q^T: lane holds scores of query q0 + l32 for keys
+            // mt*32 + 16*(r/8) + 8*hi + (r%8), r = 0..15.
+            f32x16_t s[KT];
 #pragma unroll
-            for (int x = tid; x < BLK * D / 8; x += NT) {
-                const int row = x / (D / 8), ch = x % (D / 8);
-                *reinterpret_cast<uint4*>(Ks + row * KS + ch * 8) =
-                    *reinterpret_cast<const uint4*>(Kb + (int64_t)row * D + ch * 8);
-            }
-            const uint16_t* Vb = Vh + (int64_t)j * BLK * D;
+            for (int mt = 0; mt < KT; ++mt) {
 #pragma unroll
-            for (int sb = tid; sb < (BLK / 8) * (D / 8); sb += NT) {
-                const int kg = sb / (D / 8), ch = sb % (D / 8);
-                uint4 in[8];
+                for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
+                const int key = mt * 32 + kr;
 #pragma unroll
-                for (int rr = 0; rr < 8; ++rr)
-                    in[rr] = *reinterpret_cast<const uint4*>(Vb + (int64_t)(kg * 8 + rr) * D + ch * 8);
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    uint32_t w[8];
-#pragma unroll
-                    for (int rr = 0; rr < 8; ++rr) {
-                        const uint4 u = in[rr];
-                        const uint32_t dw = (c >> 1) == 0 ? u.x : (c >> 1) == 1 ? u.y : (c >> 1) == 2 ? u.z : u.w;
-                        w[rr] = dw;
-                    }
-                    uint4 out;
-                    if (c & 1) {
-                        out.x = hi_pair(w[0], w[1]);
-                        out.y = hi_pair(w[2], w[3]);
-                        out.z = hi_pair(w[4], w[5]);
-                        out.w = hi_pair(w[6], w[7]);
-                    } else {
-                        out.x = lo_pair(w[0], w[1]);
-                        out.y = lo_pair(w[2], w[3]);
-                        out.z = lo_pair(w[4], w[5]);
-                        out.w = lo_pair(w[6], w[7]);
-                    }
-                    *reinterpret_cast<uint4*>(Vt + (ch * 8 + c) * VS + kg * 8) = out;
+                for (int kk = 0; kk < KK; ++kk) {
+                    const bf16x8_t kf = __builtin_bit_cast(
+                        bf16x8_t, *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Kt) +
+                                                                   tile_off<D>(key, 2 * kk + hi)));
+                    s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[mt], 0, 0, 0);
                 }
             }
-        }
-        __syncthreads();
-        if (!active) continue;
-
-        // S^T = K Q^T: lane holds scores of query q0 + l32 for keys
-        // mt*32 + 16*(r/8) + 8*hi + (r%8), r = 0..15.
-        f32x16_t s[KT];
+            if (vk_cur < BLK) {
 #pragma unroll
-        for (int mt = 0; mt < KT; ++mt) {
+                for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-            const uint16_t* krow = Ks + (mt * 32 + kr) * KS + 8 * hi;
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = mt * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
+                        if (key >= vk_cur) s[mt][r] = -INFINITY;
+                    }
+            }
+            float mx = -INFINITY;
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_bf16x8(krow + 16 * kk), qf[kk], s[mt], 0, 0, 0);
-        }
-        if (vk < BLK) {
+            for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mn = fmaxf(m, mx * a.scale_log2);
+            const float alpha = exp2f(m - mn);
+            m = mn;
+            float ls = 0.f;
+            bf16x8_t pf[KT][2];
 #pragma unroll
             for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = mt * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
-                    if (key >= vk) s[mt][r] = -INFINITY;
+                    const float p = exp2f(fmaf(s[mt][r], a.scale_log2, -mn));
+                    ls += p;
+                    pf[mt][r >> 3][r & 7] = (__bf16)p;
                 }
-        }
-        float mx = -INFINITY;
+            l = l * alpha + ls;
 #pragma unroll
-        for (int mt = 0; mt < KT; ++mt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m, mx * a.scale_log2);
-        const float alpha = exp2f(m - mn);
-        m = mn;
-        float ls = 0.f;
-        bf16x8_t pf[KT][2];
-#pragma unroll
-        for (int mt = 0; mt < KT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = exp2f(fmaf(s[mt][r], a.scale_log2, -mn));
-                ls += p;
-                pf[mt][r >> 3][r & 7] = (__bf16)p;
-            }
-        l = l * alpha + ls;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
 
-        // O^T += V^T P^T: lane holds O^T for dv = dt*32 + 8*(r/4) + 4*hi + r%4.
+            // O^T += V^T P^T: A = V^T fragment (8 consecutive keys of channel
+            // dt*32 + l32) from two transposing reads; B = P^T from registers.
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const uint16_t* vrow = Vt + (dt * 32 + l32) * VS + 8 * hi;
+            for (int dt = 0; dt < DT; ++dt) {
+                const int dv0 = dt * 32 + 16 * ((lane >> 4) & 1);
 #pragma unroll
-            for (int mt = 0; mt < KT; ++mt)
+                for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_bf16x8(vrow + mt * 32 + 16 * s2),
-                                                                     pf[mt][s2], o[dt], 0, 0, 0);
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        const int kb = mt * 32 + 16 * s2 + 8 * hi;
+                        const s16x4_t v0 = v_tr_read<D>(Vt, kb, dv0, g16);
+                        const s16x4_t v1 = v_tr_read<D>(Vt, kb + 4, dv0, g16);
+                        const bf16x8_t vf = __builtin_bit_cast(
+                            bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[mt][s2], o[dt], 0, 0, 0);
+                    }
+            }
         }
+        stage ^= 1;
+        e = en;
+        j = jn;
+        vk = vkn;
+        have = have_next;
     }
 
     // epilogue

@@ -243,97 +243,122 @@ rowptr_kernel(int heads, int nqb, int nkb, int n_cand, int block, const int32_t*
 }
 
 // Order-preserving map of a double to an unsigned integer (larger double,
-// larger key); -0 and +0 map to the same key.
+// larger key); -0 and +0 map to the same key.  Every finite or infinite
+// double maps above 0, so 0 marks "not a candidate".
 __device__ __forceinline__ unsigned long long order_key(double v) {
     if (v == 0.0) v = 0.0;
     const long long b = __double_as_longlong(v);
     return b < 0 ? ~(unsigned long long)b : ((unsigned long long)b | 0x8000000000000000ull);
 }
 
-// "a before b" under (key descending, index ascending).
-__device__ __forceinline__ bool before(unsigned long long ka, int ia, unsigned long long kb, int ib) {
-    return ka > kb || (ka == kb && ia < ib);
-}
-
-// Per (query block, head): bitonic sort of the candidate keys in LDS, flag
-// the first K_eff, and write the flagged block indices in ascending order,
-// followed by the dense tail.  grid = (nqb, heads).
+// One wave per (head, query block) row.  Lane l holds the keys of
+// candidates j = l + 64 m (m < KPL).  A radix select over 8-bit digits
+// (most significant first, a 256-bin histogram per wave in LDS) finds the
+// K_eff-th largest key t and how many keys equal to t are needed; the row
+// then keeps every key > t and the lowest-indexed keys == t, which is the
+// total order (key descending, index ascending).  Selected indices are
+// written in ascending order with ballot prefix counts, followed by the
+// dense tail.  grid = ceil(rows / 4), 4 waves per workgroup, no barriers.
+template <int KPL>
 __global__ void __launch_bounds__(kThreads)
-topk_kernel(const double* __restrict__ keys, int nqb, int n_cand, int nkb, int log2n, int block,
+topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int nkb, int block,
             const int32_t* __restrict__ q_len, const int32_t* __restrict__ kv_len,
             const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ keff,
             int32_t* __restrict__ col_idx) {
-    __shared__ unsigned long long sk[kMaxCandidates];
-    __shared__ int si[kMaxCandidates];
-    __shared__ unsigned char flag[kMaxCandidates];
-    __shared__ int scan[kThreads];
-    const int i = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-    const int r = h * nqb + i;
+    __shared__ int hist_all[kThreads / 64][256];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = blockIdx.x * (kThreads / 64) + w;
+    if (r >= rows) return;
+    const int i = r % nqb;
     const int vq = q_len ? q_len[i] : block;
     if (vq <= 0) return;
+    int* hist = hist_all[w];
     const int start = row_ptr[r];
     const int ke = keff[r];
-    const int N = 1 << log2n;
+    const unsigned long long lt_mask = (1ull << lane) - 1ull;
     const double* row = keys + (int64_t)r * n_cand;
-    for (int x = t; x < N; x += kThreads) {
-        unsigned long long key = 0;
-        int idx = 0x7fffffff;
-        if (x < n_cand) {
-            idx = x;
-            const int v = kv_len ? kv_len[x] : block;
-            if (v > 0) {
-                key = order_key(row[x]);
-            }
-            flag[x] = 0;
+
+    unsigned long long key[KPL];
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+        const int j = lane + 64 * m;
+        key[m] = 0;
+        if (j < n_cand) {
+            const int v = kv_len ? kv_len[j] : block;
+            if (v > 0) key[m] = order_key(row[j]);
         }
-        sk[x] = key;
-        si[x] = idx;
     }
-    __syncthreads();
-    for (int k = 2; k <= N; k <<= 1) {
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-            for (int p = t; p < (N >> 1); p += kThreads) {
-                const int x = 2 * jj * (p / jj) + (p % jj);
-                const int y = x + jj;
-                const unsigned long long kx = sk[x], ky = sk[y];
-                const int ix = si[x], iy = si[y];
-                const bool up = (x & k) == 0;
-                const bool xb = before(kx, ix, ky, iy);
-                if (up != xb) {
-                    sk[x] = ky;
-                    sk[y] = kx;
-                    si[x] = iy;
-                    si[y] = ix;
+
+    unsigned long long prefix = 0, mask = 0;
+    int need = ke;
+    if (ke > 0) {
+#pragma unroll 1
+        for (int shift = 56; shift >= 0; shift -= 8) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) hist[lane * 4 + b] = 0;
+#pragma unroll
+            for (int m = 0; m < KPL; ++m)
+                if (key[m] != 0 && (key[m] & mask) == prefix) atomicAdd(&hist[(key[m] >> shift) & 255], 1);
+            // lane l owns bins 255-4l .. 252-4l (descending); find the bin
+            // where the count of keys from the top reaches `need`
+            int c[4], tot = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                c[b] = hist[255 - 4 * lane - b];
+                tot += c[b];
+            }
+            int incl = tot;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int up = __shfl_up(incl, off);
+                if (lane >= off) incl += up;
+            }
+            const unsigned long long reach = __ballot(incl >= need);
+            const int owner = __ffsll((long long)reach) - 1;
+            int digit = 0, above = 0;
+            if (lane == owner) {
+                int acc = incl - tot;  // keys in bins above this lane's first bin
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    if (acc + c[b] >= need) {
+                        digit = 255 - 4 * lane - b;
+                        above = acc;
+                        break;
+                    }
+                    acc += c[b];
                 }
             }
-            __syncthreads();
+            digit = __shfl(digit, owner);
+            above = __shfl(above, owner);
+            need -= above;
+            prefix |= (unsigned long long)digit << shift;
+            mask |= 0xFFull << shift;
         }
     }
-    for (int x = t; x < ke; x += kThreads)
-        if (si[x] < n_cand) flag[si[x]] = 1;
-    __syncthreads();
-    const int seg = (n_cand + kThreads - 1) / kThreads;
-    const int lo = t * seg < n_cand ? t * seg : n_cand;
-    const int hi = lo + seg < n_cand ? lo + seg : n_cand;
-    int cnt = 0;
-    for (int x = lo; x < hi; ++x) cnt += flag[x];
-    scan[t] = cnt;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-        const int add = t >= off ? scan[t - off] : 0;
-        __syncthreads();
-        scan[t] += add;
-        __syncthreads();
+    // ordered compaction: key > t, or key == t and among the first `need`
+    int base = start, eq_seen = 0;
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+        const bool gt = ke > 0 && key[m] > prefix;
+        const bool eq = ke > 0 && key[m] != 0 && key[m] == prefix;
+        const unsigned long long beq = __ballot(eq);
+        const int rank = eq_seen + __popcll(beq & lt_mask);
+        eq_seen += __popcll(beq);
+        const bool sel = gt || (eq && rank < need);
+        const unsigned long long bs = __ballot(sel);
+        if (sel) col_idx[base + __popcll(bs & lt_mask)] = lane + 64 * m;
+        base += __popcll(bs);
     }
-    int pos = start + scan[t] - cnt;
-    for (int x = lo; x < hi; ++x)
-        if (flag[x]) col_idx[pos++] = x;
-    if (t == 0) {
-        int p = start + ke;
-        for (int jb = n_cand; jb < nkb; ++jb) {
+    for (int j0 = n_cand; j0 < nkb; j0 += 64) {
+        const int jb = j0 + lane;
+        bool take = false;
+        if (jb < nkb) {
             const int v = kv_len ? kv_len[jb] : block;
-            if (v > 0) col_idx[p++] = jb;
+            take = v > 0;
         }
+        const unsigned long long bt = __ballot(take);
+        if (take) col_idx[base + __popcll(bt & lt_mask)] = jb;
+        base += __popcll(bt);
     }
 }
 
@@ -386,11 +411,21 @@ hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* w
     hipLaunchKernelGGL(rowptr_kernel, dim3(1), dim3(1024), 0, stream, a->heads, a->nqb, a->nkb, n_cand, a->block,
                        a->q_block_len, a->kv_block_len, a->k_per_row ? 0 : a->k_fixed, a->k_per_row,
                        a->k_max, want_flags ? flags : nullptr, a->row_ptr, keff, a->fallback_counts);
-    // 6. selection
-    int log2n = 1;
-    while ((1 << log2n) < n_cand) ++log2n;
-    hipLaunchKernelGGL(topk_kernel, dim3(a->nqb, a->heads), dim3(kThreads), 0, stream, keys, a->nqb, n_cand, a->nkb,
-                       log2n, a->block, a->q_block_len, a->kv_block_len, a->row_ptr, keff, a->col_idx);
+    // 6. selection: one wave per row
+    const int rows = a->heads * a->nqb;
+    const dim3 grid((rows + kThreads / 64 - 1) / (kThreads / 64));
+#define BSA_TOPK(KPL)                                                                                       \
+    hipLaunchKernelGGL(topk_kernel<KPL>, grid, dim3(kThreads), 0, stream, keys, rows, a->nqb, n_cand, a->nkb, \
+                       a->block, a->q_block_len, a->kv_block_len, a->row_ptr, keff, a->col_idx)
+    if (n_cand <= 64 * 8)
+        BSA_TOPK(8);
+    else if (n_cand <= 64 * 16)
+        BSA_TOPK(16);
+    else if (n_cand <= 64 * 32)
+        BSA_TOPK(32);
+    else
+        BSA_TOPK(64);
+#undef BSA_TOPK
     return hipGetLastError();
 }
 
