@@ -150,6 +150,77 @@ def read_traffic(per_launch_bytes):
     return t.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
+
+
+def profile_attention(launches: int):
+    """Counter-collection mode: set up C4 at chunk 48, route once, then run
+    ``launches`` attention launches and one plain 1 GiB device copy (the
+    calibration kernel for the byte counters).  Prints nothing but a summary
+    line; meant to run under rocprofv3 --pmc."""
+    import torch
+    st = setup_c4(48, device="cuda:0")
+    ra = st["ra"]
+    run_step(st)
+    torch.cuda.synchronize()
+    # attention only, on the routed lists of the step above
+    from block_sparse_attention_gilbert_amd import block_sparse_attn
+    nkb = ra.store_chunks * ra.nbc
+    r = ra.route_out
+    for _ in range(launches):
+        block_sparse_attn(ra.q_blk, ra.k_store[:, : nkb * ra.block], ra.v_store[:, : nkb * ra.block], r["row_ptr"],
+                          r["col_idx"], block=ra.block, scale=ra.scale, q_block_len=ra.q_len,
+                          kv_block_len=ra.kv_len[:nkb], out=ra.o_blk, lse=ra.lse)
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print("profile-attention done: %d attention launches, one %d-byte copy" % (launches, COPY_BYTES), flush=True)
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, out_path: str):
+    """Turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then WRITE_SIZE; KiB
+    per dispatch) into HBM bytes per attention launch, each counter scaled by
+    what it reads for the plain copy kernel of known size."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name", counter) != counter:
+                    continue
+                name = row["Kernel_Name"]
+                vals.setdefault(name, []).append(float(row["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(vals, key):
+        ks = [k for k in vals if key in k]
+        return [v for k in ks for v in vals[k]]
+
+    attn_f = pick(fetch, "attn_bf16_kernel")
+    attn_w = pick(write, "attn_bf16_kernel")
+    copy_f = pick(fetch, "copy")
+    copy_w = pick(write, "copy")
+    f_factor = COPY_BYTES / (max(copy_f) * 1024.0)
+    w_factor = COPY_BYTES / (max(copy_w) * 1024.0)
+    fetch_b = sum(attn_f) / len(attn_f) * 1024.0 * f_factor
+    write_b = sum(attn_w) / len(attn_w) * 1024.0 * w_factor
+    out = {"kernel": "attn_bf16_kernel<128,128,sparse>", "workload": "C4 chunk 48",
+           "attn_source_sha256_16": attn_source_hash(),
+           "fetch_kib_per_launch": sum(attn_f) / len(attn_f), "write_kib_per_launch": sum(attn_w) / len(attn_w),
+           "copy_bytes": COPY_BYTES, "copy_fetch_kib": max(copy_f), "copy_write_kib": max(copy_w),
+           "fetch_scale": f_factor, "write_scale": w_factor,
+           "hbm_bytes_per_launch": fetch_b + write_b, "fetch_bytes_per_launch": fetch_b,
+           "write_bytes_per_launch": write_b}
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,10 +228,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--chunk", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=40)
     ap.add_argument("--dense", action="store_true", help="also time dense attention at the same chunk")
     ap.add_argument("--sweep", default=None, help="write a chunk 1..C sparse/dense sweep to this JSONL file")
+    ap.add_argument("--profile-attention", type=int, default=0, metavar="N",
+                    help="counter mode: N attention launches + a 1 GiB copy, no JSON line")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
+                    help="write HBM bytes per attention launch from two rocprofv3 --pmc CSVs")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode (see the sharding notes)",
               file=sys.stderr)
@@ -168,6 +246,10 @@ def main():
 
     import torch
     import block_sparse_attention_gilbert_amd as bsa  # fails loudly if libbsa.so is missing
+
+    if args.profile_attention:
+        profile_attention(args.profile_attention)
+        return
 
     dev = "cuda:0"
     t_setup = time.perf_counter()

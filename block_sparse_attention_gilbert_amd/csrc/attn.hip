@@ -80,71 +80,139 @@ __device__ __forceinline__ int key_of_row(int m) {
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+typedef const __attribute__((address_space(4))) int32_t const_i32_t;
 
-// LDS tile layout: rows of D bf16 (no padding), 16-byte chunks XOR-swizzled
-// by row so that the 32 rows an MFMA operand read touches fall in distinct
-// banks.  Byte offset of (row, 16-byte chunk c) inside a tile.
+constexpr int kSubKeys = 64;  // keys per pipeline stage (sub-tile)
+constexpr int kStages = 4;    // LDS stages; kStages - 1 sub-tiles in flight
+constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
+
+// LDS sub-tile layout: kSubKeys rows of D bf16 (no padding), 16-byte chunks
+// XOR-swizzled by row so that the 32 rows an MFMA operand read touches fall
+// in distinct banks.  Byte offset of (row, 16-byte chunk c).
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int c) {
     constexpr int CPR = D / 8;  // chunks per row
     return row * (D * 2) + ((c ^ (row & (CPR - 1))) << 4);
 }
 
-// Direct global -> LDS copy of one BLK x D bf16 tile into the swizzled
-// layout.  One 16-byte load per lane lands at lds_base + 16 * lane, so lane
-// l of wave-instruction I fills row r = I * RPI + l / CPR, physical chunk
+// Direct global -> LDS copy of one kSubKeys x D bf16 sub-tile into the
+// swizzled layout.  One 16-byte load per lane lands at base + 16 * lane, so
+// lane l of wave-instruction I fills row I * RPI + l / CPR, physical chunk
 // l % CPR, and fetches the logical chunk that belongs there.
-template <int BLK, int D, int NW>
-__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ g, uint16_t* lds_tile, int wave, int lane) {
+template <int D, int NW>
+__device__ __forceinline__ void dma_sub(const uint16_t* __restrict__ g, uint16_t* lds_tile, int wave, int lane) {
     constexpr int CPR = D / 8;
-    constexpr int RPI = 64 / CPR;                  // rows per wave-instruction (1 KB)
-    constexpr int NI = BLK * D * 2 / 1024 / NW;    // instructions per wave
+    constexpr int RPI = 64 / CPR;                     // rows per wave-instruction (1 KB)
+    constexpr int NI = kSubKeys * D * 2 / 1024 / NW;  // instructions per wave
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
         const int I = n * NW + wave;
         const int row = I * RPI + lane / CPR;
-        const int pc = lane % CPR;
-        const int c = pc ^ (row & (CPR - 1));
-        const uint16_t* src = g + row * D + c * 8;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+        const int c = (lane % CPR) ^ (row & (CPR - 1));
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g + row * D + c * 8),
                                          (__attribute__((address_space(3))) void*)((lds_u16_t*)lds_tile + I * 512),
                                          16, 0, 0);
     }
 }
 
-// Transposing LDS read of V: in each 16-lane group, lane i returns
-// V[kb + j][dv0 + i] for j = 0..3 (four consecutive keys of one channel);
-// lane a = 4j + r of the group addresses V[kb + j][dv0 + 4r .. 4r+3].
-template <int D>
-__device__ __forceinline__ s16x4_t v_tr_read(const uint16_t* v_tile, int kb, int dv0, int i) {
-    const int j = i >> 2, r = i & 3;
-    const int row = kb + j;
-    const int col = dv0 + 4 * r;  // 4-element piece: chunk col/8, half (col/4)%2
-    const int off = tile_off<D>(row, col >> 3) + ((col >> 2) & 1) * 8;
-    lds_s16x4_t* p = (lds_s16x4_t*)((__attribute__((address_space(3))) char*)v_tile + off);
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+// Workgroup barrier for the copy pipeline.  A fenced barrier
+// (__syncthreads, or an LDS-scoped fence, since LDS-DMA writes are pending
+// LDS writes) makes the compiler drain every outstanding copy, including the
+// stages still streaming in.  Here each wave has already waited (vmcnt) for
+// its own copies of the stage about to be read, and every read of the stage
+// about to be overwritten was consumed by an MFMA before the barrier, so a
+// bare s_barrier is enough; the empty asm statements only stop the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    // gfx9 s_waitcnt: vmcnt[3:0] and [15:14], expcnt[6:4] (7 = no wait),
+    // lgkmcnt[11:8] (15 = no wait)
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Cursor over the sub-tiles of a row's list: listed block j (skipping
+// out-of-range entries and blocks without valid keys), sub-tile `sub`.
+template <int BLK, bool DENSE>
+struct Cursor {
+    int e, e1, j, vk, sub;
+    bool have;
+    const_i32_t* col;
+    const_i32_t* kvl;
+    int nkb;
+    __device__ __forceinline__ void seek() {
+        for (; e < e1; ++e) {
+            j = DENSE ? e : col[e];
+            if (j < 0 || j >= nkb) continue;
+            vk = kvl ? kvl[j] : BLK;
+            vk = vk > BLK ? BLK : vk;
+            if (vk > 0) {
+                have = true;
+                return;
+            }
+        }
+        have = false;
+    }
+    __device__ __forceinline__ void advance() {
+        ++sub;
+        if (sub * kSubKeys >= vk) {
+            sub = 0;
+            ++e;
+            seek();
+        }
+    }
+    __device__ __forceinline__ int nvalid() const {
+        const int n = vk - sub * kSubKeys;
+        return n < kSubKeys ? n : kSubKeys;
+    }
+};
+
+// Workgroup of 2 * BLK/32 waves: wave w owns query rows 32*(w % QG) .. +31
+// (QG = BLK/32 query groups) and key half kh = w / QG of every 64-key stage
+// (keys 32*kh .. 32*kh+31).  Each wave keeps its own online-softmax state
+// over its keys; the two halves of a query group are merged through LDS at
+// the end.  Two waves per SIMD let the hardware overlap one wave's LDS and
+// exponential latency with the other's matrix instructions.
 template <int BLK, int D, bool DENSE>
-__global__ void __launch_bounds__(BLK * 2) attn_bf16_kernel(AttnArgs a) {
-    constexpr int NW = BLK / 32;           // waves; each owns 32 query rows
-    constexpr int KT = BLK / 32, DT = D / 32, KK = D / 16;
-    constexpr int TILE = BLK * D;          // elements per K or V tile
-    // two stages of (K tile, V tile)
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * TILE];
+__global__ void __launch_bounds__(BLK * 4, 1) attn_bf16_kernel(AttnArgs a) {
+    constexpr int QG = BLK / 32;               // query groups of 32 rows
+    constexpr int NW = 2 * QG;                 // waves
+    constexpr int DT = D / 32, KK = D / 16;
+    constexpr int SUBE = kSubKeys * D;         // elements of a K or V sub-tile
+    constexpr int NI = 2 * (kSubKeys * D * 2 / 1024 / NW);  // DMA instructions per wave per stage
+    __shared__ __attribute__((aligned(1024))) uint16_t st0[2 * SUBE];
+    __shared__ __attribute__((aligned(1024))) uint16_t st1[2 * SUBE];
+    __shared__ __attribute__((aligned(1024))) uint16_t st2[2 * SUBE];
+    __shared__ __attribute__((aligned(1024))) uint16_t st3[2 * SUBE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int qg = wave % QG, kh = wave / QG;
     const int hi = lane >> 5, l32 = lane & 31, g16 = lane & 15;
     int h, i;
     map_item(a.heads * a.nqb, a.nqb, h, i);
     int vq = a.q_len ? a.q_len[i] : BLK;
     vq = vq < 0 ? 0 : (vq > BLK ? BLK : vq);
-    const int q0 = wave * 32;
+    const int q0 = qg * 32;
     const bool active = q0 < vq;
+    const bool valid_row = q0 + l32 < vq;
 
     const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + h * a.q_hs + (int64_t)i * BLK * D;
     const uint16_t* Kh = static_cast<const uint16_t*>(a.k) + h * a.k_hs;
     const uint16_t* Vh = static_cast<const uint16_t*>(a.v) + h * a.v_hs;
+
+    // Q^T fragments (B operand of S^T = K Q^T), held for the whole walk
+    bf16x8_t qf[KK];
+    {
+        const uint16_t* qrow = Qb + (int64_t)(q0 + l32) * D + 8 * hi;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qf[kk] = lds_bf16x8(qrow + 16 * kk);
+    }
 
     int e0, e1;
     if (DENSE) {
@@ -152,137 +220,188 @@ __global__ void __launch_bounds__(BLK * 2) attn_bf16_kernel(AttnArgs a) {
         e1 = a.nkb;
     } else {
         const int row = h * a.nqb + i;
-        e0 = a.row_ptr[row];
-        e1 = a.row_ptr[row + 1];
+        const_i32_t* rp = (const_i32_t*)a.row_ptr;
+        e0 = rp[row];
+        e1 = rp[row + 1];
         e0 = e0 < 0 ? 0 : e0;
         e1 = e1 > a.col_len ? (int)a.col_len : e1;
     }
-    // next listed block at or after e with at least one valid key, or -1
-    auto next_valid = [&](int& e, int& j, int& vk) {
-        for (; e < e1; ++e) {
-            j = DENSE ? e : a.col_idx[e];
-            if (j < 0 || j >= a.nkb) continue;
-            vk = a.kv_len ? a.kv_len[j] : BLK;
-            vk = vk > BLK ? BLK : vk;
-            if (vk > 0) return true;
-        }
-        return false;
+    Cursor<BLK, DENSE> ic{e0, e1, 0, 0, 0, false, (const_i32_t*)a.col_idx, (const_i32_t*)a.kv_len, a.nkb};
+    ic.seek();
+    Cursor<BLK, DENSE> cc = ic;
+    int issued = 0, computed = 0;
+    auto issue = [&](uint16_t* stage) {
+        const int64_t off = ((int64_t)ic.j * BLK + ic.sub * kSubKeys) * D;
+        dma_sub<D, NW>(Kh + off, stage, wave, lane);
+        dma_sub<D, NW>(Vh + off, stage + SUBE, wave, lane);
+        ic.advance();
+        ++issued;
     };
+    if (ic.have) issue(st0);
+    if (ic.have) issue(st1);
+    if (ic.have) issue(st2);
 
-    int e = e0, j = 0, vk = 0;
-    bool have = next_valid(e, j, vk);
-    if (have) {
-        dma_tile<BLK, D, NW>(Kh + (int64_t)j * TILE, lds, wave, lane);
-        dma_tile<BLK, D, NW>(Vh + (int64_t)j * TILE, lds + TILE, wave, lane);
-    }
-
-    bf16x8_t qf[KK];
-    {
-        const uint16_t* qrow = Qb + (int64_t)(q0 + l32) * D + 8 * hi;
+    // per-lane LDS byte offsets (loop invariant): this wave's 32 keys start
+    // at row 32*kh of the stage
+    const int kr = 32 * kh + key_of_row(l32);
+    int koff[KK];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qf[kk] = lds_bf16x8(qrow + 16 * kk);
+    for (int kk = 0; kk < KK; ++kk) koff[kk] = tile_off<D>(kr, 2 * kk + hi);
+    int voff[DT][2];
+    {
+        const int j4 = g16 >> 2, r4 = g16 & 3, g2 = (lane >> 4) & 1;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int h4 = 0; h4 < 2; ++h4) {
+                const int row = 32 * kh + 8 * hi + 4 * h4 + j4;  // + 16*s2
+                const int col = dt * 32 + 16 * g2 + 4 * r4;
+                voff[dt][h4] = tile_off<D>(row, col >> 3) + ((col >> 2) & 1) * 8 + SUBE * 2;
+            }
     }
+
     f32x16_t o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
     float m = -INFINITY, l = 0.f;
-    const int kr = key_of_row(l32);
-    int stage = 0;
+    const float c2 = a.scale_log2;
 
-    while (have) {
-        // this stage's tile has landed (every wave waited on its own copies)
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        const int vk_cur = vk;
-        int en = e + 1, jn = 0, vkn = 0;
-        const bool have_next = next_valid(en, jn, vkn);
-        if (have_next) {
-            uint16_t* nxt = lds + (stage ^ 1) * 2 * TILE;
-            dma_tile<BLK, D, NW>(Kh + (int64_t)jn * TILE, nxt, wave, lane);
-            dma_tile<BLK, D, NW>(Vh + (int64_t)jn * TILE, nxt + TILE, wave, lane);
+    auto compute = [&](const uint16_t* stage) {
+        const int nv = cc.nvalid() - 32 * kh;  // valid keys of this wave's half (may be <= 0)
+        if (!active) return;
+        const char* base = reinterpret_cast<const char*>(stage);
+        bf16x8_t kf[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            kf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(base + koff[kk]));
+        s16x4_t vr[2][DT][2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int h4 = 0; h4 < 2; ++h4)
+                    vr[s2][dt][h4] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4_t*)((__attribute__((address_space(3))) char*)stage + voff[dt][h4] +
+                                       s2 * 16 * D * 2));
+        // S^T = K Q^T over this wave's 32 keys: lane holds the scores of query
+        // q0 + l32 for keys 32*kh + 16*(r/8) + 8*hi + (r%8), r = 0..15.
+        f32x16_t s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+        if (nv < 32) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = 16 * (r >> 3) + 8 * hi + (r & 7);
+                if (key >= nv) s[r] = -INFINITY;
+            }
         }
-        const uint16_t* Kt = lds + stage * 2 * TILE;
-        const uint16_t* Vt = Kt + TILE;
-
-        if (active) {
-            // S^T = K Q^T: lane holds scores of query q0 + l32 for keys
-            // mt*32 + 16*(r/8) + 8*hi + (r%8), r = 0..15.
-            f32x16_t s[KT];
+        float mx = -INFINITY;
 #pragma unroll
-            for (int mt = 0; mt < KT; ++mt) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-                const int key = mt * 32 + kr;
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    const bf16x8_t kf = __builtin_bit_cast(
-                        bf16x8_t, *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Kt) +
-                                                                   tile_off<D>(key, 2 * kk + hi)));
-                    s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[mt], 0, 0, 0);
-                }
-            }
-            if (vk_cur < BLK) {
-#pragma unroll
-                for (int mt = 0; mt < KT; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = mt * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
-                        if (key >= vk_cur) s[mt][r] = -INFINITY;
-                    }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int mt = 0; mt < KT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mn = fmaxf(m, mx * a.scale_log2);
-            const float alpha = exp2f(m - mn);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+        // lazy rescaling: a query's reference max moves only when its own
+        // max passes it by more than kRescaleSlack (so p <= 2^slack); each
+        // query's arithmetic depends on its own scores only.  Padded query
+        // rows never move it (their results are discarded).
+        const bool need = valid_row && mx > m + kRescaleSlack;
+        if (__any(need)) {
+            const float mn = need ? mx : m;
+            const float alpha = need ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
             m = mn;
-            float ls = 0.f;
-            bf16x8_t pf[KT][2];
-#pragma unroll
-            for (int mt = 0; mt < KT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = exp2f(fmaf(s[mt][r], a.scale_log2, -mn));
-                    ls += p;
-                    pf[mt][r >> 3][r & 7] = (__bf16)p;
-                }
-            l = l * alpha + ls;
+            l *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-
-            // O^T += V^T P^T: A = V^T fragment (8 consecutive keys of channel
-            // dt*32 + l32) from two transposing reads; B = P^T from registers.
+        }
+        // before the first valid key the reference is -inf and every score
+        // is -inf: use 0 so those p are exactly 0
+        const float mref = m == -INFINITY ? 0.f : m;
+        float ls = 0.f;
+        bf16x8_t pf[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mref));
+            ls += p;
+            pf[r >> 3][r & 7] = (__bf16)p;
+        }
+        l += ls;
+        // O^T += V^T P^T over this wave's keys; four independent chains (dt)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const int dv0 = dt * 32 + 16 * ((lane >> 4) & 1);
-#pragma unroll
-                for (int mt = 0; mt < KT; ++mt)
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) {
-                        const int kb = mt * 32 + 16 * s2 + 8 * hi;
-                        const s16x4_t v0 = v_tr_read<D>(Vt, kb, dv0, g16);
-                        const s16x4_t v1 = v_tr_read<D>(Vt, kb + 4, dv0, g16);
-                        const bf16x8_t vf = __builtin_bit_cast(
-                            bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[mt][s2], o[dt], 0, 0, 0);
-                    }
+                const bf16x8_t vf = __builtin_bit_cast(
+                    bf16x8_t, __builtin_shufflevector(vr[s2][dt][0], vr[s2][dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s2], o[dt], 0, 0, 0);
             }
-        }
-        stage ^= 1;
-        e = en;
-        j = jn;
-        vk = vkn;
-        have = have_next;
+    };
+
+    // Sub-tile t lives in stage t % 4; while it is multiplied, sub-tiles
+    // t+1 .. t+3 stream in.  The loop is unrolled over the four stages so
+    // every LDS access names one stage array (no false waits on the others).
+    auto step = [&](uint16_t* cur, uint16_t* nxt) {
+        const int later = issued - computed - 1;  // stages issued after this one
+        if (later >= 2)
+            wait_vmcnt<2 * NI>();
+        else if (later == 1)
+            wait_vmcnt<NI>();
+        else
+            wait_vmcnt<0>();
+        lds_barrier();
+        if (ic.have) issue(nxt);
+        compute(cur);
+        cc.advance();
+        ++computed;
+    };
+    while (computed < issued) {
+        step(st0, st3);
+        if (computed >= issued) break;
+        step(st1, st0);
+        if (computed >= issued) break;
+        step(st2, st1);
+        if (computed >= issued) break;
+        step(st3, st2);
     }
 
-    // epilogue
+    // merge the two key halves of each query group through LDS (the stage
+    // buffers are free: every issued copy was consumed by the loop)
+    constexpr int XF = 2 + 16 * DT;  // floats per lane: m, l, o
+    static_assert(QG <= kStages && XF * 64 * 4 <= 2 * SUBE * 2, "exchange buffer");
+    float* xch = reinterpret_cast<float*>(qg == 0 ? st0 : qg == 1 ? st1 : qg == 2 ? st2 : st3);
+    lds_barrier();
+    if (kh == 1) {
+        float* x = xch + lane;
+        x[0] = m;
+        x[64] = l;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[(2 + 16 * dt + r) * 64] = o[dt][r];
+    }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (kh == 1) return;
+    {
+        const float* x = xch + lane;
+        const float mb = x[0], lb = x[64];
+        const float mm = fmaxf(m, mb);
+        const float fa = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+        const float fb = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb - mm);
+        l = l * fa + lb * fb;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] = o[dt][r] * fa + x[(2 + 16 * dt + r) * 64] * fb;
+        m = mm;
+    }
+
+    // epilogue (kh == 0 waves)
     const float lt = l + __shfl_xor(l, 32);
     const int qrow = q0 + l32;
     const bool live = active && qrow < vq && lt > 0.f;
@@ -385,9 +504,9 @@ template <int BLK, int D>
 hipError_t launch_typed(const AttnArgs& args, int dtype, bool dense, int total, hipStream_t stream) {
     if (dtype == BSA_BF16) {
         if (dense)
-            hipLaunchKernelGGL((attn_bf16_kernel<BLK, D, true>), dim3(total), dim3(BLK * 2), 0, stream, args);
+            hipLaunchKernelGGL((attn_bf16_kernel<BLK, D, true>), dim3(total), dim3(BLK * 4), 0, stream, args);
         else
-            hipLaunchKernelGGL((attn_bf16_kernel<BLK, D, false>), dim3(total), dim3(BLK * 2), 0, stream, args);
+            hipLaunchKernelGGL((attn_bf16_kernel<BLK, D, false>), dim3(total), dim3(BLK * 4), 0, stream, args);
     } else {
         if (dense)
             hipLaunchKernelGGL((attn_f32_kernel<BLK, D, true>), dim3(total), dim3(BLK * (D / 32)), 0, stream, args);

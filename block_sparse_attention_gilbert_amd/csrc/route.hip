@@ -30,32 +30,38 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t bits16) {
     return (double)__uint_as_float(bits16 << 16);
 }
 
-// Mean of the valid rows of each block.  grid = (blocks to pool, heads).
-// Thread t owns one 16-byte chunk of a row and a stride of rows.
+// Mean of the valid rows of each block; one wave per block, four blocks per
+// workgroup.  grid = (ceil(blocks / 4), heads).  Lane l owns one 16-byte
+// chunk (l % chunks) of rows l / chunks, + groups, ...; the partial sums of
+// the row groups are combined with butterfly shuffles (exact in float64, so
+// the combination order does not matter).
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads)
 pool_kernel(const void* __restrict__ x, int64_t head_stride, int d, int block,
-            const int32_t* __restrict__ lens, int b_begin, double* __restrict__ out,
+            const int32_t* __restrict__ lens, int b_begin, int nb, double* __restrict__ out,
             int64_t out_head_blocks) {
-    __shared__ double part[2048];
     constexpr int CE = BF16 ? 8 : 4;  // elements per 16-byte chunk
-    const int b = b_begin + blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int bl = blockIdx.x * (kThreads / 64) + w;
+    if (bl >= nb) return;
+    const int b = b_begin + bl, h = blockIdx.y;
     int valid = lens ? lens[b] : block;
     valid = valid < 0 ? 0 : (valid > block ? block : valid);
-    const int chunks = d / CE, groups = kThreads / chunks;
-    const int ch = t % chunks, g = t / chunks;
+    const int chunks = d / CE, groups = 64 / chunks;
+    const int ch = lane % chunks, g = lane / chunks;
     double acc[CE];
 #pragma unroll
     for (int e = 0; e < CE; ++e) acc[e] = 0.0;
     const int64_t base = h * head_stride + (int64_t)b * block * d + ch * CE;
+#pragma unroll 8
     for (int row = g; row < valid; row += groups) {
         if (BF16) {
             const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + base + (int64_t)row * d);
-            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+            const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc[2 * e] += bf16_to_f64(w[e] & 0xFFFFu);
-                acc[2 * e + 1] += bf16_to_f64(w[e] >> 16);
+                acc[2 * e] += bf16_to_f64(wd[e] & 0xFFFFu);
+                acc[2 * e + 1] += bf16_to_f64(wd[e] >> 16);
             }
         } else {
             const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + base + (int64_t)row * d);
@@ -65,13 +71,13 @@ pool_kernel(const void* __restrict__ x, int64_t head_stride, int d, int block,
             acc[3] += (double)f.w;
         }
     }
+    for (int off = chunks; off < 64; off <<= 1)
 #pragma unroll
-    for (int e = 0; e < CE; ++e) part[g * d + ch * CE + e] = acc[e];
-    __syncthreads();
-    if (t < d) {
-        double s = 0.0;
-        for (int gg = 0; gg < groups; ++gg) s += part[gg * d + t];
-        out[(h * out_head_blocks + b) * d + t] = valid > 0 ? s / (double)valid : 0.0;
+        for (int e = 0; e < CE; ++e) acc[e] += __shfl_xor(acc[e], off);
+    if (g == 0) {
+        double* o = out + (h * out_head_blocks + b) * d + ch * CE;
+#pragma unroll
+        for (int e = 0; e < CE; ++e) o[e] = valid > 0 ? acc[e] / (double)valid : 0.0;
     }
 }
 
@@ -106,55 +112,73 @@ overlap_flags_kernel(const float* __restrict__ overlap, int64_t ors, int n_cand,
 }
 
 // kappa[h][i][j] = (qbar_i . kbar_j) * scale + log1p(lambda * g_hat_ij).
-// grid = (ceil(n_cand / 64), heads).  Thread (jl, rs) = (t % 64, t / 64)
-// scores candidate j0 + jl against rows r0 + rs + 4m; pooled vectors are
-// staged through LDS 32 channels at a time.
-constexpr int kScoreJ = 64, kScoreDC = 32, kScoreRG = 32;
+// grid = (ceil(n_cand / 128), heads); each workgroup scores 128 candidates
+// against every query-block row, 40 rows per pass.  Thread t owns
+// candidates j0 + t%64 and j0 + 64 + t%64 and rows 10*(t/64) .. +9 of the
+// pass (each wave owns 10 rows, so its pooled-query reads are broadcasts).
+// Pooled vectors are staged through LDS 32 channels at a time; every dot
+// product accumulates over channels in order 0..d-1.
+constexpr int kScoreJ = 128, kScoreRows = 40, kScoreDC = 32, kScoreRPT = kScoreRows / (kThreads / 64);
+
+__device__ __attribute__((noinline)) double overlap_bias(double g, double lambda, double g_ref, double tau) {
+    const double gh = g <= tau ? 0.0 : fmin(1.0, g / g_ref);
+    return log1p(lambda * gh);
+}
 
 __global__ void __launch_bounds__(kThreads)
 score_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar, int64_t kbar_head_blocks,
              int nqb, int n_cand, int d, double scale, const float* __restrict__ overlap, int64_t ors,
              double lambda, double g_ref, double tau, double* __restrict__ keys) {
-    __shared__ double kt[kScoreJ][kScoreDC + 1];
-    __shared__ double qt[kScoreRG][kScoreDC];
+    __shared__ double kt[kScoreDC][kScoreJ];
+    __shared__ __attribute__((aligned(16))) double qt[kScoreRows][kScoreDC];
     const int h = blockIdx.y, j0 = blockIdx.x * kScoreJ, t = threadIdx.x;
-    const int jl = t % kScoreJ, rs = t / kScoreJ;
-    const int j = j0 + jl;
-    constexpr int RPT = kScoreRG / (kThreads / kScoreJ);  // rows per thread
-    for (int r0 = 0; r0 < nqb; r0 += kScoreRG) {
-        double acc[RPT];
+    const int cl = t % 64, rq = t / 64;
+    const int ja = j0 + cl, jb = j0 + 64 + cl;
+    for (int r0 = 0; r0 < nqb; r0 += kScoreRows) {
+        double acc_a[kScoreRPT], acc_b[kScoreRPT];
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) acc[m] = 0.0;
+        for (int m = 0; m < kScoreRPT; ++m) acc_a[m] = acc_b[m] = 0.0;
         for (int dc = 0; dc < d; dc += kScoreDC) {
             __syncthreads();
+            // kt[dd][c] = kbar[j0 + c][dc + dd]; 32 consecutive threads read one
+            // candidate's 32 channels
             for (int x = t; x < kScoreJ * kScoreDC; x += kThreads) {
-                const int jj = x / kScoreDC, dd = x % kScoreDC, jg = j0 + jj;
-                kt[jj][dd] = jg < n_cand ? kbar[(h * kbar_head_blocks + jg) * d + dc + dd] : 0.0;
+                const int c = x / kScoreDC, dd = x % kScoreDC, jg = j0 + c;
+                kt[dd][c] = jg < n_cand ? kbar[(h * kbar_head_blocks + jg) * d + dc + dd] : 0.0;
             }
-            for (int x = t; x < kScoreRG * kScoreDC; x += kThreads) {
+            for (int x = t; x < kScoreRows * kScoreDC; x += kThreads) {
                 const int rr = x / kScoreDC, dd = x % kScoreDC, ig = r0 + rr;
                 qt[rr][dd] = ig < nqb ? qbar[((int64_t)h * nqb + ig) * d + dc + dd] : 0.0;
             }
             __syncthreads();
-#pragma unroll 8
-            for (int dd = 0; dd < kScoreDC; ++dd) {
-                const double kv = kt[jl][dd];
+#pragma unroll 4
+            for (int dd = 0; dd < kScoreDC; dd += 2) {
+                const double ka0 = kt[dd][cl], kb0 = kt[dd][64 + cl];
+                const double ka1 = kt[dd + 1][cl], kb1 = kt[dd + 1][64 + cl];
 #pragma unroll
-                for (int m = 0; m < RPT; ++m) acc[m] = fma(qt[rs + 4 * m][dd], kv, acc[m]);
+                for (int m = 0; m < kScoreRPT; ++m) {
+                    const double2 q2 = *reinterpret_cast<const double2*>(&qt[rq * kScoreRPT + m][dd]);
+                    acc_a[m] = fma(q2.x, ka0, acc_a[m]);
+                    acc_b[m] = fma(q2.x, kb0, acc_b[m]);
+                    acc_a[m] = fma(q2.y, ka1, acc_a[m]);
+                    acc_b[m] = fma(q2.y, kb1, acc_b[m]);
+                }
             }
         }
-        if (j < n_cand) {
 #pragma unroll
-            for (int m = 0; m < RPT; ++m) {
-                const int i = r0 + rs + 4 * m;
-                if (i >= nqb) continue;
-                double kappa = acc[m] * scale;
-                if (overlap) {
-                    const double g = (double)overlap[(int64_t)i * ors + j];
-                    const double gh = g <= tau ? 0.0 : fmin(1.0, g / g_ref);
-                    kappa += log1p(lambda * gh);
-                }
-                keys[((int64_t)h * nqb + i) * n_cand + j] = kappa;
+        for (int m = 0; m < kScoreRPT; ++m) {
+            const int i = r0 + rq * kScoreRPT + m;
+            if (i >= nqb) continue;
+            double* krow = keys + ((int64_t)h * nqb + i) * n_cand;
+            if (ja < n_cand) {
+                double kap = acc_a[m] * scale;
+                if (overlap) kap += overlap_bias((double)overlap[(int64_t)i * ors + ja], lambda, g_ref, tau);
+                krow[ja] = kap;
+            }
+            if (jb < n_cand) {
+                double kap = acc_b[m] * scale;
+                if (overlap) kap += overlap_bias((double)overlap[(int64_t)i * ors + jb], lambda, g_ref, tau);
+                krow[jb] = kap;
             }
         }
     }
@@ -376,24 +400,25 @@ hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* w
 
     // 1. pooled queries
     {
-        dim3 grid(a->nqb, a->heads);
+        dim3 grid((a->nqb + 3) / 4, a->heads);
         if (bf16)
             hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kThreads), 0, stream, a->q, a->q_head_stride, a->d,
-                               a->block, a->q_block_len, 0, qbar, (int64_t)a->nqb);
+                               a->block, a->q_block_len, 0, a->nqb, qbar, (int64_t)a->nqb);
         else
             hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kThreads), 0, stream, a->q, a->q_head_stride, a->d,
-                               a->block, a->q_block_len, 0, qbar, (int64_t)a->nqb);
+                               a->block, a->q_block_len, 0, a->nqb, qbar, (int64_t)a->nqb);
     }
     // 2. pooled keys of the candidates not yet in the cache
     const int kb0 = a->kpool ? a->kpool_valid_blocks : 0;
     if (n_cand > kb0) {
-        dim3 grid(n_cand - kb0, a->heads);
+        const int nb = n_cand - kb0;
+        dim3 grid((nb + 3) / 4, a->heads);
         if (bf16)
             hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kThreads), 0, stream, a->k, a->k_head_stride, a->d,
-                               a->block, a->kv_block_len, kb0, kbar, (int64_t)n_cand);
+                               a->block, a->kv_block_len, kb0, nb, kbar, (int64_t)n_cand);
         else
             hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kThreads), 0, stream, a->k, a->k_head_stride, a->d,
-                               a->block, a->kv_block_len, kb0, kbar, (int64_t)n_cand);
+                               a->block, a->kv_block_len, kb0, nb, kbar, (int64_t)n_cand);
     }
     // 3. overlap row flags (for the fallback counts)
     const bool want_flags = a->overlap && a->fallback_counts && n_cand > 0;
