@@ -155,8 +155,8 @@ COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 
 def profile_attention(launches: int):
     """Counter-collection mode: set up C4 at chunk 48, route once, then run
-    ``launches`` attention launches and one plain 1 GiB device copy (the
-    calibration kernel for the byte counters).  Prints nothing but a summary
+    ``launches`` block-sparse attention launches, two dense ones, and one
+    plain 1 GiB device copy (the calibration kernel for the byte counters).  Prints nothing but a summary
     line; meant to run under rocprofv3 --pmc."""
     import torch
     st = setup_c4(48, device="cuda:0")
@@ -171,6 +171,8 @@ def profile_attention(launches: int):
         block_sparse_attn(ra.q_blk, ra.k_store[:, : nkb * ra.block], ra.v_store[:, : nkb * ra.block], r["row_ptr"],
                           r["col_idx"], block=ra.block, scale=ra.scale, q_block_len=ra.q_len,
                           kv_block_len=ra.kv_len[:nkb], out=ra.o_blk, lse=ra.lse)
+    for _ in range(2):  # dense attention over the same history, for comparison counters
+        ra.dense(st["cur"])
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -201,8 +203,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_path: str):
         ks = [k for k in vals if key in k]
         return [v for k in ks for v in vals[k]]
 
-    attn_f = pick(fetch, "attn_bf16_kernel")
-    attn_w = pick(write, "attn_bf16_kernel")
+    attn_f = pick(fetch, "attn_bf16_kernel<128, 128, false>")
+    attn_w = pick(write, "attn_bf16_kernel<128, 128, false>")
     copy_f = pick(fetch, "copy")
     copy_w = pick(write, "copy")
     f_factor = COPY_BYTES / (max(copy_f) * 1024.0)

@@ -87,19 +87,29 @@ constexpr int kStages = 4;    // LDS stages; kStages - 1 sub-tiles in flight
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
 
 // LDS sub-tile layout: kSubKeys rows of D bf16 (no padding), 16-byte chunks
-// XOR-swizzled by row so that the 32 rows an MFMA operand read touches fall
-// in distinct banks.  Byte offset of (row, 16-byte chunk c).
-template <int D>
-__device__ __forceinline__ int tile_off(int row, int c) {
+// XOR-swizzled by row.  K tiles are read by ds_read_b128 with 16 lanes per
+// LDS cycle touching 16 different rows at one chunk: XOR with row % 16
+// spreads them over all bank groups.  V tiles are read by transposing 8-byte
+// reads in which 32 lanes touch 4 consecutive rows x 4 consecutive chunks:
+// XOR with 4 * (row % 4) (d = 128; 4 * (row/2 % 2) for d = 64, two rows per
+// bank period) gives those 16 chunk accesses 16 distinct bank groups.
+template <int D, bool IS_V>
+__device__ __forceinline__ int swz(int row) {
     constexpr int CPR = D / 8;  // chunks per row
-    return row * (D * 2) + ((c ^ (row & (CPR - 1))) << 4);
+    if (!IS_V) return row & (CPR - 1);
+    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
+template <int D, bool IS_V>
+__device__ __forceinline__ int tile_off(int row, int c) {
+    return row * (D * 2) + ((c ^ swz<D, IS_V>(row)) << 4);
 }
 
 // Direct global -> LDS copy of one kSubKeys x D bf16 sub-tile into the
 // swizzled layout.  One 16-byte load per lane lands at base + 16 * lane, so
 // lane l of wave-instruction I fills row I * RPI + l / CPR, physical chunk
 // l % CPR, and fetches the logical chunk that belongs there.
-template <int D, int NW>
+template <int D, int NW, bool IS_V>
 __device__ __forceinline__ void dma_sub(const uint16_t* __restrict__ g, uint16_t* lds_tile, int wave, int lane) {
     constexpr int CPR = D / 8;
     constexpr int RPI = 64 / CPR;                     // rows per wave-instruction (1 KB)
@@ -108,11 +118,22 @@ __device__ __forceinline__ void dma_sub(const uint16_t* __restrict__ g, uint16_t
     for (int n = 0; n < NI; ++n) {
         const int I = n * NW + wave;
         const int row = I * RPI + lane / CPR;
-        const int c = (lane % CPR) ^ (row & (CPR - 1));
+        const int c = (lane % CPR) ^ swz<D, IS_V>(row);
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g + row * D + c * 8),
                                          (__attribute__((address_space(3))) void*)((lds_u16_t*)lds_tile + I * 512),
                                          16, 0, 0);
     }
+}
+
+// max over the two lanes l and l ^ 32 (which hold one query's two key halves)
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float add_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Workgroup barrier for the copy pipeline.  A fenced barrier
@@ -232,8 +253,8 @@ __global__ void __launch_bounds__(BLK * 4, 1) attn_bf16_kernel(AttnArgs a) {
     int issued = 0, computed = 0;
     auto issue = [&](uint16_t* stage) {
         const int64_t off = ((int64_t)ic.j * BLK + ic.sub * kSubKeys) * D;
-        dma_sub<D, NW>(Kh + off, stage, wave, lane);
-        dma_sub<D, NW>(Vh + off, stage + SUBE, wave, lane);
+        dma_sub<D, NW, false>(Kh + off, stage, wave, lane);
+        dma_sub<D, NW, true>(Vh + off, stage + SUBE, wave, lane);
         ic.advance();
         ++issued;
     };
@@ -246,7 +267,7 @@ __global__ void __launch_bounds__(BLK * 4, 1) attn_bf16_kernel(AttnArgs a) {
     const int kr = 32 * kh + key_of_row(l32);
     int koff[KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) koff[kk] = tile_off<D>(kr, 2 * kk + hi);
+    for (int kk = 0; kk < KK; ++kk) koff[kk] = tile_off<D, false>(kr, 2 * kk + hi);
     int voff[DT][2];
     {
         const int j4 = g16 >> 2, r4 = g16 & 3, g2 = (lane >> 4) & 1;
@@ -256,7 +277,7 @@ __global__ void __launch_bounds__(BLK * 4, 1) attn_bf16_kernel(AttnArgs a) {
             for (int h4 = 0; h4 < 2; ++h4) {
                 const int row = 32 * kh + 8 * hi + 4 * h4 + j4;  // + 16*s2
                 const int col = dt * 32 + 16 * g2 + 4 * r4;
-                voff[dt][h4] = tile_off<D>(row, col >> 3) + ((col >> 2) & 1) * 8 + SUBE * 2;
+                voff[dt][h4] = tile_off<D, true>(row, col >> 3) + ((col >> 2) & 1) * 8 + SUBE * 2;
             }
     }
 
@@ -303,7 +324,7 @@ __global__ void __launch_bounds__(BLK * 4, 1) attn_bf16_kernel(AttnArgs a) {
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+        mx = max_halves(mx) * c2;
         // lazy rescaling: a query's reference max moves only when its own
         // max passes it by more than kRescaleSlack (so p <= 2^slack); each
         // query's arithmetic depends on its own scores only.  Padded query
@@ -402,7 +423,7 @@ __global__ void __launch_bounds__(BLK * 4, 1) attn_bf16_kernel(AttnArgs a) {
     }
 
     // epilogue (kh == 0 waves)
-    const float lt = l + __shfl_xor(l, 32);
+    const float lt = add_halves(l);
     const int qrow = q0 + l32;
     const bool live = active && qrow < vq && lt > 0.f;
     const float inv = live ? 1.f / lt : 0.f;

@@ -70,3 +70,13 @@ def test_permute_into_store_slot_and_token_stride():
     out = torch.zeros((L, 2, heads, d), dtype=torch.bfloat16, device=dev)
     bsa.gilbert_perm(slot, perm, block=block, inverse=True, dst=out[:, 1])
     assert torch.equal(out[:, 1], k_raster) and torch.all(out[:, 0] == 0)
+
+
+def test_index_large_grid():
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    shape = (21, 60, 104)   # 131,040 cells: a 21-frame, 2x-resolution chunk
+    perm, inv = bsa.gilbert_index(*shape, device=dev)
+    ref, ref_inv = gilbert_order(*shape)
+    assert np.array_equal(perm.cpu().numpy(), ref)
+    assert np.array_equal(inv.cpu().numpy(), ref_inv)

@@ -148,3 +148,28 @@ def test_route_edge_cases():
             assert_lists_equal(got[h], ref["lists"], "K=%d tail=%d head %d" % (K, tail, h))
             assert len(got[h][1]) == 0
             assert all(6 not in l.tolist() for l in got[h])
+
+
+def test_route_maximum_candidates():
+    """4096 candidates (the largest the selection supports) with per-row
+    budgets up to 143 and a dense tail, against the oracle."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    rng = np.random.default_rng(4096)
+    heads, d, bs, nqb, n_cand, tail = 2, 64, 64, 3, 4096, 3
+    nkb = n_cand + tail
+    q = torch.from_numpy(rng.standard_normal((heads, nqb * bs, d)).astype(np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy(rng.standard_normal((heads, nkb * bs, d)).astype(np.float32)).to(torch.bfloat16)
+    kpr = rng.integers(0, 144, size=heads * nqb).astype(np.int32)
+    kpr[0] = 143
+    r = bsa.route_topk(q.to(dev), k.to(dev), block=bs, nqb=nqb, nkb=nkb, scale=0.125,
+                       k_per_row=torch.from_numpy(kpr).to(dev), k_max=143, n_dense_tail_blocks=tail)
+    got = csr_lists(r["row_ptr"], r["col_idx"], heads, nqb)
+    for h in range(heads):
+        ref = oroute.route_head(f64(q[h]), f64(k[h]), [bs] * nqb, [bs] * nkb, bs, scale=0.125,
+                                k_per_row=kpr[h * nqb:(h + 1) * nqb], n_dense_tail=tail)
+        assert_lists_equal(got[h], ref["lists"], "max candidates head %d" % h)
+    with pytest.raises(bsa.BsaError) as err:  # one candidate more than the selection handles
+        bsa.route_topk(q.to(dev), torch.zeros((heads, (n_cand + 1) * bs, d), dtype=torch.bfloat16, device=dev),
+                       block=bs, nqb=nqb, nkb=n_cand + 1, scale=0.125, k_fixed=5)
+    assert err.value.code == bsa.BSA_EUNSUPPORTED
