@@ -29,6 +29,8 @@
 // and LSE = -inf.  Waves whose 32 query rows are all padding skip the math.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace bsa {
@@ -82,7 +84,7 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
 typedef const __attribute__((address_space(4))) int32_t const_i32_t;
 
-constexpr int kSubKeys = 64;  // keys per pipeline stage (sub-tile)
+constexpr int kSubKeys = 32;  // keys per pipeline stage (sub-tile)
 constexpr int kStages = 4;    // LDS stages; kStages - 1 sub-tiles in flight
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
 
@@ -158,68 +160,58 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Cursor over the sub-tiles of a row's list: listed block j (skipping
-// out-of-range entries and blocks without valid keys), sub-tile `sub`.
+// Cursor over the listed blocks of a row: block j with vk valid keys,
+// skipping out-of-range entries and blocks without valid keys.  When the
+// list is exhausted `have` drops and j keeps the last valid block.
 template <int BLK, bool DENSE>
-struct Cursor {
-    int e, e1, j, vk, sub;
+struct BlockCursor {
+    int e, e1, j, vk;
     bool have;
     const_i32_t* col;
     const_i32_t* kvl;
     int nkb;
-    __device__ __forceinline__ void seek() {
+    __device__ __forceinline__ void next() {
         for (; e < e1; ++e) {
-            j = DENSE ? e : col[e];
-            if (j < 0 || j >= nkb) continue;
-            vk = kvl ? kvl[j] : BLK;
-            vk = vk > BLK ? BLK : vk;
-            if (vk > 0) {
+            const int jj = DENSE ? e : col[e];
+            if (jj < 0 || jj >= nkb) continue;
+            int v = kvl ? kvl[jj] : BLK;
+            v = v > BLK ? BLK : v;
+            if (v > 0) {
+                j = jj;
+                vk = v;
+                ++e;
                 have = true;
                 return;
             }
         }
         have = false;
     }
-    __device__ __forceinline__ void advance() {
-        ++sub;
-        if (sub * kSubKeys >= vk) {
-            sub = 0;
-            ++e;
-            seek();
-        }
-    }
-    __device__ __forceinline__ int nvalid() const {
-        const int n = vk - sub * kSubKeys;
-        return n < kSubKeys ? n : kSubKeys;
-    }
 };
 
-// Workgroup of 2 * BLK/32 waves: wave w owns query rows 32*(w % QG) .. +31
-// (QG = BLK/32 query groups) and key half kh = w / QG of every 64-key stage
-// (keys 32*kh .. 32*kh+31).  Each wave keeps its own online-softmax state
-// over its keys; the two halves of a query group are merged through LDS at
-// the end.  Two waves per SIMD let the hardware overlap one wave's LDS and
-// exponential latency with the other's matrix instructions.
+// Workgroup of BLK/32 waves, one (head, query block); wave w owns query rows
+// 32w .. 32w+31 and every key.  Each 32-key stage is 2 x 8 KB (d = 128), so
+// a workgroup needs 64 KB of LDS and two workgroups share a CU: their
+// independent barriers let the hardware overlap one workgroup's softmax and
+// LDS latency with the other's matrix instructions.
 template <int BLK, int D, bool DENSE>
-__global__ void __launch_bounds__(BLK * 4, 1) attn_bf16_kernel(AttnArgs a) {
-    constexpr int QG = BLK / 32;               // query groups of 32 rows
-    constexpr int NW = 2 * QG;                 // waves
+__global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
+    constexpr int NW = BLK / 32;               // waves
     constexpr int DT = D / 32, KK = D / 16;
     constexpr int SUBE = kSubKeys * D;         // elements of a K or V sub-tile
     constexpr int NI = 2 * (kSubKeys * D * 2 / 1024 / NW);  // DMA instructions per wave per stage
+    static_assert(kSubKeys * D * 2 % (1024 * NW) == 0, "stage copy must split evenly over the waves");
     __shared__ __attribute__((aligned(1024))) uint16_t st0[2 * SUBE];
     __shared__ __attribute__((aligned(1024))) uint16_t st1[2 * SUBE];
     __shared__ __attribute__((aligned(1024))) uint16_t st2[2 * SUBE];
     __shared__ __attribute__((aligned(1024))) uint16_t st3[2 * SUBE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int qg = wave % QG, kh = wave / QG;
     const int hi = lane >> 5, l32 = lane & 31, g16 = lane & 15;
     int h, i;
     map_item(a.heads * a.nqb, a.nqb, h, i);
     int vq = a.q_len ? a.q_len[i] : BLK;
     vq = vq < 0 ? 0 : (vq > BLK ? BLK : vq);
-    const int q0 = qg * 32;
+    const int q0 = wave * 32;
     const bool active = q0 < vq;
     const bool valid_row = q0 + l32 < vq;
 
@@ -247,24 +239,40 @@ __global__ void __launch_bounds__(BLK * 4, 1) attn_bf16_kernel(AttnArgs a) {
         e0 = e0 < 0 ? 0 : e0;
         e1 = e1 > a.col_len ? (int)a.col_len : e1;
     }
-    Cursor<BLK, DENSE> ic{e0, e1, 0, 0, 0, false, (const_i32_t*)a.col_idx, (const_i32_t*)a.kv_len, a.nkb};
-    ic.seek();
-    Cursor<BLK, DENSE> cc = ic;
-    int issued = 0, computed = 0;
-    auto issue = [&](uint16_t* stage) {
-        const int64_t off = ((int64_t)ic.j * BLK + ic.sub * kSubKeys) * D;
+    // Every listed block is SUBS stages of kSubKeys keys; slot t is stage
+    // t % 4, sub-tile t % SUBS of block t / SUBS.  Three slots are always in
+    // flight: past the end of the list the copies repeat the last block
+    // (never computed), so every wait is the same vmcnt.
+    constexpr int SUBS = BLK / kSubKeys;
+    static_assert(kStages % SUBS == 0, "stages must hold whole blocks");
+    BlockCursor<BLK, DENSE> ic{e0, e1, 0, 0, false, (const_i32_t*)a.col_idx, (const_i32_t*)a.kv_len, a.nkb};
+    ic.next();
+    if (!ic.have) {
+        // empty list: zeros and -inf, no copies in flight
+        const int qrow = q0 + l32;
+        uint16_t* Orow = static_cast<uint16_t*>(a.o) + h * a.o_hs + ((int64_t)i * BLK + qrow) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) *reinterpret_cast<uint2*>(Orow + dt * 32 + 8 * g + 4 * hi) = make_uint2(0u, 0u);
+        if (a.lse && hi == 0) a.lse[(int64_t)h * a.nqb * BLK + (int64_t)i * BLK + qrow] = -INFINITY;
+        return;
+    }
+    BlockCursor<BLK, DENSE> cc = ic;
+    auto issue = [&](uint16_t* stage, int sub) {
+        const int64_t off = ((int64_t)ic.j * BLK + sub * kSubKeys) * D;
         dma_sub<D, NW, false>(Kh + off, stage, wave, lane);
         dma_sub<D, NW, true>(Vh + off, stage + SUBE, wave, lane);
-        ic.advance();
-        ++issued;
     };
-    if (ic.have) issue(st0);
-    if (ic.have) issue(st1);
-    if (ic.have) issue(st2);
+    // prologue: slots 0, 1, 2
+    issue(st0, 0);
+    if (1 % SUBS == 0) ic.next();
+    issue(st1, 1 % SUBS);
+    if (2 % SUBS == 0) ic.next();
+    issue(st2, 2 % SUBS);
 
-    // per-lane LDS byte offsets (loop invariant): this wave's 32 keys start
-    // at row 32*kh of the stage
-    const int kr = 32 * kh + key_of_row(l32);
+    // per-lane LDS byte offsets (loop invariant)
+    const int kr = key_of_row(l32);
     int koff[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) koff[kk] = tile_off<D, false>(kr, 2 * kk + hi);
@@ -275,7 +283,7 @@ __global__ void __launch_bounds__(BLK * 4, 1) attn_bf16_kernel(AttnArgs a) {
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int h4 = 0; h4 < 2; ++h4) {
-                const int row = 32 * kh + 8 * hi + 4 * h4 + j4;  // + 16*s2
+                const int row = 8 * hi + 4 * h4 + j4;  // + 16*s2
                 const int col = dt * 32 + 16 * g2 + 4 * r4;
                 voff[dt][h4] = tile_off<D, true>(row, col >> 3) + ((col >> 2) & 1) * 8 + SUBE * 2;
             }
@@ -289,9 +297,8 @@ __global__ void __launch_bounds__(BLK * 4, 1) attn_bf16_kernel(AttnArgs a) {
     float m = -INFINITY, l = 0.f;
     const float c2 = a.scale_log2;
 
-    auto compute = [&](const uint16_t* stage) {
-        const int nv = cc.nvalid() - 32 * kh;  // valid keys of this wave's half (may be <= 0)
-        if (!active) return;
+    auto compute = [&](const uint16_t* stage, int nv) {
+        if (!active || nv <= 0) return;
         const char* base = reinterpret_cast<const char*>(stage);
         bf16x8_t kf[KK];
 #pragma unroll
@@ -307,14 +314,14 @@ __global__ void __launch_bounds__(BLK * 4, 1) attn_bf16_kernel(AttnArgs a) {
                     vr[s2][dt][h4] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (lds_s16x4_t*)((__attribute__((address_space(3))) char*)stage + voff[dt][h4] +
                                        s2 * 16 * D * 2));
-        // S^T = K Q^T over this wave's 32 keys: lane holds the scores of query
-        // q0 + l32 for keys 32*kh + 16*(r/8) + 8*hi + (r%8), r = 0..15.
+        // S^T = K Q^T over the stage's 32 keys: lane holds the scores of
+        // query q0 + l32 for keys 16*(r/8) + 8*hi + (r%8), r = 0..15.
         f32x16_t s;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-        if (nv < 32) {
+        if (nv < kSubKeys) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = 16 * (r >> 3) + 8 * hi + (r & 7);
@@ -340,8 +347,7 @@ __global__ void __launch_bounds__(BLK * 4, 1) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
         }
-        // before the first valid key the reference is -inf and every score
-        // is -inf: use 0 so those p are exactly 0
+        // padded query rows keep m = -inf: use 0 so their p stay finite
         const float mref = m == -INFINITY ? 0.f : m;
         float ls = 0.f;
         bf16x8_t pf[2];
@@ -352,7 +358,7 @@ __global__ void __launch_bounds__(BLK * 4, 1) attn_bf16_kernel(AttnArgs a) {
             pf[r >> 3][r & 7] = (__bf16)p;
         }
         l += ls;
-        // O^T += V^T P^T over this wave's keys; four independent chains (dt)
+        // O^T += V^T P^T; four independent chains (dt)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -363,66 +369,32 @@ __global__ void __launch_bounds__(BLK * 4, 1) attn_bf16_kernel(AttnArgs a) {
             }
     };
 
-    // Sub-tile t lives in stage t % 4; while it is multiplied, sub-tiles
-    // t+1 .. t+3 stream in.  The loop is unrolled over the four stages so
-    // every LDS access names one stage array (no false waits on the others).
-    auto step = [&](uint16_t* cur, uint16_t* nxt) {
-        const int later = issued - computed - 1;  // stages issued after this one
-        if (later >= 2)
-            wait_vmcnt<2 * NI>();
-        else if (later == 1)
-            wait_vmcnt<NI>();
-        else
-            wait_vmcnt<0>();
+    // Slot t (stage K = t % 4): wait for its copies, barrier, issue slot
+    // t + 3 into the stage freed by slot t - 1, multiply.  Unrolled over the
+    // four stages so stage arrays and sub-tile indices are compile-time.
+    auto step = [&](auto K_, uint16_t* cur, uint16_t* nxt) {
+        constexpr int K = decltype(K_)::value;
+        constexpr int SUB_C = K % SUBS, SUB_I = (K + 3) % SUBS;
+        wait_vmcnt<2 * NI>();
         lds_barrier();
-        if (ic.have) issue(nxt);
-        compute(cur);
-        cc.advance();
-        ++computed;
+        if (SUB_I == 0) ic.next();
+        issue(nxt, SUB_I);
+        compute(cur, cc.vk - SUB_C * kSubKeys);
+        if (SUB_C == SUBS - 1) cc.next();
     };
-    while (computed < issued) {
-        step(st0, st3);
-        if (computed >= issued) break;
-        step(st1, st0);
-        if (computed >= issued) break;
-        step(st2, st1);
-        if (computed >= issued) break;
-        step(st3, st2);
+    for (;;) {
+        step(std::integral_constant<int, 0>(), st0, st3);
+        if (!cc.have) break;
+        step(std::integral_constant<int, 1>(), st1, st0);
+        if (!cc.have) break;
+        step(std::integral_constant<int, 2>(), st2, st1);
+        if (!cc.have) break;
+        step(std::integral_constant<int, 3>(), st3, st2);
+        if (!cc.have) break;
     }
+    wait_vmcnt<0>();  // the copies past the end must land before the LDS is released
 
-    // merge the two key halves of each query group through LDS (the stage
-    // buffers are free: every issued copy was consumed by the loop)
-    constexpr int XF = 2 + 16 * DT;  // floats per lane: m, l, o
-    static_assert(QG <= kStages && XF * 64 * 4 <= 2 * SUBE * 2, "exchange buffer");
-    float* xch = reinterpret_cast<float*>(qg == 0 ? st0 : qg == 1 ? st1 : qg == 2 ? st2 : st3);
-    lds_barrier();
-    if (kh == 1) {
-        float* x = xch + lane;
-        x[0] = m;
-        x[64] = l;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) x[(2 + 16 * dt + r) * 64] = o[dt][r];
-    }
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    lds_barrier();
-    if (kh == 1) return;
-    {
-        const float* x = xch + lane;
-        const float mb = x[0], lb = x[64];
-        const float mm = fmaxf(m, mb);
-        const float fa = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
-        const float fb = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb - mm);
-        l = l * fa + lb * fb;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] = o[dt][r] * fa + x[(2 + 16 * dt + r) * 64] * fb;
-        m = mm;
-    }
-
-    // epilogue (kh == 0 waves)
+    // epilogue
     const float lt = add_halves(l);
     const int qrow = q0 + l32;
     const bool live = active && qrow < vq && lt > 0.f;
@@ -525,9 +497,9 @@ template <int BLK, int D>
 hipError_t launch_typed(const AttnArgs& args, int dtype, bool dense, int total, hipStream_t stream) {
     if (dtype == BSA_BF16) {
         if (dense)
-            hipLaunchKernelGGL((attn_bf16_kernel<BLK, D, true>), dim3(total), dim3(BLK * 4), 0, stream, args);
+            hipLaunchKernelGGL((attn_bf16_kernel<BLK, D, true>), dim3(total), dim3(BLK * 2), 0, stream, args);
         else
-            hipLaunchKernelGGL((attn_bf16_kernel<BLK, D, false>), dim3(total), dim3(BLK * 4), 0, stream, args);
+            hipLaunchKernelGGL((attn_bf16_kernel<BLK, D, false>), dim3(total), dim3(BLK * 2), 0, stream, args);
     } else {
         if (dense)
             hipLaunchKernelGGL((attn_f32_kernel<BLK, D, true>), dim3(total), dim3(BLK * (D / 32)), 0, stream, args);
