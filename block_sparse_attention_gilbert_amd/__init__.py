@@ -53,7 +53,7 @@ class RouteArgs(ctypes.Structure):
         ("lam", ctypes.c_double), ("g_ref", ctypes.c_double), ("tau", ctypes.c_double),
         ("k_fixed", _i), ("k_per_row", _p), ("k_max", _i),
         ("n_dense_tail_blocks", _i),
-        ("kpool", _p), ("kpool_valid_blocks", _i),
+        ("kpool", _p), ("kpool_valid_blocks", _i), ("kpool_head_blocks", _i),
         ("row_ptr", _p), ("col_idx", _p), ("col_capacity", _i64),
         ("fallback_counts", _p), ("sel_keys", _p),
     ]
@@ -211,7 +211,13 @@ def _route_args(q, k, *, block, nqb, nkb, q_block_len, kv_block_len, scale, over
     a.k_per_row = None if k_per_row is None else k_per_row.data_ptr()
     a.k_max = int(k_max) if k_max is not None else int(k_fixed)
     a.n_dense_tail_blocks = int(n_dense_tail_blocks)
-    a.kpool = None if kpool is None else kpool.data_ptr()
+    if kpool is not None:
+        if kpool.dtype != torch.float64 or kpool.dim() != 3 or kpool.shape[2] != d or kpool.stride(2) != 1 \
+                or kpool.stride(1) != d or kpool.stride(0) % d:
+            raise ValueError("kpool must be float64 [heads][blocks][d] with contiguous blocks")
+        if kpool.shape[0] != heads or kpool.shape[1] < nkb - n_dense_tail_blocks:
+            raise ValueError("kpool must hold heads x (nkb - n_dense_tail_blocks) pooled keys")
+        a.kpool, a.kpool_head_blocks = kpool.data_ptr(), kpool.stride(0) // d
     a.kpool_valid_blocks = int(kpool_valid_blocks)
     if row_ptr is not None:
         a.row_ptr, a.col_idx, a.col_capacity = row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel()

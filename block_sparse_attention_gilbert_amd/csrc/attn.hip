@@ -85,7 +85,6 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
 typedef const __attribute__((address_space(4))) int32_t const_i32_t;
 
 constexpr int kSubKeys = 32;  // keys per pipeline stage (sub-tile)
-constexpr int kStages = 4;    // LDS stages; kStages - 1 sub-tiles in flight
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
 
 // LDS sub-tile layout: kSubKeys rows of D bf16 (no padding), 16-byte chunks
@@ -107,24 +106,37 @@ __device__ __forceinline__ int tile_off(int row, int c) {
     return row * (D * 2) + ((c ^ swz<D, IS_V>(row)) << 4);
 }
 
-// Direct global -> LDS copy of one kSubKeys x D bf16 sub-tile into the
-// swizzled layout.  One 16-byte load per lane lands at base + 16 * lane, so
-// lane l of wave-instruction I fills row I * RPI + l / CPR, physical chunk
-// l % CPR, and fetches the logical chunk that belongs there.
+// Per-lane byte offsets of the direct global -> LDS copy of one
+// kSubKeys x D bf16 sub-tile into the swizzled layout.  One 16-byte buffer
+// load per lane lands at the LDS address in M0 + 16 * lane, so lane l of
+// wave-instruction I fills row I * RPI + l / CPR, physical chunk l % CPR, and
+// fetches the logical chunk that belongs there.  The offsets do not depend
+// on the block, so they are computed once.
 template <int D, int NW, bool IS_V>
-__device__ __forceinline__ void dma_sub(const uint16_t* __restrict__ g, uint16_t* lds_tile, int wave, int lane) {
+__device__ __forceinline__ uint32_t dma_lane_offset(int n, int wave, int lane) {
     constexpr int CPR = D / 8;
-    constexpr int RPI = 64 / CPR;                     // rows per wave-instruction (1 KB)
-    constexpr int NI = kSubKeys * D * 2 / 1024 / NW;  // instructions per wave
+    constexpr int RPI = 64 / CPR;  // rows per wave-instruction (1 KB)
+    const int I = n * NW + wave;
+    const int row = I * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ swz<D, IS_V>(row);
+    return (uint32_t)(row * D + c * 8) * 2u;
+}
+
+// Issue the copies of one sub-tile: NI wave-instructions, buffer resource =
+// the block, scalar offset = the sub-tile, vector offset = the lane's.
+template <int NI, int NW>
+__device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t rsrc, uint32_t sub_off, const uint32_t* voff,
+                                          uint16_t* lds_tile, int wave) {
 #pragma unroll
-    for (int n = 0; n < NI; ++n) {
-        const int I = n * NW + wave;
-        const int row = I * RPI + lane / CPR;
-        const int c = (lane % CPR) ^ swz<D, IS_V>(row);
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g + row * D + c * 8),
-                                         (__attribute__((address_space(3))) void*)((lds_u16_t*)lds_tile + I * 512),
-                                         16, 0, 0);
-    }
+    for (int n = 0; n < NI; ++n)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void*)((lds_u16_t*)lds_tile + (n * NW + wave) * 512), 16,
+            voff[n], sub_off, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t* base) {
+    // raw buffer, no stride; 0x00020000 = 32-bit data format (untyped loads)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, 0x7fffffff, 0x00020000);
 }
 
 // max over the two lanes l and l ^ 32 (which hold one query's two key halves)
@@ -142,7 +154,7 @@ __device__ __forceinline__ float add_halves(float x) {
 // (__syncthreads, or an LDS-scoped fence, since LDS-DMA writes are pending
 // LDS writes) makes the compiler drain every outstanding copy, including the
 // stages still streaming in.  Here each wave has already waited (vmcnt) for
-// its own copies of the stage about to be read, and every read of the stage
+// its own copies of the stages about to be read, and every read of the stages
 // about to be overwritten was consumed by an MFMA before the barrier, so a
 // bare s_barrier is enough; the empty asm statements only stop the compiler
 // from moving memory accesses across it.
@@ -160,52 +172,88 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Cursor over the listed blocks of a row: block j with vk valid keys,
-// skipping out-of-range entries and blocks without valid keys.  When the
-// list is exhausted `have` drops and j keeps the last valid block.
-template <int BLK, bool DENSE>
-struct BlockCursor {
-    int e, e1, j, vk;
-    bool have;
+// Reader of one row's list: returns the next in-range block index, or -1
+// when the list is exhausted.  The next entry is loaded one call ahead, so
+// the scalar load is long complete when it is used; out-of-range entries
+// take a slow path.
+template <bool DENSE>
+struct ListReader {
     const_i32_t* col;
-    const_i32_t* kvl;
-    int nkb;
-    __device__ __forceinline__ void next() {
-        for (; e < e1; ++e) {
-            const int jj = DENSE ? e : col[e];
-            if (jj < 0 || jj >= nkb) continue;
-            int v = kvl ? kvl[jj] : BLK;
-            v = v > BLK ? BLK : v;
-            if (v > 0) {
-                j = jj;
-                vk = v;
-                ++e;
-                have = true;
-                return;
+    int e, e1, nkb, pre;
+    __device__ __forceinline__ void init(const_i32_t* c, int e0_, int e1_, int nkb_) {
+        col = c;
+        e = e0_;
+        e1 = e1_;
+        nkb = nkb_;
+        pre = (!DENSE && e < e1) ? col[e] : 0;
+    }
+    __device__ __forceinline__ int next() {
+        if (DENSE) return e < e1 ? e++ : -1;
+        if (e >= e1) return -1;
+        int j = pre;
+        ++e;
+        pre = col[e < e1 ? e : e1 - 1];
+        if (__builtin_expect(j < 0 || j >= nkb, 0)) {
+            j = -1;
+            while (e < e1) {
+                const int jj = col[e++];
+                if (jj >= 0 && jj < nkb) {
+                    j = jj;
+                    break;
+                }
             }
+            pre = col[e < e1 ? e : e1 - 1];
         }
-        have = false;
+        return j;
     }
 };
 
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>());
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Scheduling fence: the compiler keeps the instruction order across it.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Workgroup of BLK/32 waves, one (head, query block); wave w owns query rows
-// 32w .. 32w+31 and every key.  Each 32-key stage is 2 x 8 KB (d = 128), so
-// a workgroup needs 64 KB of LDS and two workgroups share a CU: their
-// independent barriers let the hardware overlap one workgroup's softmax and
-// LDS latency with the other's matrix instructions.
+// 32w .. 32w+31 and every key.  Keys stream in sub-tiles of kSubKeys: slot t
+// is sub-tile t % SUBS of the t / SUBS-th listed block.  K and V have rings
+// of four 32-key sub-tiles each (2 x 32 KB at d = 128, so two workgroups
+// share a CU and overlap each other's softmax with their matrix work).
+//
+// Iteration t, after one barrier:
+//   copies      K of slot t+4 and V of slot t+3 are issued into the buffers
+//               freed by iteration t-1 (three sub-tiles of each in flight);
+//   phase A     S(t+1) = K(t+1) Q^T on the matrix cores while the vector
+//               units exponentiate slot t's scores into bf16 P(t);
+//   phase B     O^T += V(t)^T P(t)^T on the matrix cores while the vector
+//               units scale S(t+1) into base-2 logits, take its row maximum
+//               and add P(t) into the running row sums.
+// The running reference max per query moves only when a sub-tile's maximum
+// passes it by more than kRescaleSlack (a rare, wave-uniform branch), so
+// p <= 2^slack and each query's arithmetic depends on its own scores only.
 template <int BLK, int D, bool DENSE>
 __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
-    constexpr int NW = BLK / 32;               // waves
+    constexpr int NW = BLK / 32;  // waves
     constexpr int DT = D / 32, KK = D / 16;
-    constexpr int SUBE = kSubKeys * D;         // elements of a K or V sub-tile
-    constexpr int NI = 2 * (kSubKeys * D * 2 / 1024 / NW);  // DMA instructions per wave per stage
-    static_assert(kSubKeys * D * 2 % (1024 * NW) == 0, "stage copy must split evenly over the waves");
-    __shared__ __attribute__((aligned(1024))) uint16_t st0[2 * SUBE];
-    __shared__ __attribute__((aligned(1024))) uint16_t st1[2 * SUBE];
-    __shared__ __attribute__((aligned(1024))) uint16_t st2[2 * SUBE];
-    __shared__ __attribute__((aligned(1024))) uint16_t st3[2 * SUBE];
+    constexpr int SUBE = kSubKeys * D;     // elements of a K or V sub-tile
+    constexpr int SUBS = BLK / kSubKeys;   // sub-tiles per block
+    constexpr int NI = kSubKeys * D * 2 / 1024 / NW;  // copy instructions per wave per sub-tile
+    constexpr int LAG = 3 / SUBS;          // blocks between the K-copy cursor and slot t+1
+    static_assert(kSubKeys * D * 2 % (1024 * NW) == 0, "sub-tile copy must split evenly over the waves");
+    static_assert(4 % SUBS == 0, "the four-slot unroll must hold whole blocks");
+    __shared__ __attribute__((aligned(1024))) uint16_t kb0[SUBE], kb1[SUBE], kb2[SUBE], kb3[SUBE];
+    __shared__ __attribute__((aligned(1024))) uint16_t vb0[SUBE], vb1[SUBE], vb2[SUBE], vb3[SUBE];
+    uint16_t* const KB[4] = {kb0, kb1, kb2, kb3};
+    uint16_t* const VB[4] = {vb0, vb1, vb2, vb3};
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, l32 = lane & 31, g16 = lane & 15;
     int h, i;
     map_item(a.heads * a.nqb, a.nqb, h, i);
@@ -239,15 +287,15 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         e0 = e0 < 0 ? 0 : e0;
         e1 = e1 > a.col_len ? (int)a.col_len : e1;
     }
-    // Every listed block is SUBS stages of kSubKeys keys; slot t is stage
-    // t % 4, sub-tile t % SUBS of block t / SUBS.  Three slots are always in
-    // flight: past the end of the list the copies repeat the last block
-    // (never computed), so every wait is the same vmcnt.
-    constexpr int SUBS = BLK / kSubKeys;
-    static_assert(kStages % SUBS == 0, "stages must hold whole blocks");
-    BlockCursor<BLK, DENSE> ic{e0, e1, 0, 0, false, (const_i32_t*)a.col_idx, (const_i32_t*)a.kv_len, a.nkb};
-    ic.next();
-    if (!ic.have) {
+    const_i32_t* kvl = (const_i32_t*)a.kv_len;
+    ListReader<DENSE> list;
+    list.init((const_i32_t*)a.col_idx, e0, e1, a.nkb);
+
+    // K-copy cursor: block jk; the blocks it has entered are published to a
+    // two-deep history (j, valid keys; -1 keys past the end) that the V-copy
+    // cursor (same block) and the compute cursor (LAG blocks behind) read.
+    int jk = list.next();
+    if (jk < 0) {
         // empty list: zeros and -inf, no copies in flight
         const int qrow = q0 + l32;
         uint16_t* Orow = static_cast<uint16_t*>(a.o) + h * a.o_hs + ((int64_t)i * BLK + qrow) * D;
@@ -258,18 +306,46 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         if (a.lse && hi == 0) a.lse[(int64_t)h * a.nqb * BLK + (int64_t)i * BLK + qrow] = -INFINITY;
         return;
     }
-    BlockCursor<BLK, DENSE> cc = ic;
-    auto issue = [&](uint16_t* stage, int sub) {
-        const int64_t off = ((int64_t)ic.j * BLK + sub * kSubKeys) * D;
-        dma_sub<D, NW, false>(Kh + off, stage, wave, lane);
-        dma_sub<D, NW, true>(Vh + off, stage + SUBE, wave, lane);
+    int h0j = jk, h0v = kvl ? kvl[jk] : BLK, h1v = 0;
+    bool h0end = false, h1end = true;
+    auto k_advance = [&]() __attribute__((always_inline)) {
+        h1v = h0v;
+        h1end = h0end;
+        const int nj = h0end ? -1 : list.next();
+        if (nj >= 0) {
+            jk = nj;
+            h0v = kvl ? kvl[nj] : BLK;
+        } else {
+            h0end = true;  // copies past the end repeat the last block (never computed)
+        }
+        h0j = jk;
     };
-    // prologue: slots 0, 1, 2
-    issue(st0, 0);
-    if (1 % SUBS == 0) ic.next();
-    issue(st1, 1 % SUBS);
-    if (2 % SUBS == 0) ic.next();
-    issue(st2, 2 % SUBS);
+    int jv = jk;
+
+    uint32_t koffs[NI], voffs[NI];
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+        koffs[n] = dma_lane_offset<D, NW, false>(n, wave, lane);
+        voffs[n] = dma_lane_offset<D, NW, true>(n, wave, lane);
+    }
+    constexpr uint32_t kSubBytes = kSubKeys * D * 2;
+    auto issue_k = [&](int buf, int sub) __attribute__((always_inline)) {
+        dma_issue<NI, NW>(block_rsrc(Kh + (int64_t)jk * BLK * D), sub * kSubBytes, koffs, KB[buf], wave);
+    };
+    auto issue_v = [&](int buf, int sub) __attribute__((always_inline)) {
+        dma_issue<NI, NW>(block_rsrc(Vh + (int64_t)jv * BLK * D), sub * kSubBytes, voffs, VB[buf], wave);
+    };
+
+    // prologue: K of slots 0..3, V of slots 0..2
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        if (s > 0 && s % SUBS == 0) k_advance();
+        issue_k(s, s % SUBS);
+        if (s < 3) {
+            if (s % SUBS == 0) jv = h0j;
+            issue_v(s, s % SUBS);
+        }
+    }
 
     // per-lane LDS byte offsets (loop invariant)
     const int kr = key_of_row(l32);
@@ -285,7 +361,7 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
             for (int h4 = 0; h4 < 2; ++h4) {
                 const int row = 8 * hi + 4 * h4 + j4;  // + 16*s2
                 const int col = dt * 32 + 16 * g2 + 4 * r4;
-                voff[dt][h4] = tile_off<D, true>(row, col >> 3) + ((col >> 2) & 1) * 8 + SUBE * 2;
+                voff[dt][h4] = tile_off<D, true>(row, col >> 3) + ((col >> 2) & 1) * 8;
             }
     }
 
@@ -294,17 +370,33 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-    float m = -INFINITY, l = 0.f;
+    float ref = 0.f, l = 0.f;  // reference max (base-2 logit units) and partial row sum
+    bool ref_set = false;
     const float c2 = a.scale_log2;
+    f32x16_t xc;  // base-2 logits of slot t relative to ref
 
-    auto compute = [&](const uint16_t* stage, int nv) {
-        if (!active || nv <= 0) return;
-        const char* base = reinterpret_cast<const char*>(stage);
+    auto scores = [&](const uint16_t* kbuf) __attribute__((always_inline)) {
+        const char* base = reinterpret_cast<const char*>(kbuf);
         bf16x8_t kf[KK];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
             kf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(base + koff[kk]));
-        s16x4_t vr[2][DT][2];
+        f32x16_t s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+        return s;
+    };
+    // lane holds keys 16*(r/8) + 8*hi + (r%8) of the sub-tile
+    auto mask = [&](f32x16_t& s, int nv) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = 16 * (r >> 3) + 8 * hi + (r & 7);
+            if (key >= nv) s[r] = -INFINITY;
+        }
+    };
+    auto load_v = [&](const uint16_t* vbuf, s16x4_t (&vr)[2][DT][2]) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -312,53 +404,21 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
                 for (int h4 = 0; h4 < 2; ++h4)
                     vr[s2][dt][h4] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4_t*)((__attribute__((address_space(3))) char*)stage + voff[dt][h4] +
+                        (lds_s16x4_t*)((__attribute__((address_space(3))) char*)vbuf + voff[dt][h4] +
                                        s2 * 16 * D * 2));
-        // S^T = K Q^T over the stage's 32 keys: lane holds the scores of
-        // query q0 + l32 for keys 16*(r/8) + 8*hi + (r%8), r = 0..15.
-        f32x16_t s;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-        if (nv < kSubKeys) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = 16 * (r >> 3) + 8 * hi + (r & 7);
-                if (key >= nv) s[r] = -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        mx = max_halves(mx) * c2;
-        // lazy rescaling: a query's reference max moves only when its own
-        // max passes it by more than kRescaleSlack (so p <= 2^slack); each
-        // query's arithmetic depends on its own scores only.  Padded query
-        // rows never move it (their results are discarded).
-        const bool need = valid_row && mx > m + kRescaleSlack;
-        if (__any(need)) {
-            const float mn = need ? mx : m;
-            const float alpha = need ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
-            m = mn;
-            l *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-        }
-        // padded query rows keep m = -inf: use 0 so their p stay finite
-        const float mref = m == -INFINITY ? 0.f : m;
+    };
+    // bf16 P of slot t and its fp32 row sum
+    auto exp_p = [&](bf16x8_t (&pf)[2]) __attribute__((always_inline)) {
         float ls = 0.f;
-        bf16x8_t pf[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -mref));
+            const float p = __builtin_amdgcn_exp2f(xc[r]);
             ls += p;
             pf[r >> 3][r & 7] = (__bf16)p;
         }
         l += ls;
-        // O^T += V^T P^T; four independent chains (dt)
+    };
+    auto pv = [&](const s16x4_t (&vr)[2][DT][2], const bf16x8_t (&pf)[2]) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -368,36 +428,203 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s2], o[dt], 0, 0, 0);
             }
     };
+    // scale raw scores into logits relative to ref and take the pair max;
+    // then move ref (rare, wave-uniform branch) where the sub-tile's maximum
+    // passes it by more than the slack, or first sets it
+    float mx = -INFINITY;
+    auto logits_scale = [&](const f32x16_t& s) __attribute__((always_inline)) {
+        float m3 = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            xc[r] = fmaf(s[r], c2, -ref);
+            m3 = fmaxf(m3, xc[r]);
+        }
+        mx = max_halves(m3);
+    };
+    auto logits_check = [&]() __attribute__((always_inline)) {
+        const float thr = ref_set ? kRescaleSlack : -INFINITY;
+        const bool need = valid_row & (mx > thr);
+        if (__any(need)) {
+            const float shift = need ? mx : 0.f;
+            const float alpha = (need && ref_set) ? __builtin_amdgcn_exp2f(-shift) : 1.0f;
+            ref += shift;
+            ref_set = ref_set || need;
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xc[r] -= shift;
+        }
+    };
 
-    // Slot t (stage K = t % 4): wait for its copies, barrier, issue slot
-    // t + 3 into the stage freed by slot t - 1, multiply.  Unrolled over the
-    // four stages so stage arrays and sub-tile indices are compile-time.
-    auto step = [&](auto K_, uint16_t* cur, uint16_t* nxt) {
+    // slot 0: wait for its K copy, scores, first reference
+    wait_vmcnt<6 * NI>();
+    lds_barrier();
+    int cvk = LAG == 0 ? h0v : h1v;  // valid keys of the block of slot t+1 (unclamped)
+    if (active) {
+        f32x16_t s = scores(KB[0]);
+        if (cvk < kSubKeys) mask(s, cvk);
+        logits_scale(s);
+        logits_check();
+    }
+
+    // Iteration t (K = t % 4): the body reads K slot t+1 from buffer
+    // (K+1) % 4 and V slot t from buffer K, and refills buffer K with K slot
+    // t+4 and buffer (K+3) % 4 with V slot t+3.  Returns false when slot t+1
+    // does not exist; slot t is then finished by the tail.
+    // One iteration's math, in fenced segments so that each matrix
+    // instruction is issued beside vector work that does not depend on it:
+    //   phase A  KK segments, each: K fragment read three ahead, two V reads,
+    //            one S(t+1) MFMA, a share of slot t's exponentials (list A);
+    //   phase B  KK segments, each: one PV(t) MFMA and a share of list B
+    //            (second half of P(t) to bf16, the row sum of P(t), slot
+    //            t+1's logits and running maximum).
+    // Between the phases, keys >= nv of slot t+1 are masked (a rare,
+    // wave-uniform branch: only a block's last, partly valid sub-tiles).
+    auto body = [&](const uint16_t* kbuf, const uint16_t* vbuf, int nv) __attribute__((always_inline)) {
+        constexpr int KD = 3;                       // K fragment read distance
+        constexpr int VPS = 4 * DT / KK;            // V reads per phase-A segment
+        constexpr int NA = 16 + 4;                  // list A: 16 exp2, 4 packs of P[0..7]
+        constexpr int NB = 4 + 16 + 24;              // list B
+        const char* kb = reinterpret_cast<const char*>(kbuf);
+        bf16x8_t kf[KK];
+        s16x4_t vr[2][DT][2];
+        float p[16];
+        bf16x8_t pf[2];
+        f32x16_t sn;
+        float m3 = -INFINITY, ls = 0.f;
+        auto rdk = [&](int kk) __attribute__((always_inline)) {
+            kf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kb + koff[kk]));
+        };
+        auto rdv = [&](int idx) __attribute__((always_inline)) {
+            const int s2 = idx / (2 * DT), dt = (idx / 2) % DT, h4 = idx % 2;
+            vr[s2][dt][h4] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_t*)((__attribute__((address_space(3))) char*)vbuf + voff[dt][h4] + s2 * 16 * D * 2));
+        };
+        // list A: exp2 of keys 0..7, pack them, exp2 of keys 8..15
+        auto opA = [&](auto I_) __attribute__((always_inline)) {
+            constexpr int I = decltype(I_)::value;
+            if constexpr (I < 8) {
+                p[I] = __builtin_amdgcn_exp2f(xc[I]);
+            } else if constexpr (I < 12) {
+                constexpr int e = 2 * (I - 8);
+                pf[0][e] = (__bf16)p[e];
+                pf[0][e + 1] = (__bf16)p[e + 1];
+            } else {
+                p[I - 4] = __builtin_amdgcn_exp2f(xc[I - 4]);
+            }
+        };
+        // list B: pack keys 8..15, row sum, logits + maximum
+        auto opB = [&](auto I_) __attribute__((always_inline)) {
+            constexpr int I = decltype(I_)::value;
+            if constexpr (I < 4) {
+                constexpr int e = 2 * I;
+                pf[1][e] = (__bf16)p[8 + e];
+                pf[1][e + 1] = (__bf16)p[9 + e];
+            } else if constexpr (I < 20) {
+                ls += p[I - 4];
+            } else {
+                constexpr int q = I - 20, k = q / 3;
+                if constexpr (q % 3 == 0) {
+                    xc[2 * k] = fmaf(sn[2 * k], c2, -ref);
+                } else if constexpr (q % 3 == 1) {
+                    xc[2 * k + 1] = fmaf(sn[2 * k + 1], c2, -ref);
+                } else {
+                    m3 = fmaxf(m3, fmaxf(xc[2 * k], xc[2 * k + 1]));
+                }
+            }
+        };
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sn[r] = 0.f;
+        // phase A (a few exponentials first, to cover the first K read)
+        constexpr int NA0 = 4;
+#pragma unroll
+        for (int n = 0; n < KD; ++n) rdk(n);
+        static_for<0, NA0>(opA);
+        sched_fence();
+        static_for<0, KK>([&](auto N_) __attribute__((always_inline)) {
+            constexpr int n = decltype(N_)::value;
+            if constexpr (n + KD < KK) rdk(n + KD);
+#pragma unroll
+            for (int v = 0; v < VPS; ++v) rdv(n * VPS + v);
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[n], qf[n], sn, 0, 0, 0);
+            static_for<NA0 + n * (NA - NA0) / KK, NA0 + (n + 1) * (NA - NA0) / KK>(opA);
+            sched_fence();
+        });
+        // keep phase A's results here: without these uses the compiler sinks
+        // the exponentials past the branch below, out of phase A
+        __asm__ volatile("" ::"v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]),
+                         "v"(p[7]), "v"(p[8]), "v"(p[9]), "v"(p[10]), "v"(p[11]), "v"(p[12]), "v"(p[13]),
+                         "v"(p[14]), "v"(p[15]));
+        __asm__ volatile("" ::"v"(pf[0]));
+        if (nv < kSubKeys) mask(sn, nv);
+        // phase B
+        static_for<0, KK>([&](auto N_) __attribute__((always_inline)) {
+            constexpr int n = decltype(N_)::value;
+            constexpr int s2 = n / DT, dt = n % DT;
+            const bf16x8_t vf = __builtin_bit_cast(
+                bf16x8_t, __builtin_shufflevector(vr[s2][dt][0], vr[s2][dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s2], o[dt], 0, 0, 0);
+            static_for<n * NB / KK, (n + 1) * NB / KK>(opB);
+            sched_fence();
+        });
+        __asm__ volatile("" ::"v"(ls), "v"(m3));
+        l += ls;
+        mx = max_halves(m3);
+        logits_check();
+    };
+    auto step = [&](auto K_) __attribute__((always_inline)) -> bool {
         constexpr int K = decltype(K_)::value;
-        constexpr int SUB_C = K % SUBS, SUB_I = (K + 3) % SUBS;
-        wait_vmcnt<2 * NI>();
+        constexpr int SUB_K = (K + 4) % SUBS, SUB_V = (K + 3) % SUBS, SUB_N = (K + 1) % SUBS;
+        wait_vmcnt<4 * NI>();
         lds_barrier();
-        if (SUB_I == 0) ic.next();
-        issue(nxt, SUB_I);
-        compute(cur, cc.vk - SUB_C * kSubKeys);
-        if (SUB_C == SUBS - 1) cc.next();
+        if (SUB_K == 0) k_advance();
+        issue_k(K, SUB_K);
+        if (SUB_V == 0) jv = h0j;
+        issue_v((K + 3) % 4, SUB_V);
+        if (SUB_N == 0) {
+            cvk = LAG == 0 ? h0v : h1v;
+            if (LAG == 0 ? h0end : h1end) return false;
+        }
+        if (active) body(KB[(K + 1) % 4], VB[K], cvk - SUB_N * kSubKeys);
+        return true;
+    };
+    auto tail = [&](auto K_) __attribute__((always_inline)) {
+        constexpr int K = decltype(K_)::value;
+        if (active) {
+            s16x4_t vr[2][DT][2];
+            load_v(VB[K], vr);
+            bf16x8_t pf[2];
+            exp_p(pf);
+            pv(vr, pf);
+        }
     };
     for (;;) {
-        step(std::integral_constant<int, 0>(), st0, st3);
-        if (!cc.have) break;
-        step(std::integral_constant<int, 1>(), st1, st0);
-        if (!cc.have) break;
-        step(std::integral_constant<int, 2>(), st2, st1);
-        if (!cc.have) break;
-        step(std::integral_constant<int, 3>(), st3, st2);
-        if (!cc.have) break;
+        if (!step(std::integral_constant<int, 0>())) {
+            tail(std::integral_constant<int, 0>());
+            break;
+        }
+        if (!step(std::integral_constant<int, 1>())) {
+            tail(std::integral_constant<int, 1>());
+            break;
+        }
+        if (!step(std::integral_constant<int, 2>())) {
+            tail(std::integral_constant<int, 2>());
+            break;
+        }
+        if (!step(std::integral_constant<int, 3>())) {
+            tail(std::integral_constant<int, 3>());
+            break;
+        }
     }
     wait_vmcnt<0>();  // the copies past the end must land before the LDS is released
 
     // epilogue
     const float lt = add_halves(l);
     const int qrow = q0 + l32;
-    const bool live = active && qrow < vq && lt > 0.f;
+    const bool live = active && valid_row && lt > 0.f;
     const float inv = live ? 1.f / lt : 0.f;
     uint16_t* Orow = static_cast<uint16_t*>(a.o) + h * a.o_hs + ((int64_t)i * BLK + qrow) * D;
 #pragma unroll
@@ -414,7 +641,7 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
             *reinterpret_cast<uint2*>(Orow + dv) = packed;
         }
     if (a.lse && hi == 0)
-        a.lse[(int64_t)h * a.nqb * BLK + (int64_t)i * BLK + qrow] = live ? (m + log2f(lt)) * kLn2 : -INFINITY;
+        a.lse[(int64_t)h * a.nqb * BLK + (int64_t)i * BLK + qrow] = live ? (ref + log2f(lt)) * kLn2 : -INFINITY;
 }
 
 // fp32 path: D/32 threads per query row, each owning 32 channels of q and

@@ -393,6 +393,7 @@ hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* w
     double* qbar = reinterpret_cast<double*>(w + lay.qbar);
     const int n_cand = lay.n_cand;
     double* kbar = lay.kbar_in_ws ? reinterpret_cast<double*>(w + lay.kbar) : a->kpool;
+    const int64_t kbar_head_blocks = (!lay.kbar_in_ws && a->kpool_head_blocks > 0) ? a->kpool_head_blocks : n_cand;
     double* keys = lay.keys_in_ws ? reinterpret_cast<double*>(w + lay.keys) : a->sel_keys;
     int32_t* keff = reinterpret_cast<int32_t*>(w + lay.keff);
     int32_t* flags = reinterpret_cast<int32_t*>(w + lay.flags);
@@ -415,10 +416,10 @@ hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* w
         dim3 grid((nb + 3) / 4, a->heads);
         if (bf16)
             hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kThreads), 0, stream, a->k, a->k_head_stride, a->d,
-                               a->block, a->kv_block_len, kb0, nb, kbar, (int64_t)n_cand);
+                               a->block, a->kv_block_len, kb0, nb, kbar, kbar_head_blocks);
         else
             hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kThreads), 0, stream, a->k, a->k_head_stride, a->d,
-                               a->block, a->kv_block_len, kb0, nb, kbar, (int64_t)n_cand);
+                               a->block, a->kv_block_len, kb0, nb, kbar, kbar_head_blocks);
     }
     // 3. overlap row flags (for the fallback counts)
     const bool want_flags = a->overlap && a->fallback_counts && n_cand > 0;
@@ -428,7 +429,7 @@ hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* w
     // 4. selection keys
     if (n_cand > 0) {
         dim3 grid((n_cand + kScoreJ - 1) / kScoreJ, a->heads);
-        hipLaunchKernelGGL(score_kernel, grid, dim3(kThreads), 0, stream, qbar, kbar, (int64_t)n_cand, a->nqb,
+        hipLaunchKernelGGL(score_kernel, grid, dim3(kThreads), 0, stream, qbar, kbar, kbar_head_blocks, a->nqb,
                            n_cand, a->d, a->scale, a->overlap, a->overlap_row_stride, a->lambda, a->g_ref, a->tau,
                            keys);
     }

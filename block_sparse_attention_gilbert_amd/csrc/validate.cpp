@@ -153,6 +153,8 @@ int validate_route(const bsa_route_args* a, RouteLayout* lay) {
     if (kcap > n_cand) kcap = n_cand;
     if (a->kpool && (a->kpool_valid_blocks < 0 || a->kpool_valid_blocks > n_cand))
         return fail(BSA_EINVAL, "kpool_valid_blocks %d outside [0, %d]", a->kpool_valid_blocks, n_cand);
+    if (a->kpool && a->kpool_head_blocks != 0 && a->kpool_head_blocks < n_cand)
+        return fail(BSA_EINVAL, "kpool_head_blocks %d below the candidate count %d", a->kpool_head_blocks, n_cand);
     const int64_t need = (int64_t)a->heads * a->nqb * ((int64_t)kcap + a->n_dense_tail_blocks);
     if (a->col_capacity < need)
         return fail(BSA_EINVAL, "col_capacity %lld < heads*nqb*(k cap + dense tail) = %lld",

@@ -12,7 +12,10 @@ Per call (``RoutedAttention.step``):
 2. Q, K, V of the current chunk, raster token-major ``[L][heads][d]``, are
    permuted into Gilbert head-major block-padded layout; K and V land in the
    current chunk's slot of the KV store (the store grows by appending);
-3. the router pools, scores, fuses and selects over the visible history;
+3. the router pools, scores, fuses and selects over the visible history.
+   The pooled keys of the history are kept in a float64 cache across calls
+   (the store only grows by appending), so a call pools only the blocks
+   appended or rewritten since the previous call;
 4. block-sparse attention over the selected blocks;
 5. O is permuted back to raster order.
 
@@ -43,7 +46,8 @@ class RoutedAttention:
 
     def __init__(self, grid, heads: int, d: int, block: int, store_chunks: int, dtype=torch.bfloat16,
                  device="cuda", k_cap: int = 50, n_dense_tail_chunks: int = 0,
-                 k_store: Optional[torch.Tensor] = None, v_store: Optional[torch.Tensor] = None):
+                 k_store: Optional[torch.Tensor] = None, v_store: Optional[torch.Tensor] = None,
+                 use_kpool: bool = True):
         self.grid = tuple(grid)
         self.L = grid[0] * grid[1] * grid[2]
         self.heads, self.d, self.block, self.dtype, self.device = heads, d, block, dtype, device
@@ -73,6 +77,16 @@ class RoutedAttention:
             "sel_keys": None,
         }
         self.workspace = None
+        # pooled-key cache: blocks < _kpool_valid hold the means of the
+        # store's current contents
+        self.use_kpool = use_kpool
+        self.kpool = torch.empty((heads, nkb_max, d), dtype=torch.float64, device=device) if use_kpool else None
+        self._kpool_valid = 0
+
+    def invalidate_kpool(self, first_block: int = 0):
+        """Forget cached pooled keys from ``first_block`` on (call after
+        writing the store other than through ``append``)."""
+        self._kpool_valid = min(self._kpool_valid, max(0, int(first_block)))
 
     def slot(self, c: int):
         """K and V views of chunk ``c``'s slot of the store."""
@@ -82,6 +96,7 @@ class RoutedAttention:
     def append(self, k_raster, v_raster, c: int, stream=None):
         """Permute a chunk's raster K and V into slot ``c`` of the store."""
         ks, vs = self.slot(c)
+        self.invalidate_kpool(c * self.nbc)
         gilbert_perm(k_raster, self.perm, block=self.block, dst=ks, stream=stream)
         gilbert_perm(v_raster, self.perm, block=self.block, dst=vs, stream=stream)
 
@@ -110,12 +125,17 @@ class RoutedAttention:
         k_hist, v_hist = self.k_store[:, : nkb * self.block], self.v_store[:, : nkb * self.block]
         tail = self.n_dense_tail_chunks * self.nbc
         kf = self.k_cap if k_fixed is None else k_fixed
+        n_cand = nkb - tail
+        valid = min(self._kpool_valid, n_cand)
         r = route_topk(self.q_blk, k_hist, block=self.block, nqb=self.nbc, nkb=nkb, scale=self.scale,
                        q_block_len=self.q_len, kv_block_len=self.kv_len[:nkb], overlap=overlap, lam=lam,
                        g_ref=g_ref, tau=tau, k_fixed=kf, k_per_row=k_per_row,
                        k_max=self.k_cap if k_per_row is not None else None, n_dense_tail_blocks=tail,
+                       kpool=self.kpool, kpool_valid_blocks=valid if self.use_kpool else 0,
                        out=self.route_out, workspace=self.workspace, stream=stream)
         self.workspace = r["workspace"]
+        if self.use_kpool:
+            self._kpool_valid = max(valid, n_cand)
         if attn_events is not None:
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             ev[0].record(stream)

@@ -139,11 +139,16 @@ int bsa_gilbert_perm(const void* src, void* dst, const int32_t* perm, int L, int
  *                 candidates; every non-empty list ends with those of them
  *                 that hold a valid token (the current chunk, attended
  *                 densely).  Candidates are blocks 0 .. nkb-n_dense_tail-1.
- *  kpool          float64[heads][n_candidates][d] pooled-key cache (NULL:
- *                 pool every candidate into the workspace).  Blocks
+ *  kpool          float64[heads][kpool_head_blocks][d] pooled-key cache
+ *                 (NULL: pool every candidate into the workspace).  Blocks
  *                 < kpool_valid_blocks are taken from the cache as they
  *                 are; blocks >= kpool_valid_blocks are pooled and written
- *                 into it.
+ *                 into it.  A KV history only grows by appending, so a
+ *                 caller keeps the cache across calls and pools only the
+ *                 blocks appended (or rewritten) since the last call.
+ *  kpool_head_blocks  blocks per head of the cache (its head stride is
+ *                 kpool_head_blocks*d); 0 means n_candidates.  Must be 0 or
+ *                 >= n_candidates, so one cache can serve a growing history.
  * Outputs (device):
  *  row_ptr        int32[heads*nqb + 1]; row r = h*nqb + i.
  *  col_idx        int32[col_capacity]; row r's list is col_idx[row_ptr[r] ..
@@ -189,6 +194,7 @@ typedef struct bsa_route_args {
     int n_dense_tail_blocks;
     double* kpool;
     int kpool_valid_blocks;
+    int kpool_head_blocks;
     int32_t* row_ptr;
     int32_t* col_idx;
     int64_t col_capacity;

@@ -136,6 +136,8 @@ def test_route_rejects_and_sizes():
                               FAKE, need, None) == bsa.BSA_EINVAL
     assert lib.bsa_route_topk(ctypes.byref(_route_args(kpool=0x60000, kpool_valid_blocks=1777)), FAKE, need,
                               None) == bsa.BSA_EINVAL
+    assert lib.bsa_route_topk(ctypes.byref(_route_args(kpool=0x60000, kpool_head_blocks=1775)), FAKE, need,
+                              None) == bsa.BSA_EINVAL
     assert lib.bsa_route_topk(ctypes.byref(_route_args(k_per_row=0x70000, k_max=-1)), FAKE, need, None) \
         == bsa.BSA_EINVAL
     # kpool and sel_keys shrink the workspace

@@ -126,6 +126,31 @@ def test_pooled_key_cache_incremental():
         assert np.array_equal(cache[h].cpu().numpy(), ref["kbar"])   # exact block means
 
 
+def test_pooled_key_cache_grows_with_history():
+    """One cache with a fixed head stride serves a history that grows by a
+    chunk per call: each call pools only the appended chunk."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    w = workloads.c4(c=3, heads=[0, 1, 2])
+    ql = torch.from_numpy(w.q_len).to(dev)
+    kl = torch.from_numpy(w.k_len).to(dev)
+    q, k = w.q.to(dev), w.k.to(dev)
+    cache = torch.full((w.heads, 5 * 37, w.d), float("nan"), dtype=torch.float64, device=dev)  # room for 5 chunks
+    valid = 0
+    for c in (1, 2, 3):
+        nkb = 37 * c
+        r = bsa.route_topk(q, k, block=128, nqb=37, nkb=nkb, scale=w.scale, q_block_len=ql, kv_block_len=kl[:nkb],
+                           k_fixed=50, kpool=cache, kpool_valid_blocks=valid)
+        valid = nkb
+        lists = csr_lists(r["row_ptr"], r["col_idx"], w.heads, 37)
+        for h in range(w.heads):
+            ref = oroute.route_head(f64(w.q[h]), f64(w.k[h])[: nkb * 128], w.q_len, w.k_len[:nkb], w.bs,
+                                    scale=w.scale, k_per_row=w.k_per_row[:37])
+            assert_lists_equal(lists[h], ref["lists"], "growing cache c=%d head %d" % (c, h))
+            assert np.array_equal(cache[h, :nkb].cpu().numpy(), ref["kbar"])
+    assert torch.isnan(cache[:, 111:]).all()   # nothing written past the history
+
+
 def test_route_edge_cases():
     dev = need_gpu()
     import block_sparse_attention_gilbert_amd as bsa
