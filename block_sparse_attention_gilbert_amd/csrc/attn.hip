@@ -122,8 +122,10 @@ __device__ __forceinline__ uint32_t dma_lane_offset(int n, int wave, int lane) {
     return (uint32_t)(row * D + c * 8) * 2u;
 }
 
-// Issue the copies of one sub-tile: NI wave-instructions, buffer resource =
-// the block, scalar offset = the sub-tile, vector offset = the lane's.
+// Issue the copies of one sub-tile: NI wave-instructions; buffer resource =
+// the block, bounded to its valid rows; scalar offset = the sub-tile, vector
+// offset = the lane's.  The bound applies to the whole offset (scalar +
+// vector): rows past it are not fetched and land in LDS as zeros.
 template <int NI, int NW>
 __device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t rsrc, uint32_t sub_off, const uint32_t* voff,
                                           uint16_t* lds_tile, int wave) {
@@ -134,15 +136,28 @@ __device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
             voff[n], sub_off, 0, 0);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t* base) {
-    // raw buffer, no stride; 0x00020000 = 32-bit data format (untyped loads)
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, 0x7fffffff, 0x00020000);
+// Raw buffer (no stride) over nbytes from base; 0x00020000 = 32-bit data
+// format (untyped loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t* base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, (int)nbytes, 0x00020000);
+}
+
+// Plain v_max3_f32 / v_max_f32.  fmaxf must quiet signalling NaNs, so the
+// compiler canonicalises both inputs first (two extra instructions per
+// maximum); the scores here are MFMA and FMA results (never signalling), so
+// the bare instructions give the same maxima.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+    float r;
+    __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
 }
 
 // max over the two lanes l and l ^ 32 (which hold one query's two key halves)
 __device__ __forceinline__ float max_halves(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    float m;
+    __asm__("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+    return m;
 }
 
 __device__ __forceinline__ float add_halves(float x) {
@@ -306,17 +321,26 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         if (a.lse && hi == 0) a.lse[(int64_t)h * a.nqb * BLK + (int64_t)i * BLK + qrow] = -INFINITY;
         return;
     }
-    int h0j = jk, h0v = kvl ? kvl[jk] : BLK, h1v = 0;
-    bool h0end = false, h1end = true;
+    // valid keys of a block, clamped to [0, BLK]; readfirstlane keeps the
+    // clamp (a VALU med3) from making the copy bounds look divergent
+    auto block_keys = [&](int j) __attribute__((always_inline)) {
+        if (!kvl) return BLK;
+        const int v = kvl[j];
+        return __builtin_amdgcn_readfirstlane(v < 0 ? 0 : (v > BLK ? BLK : v));
+    };
+    int h0j = jk, h0v = block_keys(jk), h1v = 0;
+    int kvk = 0, vvk = 0;  // valid keys of the blocks being copied (0 past the end)
+    int h0end = 0, h1end = 1;  // ints, not bools: kept in scalar registers
     auto k_advance = [&]() __attribute__((always_inline)) {
         h1v = h0v;
         h1end = h0end;
         const int nj = h0end ? -1 : list.next();
         if (nj >= 0) {
             jk = nj;
-            h0v = kvl ? kvl[nj] : BLK;
+            h0v = block_keys(nj);
         } else {
-            h0end = true;  // copies past the end repeat the last block (never computed)
+            h0end = 1;  // copies past the end fetch nothing (never computed)
+            h0v = 0;
         }
         h0j = jk;
     };
@@ -329,11 +353,16 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         voffs[n] = dma_lane_offset<D, NW, true>(n, wave, lane);
     }
     constexpr uint32_t kSubBytes = kSubKeys * D * 2;
+    // copies of one sub-tile, bounded to the block's valid rows: padded rows
+    // and copies past the end of the list (0 valid keys) fetch nothing
     auto issue_k = [&](int buf, int sub) __attribute__((always_inline)) {
-        dma_issue<NI, NW>(block_rsrc(Kh + (int64_t)jk * BLK * D), sub * kSubBytes, koffs, KB[buf], wave);
+        kvk = h0v;
+        dma_issue<NI, NW>(block_rsrc(Kh + (int64_t)jk * BLK * D, (uint32_t)kvk * (D * 2)), sub * kSubBytes, koffs,
+                          KB[buf], wave);
     };
     auto issue_v = [&](int buf, int sub) __attribute__((always_inline)) {
-        dma_issue<NI, NW>(block_rsrc(Vh + (int64_t)jv * BLK * D), sub * kSubBytes, voffs, VB[buf], wave);
+        dma_issue<NI, NW>(block_rsrc(Vh + (int64_t)jv * BLK * D, (uint32_t)vvk * (D * 2)), sub * kSubBytes, voffs,
+                          VB[buf], wave);
     };
 
     // prologue: K of slots 0..3, V of slots 0..2
@@ -342,7 +371,10 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         if (s > 0 && s % SUBS == 0) k_advance();
         issue_k(s, s % SUBS);
         if (s < 3) {
-            if (s % SUBS == 0) jv = h0j;
+            if (s % SUBS == 0) {
+                jv = h0j;
+                vvk = h0v;
+            }
             issue_v(s, s % SUBS);
         }
     }
@@ -462,7 +494,7 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
     // slot 0: wait for its K copy, scores, first reference
     wait_vmcnt<6 * NI>();
     lds_barrier();
-    int cvk = LAG == 0 ? h0v : h1v;  // valid keys of the block of slot t+1 (unclamped)
+    int cvk = LAG == 0 ? h0v : h1v;  // valid keys of the block of slot t+1
     if (active) {
         f32x16_t s = scores(KB[0]);
         if (cvk < kSubKeys) mask(s, cvk);
@@ -494,7 +526,7 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         float p[16];
         bf16x8_t pf[2];
         f32x16_t sn;
-        float m3 = -INFINITY, ls = 0.f;
+        float m3 = -INFINITY, ls;
         auto rdk = [&](int kk) __attribute__((always_inline)) {
             kf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kb + koff[kk]));
         };
@@ -523,6 +555,8 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
                 constexpr int e = 2 * I;
                 pf[1][e] = (__bf16)p[8 + e];
                 pf[1][e + 1] = (__bf16)p[9 + e];
+            } else if constexpr (I == 4) {
+                ls = p[0];
             } else if constexpr (I < 20) {
                 ls += p[I - 4];
             } else {
@@ -532,7 +566,7 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
                 } else if constexpr (q % 3 == 1) {
                     xc[2 * k + 1] = fmaf(sn[2 * k + 1], c2, -ref);
                 } else {
-                    m3 = fmaxf(m3, fmaxf(xc[2 * k], xc[2 * k + 1]));
+                    m3 = max3_raw(m3, xc[2 * k], xc[2 * k + 1]);
                 }
             }
         };
@@ -582,7 +616,10 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         lds_barrier();
         if (SUB_K == 0) k_advance();
         issue_k(K, SUB_K);
-        if (SUB_V == 0) jv = h0j;
+        if (SUB_V == 0) {
+            jv = h0j;
+            vvk = h0v;
+        }
         issue_v((K + 3) % 4, SUB_V);
         if (SUB_N == 0) {
             cvk = LAG == 0 ? h0v : h1v;

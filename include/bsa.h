@@ -124,8 +124,8 @@ int bsa_gilbert_perm(const void* src, void* dst, const int32_t* perm, int L, int
  *                 nqb*block, k rows = nkb*block; head strides in elements.
  *  q_block_len    int32[nqb] valid tokens per query block (NULL: all full).
  *  kv_block_len   int32[nkb] valid tokens per KV block (NULL: all full).
- *                 Padded rows must be finite; they are never read by the
- *                 pooling.
+ *                 Rows past a block's valid length are never read; they
+ *                 may hold anything.
  *  scale          score scale (normally 1/sqrt(d)).
  *  overlap        float32[nqb][overlap_row_stride] (NULL: no bias); entry
  *                 (i, j) is the geometric overlap of query block i with
@@ -231,7 +231,11 @@ int bsa_route_topk(const bsa_route_args* args, void* workspace, size_t workspace
  *                 o_head_stride.
  *  lse            float32[heads][nqb*block] (nullable): natural-log
  *                 log-sum-exp of the scaled scores per query row.
- *  q_block_len, kv_block_len  as for the router (NULL: all full).
+ *  q_block_len, kv_block_len  as for the router (NULL: all full).  K and
+ *                 V rows past a block's valid length are never fetched
+ *                 (bf16) or never weighted (fp32), and padded query rows
+ *                 never reach another row's result, so padding may hold
+ *                 anything, NaN included.
  *  row_ptr        int32[heads*nqb + 1], col_idx int32[col_len]: the lists
  *                 (row r = h*nqb + i).  Entries outside [0, nkb) and ranges
  *                 outside [0, col_len) are ignored.

@@ -130,6 +130,14 @@ def test_deterministic_and_padding_inert():
     o3, l3 = bsa.block_sparse_attn(q2, k2, v2, r["row_ptr"], r["col_idx"], **args)
     torch.cuda.synchronize()
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    # padded rows are never fetched: NaN there changes nothing either
+    q2[:, 36 * 128 + 72:] = float("nan")
+    for c in range(2):
+        k2[:, (c * 37 + 36) * 128 + 72:(c * 37 + 37) * 128] = float("nan")
+        v2[:, (c * 37 + 36) * 128 + 72:(c * 37 + 37) * 128] = float("nan")
+    o4, l4 = bsa.block_sparse_attn(q2, k2, v2, r["row_ptr"], r["col_idx"], **args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o4) and torch.equal(l1, l4)
 
 
 @pytest.mark.parametrize("block,d", [(64, 64), (64, 128), (128, 64)])
