@@ -179,6 +179,9 @@ __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("" ::: "memory");
 }
 
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt fields at their maxima)
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     // gfx9 s_waitcnt: vmcnt[3:0] and [15:14], expcnt[6:4] (7 = no wait),
@@ -187,37 +190,54 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Reader of one row's list: returns the next in-range block index, or -1
-// when the list is exhausted.  The next entry is loaded one call ahead, so
-// the scalar load is long complete when it is used; out-of-range entries
-// take a slow path.
-template <bool DENSE>
+// Reader of one row's list of KV blocks.  next() returns the next in-range
+// block and its valid-key count (clamped to [0, BLK]), or -1 at the end.
+// The scalar loads for the following entry are issued by prefetch1() (its
+// block index) and prefetch2() (its key count, which needs the index) at the
+// end of the two iterations after a next(), and waited for at the top of the
+// next iteration, where no LDS read is in flight: a scalar load pending
+// during the LDS reads would force every LDS wait to lgkmcnt(0), since
+// scalar loads complete out of order.  Out-of-range entries take a slow
+// path with direct loads.
+template <int BLK, bool DENSE>
 struct ListReader {
     const_i32_t* col;
-    int e, e1, nkb, pre;
-    __device__ __forceinline__ void init(const_i32_t* c, int e0_, int e1_, int nkb_) {
+    const_i32_t* kvl;
+    int e, e1, nkb, pj, pv;
+    __device__ __forceinline__ int keys(int v) const {
+        return __builtin_amdgcn_readfirstlane(v < 0 ? 0 : (v > BLK ? BLK : v));
+    }
+    __device__ __forceinline__ int clamp_j(int j) const { return j < 0 ? 0 : (j >= nkb ? nkb - 1 : j); }
+    __device__ __forceinline__ void init(const_i32_t* c, const_i32_t* kv, int e0_, int e1_, int nkb_) {
         col = c;
+        kvl = kv;
         e = e0_;
         e1 = e1_;
         nkb = nkb_;
-        pre = (!DENSE && e < e1) ? col[e] : 0;
+        pj = DENSE ? e : (e < e1 ? col[e] : 0);
+        pv = kvl ? kvl[clamp_j(pj)] : BLK;
     }
-    __device__ __forceinline__ int next() {
-        if (DENSE) return e < e1 ? e++ : -1;
+    __device__ __forceinline__ void prefetch1() {
+        pj = DENSE ? e : col[e < e1 ? e : e1 - 1];
+    }
+    __device__ __forceinline__ void prefetch2() {
+        if (kvl) pv = kvl[clamp_j(pj)];
+    }
+    __device__ __forceinline__ int next(int& vk) {
         if (e >= e1) return -1;
-        int j = pre;
+        int j = pj;
+        vk = keys(pv);
         ++e;
-        pre = col[e < e1 ? e : e1 - 1];
         if (__builtin_expect(j < 0 || j >= nkb, 0)) {
             j = -1;
             while (e < e1) {
                 const int jj = col[e++];
                 if (jj >= 0 && jj < nkb) {
                     j = jj;
+                    vk = keys(kvl ? kvl[jj] : BLK);
                     break;
                 }
             }
-            pre = col[e < e1 ? e : e1 - 1];
         }
         return j;
     }
@@ -302,14 +322,14 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         e0 = e0 < 0 ? 0 : e0;
         e1 = e1 > a.col_len ? (int)a.col_len : e1;
     }
-    const_i32_t* kvl = (const_i32_t*)a.kv_len;
-    ListReader<DENSE> list;
-    list.init((const_i32_t*)a.col_idx, e0, e1, a.nkb);
+    ListReader<BLK, DENSE> list;
+    list.init((const_i32_t*)a.col_idx, (const_i32_t*)a.kv_len, e0, e1, a.nkb);
 
     // K-copy cursor: block jk; the blocks it has entered are published to a
     // two-deep history (j, valid keys; -1 keys past the end) that the V-copy
     // cursor (same block) and the compute cursor (LAG blocks behind) read.
-    int jk = list.next();
+    int jk, h0v;
+    jk = list.next(h0v);
     if (jk < 0) {
         // empty list: zeros and -inf, no copies in flight
         const int qrow = q0 + l32;
@@ -321,29 +341,23 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         if (a.lse && hi == 0) a.lse[(int64_t)h * a.nqb * BLK + (int64_t)i * BLK + qrow] = -INFINITY;
         return;
     }
-    // valid keys of a block, clamped to [0, BLK]; readfirstlane keeps the
-    // clamp (a VALU med3) from making the copy bounds look divergent
-    auto block_keys = [&](int j) __attribute__((always_inline)) {
-        if (!kvl) return BLK;
-        const int v = kvl[j];
-        return __builtin_amdgcn_readfirstlane(v < 0 ? 0 : (v > BLK ? BLK : v));
-    };
-    int h0j = jk, h0v = block_keys(jk), h1v = 0;
-    int kvk = 0, vvk = 0;  // valid keys of the blocks being copied (0 past the end)
+    int h0j = jk, h1v = 0;
     int h0end = 0, h1end = 1;  // ints, not bools: kept in scalar registers
     auto k_advance = [&]() __attribute__((always_inline)) {
         h1v = h0v;
         h1end = h0end;
-        const int nj = h0end ? -1 : list.next();
+        int nv = 0;
+        const int nj = h0end ? -1 : list.next(nv);
         if (nj >= 0) {
             jk = nj;
-            h0v = block_keys(nj);
+            h0v = nv;
         } else {
             h0end = 1;  // copies past the end fetch nothing (never computed)
             h0v = 0;
         }
         h0j = jk;
     };
+    int kvk = 0, vvk = 0;  // valid keys of the blocks being copied (0 past the end)
     int jv = jk;
 
     uint32_t koffs[NI], voffs[NI];
@@ -366,9 +380,15 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
     };
 
     // prologue: K of slots 0..3, V of slots 0..2
+    list.prefetch1();
+    list.prefetch2();
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        if (s > 0 && s % SUBS == 0) k_advance();
+        if (s > 0 && s % SUBS == 0) {
+            k_advance();
+            list.prefetch1();
+            list.prefetch2();
+        }
         issue_k(s, s % SUBS);
         if (s < 3) {
             if (s % SUBS == 0) {
@@ -494,6 +514,7 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
     // slot 0: wait for its K copy, scores, first reference
     wait_vmcnt<6 * NI>();
     lds_barrier();
+    wait_lgkmcnt0();
     int cvk = LAG == 0 ? h0v : h1v;  // valid keys of the block of slot t+1
     if (active) {
         f32x16_t s = scores(KB[0]);
@@ -614,6 +635,7 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         constexpr int SUB_K = (K + 4) % SUBS, SUB_V = (K + 3) % SUBS, SUB_N = (K + 1) % SUBS;
         wait_vmcnt<4 * NI>();
         lds_barrier();
+        wait_lgkmcnt0();  // the list prefetches of the previous iteration
         if (SUB_K == 0) k_advance();
         issue_k(K, SUB_K);
         if (SUB_V == 0) {
@@ -626,6 +648,9 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
             if (LAG == 0 ? h0end : h1end) return false;
         }
         if (active) body(KB[(K + 1) % 4], VB[K], cvk - SUB_N * kSubKeys);
+        // the next block's list entry, two loads on two iterations
+        if (SUB_K == 0) list.prefetch1();
+        if (SUB_V == 0) list.prefetch2();
         return true;
     };
     auto tail = [&](auto K_) __attribute__((always_inline)) {
