@@ -112,75 +112,69 @@ overlap_flags_kernel(const float* __restrict__ overlap, int64_t ors, int n_cand,
 }
 
 // kappa[h][i][j] = (qbar_i . kbar_j) * scale + log1p(lambda * g_hat_ij).
-// grid = (ceil(n_cand / 128), heads); each workgroup scores 128 candidates
-// against every query-block row, 40 rows per pass.  Thread t owns
-// candidates j0 + t%64 and j0 + 64 + t%64 and rows 10*(t/64) .. +9 of the
-// pass (each wave owns 10 rows, so its pooled-query reads are broadcasts).
-// Pooled vectors are staged through LDS 32 channels at a time; every dot
-// product accumulates over channels in order 0..d-1.
-constexpr int kScoreJ = 128, kScoreRows = 40, kScoreDC = 32, kScoreRPT = kScoreRows / (kThreads / 64);
+constexpr int kScoreJ = 64, kScoreRows = 40, kScoreRPT = kScoreRows / (kThreads / 64), kScoreDC = 32;
 
 __device__ __attribute__((noinline)) double overlap_bias(double g, double lambda, double g_ref, double tau) {
     const double gh = g <= tau ? 0.0 : fmin(1.0, g / g_ref);
     return log1p(lambda * gh);
 }
 
+// Selection keys of one head for 64 candidates (one per lane) and up to 40
+// query blocks (10 per wave).  grid = (ceil(n_cand / 64), heads,
+// ceil(nqb / 40)).  The pooled vectors are staged through LDS 32 channels
+// at a time with coalesced 16-byte loads: keys row-major with one double of
+// padding per row (a lane reads its candidate's row; consecutive rows fall
+// in different banks), queries row-major (read as broadcasts).  Each lane
+// keeps 10 float64 dot products in registers: sequential fma over d.
 __global__ void __launch_bounds__(kThreads)
 score_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar, int64_t kbar_head_blocks,
              int nqb, int n_cand, int d, double scale, const float* __restrict__ overlap, int64_t ors,
              double lambda, double g_ref, double tau, double* __restrict__ keys) {
-    __shared__ double kt[kScoreDC][kScoreJ];
-    __shared__ __attribute__((aligned(16))) double qt[kScoreRows][kScoreDC];
-    const int h = blockIdx.y, j0 = blockIdx.x * kScoreJ, t = threadIdx.x;
-    const int cl = t % 64, rq = t / 64;
-    const int ja = j0 + cl, jb = j0 + 64 + cl;
-    for (int r0 = 0; r0 < nqb; r0 += kScoreRows) {
-        double acc_a[kScoreRPT], acc_b[kScoreRPT];
+    __shared__ __attribute__((aligned(16))) double ks[kScoreJ][kScoreDC + 1];
+    __shared__ __attribute__((aligned(16))) double qs[kScoreRows][kScoreDC];
+    const int h = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int j0 = blockIdx.x * kScoreJ, j = j0 + lane;
+    const int r0 = blockIdx.z * kScoreRows;
+    const int nr = min(kScoreRows, nqb - r0);
+    double acc[kScoreRPT];
 #pragma unroll
-        for (int m = 0; m < kScoreRPT; ++m) acc_a[m] = acc_b[m] = 0.0;
-        for (int dc = 0; dc < d; dc += kScoreDC) {
-            __syncthreads();
-            // kt[dd][c] = kbar[j0 + c][dc + dd]; 32 consecutive threads read one
-            // candidate's 32 channels
-            for (int x = t; x < kScoreJ * kScoreDC; x += kThreads) {
-                const int c = x / kScoreDC, dd = x % kScoreDC, jg = j0 + c;
-                kt[dd][c] = jg < n_cand ? kbar[(h * kbar_head_blocks + jg) * d + dc + dd] : 0.0;
-            }
-            for (int x = t; x < kScoreRows * kScoreDC; x += kThreads) {
-                const int rr = x / kScoreDC, dd = x % kScoreDC, ig = r0 + rr;
-                qt[rr][dd] = ig < nqb ? qbar[((int64_t)h * nqb + ig) * d + dc + dd] : 0.0;
-            }
-            __syncthreads();
-#pragma unroll 4
-            for (int dd = 0; dd < kScoreDC; dd += 2) {
-                const double ka0 = kt[dd][cl], kb0 = kt[dd][64 + cl];
-                const double ka1 = kt[dd + 1][cl], kb1 = kt[dd + 1][64 + cl];
+    for (int m = 0; m < kScoreRPT; ++m) acc[m] = 0.0;
+    for (int dc = 0; dc < d; dc += kScoreDC) {
+        __syncthreads();
+        // 64 rows x 32 channels of pooled keys: 16 consecutive threads read
+        // one row's 256 bytes
 #pragma unroll
-                for (int m = 0; m < kScoreRPT; ++m) {
-                    const double2 q2 = *reinterpret_cast<const double2*>(&qt[rq * kScoreRPT + m][dd]);
-                    acc_a[m] = fma(q2.x, ka0, acc_a[m]);
-                    acc_b[m] = fma(q2.x, kb0, acc_b[m]);
-                    acc_a[m] = fma(q2.y, ka1, acc_a[m]);
-                    acc_b[m] = fma(q2.y, kb1, acc_b[m]);
-                }
-            }
+        for (int x = t; x < kScoreJ * kScoreDC / 2; x += kThreads) {
+            const int c = x / (kScoreDC / 2), p2 = x % (kScoreDC / 2), jg = j0 + c;
+            double2 v = make_double2(0.0, 0.0);
+            if (jg < n_cand)
+                v = *reinterpret_cast<const double2*>(kbar + ((int64_t)h * kbar_head_blocks + jg) * d + dc + 2 * p2);
+            ks[c][2 * p2] = v.x;
+            ks[c][2 * p2 + 1] = v.y;
         }
-#pragma unroll
-        for (int m = 0; m < kScoreRPT; ++m) {
-            const int i = r0 + rq * kScoreRPT + m;
-            if (i >= nqb) continue;
-            double* krow = keys + ((int64_t)h * nqb + i) * n_cand;
-            if (ja < n_cand) {
-                double kap = acc_a[m] * scale;
-                if (overlap) kap += overlap_bias((double)overlap[(int64_t)i * ors + ja], lambda, g_ref, tau);
-                krow[ja] = kap;
-            }
-            if (jb < n_cand) {
-                double kap = acc_b[m] * scale;
-                if (overlap) kap += overlap_bias((double)overlap[(int64_t)i * ors + jb], lambda, g_ref, tau);
-                krow[jb] = kap;
-            }
+        for (int x = t; x < kScoreRows * kScoreDC / 2; x += kThreads) {
+            const int rr = x / (kScoreDC / 2), p2 = x % (kScoreDC / 2);
+            double2 v = make_double2(0.0, 0.0);
+            if (rr < nr) v = *reinterpret_cast<const double2*>(qbar + ((int64_t)h * nqb + r0 + rr) * d + dc + 2 * p2);
+            *reinterpret_cast<double2*>(&qs[rr][2 * p2]) = v;
         }
+        __syncthreads();
+#pragma unroll 8
+        for (int dd = 0; dd < kScoreDC; ++dd) {
+            const double kv = ks[lane][dd];
+#pragma unroll
+            for (int m = 0; m < kScoreRPT; ++m) acc[m] = fma(qs[w + 4 * m][dd], kv, acc[m]);
+        }
+    }
+    if (j >= n_cand) return;
+#pragma unroll
+    for (int m = 0; m < kScoreRPT; ++m) {
+        const int rr = w + 4 * m;
+        if (rr >= nr) continue;
+        const int i = r0 + rr;
+        double kap = acc[m] * scale;
+        if (overlap) kap += overlap_bias((double)overlap[(int64_t)i * ors + j], lambda, g_ref, tau);
+        keys[((int64_t)h * nqb + i) * n_cand + j] = kap;
     }
 }
 
@@ -275,6 +269,75 @@ __device__ __forceinline__ unsigned long long order_key(double v) {
     return b < 0 ? ~(unsigned long long)b : ((unsigned long long)b | 0x8000000000000000ull);
 }
 
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+    const int lo = __shfl_xor((int)(unsigned)v, m), hi = __shfl_xor((int)(unsigned)(v >> 32), m);
+    return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
+}
+
+__device__ __forceinline__ unsigned long long shfl_u64(unsigned long long v, int src) {
+    const int lo = __shfl((int)(unsigned)v, src), hi = __shfl((int)(unsigned)(v >> 32), src);
+    return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
+}
+
+// (key, index) order of the selection: larger key first, lower index first
+// among equal keys.
+__device__ __forceinline__ bool sel_before(unsigned long long ka, int ia, unsigned long long kb, int ib) {
+    return ka > kb || (ka == kb && ia < ib);
+}
+
+// Bitonic sort of 128 (key, index) pairs held two per lane (element lane and
+// element lane + 64) into selection order, across the wave.
+__device__ __forceinline__ void wave_sort128(unsigned long long& ka, int& ia, unsigned long long& kb, int& ib,
+                                             int lane) {
+#pragma unroll
+    for (int k = 2; k <= 128; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            if (j == 64) {
+                // pairs (lane, lane + 64); k == 128, so the lower keeps the first
+                if (sel_before(kb, ib, ka, ia)) {
+                    const unsigned long long tk = ka;
+                    const int ti = ia;
+                    ka = kb;
+                    ia = ib;
+                    kb = tk;
+                    ib = ti;
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    unsigned long long& kv = s ? kb : ka;
+                    int& iv = s ? ib : ia;
+                    const int e = lane + 64 * s;
+                    const unsigned long long ko = shfl_xor_u64(kv, j);
+                    const int io = __shfl_xor(iv, j);
+                    const bool first = (e & j) == 0, desc = (e & k) == 0;
+                    const bool mine_first = sel_before(kv, iv, ko, io);
+                    if (first == desc ? !mine_first : mine_first) {
+                        kv = ko;
+                        iv = io;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Bitonic sort of one value per lane, largest first.
+__device__ __forceinline__ unsigned long long wave_sort64_desc(unsigned long long v, int lane) {
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const unsigned long long o = shfl_xor_u64(v, j);
+            const bool first = (lane & j) == 0, desc = (lane & k) == 0;
+            const unsigned long long hi = v > o ? v : o, lo = v > o ? o : v;
+            v = first == desc ? hi : lo;
+        }
+    }
+    return v;
+}
+
 // One wave per (head, query block) row.  Lane l holds the keys of
 // candidates j = l + 64 m (m < KPL).  A radix select over 8-bit digits
 // (most significant first, a 256-bin histogram per wave in LDS) finds the
@@ -290,6 +353,8 @@ topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int 
             const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ keff,
             int32_t* __restrict__ col_idx) {
     __shared__ int hist_all[kThreads / 64][256];
+    __shared__ unsigned long long cand_key[kThreads / 64][128];
+    __shared__ int cand_idx[kThreads / 64][128];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = blockIdx.x * (kThreads / 64) + w;
     if (r >= rows) return;
@@ -315,7 +380,57 @@ topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int 
 
     unsigned long long prefix = 0, mask = 0;
     int need = ke;
-    if (ke > 0) {
+    bool found = false;
+    if (ke > 0 && ke <= 64) {
+        // Fast path.  The ke-th largest lane maximum L is a lower bound of
+        // the ke-th largest key (ke lanes hold a key >= L), so every selected
+        // key is >= L.  When at most 128 keys are >= L, they are gathered,
+        // sorted in selection order, and the ke-th gives the threshold.
+        unsigned long long lm = 0;
+#pragma unroll
+        for (int m = 0; m < KPL; ++m) lm = key[m] > lm ? key[m] : lm;
+        const unsigned long long L = shfl_u64(wave_sort64_desc(lm, lane), ke - 1);
+        int c = 0;
+#pragma unroll
+        for (int m = 0; m < KPL; ++m) c += __popcll(__ballot(key[m] != 0 && key[m] >= L));
+        if (c <= 128) {
+            unsigned long long* ck = cand_key[w];
+            int* ci = cand_idx[w];
+            int pos = 0;
+#pragma unroll
+            for (int m = 0; m < KPL; ++m) {
+                const bool cand = key[m] != 0 && key[m] >= L;
+                const unsigned long long b = __ballot(cand);
+                if (cand) {
+                    const int at = pos + __popcll(b & lt_mask);
+                    ck[at] = key[m];
+                    ci[at] = lane + 64 * m;
+                }
+                pos += __popcll(b);
+            }
+            for (int e = c + lane; e < 128; e += 64) {
+                ck[e] = 0;
+                ci[e] = 0x7fffffff;
+            }
+            __builtin_amdgcn_wave_barrier();
+            __asm__ volatile("" ::: "memory");
+            unsigned long long ka = ck[lane], kb = ck[lane + 64];
+            int ia = ci[lane], ib = ci[lane + 64];
+            wave_sort128(ka, ia, kb, ib, lane);
+            const int p = ke - 1;
+            const unsigned long long kt = shfl_u64(p < 64 ? ka : kb, p & 63);
+            const int it = __shfl(p < 64 ? ia : ib, p & 63);
+            // threshold key and how many keys equal to it are taken (those
+            // with index <= it, in ascending index order)
+            int eq_take = 0;
+#pragma unroll
+            for (int m = 0; m < KPL; ++m) eq_take += __popcll(__ballot(key[m] == kt && lane + 64 * m <= it));
+            prefix = kt;
+            need = eq_take;
+            found = true;
+        }
+    }
+    if (ke > 0 && !found) {
 #pragma unroll 1
         for (int shift = 56; shift >= 0; shift -= 8) {
 #pragma unroll
@@ -428,7 +543,7 @@ hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* w
                            a->overlap_row_stride, n_cand, a->tau, flags);
     // 4. selection keys
     if (n_cand > 0) {
-        dim3 grid((n_cand + kScoreJ - 1) / kScoreJ, a->heads);
+        dim3 grid((n_cand + kScoreJ - 1) / kScoreJ, a->heads, (a->nqb + kScoreRows - 1) / kScoreRows);
         hipLaunchKernelGGL(score_kernel, grid, dim3(kThreads), 0, stream, qbar, kbar, kbar_head_blocks, a->nqb,
                            n_cand, a->d, a->scale, a->overlap, a->overlap_row_stride, a->lambda, a->g_ref, a->tau,
                            keys);
