@@ -2,7 +2,7 @@
 48 on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk C]
-                    [--no-cpu-baseline] [--dense] [--sweep FILE]
+                    [--no-cpu-baseline] [--dense] [--sweep FILE] [--rollout FILE]
 
 Workload: the 14B-like growing-context layer -- 40 heads, head dim 128, a
 3 x 30 x 52 latent chunk (4680 tokens, 37 blocks of 128), a KV history of C
@@ -236,6 +236,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=40)
     ap.add_argument("--dense", action="store_true", help="also time dense attention at the same chunk")
     ap.add_argument("--sweep", default=None, help="write a chunk 1..C sparse/dense sweep to this JSONL file")
+    ap.add_argument("--rollout", default=None,
+                    help="write a 1..C chunk rollout (append, route with the pooled-key cache, attend) to this JSONL file")
     ap.add_argument("--profile-attention", type=int, default=0, metavar="N",
                     help="counter mode: N attention launches + a 1 GiB copy, no JSON line")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
@@ -282,7 +284,8 @@ def main():
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
-    attn_ms = sum(a.elapsed_time(b) for a, b in events) / len(events)
+    attn_all = sorted(a.elapsed_time(b) for a, b in events)
+    attn_ms = sum(attn_all) / len(attn_all)
 
     # the same step with the pooled-key cache dropped before each call
     n_full = max(1, min(args.steps, 5))
@@ -323,7 +326,11 @@ def main():
                            "history pools; score all 1776 candidates; top-K) + block-sparse attention "
                            "+ inverse permute", "parallelism": "single GPU"},
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "attn": {"ms_per_call": round(attn_ms, 4), "effective_tflops": round(attn_tflops, 2),
+        "attn": {"ms_per_call": round(attn_ms, 4),
+                 "ms_median": round(attn_all[len(attn_all) // 2], 4),
+                 "ms_p10": round(attn_all[len(attn_all) // 10], 4),
+                 "ms_p90": round(attn_all[(9 * len(attn_all)) // 10], 4),
+                 "effective_tflops": round(attn_tflops, 2),
                  "pct_bf16_mfma_peak": round(100.0 * attn_tflops / PEAK_BF16_TFLOPS, 2),
                  "tile_tflops": round(wc["tile_flop"] / (attn_ms * 1e-3) / 1e12, 2),
                  "effective_flop": wc["flop"], "listed_blocks": wc["pairs"],
@@ -349,6 +356,8 @@ def main():
                         "speedup_sparse_vs_dense": round(dms / attn_ms, 2)}
     if args.sweep:
         sweep(st, args.sweep)
+    if args.rollout:
+        rollout(st, args.rollout)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(st, args.cpu_heads)
     print(json.dumps(out), flush=True)
@@ -380,6 +389,46 @@ def sweep(st, path):
                                 "dense_attn_ms": round(e0.elapsed_time(e1) / 3, 4)}) + "\n")
             f.flush()
             print("sweep chunk %d done" % c, file=sys.stderr, flush=True)
+
+
+def rollout(st, path, reps: int = 5):
+    """A chunked rollout on a fresh KV store: for chunk c = 0..C-1 one call
+    appends chunk c's K and V (Gilbert permutation into slot c), permutes the
+    queries, routes over chunks 0..c (pooling only chunk c's keys; the
+    history's pooled keys come from the cache) and attends.  Each chunk's
+    call is timed ``reps`` times (each repeat rewrites slot c with the same
+    bits), whole call and attention alone, with events on the stream."""
+    import torch
+    from block_sparse_attention_gilbert_amd import gilbert_perm
+    from block_sparse_attention_gilbert_amd.pipeline import RoutedAttention
+    w, src = st["w"], st["ra"]
+    chunks = src.store_chunks
+    ra = RoutedAttention(src.grid, w.heads, w.d, w.bs, chunks, device=src.device, k_cap=50)
+    q_raster = st["q_raster"]
+    with open(path, "w") as f:
+        for c in range(chunks):
+            ks, vs = src.slot(c)
+            k_r = gilbert_perm(ks, src.perm, block=w.bs, inverse=True)
+            v_r = gilbert_perm(vs, src.perm, block=w.bs, inverse=True)
+            ra.step(q_raster, k_r, v_r, c)
+            torch.cuda.synchronize()
+            steps, attn = [], []
+            for _ in range(reps):
+                ev = []
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                ra.step(q_raster, k_r, v_r, c, attn_events=ev)
+                e1.record()
+                torch.cuda.synchronize()
+                steps.append(e0.elapsed_time(e1))
+                attn.append(ev[0][0].elapsed_time(ev[0][1]))
+            assert torch.equal(ra.slot(c)[0], ks), "rollout store slot differs from the generated chunk"
+            steps.sort()
+            attn.sort()
+            f.write(json.dumps({"chunk": c + 1, "kv_tokens": (c + 1) * 4680, "step_ms": round(steps[reps // 2], 4),
+                                "attn_ms": round(attn[reps // 2], 4)}) + "\n")
+            f.flush()
+            print("rollout chunk %d done" % (c + 1), file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":
