@@ -17,7 +17,9 @@ routing (mean-pool Q and the K blocks appended since the previous call --
 the pooled history keys are cached across calls, as the store only grows by
 appending -- then score, top-K, CSR); block-sparse attention; inverse
 permutation of O.  The step time with every history block re-pooled is
-reported beside it (``step_full_k_pool_ms``).
+reported beside it (``step_full_k_pool_ms``), and so is the same step
+replayed from a HIP graph (``step_hip_graph_ms``: identical kernels, no
+launch gaps; every replay is checked bitwise against the eager step).
 
 Printed: one JSON line.  ``value`` = effective TFLOP/s of the step (valid
 selected (query, key) pairs x 4 d FLOP, divided by the step time).  The
@@ -108,6 +110,41 @@ def work_counts(row_ptr, col_idx, q_len, k_len, heads, nqb, bs, d):
     list_bytes = 4 * (len(rp) + int(rp[-1]))
     return dict(flop=flop, tile_flop=tile_flop, pairs=pairs, uniq_rows=uniq_rows,
                 alg_bytes=kv_bytes + qo_bytes + list_bytes, visits=pairs)
+
+
+def step_graph_ms(st, reps: int):
+    """The same step captured once into a HIP graph and replayed (the
+    kernels are unchanged; the launch gaps between them go).  Every replay's
+    output must equal the eager step's bitwise; returns ms per replay."""
+    import torch
+    ra = st["ra"]
+    o_eager, _ = run_step(st)
+    o_eager = o_eager.clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_step(st)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run_step(st)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ra.o_raster, o_eager), "graph replay differs from the eager step"
+        run_step(st)  # eager work between replays
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    assert torch.equal(ra.o_raster, o_eager), "graph replay differs from the eager step"
+    return e0.elapsed_time(e1) / reps
 
 
 def cpu_baseline(st, n_heads=2):
@@ -300,6 +337,8 @@ def main():
     torch.cuda.synchronize()
     ms_full_pool = f0.elapsed_time(f1) / n_full
 
+    ms_graph = step_graph_ms(st, n_full)
+
     wc = work_counts(r["row_ptr"], r["col_idx"], w.q_len, w.k_len, w.heads, w.nqb, w.bs, w.d)
     value = wc["flop"] / (ms_step * 1e-3) / 1e12
     attn_tflops = wc["flop"] / (attn_ms * 1e-3) / 1e12
@@ -314,6 +353,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "step_full_k_pool_ms": round(ms_full_pool, 4),
+        "step_hip_graph_ms": None if ms_graph is None else round(ms_graph, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -1,0 +1,49 @@
+"""One routed-attention call captured into a HIP graph: every replay, with
+eager calls and synchronisations between the replays, must equal the eager
+call bitwise (the library records no memset node and allocates nothing
+during the call)."""
+
+import pytest
+import torch
+
+import workloads
+
+from helpers import need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def test_step_graph_replays_match_eager():
+    dev = need_gpu()
+    from block_sparse_attention_gilbert_amd import gilbert_perm
+    from block_sparse_attention_gilbert_amd.pipeline import RoutedAttention
+    w = workloads.c4(c=3, heads=[0, 1, 2])
+    ra = RoutedAttention((3, 30, 52), w.heads, w.d, w.bs, 3, device=dev, k_cap=50,
+                         k_store=w.k.contiguous().to(dev), v_store=w.v.contiguous().to(dev))
+    ks, vs = ra.slot(2)
+    q_r = gilbert_perm(w.q.to(dev), ra.perm, block=128, inverse=True)
+    k_r = gilbert_perm(ks, ra.perm, block=128, inverse=True).clone()
+    v_r = gilbert_perm(vs, ra.perm, block=128, inverse=True).clone()
+    o_eager = ra.step(q_r, k_r, v_r, 2)[0].clone()
+    lse_eager = ra.lse.clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ra.step(q_r, k_r, v_r, 2)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        ra.step(q_r, k_r, v_r, 2)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        ra.o_raster.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ra.o_raster, o_eager), rep
+        assert torch.equal(ra.lse, lse_eager), rep
+        ra.step(q_r, k_r, v_r, 2)            # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(ra.o_raster, o_eager), rep
