@@ -8,8 +8,10 @@ given.  PyTorch provides device memory and streams.  If the library has not
 been built, importing this package raises ImportError; there is no fallback.
 
 Entry points (same names as the C ABI, without the ``bsa_`` prefix):
-``gilbert_index``, ``gilbert_perm``, ``route_topk`` (with
-``route_workspace_size``), ``block_sparse_attn``, ``dense_attn``.
+``gilbert_index``, ``gilbert_perm``, ``gilbert_block_window``,
+``route_topk`` (with ``route_workspace_size``), ``route_materialize`` (with
+``route_materialize_workspace_size``), ``block_sparse_attn``,
+``dense_attn``.
 """
 
 from __future__ import annotations
@@ -59,6 +61,18 @@ class RouteArgs(ctypes.Structure):
     ]
 
 
+class MaterializeArgs(ctypes.Structure):
+    """Mirror of ``bsa_materialize_args``."""
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("coverage", _p), ("eta_cov", ctypes.c_double),
+        ("k_cov", _i), ("k_unc", _i), ("mass", ctypes.c_double),
+        ("prev_begin", _i), ("prev_end", _i),
+        ("window", _p), ("window_len", _p), ("window_stride", _i),
+        ("ref_begin", _i), ("ref_end", _i),
+    ]
+
+
 _lib.bsa_version.restype = _i
 _lib.bsa_strerror.restype = ctypes.c_char_p
 _lib.bsa_strerror.argtypes = [_i]
@@ -67,6 +81,13 @@ _lib.bsa_gilbert_index.restype = _i
 _lib.bsa_gilbert_index.argtypes = [_i, _i, _i, _p, _p, _p]
 _lib.bsa_gilbert_perm.restype = _i
 _lib.bsa_gilbert_perm.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i64, _i64, _i, _i, _p]
+_lib.bsa_gilbert_block_window.restype = _i
+_lib.bsa_gilbert_block_window.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p]
+_lib.bsa_route_materialize_workspace_size.restype = ctypes.c_size_t
+_lib.bsa_route_materialize_workspace_size.argtypes = [ctypes.POINTER(RouteArgs), ctypes.POINTER(MaterializeArgs)]
+_lib.bsa_route_materialize.restype = _i
+_lib.bsa_route_materialize.argtypes = [ctypes.POINTER(RouteArgs), ctypes.POINTER(MaterializeArgs), _p,
+                                       ctypes.c_size_t, _p]
 _lib.bsa_route_workspace_size.restype = ctypes.c_size_t
 _lib.bsa_route_workspace_size.argtypes = [ctypes.POINTER(RouteArgs)]
 _lib.bsa_route_topk.restype = _i
@@ -78,8 +99,9 @@ _lib.bsa_dense_attn.restype = _i
 _lib.bsa_dense_attn.argtypes = _ATTN_COMMON + [_f, _p]
 
 EXPORTED = ("bsa_version", "bsa_strerror", "bsa_last_error_detail", "bsa_gilbert_index",
-            "bsa_gilbert_perm", "bsa_route_workspace_size", "bsa_route_topk",
-            "bsa_block_sparse_attn", "bsa_dense_attn")
+            "bsa_gilbert_perm", "bsa_gilbert_block_window", "bsa_route_workspace_size", "bsa_route_topk",
+            "bsa_route_materialize_workspace_size", "bsa_route_materialize", "bsa_block_sparse_attn",
+            "bsa_dense_attn")
 
 
 class BsaError(RuntimeError):
@@ -186,6 +208,27 @@ def gilbert_perm(src: torch.Tensor, perm: torch.Tensor, *, block: int, inverse: 
     return dst
 
 
+def gilbert_block_window(perm: torch.Tensor, inv: torch.Tensor, grid, *, block: int, q_chunk: int,
+                         out=None, stream=None):
+    """Local window of every query block of chunk ``q_chunk``: ``(window,
+    window_len)`` with ``window`` int32 ``[n_blocks][2*n_blocks]`` (row b's
+    first ``window_len[b]`` entries are its absolute KV block indices,
+    ascending)."""
+    _need_gpu(perm, inv)
+    perm, inv = _i32(perm, "perm"), _i32(inv, "inv")
+    T, H, W = grid
+    nbc = -(-(T * H * W) // block)
+    if out is None:
+        out = (torch.empty((nbc, 2 * nbc), dtype=torch.int32, device=perm.device),
+               torch.empty(nbc, dtype=torch.int32, device=perm.device))
+    window, window_len = out
+    if window.dtype != torch.int32 or window.dim() != 2 or window.stride(1) != 1 or window.shape[0] < nbc:
+        raise ValueError("window must be int32 [n_blocks][stride] with contiguous rows")
+    _check(_lib.bsa_gilbert_block_window(_ptr(perm), _ptr(inv), T, H, W, block, q_chunk, _ptr(window),
+                                         _ptr(_i32(window_len, "window_len")), window.stride(0), _stream(stream)))
+    return window, window_len
+
+
 # --------------------------------------------------------------------- router
 
 def _route_args(q, k, *, block, nqb, nkb, q_block_len, kv_block_len, scale, overlap, lam, g_ref, tau,
@@ -278,6 +321,91 @@ def route_workspace_size(q, k, **kw) -> int:
     return _lib.bsa_route_workspace_size(ctypes.byref(a))
 
 
+def _materialize_args(coverage, eta_cov, k_cov, k_unc, mass, prev_blocks, window, window_len, ref_blocks):
+    m = MaterializeArgs()
+    m.struct_size = ctypes.sizeof(MaterializeArgs)
+    if coverage is not None:
+        if coverage.dtype != torch.float32 or not coverage.is_contiguous():
+            raise ValueError("coverage must be a contiguous float32 tensor")
+        m.coverage = coverage.data_ptr()
+    m.eta_cov, m.k_cov, m.k_unc, m.mass = float(eta_cov), int(k_cov), int(k_unc), float(mass)
+    m.prev_begin, m.prev_end = int(prev_blocks[0]), int(prev_blocks[1])
+    if window is not None:
+        if window.dtype != torch.int32 or window.dim() != 2 or window.stride(1) != 1:
+            raise ValueError("window must be int32 [nqb][stride] with contiguous rows")
+        m.window, m.window_len, m.window_stride = (window.data_ptr(), _i32(window_len, "window_len").data_ptr(),
+                                                   window.stride(0))
+    m.ref_begin, m.ref_end = int(ref_blocks[0]), int(ref_blocks[1])
+    return m
+
+
+def materialize_capacity(heads: int, nqb: int, nkb: int, *, k_cov: int, k_unc: int, prev_blocks=(0, 0),
+                         window_stride: int = 0, ref_blocks=(0, 0)) -> int:
+    """Entries ``col_idx`` must hold for ``route_materialize``."""
+    clip = lambda x: min(int(x), nkb)
+    per_row = max(clip(prev_blocks[1]) - clip(prev_blocks[0]), k_cov, k_unc) + window_stride \
+        + clip(ref_blocks[1]) - clip(ref_blocks[0])
+    return heads * nqb * min(nkb, per_row)
+
+
+def route_materialize(q: torch.Tensor, k: torch.Tensor, *, block: int, nqb: int, nkb: int, scale: float,
+                      q_block_len=None, kv_block_len=None, overlap=None, lam: float = 2.0, g_ref: float = 0.2,
+                      tau: float = 0.1, coverage=None, eta_cov: float = 0.9, k_cov: int = 80, k_unc: int = 150,
+                      mass: float = 0.9, prev_blocks=(0, 0), window=None, window_len=None, ref_blocks=(0, 0),
+                      kpool=None, kpool_valid_blocks: int = 0, want_keys: bool = False,
+                      out: Optional[dict] = None, workspace=None, stream=None):
+    """Materialised routes: coverage-gated budgets, the previous chunk's
+    reservation, the cumulative-mass prefix, the local window and the
+    reference blocks.  Returns a dict with ``row_ptr`` and ``col_idx``
+    (capacity-sized; the first ``row_ptr[-1]`` entries are the lists) and
+    optionally ``sel_keys``."""
+    _need_gpu(q, k, q_block_len, kv_block_len, overlap, coverage, window, window_len, kpool)
+    heads = q.shape[0]
+    dev = q.device
+    wstride = 0 if window is None else window.stride(0)
+    if out is None:
+        cap = materialize_capacity(heads, nqb, nkb, k_cov=k_cov, k_unc=k_unc, prev_blocks=prev_blocks,
+                                   window_stride=wstride, ref_blocks=ref_blocks)
+        out = {
+            "row_ptr": torch.empty(heads * nqb + 1, dtype=torch.int32, device=dev),
+            "col_idx": torch.empty(max(1, cap), dtype=torch.int32, device=dev),
+            "sel_keys": torch.empty((heads, nqb, nkb), dtype=torch.float64, device=dev) if want_keys else None,
+        }
+    a = _route_args(q, k, block=block, nqb=nqb, nkb=nkb, q_block_len=_i32(q_block_len, "q_block_len"),
+                    kv_block_len=_i32(kv_block_len, "kv_block_len"), scale=scale, overlap=overlap, lam=lam,
+                    g_ref=g_ref, tau=tau, k_fixed=0, k_per_row=None, k_max=0, n_dense_tail_blocks=0, kpool=kpool,
+                    kpool_valid_blocks=kpool_valid_blocks, row_ptr=out["row_ptr"], col_idx=out["col_idx"],
+                    fallback_counts=None, sel_keys=out.get("sel_keys"))
+    m = _materialize_args(coverage, eta_cov, k_cov, k_unc, mass, prev_blocks, window, window_len, ref_blocks)
+    need = _lib.bsa_route_materialize_workspace_size(ctypes.byref(a), ctypes.byref(m))
+    if need == 0:
+        _check(_lib.bsa_route_materialize(ctypes.byref(a), ctypes.byref(m), None, 0, _stream(stream)))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    out["workspace"] = workspace
+    _check(_lib.bsa_route_materialize(ctypes.byref(a), ctypes.byref(m), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)))
+    return out
+
+
+def route_materialize_workspace_size(q, k, *, block, nqb, nkb, scale, q_block_len=None, kv_block_len=None,
+                                     overlap=None, coverage=None, eta_cov=0.9, k_cov=80, k_unc=150, mass=0.9,
+                                     prev_blocks=(0, 0), window=None, window_len=None, ref_blocks=(0, 0),
+                                     kpool=None, kpool_valid_blocks=0, col_capacity=None) -> int:
+    """Workspace bytes ``route_materialize`` needs for these arguments."""
+    a = _route_args(q, k, block=block, nqb=nqb, nkb=nkb, q_block_len=q_block_len, kv_block_len=kv_block_len,
+                    scale=scale, overlap=overlap, lam=2.0, g_ref=0.2, tau=0.1, k_fixed=0, k_per_row=None, k_max=0,
+                    n_dense_tail_blocks=0, kpool=kpool, kpool_valid_blocks=kpool_valid_blocks, row_ptr=None,
+                    col_idx=None, fallback_counts=None, sel_keys=None)
+    a.row_ptr, a.col_idx = 1, 1
+    wstride = 0 if window is None else window.stride(0)
+    a.col_capacity = col_capacity if col_capacity is not None else materialize_capacity(
+        q.shape[0], nqb, nkb, k_cov=k_cov, k_unc=k_unc, prev_blocks=prev_blocks, window_stride=wstride,
+        ref_blocks=ref_blocks)
+    m = _materialize_args(coverage, eta_cov, k_cov, k_unc, mass, prev_blocks, window, window_len, ref_blocks)
+    return _lib.bsa_route_materialize_workspace_size(ctypes.byref(a), ctypes.byref(m))
+
+
 # --------------------------------------------------------------------- attention
 
 def _attn_prep(q, k, v, out, lse, block):
@@ -330,6 +458,7 @@ def dense_attn(q, k, v, *, block: int, scale: Optional[float] = None, q_block_le
     return out, lse
 
 
-__all__ = ["gilbert_index", "gilbert_perm", "route_topk", "route_workspace_size", "route_capacity",
-           "block_sparse_attn", "dense_attn", "version", "library", "BsaError", "RouteArgs", "EXPORTED",
+__all__ = ["gilbert_index", "gilbert_perm", "gilbert_block_window", "route_topk", "route_workspace_size",
+           "route_capacity", "route_materialize", "route_materialize_workspace_size", "materialize_capacity",
+           "MaterializeArgs", "block_sparse_attn", "dense_attn", "version", "library", "BsaError", "RouteArgs", "EXPORTED",
            "BSA_OK", "BSA_EINVAL", "BSA_EUNSUPPORTED", "BSA_EWORKSPACE", "BSA_EHIP", "BSA_BF16", "BSA_F32"]

@@ -47,6 +47,30 @@ int bsa_route_topk(const bsa_route_args* args, void* workspace, size_t workspace
     return hip_status(bsa::launch_route(args, lay, workspace, stream), "route launch");
 }
 
+int bsa_gilbert_block_window(const int32_t* perm, const int32_t* inv, int T, int H, int W, int block, int q_chunk,
+                             int32_t* window, int32_t* window_len, int window_stride, hipStream_t stream) {
+    bsa::clear_error();
+    const int st = bsa::validate_block_window(perm, inv, T, H, W, block, q_chunk, window, window_len, window_stride);
+    if (st != BSA_OK) return st;
+    return hip_status(bsa::launch_block_window(perm, inv, T, H, W, block, q_chunk, window, window_len, window_stride,
+                                               stream),
+                      "gilbert_block_window launch");
+}
+
+int bsa_route_materialize(const bsa_route_args* args, const bsa_materialize_args* margs, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    bsa::clear_error();
+    bsa::RouteLayout lay;
+    const int st = bsa::validate_materialize(args, margs, &lay);
+    if (st != BSA_OK) return st;
+    if (!workspace) return bsa::fail(BSA_EWORKSPACE, "workspace is NULL (%zu bytes needed)", lay.total);
+    if (workspace_bytes < lay.total)
+        return bsa::fail(BSA_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, lay.total);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return bsa::fail(BSA_EWORKSPACE, "workspace must be 256-byte aligned");
+    return hip_status(bsa::launch_materialize(args, margs, lay, workspace, stream), "route_materialize launch");
+}
+
 int bsa_block_sparse_attn(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int heads,
                           int d, int block, int nqb, int nkb, int64_t q_head_stride, int64_t k_head_stride,
                           int64_t v_head_stride, int64_t o_head_stride, const int32_t* q_block_len,

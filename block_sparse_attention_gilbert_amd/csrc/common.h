@@ -38,7 +38,7 @@ struct AttnProblem {
 
 // Workspace layout of the router (byte offsets, 256-byte aligned).
 struct RouteLayout {
-    size_t qbar, kbar, keys, keff, flags, total;
+    size_t qbar, kbar, keys, keff, flags, bitmap, counts, total;
     int n_cand;
     bool kbar_in_ws, keys_in_ws;
 };
@@ -49,9 +49,16 @@ int validate_gilbert_perm(const void* src, const void* dst, const int32_t* perm,
                           int64_t gilbert_head_stride, int inverse, int dtype);
 int validate_attn(const AttnProblem& p, bool dense);
 int validate_route(const bsa_route_args* a, RouteLayout* lay);
+int validate_materialize(const bsa_route_args* a, const bsa_materialize_args* m, RouteLayout* lay);
+int validate_block_window(const int32_t* perm, const int32_t* inv, int T, int H, int W, int block, int q_chunk,
+                          const int32_t* window, const int32_t* window_len, int window_stride);
 size_t route_layout(const bsa_route_args* a, RouteLayout* lay);
 
 // Largest candidate count the in-LDS top-K sort handles.
 constexpr int kMaxCandidates = 4096;
+// Largest K_unc of the route materialisation.
+constexpr int kMaxUncovered = 256;
+// Largest number of blocks per chunk of the local-window builder.
+constexpr int kMaxWindowChunkBlocks = 1024;
 
 }  // namespace bsa

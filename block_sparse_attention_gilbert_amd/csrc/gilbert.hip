@@ -87,6 +87,83 @@ __global__ void gilbert_perm_kernel(const uint4* __restrict__ src, uint4* __rest
 
 }  // namespace
 
+// Local window of each query block: one workgroup per block b of the chunk;
+// each thread takes tokens of b, walks the 27 cells of their 3 x 3 x 3
+// neighbourhood (the cell itself included; time crosses into the previous
+// chunk, never into the next) and sets the bit of the block holding each
+// cell in an LDS bitmap over the previous and the current chunk's blocks.
+// The bitmap is then written out in ascending block order.
+// [Velox: Spatial Memory Makes World Models Efficient -- Methodology,
+//  Step 5: routes are unioned with a 26-neighbour local window in a
+//  global-aligned Gilbert block ordering]
+constexpr int kWindowWords = 2 * kMaxWindowChunkBlocks / 32;  // bitmap words: 2 chunks
+
+static_assert(kWindowWords == 64, "one wave compacts the window bitmap");
+
+__global__ void __launch_bounds__(256)
+block_window_kernel(const int32_t* __restrict__ perm, const int32_t* __restrict__ inv, int T, int H, int W,
+                    int block, int nbc, int q_chunk, int32_t* __restrict__ window, int32_t* __restrict__ window_len,
+                    int stride) {
+    __shared__ unsigned bits[kWindowWords];
+    __shared__ int wsum[4];
+    const int b = blockIdx.x, t = threadIdx.x;
+    const int L = T * H * W;
+    if (t < kWindowWords) bits[t] = 0u;
+    __syncthreads();
+    const int g1 = min(L, (b + 1) * block);
+    for (int gp = b * block + t; gp < g1; gp += blockDim.x) {
+        const int cell = perm[gp];
+        const int tt0 = cell / (H * W), rem = cell % (H * W), h0 = rem / W, w0 = rem % W;
+        for (int dt = -1; dt <= 1; ++dt) {
+            int tt = tt0 + dt, slot = 1;  // slot 1: the query chunk, 0: the previous one
+            if (tt < 0) {
+                tt += T;
+                slot = 0;
+            } else if (tt >= T) {
+                continue;
+            }
+            if (slot == 0 && q_chunk == 0) continue;
+            for (int dh = -1; dh <= 1; ++dh) {
+                const int hh = h0 + dh;
+                if (hh < 0 || hh >= H) continue;
+                for (int dw = -1; dw <= 1; ++dw) {
+                    const int ww = w0 + dw;
+                    if (ww < 0 || ww >= W) continue;
+                    const int nb = inv[(tt * H + hh) * W + ww] / block;
+                    const int bit = slot * nbc + nb;
+                    atomicOr(&bits[bit >> 5], 1u << (bit & 31));
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // ascending order: word w holds bits 32w .. 32w+31; threads 0..63 own a
+    // word each, an exclusive scan of their counts gives the write offsets
+    const int lane = t & 63, wv = t >> 6;
+    const unsigned word = t < kWindowWords ? bits[t] : 0u;
+    const int cnt = __popc(word);
+    int incl = cnt;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int up = __shfl_up(incl, off);
+        if (lane >= off) incl += up;
+    }
+    if (wv == 0) {
+        int pos = incl - cnt;
+        unsigned x = word;
+        int32_t* row = window + (int64_t)b * stride;
+        while (x) {
+            const int k = __ffs(x) - 1;
+            x &= x - 1;
+            const int bit = 32 * t + k;
+            const int slot = bit >= nbc ? 1 : 0;
+            row[pos++] = (q_chunk - 1 + slot) * nbc + (bit - slot * nbc);
+        }
+        if (lane == 63) wsum[0] = incl;
+    }
+    __syncthreads();
+    if (t == 0) window_len[b] = wsum[0];
+}
+
 hipError_t launch_gilbert_index(int T, int H, int W, int32_t* perm, int32_t* inv, hipStream_t stream) {
     const int64_t n = (int64_t)T * H * W;
     const int threads = 256;
@@ -115,6 +192,15 @@ hipError_t launch_gilbert_perm(const void* src, void* dst, const int32_t* perm, 
         hipLaunchKernelGGL(gilbert_perm_kernel<false>, dim3(blocks), dim3(threads), 0, stream,
                            static_cast<const uint4*>(src), static_cast<uint4*>(dst), perm, L, heads,
                            chunks_per_row, rows_total, rts_c, ghs_c);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_window(const int32_t* perm, const int32_t* inv, int T, int H, int W, int block, int q_chunk,
+                               int32_t* window, int32_t* window_len, int stride, hipStream_t stream) {
+    const int L = T * H * W;
+    const int nbc = (L + block - 1) / block;
+    hipLaunchKernelGGL(block_window_kernel, dim3(nbc), dim3(256), 0, stream, perm, inv, T, H, W, block, nbc, q_chunk,
+                       window, window_len, stride);
     return hipGetLastError();
 }
 

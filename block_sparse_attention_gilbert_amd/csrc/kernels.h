@@ -16,6 +16,12 @@ hipError_t launch_gilbert_perm(const void* src, void* dst, const int32_t* perm, 
 
 hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* ws, hipStream_t stream);
 
+hipError_t launch_block_window(const int32_t* perm, const int32_t* inv, int T, int H, int W, int block, int q_chunk,
+                               int32_t* window, int32_t* window_len, int stride, hipStream_t stream);
+
+hipError_t launch_materialize(const bsa_route_args* a, const bsa_materialize_args* m, const RouteLayout& lay,
+                              void* ws, hipStream_t stream);
+
 hipError_t launch_attn(const AttnProblem& p, bool dense, hipStream_t stream);
 
 }  // namespace bsa

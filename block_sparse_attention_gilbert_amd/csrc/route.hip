@@ -129,7 +129,8 @@ __device__ __attribute__((noinline)) double overlap_bias(double g, double lambda
 __global__ void __launch_bounds__(kThreads)
 score_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar, int64_t kbar_head_blocks,
              int nqb, int n_cand, int d, double scale, const float* __restrict__ overlap, int64_t ors,
-             double lambda, double g_ref, double tau, double* __restrict__ keys) {
+             double lambda, double g_ref, double tau, const float* __restrict__ coverage, double eta_cov,
+             double* __restrict__ keys) {
     __shared__ __attribute__((aligned(16))) double ks[kScoreJ][kScoreDC + 1];
     __shared__ __attribute__((aligned(16))) double qs[kScoreRows][kScoreDC];
     const int h = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -173,7 +174,10 @@ score_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar, i
         if (rr >= nr) continue;
         const int i = r0 + rr;
         double kap = acc[m] * scale;
-        if (overlap) kap += overlap_bias((double)overlap[(int64_t)i * ors + j], lambda, g_ref, tau);
+        // the geometric bias applies to well-covered query blocks only (all
+        // of them when no coverage is given)
+        if (overlap && (!coverage || (double)coverage[i] >= eta_cov))
+            kap += overlap_bias((double)overlap[(int64_t)i * ors + j], lambda, g_ref, tau);
         keys[((int64_t)h * nqb + i) * n_cand + j] = kap;
     }
 }
@@ -346,40 +350,19 @@ __device__ __forceinline__ unsigned long long wave_sort64_desc(unsigned long lon
 // total order (key descending, index ascending).  Selected indices are
 // written in ascending order with ballot prefix counts, followed by the
 // dense tail.  grid = ceil(rows / 4), 4 waves per workgroup, no barriers.
+// Threshold of the top-ke selection over the keys of one row held by a
+// wave (lane l: keys of candidates l + 64 m; 0 = not a candidate): the
+// selected set is every key > prefix plus the first `need` keys == prefix
+// in ascending candidate order.  `hist` is a 256-int and cand_key /
+// cand_idx 128-entry per-wave LDS scratch.
 template <int KPL>
-__global__ void __launch_bounds__(kThreads)
-topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int nkb, int block,
-            const int32_t* __restrict__ q_len, const int32_t* __restrict__ kv_len,
-            const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ keff,
-            int32_t* __restrict__ col_idx) {
-    __shared__ int hist_all[kThreads / 64][256];
-    __shared__ unsigned long long cand_key[kThreads / 64][128];
-    __shared__ int cand_idx[kThreads / 64][128];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int r = blockIdx.x * (kThreads / 64) + w;
-    if (r >= rows) return;
-    const int i = r % nqb;
-    const int vq = q_len ? q_len[i] : block;
-    if (vq <= 0) return;
-    int* hist = hist_all[w];
-    const int start = row_ptr[r];
-    const int ke = keff[r];
+__device__ __forceinline__ void select_threshold(const unsigned long long (&key)[KPL], int ke, int lane,
+                                                 int* hist, unsigned long long* cand_key, int* cand_idx,
+                                                 unsigned long long& prefix, int& need) {
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
-    const double* row = keys + (int64_t)r * n_cand;
-
-    unsigned long long key[KPL];
-#pragma unroll
-    for (int m = 0; m < KPL; ++m) {
-        const int j = lane + 64 * m;
-        key[m] = 0;
-        if (j < n_cand) {
-            const int v = kv_len ? kv_len[j] : block;
-            if (v > 0) key[m] = order_key(row[j]);
-        }
-    }
-
-    unsigned long long prefix = 0, mask = 0;
-    int need = ke;
+    unsigned long long mask = 0;
+    prefix = 0;
+    need = ke;
     bool found = false;
     if (ke > 0 && ke <= 64) {
         // Fast path.  The ke-th largest lane maximum L is a lower bound of
@@ -394,8 +377,8 @@ topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int 
 #pragma unroll
         for (int m = 0; m < KPL; ++m) c += __popcll(__ballot(key[m] != 0 && key[m] >= L));
         if (c <= 128) {
-            unsigned long long* ck = cand_key[w];
-            int* ci = cand_idx[w];
+            unsigned long long* ck = cand_key;
+            int* ci = cand_idx;
             int pos = 0;
 #pragma unroll
             for (int m = 0; m < KPL; ++m) {
@@ -474,6 +457,43 @@ topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int 
             mask |= 0xFFull << shift;
         }
     }
+}
+
+template <int KPL>
+__global__ void __launch_bounds__(kThreads)
+topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int nkb, int block,
+            const int32_t* __restrict__ q_len, const int32_t* __restrict__ kv_len,
+            const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ keff,
+            int32_t* __restrict__ col_idx) {
+    __shared__ int hist_all[kThreads / 64][256];
+    __shared__ unsigned long long cand_key[kThreads / 64][128];
+    __shared__ int cand_idx[kThreads / 64][128];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = blockIdx.x * (kThreads / 64) + w;
+    if (r >= rows) return;
+    const int i = r % nqb;
+    const int vq = q_len ? q_len[i] : block;
+    if (vq <= 0) return;
+    int* hist = hist_all[w];
+    const int start = row_ptr[r];
+    const int ke = keff[r];
+    const unsigned long long lt_mask = (1ull << lane) - 1ull;
+    const double* row = keys + (int64_t)r * n_cand;
+
+    unsigned long long key[KPL];
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+        const int j = lane + 64 * m;
+        key[m] = 0;
+        if (j < n_cand) {
+            const int v = kv_len ? kv_len[j] : block;
+            if (v > 0) key[m] = order_key(row[j]);
+        }
+    }
+
+    unsigned long long prefix;
+    int need;
+    select_threshold<KPL>(key, ke, lane, hist, cand_key[w], cand_idx[w], prefix, need);
     // ordered compaction: key > t, or key == t and among the first `need`
     int base = start, eq_seen = 0;
 #pragma unroll
@@ -501,20 +521,292 @@ topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int 
     }
 }
 
+// ------------------------------------------------------------------------
+// Route materialisation.
+// [Velox: Spatial Memory Makes World Models Efficient -- Methodology,
+//  Step 3: a coverage score per query block; Step 4: the geometric fusion
+//  applies to well-covered blocks; Step 5: a well-covered query block first
+//  reserves the previous chunk's KV blocks, then takes the top-scoring
+//  remaining blocks up to K_cov; a poorly covered one takes the smallest
+//  prefix of the model distribution whose cumulative mass reaches a
+//  threshold, at most K_unc blocks; both are unioned, outside the budget,
+//  with the local window and with optional reference-frame blocks]
+//
+// One wave per (head, query block) row builds the row's membership bitmap
+// in LDS (one bit per KV block) and writes it out with its population
+// count; an exclusive scan turns the counts into row pointers, and a last
+// pass writes the set bits of each row, ascending, into its CSR list.
+
+// Largest K_unc: the ordered top-K_unc of a row is sorted in one wave's LDS.
+constexpr int kMaxUnc = kMaxUncovered;
+
+__device__ __forceinline__ double key_value(unsigned long long key) {
+    const unsigned long long b = (key & 0x8000000000000000ull) ? (key & 0x7fffffffffffffffull) : ~key;
+    return __longlong_as_double((long long)b);
+}
+
+// Bitonic sort of 256 (key, index) pairs in LDS into selection order by one
+// wave; in each of the 36 stages a lane compare-exchanges two of the 128
+// disjoint pairs.
+__device__ __forceinline__ void wave_sort256_lds(unsigned long long* k, int* ix, int lane) {
+#pragma unroll 1
+    for (int size = 2; size <= kMaxUnc; size <<= 1) {
+#pragma unroll 1
+        for (int j = size >> 1; j > 0; j >>= 1) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int p = lane + 64 * s;
+                const int a = ((p & ~(j - 1)) << 1) | (p & (j - 1)), b = a + j;
+                const unsigned long long ka = k[a], kb = k[b];
+                const int ia = ix[a], ib = ix[b];
+                const bool up = (a & size) == 0;
+                if (up ? sel_before(kb, ib, ka, ia) : sel_before(ka, ia, kb, ib)) {
+                    k[a] = kb;
+                    ix[a] = ib;
+                    k[b] = ka;
+                    ix[b] = ia;
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            __asm__ volatile("" ::: "memory");
+        }
+    }
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+template <int KPL>
+__global__ void __launch_bounds__(kThreads)
+materialize_kernel(const double* __restrict__ keys, int rows, int nqb, int nkb, int block,
+                   const int32_t* __restrict__ q_len, const int32_t* __restrict__ kv_len,
+                   const float* __restrict__ coverage, double eta_cov, int k_cov, int k_unc, double mass,
+                   int prev_begin, int prev_end, const int32_t* __restrict__ window,
+                   const int32_t* __restrict__ window_len, int window_stride, int ref_begin, int ref_end,
+                   int nwords, uint32_t* __restrict__ bitmap, int32_t* __restrict__ counts) {
+    __shared__ int hist_all[kThreads / 64][256];
+    __shared__ unsigned long long skey_all[kThreads / 64][kMaxUnc];
+    __shared__ int sidx_all[kThreads / 64][kMaxUnc];
+    __shared__ double sp_all[kThreads / 64][kMaxUnc];
+    __shared__ uint32_t bits_all[kThreads / 64][kMaxCandidates / 32];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = blockIdx.x * (kThreads / 64) + w;
+    if (r >= rows) return;
+    const int i = r % nqb;
+    uint32_t* bits = bits_all[w];
+    unsigned long long* skey = skey_all[w];
+    int* sidx = sidx_all[w];
+    double* sp = sp_all[w];
+    const unsigned long long lt_mask = (1ull << lane) - 1ull;
+    for (int x = lane; x < nwords; x += 64) bits[x] = 0u;
+    __builtin_amdgcn_wave_barrier();
+    __asm__ volatile("" ::: "memory");
+    const int vq = q_len ? q_len[i] : block;
+    if (vq > 0) {
+        const bool covered = !coverage || (double)coverage[i] >= eta_cov;
+        const double* row = keys + (int64_t)r * nkb;
+        // keys of the visible blocks (0: not a candidate); a well-covered row
+        // sets the bits of the visible reserved blocks instead
+        unsigned long long key[KPL];
+        int n_res = 0, n_key = 0;
+#pragma unroll
+        for (int m = 0; m < KPL; ++m) {
+            const int j = lane + 64 * m;
+            key[m] = 0;
+            bool res = false;
+            if (j < nkb && (kv_len ? kv_len[j] : block) > 0) {
+                res = covered && j >= prev_begin && j < prev_end;
+                if (res)
+                    atomicOr(&bits[j >> 5], 1u << (j & 31));
+                else
+                    key[m] = order_key(row[j]);
+            }
+            n_res += __popcll(__ballot(res));
+            n_key += __popcll(__ballot(key[m] != 0));
+        }
+        int ke;
+        if (covered) {
+            const int n_fill = k_cov - n_res > 0 ? k_cov - n_res : 0;
+            ke = n_fill < n_key ? n_fill : n_key;
+        } else {
+            ke = k_unc < n_key ? k_unc : n_key;
+        }
+        if (ke > 0) {
+            unsigned long long prefix;
+            int need;
+            select_threshold<KPL>(key, ke, lane, hist_all[w], skey, sidx, prefix, need);
+            __builtin_amdgcn_wave_barrier();
+            __asm__ volatile("" ::: "memory");
+            // the selected keys in ascending block order: a well-covered row
+            // sets their bits, a poorly covered one gathers them for sorting
+            int base = 0, eq_seen = 0;
+#pragma unroll
+            for (int m = 0; m < KPL; ++m) {
+                const bool gt = key[m] > prefix;
+                const bool eq = key[m] != 0 && key[m] == prefix;
+                const unsigned long long beq = __ballot(eq);
+                const int rank = eq_seen + __popcll(beq & lt_mask);
+                eq_seen += __popcll(beq);
+                const bool sel = gt || (eq && rank < need);
+                const unsigned long long bs = __ballot(sel);
+                if (sel) {
+                    const int j = lane + 64 * m;
+                    if (covered) {
+                        atomicOr(&bits[j >> 5], 1u << (j & 31));
+                    } else {
+                        const int at = base + __popcll(bs & lt_mask);
+                        skey[at] = key[m];
+                        sidx[at] = j;
+                    }
+                }
+                base += __popcll(bs);
+            }
+            if (!covered) {
+                // the model distribution p = softmax(s) over the visible
+                // blocks: its maximum and normaliser
+                unsigned long long kmax = 0;
+#pragma unroll
+                for (int m = 0; m < KPL; ++m) kmax = key[m] > kmax ? key[m] : kmax;
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) {
+                    const unsigned long long ko = shfl_xor_u64(kmax, o);
+                    kmax = ko > kmax ? ko : kmax;
+                }
+                const double smax = key_value(kmax);
+                double z = 0.0;
+#pragma unroll
+                for (int m = 0; m < KPL; ++m)
+                    if (key[m] != 0) z += exp(key_value(key[m]) - smax);
+                z = wave_sum_f64(z);
+                for (int e = ke + lane; e < kMaxUnc; e += 64) {
+                    skey[e] = 0;
+                    sidx[e] = 0x7fffffff;
+                }
+                __builtin_amdgcn_wave_barrier();
+                __asm__ volatile("" ::: "memory");
+                wave_sort256_lds(skey, sidx, lane);
+                for (int e = lane; e < ke; e += 64) sp[e] = exp(key_value(skey[e]) - smax) / z;
+                __builtin_amdgcn_wave_barrier();
+                __asm__ volatile("" ::: "memory");
+                // shortest prefix, in selection order, whose running sum of p
+                // reaches the mass (all ke blocks if none does)
+                int take = ke;
+                if (lane == 0) {
+                    double csum = 0.0;
+                    for (int e = 0; e < ke; ++e) {
+                        csum += sp[e];
+                        if (csum >= mass) {
+                            take = e + 1;
+                            break;
+                        }
+                    }
+                }
+                take = __shfl(take, 0);
+                for (int e = lane; e < take; e += 64) atomicOr(&bits[sidx[e] >> 5], 1u << (sidx[e] & 31));
+            }
+        }
+        // the local window and the reference blocks, visible ones only
+        if (window) {
+            int len = window_len[i];
+            len = len < 0 ? 0 : (len > window_stride ? window_stride : len);
+            const int32_t* wrow = window + (int64_t)i * window_stride;
+            for (int x = lane; x < len; x += 64) {
+                const int j = wrow[x];
+                if (j >= 0 && j < nkb && (kv_len ? kv_len[j] : block) > 0) atomicOr(&bits[j >> 5], 1u << (j & 31));
+            }
+        }
+        for (int j = ref_begin + lane; j < ref_end; j += 64)
+            if ((kv_len ? kv_len[j] : block) > 0) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    }
+    __builtin_amdgcn_wave_barrier();
+    __asm__ volatile("" ::: "memory");
+    int cnt = 0;
+    for (int x = lane; x < nwords; x += 64) {
+        const uint32_t b = bits[x];
+        bitmap[(int64_t)r * nwords + x] = b;
+        cnt += __popc(b);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+    if (lane == 0) counts[r] = cnt;
+}
+
+// Single workgroup: exclusive prefix sum of the row counts into row_ptr.
+__global__ void __launch_bounds__(1024)
+scan_counts_kernel(const int32_t* __restrict__ counts, int rows, int32_t* __restrict__ row_ptr) {
+    __shared__ int sh[1024];
+    const int t = threadIdx.x;
+    int carry = 0;
+    for (int base = 0; base < rows; base += 1024) {
+        const int r = base + t;
+        const int v = r < rows ? counts[r] : 0;
+        __syncthreads();
+        sh[t] = v;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int add = t >= off ? sh[t - off] : 0;
+            __syncthreads();
+            sh[t] += add;
+            __syncthreads();
+        }
+        if (r < rows) row_ptr[r] = carry + sh[t] - v;
+        carry += sh[1023];
+    }
+    if (t == 0) row_ptr[rows] = carry;
+}
+
+// One wave per row: the set bits of the row's bitmap, ascending, into its
+// list.  Lane l owns words l, l + 64, ...; a wave prefix sum of the
+// population counts gives each word's write offset.
+__global__ void __launch_bounds__(kThreads)
+emit_lists_kernel(const uint32_t* __restrict__ bitmap, int rows, int nwords, const int32_t* __restrict__ row_ptr,
+                  int32_t* __restrict__ col_idx) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    int base = row_ptr[r];
+    for (int x0 = 0; x0 < nwords; x0 += 64) {
+        const int x = x0 + lane;
+        uint32_t b = x < nwords ? bitmap[(int64_t)r * nwords + x] : 0u;
+        const int c = __popc(b);
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int up = __shfl_up(incl, off);
+            if (lane >= off) incl += up;
+        }
+        int pos = base + incl - c;
+        while (b) {
+            const int k = __ffs(b) - 1;
+            b &= b - 1;
+            col_idx[pos++] = 32 * x + k;
+        }
+        base += __shfl(incl, 63);
+    }
+}
+
 }  // namespace
 
-hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* ws, hipStream_t stream) {
+namespace {
+
+// Pooled queries, pooled keys of the candidates not yet cached, the overlap
+// row flags (when wanted) and the selection keys of every row; the bias is
+// applied only to rows with coverage >= eta_cov when coverage is given.
+void launch_pool_score(const bsa_route_args* a, const RouteLayout& lay, void* ws, const float* coverage,
+                       double eta_cov, bool want_flags, hipStream_t stream) {
     char* w = static_cast<char*>(ws);
     double* qbar = reinterpret_cast<double*>(w + lay.qbar);
     const int n_cand = lay.n_cand;
     double* kbar = lay.kbar_in_ws ? reinterpret_cast<double*>(w + lay.kbar) : a->kpool;
     const int64_t kbar_head_blocks = (!lay.kbar_in_ws && a->kpool_head_blocks > 0) ? a->kpool_head_blocks : n_cand;
     double* keys = lay.keys_in_ws ? reinterpret_cast<double*>(w + lay.keys) : a->sel_keys;
-    int32_t* keff = reinterpret_cast<int32_t*>(w + lay.keff);
     int32_t* flags = reinterpret_cast<int32_t*>(w + lay.flags);
     const bool bf16 = a->dtype == BSA_BF16;
 
-    // 1. pooled queries
+    // pooled queries
     {
         dim3 grid((a->nqb + 3) / 4, a->heads);
         if (bf16)
@@ -524,7 +816,7 @@ hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* w
             hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kThreads), 0, stream, a->q, a->q_head_stride, a->d,
                                a->block, a->q_block_len, 0, a->nqb, qbar, (int64_t)a->nqb);
     }
-    // 2. pooled keys of the candidates not yet in the cache
+    // pooled keys of the candidates not yet in the cache
     const int kb0 = a->kpool ? a->kpool_valid_blocks : 0;
     if (n_cand > kb0) {
         const int nb = n_cand - kb0;
@@ -536,18 +828,30 @@ hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* w
             hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kThreads), 0, stream, a->k, a->k_head_stride, a->d,
                                a->block, a->kv_block_len, kb0, nb, kbar, kbar_head_blocks);
     }
-    // 3. overlap row flags (for the fallback counts)
-    const bool want_flags = a->overlap && a->fallback_counts && n_cand > 0;
+    // overlap row flags (for the fallback counts)
     if (want_flags)
         hipLaunchKernelGGL(overlap_flags_kernel, dim3(a->nqb), dim3(kThreads), 0, stream, a->overlap,
                            a->overlap_row_stride, n_cand, a->tau, flags);
-    // 4. selection keys
+    // selection keys
     if (n_cand > 0) {
         dim3 grid((n_cand + kScoreJ - 1) / kScoreJ, a->heads, (a->nqb + kScoreRows - 1) / kScoreRows);
         hipLaunchKernelGGL(score_kernel, grid, dim3(kThreads), 0, stream, qbar, kbar, kbar_head_blocks, a->nqb,
                            n_cand, a->d, a->scale, a->overlap, a->overlap_row_stride, a->lambda, a->g_ref, a->tau,
-                           keys);
+                           coverage, eta_cov, keys);
     }
+}
+
+}  // namespace
+
+hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* ws, hipStream_t stream) {
+    char* w = static_cast<char*>(ws);
+    const int n_cand = lay.n_cand;
+    double* keys = lay.keys_in_ws ? reinterpret_cast<double*>(w + lay.keys) : a->sel_keys;
+    int32_t* keff = reinterpret_cast<int32_t*>(w + lay.keff);
+    int32_t* flags = reinterpret_cast<int32_t*>(w + lay.flags);
+    const bool want_flags = a->overlap && a->fallback_counts && n_cand > 0;
+    // 1-4. pooled queries and keys, overlap flags, selection keys
+    launch_pool_score(a, lay, ws, nullptr, 0.0, want_flags, stream);
     // 5. list lengths and row pointers
     hipLaunchKernelGGL(rowptr_kernel, dim3(1), dim3(1024), 0, stream, a->heads, a->nqb, a->nkb, n_cand, a->block,
                        a->q_block_len, a->kv_block_len, a->k_per_row ? 0 : a->k_fixed, a->k_per_row,
@@ -567,6 +871,37 @@ hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* w
     else
         BSA_TOPK(64);
 #undef BSA_TOPK
+    return hipGetLastError();
+}
+
+hipError_t launch_materialize(const bsa_route_args* a, const bsa_materialize_args* m, const RouteLayout& lay,
+                              void* ws, hipStream_t stream) {
+    char* w = static_cast<char*>(ws);
+    const double* keys = lay.keys_in_ws ? reinterpret_cast<const double*>(w + lay.keys) : a->sel_keys;
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(w + lay.bitmap);
+    int32_t* counts = reinterpret_cast<int32_t*>(w + lay.counts);
+    const int nkb = a->nkb, rows = a->heads * a->nqb;
+    const int nwords = (nkb + 31) / 32;
+    launch_pool_score(a, lay, ws, m->coverage, m->eta_cov, false, stream);
+    const int pb = m->prev_begin < nkb ? m->prev_begin : nkb, pe = m->prev_end < nkb ? m->prev_end : nkb;
+    const int rb = m->ref_begin < nkb ? m->ref_begin : nkb, re = m->ref_end < nkb ? m->ref_end : nkb;
+    const dim3 grid((rows + kThreads / 64 - 1) / (kThreads / 64));
+#define BSA_MAT(KPL)                                                                                            \
+    hipLaunchKernelGGL(materialize_kernel<KPL>, grid, dim3(kThreads), 0, stream, keys, rows, a->nqb, nkb,        \
+                       a->block, a->q_block_len, a->kv_block_len, m->coverage, m->eta_cov, m->k_cov, m->k_unc,  \
+                       m->mass, pb, pe, m->window, m->window_len, m->window_stride, rb, re, nwords, bitmap, counts)
+    if (nkb <= 64 * 8)
+        BSA_MAT(8);
+    else if (nkb <= 64 * 16)
+        BSA_MAT(16);
+    else if (nkb <= 64 * 32)
+        BSA_MAT(32);
+    else
+        BSA_MAT(64);
+#undef BSA_MAT
+    hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(1024), 0, stream, counts, rows, a->row_ptr);
+    hipLaunchKernelGGL(emit_lists_kernel, grid, dim3(kThreads), 0, stream, bitmap, rows, nwords, a->row_ptr,
+                       a->col_idx);
     return hipGetLastError();
 }
 

@@ -106,6 +106,7 @@ size_t route_layout(const bsa_route_args* a, RouteLayout* lay) {
     off = align256(off + sizeof(int32_t) * ((size_t)a->heads * a->nqb + 8));
     lay->flags = off;
     off = align256(off + sizeof(int32_t) * ((size_t)a->nqb + 8));
+    lay->bitmap = lay->counts = off;
     lay->total = off;
     return off;
 }
@@ -163,6 +164,77 @@ int validate_route(const bsa_route_args* a, RouteLayout* lay) {
     return BSA_OK;
 }
 
+int validate_materialize(const bsa_route_args* a, const bsa_materialize_args* m, RouteLayout* lay) {
+    if (!a) return fail(BSA_EINVAL, "args is NULL");
+    if (!m) return fail(BSA_EINVAL, "materialize args is NULL");
+    if (m->struct_size != sizeof(bsa_materialize_args))
+        return fail(BSA_EINVAL, "struct_size %zu != sizeof(bsa_materialize_args) %zu", m->struct_size,
+                    sizeof(bsa_materialize_args));
+    if (a->struct_size == sizeof(bsa_route_args)) {
+        if (a->k_per_row) return fail(BSA_EINVAL, "k_per_row must be NULL: the budgets are k_cov and k_unc");
+        if (a->n_dense_tail_blocks != 0)
+            return fail(BSA_EINVAL, "n_dense_tail_blocks must be 0: every KV block is a candidate");
+        if (a->fallback_counts) return fail(BSA_EINVAL, "fallback_counts must be NULL (not produced)");
+    }
+    // the router's own checks, with the top-K budget out of the way
+    bsa_route_args base = *a;
+    base.k_fixed = 0;
+    base.k_max = 0;
+    const int st = validate_route(&base, lay);
+    if (st != BSA_OK) return st;
+    if (m->k_cov < 0) return fail(BSA_EINVAL, "k_cov %d < 0", m->k_cov);
+    if (m->k_unc < 0 || m->k_unc > kMaxUncovered)
+        return fail(m->k_unc < 0 ? BSA_EINVAL : BSA_EUNSUPPORTED, "k_unc %d outside [0, %d]", m->k_unc,
+                    kMaxUncovered);
+    if (!(m->eta_cov == m->eta_cov)) return fail(BSA_EINVAL, "eta_cov is NaN");
+    if (!(m->mass == m->mass)) return fail(BSA_EINVAL, "mass is NaN");
+    if (m->prev_begin < 0 || m->prev_end < m->prev_begin)
+        return fail(BSA_EINVAL, "previous-chunk range [%d, %d) invalid", m->prev_begin, m->prev_end);
+    if (m->ref_begin < 0 || m->ref_end < m->ref_begin)
+        return fail(BSA_EINVAL, "reference range [%d, %d) invalid", m->ref_begin, m->ref_end);
+    if (m->window && (!m->window_len || m->window_stride < 0))
+        return fail(BSA_EINVAL, "window needs window_len and window_stride >= 0");
+    const int nkb = a->nkb;
+    auto clip = [nkb](int x) { return x < nkb ? x : nkb; };
+    const int64_t n_prev = clip(m->prev_end) - clip(m->prev_begin);
+    const int64_t n_ref = clip(m->ref_end) - clip(m->ref_begin);
+    int64_t per_row = n_prev;
+    if (m->k_cov > per_row) per_row = m->k_cov;
+    if (m->k_unc > per_row) per_row = m->k_unc;
+    per_row += (m->window ? m->window_stride : 0) + n_ref;
+    if (per_row > nkb) per_row = nkb;
+    const int64_t need = (int64_t)a->heads * a->nqb * per_row;
+    if (a->col_capacity < need)
+        return fail(BSA_EINVAL,
+                    "col_capacity %lld < heads*nqb*min(nkb, max(prev, k_cov, k_unc) + window_stride + ref) = %lld",
+                    (long long)a->col_capacity, (long long)need);
+    size_t off = lay->total;
+    lay->bitmap = off;
+    off = align256(off + sizeof(uint32_t) * (size_t)a->heads * a->nqb * ceil_div(nkb, 32));
+    lay->counts = off;
+    off = align256(off + sizeof(int32_t) * ((size_t)a->heads * a->nqb + 8));
+    lay->total = off;
+    return BSA_OK;
+}
+
+int validate_block_window(const int32_t* perm, const int32_t* inv, int T, int H, int W, int block, int q_chunk,
+                          const int32_t* window, const int32_t* window_len, int window_stride) {
+    if (T < 1 || H < 1 || W < 1) return fail(BSA_EINVAL, "grid %d x %d x %d: dimensions must be >= 1", T, H, W);
+    const int64_t L = (int64_t)T * H * W;
+    if (L > INT32_MAX) return fail(BSA_EINVAL, "grid %d x %d x %d exceeds 2^31-1 cells", T, H, W);
+    if (!perm || !inv || !window || !window_len)
+        return fail(BSA_EINVAL, "perm, inv, window and window_len must be non-NULL");
+    if (block < 1) return fail(BSA_EINVAL, "block %d < 1", block);
+    if (q_chunk < 0) return fail(BSA_EINVAL, "q_chunk %d < 0", q_chunk);
+    const int64_t nbc = ceil_div(L, block);
+    if (nbc > kMaxWindowChunkBlocks)
+        return fail(BSA_EUNSUPPORTED, "%lld blocks per chunk exceed %d", (long long)nbc, kMaxWindowChunkBlocks);
+    if (window_stride < 2 * nbc)
+        return fail(BSA_EINVAL, "window_stride %d < 2 * blocks per chunk (%lld)", window_stride, (long long)(2 * nbc));
+    if (((int64_t)q_chunk + 1) * nbc > INT32_MAX) return fail(BSA_EINVAL, "block indices exceed 2^31-1");
+    return BSA_OK;
+}
+
 }  // namespace bsa
 
 extern "C" {
@@ -185,6 +257,12 @@ const char* bsa_last_error_detail(void) { return bsa::last_detail(); }
 size_t bsa_route_workspace_size(const bsa_route_args* args) {
     bsa::RouteLayout lay;
     if (bsa::validate_route(args, &lay) != BSA_OK) return 0;
+    return lay.total;
+}
+
+size_t bsa_route_materialize_workspace_size(const bsa_route_args* args, const bsa_materialize_args* margs) {
+    bsa::RouteLayout lay;
+    if (bsa::validate_materialize(args, margs, &lay) != BSA_OK) return 0;
     return lay.total;
 }
 

@@ -218,6 +218,116 @@ int bsa_route_topk(const bsa_route_args* args, void* workspace, size_t workspace
                    hipStream_t stream);
 
 /*
+ * bsa_gilbert_block_window -- the local window of every query block of one
+ * chunk, in block indices of the Gilbert-ordered history.
+ * [Velox -- Methodology, Step 5 (routes are unioned with a 26-neighbour
+ *  local window in the global-aligned Gilbert block ordering); Key
+ *  Contributions 3 (global-aligned Gilbert KV storage)]
+ *
+ * perm, inv      device int32[T*H*W]: a chunk grid's curve and its inverse
+ *                (bsa_gilbert_index).  Chunk c of the history occupies
+ *                blocks c*n_blocks .. (c+1)*n_blocks - 1, n_blocks =
+ *                ceil(T*H*W / block), its tokens in curve order.
+ * window         device int32[n_blocks][window_stride]: row b receives,
+ *                ascending, the absolute indices of the KV blocks holding
+ *                any cell of the 3 x 3 x 3 neighbourhood (the cell itself
+ *                included, cut at the spatial border) of any token of
+ *                query block b of chunk q_chunk.  A step back in time from
+ *                a chunk's first frame lands in the last frame of chunk
+ *                q_chunk - 1 (none for q_chunk = 0); a step forward from its
+ *                last frame would land in chunk q_chunk + 1, which is not
+ *                history and is left out.  Entries past window_len[b] are
+ *                not written.
+ * window_len     device int32[n_blocks]: entries of each row (<= 2*n_blocks).
+ * Errors: BSA_EINVAL (null pointers, a dimension < 1, block < 1,
+ * q_chunk < 0, window_stride < 2*n_blocks, block indices past 2^31-1),
+ * BSA_EUNSUPPORTED (n_blocks > 1024).
+ */
+int bsa_gilbert_block_window(const int32_t* perm, const int32_t* inv, int T, int H, int W, int block,
+                             int q_chunk, int32_t* window, int32_t* window_len, int window_stride,
+                             hipStream_t stream);
+
+/*
+ * Route materialisation arguments.  Set struct_size =
+ * sizeof(bsa_materialize_args).
+ * [Velox -- Methodology, Step 3 (a coverage score per query block: the
+ *  share of its tokens inside a valid historical slab); Step 4 (the fusion
+ *  applies to well-covered blocks); Step 5 (reservation, top-scoring fill
+ *  up to K_cov, cumulative-mass prefix capped at K_unc, local window and
+ *  reference blocks outside the budget); the calibrated eta_cov = 0.9,
+ *  K_cov = 80, K_unc = 150 close the Methodology section]
+ *
+ *  coverage       device float32[nqb] (NULL: every query block is well
+ *                 covered); shared by all heads.  Query block i is well
+ *                 covered when coverage[i] >= eta_cov.
+ *  k_cov          budget of a well-covered row (reserved blocks count
+ *                 towards it).
+ *  k_unc          cap of a poorly covered row's prefix, 0 .. 256.
+ *  mass           cumulative-mass threshold of a poorly covered row.
+ *  prev_begin, prev_end  block range [begin, end) reserved by every
+ *                 well-covered row (the previous chunk); clipped to nkb.
+ *  window, window_len, window_stride  per-query-block window rows as
+ *                 written by bsa_gilbert_block_window (NULL: none); row i
+ *                 holds window_len[i] (clamped to [0, window_stride])
+ *                 absolute block indices; indices outside [0, nkb) are
+ *                 ignored.
+ *  ref_begin, ref_end    reference-frame block range [begin, end); clipped
+ *                 to nkb.
+ */
+typedef struct bsa_materialize_args {
+    size_t struct_size;
+    const float* coverage;
+    double eta_cov;
+    int k_cov;
+    int k_unc;
+    double mass;
+    int prev_begin;
+    int prev_end;
+    const int32_t* window;
+    const int32_t* window_len;
+    int window_stride;
+    int ref_begin;
+    int ref_end;
+} bsa_materialize_args;
+
+/* Bytes of workspace bsa_route_materialize needs (0 if the arguments are
+ * invalid). */
+size_t bsa_route_materialize_workspace_size(const bsa_route_args* args,
+                                            const bsa_materialize_args* margs);
+
+/*
+ * bsa_route_materialize -- the routed lists of every (head, query block)
+ * row: pool and score as bsa_route_topk (the overlap bias only on
+ * well-covered rows; every KV block is a candidate), then per row:
+ *  - well covered: the visible blocks of [prev_begin, prev_end), all of
+ *    them, plus the max(0, k_cov - reserved) others with the largest
+ *    kappa (ties to the lower index);
+ *  - poorly covered: with p = softmax(s) over the visible blocks and the
+ *    visible blocks ordered by (s descending, index ascending), the
+ *    shortest prefix whose running sum of p reaches mass, at most k_unc
+ *    blocks (all k_unc, or all visible blocks, if none reaches it);
+ *  - either: every visible block of its window row and of
+ *    [ref_begin, ref_end).
+ * Only blocks with a valid token enter a list; a query block with no valid
+ * token gets an empty list.  Lists are ascending and duplicate-free and are
+ * written packed: row r's list is col_idx[row_ptr[r] .. row_ptr[r+1]-1].
+ * Of bsa_route_args, k_fixed and k_max are ignored; k_per_row and
+ * fallback_counts must be NULL and n_dense_tail_blocks 0; kpool and
+ * sel_keys work as for bsa_route_topk (sel_keys then hold s on poorly
+ * covered rows).  The running sum is taken in float64 in list order, so a
+ * sum that reaches mass within rounding can end the prefix one block apart
+ * from another summation order.
+ * workspace: as for bsa_route_topk, bsa_route_materialize_workspace_size
+ * bytes.
+ * Errors: BSA_EINVAL (arguments; col_capacity below heads*nqb*min(nkb,
+ * max(prev range, k_cov, k_unc) + window_stride + ref range)),
+ * BSA_EUNSUPPORTED (k_unc > 256, more than 4096 KV blocks, d or block),
+ * BSA_EWORKSPACE.
+ */
+int bsa_route_materialize(const bsa_route_args* args, const bsa_materialize_args* margs,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * bsa_block_sparse_attn -- attention of every query block over its listed
  * KV blocks.
  * [Velox -- Methodology, Step 6: an indexed block-sparse kernel, not a dense

@@ -145,6 +145,58 @@ def test_route_rejects_and_sizes():
     assert 0 < small < need
 
 
+def _mat_args(**over):
+    m = bsa.MaterializeArgs()
+    m.struct_size = ctypes.sizeof(bsa.MaterializeArgs)
+    m.eta_cov, m.k_cov, m.k_unc, m.mass = 0.9, 80, 150, 0.9
+    m.prev_begin, m.prev_end = 1665, 1702
+    m.window, m.window_len, m.window_stride = 0x90000, 0xA0000, 74
+    for k, v in over.items():
+        setattr(m, k, v)
+    return m
+
+
+def test_materialize_rejects_and_sizes():
+    # 40 heads x 37 query blocks; per row min(1776, max(37, 80, 150) + 74 + 0) = 224
+    cap = 1480 * 224
+    a, m = _route_args(col_capacity=cap), _mat_args()
+    need = lib.bsa_route_materialize_workspace_size(ctypes.byref(a), ctypes.byref(m))
+    # the router's workspace plus a 56-word bitmap and a count per row
+    assert need >= lib.bsa_route_workspace_size(ctypes.byref(a)) + 4 * 1480 * 56
+    f = lambda a, m, ws=FAKE, n=need: lib.bsa_route_materialize(ctypes.byref(a), ctypes.byref(m), ws, n, None)
+    assert f(a, m, None, 0) == bsa.BSA_EWORKSPACE
+    assert f(a, m, FAKE, need - 1) == bsa.BSA_EWORKSPACE
+    assert f(_route_args(col_capacity=cap - 1), m) == bsa.BSA_EINVAL
+    assert "col_capacity" in lib.bsa_last_error_detail().decode()
+    assert f(a, _mat_args(struct_size=8)) == bsa.BSA_EINVAL
+    assert lib.bsa_route_materialize_workspace_size(ctypes.byref(a), ctypes.byref(_mat_args(struct_size=8))) == 0
+    assert f(a, _mat_args(k_unc=257)) == bsa.BSA_EUNSUPPORTED
+    assert f(a, _mat_args(k_cov=-1)) == bsa.BSA_EINVAL
+    assert f(a, _mat_args(mass=float("nan"))) == bsa.BSA_EINVAL
+    assert f(a, _mat_args(prev_begin=5, prev_end=4)) == bsa.BSA_EINVAL
+    assert f(a, _mat_args(ref_begin=-1, ref_end=4)) == bsa.BSA_EINVAL
+    assert f(a, _mat_args(window_len=None)) == bsa.BSA_EINVAL
+    assert f(_route_args(col_capacity=cap, k_per_row=0x70000), m) == bsa.BSA_EINVAL
+    assert f(_route_args(col_capacity=cap, n_dense_tail_blocks=37), m) == bsa.BSA_EINVAL
+    assert f(_route_args(col_capacity=cap, fallback_counts=0x70000), m) == bsa.BSA_EINVAL
+    assert f(_route_args(col_capacity=cap, nkb=5000), m) == bsa.BSA_EUNSUPPORTED
+    # a reference range past nkb is clipped, so it adds nothing beyond nkb
+    # (validation passes, so the missing workspace is what is reported)
+    assert f(_route_args(col_capacity=1480 * 1776), _mat_args(ref_begin=0, ref_end=10**6), None, 0) \
+        == bsa.BSA_EWORKSPACE
+
+
+def test_block_window_rejects():
+    f = lib.bsa_gilbert_block_window
+    assert f(FAKE, None, 3, 30, 52, 128, 1, FAKE, FAKE, 74, None) == bsa.BSA_EINVAL
+    assert f(FAKE, FAKE, 0, 30, 52, 128, 1, FAKE, FAKE, 74, None) == bsa.BSA_EINVAL
+    assert f(FAKE, FAKE, 3, 30, 52, 0, 1, FAKE, FAKE, 74, None) == bsa.BSA_EINVAL
+    assert f(FAKE, FAKE, 3, 30, 52, 128, -1, FAKE, FAKE, 74, None) == bsa.BSA_EINVAL
+    assert f(FAKE, FAKE, 3, 30, 52, 128, 1, FAKE, FAKE, 73, None) == bsa.BSA_EINVAL
+    assert "window_stride" in lib.bsa_last_error_detail().decode()
+    assert f(FAKE, FAKE, 3, 30, 52, 4, 1, FAKE, FAKE, 4000, None) == bsa.BSA_EUNSUPPORTED
+
+
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
 def test_host_descent_matches_oracle(tmp_path):

@@ -30,7 +30,7 @@ import numpy as np
 import torch
 
 # stream tags
-T_QNOISE, T_KNOISE, T_V, T_QOFF, T_KOFF, T_OVERLAP, T_ZROWS, T_KROW, T_FIELD, T_MIXQ, T_MIXK = range(11)
+T_QNOISE, T_KNOISE, T_V, T_QOFF, T_KOFF, T_OVERLAP, T_ZROWS, T_KROW, T_FIELD, T_MIXQ, T_MIXK, T_COVER = range(12)
 
 CHUNK_GRID = (3, 30, 52)           # latent frames x height x width of one chunk
 CHUNK_TOKENS = 3 * 30 * 52         # 4680
@@ -84,6 +84,7 @@ class Workload:
     k: Optional[torch.Tensor] = None
     v: Optional[torch.Tensor] = None
     overlap: Optional[np.ndarray] = None  # [nqb][n_candidates] float32
+    coverage: Optional[np.ndarray] = None  # [nqb] float32
     lam: float = 2.0
     g_ref: float = 0.2
     tau: float = 0.1
@@ -213,6 +214,28 @@ def c4(c: int = 48, heads=None, n_store_chunks: Optional[int] = None) -> Workloa
                     notes=f"store chunks allocated: {n_store}")
 
 
+def c4_routes(c: int = 48, heads=None, n_store_chunks: Optional[int] = None) -> Workload:
+    """C4 plus the inputs of route materialisation: a coverage per query
+    block and an overlap with every KV block.
+
+    Coverage is a share of a block's valid tokens, n / q_len with n =
+    round(u * q_len), u ~ Beta(4, 0.7) (P(u >= 0.9) is about 0.5);
+    three blocks are set to exactly 0.9 in float32 (just below 0.9 in
+    float64) and two to 1.  Overlap ~ Beta(0.5, 2) in float64, stored as
+    float32, over the whole history."""
+    w = c4(c, heads, n_store_chunks)
+    rng = _rng(1005, T_COVER, 0, 0)
+    u = rng.beta(4.0, 0.7, size=w.nqb)
+    cov = np.round(u * w.q_len) / w.q_len
+    pick = rng.choice(w.nqb, 5, replace=False)
+    cov[pick[:3]] = np.float32(0.9)
+    cov[pick[3:]] = 1.0
+    w.coverage = cov.astype(np.float32)
+    w.overlap = _rng(1005, T_OVERLAP, 0, 0).beta(0.5, 2.0, size=(w.nqb, w.nkb)).astype(np.float32)
+    w.name = f"C4R-materialised-routes-c{c}-bf16"
+    return w
+
+
 def _field_params(seed):
     """Rank-8 smooth field: each component is a sum of 4 cosines with integer
     wave numbers in {0,1,2}^3 (not all zero) over (frame/144, y/30, x/52)
@@ -303,7 +326,7 @@ def c5(heads=None, n_chunks: int = 48) -> Workload:
                     q_raster=q_r, k_raster=k_r, v_raster=v_r, head_ids=head_ids)
 
 
-REGISTRY = {"C1": c1, "C2": c2, "C3": c3, "C4": c4, "C5": c5}
+REGISTRY = {"C1": c1, "C2": c2, "C3": c3, "C4": c4, "C5": c5, "C4R": c4_routes}
 
 
 def get(name: str, **kw) -> Workload:
