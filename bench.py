@@ -19,7 +19,11 @@ appending -- then score, top-K, CSR); block-sparse attention; inverse
 permutation of O.  The step time with every history block re-pooled is
 reported beside it (``step_full_k_pool_ms``), and so is the same step
 replayed from a HIP graph (``step_hip_graph_ms``: identical kernels, no
-launch gaps; every replay is checked bitwise against the eager step).
+launch gaps; every replay is checked bitwise against the eager step), and
+the step with the materialised route instead of the top-K
+(``materialized``: coverage-gated budgets, previous-chunk reservation,
+cumulative-mass prefix and the local window, on seeded coverage and
+overlap).
 
 Printed: one JSON line.  ``value`` = effective TFLOP/s of the step (valid
 selected (query, key) pairs x 4 d FLOP, divided by the step time).  The
@@ -147,6 +151,60 @@ def step_graph_ms(st, reps: int):
     return e0.elapsed_time(e1) / reps
 
 
+def materialized(st, reps: int):
+    """The step with the materialised route instead of the fixed top-K, at
+    the same chunk: coverage-gated budgets (eta_cov 0.9, K_cov 80, K_unc
+    150, mass 0.9), the previous chunk reserved, the chunk's local window
+    rebuilt on the GPU, no reference blocks; seeded coverage and overlap
+    (``workloads.route_inputs``).  Times the whole step, the routing part
+    (window + materialisation) and the attention launch."""
+    import numpy as np
+    import torch
+
+    import workloads
+
+    w, ra = st["w"], st["ra"]
+    dev = ra.device
+    cov, ov = workloads.route_inputs(w.q_len, w.nkb)
+    mat = dict(coverage=torch.from_numpy(cov).to(dev), k_cov=80, k_unc=150, mass=0.9)
+    overlap = torch.from_numpy(ov).to(dev)
+
+    def one(events=None):
+        return ra.step(st["q_raster"], st["k_raster"], st["v_raster"], st["cur"], overlap=overlap,
+                       materialize=mat, attn_events=events)
+
+    for _ in range(2):
+        one()
+    torch.cuda.synchronize()
+    events = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        _, r = one(events)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / reps
+    attn_ms = sum(a.elapsed_time(b) for a, b in events) / len(events)
+    # the routing part alone (the pooled keys are cached, as in the step)
+    e0.record()
+    for _ in range(reps):
+        ra.route_materialized(st["cur"], overlap=overlap, **mat)
+    e1.record()
+    torch.cuda.synchronize()
+    route_ms = e0.elapsed_time(e1) / reps
+    wc = work_counts(r["row_ptr"], r["col_idx"], w.q_len, w.k_len, w.heads, w.nqb, w.bs, w.d)
+    rp = r["row_ptr"].cpu().numpy()
+    lens = np.diff(rp)
+    return {"ms_per_step": round(ms_step, 4), "route_ms": round(route_ms, 4), "attn_ms": round(attn_ms, 4),
+            "step_effective_tflops": round(wc["flop"] / (ms_step * 1e-3) / 1e12, 2),
+            "attn_effective_tflops": round(wc["flop"] / (attn_ms * 1e-3) / 1e12, 2),
+            "attn_achieved_gbs": round(wc["alg_bytes"] / (attn_ms * 1e-3) / 1e9, 1),
+            "list_len_mean": round(float(lens.mean()), 2), "list_len_min": int(lens.min()),
+            "list_len_max": int(lens.max()), "covered_query_blocks": int((cov >= 0.9).sum()),
+            "query_blocks": int(w.nqb), "params": "eta_cov 0.9, K_cov 80, K_unc 150, mass 0.9, window on, "
+                                                   "no reference blocks"}
+
+
 def cpu_baseline(st, n_heads=2):
     """Time the float64 oracle (route + attention) on ``n_heads`` heads of the
     same workload; report effective TFLOP/s on that sample."""
@@ -272,6 +330,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=40)
     ap.add_argument("--dense", action="store_true", help="also time dense attention at the same chunk")
+    ap.add_argument("--no-materialized", action="store_true",
+                    help="skip timing the step with the materialised route")
     ap.add_argument("--sweep", default=None, help="write a chunk 1..C sparse/dense sweep to this JSONL file")
     ap.add_argument("--rollout", default=None,
                     help="write a 1..C chunk rollout (append, route with the pooled-key cache, attend) to this JSONL file")
@@ -394,6 +454,8 @@ def main():
         dflop = 4 * w.d * int(w.q_len.sum()) * int(w.k_len.sum()) * w.heads
         out["dense"] = {"ms_per_call": round(dms, 3), "effective_tflops": round(dflop / (dms * 1e-3) / 1e12, 2),
                         "speedup_sparse_vs_dense": round(dms / attn_ms, 2)}
+    if not args.no_materialized:
+        out["materialized"] = materialized(st, max(1, min(args.steps, 10)))
     if args.sweep:
         sweep(st, args.sweep)
     if args.rollout:

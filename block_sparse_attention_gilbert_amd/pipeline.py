@@ -15,7 +15,12 @@ Per call (``RoutedAttention.step``):
 3. the router pools, scores, fuses and selects over the visible history.
    The pooled keys of the history are kept in a float64 cache across calls
    (the store only grows by appending), so a call pools only the blocks
-   appended or rewritten since the previous call;
+   appended or rewritten since the previous call.  The selection is either
+   a top-K per row, or the materialised route (``materialize=``): coverage-
+   gated budgets, the previous chunk's reservation, the cumulative-mass
+   prefix, and the chunk's local window in Gilbert block order (built on
+   the GPU for each call) plus reference blocks [Velox -- Methodology,
+   Step 5];
 4. block-sparse attention over the selected blocks;
 5. O is permuted back to raster order.
 
@@ -30,8 +35,8 @@ from typing import Optional
 
 import torch
 
-from . import (_check, _lib, _ptr, _stream, block_sparse_attn, dense_attn, gilbert_index, gilbert_perm,
-               route_capacity, route_topk)
+from . import (_check, _lib, _ptr, _stream, block_sparse_attn, dense_attn, gilbert_block_window, gilbert_index,
+               gilbert_perm, materialize_capacity, route_capacity, route_materialize, route_topk)
 
 
 def block_lengths(tokens: int, block: int, n_chunks: int = 1, device="cuda") -> torch.Tensor:
@@ -82,6 +87,12 @@ class RoutedAttention:
         self.use_kpool = use_kpool
         self.kpool = torch.empty((heads, nkb_max, d), dtype=torch.float64, device=device) if use_kpool else None
         self._kpool_valid = 0
+        # materialised routes: window rows of the current chunk, lists and
+        # workspace (allocated on first use)
+        self.window = torch.empty((self.nbc, 2 * self.nbc), dtype=torch.int32, device=device)
+        self.window_len = torch.empty(self.nbc, dtype=torch.int32, device=device)
+        self.mat_out = None
+        self.mat_workspace = None
 
     def invalidate_kpool(self, first_block: int = 0):
         """Forget cached pooled keys from ``first_block`` on (call after
@@ -102,27 +113,36 @@ class RoutedAttention:
 
     def step(self, q_raster, k_raster, v_raster, c: int, *, k_fixed: Optional[int] = None,
              k_per_row: Optional[torch.Tensor] = None, overlap: Optional[torch.Tensor] = None,
-             lam=2.0, g_ref=0.2, tau=0.1, refresh_index: bool = True, stream=None, attn_events=None):
+             lam=2.0, g_ref=0.2, tau=0.1, materialize: Optional[dict] = None, refresh_index: bool = True,
+             stream=None, attn_events=None):
         """One attention call for chunk ``c`` (0-based) over chunks 0..c.
         Returns ``(o_raster, route_out)``.  ``attn_events``: optional list
         that receives a (start, end) pair of timing events recorded around
-        the attention kernel on the stream it runs on."""
+        the attention kernel on the stream it runs on.  ``materialize``:
+        keyword arguments of ``route_materialize`` (``coverage``,
+        ``eta_cov``, ``k_cov``, ``k_unc``, ``mass``, ``ref_blocks``; plus
+        ``window=False`` to leave the local window out) to route with the
+        materialised lists instead of a top-K."""
         if refresh_index:
             self._index(stream)
         self.append(k_raster, v_raster, c, stream)
         gilbert_perm(q_raster, self.perm, block=self.block, dst=self.q_blk, stream=stream)
         r = self.route_and_attend(c, k_fixed=k_fixed, k_per_row=k_per_row, overlap=overlap, lam=lam, g_ref=g_ref,
-                                  tau=tau, stream=stream, attn_events=attn_events)
+                                  tau=tau, materialize=materialize, stream=stream, attn_events=attn_events)
         gilbert_perm(self.o_blk, self.perm, block=self.block, inverse=True, dst=self.o_raster, stream=stream)
         return self.o_raster, r
 
     def route_and_attend(self, c: int, *, k_fixed: Optional[int] = None, k_per_row: Optional[torch.Tensor] = None,
-                         overlap: Optional[torch.Tensor] = None, lam=2.0, g_ref=0.2, tau=0.1, stream=None,
-                         attn_events=None):
+                         overlap: Optional[torch.Tensor] = None, lam=2.0, g_ref=0.2, tau=0.1,
+                         materialize: Optional[dict] = None, stream=None, attn_events=None):
         """Route the already permuted queries over chunks 0..c of the store
         and attend; the result stays in Gilbert layout (``o_blk``, ``lse``)."""
         nkb = (c + 1) * self.nbc
         k_hist, v_hist = self.k_store[:, : nkb * self.block], self.v_store[:, : nkb * self.block]
+        if materialize is not None:
+            r = self.route_materialized(c, overlap=overlap, lam=lam, g_ref=g_ref, tau=tau, stream=stream,
+                                        **materialize)
+            return self._attend(r, nkb, k_hist, v_hist, stream, attn_events)
         tail = self.n_dense_tail_chunks * self.nbc
         kf = self.k_cap if k_fixed is None else k_fixed
         n_cand = nkb - tail
@@ -136,6 +156,40 @@ class RoutedAttention:
         self.workspace = r["workspace"]
         if self.use_kpool:
             self._kpool_valid = max(valid, n_cand)
+        return self._attend(r, nkb, k_hist, v_hist, stream, attn_events)
+
+    def route_materialized(self, c: int, *, coverage=None, eta_cov=0.9, k_cov=80, k_unc=150, mass=0.9,
+                           ref_blocks=(0, 0), window: bool = True, overlap=None, lam=2.0, g_ref=0.2, tau=0.1,
+                           stream=None):
+        """Materialised routes of the current queries over chunks 0..c:
+        chunk c-1 is the reserved previous chunk; the local window of chunk
+        c is rebuilt into the preallocated rows first."""
+        nkb = (c + 1) * self.nbc
+        k_hist = self.k_store[:, : nkb * self.block]
+        if window:
+            gilbert_block_window(self.perm, self.inv, self.grid, block=self.block, q_chunk=c,
+                                 out=(self.window, self.window_len), stream=stream)
+        prev = ((c - 1) * self.nbc, c * self.nbc) if c > 0 else (0, 0)
+        cap = materialize_capacity(self.heads, self.nbc, nkb, k_cov=k_cov, k_unc=k_unc, prev_blocks=prev,
+                                   window_stride=self.window.stride(0) if window else 0, ref_blocks=ref_blocks)
+        if self.mat_out is None or self.mat_out["col_idx"].numel() < cap:
+            self.mat_out = {"row_ptr": torch.empty(self.heads * self.nbc + 1, dtype=torch.int32, device=self.device),
+                            "col_idx": torch.empty(max(1, cap), dtype=torch.int32, device=self.device),
+                            "sel_keys": None}
+        valid = min(self._kpool_valid, nkb)
+        r = route_materialize(self.q_blk, k_hist, block=self.block, nqb=self.nbc, nkb=nkb, scale=self.scale,
+                              q_block_len=self.q_len, kv_block_len=self.kv_len[:nkb], overlap=overlap, lam=lam,
+                              g_ref=g_ref, tau=tau, coverage=coverage, eta_cov=eta_cov, k_cov=k_cov, k_unc=k_unc,
+                              mass=mass, prev_blocks=prev, window=self.window if window else None,
+                              window_len=self.window_len if window else None, ref_blocks=ref_blocks,
+                              kpool=self.kpool, kpool_valid_blocks=valid if self.use_kpool else 0,
+                              out=self.mat_out, workspace=self.mat_workspace, stream=stream)
+        self.mat_workspace = r["workspace"]
+        if self.use_kpool:
+            self._kpool_valid = max(valid, nkb)
+        return r
+
+    def _attend(self, r, nkb, k_hist, v_hist, stream, attn_events):
         if attn_events is not None:
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             ev[0].record(stream)

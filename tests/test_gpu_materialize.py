@@ -162,3 +162,39 @@ def test_materialize_all_covered_is_the_top_k_router():
                                 g_ref=w.g_ref)
         assert_lists_equal(l1[h], ref["lists"], "head %d" % h)
         assert_lists_equal(l2[h], ref["lists"], "cached head %d" % h)
+
+
+def test_pipeline_step_with_materialised_routes():
+    """One call of the chunked pipeline with the materialised route (window
+    rebuilt on the GPU inside the step): lists equal the oracle's, and the
+    attention over them matches the oracle within the bf16 bounds."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    from block_sparse_attention_gilbert_amd.pipeline import RoutedAttention
+    from oracle import attention as oatt
+
+    from helpers import BF16_MAX_ABS, BF16_MEAN_ABS, err_summary, valid_rows
+
+    c = 3
+    w = workloads.c4_routes(c=c, heads=[0, 5])
+    ra = RoutedAttention(workloads.CHUNK_GRID, w.heads, w.d, w.bs, c, device=dev, k_store=w.k.contiguous().to(dev),
+                         v_store=w.v.contiguous().to(dev))
+    ks, vs = ra.slot(c - 1)
+    q_r = bsa.gilbert_perm(w.q.to(dev), ra.perm, block=w.bs, inverse=True)
+    k_r = bsa.gilbert_perm(ks, ra.perm, block=w.bs, inverse=True)
+    v_r = bsa.gilbert_perm(vs, ra.perm, block=w.bs, inverse=True)
+    mat = dict(coverage=torch.from_numpy(w.coverage).to(dev), k_cov=80, k_unc=150, mass=0.9, ref_blocks=(0, 3))
+    _, r = ra.step(q_r, k_r, v_r, c - 1, overlap=torch.from_numpy(w.overlap).to(dev), materialize=mat)
+    torch.cuda.synchronize()
+    got = csr_lists(r["row_ptr"], r["col_idx"], w.heads, w.nqb)
+    win = om.block_window(gilbert_order(*workloads.CHUNK_GRID)[0], workloads.CHUNK_GRID, w.bs, c - 1)
+    vmask = valid_rows(w.q_len, w.bs)
+    for hi in range(w.heads):
+        q, k, v = f64(w.q[hi]), f64(w.k[hi]), f64(w.v[hi])
+        ref = om.materialize_head(q, k, w.q_len, w.k_len, w.bs, scale=w.scale, coverage=w.coverage, k_cov=80,
+                                  k_unc=150, mass=0.9, prev_blocks=((c - 2) * w.nqb, (c - 1) * w.nqb), windows=win,
+                                  ref_blocks=(0, 3), overlap=w.overlap, lam=w.lam, tau=w.tau, g_ref=w.g_ref)
+        assert_lists_equal(got[hi], ref["lists"], "head %d" % hi)
+        o_ref, _ = oatt.block_sparse_head(q, k, v, w.q_len, w.k_len, w.bs, ref["lists"], w.scale)
+        mx, mean = err_summary(f64(ra.o_blk[hi]), o_ref, vmask)
+        assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (hi, mx, mean)

@@ -214,24 +214,31 @@ def c4(c: int = 48, heads=None, n_store_chunks: Optional[int] = None) -> Workloa
                     notes=f"store chunks allocated: {n_store}")
 
 
-def c4_routes(c: int = 48, heads=None, n_store_chunks: Optional[int] = None) -> Workload:
-    """C4 plus the inputs of route materialisation: a coverage per query
-    block and an overlap with every KV block.
+def route_inputs(q_len: np.ndarray, nkb: int):
+    """Inputs of route materialisation for one query chunk: a coverage per
+    query block and an overlap with every KV block of the history.
 
     Coverage is a share of a block's valid tokens, n / q_len with n =
-    round(u * q_len), u ~ Beta(4, 0.7) (P(u >= 0.9) is about 0.5);
-    three blocks are set to exactly 0.9 in float32 (just below 0.9 in
-    float64) and two to 1.  Overlap ~ Beta(0.5, 2) in float64, stored as
-    float32, over the whole history."""
-    w = c4(c, heads, n_store_chunks)
+    round(u * q_len), u ~ Beta(4, 0.7) (P(u >= 0.9) is about 0.5); three
+    blocks are set to exactly 0.9 in float32 (just below 0.9 in float64) and
+    two to 1.  Overlap ~ Beta(0.5, 2) in float64, stored as float32.
+    Returns ``(coverage[nqb], overlap[nqb][nkb])``, both float32."""
+    q_len = np.asarray(q_len)
+    nqb = len(q_len)
     rng = _rng(1005, T_COVER, 0, 0)
-    u = rng.beta(4.0, 0.7, size=w.nqb)
-    cov = np.round(u * w.q_len) / w.q_len
-    pick = rng.choice(w.nqb, 5, replace=False)
+    u = rng.beta(4.0, 0.7, size=nqb)
+    cov = np.round(u * q_len) / np.maximum(q_len, 1)
+    pick = rng.choice(nqb, min(nqb, 5), replace=False)
     cov[pick[:3]] = np.float32(0.9)
     cov[pick[3:]] = 1.0
-    w.coverage = cov.astype(np.float32)
-    w.overlap = _rng(1005, T_OVERLAP, 0, 0).beta(0.5, 2.0, size=(w.nqb, w.nkb)).astype(np.float32)
+    overlap = _rng(1005, T_OVERLAP, nkb, 0).beta(0.5, 2.0, size=(nqb, nkb)).astype(np.float32)
+    return cov.astype(np.float32), overlap
+
+
+def c4_routes(c: int = 48, heads=None, n_store_chunks: Optional[int] = None) -> Workload:
+    """C4 plus the inputs of route materialisation (``route_inputs``)."""
+    w = c4(c, heads, n_store_chunks)
+    w.coverage, w.overlap = route_inputs(w.q_len, w.nkb)
     w.name = f"C4R-materialised-routes-c{c}-bf16"
     return w
 
