@@ -30,7 +30,8 @@ import numpy as np
 import torch
 
 # stream tags
-T_QNOISE, T_KNOISE, T_V, T_QOFF, T_KOFF, T_OVERLAP, T_ZROWS, T_KROW, T_FIELD, T_MIXQ, T_MIXK, T_COVER = range(12)
+(T_QNOISE, T_KNOISE, T_V, T_QOFF, T_KOFF, T_OVERLAP, T_ZROWS, T_KROW, T_FIELD, T_MIXQ, T_MIXK, T_COVER, T_SLAB,
+ T_DEPTH) = range(14)
 
 CHUNK_GRID = (3, 30, 52)           # latent frames x height x width of one chunk
 CHUNK_TOKENS = 3 * 30 * 52         # 4680
@@ -233,6 +234,70 @@ def route_inputs(q_len: np.ndarray, nkb: int):
     cov[pick[3:]] = 1.0
     overlap = _rng(1005, T_OVERLAP, nkb, 0).beta(0.5, 2.0, size=(nqb, nkb)).astype(np.float32)
     return cov.astype(np.float32), overlap
+
+
+def _rotation(yaw: float, pitch: float) -> np.ndarray:
+    cy_, sy = math.cos(yaw), math.sin(yaw)
+    cp, sp = math.cos(pitch), math.sin(pitch)
+    ry = np.array([[cy_, 0.0, sy], [0.0, 1.0, 0.0], [-sy, 0.0, cy_]])
+    rx = np.array([[1.0, 0.0, 0.0], [0.0, cp, -sp], [0.0, sp, cp]])
+    return ry @ rx
+
+
+def _slabs(rng, n_blocks, cam_of_frame, grid):
+    """1-3 slabs per block in distinct frames: a token rectangle (rows 2-7,
+    columns 4-13 tokens, inside the grid) and a depth interval (middle
+    3 + 10 u, thickness 10-40 % of it)."""
+    T, H, W = grid
+    ptr, cam, geom = [0], [], []
+    for b in range(n_blocks):
+        k = int(rng.integers(1, 4))
+        for f in sorted(rng.choice(T, size=min(k, T), replace=False)):
+            hh, ww = int(rng.integers(2, 8)), int(rng.integers(4, 14))
+            v0, u0 = int(rng.integers(0, H - hh + 1)), int(rng.integers(0, W - ww + 1))
+            zm = 3.0 + 10.0 * rng.random()
+            th = zm * rng.uniform(0.1, 0.4)
+            cam.append(cam_of_frame(b, int(f)))
+            geom.append((u0, v0, u0 + ww, v0 + hh, zm - th / 2.0, zm + th / 2.0))
+        ptr.append(len(cam))
+    return (np.asarray(ptr, dtype=np.int32), np.asarray(cam, dtype=np.int32),
+            np.asarray(geom, dtype=np.float64).reshape(-1, 6))
+
+
+def geometry_inputs(q_chunk: int, nbc: int, grid=CHUNK_GRID):
+    """Inputs of the geometric overlap and coverage for query chunk
+    ``q_chunk`` of a rollout: cameras of every frame so far, frustum slabs
+    of the historical blocks (chunks 0 .. q_chunk-1; the query chunk's own
+    blocks have none), slabs of the query blocks, and a depth per query
+    token.
+
+    Cameras (float64 [frames][16]: fx, fy, cx, cy, world-from-camera R
+    row-major, centre C) follow a path that moves 0.12 units forward and
+    0.04 sideways per latent frame while the view swings (yaw 0.3 sin(0.07
+    g), pitch 0.05 sin(0.11 g) for frame g); fx = fy = 36, principal point at
+    the grid centre, in token units.  Slabs: ``_slabs``.  Query depth: a
+    smooth field 4 + 3 (1 + sin(0.2 w + 0.5 t)) (h + 1) / H plus N(0, 0.1),
+    NaN (no depth) on the top three token rows, float32 raster [T][H][W]."""
+    T, H, W = grid
+    n_frames = T * (q_chunk + 1)
+    cams = np.zeros((n_frames, 16))
+    for g in range(n_frames):
+        R = _rotation(0.3 * math.sin(0.07 * g), 0.05 * math.sin(0.11 * g))
+        cams[g, :4] = (36.0, 36.0, W / 2.0, H / 2.0)
+        cams[g, 4:13] = R.reshape(-1)
+        cams[g, 13:16] = (0.04 * g, 0.0, 0.12 * g)
+    rng = _rng(1006, T_SLAB, q_chunk, 0)
+    h_ptr, h_cam, h_geom = _slabs(rng, q_chunk * nbc, lambda b, f: T * (b // nbc) + f, grid)
+    # the query chunk's own blocks carry no historical slab
+    h_ptr = np.concatenate([h_ptr, np.full(nbc, h_ptr[-1], dtype=np.int32)])
+    q_ptr, q_cam, q_geom = _slabs(_rng(1006, T_SLAB, q_chunk, 1), nbc, lambda b, f: T * q_chunk + f, grid)
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    depth = 4.0 + 3.0 * (1.0 + np.sin(0.2 * w + 0.5 * t)) * (h + 1) / H
+    depth = depth + _rng(1006, T_DEPTH, q_chunk, 0).normal(0.0, 0.1, size=depth.shape)
+    depth[:, :3, :] = np.nan
+    return dict(cams=cams, h_ptr=h_ptr, h_cam=h_cam, h_geom=h_geom, q_ptr=q_ptr, q_cam=q_cam, q_geom=q_geom,
+                frame_cam=np.arange(T * q_chunk, T * (q_chunk + 1), dtype=np.int32),
+                depth=depth.astype(np.float32), grid=tuple(grid))
 
 
 def c4_routes(c: int = 48, heads=None, n_store_chunks: Optional[int] = None) -> Workload:
