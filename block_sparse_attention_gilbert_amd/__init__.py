@@ -9,7 +9,8 @@ been built, importing this package raises ImportError; there is no fallback.
 
 Entry points (same names as the C ABI, without the ``bsa_`` prefix):
 ``gilbert_index``, ``gilbert_perm``, ``gilbert_block_window``,
-``route_topk`` (with ``route_workspace_size``), ``route_materialize`` (with
+``slab_overlap``, ``slab_coverage``, ``route_topk`` (with
+``route_workspace_size``), ``route_materialize`` (with
 ``route_materialize_workspace_size``), ``block_sparse_attn``,
 ``dense_attn``.
 """
@@ -88,6 +89,10 @@ _lib.bsa_route_materialize_workspace_size.argtypes = [ctypes.POINTER(RouteArgs),
 _lib.bsa_route_materialize.restype = _i
 _lib.bsa_route_materialize.argtypes = [ctypes.POINTER(RouteArgs), ctypes.POINTER(MaterializeArgs), _p,
                                        ctypes.c_size_t, _p]
+_lib.bsa_slab_overlap.restype = _i
+_lib.bsa_slab_overlap.argtypes = [_p, _i, _p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _i64, _p]
+_lib.bsa_slab_coverage.restype = _i
+_lib.bsa_slab_coverage.argtypes = [_p, _i, _p, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p]
 _lib.bsa_route_workspace_size.restype = ctypes.c_size_t
 _lib.bsa_route_workspace_size.argtypes = [ctypes.POINTER(RouteArgs)]
 _lib.bsa_route_topk.restype = _i
@@ -100,8 +105,8 @@ _lib.bsa_dense_attn.argtypes = _ATTN_COMMON + [_f, _p]
 
 EXPORTED = ("bsa_version", "bsa_strerror", "bsa_last_error_detail", "bsa_gilbert_index",
             "bsa_gilbert_perm", "bsa_gilbert_block_window", "bsa_route_workspace_size", "bsa_route_topk",
-            "bsa_route_materialize_workspace_size", "bsa_route_materialize", "bsa_block_sparse_attn",
-            "bsa_dense_attn")
+            "bsa_route_materialize_workspace_size", "bsa_route_materialize", "bsa_slab_overlap",
+            "bsa_slab_coverage", "bsa_block_sparse_attn", "bsa_dense_attn")
 
 
 class BsaError(RuntimeError):
@@ -229,6 +234,59 @@ def gilbert_block_window(perm: torch.Tensor, inv: torch.Tensor, grid, *, block: 
     return window, window_len
 
 
+# --------------------------------------------------------------------- geometry
+
+def _f64(t: Optional[torch.Tensor], name: str, cols: Optional[int] = None):
+    if t is None:
+        return None
+    if t.dtype != torch.float64 or not t.is_contiguous() or (cols is not None and (t.dim() != 2 or t.shape[1] != cols)):
+        raise ValueError("%s must be a contiguous float64 tensor%s" % (name, "" if cols is None else
+                                                                        " of shape [n][%d]" % cols))
+    return t
+
+
+def slab_overlap(cams, q_slab_ptr, q_slab_cam, q_slab_geom, h_slab_ptr, h_slab_cam, h_slab_geom, *,
+                 grid_n: int = 8, out: Optional[torch.Tensor] = None, stream=None):
+    """Overlap ``[nqb][nkb]`` float32 of query blocks with historical blocks
+    from their frustum slabs (CSR per block: ``*_ptr``, ``*_cam``,
+    ``*_geom`` float64 ``[n][6]``)."""
+    _need_gpu(cams, q_slab_ptr, q_slab_cam, q_slab_geom, h_slab_ptr, h_slab_cam, h_slab_geom, out)
+    cams = _f64(cams, "cams", 16)
+    q_slab_geom, h_slab_geom = _f64(q_slab_geom, "q_slab_geom", 6), _f64(h_slab_geom, "h_slab_geom", 6)
+    q_slab_ptr, h_slab_ptr = _i32(q_slab_ptr, "q_slab_ptr"), _i32(h_slab_ptr, "h_slab_ptr")
+    q_slab_cam, h_slab_cam = _i32(q_slab_cam, "q_slab_cam"), _i32(h_slab_cam, "h_slab_cam")
+    nqb, nkb = q_slab_ptr.numel() - 1, h_slab_ptr.numel() - 1
+    if out is None:
+        out = torch.empty((nqb, nkb), dtype=torch.float32, device=cams.device)
+    if out.dtype != torch.float32 or out.dim() != 2 or out.stride(1) != 1:
+        raise ValueError("out must be float32 [nqb][stride] with contiguous rows")
+    _check(_lib.bsa_slab_overlap(_ptr(cams), cams.shape[0], _ptr(q_slab_ptr), _ptr(q_slab_cam), _ptr(q_slab_geom),
+                                 nqb, q_slab_cam.numel(), _ptr(h_slab_ptr), _ptr(h_slab_cam), _ptr(h_slab_geom), nkb,
+                                 h_slab_cam.numel(), grid_n, _ptr(out), out.stride(0), _stream(stream)))
+    return out
+
+
+def slab_coverage(cams, perm, grid, frame_cam, depth, h_slab_cam, h_slab_geom, *, block: int,
+                  out: Optional[torch.Tensor] = None, stream=None):
+    """Coverage ``[ceil(T*H*W / block)]`` float32 of the query blocks of a
+    chunk by the historical slabs."""
+    _need_gpu(cams, perm, frame_cam, depth, h_slab_cam, h_slab_geom, out)
+    cams = _f64(cams, "cams", 16)
+    h_slab_geom = _f64(h_slab_geom, "h_slab_geom", 6)
+    T, H, W = grid
+    if depth.dtype != torch.float32 or not depth.is_contiguous() or depth.numel() != T * H * W:
+        raise ValueError("depth must be a contiguous float32 raster of T*H*W values")
+    nqb = -(-(T * H * W) // block)
+    if out is None:
+        out = torch.empty(nqb, dtype=torch.float32, device=cams.device)
+    _check(_lib.bsa_slab_coverage(_ptr(cams), cams.shape[0], _ptr(_i32(perm, "perm")), T, H, W, block,
+                                  _ptr(_i32(frame_cam, "frame_cam")), _ptr(depth),
+                                  _ptr(_i32(h_slab_cam, "h_slab_cam")), _ptr(h_slab_geom),
+                                  h_slab_cam.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+# --------------------------------------------------------------------- router
 # --------------------------------------------------------------------- router
 
 def _route_args(q, k, *, block, nqb, nkb, q_block_len, kv_block_len, scale, overlap, lam, g_ref, tau,
@@ -458,7 +516,7 @@ def dense_attn(q, k, v, *, block: int, scale: Optional[float] = None, q_block_le
     return out, lse
 
 
-__all__ = ["gilbert_index", "gilbert_perm", "gilbert_block_window", "route_topk", "route_workspace_size",
+__all__ = ["gilbert_index", "gilbert_perm", "gilbert_block_window", "slab_overlap", "slab_coverage", "route_topk", "route_workspace_size",
            "route_capacity", "route_materialize", "route_materialize_workspace_size", "materialize_capacity",
            "MaterializeArgs", "block_sparse_attn", "dense_attn", "version", "library", "BsaError", "RouteArgs", "EXPORTED",
            "BSA_OK", "BSA_EINVAL", "BSA_EUNSUPPORTED", "BSA_EWORKSPACE", "BSA_EHIP", "BSA_BF16", "BSA_F32"]

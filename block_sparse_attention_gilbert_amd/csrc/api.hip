@@ -71,6 +71,33 @@ int bsa_route_materialize(const bsa_route_args* args, const bsa_materialize_args
     return hip_status(bsa::launch_materialize(args, margs, lay, workspace, stream), "route_materialize launch");
 }
 
+int bsa_slab_overlap(const double* cams, int n_cams, const int32_t* q_slab_ptr, const int32_t* q_slab_cam,
+                     const double* q_slab_geom, int nqb, int n_q_slabs, const int32_t* h_slab_ptr,
+                     const int32_t* h_slab_cam, const double* h_slab_geom, int nkb, int n_h_slabs, int grid_n,
+                     float* overlap, int64_t overlap_row_stride, hipStream_t stream) {
+    bsa::clear_error();
+    const int st = bsa::validate_slab_overlap(cams, n_cams, q_slab_ptr, q_slab_cam, q_slab_geom, nqb, n_q_slabs,
+                                              h_slab_ptr, h_slab_cam, h_slab_geom, nkb, n_h_slabs, grid_n, overlap,
+                                              overlap_row_stride);
+    if (st != BSA_OK) return st;
+    return hip_status(bsa::launch_slab_overlap(cams, n_cams, q_slab_ptr, q_slab_cam, q_slab_geom, nqb, n_q_slabs,
+                                               h_slab_ptr, h_slab_cam, h_slab_geom, nkb, n_h_slabs, grid_n, overlap,
+                                               overlap_row_stride, stream),
+                      "slab_overlap launch");
+}
+
+int bsa_slab_coverage(const double* cams, int n_cams, const int32_t* perm, int T, int H, int W, int block,
+                      const int32_t* frame_cam, const float* depth, const int32_t* h_slab_cam,
+                      const double* h_slab_geom, int n_h_slabs, float* coverage, hipStream_t stream) {
+    bsa::clear_error();
+    const int st = bsa::validate_slab_coverage(cams, n_cams, perm, T, H, W, block, frame_cam, depth, h_slab_cam,
+                                               h_slab_geom, n_h_slabs, coverage);
+    if (st != BSA_OK) return st;
+    return hip_status(bsa::launch_slab_coverage(cams, n_cams, perm, T, H, W, block, frame_cam, depth, h_slab_cam,
+                                                h_slab_geom, n_h_slabs, coverage, stream),
+                      "slab_coverage launch");
+}
+
 int bsa_block_sparse_attn(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int heads,
                           int d, int block, int nqb, int nkb, int64_t q_head_stride, int64_t k_head_stride,
                           int64_t v_head_stride, int64_t o_head_stride, const int32_t* q_block_len,

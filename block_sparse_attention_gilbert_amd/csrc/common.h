@@ -56,6 +56,13 @@ size_t route_layout(const bsa_route_args* a, RouteLayout* lay);
 
 // Largest candidate count the in-LDS top-K sort handles.
 constexpr int kMaxCandidates = 4096;
+int validate_slab_overlap(const double* cams, int n_cams, const int32_t* q_ptr, const int32_t* q_cam,
+                          const double* q_geom, int nqb, int n_q, const int32_t* h_ptr, const int32_t* h_cam,
+                          const double* h_geom, int nkb, int n_h, int grid_n, const float* overlap, int64_t stride);
+int validate_slab_coverage(const double* cams, int n_cams, const int32_t* perm, int T, int H, int W, int block,
+                           const int32_t* frame_cam, const float* depth, const int32_t* h_cam, const double* h_geom,
+                           int n_h, const float* coverage);
+
 // Largest K_unc of the route materialisation.
 constexpr int kMaxUncovered = 256;
 // Largest number of blocks per chunk of the local-window builder.

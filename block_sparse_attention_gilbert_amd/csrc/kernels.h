@@ -22,6 +22,15 @@ hipError_t launch_block_window(const int32_t* perm, const int32_t* inv, int T, i
 hipError_t launch_materialize(const bsa_route_args* a, const bsa_materialize_args* m, const RouteLayout& lay,
                               void* ws, hipStream_t stream);
 
+hipError_t launch_slab_overlap(const double* cams, int n_cams, const int32_t* q_ptr, const int32_t* q_cam,
+                               const double* q_geom, int nqb, int n_q, const int32_t* h_ptr, const int32_t* h_cam,
+                               const double* h_geom, int nkb, int n_h, int grid_n, float* overlap, int64_t stride,
+                               hipStream_t stream);
+
+hipError_t launch_slab_coverage(const double* cams, int n_cams, const int32_t* perm, int T, int H, int W, int block,
+                                const int32_t* frame_cam, const float* depth, const int32_t* h_cam,
+                                const double* h_geom, int n_h, float* coverage, hipStream_t stream);
+
 hipError_t launch_attn(const AttnProblem& p, bool dense, hipStream_t stream);
 
 }  // namespace bsa

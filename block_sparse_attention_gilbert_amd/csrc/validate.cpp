@@ -235,6 +235,35 @@ int validate_block_window(const int32_t* perm, const int32_t* inv, int T, int H,
     return BSA_OK;
 }
 
+int validate_slab_overlap(const double* cams, int n_cams, const int32_t* q_ptr, const int32_t* q_cam,
+                          const double* q_geom, int nqb, int n_q, const int32_t* h_ptr, const int32_t* h_cam,
+                          const double* h_geom, int nkb, int n_h, int grid_n, const float* overlap, int64_t stride) {
+    if (!cams || n_cams < 1) return fail(BSA_EINVAL, "cams must be non-NULL with n_cams >= 1");
+    if (nqb < 1 || nkb < 1) return fail(BSA_EINVAL, "nqb %d and nkb %d must be >= 1", nqb, nkb);
+    if (nqb > 65535) return fail(BSA_EUNSUPPORTED, "nqb %d > 65535", nqb);
+    if (!q_ptr || !h_ptr || !overlap) return fail(BSA_EINVAL, "q_slab_ptr, h_slab_ptr and overlap must be non-NULL");
+    if (n_q < 0 || n_h < 0) return fail(BSA_EINVAL, "slab counts must be >= 0");
+    if ((n_q > 0 && (!q_cam || !q_geom)) || (n_h > 0 && (!h_cam || !h_geom)))
+        return fail(BSA_EINVAL, "slab cameras and geometry must be non-NULL when slabs are given");
+    if (grid_n < 1 || grid_n > 64) return fail(BSA_EINVAL, "grid_n %d outside [1, 64]", grid_n);
+    if (stride < nkb) return fail(BSA_EINVAL, "overlap_row_stride %lld < nkb %d", (long long)stride, nkb);
+    return BSA_OK;
+}
+
+int validate_slab_coverage(const double* cams, int n_cams, const int32_t* perm, int T, int H, int W, int block,
+                           const int32_t* frame_cam, const float* depth, const int32_t* h_cam, const double* h_geom,
+                           int n_h, const float* coverage) {
+    if (!cams || n_cams < 1) return fail(BSA_EINVAL, "cams must be non-NULL with n_cams >= 1");
+    if (T < 1 || H < 1 || W < 1) return fail(BSA_EINVAL, "grid %d x %d x %d: dimensions must be >= 1", T, H, W);
+    if ((int64_t)T * H * W > INT32_MAX) return fail(BSA_EINVAL, "grid exceeds 2^31-1 cells");
+    if (block < 1 || block > 256) return fail(block < 1 ? BSA_EINVAL : BSA_EUNSUPPORTED, "block %d outside [1, 256]", block);
+    if (!perm || !frame_cam || !depth || !coverage)
+        return fail(BSA_EINVAL, "perm, frame_cam, depth and coverage must be non-NULL");
+    if (n_h < 0 || (n_h > 0 && (!h_cam || !h_geom)))
+        return fail(BSA_EINVAL, "historical slabs: count >= 0, cameras and geometry non-NULL when given");
+    return BSA_OK;
+}
+
 }  // namespace bsa
 
 extern "C" {

@@ -328,6 +328,71 @@ int bsa_route_materialize(const bsa_route_args* args, const bsa_materialize_args
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Frustum-slab geometry.
+ * [Velox -- Methodology, Step 1 (a historical block is kept as frustum
+ *  slabs: a token rectangle in its source camera plus a depth interval);
+ *  Step 3 (camera-facing oriented boxes, IoU of the query box with the
+ *  best-matching historical box on a deterministic grid after a
+ *  separating-axis test; coverage = share of a query block's tokens inside
+ *  a valid historical slab both spatially and in depth)]
+ *
+ * cams       device float64[n_cams][16]: fx, fy, cx, cy (token units), R
+ *            row-major (world-from-camera; columns = the camera's right,
+ *            down and forward axes in world space), C (camera centre).  A
+ *            camera point (x, y, z), z > 0, sits at token coordinates
+ *            u = fx x / z + cx (column), v = fy y / z + cy (row); token
+ *            (h, w) covers [w, w+1) x [h, h+1).
+ * slabs      grouped by block: block b's slabs are entries ptr[b] ..
+ *            ptr[b+1]-1 (clamped to [0, n_slabs)) of cam (int32, index
+ *            into cams; entries outside [0, n_cams) are skipped) and geom
+ *            (float64[6]: u0, v0, u1, v1, z_lo, z_hi: the rectangle
+ *            [u0, u1) x [v0, v1) and the camera-z interval [z_lo, z_hi]).
+ *            Only valid slabs are passed.
+ * The box of a slab: the camera's axes; centre on the ray through the
+ * rectangle's centre at z_m = (z_lo + z_hi)/2; half extents (u1-u0) z_m /
+ * (2 fx), (v1-v0) z_m / (2 fy), (z_hi-z_lo)/2.  All arithmetic is float64.
+ */
+
+/*
+ * bsa_slab_overlap -- overlap[i * overlap_row_stride + j] (float32) = the
+ * largest IoU over the pairs (query slab of block i, historical slab of
+ * block j); 0 if either block has no slab.  A pair's IoU is 0 when a
+ * separating axis exists (15 axes: the 6 face normals and the 9 edge cross
+ * products, those of squared length < 1e-12 skipped; touching boxes are not
+ * separated); otherwise, with cnt = the cell centres of the query box's
+ * grid_n^3 grid that lie inside the historical box (closed), inter =
+ * vol_q cnt / grid_n^3 and IoU = inter / (vol_q + vol_h - inter) (0 if the
+ * union has no volume).  The result feeds bsa_route_topk /
+ * bsa_route_materialize as their overlap input.
+ * Errors: BSA_EINVAL (null pointers, counts, grid_n outside [1, 64],
+ * overlap_row_stride < nkb), BSA_EUNSUPPORTED (nqb > 65535).
+ */
+int bsa_slab_overlap(const double* cams, int n_cams, const int32_t* q_slab_ptr,
+                     const int32_t* q_slab_cam, const double* q_slab_geom, int nqb, int n_q_slabs,
+                     const int32_t* h_slab_ptr, const int32_t* h_slab_cam,
+                     const double* h_slab_geom, int nkb, int n_h_slabs, int grid_n, float* overlap,
+                     int64_t overlap_row_stride, hipStream_t stream);
+
+/*
+ * bsa_slab_coverage -- coverage[i] (float32) of each of the ceil(T*H*W /
+ * block) query blocks of a chunk: the share of its tokens whose point lies
+ * inside some historical slab.  The tokens of block i are curve positions
+ * i*block .. (i+1)*block-1 of perm (bsa_gilbert_index); a token at raster
+ * cell (t, h, w) has its point at token coordinates (w + 1/2, h + 1/2) and
+ * depth depth[cell] (float32 raster [T][H][W]; NaN or <= 0: no depth, never
+ * covered) in camera frame_cam[t] (int32[T]).  The point is inside a slab
+ * when, in the slab's camera, z > 0, (u, v) lies in the rectangle and z in
+ * [z_lo, z_hi].  coverage = covered tokens / tokens of the block, the
+ * quotient taken in float64 and rounded to float32.
+ * Errors: BSA_EINVAL (null pointers, dimensions, block < 1),
+ * BSA_EUNSUPPORTED (block > 256).
+ */
+int bsa_slab_coverage(const double* cams, int n_cams, const int32_t* perm, int T, int H, int W,
+                      int block, const int32_t* frame_cam, const float* depth,
+                      const int32_t* h_slab_cam, const double* h_slab_geom, int n_h_slabs,
+                      float* coverage, hipStream_t stream);
+
+/*
  * bsa_block_sparse_attn -- attention of every query block over its listed
  * KV blocks.
  * [Velox -- Methodology, Step 6: an indexed block-sparse kernel, not a dense

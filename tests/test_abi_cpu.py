@@ -197,6 +197,37 @@ def test_block_window_rejects():
     assert f(FAKE, FAKE, 3, 30, 52, 4, 1, FAKE, FAKE, 4000, None) == bsa.BSA_EUNSUPPORTED
 
 
+def test_slab_geometry_rejects():
+    f = lib.bsa_slab_overlap
+    ok = (FAKE, 4, FAKE, FAKE, FAKE, 37, 40, FAKE, FAKE, FAKE, 148, 120, 8, FAKE, 148, None)
+    def bad(i, v):
+        args = list(ok)
+        args[i] = v
+        return f(*args)
+    assert bad(0, None) == bsa.BSA_EINVAL                 # cams
+    assert bad(1, 0) == bsa.BSA_EINVAL                    # n_cams
+    assert bad(5, 0) == bsa.BSA_EINVAL                    # nqb
+    assert bad(5, 70000) == bsa.BSA_EUNSUPPORTED
+    assert bad(2, None) == bsa.BSA_EINVAL                 # q_slab_ptr
+    assert bad(3, None) == bsa.BSA_EINVAL                 # q_slab_cam with slabs
+    assert bad(11, -1) == bsa.BSA_EINVAL                  # n_h_slabs
+    assert bad(12, 0) == bsa.BSA_EINVAL and bad(12, 65) == bsa.BSA_EINVAL
+    assert bad(14, 147) == bsa.BSA_EINVAL                 # stride < nkb
+    assert "overlap_row_stride" in lib.bsa_last_error_detail().decode()
+    g = lib.bsa_slab_coverage
+    okc = (FAKE, 4, FAKE, 3, 30, 52, 128, FAKE, FAKE, FAKE, FAKE, 120, FAKE, None)
+    def badc(i, v):
+        args = list(okc)
+        args[i] = v
+        return g(*args)
+    assert badc(6, 257) == bsa.BSA_EUNSUPPORTED
+    assert badc(6, 0) == bsa.BSA_EINVAL
+    assert badc(3, 0) == bsa.BSA_EINVAL
+    assert badc(7, None) == bsa.BSA_EINVAL                # frame_cam
+    assert badc(9, None) == bsa.BSA_EINVAL                # h_slab_cam with slabs
+    assert badc(12, None) == bsa.BSA_EINVAL               # coverage
+
+
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
 def test_host_descent_matches_oracle(tmp_path):

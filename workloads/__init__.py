@@ -244,21 +244,71 @@ def _rotation(yaw: float, pitch: float) -> np.ndarray:
     return ry @ rx
 
 
-def _slabs(rng, n_blocks, cam_of_frame, grid):
-    """1-3 slabs per block in distinct frames: a token rectangle (rows 2-7,
-    columns 4-13 tokens, inside the grid) and a depth interval (middle
-    3 + 10 u, thickness 10-40 % of it)."""
+# A synthetic scene for the slab geometry: a corridor 12 units wide along
+# +z (walls x = -6 and x = +6, from the floor y = +1.5 up to y = -3; the
+# camera's y axis points down), a floor, and an end wall at z = 40; rays
+# that leave over the walls see sky (no depth).
+_ROOM_X, _FLOOR_Y, _TOP_Y, _END_Z = 6.0, 1.5, -3.0, 40.0
+
+
+def _camera(g: int, grid) -> np.ndarray:
+    T, H, W = grid
+    cam = np.zeros(16)
+    R = _rotation(0.3 * math.sin(0.07 * g), 0.05 * math.sin(0.11 * g))
+    cam[:4] = (36.0, 36.0, W / 2.0, H / 2.0)
+    cam[4:13] = R.reshape(-1)
+    cam[13:16] = (1.5 * math.sin(0.02 * g), 0.0, 0.12 * g)
+    return cam
+
+
+def _raycast(cam: np.ndarray, u: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Camera depth of the scene along the rays through token coordinates
+    (u, v); NaN where the ray sees sky."""
+    fx, fy, cx, cy = cam[:4]
+    R, C = cam[4:13].reshape(3, 3), cam[13:16]
+    dc = np.stack([(u - cx) / fx, (v - cy) / fy, np.ones_like(u)], axis=-1)
+    dw = dc @ R.T
+    best = np.full(u.shape, np.inf)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        for axis, plane in ((0, -_ROOM_X), (0, _ROOM_X), (1, _FLOOR_Y), (2, _END_Z)):
+            t = (plane - C[axis]) / dw[..., axis]
+            hit = C + t[..., None] * dw
+            ok = (t > 0) & np.isfinite(t)
+            ok &= (hit[..., 0] >= -_ROOM_X - 1e-9) & (hit[..., 0] <= _ROOM_X + 1e-9)
+            ok &= (hit[..., 1] >= _TOP_Y) & (hit[..., 1] <= _FLOOR_Y + 1e-9) & (hit[..., 2] <= _END_Z + 1e-9)
+            best = np.where(ok & (t < best), t, best)
+    return np.where(np.isfinite(best), best, np.nan)   # dc has unit camera z, so t is the camera depth
+
+
+def _slabs(rng, n_blocks, cam_of_frame, cams, grid):
+    """Slabs of ``n_blocks`` blocks, standing in for the reconstruction of
+    the pages' Step 1: per block 1-3 distinct frames, each a token rectangle
+    (2-7 rows, 4-13 columns, at most the grid) whose depth interval is the
+    10th-90th percentile of the scene depth at its token centres, widened
+    to a thickness of at least 0.1; a rectangle with fewer than 4 depth
+    samples or a spread above 60 % of its median depth gives no slab."""
     T, H, W = grid
     ptr, cam, geom = [0], [], []
     for b in range(n_blocks):
         k = int(rng.integers(1, 4))
         for f in sorted(rng.choice(T, size=min(k, T), replace=False)):
-            hh, ww = int(rng.integers(2, 8)), int(rng.integers(4, 14))
+            hh = int(rng.integers(min(2, H), min(8, H + 1)))
+            ww = int(rng.integers(min(4, W), min(14, W + 1)))
             v0, u0 = int(rng.integers(0, H - hh + 1)), int(rng.integers(0, W - ww + 1))
-            zm = 3.0 + 10.0 * rng.random()
-            th = zm * rng.uniform(0.1, 0.4)
-            cam.append(cam_of_frame(b, int(f)))
-            geom.append((u0, v0, u0 + ww, v0 + hh, zm - th / 2.0, zm + th / 2.0))
+            ci = cam_of_frame(b, int(f))
+            vv, uu = np.meshgrid(np.arange(v0, v0 + hh) + 0.5, np.arange(u0, u0 + ww) + 0.5, indexing="ij")
+            z = _raycast(cams[ci], uu.reshape(-1), vv.reshape(-1))
+            z = z[np.isfinite(z)]
+            if z.size < 4:
+                continue
+            lo, hi, med = np.percentile(z, 10), np.percentile(z, 90), np.median(z)
+            if hi - lo > 0.6 * med:
+                continue
+            if hi - lo < 0.1:
+                mid = (lo + hi) / 2.0
+                lo, hi = mid - 0.05, mid + 0.05
+            cam.append(ci)
+            geom.append((u0, v0, u0 + ww, v0 + hh, lo, hi))
         ptr.append(len(cam))
     return (np.asarray(ptr, dtype=np.int32), np.asarray(cam, dtype=np.int32),
             np.asarray(geom, dtype=np.float64).reshape(-1, 6))
@@ -271,30 +321,25 @@ def geometry_inputs(q_chunk: int, nbc: int, grid=CHUNK_GRID):
     blocks have none), slabs of the query blocks, and a depth per query
     token.
 
-    Cameras (float64 [frames][16]: fx, fy, cx, cy, world-from-camera R
-    row-major, centre C) follow a path that moves 0.12 units forward and
-    0.04 sideways per latent frame while the view swings (yaw 0.3 sin(0.07
-    g), pitch 0.05 sin(0.11 g) for frame g); fx = fy = 36, principal point at
-    the grid centre, in token units.  Slabs: ``_slabs``.  Query depth: a
-    smooth field 4 + 3 (1 + sin(0.2 w + 0.5 t)) (h + 1) / H plus N(0, 0.1),
-    NaN (no depth) on the top three token rows, float32 raster [T][H][W]."""
+    A camera moves through a synthetic corridor (``_raycast``): at latent
+    frame g it sits at (1.5 sin(0.02 g), 0, 0.12 g) with yaw 0.3 sin(0.07 g)
+    and pitch 0.05 sin(0.11 g); fx = fy = 36,
+    principal point at the grid centre, token units; cameras are float64
+    [frames][16] (fx, fy, cx, cy, world-from-camera R row-major, centre).
+    Slabs: ``_slabs``.  Query depth: the scene depth at each token centre of
+    the query chunk times (1 + N(0, 0.01)), NaN over sky, float32 raster
+    [T][H][W]."""
     T, H, W = grid
     n_frames = T * (q_chunk + 1)
-    cams = np.zeros((n_frames, 16))
-    for g in range(n_frames):
-        R = _rotation(0.3 * math.sin(0.07 * g), 0.05 * math.sin(0.11 * g))
-        cams[g, :4] = (36.0, 36.0, W / 2.0, H / 2.0)
-        cams[g, 4:13] = R.reshape(-1)
-        cams[g, 13:16] = (0.04 * g, 0.0, 0.12 * g)
+    cams = np.stack([_camera(g, grid) for g in range(n_frames)])
     rng = _rng(1006, T_SLAB, q_chunk, 0)
-    h_ptr, h_cam, h_geom = _slabs(rng, q_chunk * nbc, lambda b, f: T * (b // nbc) + f, grid)
+    h_ptr, h_cam, h_geom = _slabs(rng, q_chunk * nbc, lambda b, f: T * (b // nbc) + f, cams, grid)
     # the query chunk's own blocks carry no historical slab
     h_ptr = np.concatenate([h_ptr, np.full(nbc, h_ptr[-1], dtype=np.int32)])
-    q_ptr, q_cam, q_geom = _slabs(_rng(1006, T_SLAB, q_chunk, 1), nbc, lambda b, f: T * q_chunk + f, grid)
-    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
-    depth = 4.0 + 3.0 * (1.0 + np.sin(0.2 * w + 0.5 * t)) * (h + 1) / H
-    depth = depth + _rng(1006, T_DEPTH, q_chunk, 0).normal(0.0, 0.1, size=depth.shape)
-    depth[:, :3, :] = np.nan
+    q_ptr, q_cam, q_geom = _slabs(_rng(1006, T_SLAB, q_chunk, 1), nbc, lambda b, f: T * q_chunk + f, cams, grid)
+    vv, uu = np.meshgrid(np.arange(H) + 0.5, np.arange(W) + 0.5, indexing="ij")
+    noise = _rng(1006, T_DEPTH, q_chunk, 0).normal(0.0, 0.01, size=(T, H, W))
+    depth = np.stack([_raycast(cams[T * q_chunk + t], uu, vv) for t in range(T)]) * (1.0 + noise)
     return dict(cams=cams, h_ptr=h_ptr, h_cam=h_cam, h_geom=h_geom, q_ptr=q_ptr, q_cam=q_cam, q_geom=q_geom,
                 frame_cam=np.arange(T * q_chunk, T * (q_chunk + 1), dtype=np.int32),
                 depth=depth.astype(np.float32), grid=tuple(grid))
