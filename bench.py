@@ -22,8 +22,9 @@ replayed from a HIP graph (``step_hip_graph_ms``: identical kernels, no
 launch gaps; every replay is checked bitwise against the eager step), and
 the step with the materialised route instead of the top-K
 (``materialized``: coverage-gated budgets, previous-chunk reservation,
-cumulative-mass prefix and the local window, on seeded coverage and
-overlap).
+cumulative-mass prefix and the local window), its overlap and coverage
+produced from frustum slabs on the GPU (``geometry``: camera-facing boxes,
+separating-axis test, grid IoU; once per chunk, shared by all layers).
 
 Printed: one JSON line.  ``value`` = effective TFLOP/s of the step (valid
 selected (query, key) pairs x 4 d FLOP, divided by the step time).  The
@@ -151,23 +152,67 @@ def step_graph_ms(st, reps: int):
     return e0.elapsed_time(e1) / reps
 
 
-def materialized(st, reps: int):
-    """The step with the materialised route instead of the fixed top-K, at
-    the same chunk: coverage-gated budgets (eta_cov 0.9, K_cov 80, K_unc
-    150, mass 0.9), the previous chunk reserved, the chunk's local window
-    rebuilt on the GPU, no reference blocks; seeded coverage and overlap
-    (``workloads.route_inputs``).  Times the whole step, the routing part
-    (window + materialisation) and the attention launch."""
+def geometry(st, reps: int):
+    """Overlap and coverage of the current chunk's query blocks from frustum
+    slabs (``workloads.geometry_inputs``: a camera path through a ray-cast
+    corridor, slabs of every historical block, query depth), timed on the
+    GPU; computed once per chunk and shared by every layer of the model."""
     import numpy as np
     import torch
 
+    import block_sparse_attention_gilbert_amd as bsa
     import workloads
 
     w, ra = st["w"], st["ra"]
     dev = ra.device
-    cov, ov = workloads.route_inputs(w.q_len, w.nkb)
-    mat = dict(coverage=torch.from_numpy(cov).to(dev), k_cov=80, k_unc=150, mass=0.9)
-    overlap = torch.from_numpy(ov).to(dev)
+    g = workloads.geometry_inputs(st["cur"], w.nqb)
+    d = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) if isinstance(v, np.ndarray) else v
+         for k, v in g.items()}
+    ov = torch.empty((w.nqb, w.nkb), dtype=torch.float32, device=dev)
+    cov = torch.empty(w.nqb, dtype=torch.float32, device=dev)
+
+    def overlap():
+        bsa.slab_overlap(d["cams"], d["q_ptr"], d["q_cam"], d["q_geom"], d["h_ptr"], d["h_cam"], d["h_geom"], out=ov)
+
+    def coverage():
+        bsa.slab_coverage(d["cams"], ra.perm, g["grid"], d["frame_cam"], d["depth"], d["h_cam"], d["h_geom"],
+                          block=w.bs, out=cov)
+
+    times = {}
+    for name, fn in (("overlap", overlap), ("coverage", coverage)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) / reps
+    nq = np.diff(g["q_ptr"])
+    nh = np.diff(g["h_ptr"])
+    ovh = ov.cpu().numpy()
+    covh = cov.cpu().numpy()
+    summary = {"overlap_ms": round(times["overlap"], 4), "coverage_ms": round(times["coverage"], 4),
+               "query_slabs": int(nq.sum()), "historical_slabs": int(nh.sum()),
+               "slab_pairs": int(nq.sum()) * int(nh.sum()), "positive_block_pairs": int((ovh > 0).sum()),
+               "median_positive_overlap": round(float(np.median(ovh[ovh > 0])), 4) if (ovh > 0).any() else 0.0,
+               "covered_query_blocks": int((covh >= 0.9).sum()), "grid_n": 8}
+    return summary, ov, cov
+
+
+def materialized(st, reps: int, overlap, coverage):
+    """The step with the materialised route instead of the fixed top-K, at
+    the same chunk: coverage-gated budgets (eta_cov 0.9, K_cov 80, K_unc
+    150, mass 0.9), the previous chunk reserved, the chunk's local window
+    rebuilt on the GPU, no reference blocks, with the overlap and coverage
+    the slab geometry produced.  Times the whole step, the routing part
+    (window + materialisation) and the attention launch."""
+    import numpy as np
+    import torch
+
+    w, ra = st["w"], st["ra"]
+    mat = dict(coverage=coverage, k_cov=80, k_unc=150, mass=0.9)
 
     def one(events=None):
         return ra.step(st["q_raster"], st["k_raster"], st["v_raster"], st["cur"], overlap=overlap,
@@ -193,16 +238,16 @@ def materialized(st, reps: int):
     torch.cuda.synchronize()
     route_ms = e0.elapsed_time(e1) / reps
     wc = work_counts(r["row_ptr"], r["col_idx"], w.q_len, w.k_len, w.heads, w.nqb, w.bs, w.d)
-    rp = r["row_ptr"].cpu().numpy()
-    lens = np.diff(rp)
+    lens = np.diff(r["row_ptr"].cpu().numpy())
     return {"ms_per_step": round(ms_step, 4), "route_ms": round(route_ms, 4), "attn_ms": round(attn_ms, 4),
             "step_effective_tflops": round(wc["flop"] / (ms_step * 1e-3) / 1e12, 2),
             "attn_effective_tflops": round(wc["flop"] / (attn_ms * 1e-3) / 1e12, 2),
             "attn_achieved_gbs": round(wc["alg_bytes"] / (attn_ms * 1e-3) / 1e9, 1),
             "list_len_mean": round(float(lens.mean()), 2), "list_len_min": int(lens.min()),
-            "list_len_max": int(lens.max()), "covered_query_blocks": int((cov >= 0.9).sum()),
-            "query_blocks": int(w.nqb), "params": "eta_cov 0.9, K_cov 80, K_unc 150, mass 0.9, window on, "
-                                                   "no reference blocks"}
+            "list_len_max": int(lens.max()),
+            "covered_query_blocks": int((coverage.cpu().numpy() >= 0.9).sum()), "query_blocks": int(w.nqb),
+            "params": "eta_cov 0.9, K_cov 80, K_unc 150, mass 0.9, window on, no reference blocks; overlap and "
+                      "coverage from the slab geometry"}
 
 
 def cpu_baseline(st, n_heads=2):
@@ -331,7 +376,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=40)
     ap.add_argument("--dense", action="store_true", help="also time dense attention at the same chunk")
     ap.add_argument("--no-materialized", action="store_true",
-                    help="skip timing the step with the materialised route")
+                    help="skip timing the slab geometry and the step with the materialised route")
     ap.add_argument("--sweep", default=None, help="write a chunk 1..C sparse/dense sweep to this JSONL file")
     ap.add_argument("--rollout", default=None,
                     help="write a 1..C chunk rollout (append, route with the pooled-key cache, attend) to this JSONL file")
@@ -455,7 +500,9 @@ def main():
         out["dense"] = {"ms_per_call": round(dms, 3), "effective_tflops": round(dflop / (dms * 1e-3) / 1e12, 2),
                         "speedup_sparse_vs_dense": round(dms / attn_ms, 2)}
     if not args.no_materialized:
-        out["materialized"] = materialized(st, max(1, min(args.steps, 10)))
+        geo, ov, cov = geometry(st, max(1, min(args.steps, 10)))
+        out["geometry"] = geo
+        out["materialized"] = materialized(st, max(1, min(args.steps, 10)), ov, cov)
     if args.sweep:
         sweep(st, args.sweep)
     if args.rollout:

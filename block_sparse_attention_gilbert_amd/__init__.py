@@ -92,7 +92,9 @@ _lib.bsa_route_materialize.argtypes = [ctypes.POINTER(RouteArgs), ctypes.POINTER
 _lib.bsa_slab_overlap.restype = _i
 _lib.bsa_slab_overlap.argtypes = [_p, _i, _p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _i64, _p]
 _lib.bsa_slab_coverage.restype = _i
-_lib.bsa_slab_coverage.argtypes = [_p, _i, _p, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p]
+_lib.bsa_slab_coverage.argtypes = [_p, _i, _p, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p, ctypes.c_size_t, _p]
+_lib.bsa_slab_coverage_workspace_size.restype = ctypes.c_size_t
+_lib.bsa_slab_coverage_workspace_size.argtypes = [_i, _i, _i]
 _lib.bsa_route_workspace_size.restype = ctypes.c_size_t
 _lib.bsa_route_workspace_size.argtypes = [ctypes.POINTER(RouteArgs)]
 _lib.bsa_route_topk.restype = _i
@@ -106,7 +108,7 @@ _lib.bsa_dense_attn.argtypes = _ATTN_COMMON + [_f, _p]
 EXPORTED = ("bsa_version", "bsa_strerror", "bsa_last_error_detail", "bsa_gilbert_index",
             "bsa_gilbert_perm", "bsa_gilbert_block_window", "bsa_route_workspace_size", "bsa_route_topk",
             "bsa_route_materialize_workspace_size", "bsa_route_materialize", "bsa_slab_overlap",
-            "bsa_slab_coverage", "bsa_block_sparse_attn", "bsa_dense_attn")
+            "bsa_slab_coverage", "bsa_slab_coverage_workspace_size", "bsa_block_sparse_attn", "bsa_dense_attn")
 
 
 class BsaError(RuntimeError):
@@ -267,9 +269,11 @@ def slab_overlap(cams, q_slab_ptr, q_slab_cam, q_slab_geom, h_slab_ptr, h_slab_c
 
 
 def slab_coverage(cams, perm, grid, frame_cam, depth, h_slab_cam, h_slab_geom, *, block: int,
-                  out: Optional[torch.Tensor] = None, stream=None):
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
     """Coverage ``[ceil(T*H*W / block)]`` float32 of the query blocks of a
-    chunk by the historical slabs."""
+    chunk by the historical slabs.  ``workspace`` (uint8, at least
+    ``bsa_slab_coverage_workspace_size`` bytes) may be passed in to avoid an
+    allocation."""
     _need_gpu(cams, perm, frame_cam, depth, h_slab_cam, h_slab_geom, out)
     cams = _f64(cams, "cams", 16)
     h_slab_geom = _f64(h_slab_geom, "h_slab_geom", 6)
@@ -279,10 +283,14 @@ def slab_coverage(cams, perm, grid, frame_cam, depth, h_slab_cam, h_slab_geom, *
     nqb = -(-(T * H * W) // block)
     if out is None:
         out = torch.empty(nqb, dtype=torch.float32, device=cams.device)
+    need = _lib.bsa_slab_coverage_workspace_size(T, H, W)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=cams.device)
     _check(_lib.bsa_slab_coverage(_ptr(cams), cams.shape[0], _ptr(_i32(perm, "perm")), T, H, W, block,
                                   _ptr(_i32(frame_cam, "frame_cam")), _ptr(depth),
                                   _ptr(_i32(h_slab_cam, "h_slab_cam")), _ptr(h_slab_geom),
-                                  h_slab_cam.numel(), _ptr(out), _stream(stream)))
+                                  h_slab_cam.numel(), _ptr(out), _ptr(workspace), workspace.numel(),
+                                  _stream(stream)))
     return out
 
 

@@ -88,13 +88,19 @@ int bsa_slab_overlap(const double* cams, int n_cams, const int32_t* q_slab_ptr, 
 
 int bsa_slab_coverage(const double* cams, int n_cams, const int32_t* perm, int T, int H, int W, int block,
                       const int32_t* frame_cam, const float* depth, const int32_t* h_slab_cam,
-                      const double* h_slab_geom, int n_h_slabs, float* coverage, hipStream_t stream) {
+                      const double* h_slab_geom, int n_h_slabs, float* coverage, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
     bsa::clear_error();
     const int st = bsa::validate_slab_coverage(cams, n_cams, perm, T, H, W, block, frame_cam, depth, h_slab_cam,
                                                h_slab_geom, n_h_slabs, coverage);
     if (st != BSA_OK) return st;
+    const size_t need = bsa_slab_coverage_workspace_size(T, H, W);
+    if (!workspace) return bsa::fail(BSA_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+        return bsa::fail(BSA_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 3u) return bsa::fail(BSA_EWORKSPACE, "workspace must be 4-byte aligned");
     return hip_status(bsa::launch_slab_coverage(cams, n_cams, perm, T, H, W, block, frame_cam, depth, h_slab_cam,
-                                                h_slab_geom, n_h_slabs, coverage, stream),
+                                                h_slab_geom, n_h_slabs, coverage, workspace, stream),
                       "slab_coverage launch");
 }
 

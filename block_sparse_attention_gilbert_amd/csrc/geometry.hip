@@ -88,134 +88,182 @@ __device__ bool separated(const Box& A, const Box& B) {
     return false;
 }
 
-// IoU of query box A and historical box B on the n^3 cell centres of A.
-__device__ double grid_iou(const Box& A, const Box& B, int n) {
-    if (separated(A, B)) return 0.0;
-    int cnt = 0;
-    for (int i = 0; i < n; ++i) {
-        const double si = (2.0 * i + 1.0) / n - 1.0;
-        double pi[3];
-#pragma unroll
-        for (int r = 0; r < 3; ++r) pi[r] = (si * A.e[0]) * A.a[0][r];
-        for (int j = 0; j < n; ++j) {
-            const double sj = (2.0 * j + 1.0) / n - 1.0;
-            double pj[3];
-#pragma unroll
-            for (int r = 0; r < 3; ++r) pj[r] = pi[r] + (sj * A.e[1]) * A.a[1][r];
-            for (int l = 0; l < n; ++l) {
-                const double sl = (2.0 * l + 1.0) / n - 1.0;
-                double q[3];
-#pragma unroll
-                for (int r = 0; r < 3; ++r) q[r] = A.c[r] + (pj[r] + (sl * A.e[2]) * A.a[2][r]) - B.c[r];
-                bool in = true;
-#pragma unroll
-                for (int m = 0; m < 3; ++m) in = in && fabs(dot3(q, B.a[m])) <= B.e[m];
-                cnt += in ? 1 : 0;
-            }
-        }
-    }
-    const double va = 8.0 * A.e[0] * A.e[1] * A.e[2];
-    const double vb = 8.0 * B.e[0] * B.e[1] * B.e[2];
-    const double inter = va * cnt / (double)(n * n * n);
-    const double uni = va + vb - inter;
-    return uni > 0.0 ? inter / uni : 0.0;
-}
-
 __device__ __forceinline__ int clamp_range(int x, int n) { return x < 0 ? 0 : (x > n ? n : x); }
 
-// One thread per (query block i, historical block j): the largest IoU over
-// the pairs of their slabs.  grid = (ceil(nkb / 256), nqb).
+constexpr int kMaxGrid = 64;
+
+// One lane per (query block i, historical block j), 64 consecutive j per
+// wave; grid = (ceil(nkb / 256), nqb).  For each query slab (the same for
+// the whole workgroup) and each position b in the historical block's slab
+// list, every lane builds its historical box and runs the separating-axis
+// test; the pairs that pass are then counted one at a time by the whole
+// wave, each lane taking every 64th point of the query box's grid.  A
+// lane's largest IoU is its result.
 __global__ void __launch_bounds__(256)
 slab_overlap_kernel(const double* __restrict__ cams, int n_cams, const int32_t* __restrict__ q_ptr,
                     const int32_t* __restrict__ q_cam, const double* __restrict__ q_geom, int n_q,
                     const int32_t* __restrict__ h_ptr, const int32_t* __restrict__ h_cam,
                     const double* __restrict__ h_geom, int n_h, int nkb, int n, float* __restrict__ overlap,
                     int64_t stride) {
-    const int i = blockIdx.y;
-    const int j = blockIdx.x * 256 + threadIdx.x;
-    if (j >= nkb) return;
+    __shared__ double sgrid[kMaxGrid];
+    __shared__ Box hb_all[4][64];
+    const int i = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int j = blockIdx.x * 256 + t;
+    if (t < n) sgrid[t] = (2.0 * t + 1.0) / n - 1.0;
+    __syncthreads();
+    const bool live = j < nkb;
     const int qa = clamp_range(q_ptr[i], n_q), qb = clamp_range(q_ptr[i + 1], n_q);
-    const int ha = clamp_range(h_ptr[j], n_h), hb = clamp_range(h_ptr[j + 1], n_h);
+    int ha = 0, hn = 0;
+    if (live) {
+        ha = clamp_range(h_ptr[j], n_h);
+        hn = clamp_range(h_ptr[j + 1], n_h) - ha;
+        hn = hn < 0 ? 0 : hn;
+    }
+    int hmax = hn;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) hmax = max(hmax, __shfl_xor(hmax, o));
+    Box* hb = hb_all[w];
+    const int n3 = n * n * n, nn = n * n;
     double best = 0.0;
     for (int a = qa; a < qb; ++a) {
         const int ca = q_cam[a];
         if (ca < 0 || ca >= n_cams) continue;
         Box A;
         slab_box(cams + 16 * ca, q_geom + 6 * a, A);
-        for (int b = ha; b < hb; ++b) {
-            const int cb = h_cam[b];
-            if (cb < 0 || cb >= n_cams) continue;
-            Box B;
-            slab_box(cams + 16 * cb, h_geom + 6 * b, B);
-            best = fmax(best, grid_iou(A, B, n));
+        const double va = 8.0 * A.e[0] * A.e[1] * A.e[2];
+        for (int b = 0; b < hmax; ++b) {
+            bool need = false;
+            if (b < hn) {
+                const int cb = h_cam[ha + b];
+                if (cb >= 0 && cb < n_cams) {
+                    Box B;
+                    slab_box(cams + 16 * cb, h_geom + 6 * (ha + b), B);
+                    need = !separated(A, B);
+                    hb[lane] = B;
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            __asm__ volatile("" ::: "memory");
+            unsigned long long pend = __ballot(need);
+            while (pend) {
+                const int owner = __ffsll((long long)pend) - 1;
+                pend &= pend - 1;
+                const Box& B = hb[owner];
+                int cnt = 0;
+                for (int idx = lane; idx < n3; idx += 64) {
+                    const double si = sgrid[idx / nn], sj = sgrid[(idx / n) % n], sl = sgrid[idx % n];
+                    double q[3];
+#pragma unroll
+                    for (int r = 0; r < 3; ++r)
+                        q[r] = A.c[r] + (((si * A.e[0]) * A.a[0][r] + (sj * A.e[1]) * A.a[1][r]) +
+                                         (sl * A.e[2]) * A.a[2][r]) - B.c[r];
+                    bool in = true;
+#pragma unroll
+                    for (int m = 0; m < 3; ++m) in = in && fabs(dot3(q, B.a[m])) <= B.e[m];
+                    cnt += in ? 1 : 0;
+                }
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+                if (lane == owner) {
+                    const double vb = 8.0 * B.e[0] * B.e[1] * B.e[2];
+                    const double inter = va * cnt / (double)n3;
+                    const double uni = va + vb - inter;
+                    best = fmax(best, uni > 0.0 ? inter / uni : 0.0);
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            __asm__ volatile("" ::: "memory");
         }
     }
-    overlap[(int64_t)i * stride + j] = (float)best;
+    if (live) overlap[(int64_t)i * stride + j] = (float)best;
 }
 
-// One workgroup of 16 waves per query block.  The block's tokens are split
-// in groups of 64 (one per lane); the historical slabs are split among the
-// waves of a token group (wave-uniform slab index, so slab and camera loads
-// are scalar).  A token is covered when its point lies inside any slab.
-__global__ void __launch_bounds__(1024)
-slab_coverage_kernel(const double* __restrict__ cams, int n_cams, const int32_t* __restrict__ perm, int L, int H,
-                     int W, int block, const int32_t* __restrict__ frame_cam, const float* __restrict__ depth,
-                     const int32_t* __restrict__ h_cam, const double* __restrict__ h_geom, int n_h,
-                     float* __restrict__ coverage) {
-    __shared__ int flag[256];
-    const int i = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int groups = (block + 63) / 64, per = 16 / groups;
-    const int g = w / per, s = w % per;
-    const int g0 = i * block, g1 = min(L, g0 + block), ntok = g1 - g0;
-    if (t < 256) flag[t] = 0;
+// Coverage, first pass: one thread per token (curve position), a chunk of
+// kCovChunk historical slabs per workgroup row (grid = (ceil(L / 256),
+// ceil(n_h / kCovChunk))).  The chunk's slabs and their cameras are staged
+// in LDS and read as broadcasts; a covered token sets its bit in `flags`
+// (integer OR, so the order of the chunks does not matter).
+constexpr int kCovChunk = 128;
+
+struct SlabCam {
+    double geo[6];
+    double cam[16];
+};
+
+__global__ void __launch_bounds__(256)
+slab_cover_flags_kernel(const double* __restrict__ cams, int n_cams, const int32_t* __restrict__ perm, int L, int H,
+                        int W, const int32_t* __restrict__ frame_cam, const float* __restrict__ depth,
+                        const int32_t* __restrict__ h_cam, const double* __restrict__ h_geom, int n_h,
+                        uint32_t* __restrict__ flags) {
+    __shared__ SlabCam sc[kCovChunk];
+    __shared__ int ok[kCovChunk];
+    const int t = threadIdx.x;
+    const int k0 = blockIdx.y * kCovChunk, nk = min(kCovChunk, n_h - k0);
+    for (int x = t; x < nk * 22; x += 256) {
+        const int k = x / 22, f = x % 22;
+        const int cs = h_cam[k0 + k];
+        const bool good = cs >= 0 && cs < n_cams;
+        double v = 0.0;
+        if (f < 6)
+            v = h_geom[6 * (k0 + k) + f];
+        else if (good)
+            v = cams[16 * cs + (f - 6)];
+        if (f < 6)
+            sc[k].geo[f] = v;
+        else
+            sc[k].cam[f - 6] = v;
+        if (f == 0) ok[k] = good ? 1 : 0;
+    }
     __syncthreads();
-    const int tok = g * 64 + lane;
-    const bool mine = g < groups && tok < ntok;
-    double X[3] = {0.0, 0.0, 0.0};
-    bool has_point = false;
-    if (mine) {
-        const int cell = perm[g0 + tok];
-        const bool in_grid = cell >= 0 && cell < L;
-        const int c = in_grid ? cell : 0;
-        const int tt = c / (H * W), rem = c % (H * W), hh = rem / W, ww = rem % W;
-        const int cf = frame_cam[tt];
-        const double z = (double)depth[c];
-        if (in_grid && cf >= 0 && cf < n_cams && z > 0.0) {
-            const double* cam = cams + 16 * cf;
-            const double pc[3] = {((ww + 0.5) - cam[2]) * z / cam[0], ((hh + 0.5) - cam[3]) * z / cam[1], z};
+    const int gp = blockIdx.x * 256 + t;
+    if (gp >= L) return;
+    const int cell = perm[gp];
+    if (cell < 0 || cell >= L) return;
+    const int tt = cell / (H * W), rem = cell % (H * W), hh = rem / W, ww = rem % W;
+    const int cf = frame_cam[tt];
+    const double z0 = (double)depth[cell];
+    if (cf < 0 || cf >= n_cams || !(z0 > 0.0)) return;
+    const double* cam = cams + 16 * cf;
+    const double pc[3] = {((ww + 0.5) - cam[2]) * z0 / cam[0], ((hh + 0.5) - cam[3]) * z0 / cam[1], z0};
+    double X[3];
 #pragma unroll
-            for (int r = 0; r < 3; ++r) X[r] = dot3(cam + 4 + 3 * r, pc) + cam[13 + r];
-            has_point = true;
+    for (int r = 0; r < 3; ++r) X[r] = dot3(cam + 4 + 3 * r, pc) + cam[13 + r];
+    for (int k = 0; k < nk; ++k) {
+        if (!ok[k]) continue;
+        const double* c = sc[k].cam;
+        const double* geo = sc[k].geo;
+        const double d[3] = {X[0] - c[13], X[1] - c[14], X[2] - c[15]};
+        // camera coordinates: R^T d (R's columns are the camera axes)
+        const double x = c[4] * d[0] + c[7] * d[1] + c[10] * d[2];
+        const double y = c[5] * d[0] + c[8] * d[1] + c[11] * d[2];
+        const double z = c[6] * d[0] + c[9] * d[1] + c[12] * d[2];
+        if (!(z > 0.0) || z < geo[4] || z > geo[5]) continue;
+        const double u = c[0] * x / z + c[2], v = c[1] * y / z + c[3];
+        if (geo[0] <= u && u < geo[2] && geo[1] <= v && v < geo[3]) {
+            atomicOr(&flags[gp >> 5], 1u << (gp & 31));
+            break;
         }
     }
-    bool covered = false;
-    if (g < groups) {
-        for (int k = s; k < n_h; k += per) {
-            if (__all(!has_point || covered)) break;
-            const int cs = h_cam[k];
-            if (cs < 0 || cs >= n_cams) continue;
-            const double* cam = cams + 16 * cs;
-            const double* geo = h_geom + 6 * k;
-            const double d[3] = {X[0] - cam[13], X[1] - cam[14], X[2] - cam[15]};
-            // camera coordinates: R^T d (R's columns are the camera axes)
-            const double x = cam[4] * d[0] + cam[7] * d[1] + cam[10] * d[2];
-            const double y = cam[5] * d[0] + cam[8] * d[1] + cam[11] * d[2];
-            const double z = cam[6] * d[0] + cam[9] * d[1] + cam[12] * d[2];
-            if (has_point && !covered && z > 0.0) {
-                const double u = cam[0] * x / z + cam[2], v = cam[1] * y / z + cam[3];
-                covered = geo[0] <= u && u < geo[2] && geo[1] <= v && v < geo[3] && geo[4] <= z && z <= geo[5];
-            }
-        }
-    }
-    if (mine && covered) atomicOr(&flag[tok], 1);
-    __syncthreads();
-    if (w == 0) {
-        int cnt = 0;
-        for (int x = lane; x < ntok; x += 64) cnt += flag[x];
+}
+
+__global__ void __launch_bounds__(256) fill_u32_kernel(uint32_t* __restrict__ p, int n) {
+    const int x = blockIdx.x * 256 + threadIdx.x;
+    if (x < n) p[x] = 0u;
+}
+
+// Coverage, second pass: one wave per query block counts the set bits of
+// its curve positions.
+__global__ void __launch_bounds__(256)
+slab_cover_count_kernel(const uint32_t* __restrict__ flags, int L, int block, int nqb, float* __restrict__ coverage) {
+    const int lane = threadIdx.x & 63;
+    const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= nqb) return;
+    const int g0 = i * block, g1 = min(L, g0 + block);
+    int cnt = 0;
+    for (int gp = g0 + lane; gp < g1; gp += 64) cnt += (flags[gp >> 5] >> (gp & 31)) & 1u;
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
-        if (lane == 0) coverage[i] = ntok > 0 ? (float)((double)cnt / (double)ntok) : 0.0f;
-    }
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+    if (lane == 0) coverage[i] = g1 > g0 ? (float)((double)cnt / (double)(g1 - g0)) : 0.0f;
 }
 
 }  // namespace
@@ -232,11 +280,19 @@ hipError_t launch_slab_overlap(const double* cams, int n_cams, const int32_t* q_
 
 hipError_t launch_slab_coverage(const double* cams, int n_cams, const int32_t* perm, int T, int H, int W, int block,
                                 const int32_t* frame_cam, const float* depth, const int32_t* h_cam,
-                                const double* h_geom, int n_h, float* coverage, hipStream_t stream) {
+                                const double* h_geom, int n_h, float* coverage, void* ws, hipStream_t stream) {
     const int L = T * H * W;
     const int nqb = (L + block - 1) / block;
-    hipLaunchKernelGGL(slab_coverage_kernel, dim3(nqb), dim3(1024), 0, stream, cams, n_cams, perm, L, H, W, block,
-                       frame_cam, depth, h_cam, h_geom, n_h, coverage);
+    const int words = (L + 31) / 32;
+    uint32_t* flags = static_cast<uint32_t*>(ws);
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((words + 255) / 256), dim3(256), 0, stream, flags, words);
+    if (n_h > 0) {
+        const dim3 grid((L + 255) / 256, (n_h + kCovChunk - 1) / kCovChunk);
+        hipLaunchKernelGGL(slab_cover_flags_kernel, grid, dim3(256), 0, stream, cams, n_cams, perm, L, H, W, frame_cam,
+                           depth, h_cam, h_geom, n_h, flags);
+    }
+    hipLaunchKernelGGL(slab_cover_count_kernel, dim3((nqb + 3) / 4), dim3(256), 0, stream, flags, L, block, nqb,
+                       coverage);
     return hipGetLastError();
 }
 

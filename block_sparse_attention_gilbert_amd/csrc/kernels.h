@@ -29,7 +29,7 @@ hipError_t launch_slab_overlap(const double* cams, int n_cams, const int32_t* q_
 
 hipError_t launch_slab_coverage(const double* cams, int n_cams, const int32_t* perm, int T, int H, int W, int block,
                                 const int32_t* frame_cam, const float* depth, const int32_t* h_cam,
-                                const double* h_geom, int n_h, float* coverage, hipStream_t stream);
+                                const double* h_geom, int n_h, float* coverage, void* ws, hipStream_t stream);
 
 hipError_t launch_attn(const AttnProblem& p, bool dense, hipStream_t stream);
 

@@ -256,11 +256,12 @@ int validate_slab_coverage(const double* cams, int n_cams, const int32_t* perm, 
     if (!cams || n_cams < 1) return fail(BSA_EINVAL, "cams must be non-NULL with n_cams >= 1");
     if (T < 1 || H < 1 || W < 1) return fail(BSA_EINVAL, "grid %d x %d x %d: dimensions must be >= 1", T, H, W);
     if ((int64_t)T * H * W > INT32_MAX) return fail(BSA_EINVAL, "grid exceeds 2^31-1 cells");
-    if (block < 1 || block > 256) return fail(block < 1 ? BSA_EINVAL : BSA_EUNSUPPORTED, "block %d outside [1, 256]", block);
+    if (block < 1) return fail(BSA_EINVAL, "block %d < 1", block);
     if (!perm || !frame_cam || !depth || !coverage)
         return fail(BSA_EINVAL, "perm, frame_cam, depth and coverage must be non-NULL");
     if (n_h < 0 || (n_h > 0 && (!h_cam || !h_geom)))
         return fail(BSA_EINVAL, "historical slabs: count >= 0, cameras and geometry non-NULL when given");
+    if (n_h > 65535 * 128) return fail(BSA_EUNSUPPORTED, "%d historical slabs exceed %d", n_h, 65535 * 128);
     return BSA_OK;
 }
 
@@ -293,6 +294,11 @@ size_t bsa_route_materialize_workspace_size(const bsa_route_args* args, const bs
     bsa::RouteLayout lay;
     if (bsa::validate_materialize(args, margs, &lay) != BSA_OK) return 0;
     return lay.total;
+}
+
+size_t bsa_slab_coverage_workspace_size(int T, int H, int W) {
+    if (T < 1 || H < 1 || W < 1 || (int64_t)T * H * W > INT32_MAX) return 0;
+    return sizeof(uint32_t) * (size_t)bsa::ceil_div((int64_t)T * H * W, 32);
 }
 
 }  // extern "C"

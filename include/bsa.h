@@ -377,20 +377,28 @@ int bsa_slab_overlap(const double* cams, int n_cams, const int32_t* q_slab_ptr,
  * bsa_slab_coverage -- coverage[i] (float32) of each of the ceil(T*H*W /
  * block) query blocks of a chunk: the share of its tokens whose point lies
  * inside some historical slab.  The tokens of block i are curve positions
- * i*block .. (i+1)*block-1 of perm (bsa_gilbert_index); a token at raster
- * cell (t, h, w) has its point at token coordinates (w + 1/2, h + 1/2) and
- * depth depth[cell] (float32 raster [T][H][W]; NaN or <= 0: no depth, never
- * covered) in camera frame_cam[t] (int32[T]).  The point is inside a slab
- * when, in the slab's camera, z > 0, (u, v) lies in the rectangle and z in
- * [z_lo, z_hi].  coverage = covered tokens / tokens of the block, the
- * quotient taken in float64 and rounded to float32.
+ * i*block .. (i+1)*block-1 of perm (bsa_gilbert_index; entries outside
+ * [0, T*H*W) are never covered); a token at raster cell (t, h, w) has its
+ * point at token coordinates (w + 1/2, h + 1/2) and depth depth[cell]
+ * (float32 raster [T][H][W]; NaN or <= 0: no depth, never covered) in
+ * camera frame_cam[t] (int32[T]).  The point is inside a slab when, in the
+ * slab's camera, z > 0, (u, v) lies in the rectangle and z in [z_lo, z_hi].
+ * coverage = covered tokens / tokens of the block, the quotient taken in
+ * float64 and rounded to float32.
+ * workspace: device memory of bsa_slab_coverage_workspace_size(T, H, W)
+ * bytes (one bit per token), 4-byte aligned, owned by the caller, cleared
+ * by the call itself.
  * Errors: BSA_EINVAL (null pointers, dimensions, block < 1),
- * BSA_EUNSUPPORTED (block > 256).
+ * BSA_EUNSUPPORTED (more than 65535*128 slabs), BSA_EWORKSPACE.
  */
 int bsa_slab_coverage(const double* cams, int n_cams, const int32_t* perm, int T, int H, int W,
                       int block, const int32_t* frame_cam, const float* depth,
                       const int32_t* h_slab_cam, const double* h_slab_geom, int n_h_slabs,
-                      float* coverage, hipStream_t stream);
+                      float* coverage, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace bsa_slab_coverage needs for a T x H x W chunk (0 if
+ * the dimensions are invalid). */
+size_t bsa_slab_coverage_workspace_size(int T, int H, int W);
 
 /*
  * bsa_block_sparse_attn -- attention of every query block over its listed

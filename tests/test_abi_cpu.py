@@ -215,12 +215,17 @@ def test_slab_geometry_rejects():
     assert bad(14, 147) == bsa.BSA_EINVAL                 # stride < nkb
     assert "overlap_row_stride" in lib.bsa_last_error_detail().decode()
     g = lib.bsa_slab_coverage
-    okc = (FAKE, 4, FAKE, 3, 30, 52, 128, FAKE, FAKE, FAKE, FAKE, 120, FAKE, None)
+    okc = (FAKE, 4, FAKE, 3, 30, 52, 128, FAKE, FAKE, FAKE, FAKE, 120, FAKE, FAKE, 588, None)
     def badc(i, v):
         args = list(okc)
         args[i] = v
         return g(*args)
-    assert badc(6, 257) == bsa.BSA_EUNSUPPORTED
+    assert lib.bsa_slab_coverage_workspace_size(3, 30, 52) == 4 * 147
+    assert lib.bsa_slab_coverage_workspace_size(0, 30, 52) == 0
+    assert badc(13, None) == bsa.BSA_EWORKSPACE
+    assert badc(14, 587) == bsa.BSA_EWORKSPACE
+    assert badc(13, ctypes.c_void_p(0x10002)) == bsa.BSA_EWORKSPACE
+    assert badc(11, 65535 * 128 + 1) == bsa.BSA_EUNSUPPORTED
     assert badc(6, 0) == bsa.BSA_EINVAL
     assert badc(3, 0) == bsa.BSA_EINVAL
     assert badc(7, None) == bsa.BSA_EINVAL                # frame_cam

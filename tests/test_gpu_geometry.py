@@ -81,11 +81,11 @@ def test_slab_overlap_and_coverage_at_chunk_48_sampled():
     assert np.array_equal(cov.cpu().numpy()[blocks], ref_cov.astype(np.float32))
 
 
-@pytest.mark.parametrize("block", [128, 64, 1, 200])
+@pytest.mark.parametrize("block", [128, 64, 1, 200, 300])
 def test_slab_coverage_matches_oracle(block):
     dev = need_gpu()
     import block_sparse_attention_gilbert_amd as bsa
-    grid = (3, 30, 52) if block in (128, 64) else (2, 6, 9)
+    grid = (3, 30, 52) if block in (128, 64, 300) else (2, 6, 9)
     g = workloads.geometry_inputs(3, 37, grid=grid)
     d = _dev(g, dev)
     perm, _ = bsa.gilbert_index(*grid, device=dev)
