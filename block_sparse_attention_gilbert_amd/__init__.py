@@ -9,6 +9,7 @@ been built, importing this package raises ImportError; there is no fallback.
 
 Entry points (same names as the C ABI, without the ``bsa_`` prefix):
 ``gilbert_index``, ``gilbert_perm``, ``gilbert_block_window``,
+``gilbert_tile_index``, ``tile_perm``, ``tile_block_window``,
 ``slab_overlap``, ``slab_coverage``, ``route_topk`` (with
 ``route_workspace_size``), ``route_materialize`` (with
 ``route_materialize_workspace_size``), ``block_sparse_attn``,
@@ -89,6 +90,12 @@ _lib.bsa_route_materialize_workspace_size.argtypes = [ctypes.POINTER(RouteArgs),
 _lib.bsa_route_materialize.restype = _i
 _lib.bsa_route_materialize.argtypes = [ctypes.POINTER(RouteArgs), ctypes.POINTER(MaterializeArgs), _p,
                                        ctypes.c_size_t, _p]
+_lib.bsa_gilbert_tile_index.restype = _i
+_lib.bsa_gilbert_tile_index.argtypes = [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p]
+_lib.bsa_tile_perm.restype = _i
+_lib.bsa_tile_perm.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i64, _i64, _i, _i, _p]
+_lib.bsa_tile_block_window.restype = _i
+_lib.bsa_tile_block_window.argtypes = [_p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _i, _p]
 _lib.bsa_slab_overlap.restype = _i
 _lib.bsa_slab_overlap.argtypes = [_p, _i, _p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _p, _i64, _p]
 _lib.bsa_slab_coverage.restype = _i
@@ -106,7 +113,8 @@ _lib.bsa_dense_attn.restype = _i
 _lib.bsa_dense_attn.argtypes = _ATTN_COMMON + [_f, _p]
 
 EXPORTED = ("bsa_version", "bsa_strerror", "bsa_last_error_detail", "bsa_gilbert_index",
-            "bsa_gilbert_perm", "bsa_gilbert_block_window", "bsa_route_workspace_size", "bsa_route_topk",
+            "bsa_gilbert_perm", "bsa_gilbert_block_window", "bsa_gilbert_tile_index", "bsa_tile_perm",
+            "bsa_tile_block_window", "bsa_route_workspace_size", "bsa_route_topk",
             "bsa_route_materialize_workspace_size", "bsa_route_materialize", "bsa_slab_overlap",
             "bsa_slab_coverage", "bsa_slab_coverage_workspace_size", "bsa_block_sparse_attn", "bsa_dense_attn")
 
@@ -233,6 +241,78 @@ def gilbert_block_window(perm: torch.Tensor, inv: torch.Tensor, grid, *, block: 
         raise ValueError("window must be int32 [n_blocks][stride] with contiguous rows")
     _check(_lib.bsa_gilbert_block_window(_ptr(perm), _ptr(inv), T, H, W, block, q_chunk, _ptr(window),
                                          _ptr(_i32(window_len, "window_len")), window.stride(0), _stream(stream)))
+    return window, window_len
+
+
+def tile_grid(grid, tile):
+    """Tiles along each axis of a chunk grid."""
+    return tuple(-(-g // t) for g, t in zip(grid, tile))
+
+
+def gilbert_tile_index(T: int, H: int, W: int, tile, device="cuda", stream=None, with_cell_row=True):
+    """Fixed 3-D tile layout of a chunk: ``(row_cell, block_len, cell_row)``
+    int32 tensors (``row_cell[r]`` = raster cell of row r, -1 for padding)."""
+    tt, th, tw = tile
+    n_tiles = 1
+    for x in tile_grid((T, H, W), tile):
+        n_tiles *= x
+    row_cell = torch.empty(n_tiles * tt * th * tw, dtype=torch.int32, device=device)
+    block_len = torch.empty(n_tiles, dtype=torch.int32, device=device)
+    cell_row = torch.empty(T * H * W, dtype=torch.int32, device=device) if with_cell_row else None
+    _check(_lib.bsa_gilbert_tile_index(T, H, W, tt, th, tw, _ptr(row_cell), _ptr(block_len), _ptr(cell_row),
+                                       _stream(stream)))
+    return row_cell, block_len, cell_row
+
+
+def tile_perm(src: torch.Tensor, row_cell: torch.Tensor, *, inverse: bool = False,
+              dst: Optional[torch.Tensor] = None, L: Optional[int] = None, stream=None):
+    """Raster ``[L][heads][d]`` -> tiled ``[heads][n_rows][d]``
+    (``inverse=False``) or back, through the tile layout's ``row_cell``."""
+    _need_gpu(src, row_cell, dst)
+    row_cell = _i32(row_cell, "row_cell")
+    n_rows = row_cell.numel()
+    if not inverse:
+        L_, heads, d = src.shape
+        if src.stride(2) != 1 or src.stride(1) != d:
+            raise ValueError("raster src must have contiguous [heads][d] per token")
+        if dst is None:
+            dst = torch.empty((heads, n_rows, d), dtype=src.dtype, device=src.device)
+        _, drows, ths = _heads_rows(dst, d)
+        if drows < n_rows:
+            raise ValueError("dst holds %d rows per head, %d needed" % (drows, n_rows))
+        _check(_lib.bsa_tile_perm(_ptr(src), _ptr(dst), _ptr(row_cell), n_rows, L_, heads, d, src.stride(0), ths, 0,
+                                  _dtype_code(src), _stream(stream)))
+        return dst
+    d = src.shape[2]
+    heads, _, ths = _heads_rows(src, d)
+    if L is None:
+        raise ValueError("L (tokens of the chunk) is required for the inverse permutation")
+    if dst is None:
+        dst = torch.empty((L, heads, d), dtype=src.dtype, device=src.device)
+    if dst.stride(2) != 1 or dst.stride(1) != d:
+        raise ValueError("raster dst must have contiguous [heads][d] per token")
+    _check(_lib.bsa_tile_perm(_ptr(src), _ptr(dst), _ptr(row_cell), n_rows, L, heads, d, dst.stride(0), ths, 1,
+                              _dtype_code(src), _stream(stream)))
+    return dst
+
+
+def tile_block_window(row_cell: torch.Tensor, cell_row: torch.Tensor, grid, *, block: int, q_chunk: int, out=None,
+                      stream=None):
+    """Local window of every tile block of chunk ``q_chunk``: ``(window,
+    window_len)`` as ``gilbert_block_window``."""
+    _need_gpu(row_cell, cell_row)
+    row_cell, cell_row = _i32(row_cell, "row_cell"), _i32(cell_row, "cell_row")
+    T, H, W = grid
+    n_rows = row_cell.numel()
+    nbc = n_rows // block
+    if out is None:
+        out = (torch.empty((nbc, 2 * nbc), dtype=torch.int32, device=row_cell.device),
+               torch.empty(nbc, dtype=torch.int32, device=row_cell.device))
+    window, window_len = out
+    if window.dtype != torch.int32 or window.dim() != 2 or window.stride(1) != 1 or window.shape[0] < nbc:
+        raise ValueError("window must be int32 [n_blocks][stride] with contiguous rows")
+    _check(_lib.bsa_tile_block_window(_ptr(row_cell), _ptr(cell_row), n_rows, T, H, W, block, q_chunk, _ptr(window),
+                                      _ptr(_i32(window_len, "window_len")), window.stride(0), _stream(stream)))
     return window, window_len
 
 
@@ -524,7 +604,8 @@ def dense_attn(q, k, v, *, block: int, scale: Optional[float] = None, q_block_le
     return out, lse
 
 
-__all__ = ["gilbert_index", "gilbert_perm", "gilbert_block_window", "slab_overlap", "slab_coverage", "route_topk", "route_workspace_size",
+__all__ = ["gilbert_index", "gilbert_perm", "gilbert_block_window", "gilbert_tile_index", "tile_perm",
+           "tile_block_window", "tile_grid", "slab_overlap", "slab_coverage", "route_topk", "route_workspace_size",
            "route_capacity", "route_materialize", "route_materialize_workspace_size", "materialize_capacity",
            "MaterializeArgs", "block_sparse_attn", "dense_attn", "version", "library", "BsaError", "RouteArgs", "EXPORTED",
            "BSA_OK", "BSA_EINVAL", "BSA_EUNSUPPORTED", "BSA_EWORKSPACE", "BSA_EHIP", "BSA_BF16", "BSA_F32"]

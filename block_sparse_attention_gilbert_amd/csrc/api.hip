@@ -57,6 +57,37 @@ int bsa_gilbert_block_window(const int32_t* perm, const int32_t* inv, int T, int
                       "gilbert_block_window launch");
 }
 
+int bsa_gilbert_tile_index(int T, int H, int W, int tile_t, int tile_h, int tile_w, int32_t* row_cell,
+                           int32_t* block_len, int32_t* cell_row, hipStream_t stream) {
+    bsa::clear_error();
+    const int st = bsa::validate_tile_index(T, H, W, tile_t, tile_h, tile_w, row_cell, block_len);
+    if (st != BSA_OK) return st;
+    return hip_status(bsa::launch_tile_index(T, H, W, tile_t, tile_h, tile_w, row_cell, block_len, cell_row, stream),
+                      "gilbert_tile_index launch");
+}
+
+int bsa_tile_perm(const void* src, void* dst, const int32_t* row_cell, int n_rows, int L, int heads, int d,
+                  int64_t raster_token_stride, int64_t tiled_head_stride, int inverse, int dtype, hipStream_t stream) {
+    bsa::clear_error();
+    const int st = bsa::validate_tile_perm(src, dst, row_cell, n_rows, L, heads, d, raster_token_stride,
+                                           tiled_head_stride, inverse, dtype);
+    if (st != BSA_OK) return st;
+    return hip_status(bsa::launch_tile_perm(src, dst, row_cell, n_rows, L, heads, d, raster_token_stride,
+                                            tiled_head_stride, inverse, dtype, stream),
+                      "tile_perm launch");
+}
+
+int bsa_tile_block_window(const int32_t* row_cell, const int32_t* cell_row, int n_rows, int T, int H, int W, int block,
+                          int q_chunk, int32_t* window, int32_t* window_len, int window_stride, hipStream_t stream) {
+    bsa::clear_error();
+    const int st = bsa::validate_tile_block_window(row_cell, cell_row, n_rows, T, H, W, block, q_chunk, window,
+                                                   window_len, window_stride);
+    if (st != BSA_OK) return st;
+    return hip_status(bsa::launch_tile_block_window(row_cell, cell_row, n_rows, T, H, W, block, q_chunk, window,
+                                                    window_len, window_stride, stream),
+                      "tile_block_window launch");
+}
+
 int bsa_route_materialize(const bsa_route_args* args, const bsa_materialize_args* margs, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {
     bsa::clear_error();

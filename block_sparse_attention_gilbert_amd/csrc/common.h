@@ -56,6 +56,12 @@ size_t route_layout(const bsa_route_args* a, RouteLayout* lay);
 
 // Largest candidate count the in-LDS top-K sort handles.
 constexpr int kMaxCandidates = 4096;
+int validate_tile_index(int T, int H, int W, int tt, int th, int tw, const int32_t* row_cell, const int32_t* block_len);
+int validate_tile_perm(const void* src, const void* dst, const int32_t* row_cell, int n_rows, int L, int heads, int d,
+                       int64_t raster_token_stride, int64_t tiled_head_stride, int inverse, int dtype);
+int validate_tile_block_window(const int32_t* row_cell, const int32_t* cell_row, int n_rows, int T, int H, int W,
+                               int block, int q_chunk, const int32_t* window, const int32_t* window_len,
+                               int window_stride);
 int validate_slab_overlap(const double* cams, int n_cams, const int32_t* q_ptr, const int32_t* q_cam,
                           const double* q_geom, int nqb, int n_q, const int32_t* h_ptr, const int32_t* h_cam,
                           const double* h_geom, int nkb, int n_h, int grid_n, const float* overlap, int64_t stride);

@@ -87,6 +87,60 @@ __global__ void gilbert_perm_kernel(const uint4* __restrict__ src, uint4* __rest
 
 }  // namespace
 
+// Fixed 3-D tile layout: one thread per row of the tiled chunk.  Block b
+// is the tile at position b of the Gilbert curve over the tile grid; its
+// cells, in raster order inside the (clipped) tile, fill its first rows and
+// the rest are padding (-1).
+// [Light Interaction -- abstract: 3-D block-sparse attention; Velox -- Key
+//  Contributions 3: global-aligned Gilbert KV storage]
+__global__ void tile_index_kernel(int T, int H, int W, int tt, int th, int tw, int nT, int nH, int nW,
+                                  int32_t* __restrict__ row_cell, int32_t* __restrict__ block_len,
+                                  int32_t* __restrict__ cell_row) {
+    const int V = tt * th * tw;
+    const int64_t rows = (int64_t)nT * nH * nW * V;
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= rows) return;
+    const int b = (int)(r / V), k = (int)(r % V);
+    const V3 tile = gilbert_cell(nT, nH, nW, b);
+    const int t0 = tile.t * tt, h0 = tile.h * th, w0 = tile.w * tw;
+    const int vt = min(T, t0 + tt) - t0, vh = min(H, h0 + th) - h0, vw = min(W, w0 + tw) - w0;
+    const int n = vt * vh * vw;
+    if (k == 0) block_len[b] = n;
+    if (k < n) {
+        const int kt = k / (vh * vw), kh = (k / vw) % vh, kw = k % vw;
+        const int cell = ((t0 + kt) * H + (h0 + kh)) * W + (w0 + kw);
+        row_cell[r] = cell;
+        if (cell_row) cell_row[cell] = (int32_t)r;
+    } else {
+        row_cell[r] = -1;
+    }
+}
+
+// Permutation through a row map: row i of the tiled layout holds raster
+// token row_cell[i]; rows with a negative entry are padding (written as
+// zeros forward, skipped inverse).  Same thread walk as gilbert_perm_kernel.
+template <bool INVERSE>
+__global__ void tile_perm_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                 const int32_t* __restrict__ row_cell, int L, int heads, int chunks_per_row,
+                                 int64_t rows_total, int64_t raster_token_stride_c, int64_t tiled_head_stride_c) {
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = rows_total * heads * chunks_per_row;
+    if (tid >= total) return;
+    const int ch = (int)(tid % chunks_per_row);
+    const int64_t rest = tid / chunks_per_row;
+    const int h = (int)(rest % heads);
+    const int64_t i = rest / heads;
+    const int64_t g = h * tiled_head_stride_c + i * chunks_per_row + ch;
+    const int cell = row_cell[i];
+    const bool valid = cell >= 0 && cell < L;
+    const int64_t r = (int64_t)(valid ? cell : 0) * raster_token_stride_c + (int64_t)h * chunks_per_row + ch;
+    if (!INVERSE) {
+        dst[g] = valid ? src[r] : make_uint4(0u, 0u, 0u, 0u);
+    } else if (valid) {
+        dst[r] = src[g];
+    }
+}
+
 // Local window of each query block: one workgroup per block b of the chunk;
 // each thread takes tokens of b, walks the 27 cells of their 3 x 3 x 3
 // neighbourhood (the cell itself included; time crosses into the previous
@@ -100,19 +154,25 @@ constexpr int kWindowWords = 2 * kMaxWindowChunkBlocks / 32;  // bitmap words: 2
 
 static_assert(kWindowWords == 64, "one wave compacts the window bitmap");
 
+// Rows of block b are b*block .. (b+1)*block-1, bounded by row_end; the
+// cell of row r is row_cell[r] (negative: a padding row) and the row of a
+// cell is cell_row[cell].  For blocks that are runs of the curve, row_cell
+// is the curve itself and row_end = T*H*W; for fixed tiles both come from
+// the tile layout.
 __global__ void __launch_bounds__(256)
-block_window_kernel(const int32_t* __restrict__ perm, const int32_t* __restrict__ inv, int T, int H, int W,
-                    int block, int nbc, int q_chunk, int32_t* __restrict__ window, int32_t* __restrict__ window_len,
-                    int stride) {
+block_window_kernel(const int32_t* __restrict__ row_cell, const int32_t* __restrict__ cell_row, int row_end, int T,
+                    int H, int W, int block, int nbc, int q_chunk, int32_t* __restrict__ window,
+                    int32_t* __restrict__ window_len, int stride) {
     __shared__ unsigned bits[kWindowWords];
     __shared__ int wsum[4];
     const int b = blockIdx.x, t = threadIdx.x;
     const int L = T * H * W;
     if (t < kWindowWords) bits[t] = 0u;
     __syncthreads();
-    const int g1 = min(L, (b + 1) * block);
+    const int g1 = min(row_end, (b + 1) * block);
     for (int gp = b * block + t; gp < g1; gp += blockDim.x) {
-        const int cell = perm[gp];
+        const int cell = row_cell[gp];
+        if (cell < 0 || cell >= L) continue;
         const int tt0 = cell / (H * W), rem = cell % (H * W), h0 = rem / W, w0 = rem % W;
         for (int dt = -1; dt <= 1; ++dt) {
             int tt = tt0 + dt, slot = 1;  // slot 1: the query chunk, 0: the previous one
@@ -129,7 +189,7 @@ block_window_kernel(const int32_t* __restrict__ perm, const int32_t* __restrict_
                 for (int dw = -1; dw <= 1; ++dw) {
                     const int ww = w0 + dw;
                     if (ww < 0 || ww >= W) continue;
-                    const int nb = inv[(tt * H + hh) * W + ww] / block;
+                    const int nb = cell_row[(tt * H + hh) * W + ww] / block;
                     const int bit = slot * nbc + nb;
                     atomicOr(&bits[bit >> 5], 1u << (bit & 31));
                 }
@@ -199,8 +259,45 @@ hipError_t launch_block_window(const int32_t* perm, const int32_t* inv, int T, i
                                int32_t* window, int32_t* window_len, int stride, hipStream_t stream) {
     const int L = T * H * W;
     const int nbc = (L + block - 1) / block;
-    hipLaunchKernelGGL(block_window_kernel, dim3(nbc), dim3(256), 0, stream, perm, inv, T, H, W, block, nbc, q_chunk,
-                       window, window_len, stride);
+    hipLaunchKernelGGL(block_window_kernel, dim3(nbc), dim3(256), 0, stream, perm, inv, L, T, H, W, block, nbc,
+                       q_chunk, window, window_len, stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_block_window(const int32_t* row_cell, const int32_t* cell_row, int n_rows, int T, int H, int W,
+                                    int block, int q_chunk, int32_t* window, int32_t* window_len, int stride,
+                                    hipStream_t stream) {
+    const int nbc = n_rows / block;
+    hipLaunchKernelGGL(block_window_kernel, dim3(nbc), dim3(256), 0, stream, row_cell, cell_row, n_rows, T, H, W, block,
+                       nbc, q_chunk, window, window_len, stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_index(int T, int H, int W, int tt, int th, int tw, int32_t* row_cell, int32_t* block_len,
+                             int32_t* cell_row, hipStream_t stream) {
+    const int nT = (T + tt - 1) / tt, nH = (H + th - 1) / th, nW = (W + tw - 1) / tw;
+    const int64_t rows = (int64_t)nT * nH * nW * tt * th * tw;
+    hipLaunchKernelGGL(tile_index_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, T, H, W, tt, th,
+                       tw, nT, nH, nW, row_cell, block_len, cell_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_perm(const void* src, void* dst, const int32_t* row_cell, int n_rows, int L, int heads, int d,
+                            int64_t raster_token_stride, int64_t tiled_head_stride, int inverse, int dtype,
+                            hipStream_t stream) {
+    const int eb = dtype == BSA_BF16 ? 2 : 4;
+    const int chunk_elems = 16 / eb;
+    const int chunks_per_row = d / chunk_elems;
+    const int64_t total = (int64_t)n_rows * heads * chunks_per_row;
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    const int64_t rts_c = raster_token_stride / chunk_elems;
+    const int64_t ths_c = tiled_head_stride / chunk_elems;
+    if (inverse)
+        hipLaunchKernelGGL(tile_perm_kernel<true>, dim3(blocks), dim3(256), 0, stream, static_cast<const uint4*>(src),
+                           static_cast<uint4*>(dst), row_cell, L, heads, chunks_per_row, (int64_t)n_rows, rts_c, ths_c);
+    else
+        hipLaunchKernelGGL(tile_perm_kernel<false>, dim3(blocks), dim3(256), 0, stream, static_cast<const uint4*>(src),
+                           static_cast<uint4*>(dst), row_cell, L, heads, chunks_per_row, (int64_t)n_rows, rts_c, ths_c);
     return hipGetLastError();
 }
 

@@ -19,6 +19,17 @@ hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* w
 hipError_t launch_block_window(const int32_t* perm, const int32_t* inv, int T, int H, int W, int block, int q_chunk,
                                int32_t* window, int32_t* window_len, int stride, hipStream_t stream);
 
+hipError_t launch_tile_block_window(const int32_t* row_cell, const int32_t* cell_row, int n_rows, int T, int H, int W,
+                                    int block, int q_chunk, int32_t* window, int32_t* window_len, int stride,
+                                    hipStream_t stream);
+
+hipError_t launch_tile_index(int T, int H, int W, int tt, int th, int tw, int32_t* row_cell, int32_t* block_len,
+                             int32_t* cell_row, hipStream_t stream);
+
+hipError_t launch_tile_perm(const void* src, void* dst, const int32_t* row_cell, int n_rows, int L, int heads, int d,
+                            int64_t raster_token_stride, int64_t tiled_head_stride, int inverse, int dtype,
+                            hipStream_t stream);
+
 hipError_t launch_materialize(const bsa_route_args* a, const bsa_materialize_args* m, const RouteLayout& lay,
                               void* ws, hipStream_t stream);
 

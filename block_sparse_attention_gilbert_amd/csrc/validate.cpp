@@ -235,6 +235,61 @@ int validate_block_window(const int32_t* perm, const int32_t* inv, int T, int H,
     return BSA_OK;
 }
 
+int validate_tile_index(int T, int H, int W, int tt, int th, int tw, const int32_t* row_cell, const int32_t* block_len) {
+    if (T < 1 || H < 1 || W < 1) return fail(BSA_EINVAL, "grid %d x %d x %d: dimensions must be >= 1", T, H, W);
+    if (tt < 1 || th < 1 || tw < 1) return fail(BSA_EINVAL, "tile %d x %d x %d: dimensions must be >= 1", tt, th, tw);
+    if (!row_cell || !block_len) return fail(BSA_EINVAL, "row_cell and block_len must be non-NULL");
+    const int64_t rows = ceil_div(T, tt) * ceil_div(H, th) * ceil_div(W, tw) * ((int64_t)tt * th * tw);
+    if (rows > INT32_MAX || (int64_t)T * H * W > INT32_MAX)
+        return fail(BSA_EINVAL, "tiled rows or cells exceed 2^31-1");
+    return BSA_OK;
+}
+
+int validate_tile_perm(const void* src, const void* dst, const int32_t* row_cell, int n_rows, int L, int heads, int d,
+                       int64_t raster_token_stride, int64_t tiled_head_stride, int inverse, int dtype) {
+    if (!src || !dst || !row_cell) return fail(BSA_EINVAL, "src, dst and row_cell must be non-NULL");
+    if (dtype != BSA_BF16 && dtype != BSA_F32) return fail(BSA_EUNSUPPORTED, "dtype %d", dtype);
+    if (!supported_dim(d)) return fail(BSA_EUNSUPPORTED, "d = %d (64 or 128)", d);
+    if (n_rows < 1 || L < 1 || heads < 1)
+        return fail(BSA_EINVAL, "n_rows = %d, L = %d, heads = %d must be >= 1", n_rows, L, heads);
+    if (inverse != 0 && inverse != 1) return fail(BSA_EINVAL, "inverse = %d (0 or 1)", inverse);
+    if (raster_token_stride < (int64_t)heads * d)
+        return fail(BSA_EINVAL, "raster_token_stride %lld < heads*d = %lld", (long long)raster_token_stride,
+                    (long long)heads * d);
+    if (tiled_head_stride < (int64_t)n_rows * d)
+        return fail(BSA_EINVAL, "tiled_head_stride %lld < n_rows*d = %lld", (long long)tiled_head_stride,
+                    (long long)n_rows * d);
+    const int eb = dtype_bytes(dtype);
+    if (!aligned16(src) || !aligned16(dst) || (raster_token_stride * eb) % 16 || (tiled_head_stride * eb) % 16)
+        return fail(BSA_EINVAL, "pointers and strides must be 16-byte aligned");
+    const char* s = static_cast<const char*>(src);
+    const char* t = static_cast<const char*>(dst);
+    const int64_t raster_bytes = ((int64_t)(L - 1) * raster_token_stride + (int64_t)heads * d) * eb;
+    const int64_t tiled_bytes = ((int64_t)(heads - 1) * tiled_head_stride + (int64_t)n_rows * d) * eb;
+    const int64_t sb = inverse ? tiled_bytes : raster_bytes, tb = inverse ? raster_bytes : tiled_bytes;
+    if (s < t + tb && t < s + sb) return fail(BSA_EINVAL, "src and dst overlap");
+    return BSA_OK;
+}
+
+int validate_tile_block_window(const int32_t* row_cell, const int32_t* cell_row, int n_rows, int T, int H, int W,
+                               int block, int q_chunk, const int32_t* window, const int32_t* window_len,
+                               int window_stride) {
+    if (T < 1 || H < 1 || W < 1) return fail(BSA_EINVAL, "grid %d x %d x %d: dimensions must be >= 1", T, H, W);
+    if ((int64_t)T * H * W > INT32_MAX) return fail(BSA_EINVAL, "grid exceeds 2^31-1 cells");
+    if (!row_cell || !cell_row || !window || !window_len)
+        return fail(BSA_EINVAL, "row_cell, cell_row, window and window_len must be non-NULL");
+    if (block < 1 || n_rows < 1 || n_rows % block)
+        return fail(BSA_EINVAL, "n_rows %d must be a positive multiple of block %d", n_rows, block);
+    if (q_chunk < 0) return fail(BSA_EINVAL, "q_chunk %d < 0", q_chunk);
+    const int nbc = n_rows / block;
+    if (nbc > kMaxWindowChunkBlocks)
+        return fail(BSA_EUNSUPPORTED, "%d blocks per chunk exceed %d", nbc, kMaxWindowChunkBlocks);
+    if (window_stride < 2 * nbc)
+        return fail(BSA_EINVAL, "window_stride %d < 2 * blocks per chunk (%d)", window_stride, 2 * nbc);
+    if (((int64_t)q_chunk + 1) * nbc > INT32_MAX) return fail(BSA_EINVAL, "block indices exceed 2^31-1");
+    return BSA_OK;
+}
+
 int validate_slab_overlap(const double* cams, int n_cams, const int32_t* q_ptr, const int32_t* q_cam,
                           const double* q_geom, int nqb, int n_q, const int32_t* h_ptr, const int32_t* h_cam,
                           const double* h_geom, int nkb, int n_h, int grid_n, const float* overlap, int64_t stride) {

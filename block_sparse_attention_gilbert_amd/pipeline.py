@@ -8,7 +8,10 @@ Steps 4-6; Key Contributions 3]
 
 Per call (``RoutedAttention.step``):
 
-1. the chunk's Gilbert order (computed once per grid and cached);
+1. the chunk's Gilbert order (recomputed into preallocated buffers); blocks
+   are runs of ``block`` tokens along it, or, with ``tile=(tt, th, tw)``,
+   fixed tt x th x tw tiles ordered by the Gilbert curve of the tile grid
+   [Light Interaction -- abstract: 3-D block-sparse attention];
 2. Q, K, V of the current chunk, raster token-major ``[L][heads][d]``, are
    permuted into Gilbert head-major block-padded layout; K and V land in the
    current chunk's slot of the KV store (the store grows by appending);
@@ -36,7 +39,8 @@ from typing import Optional
 import torch
 
 from . import (_check, _lib, _ptr, _stream, block_sparse_attn, dense_attn, gilbert_block_window, gilbert_index,
-               gilbert_perm, materialize_capacity, route_capacity, route_materialize, route_topk)
+               gilbert_perm, gilbert_tile_index, materialize_capacity, route_capacity, route_materialize, route_topk,
+               tile_block_window, tile_perm)
 
 
 def block_lengths(tokens: int, block: int, n_chunks: int = 1, device="cuda") -> torch.Tensor:
@@ -52,11 +56,18 @@ class RoutedAttention:
     def __init__(self, grid, heads: int, d: int, block: int, store_chunks: int, dtype=torch.bfloat16,
                  device="cuda", k_cap: int = 50, n_dense_tail_chunks: int = 0,
                  k_store: Optional[torch.Tensor] = None, v_store: Optional[torch.Tensor] = None,
-                 use_kpool: bool = True):
+                 use_kpool: bool = True, tile=None):
         self.grid = tuple(grid)
         self.L = grid[0] * grid[1] * grid[2]
         self.heads, self.d, self.block, self.dtype, self.device = heads, d, block, dtype, device
-        self.nbc = -(-self.L // block)              # blocks per chunk
+        self.tile = None if tile is None else tuple(int(x) for x in tile)
+        if self.tile is not None:
+            if self.tile[0] * self.tile[1] * self.tile[2] != block:
+                raise ValueError("the tile volume must equal the block size")
+            self.row_cell, self.block_len, self.cell_row = gilbert_tile_index(*self.grid, self.tile, device=device)
+            self.nbc = self.block_len.numel()        # blocks (tiles) per chunk
+        else:
+            self.nbc = -(-self.L // block)           # blocks per chunk
         self.rows_c = self.nbc * block
         self.store_chunks = store_chunks
         self.k_cap = k_cap
@@ -69,8 +80,12 @@ class RoutedAttention:
         self.o_blk = torch.empty((heads, self.rows_c, d), dtype=dtype, device=device)
         self.o_raster = torch.empty((self.L, heads, d), dtype=dtype, device=device)
         self.lse = torch.empty((heads, self.rows_c), dtype=torch.float32, device=device)
-        self.q_len = block_lengths(self.L, block, 1, device)
-        self.kv_len = block_lengths(self.L, block, store_chunks, device)
+        if self.tile is not None:
+            self.q_len = self.block_len.clone()
+            self.kv_len = self.block_len.repeat(store_chunks)
+        else:
+            self.q_len = block_lengths(self.L, block, 1, device)
+            self.kv_len = block_lengths(self.L, block, store_chunks, device)
         self.perm, self.inv = gilbert_index(*self.grid, device=device)
         nkb_max = store_chunks * self.nbc
         tail = n_dense_tail_chunks * self.nbc
@@ -104,12 +119,24 @@ class RoutedAttention:
         r0, r1 = c * self.rows_c, (c + 1) * self.rows_c
         return self.k_store[:, r0:r1, :], self.v_store[:, r0:r1, :]
 
+    def to_blocks(self, src, dst, stream=None):
+        """Raster ``[L][heads][d]`` -> this layout's blocks (``dst``)."""
+        if self.tile is not None:
+            return tile_perm(src, self.row_cell, dst=dst, stream=stream)
+        return gilbert_perm(src, self.perm, block=self.block, dst=dst, stream=stream)
+
+    def to_raster(self, src, dst, stream=None):
+        """This layout's blocks -> raster ``[L][heads][d]`` (``dst``)."""
+        if self.tile is not None:
+            return tile_perm(src, self.row_cell, inverse=True, dst=dst, L=self.L, stream=stream)
+        return gilbert_perm(src, self.perm, block=self.block, inverse=True, dst=dst, stream=stream)
+
     def append(self, k_raster, v_raster, c: int, stream=None):
         """Permute a chunk's raster K and V into slot ``c`` of the store."""
         ks, vs = self.slot(c)
         self.invalidate_kpool(c * self.nbc)
-        gilbert_perm(k_raster, self.perm, block=self.block, dst=ks, stream=stream)
-        gilbert_perm(v_raster, self.perm, block=self.block, dst=vs, stream=stream)
+        self.to_blocks(k_raster, ks, stream)
+        self.to_blocks(v_raster, vs, stream)
 
     def step(self, q_raster, k_raster, v_raster, c: int, *, k_fixed: Optional[int] = None,
              k_per_row: Optional[torch.Tensor] = None, overlap: Optional[torch.Tensor] = None,
@@ -126,10 +153,10 @@ class RoutedAttention:
         if refresh_index:
             self._index(stream)
         self.append(k_raster, v_raster, c, stream)
-        gilbert_perm(q_raster, self.perm, block=self.block, dst=self.q_blk, stream=stream)
+        self.to_blocks(q_raster, self.q_blk, stream)
         r = self.route_and_attend(c, k_fixed=k_fixed, k_per_row=k_per_row, overlap=overlap, lam=lam, g_ref=g_ref,
                                   tau=tau, materialize=materialize, stream=stream, attn_events=attn_events)
-        gilbert_perm(self.o_blk, self.perm, block=self.block, inverse=True, dst=self.o_raster, stream=stream)
+        self.to_raster(self.o_blk, self.o_raster, stream)
         return self.o_raster, r
 
     def route_and_attend(self, c: int, *, k_fixed: Optional[int] = None, k_per_row: Optional[torch.Tensor] = None,
@@ -166,7 +193,10 @@ class RoutedAttention:
         c is rebuilt into the preallocated rows first."""
         nkb = (c + 1) * self.nbc
         k_hist = self.k_store[:, : nkb * self.block]
-        if window:
+        if window and self.tile is not None:
+            tile_block_window(self.row_cell, self.cell_row, self.grid, block=self.block, q_chunk=c,
+                              out=(self.window, self.window_len), stream=stream)
+        elif window:
             gilbert_block_window(self.perm, self.inv, self.grid, block=self.block, q_chunk=c,
                                  out=(self.window, self.window_len), stream=stream)
         prev = ((c - 1) * self.nbc, c * self.nbc) if c > 0 else (0, 0)
@@ -202,7 +232,13 @@ class RoutedAttention:
         return r
 
     def _index(self, stream=None):
-        """Recompute the chunk's Gilbert order into the preallocated buffers."""
+        """Recompute the chunk's Gilbert order (or tile layout) into the
+        preallocated buffers."""
+        if self.tile is not None:
+            _check(_lib.bsa_gilbert_tile_index(self.grid[0], self.grid[1], self.grid[2], *self.tile,
+                                               _ptr(self.row_cell), _ptr(self.block_len), _ptr(self.cell_row),
+                                               _stream(stream)))
+            return
         _check(_lib.bsa_gilbert_index(self.grid[0], self.grid[1], self.grid[2], _ptr(self.perm), _ptr(self.inv),
                                       _stream(stream)))
 

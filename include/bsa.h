@@ -248,6 +248,64 @@ int bsa_gilbert_block_window(const int32_t* perm, const int32_t* inv, int T, int
                              hipStream_t stream);
 
 /*
+ * Fixed 3-D tile blocks.
+ * [Light Interaction -- abstract (3-D block-sparse attention); Velox -- Key
+ *  Contributions 3 (global-aligned Gilbert KV storage); Methodology,
+ *  Step 5 (26-neighbour window in the Gilbert block ordering)]
+ *
+ * A block is a tile_t x tile_h x tile_w tile of the T x H x W chunk grid, on
+ * the tile grid ceil(T/tile_t) x ceil(H/tile_h) x ceil(W/tile_w) aligned to
+ * the chunk's origin (tiles at the far edges are clipped).  Block b is the
+ * tile at position b of the Gilbert curve over the tile grid (the curve of
+ * bsa_gilbert_index).  A block has V = tile_t*tile_h*tile_w rows: its
+ * tile's cells in raster order, then padding, so every block carries a
+ * valid length and every kernel that takes per-block lengths works on it
+ * unchanged (attention and routing need V = 64 or 128).
+ */
+
+/*
+ * bsa_gilbert_tile_index -- the tile layout of a chunk.
+ * row_cell   int32[n_tiles*V]: raster cell of each row, -1 for padding.
+ * block_len  int32[n_tiles]: valid rows of each block.
+ * cell_row   int32[T*H*W] (nullable): the row of each cell.
+ * Errors: BSA_EINVAL (dimensions < 1, rows or cells past 2^31-1, NULL
+ * outputs).
+ */
+int bsa_gilbert_tile_index(int T, int H, int W, int tile_t, int tile_h, int tile_w, int32_t* row_cell,
+                           int32_t* block_len, int32_t* cell_row, hipStream_t stream);
+
+/*
+ * bsa_tile_perm -- permute a chunk between raster token-major layout
+ * (element (token t, head h, channel c) at raster[t * raster_token_stride +
+ * h * d + c], t < L) and the tiled head-major layout (element (head h, row
+ * i, channel c) at tiled[h * tiled_head_stride + i * d + c], i < n_rows)
+ * through row_cell (bsa_gilbert_tile_index; entries outside [0, L) are
+ * padding).  inverse = 0: raster -> tiled, padding rows written as zeros;
+ * inverse = 1: tiled -> raster, padding rows not read.  Bitwise copy; src
+ * and dst must not overlap.
+ * Errors: BSA_EINVAL (null pointers, sizes, strides, alignment, overlap),
+ * BSA_EUNSUPPORTED (d, dtype).
+ */
+int bsa_tile_perm(const void* src, void* dst, const int32_t* row_cell, int n_rows, int L, int heads,
+                  int d, int64_t raster_token_stride, int64_t tiled_head_stride, int inverse,
+                  int dtype, hipStream_t stream);
+
+/*
+ * bsa_tile_block_window -- bsa_gilbert_block_window for the tile layout:
+ * the blocks holding any cell of the 3 x 3 x 3 neighbourhood of any cell of
+ * query block b, which for tiles is exactly the 3 x 3 x 3 neighbourhood of
+ * b's tile (time stepping back from the first tile layer into chunk
+ * q_chunk - 1's last one, never forward into chunk q_chunk + 1).  block =
+ * V; n_rows = n_tiles*V; window rows as for bsa_gilbert_block_window.
+ * Errors: BSA_EINVAL (null pointers, n_rows not a multiple of block,
+ * q_chunk < 0, window_stride < 2*n_tiles), BSA_EUNSUPPORTED (more than
+ * 1024 tiles per chunk).
+ */
+int bsa_tile_block_window(const int32_t* row_cell, const int32_t* cell_row, int n_rows, int T, int H,
+                          int W, int block, int q_chunk, int32_t* window, int32_t* window_len,
+                          int window_stride, hipStream_t stream);
+
+/*
  * Route materialisation arguments.  Set struct_size =
  * sizeof(bsa_materialize_args).
  * [Velox -- Methodology, Step 3 (a coverage score per query block: the
