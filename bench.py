@@ -2,7 +2,7 @@
 48 on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk C]
-                    [--no-cpu-baseline] [--dense] [--sweep FILE] [--rollout FILE]
+                    [--no-cpu-baseline] [--dense] [--tiles] [--sweep FILE] [--rollout FILE]
 
 Workload: the 14B-like growing-context layer -- 40 heads, head dim 128, a
 3 x 30 x 52 latent chunk (4680 tokens, 37 blocks of 128), a KV history of C
@@ -150,6 +150,56 @@ def step_graph_ms(st, reps: int):
     torch.cuda.synchronize()
     assert torch.equal(ra.o_raster, o_eager), "graph replay differs from the eager step"
     return e0.elapsed_time(e1) / reps
+
+
+def tiles(chunk: int, reps: int, device: str, tile=(1, 8, 16)):
+    """The step with fixed 3-D tile blocks (a tile of 1 x 8 x 16 = 128 tokens;
+    48 tiles per chunk, the edge tiles partly empty) instead of 128-token
+    runs of the curve, at the same chunk, top-K 50: the same draws of C4 laid
+    out in tiles (``workloads.c4`` with the tile lengths)."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from block_sparse_attention_gilbert_amd import gilbert_tile_index
+    from block_sparse_attention_gilbert_amd.pipeline import RoutedAttention
+
+    _, block_len, _ = gilbert_tile_index(3, 30, 52, tile, device=device)
+    lens = block_len.cpu().numpy()
+    w = workloads.c4(c=chunk, chunk_lens=lens)
+    ra = RoutedAttention((3, 30, 52), w.heads, w.d, w.bs, chunk, device=device, k_cap=50,
+                         k_store=w.k.contiguous().to(device), v_store=w.v.contiguous().to(device), tile=tile)
+    cur = chunk - 1
+    ks, vs = ra.slot(cur)
+    q_r = ra.to_raster(w.q.to(device), torch.empty((4680, w.heads, w.d), dtype=w.dtype, device=device))
+    k_r = ra.to_raster(ks, torch.empty((4680, w.heads, w.d), dtype=w.dtype, device=device))
+    v_r = ra.to_raster(vs, torch.empty((4680, w.heads, w.d), dtype=w.dtype, device=device))
+    before = ks.clone()
+    for _ in range(3):
+        ra.step(q_r, k_r, v_r, cur)
+    torch.cuda.synchronize()
+    assert torch.equal(before, ra.slot(cur)[0]), "tile permutation did not reproduce the store slot"
+    del before
+    events = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        _, r = ra.step(q_r, k_r, v_r, cur, attn_events=events)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / reps
+    attn_ms = sum(a.elapsed_time(b) for a, b in events) / len(events)
+    wc = work_counts(r["row_ptr"], r["col_idx"], w.q_len, w.k_len, w.heads, w.nqb, w.bs, w.d)
+    out = {"tile": list(tile), "blocks_per_chunk": int(w.nqb), "kv_blocks": int(w.nkb),
+           "mean_valid_per_block": round(float(np.mean(lens)), 2),
+           "ms_per_step": round(ms_step, 4), "attn_ms": round(attn_ms, 4),
+           "step_effective_tflops": round(wc["flop"] / (ms_step * 1e-3) / 1e12, 2),
+           "attn_effective_tflops": round(wc["flop"] / (attn_ms * 1e-3) / 1e12, 2),
+           "attn_tile_tflops": round(wc["tile_flop"] / (attn_ms * 1e-3) / 1e12, 2),
+           "effective_flop": wc["flop"]}
+    del ra, w, ks, vs, q_r, k_r, v_r
+    torch.cuda.empty_cache()
+    return out
 
 
 def geometry(st, reps: int):
@@ -375,6 +425,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=40)
     ap.add_argument("--dense", action="store_true", help="also time dense attention at the same chunk")
+    ap.add_argument("--tiles", action="store_true",
+                    help="also time the step with fixed 1 x 8 x 16 tile blocks at the same chunk")
     ap.add_argument("--no-materialized", action="store_true",
                     help="skip timing the slab geometry and the step with the materialised route")
     ap.add_argument("--sweep", default=None, help="write a chunk 1..C sparse/dense sweep to this JSONL file")
@@ -503,6 +555,8 @@ def main():
         geo, ov, cov = geometry(st, max(1, min(args.steps, 10)))
         out["geometry"] = geo
         out["materialized"] = materialized(st, max(1, min(args.steps, 10)), ov, cov)
+    if args.tiles:
+        out["tiles"] = tiles(args.chunk, max(1, min(args.steps, 10)), dev)
     if args.sweep:
         sweep(st, args.sweep)
     if args.rollout:

@@ -190,7 +190,7 @@ def c3(heads=None) -> Workload:
     return w
 
 
-def c4(c: int = 48, heads=None, n_store_chunks: Optional[int] = None) -> Workload:
+def c4(c: int = 48, heads=None, n_store_chunks: Optional[int] = None, chunk_lens=None) -> Workload:
     """Growing-context 14B-like layer, bf16: 40 heads, d 128, a 4680-token
     query chunk (37 blocks of 128), KV history of ``c`` chunks of 4680 tokens
     (37 blocks each, the last of each chunk holds 72 tokens); N(0,1) plus
@@ -198,12 +198,14 @@ def c4(c: int = 48, heads=None, n_store_chunks: Optional[int] = None) -> Workloa
 
     The KV store is drawn chunk by chunk, so the history at ``c`` is the
     prefix of the history at any larger ``c`` (the store grows by appending).
-    ``n_store_chunks`` (default ``c``) sets how many chunks are allocated."""
+    ``n_store_chunks`` (default ``c``) sets how many chunks are allocated.
+    ``chunk_lens`` replaces the per-chunk block lengths (e.g. those of a
+    fixed-tile layout: the same draws, blocks of other valid lengths)."""
     seed, H, d, bs = 1004, 40, 128, 128
     head_ids = list(range(H)) if heads is None else list(heads)
     n_store = c if n_store_chunks is None else max(c, n_store_chunks)
-    qlen = block_lengths(CHUNK_TOKENS, bs)
-    klen_chunk = block_lengths(CHUNK_TOKENS, bs)
+    qlen = block_lengths(CHUNK_TOKENS, bs) if chunk_lens is None else np.asarray(chunk_lens, dtype=np.int32)
+    klen_chunk = qlen.copy()
     q = _blocked_tensor(seed, T_QNOISE, T_QOFF, H, head_ids, 1, qlen, bs, d, torch.bfloat16, 0.5)
     k = _blocked_tensor(seed, T_KNOISE, T_KOFF, H, head_ids, n_store, klen_chunk, bs, d, torch.bfloat16, 0.5)
     v = _blocked_tensor(seed, T_V, None, H, head_ids, n_store, klen_chunk, bs, d, torch.bfloat16, 0.0)
