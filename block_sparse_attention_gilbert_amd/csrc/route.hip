@@ -30,21 +30,24 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t bits16) {
     return (double)__uint_as_float(bits16 << 16);
 }
 
-// Mean of the valid rows of each block; one wave per block, four blocks per
-// workgroup.  grid = (ceil(blocks / 4), heads).  Lane l owns one 16-byte
-// chunk (l % chunks) of rows l / chunks, + groups, ...; the partial sums of
-// the row groups are combined with butterfly shuffles (exact in float64, so
-// the combination order does not matter).
+// Mean of the valid rows of each block: one workgroup of 4 waves per block,
+// grid = (blocks, heads).  Wave w sums rows w, w + 4, ... of its quarter of
+// the block; lane l owns one 16-byte chunk (l % chunks) of rows l / chunks,
+// + groups, ...  The partial sums (of the row groups, then of the four
+// waves) are combined with butterfly shuffles and through LDS: sums of at
+// most 128 bf16 or fp32 values are exact in float64, so the combination
+// order does not matter.  Four waves per block keep enough loads in flight
+// when only a chunk's worth of blocks is pooled.
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads)
 pool_kernel(const void* __restrict__ x, int64_t head_stride, int d, int block,
             const int32_t* __restrict__ lens, int b_begin, int nb, double* __restrict__ out,
             int64_t out_head_blocks) {
     constexpr int CE = BF16 ? 8 : 4;  // elements per 16-byte chunk
+    constexpr int NW = kThreads / 64;
+    __shared__ double part[NW][128];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int bl = blockIdx.x * (kThreads / 64) + w;
-    if (bl >= nb) return;
-    const int b = b_begin + bl, h = blockIdx.y;
+    const int b = b_begin + blockIdx.x, h = blockIdx.y;
     int valid = lens ? lens[b] : block;
     valid = valid < 0 ? 0 : (valid > block ? block : valid);
     const int chunks = d / CE, groups = 64 / chunks;
@@ -54,7 +57,7 @@ pool_kernel(const void* __restrict__ x, int64_t head_stride, int d, int block,
     for (int e = 0; e < CE; ++e) acc[e] = 0.0;
     const int64_t base = h * head_stride + (int64_t)b * block * d + ch * CE;
 #pragma unroll 8
-    for (int row = g; row < valid; row += groups) {
+    for (int row = w * groups + g; row < valid; row += NW * groups) {
         if (BF16) {
             const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + base + (int64_t)row * d);
             const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
@@ -74,10 +77,16 @@ pool_kernel(const void* __restrict__ x, int64_t head_stride, int d, int block,
     for (int off = chunks; off < 64; off <<= 1)
 #pragma unroll
         for (int e = 0; e < CE; ++e) acc[e] += __shfl_xor(acc[e], off);
-    if (g == 0) {
-        double* o = out + (h * out_head_blocks + b) * d + ch * CE;
+    if (g == 0)
 #pragma unroll
-        for (int e = 0; e < CE; ++e) o[e] = valid > 0 ? acc[e] / (double)valid : 0.0;
+        for (int e = 0; e < CE; ++e) part[w][ch * CE + e] = acc[e];
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < d) {
+        double sum = 0.0;
+#pragma unroll
+        for (int u = 0; u < NW; ++u) sum += part[u][t];
+        out[(h * out_head_blocks + b) * d + t] = valid > 0 ? sum / (double)valid : 0.0;
     }
 }
 
@@ -112,73 +121,104 @@ overlap_flags_kernel(const float* __restrict__ overlap, int64_t ors, int n_cand,
 }
 
 // kappa[h][i][j] = (qbar_i . kbar_j) * scale + log1p(lambda * g_hat_ij).
-constexpr int kScoreJ = 64, kScoreRows = 40, kScoreRPT = kScoreRows / (kThreads / 64), kScoreDC = 32;
+// Selection keys with the float64 matrix cores.  A workgroup of 4 waves
+// takes 32 candidates (two 16-candidate tiles) and 48 query blocks (three
+// 16-row tiles) of one head; grid = (ceil(n_cand / 32), heads, ceil(nqb /
+// 48)).  The channels are split among the waves: wave w takes the 16-channel
+// steps w, w + 4, ..., so each wave loads all of its operands at once and
+// the workgroup needs one memory round trip.  In a step, lane l (g = l / 16,
+// r = l % 16) holds channels 4g .. 4g+3 of pooled key (candidate r of a
+// tile) and pooled query (row r of a tile) as 32 contiguous bytes and feeds
+// them to four v_mfma_f64_16x16x4f64, the i-th on channel 4g + i: over the
+// lane groups that is a 16 x 16 x 4 product over channels 4g + i, so the
+// four products cover the step (the same channel order on both operands).
+// The four waves' partial products are summed through LDS in wave order.
+constexpr int kScoreJ = 32, kScoreRows = 48, kScoreTiles = kScoreRows / 16, kScoreJT = kScoreJ / 16;
+constexpr int kScoreMaxSteps = 2;  // 16-channel steps per wave (d <= 128)
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 __device__ __attribute__((noinline)) double overlap_bias(double g, double lambda, double g_ref, double tau) {
     const double gh = g <= tau ? 0.0 : fmin(1.0, g / g_ref);
     return log1p(lambda * gh);
 }
 
-// Selection keys of one head for 64 candidates (one per lane) and up to 40
-// query blocks (10 per wave).  grid = (ceil(n_cand / 64), heads,
-// ceil(nqb / 40)).  The pooled vectors are staged through LDS 32 channels
-// at a time with coalesced 16-byte loads: keys row-major with one double of
-// padding per row (a lane reads its candidate's row; consecutive rows fall
-// in different banks), queries row-major (read as broadcasts).  Each lane
-// keeps 10 float64 dot products in registers: sequential fma over d.
+__device__ __forceinline__ f64x4 load_f64x4(const double* p) {
+    const double2 a = *reinterpret_cast<const double2*>(p);
+    const double2 b = *reinterpret_cast<const double2*>(p + 2);
+    return f64x4{a.x, a.y, b.x, b.y};
+}
+
 __global__ void __launch_bounds__(kThreads)
 score_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar, int64_t kbar_head_blocks,
              int nqb, int n_cand, int d, double scale, const float* __restrict__ overlap, int64_t ors,
              double lambda, double g_ref, double tau, const float* __restrict__ coverage, double eta_cov,
              double* __restrict__ keys) {
-    __shared__ __attribute__((aligned(16))) double ks[kScoreJ][kScoreDC + 1];
-    __shared__ __attribute__((aligned(16))) double qs[kScoreRows][kScoreDC];
+    __shared__ f64x4 part[kThreads / 64][kScoreJT * kScoreTiles][64];
     const int h = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int j0 = blockIdx.x * kScoreJ, j = j0 + lane;
-    const int r0 = blockIdx.z * kScoreRows;
-    const int nr = min(kScoreRows, nqb - r0);
-    double acc[kScoreRPT];
+    const int g = lane >> 4, r = lane & 15;
+    const int j0 = blockIdx.x * kScoreJ, r0 = blockIdx.z * kScoreRows;
+    const int steps = d / 16;
+    const f64x4 zero = {0.0, 0.0, 0.0, 0.0};
+    f64x4 kb[kScoreMaxSteps][kScoreJT], qa[kScoreMaxSteps][kScoreTiles];
 #pragma unroll
-    for (int m = 0; m < kScoreRPT; ++m) acc[m] = 0.0;
-    for (int dc = 0; dc < d; dc += kScoreDC) {
-        __syncthreads();
-        // 64 rows x 32 channels of pooled keys: 16 consecutive threads read
-        // one row's 256 bytes
+    for (int k = 0; k < kScoreMaxSteps; ++k) {
+        const int st = w + 4 * k;
 #pragma unroll
-        for (int x = t; x < kScoreJ * kScoreDC / 2; x += kThreads) {
-            const int c = x / (kScoreDC / 2), p2 = x % (kScoreDC / 2), jg = j0 + c;
-            double2 v = make_double2(0.0, 0.0);
-            if (jg < n_cand)
-                v = *reinterpret_cast<const double2*>(kbar + ((int64_t)h * kbar_head_blocks + jg) * d + dc + 2 * p2);
-            ks[c][2 * p2] = v.x;
-            ks[c][2 * p2 + 1] = v.y;
+        for (int v = 0; v < kScoreJT; ++v) {
+            const int jc = j0 + 16 * v + r;
+            kb[k][v] = zero;
+            if (st < steps && jc < n_cand)
+                kb[k][v] = load_f64x4(kbar + ((int64_t)h * kbar_head_blocks + jc) * d + 16 * st + 4 * g);
         }
-        for (int x = t; x < kScoreRows * kScoreDC / 2; x += kThreads) {
-            const int rr = x / (kScoreDC / 2), p2 = x % (kScoreDC / 2);
-            double2 v = make_double2(0.0, 0.0);
-            if (rr < nr) v = *reinterpret_cast<const double2*>(qbar + ((int64_t)h * nqb + r0 + rr) * d + dc + 2 * p2);
-            *reinterpret_cast<double2*>(&qs[rr][2 * p2]) = v;
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int dd = 0; dd < kScoreDC; ++dd) {
-            const double kv = ks[lane][dd];
 #pragma unroll
-            for (int m = 0; m < kScoreRPT; ++m) acc[m] = fma(qs[w + 4 * m][dd], kv, acc[m]);
+        for (int u = 0; u < kScoreTiles; ++u) {
+            const int row = r0 + 16 * u + r;
+            qa[k][u] = zero;
+            if (st < steps && row < nqb) qa[k][u] = load_f64x4(qbar + ((int64_t)h * nqb + row) * d + 16 * st + 4 * g);
         }
     }
-    if (j >= n_cand) return;
+    f64x4 acc[kScoreJT][kScoreTiles];
 #pragma unroll
-    for (int m = 0; m < kScoreRPT; ++m) {
-        const int rr = w + 4 * m;
-        if (rr >= nr) continue;
-        const int i = r0 + rr;
-        double kap = acc[m] * scale;
-        // the geometric bias applies to well-covered query blocks only (all
-        // of them when no coverage is given)
-        if (overlap && (!coverage || (double)coverage[i] >= eta_cov))
-            kap += overlap_bias((double)overlap[(int64_t)i * ors + j], lambda, g_ref, tau);
-        keys[((int64_t)h * nqb + i) * n_cand + j] = kap;
+    for (int v = 0; v < kScoreJT; ++v)
+#pragma unroll
+        for (int u = 0; u < kScoreTiles; ++u) acc[v][u] = zero;
+#pragma unroll
+    for (int k = 0; k < kScoreMaxSteps; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < kScoreJT; ++v)
+#pragma unroll
+                for (int u = 0; u < kScoreTiles; ++u)
+                    acc[v][u] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[k][u][i], kb[k][v][i], acc[v][u], 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < kScoreJT; ++v)
+#pragma unroll
+        for (int u = 0; u < kScoreTiles; ++u) part[w][v * kScoreTiles + u][lane] = acc[v][u];
+    __syncthreads();
+    // each wave finishes the tiles v * kScoreTiles + u == w (mod 4): the sum
+    // of the four waves' partials, in wave order.  Accumulator layout: lane
+    // l, element e holds row l / 16 + 4e of the row tile and candidate
+    // l % 16 of the candidate tile.
+    for (int tile = w; tile < kScoreJT * kScoreTiles; tile += kThreads / 64) {
+        const int v = tile / kScoreTiles, u = tile % kScoreTiles;
+        f64x4 sum = part[0][tile][lane];
+#pragma unroll
+        for (int x = 1; x < kThreads / 64; ++x) sum += part[x][tile][lane];
+        const int jc = j0 + 16 * v + r;
+        if (jc >= n_cand) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = r0 + 16 * u + g + 4 * e;
+            if (i >= nqb) continue;
+            double kap = sum[e] * scale;
+            // the geometric bias applies to well-covered query blocks only
+            // (all of them when no coverage is given)
+            if (overlap && (!coverage || (double)coverage[i] >= eta_cov))
+                kap += overlap_bias((double)overlap[(int64_t)i * ors + jc], lambda, g_ref, tau);
+            keys[((int64_t)h * nqb + i) * n_cand + jc] = kap;
+        }
     }
 }
 
@@ -342,19 +382,17 @@ __device__ __forceinline__ unsigned long long wave_sort64_desc(unsigned long lon
     return v;
 }
 
-// One wave per (head, query block) row.  Lane l holds the keys of
-// candidates j = l + 64 m (m < KPL).  A radix select over 8-bit digits
-// (most significant first, a 256-bin histogram per wave in LDS) finds the
-// K_eff-th largest key t and how many keys equal to t are needed; the row
-// then keeps every key > t and the lowest-indexed keys == t, which is the
-// total order (key descending, index ascending).  Selected indices are
-// written in ascending order with ballot prefix counts, followed by the
-// dense tail.  grid = ceil(rows / 4), 4 waves per workgroup, no barriers.
 // Threshold of the top-ke selection over the keys of one row held by a
 // wave (lane l: keys of candidates l + 64 m; 0 = not a candidate): the
 // selected set is every key > prefix plus the first `need` keys == prefix
-// in ascending candidate order.  `hist` is a 256-int and cand_key /
-// cand_idx 128-entry per-wave LDS scratch.
+// in ascending candidate order, which is the total order (key descending,
+// index ascending).  A fast path (below) handles most rows with ke <= 64
+// (a wave bitonic network over the lane maxima, then over the at most 128
+// keys at or above the ke-th largest of them); otherwise a
+// radix select over 8-bit digits (most significant first, a 256-bin
+// histogram per wave in LDS) finds the ke-th largest key and how many keys
+// equal to it are needed.  `hist` is a 256-int and cand_key / cand_idx
+// 128-entry per-wave LDS scratch.
 template <int KPL>
 __device__ __forceinline__ void select_threshold(const unsigned long long (&key)[KPL], int ke, int lane,
                                                  int* hist, unsigned long long* cand_key, int* cand_idx,
@@ -459,12 +497,16 @@ __device__ __forceinline__ void select_threshold(const unsigned long long (&key)
     }
 }
 
+// One wave per (head, query block) row: the threshold of its top-K_eff,
+// then the selected indices in ascending order (ballot prefix counts),
+// followed by the dense tail.  grid = ceil(rows / 4), 4 waves per
+// workgroup, no barriers.
 template <int KPL>
 __global__ void __launch_bounds__(kThreads)
 topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int nkb, int block,
-            const int32_t* __restrict__ q_len, const int32_t* __restrict__ kv_len,
-            const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ keff,
-            int32_t* __restrict__ col_idx) {
+            const int32_t* __restrict__ q_len, const int32_t* __restrict__ kv_len, int k_fused,
+            int32_t* __restrict__ row_ptr, const int32_t* __restrict__ keff, int32_t* __restrict__ col_idx,
+            int32_t* __restrict__ zero_counts) {
     __shared__ int hist_all[kThreads / 64][256];
     __shared__ unsigned long long cand_key[kThreads / 64][128];
     __shared__ int cand_idx[kThreads / 64][128];
@@ -473,23 +515,53 @@ topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int 
     if (r >= rows) return;
     const int i = r % nqb;
     const int vq = q_len ? q_len[i] : block;
+    const unsigned long long lt_mask = (1ull << lane) - 1ull;
+    bool vis[KPL];
+    int n_vis = 0;
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+        const int j = lane + 64 * m;
+        vis[m] = j < n_cand && (kv_len ? kv_len[j] : block) > 0;
+        n_vis += __popcll(__ballot(vis[m]));
+    }
+    int start, ke;
+    if (k_fused >= 0) {
+        // fixed budget: every non-empty row has min(K, visible candidates)
+        // + the visible tail blocks, so a row's start is a count of the
+        // non-empty query blocks before it
+        int n_tail = 0;
+        for (int j0 = n_cand; j0 < nkb; j0 += 64) {
+            const int jb = j0 + lane;
+            n_tail += __popcll(__ballot(jb < nkb && (kv_len ? kv_len[jb] : block) > 0));
+        }
+        int before = 0, nonempty = 0;
+        for (int i0 = 0; i0 < nqb; i0 += 64) {
+            const int ib = i0 + lane;
+            const bool ne = ib < nqb && (q_len ? q_len[ib] : block) > 0;
+            nonempty += __popcll(__ballot(ne));
+            before += __popcll(__ballot(ne && ib < i));
+        }
+        const int ke0 = k_fused < n_vis ? k_fused : n_vis;
+        const int len = ke0 + n_tail;
+        start = ((r / nqb) * nonempty + before) * len;
+        ke = vq > 0 ? ke0 : 0;
+        if (lane == 0) {
+            row_ptr[r] = start;
+            if (r == rows - 1) row_ptr[rows] = start + (vq > 0 ? len : 0);
+            if (r == 0 && zero_counts) zero_counts[0] = zero_counts[1] = 0;
+        }
+    } else {
+        if (vq <= 0) return;
+        start = row_ptr[r];
+        ke = keff[r];
+    }
     if (vq <= 0) return;
     int* hist = hist_all[w];
-    const int start = row_ptr[r];
-    const int ke = keff[r];
-    const unsigned long long lt_mask = (1ull << lane) - 1ull;
     const double* row = keys + (int64_t)r * n_cand;
 
     unsigned long long key[KPL];
 #pragma unroll
-    for (int m = 0; m < KPL; ++m) {
-        const int j = lane + 64 * m;
-        key[m] = 0;
-        if (j < n_cand) {
-            const int v = kv_len ? kv_len[j] : block;
-            if (v > 0) key[m] = order_key(row[j]);
-        }
-    }
+    for (int m = 0; m < KPL; ++m) key[m] = vis[m] ? order_key(row[lane + 64 * m]) : 0ull;
 
     unsigned long long prefix;
     int need;
@@ -808,7 +880,7 @@ void launch_pool_score(const bsa_route_args* a, const RouteLayout& lay, void* ws
 
     // pooled queries
     {
-        dim3 grid((a->nqb + 3) / 4, a->heads);
+        dim3 grid(a->nqb, a->heads);
         if (bf16)
             hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kThreads), 0, stream, a->q, a->q_head_stride, a->d,
                                a->block, a->q_block_len, 0, a->nqb, qbar, (int64_t)a->nqb);
@@ -820,7 +892,7 @@ void launch_pool_score(const bsa_route_args* a, const RouteLayout& lay, void* ws
     const int kb0 = a->kpool ? a->kpool_valid_blocks : 0;
     if (n_cand > kb0) {
         const int nb = n_cand - kb0;
-        dim3 grid((nb + 3) / 4, a->heads);
+        dim3 grid(nb, a->heads);
         if (bf16)
             hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kThreads), 0, stream, a->k, a->k_head_stride, a->d,
                                a->block, a->kv_block_len, kb0, nb, kbar, kbar_head_blocks);
@@ -852,16 +924,22 @@ hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* w
     const bool want_flags = a->overlap && a->fallback_counts && n_cand > 0;
     // 1-4. pooled queries and keys, overlap flags, selection keys
     launch_pool_score(a, lay, ws, nullptr, 0.0, want_flags, stream);
-    // 5. list lengths and row pointers
-    hipLaunchKernelGGL(rowptr_kernel, dim3(1), dim3(1024), 0, stream, a->heads, a->nqb, a->nkb, n_cand, a->block,
-                       a->q_block_len, a->kv_block_len, a->k_per_row ? 0 : a->k_fixed, a->k_per_row,
-                       a->k_max, want_flags ? flags : nullptr, a->row_ptr, keff, a->fallback_counts);
+    // 5. list lengths and row pointers: with one fixed budget (and no
+    // overlap rows to count) the selection kernel derives them itself and
+    // writes the (zero) fallback counts
+    const bool fused = !a->k_per_row && !want_flags && a->nqb <= 4096;
+    if (!fused)
+        hipLaunchKernelGGL(rowptr_kernel, dim3(1), dim3(1024), 0, stream, a->heads, a->nqb, a->nkb, n_cand, a->block,
+                           a->q_block_len, a->kv_block_len, a->k_per_row ? 0 : a->k_fixed, a->k_per_row,
+                           a->k_max, want_flags ? flags : nullptr, a->row_ptr, keff, a->fallback_counts);
     // 6. selection: one wave per row
     const int rows = a->heads * a->nqb;
+    const int k_fused = fused ? a->k_fixed : -1;
     const dim3 grid((rows + kThreads / 64 - 1) / (kThreads / 64));
 #define BSA_TOPK(KPL)                                                                                       \
     hipLaunchKernelGGL(topk_kernel<KPL>, grid, dim3(kThreads), 0, stream, keys, rows, a->nqb, n_cand, a->nkb, \
-                       a->block, a->q_block_len, a->kv_block_len, a->row_ptr, keff, a->col_idx)
+                       a->block, a->q_block_len, a->kv_block_len, k_fused, a->row_ptr, keff, a->col_idx,    \
+                       fused ? a->fallback_counts : nullptr)
     if (n_cand <= 64 * 8)
         BSA_TOPK(8);
     else if (n_cand <= 64 * 16)
