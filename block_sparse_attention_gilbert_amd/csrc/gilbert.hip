@@ -54,32 +54,31 @@ __global__ void gilbert_index_kernel(int T, int H, int W, int32_t* __restrict__ 
     if (inv) inv[r] = (int32_t)i;
 }
 
-// One thread moves one 16-byte chunk of one (row, head).  Threads walk the
-// chunks of a row fastest, then heads, then rows, so raster reads cover a
-// token's heads contiguously and Gilbert writes cover whole rows.
+// One thread moves one 16-byte chunk of one (row, head).  grid.y walks the
+// rows (looping when there are more than the grid holds), grid.x the
+// (head, chunk) pairs of a row, chunks fastest: raster reads cover a
+// token's heads contiguously and Gilbert writes cover whole rows.  The
+// chunk count per row is a power of two, so no division is needed.
 template <bool INVERSE>
-__global__ void gilbert_perm_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                    const int32_t* __restrict__ perm, int L, int heads,
-                                    int chunks_per_row, int64_t rows_total,
-                                    int64_t raster_token_stride_c, int64_t gilbert_head_stride_c) {
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = rows_total * heads * chunks_per_row;
-    if (tid >= total) return;
-    const int ch = (int)(tid % chunks_per_row);
-    const int64_t rest = tid / chunks_per_row;
-    const int h = (int)(rest % heads);
-    const int64_t i = rest / heads;
-    const int64_t g = h * gilbert_head_stride_c + i * chunks_per_row + ch;
-    if (!INVERSE) {
-        if (i < L) {
-            const int64_t r = (int64_t)perm[i] * raster_token_stride_c + (int64_t)h * chunks_per_row + ch;
-            dst[g] = src[r];
-        } else {
-            dst[g] = make_uint4(0u, 0u, 0u, 0u);
-        }
-    } else {
-        if (i < L) {
-            const int64_t r = (int64_t)perm[i] * raster_token_stride_c + (int64_t)h * chunks_per_row + ch;
+__global__ void __launch_bounds__(256)
+gilbert_perm_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, const int32_t* __restrict__ perm, int L,
+                    int heads, int log2_chunks, int64_t rows_total, int64_t raster_token_stride_c,
+                    int64_t gilbert_head_stride_c) {
+    const int hc = blockIdx.x * 256 + threadIdx.x;
+    const int chunks = 1 << log2_chunks;
+    if (hc >= heads * chunks) return;
+    const int ch = hc & (chunks - 1), h = hc >> log2_chunks;
+    for (int64_t i = blockIdx.y; i < rows_total; i += gridDim.y) {
+        const int64_t g = h * gilbert_head_stride_c + i * chunks + ch;
+        if (!INVERSE) {
+            if (i < L) {
+                const int64_t r = (int64_t)perm[i] * raster_token_stride_c + (int64_t)h * chunks + ch;
+                dst[g] = src[r];
+            } else {
+                dst[g] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        } else if (i < L) {
+            const int64_t r = (int64_t)perm[i] * raster_token_stride_c + (int64_t)h * chunks + ch;
             dst[r] = src[g];
         }
     }
@@ -120,24 +119,24 @@ __global__ void tile_index_kernel(int T, int H, int W, int tt, int th, int tw, i
 // token row_cell[i]; rows with a negative entry are padding (written as
 // zeros forward, skipped inverse).  Same thread walk as gilbert_perm_kernel.
 template <bool INVERSE>
-__global__ void tile_perm_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                 const int32_t* __restrict__ row_cell, int L, int heads, int chunks_per_row,
-                                 int64_t rows_total, int64_t raster_token_stride_c, int64_t tiled_head_stride_c) {
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = rows_total * heads * chunks_per_row;
-    if (tid >= total) return;
-    const int ch = (int)(tid % chunks_per_row);
-    const int64_t rest = tid / chunks_per_row;
-    const int h = (int)(rest % heads);
-    const int64_t i = rest / heads;
-    const int64_t g = h * tiled_head_stride_c + i * chunks_per_row + ch;
-    const int cell = row_cell[i];
-    const bool valid = cell >= 0 && cell < L;
-    const int64_t r = (int64_t)(valid ? cell : 0) * raster_token_stride_c + (int64_t)h * chunks_per_row + ch;
-    if (!INVERSE) {
-        dst[g] = valid ? src[r] : make_uint4(0u, 0u, 0u, 0u);
-    } else if (valid) {
-        dst[r] = src[g];
+__global__ void __launch_bounds__(256)
+tile_perm_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, const int32_t* __restrict__ row_cell, int L,
+                 int heads, int log2_chunks, int64_t rows_total, int64_t raster_token_stride_c,
+                 int64_t tiled_head_stride_c) {
+    const int hc = blockIdx.x * 256 + threadIdx.x;
+    const int chunks = 1 << log2_chunks;
+    if (hc >= heads * chunks) return;
+    const int ch = hc & (chunks - 1), h = hc >> log2_chunks;
+    for (int64_t i = blockIdx.y; i < rows_total; i += gridDim.y) {
+        const int64_t g = h * tiled_head_stride_c + i * chunks + ch;
+        const int cell = row_cell[i];
+        const bool valid = cell >= 0 && cell < L;
+        const int64_t r = (int64_t)(valid ? cell : 0) * raster_token_stride_c + (int64_t)h * chunks + ch;
+        if (!INVERSE) {
+            dst[g] = valid ? src[r] : make_uint4(0u, 0u, 0u, 0u);
+        } else if (valid) {
+            dst[r] = src[g];
+        }
     }
 }
 
@@ -238,20 +237,17 @@ hipError_t launch_gilbert_perm(const void* src, void* dst, const int32_t* perm, 
     const int eb = dtype == BSA_BF16 ? 2 : 4;
     const int chunk_elems = 16 / eb;
     const int chunks_per_row = d / chunk_elems;
+    const int log2c = __builtin_ctz((unsigned)chunks_per_row);
     const int64_t rows_total = inverse ? (int64_t)L : ((int64_t)L + block - 1) / block * block;
-    const int64_t total = rows_total * heads * chunks_per_row;
-    const int threads = 256;
-    const unsigned blocks = (unsigned)((total + threads - 1) / threads);
+    const dim3 grid((unsigned)((heads * chunks_per_row + 255) / 256), (unsigned)(rows_total < 65535 ? rows_total : 65535));
     const int64_t rts_c = raster_token_stride / chunk_elems;
     const int64_t ghs_c = gilbert_head_stride / chunk_elems;
     if (inverse)
-        hipLaunchKernelGGL(gilbert_perm_kernel<true>, dim3(blocks), dim3(threads), 0, stream,
-                           static_cast<const uint4*>(src), static_cast<uint4*>(dst), perm, L, heads,
-                           chunks_per_row, rows_total, rts_c, ghs_c);
+        hipLaunchKernelGGL(gilbert_perm_kernel<true>, grid, dim3(256), 0, stream, static_cast<const uint4*>(src),
+                           static_cast<uint4*>(dst), perm, L, heads, log2c, rows_total, rts_c, ghs_c);
     else
-        hipLaunchKernelGGL(gilbert_perm_kernel<false>, dim3(blocks), dim3(threads), 0, stream,
-                           static_cast<const uint4*>(src), static_cast<uint4*>(dst), perm, L, heads,
-                           chunks_per_row, rows_total, rts_c, ghs_c);
+        hipLaunchKernelGGL(gilbert_perm_kernel<false>, grid, dim3(256), 0, stream, static_cast<const uint4*>(src),
+                           static_cast<uint4*>(dst), perm, L, heads, log2c, rows_total, rts_c, ghs_c);
     return hipGetLastError();
 }
 
@@ -288,16 +284,16 @@ hipError_t launch_tile_perm(const void* src, void* dst, const int32_t* row_cell,
     const int eb = dtype == BSA_BF16 ? 2 : 4;
     const int chunk_elems = 16 / eb;
     const int chunks_per_row = d / chunk_elems;
-    const int64_t total = (int64_t)n_rows * heads * chunks_per_row;
-    const unsigned blocks = (unsigned)((total + 255) / 256);
+    const int log2c = __builtin_ctz((unsigned)chunks_per_row);
+    const dim3 grid((unsigned)((heads * chunks_per_row + 255) / 256), (unsigned)(n_rows < 65535 ? n_rows : 65535));
     const int64_t rts_c = raster_token_stride / chunk_elems;
     const int64_t ths_c = tiled_head_stride / chunk_elems;
     if (inverse)
-        hipLaunchKernelGGL(tile_perm_kernel<true>, dim3(blocks), dim3(256), 0, stream, static_cast<const uint4*>(src),
-                           static_cast<uint4*>(dst), row_cell, L, heads, chunks_per_row, (int64_t)n_rows, rts_c, ths_c);
+        hipLaunchKernelGGL(tile_perm_kernel<true>, grid, dim3(256), 0, stream, static_cast<const uint4*>(src),
+                           static_cast<uint4*>(dst), row_cell, L, heads, log2c, (int64_t)n_rows, rts_c, ths_c);
     else
-        hipLaunchKernelGGL(tile_perm_kernel<false>, dim3(blocks), dim3(256), 0, stream, static_cast<const uint4*>(src),
-                           static_cast<uint4*>(dst), row_cell, L, heads, chunks_per_row, (int64_t)n_rows, rts_c, ths_c);
+        hipLaunchKernelGGL(tile_perm_kernel<false>, grid, dim3(256), 0, stream, static_cast<const uint4*>(src),
+                           static_cast<uint4*>(dst), row_cell, L, heads, log2c, (int64_t)n_rows, rts_c, ths_c);
     return hipGetLastError();
 }
 

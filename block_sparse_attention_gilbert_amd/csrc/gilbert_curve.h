@@ -30,18 +30,25 @@ __host__ __device__ inline V3 even_half(V3 v) {
 
 // Cell at curve position idx of the T x H x W grid.
 __host__ __device__ inline V3 gilbert_cell(int T, int H, int W, int64_t idx) {
-    // axes in tie order w, h, t, stably sorted by decreasing length
-    V3 ax[3] = {{0, 0, W}, {0, H, 0}, {T, 0, 0}};
-    for (int x = 1; x < 3; ++x) {
-        V3 key = ax[x];
-        int y = x - 1;
-        while (y >= 0 && vlen(ax[y]) < vlen(key)) {
-            ax[y + 1] = ax[y];
-            --y;
-        }
-        ax[y + 1] = key;
+    // axes in tie order w, h, t, stably sorted by decreasing length (a
+    // three-element insertion sort written out, so nothing is indexed)
+    V3 a = {0, 0, W}, b = {0, H, 0}, c = {T, 0, 0};
+    if (vlen(b) > vlen(a)) {
+        const V3 x = a;
+        a = b;
+        b = x;
     }
-    V3 p = {0, 0, 0}, a = ax[0], b = ax[1], c = ax[2];
+    if (vlen(c) > vlen(b)) {
+        const V3 x = b;
+        b = c;
+        c = x;
+        if (vlen(b) > vlen(a)) {
+            const V3 y = a;
+            a = b;
+            b = y;
+        }
+    }
+    V3 p = {0, 0, 0};
     int64_t i = idx;
 
     // three-dimensional levels
