@@ -100,3 +100,71 @@ def test_c5_ragged_full():
         err = np.abs(o_gpu - o_ref[rows])
         print("C5 head", h, "max", err.max(), "mean", err.mean(), flush=True)
         assert err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS
+
+
+def test_c4_chunk48_materialised_routes_sampled_heads():
+    """The materialised route at chunk 48 in the pipeline's launch
+    configuration (window rebuilt on the GPU, previous chunk reserved,
+    K_cov 80, K_unc 150, mass 0.9) on seeded coverage and overlap: every
+    route of two heads bit-exact, attention on sampled rows."""
+    dev = need_gpu()
+    from block_sparse_attention_gilbert_amd.pipeline import RoutedAttention
+    from oracle import materialize as om
+    heads = [0, 39]
+    w = workloads.c4(c=48, heads=heads)
+    cov, ov = workloads.route_inputs(w.q_len, w.nkb)
+    ra = RoutedAttention((3, 30, 52), w.heads, w.d, w.bs, 48, device=dev, k_store=w.k.contiguous().to(dev),
+                         v_store=w.v.contiguous().to(dev))
+    ra.q_blk.copy_(w.q.to(dev))
+    mat = dict(coverage=torch.from_numpy(cov).to(dev), k_cov=80, k_unc=150, mass=0.9)
+    r = ra.route_and_attend(47, overlap=torch.from_numpy(ov).to(dev), materialize=mat)
+    torch.cuda.synchronize()
+    lists = csr_lists(r["row_ptr"], r["col_idx"], w.heads, w.nqb)
+    win = om.block_window(gilbert_order(3, 30, 52)[0], (3, 30, 52), 128, 47)
+    rng = np.random.default_rng(7)
+    for hi, h in enumerate(heads):
+        q, k, v = f64(w.q[hi]), f64(w.k[hi]), f64(w.v[hi])
+        ref = om.materialize_head(q, k, w.q_len, w.k_len, w.bs, scale=w.scale, coverage=cov, k_cov=80, k_unc=150,
+                                  mass=0.9, prev_blocks=(46 * 37, 47 * 37), windows=win, overlap=ov, lam=w.lam,
+                                  tau=w.tau, g_ref=w.g_ref)
+        assert_lists_equal(lists[hi], ref["lists"], "materialised c=48 head %d" % h)
+        rows = _sample_rows(rng, w.q_len, w.bs, n=24)
+        o_ref, _ = oatt.block_sparse_head(q, k, v, w.q_len, w.k_len, w.bs, ref["lists"], w.scale, rows=rows)
+        err = np.abs(f64(ra.o_blk[hi])[rows] - o_ref[rows])
+        print("materialised head", h, "max", err.max(), "mean", err.mean(), flush=True)
+        assert err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS
+
+
+def test_c4_chunk48_fixed_tiles_sampled_heads():
+    """The 1 x 8 x 16 tile layout at chunk 48 (2304 candidate blocks, the
+    widest top-K path) in the bench's configuration: routes of two heads
+    bit-exact, attention on sampled rows, the slot rewritten bit for bit."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    from block_sparse_attention_gilbert_amd.pipeline import RoutedAttention
+    from oracle import tiles as ot
+    tile = (1, 8, 16)
+    heads = [5, 33]
+    _, bl, _ = ot.tile_layout((3, 30, 52), tile)
+    w = workloads.c4(c=48, heads=heads, chunk_lens=bl)
+    ra = RoutedAttention((3, 30, 52), w.heads, w.d, w.bs, 48, device=dev, k_store=w.k.contiguous().to(dev),
+                         v_store=w.v.contiguous().to(dev), tile=tile)
+    assert np.array_equal(ra.block_len.cpu().numpy(), bl)
+    ks, vs = ra.slot(47)
+    mk = lambda x: ra.to_raster(x, torch.empty((4680, w.heads, w.d), dtype=w.dtype, device=dev))
+    q_r, k_r, v_r = mk(w.q.to(dev)), mk(ks), mk(vs)
+    before = ks.clone()
+    _, r = ra.step(q_r, k_r, v_r, 47)
+    torch.cuda.synchronize()
+    assert torch.equal(before, ra.slot(47)[0])
+    lists = csr_lists(r["row_ptr"], r["col_idx"], w.heads, w.nqb)
+    rng = np.random.default_rng(9)
+    for hi, h in enumerate(heads):
+        q, k, v = f64(w.q[hi]), f64(w.k[hi]), f64(w.v[hi])
+        ref = oroute.route_head(q, k, w.q_len, w.k_len, w.bs, scale=w.scale, k_per_row=np.full(w.nqb, 50))
+        assert_lists_equal(lists[hi], ref["lists"], "tiles c=48 head %d" % h)
+        rows = _sample_rows(rng, w.q_len, w.bs, n=24)
+        o_ref, _ = oatt.block_sparse_head(q, k, v, w.q_len, w.k_len, w.bs, ref["lists"], w.scale, rows=rows)
+        err = np.abs(f64(ra.o_blk[hi])[rows] - o_ref[rows])
+        print("tiles head", h, "max", err.max(), "mean", err.mean(), flush=True)
+        assert err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS
