@@ -2,7 +2,7 @@
 48 on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk C]
-                    [--no-cpu-baseline] [--dense] [--tiles] [--sweep FILE] [--rollout FILE]
+                    [--no-cpu-baseline] [--no-dense] [--tiles] [--sweep FILE] [--rollout FILE]
 
 Workload: the 14B-like growing-context layer -- 40 heads, head dim 128, a
 3 x 30 x 52 latent chunk (4680 tokens, 37 blocks of 128), a KV history of C
@@ -20,6 +20,11 @@ permutation of O.  The step time with every history block re-pooled is
 reported beside it (``step_full_k_pool_ms``), and so is the same step
 replayed from a HIP graph (``step_hip_graph_ms``: identical kernels, no
 launch gaps; every replay is checked bitwise against the eager step), and
+each stage timed alone with its algorithmic bytes and GB/s, and the
+attention launch with L2 and MALL flushed before each call
+(``breakdown``), the bf16 matrix rate a register-only MFMA probe gets at
+the current clock (``mfma_probe``), dense attention through the same kernel
+(``dense``), the shader/memory clocks at start and end (``clocks``), and
 the step with the materialised route instead of the top-K
 (``materialized``: coverage-gated budgets, previous-chunk reservation,
 cumulative-mass prefix and the local window), its overlap and coverage
@@ -155,6 +160,122 @@ def step_graph_ms(st, reps: int):
     torch.cuda.synchronize()
     assert torch.equal(ra.o_raster, o_eager), "graph replay differs from the eager step"
     return e0.elapsed_time(e1) / reps
+
+
+def _time_ms(fn, reps: int, warm: int = 10, between=None):
+    """Median ms of ``fn`` over ``reps`` back-to-back calls, each bracketed
+    by events on the current stream (no host synchronisation in between, so
+    the GPU does not idle and drop its clock); ``between`` runs, untimed,
+    before each call."""
+    import statistics
+
+    import torch
+    for _ in range(warm):
+        if between:
+            between()
+        fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        if between:
+            between()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return statistics.median(a.elapsed_time(b) for a, b in evs)
+
+
+def breakdown(st, reps: int):
+    """Each stage of the step alone (median of ``reps`` calls), with its
+    algorithmic bytes and the GB/s that gives: the Gilbert index, the three
+    forward permutations (Q, K, V), the router with the pooled-key cache,
+    the attention launch, the inverse permutation of O."""
+    import torch
+    w, ra = st["w"], st["ra"]
+    cur = st["cur"]
+    ks, vs = ra.slot(cur)
+    L, heads, d = 4680, w.heads, w.d
+    raster = L * heads * d * 2
+    blocked = ra.rows_c * heads * d * 2
+
+    def fwd():
+        ra.to_blocks(st["q_raster"], ra.q_blk)
+        ra.to_blocks(st["k_raster"], ks)
+        ra.to_blocks(st["v_raster"], vs)
+
+    def route():
+        ra.invalidate_kpool(cur * ra.nbc)      # as in the step: the new chunk's keys are pooled again
+        return ra.route(cur)
+
+    nkb = w.nkb
+    k_hist, v_hist = ra.k_store[:, : nkb * w.bs], ra.v_store[:, : nkb * w.bs]
+    r = route()
+    torch.cuda.synchronize()
+    wc = work_counts(r["row_ptr"], r["col_idx"], w.q_len, w.k_len, w.heads, w.nqb, w.bs, w.d)
+    n_cand = nkb
+    route_bytes = (2 * raster                              # Q and the new chunk's K, read once
+                   + heads * n_cand * d * 8                # pooled keys (float64) read
+                   + 2 * heads * w.nqb * n_cand * 8        # selection keys written and read
+                   + 4 * (heads * w.nqb + 1 + int(r["row_ptr"][-1])))
+    stages = {
+        "gilbert_index": (lambda: ra._index(), 4 * 2 * L),
+        "forward_permutes": (fwd, 3 * (raster + blocked)),
+        "route": (route, route_bytes),
+        "attention": (lambda: ra._attend(r, nkb, k_hist, v_hist, None, None), wc["alg_bytes"]),
+        "inverse_permute": (lambda: ra.to_raster(ra.o_blk, ra.o_raster), raster + blocked),
+    }
+    out = {}
+    for name, (fn, nbytes) in stages.items():
+        ms = _time_ms(fn, reps)
+        out[name] = {"ms": round(ms, 4), "alg_bytes": int(nbytes), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    # the same attention launch with L2 and the 256 MB MALL flushed before
+    # each call (a 512 MB write, untimed, right before it)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=ra.device)
+    ms = _time_ms(lambda: ra._attend(r, nkb, k_hist, v_hist, None, None), reps, between=lambda: scrub.fill_(1))
+    del scrub
+    out["attention_cold_ms"] = round(ms, 4)
+    return out
+
+
+def mfma_probe(reps: int = 10):
+    """The bf16 matrix rate this GPU delivers right now: register-only
+    v_mfma_f32_32x32x16_bf16 chains on every CU.  ``implied_sclk_mhz`` is
+    the clock at which that rate would be the full matrix rate (256 CUs x 4
+    SIMDs x 1024 FLOP per cycle)."""
+    import torch
+
+    import block_sparse_attention_gilbert_amd as bsa
+    best = None
+    for wgs in (512, 768, 1024):          # 2, 3 or 4 workgroups per CU
+        iters = 256
+        sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+        fn = lambda: bsa._check(bsa._lib.bsa_diag_mfma_bf16(wgs, iters, bsa._ptr(sink), bsa._stream(None)))
+        ms = _time_ms(fn, reps)
+        tf = wgs * 4 * 4 * iters * 32768 / (ms * 1e-3) / 1e12
+        if best is None or tf > best["tflops"]:
+            best = {"tflops": round(tf, 1), "ms": round(ms, 4), "workgroups_per_cu": wgs // 256}
+    best["what"] = "register-only bf16 MFMA chains (4 per wave), best of 2-4 workgroups per CU"
+    best["implied_sclk_mhz"] = round(best["tflops"] * 1e12 / (256 * 4 * 1024) / 1e6)
+    return best
+
+
+def clocks():
+    """Current shader and memory clocks from rocm-smi (None if unavailable)."""
+    import re
+    import subprocess
+    try:
+        txt = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
+    except Exception:  # pragma: no cover
+        return None
+    out = {}
+    for key in ("sclk", "mclk", "fclk"):
+        m = re.search(r"%s clock level: \d+: \((\d+)Mhz\)" % key, txt)
+        if m:
+            out[key + "_mhz"] = int(m.group(1))
+    return out or None
 
 
 def tiles(chunk: int, reps: int, device: str, tile=(1, 8, 16)):
@@ -324,19 +445,26 @@ def cpu_baseline(st, n_heads=2):
         cores = len(os.sched_getaffinity(0))
     w = st["w"]
     flop = 0
+    t_route = t_attn = 0.0
     t0 = time.perf_counter()
     for h in range(n_heads):
         q = bf16_bits_to_f64(w.q[h].contiguous().view(__import__("torch").int16).numpy())
         k = bf16_bits_to_f64(w.k[h].contiguous().view(__import__("torch").int16).numpy())
         v = bf16_bits_to_f64(w.v[h].contiguous().view(__import__("torch").int16).numpy())
+        ta = time.perf_counter()
         r = oroute.route_head(q, k, w.q_len, w.k_len, w.bs, scale=w.scale, k_per_row=w.k_per_row[:w.nqb])
+        tb = time.perf_counter()
         oatt.block_sparse_head(q, k, v, w.q_len, w.k_len, w.bs, r["lists"], w.scale)
+        tc = time.perf_counter()
+        t_route += tb - ta
+        t_attn += tc - tb
         for i, lst in enumerate(r["lists"]):
             flop += 4 * w.d * int(w.q_len[i]) * int(np.asarray(w.k_len)[lst].sum())
     dt = time.perf_counter() - t0
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": "float64 oracle route + attention for %d of %d heads at chunk %d (%.1f s, %.3g FLOP)"
-                      % (n_heads, w.heads, w.nkb // 37, dt, flop)}
+                      % (n_heads, w.heads, w.nkb // 37, dt, flop),
+            "route_s": round(t_route, 2), "attention_s": round(t_attn, 2)}
 
 
 def read_traffic(per_launch_bytes):
@@ -433,7 +561,7 @@ def main():
     ap.add_argument("--chunk", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=40)
-    ap.add_argument("--dense", action="store_true", help="also time dense attention at the same chunk")
+    ap.add_argument("--no-dense", action="store_true", help="skip timing dense attention at the same chunk")
     ap.add_argument("--tiles", action="store_true",
                     help="also time the step with fixed 1 x 8 x 16 tile blocks at the same chunk")
     ap.add_argument("--no-materialized", action="store_true",
@@ -462,6 +590,7 @@ def main():
         return
 
     dev = "cuda:0"
+    clocks_start = clocks()
     t_setup = time.perf_counter()
     st = setup_c4(args.chunk, device=dev)
     w, ra = st["w"], st["ra"]
@@ -551,9 +680,10 @@ def main():
                      "traffic": traffic, "kernel": "attn_bf16_kernel<128,128,sparse>",
                      "alg_bytes_per_launch": wc["alg_bytes"]},
     }
-    if args.dense:
+    if not args.no_dense:
         ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-        ra.dense(st["cur"])
+        for _ in range(2):
+            ra.dense(st["cur"])
         torch.cuda.synchronize()
         ev[0].record()
         n_dense = max(1, min(args.steps, 5))
@@ -565,6 +695,13 @@ def main():
         dflop = 4 * w.d * int(w.q_len.sum()) * int(w.k_len.sum()) * w.heads
         out["dense"] = {"ms_per_call": round(dms, 3), "effective_tflops": round(dflop / (dms * 1e-3) / 1e12, 2),
                         "speedup_sparse_vs_dense": round(dms / attn_ms, 2)}
+    # stages alone and the attention with cold caches, then the matrix-rate
+    # probe (after dense: the scrub buffer's allocation slows the next steps)
+    out["breakdown"] = breakdown(st, max(5, min(args.steps, 20)))
+    mp = mfma_probe()
+    out["mfma_probe"] = dict(mp, attn_frac_of_probe=round(attn_tflops / mp["tflops"], 4),
+                             dense_frac_of_probe=round(out["dense"]["effective_tflops"] / mp["tflops"], 4)
+                             if "dense" in out else None)
     if not args.no_materialized:
         geo, ov, cov = geometry(st, max(1, min(args.steps, 10)))
         out["geometry"] = geo
@@ -575,6 +712,7 @@ def main():
         sweep(st, args.sweep)
     if args.rollout:
         rollout(st, args.rollout)
+    out["clocks"] = {"start": clocks_start, "end": clocks()}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(st, args.cpu_heads)
     print(json.dumps(out), flush=True)

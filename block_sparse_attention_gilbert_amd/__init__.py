@@ -102,6 +102,8 @@ _lib.bsa_slab_coverage.restype = _i
 _lib.bsa_slab_coverage.argtypes = [_p, _i, _p, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p, ctypes.c_size_t, _p]
 _lib.bsa_slab_coverage_workspace_size.restype = ctypes.c_size_t
 _lib.bsa_slab_coverage_workspace_size.argtypes = [_i, _i, _i]
+_lib.bsa_diag_mfma_bf16.restype = _i
+_lib.bsa_diag_mfma_bf16.argtypes = [_i, _i, _p, _p]
 _lib.bsa_route_workspace_size.restype = ctypes.c_size_t
 _lib.bsa_route_workspace_size.argtypes = [ctypes.POINTER(RouteArgs)]
 _lib.bsa_route_topk.restype = _i
@@ -116,7 +118,8 @@ EXPORTED = ("bsa_version", "bsa_strerror", "bsa_last_error_detail", "bsa_gilbert
             "bsa_gilbert_perm", "bsa_gilbert_block_window", "bsa_gilbert_tile_index", "bsa_tile_perm",
             "bsa_tile_block_window", "bsa_route_workspace_size", "bsa_route_topk",
             "bsa_route_materialize_workspace_size", "bsa_route_materialize", "bsa_slab_overlap",
-            "bsa_slab_coverage", "bsa_slab_coverage_workspace_size", "bsa_block_sparse_attn", "bsa_dense_attn")
+            "bsa_slab_coverage", "bsa_slab_coverage_workspace_size", "bsa_block_sparse_attn", "bsa_dense_attn",
+            "bsa_diag_mfma_bf16")
 
 
 class BsaError(RuntimeError):

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsa.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["gilbert.hip", "route.hip", "attn.hip", "geometry.hip", "api.hip"]
+HIP_SOURCES = ["gilbert.hip", "route.hip", "attn.hip", "geometry.hip", "diag.hip", "api.hip"]
 HOST_SOURCES = ["validate.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC]

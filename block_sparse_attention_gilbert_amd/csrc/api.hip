@@ -162,4 +162,12 @@ int bsa_dense_attn(const void* q, const void* k, const void* v, void* o, float* 
     return hip_status(bsa::launch_attn(p, true, stream), "dense_attn launch");
 }
 
+int bsa_diag_mfma_bf16(int workgroups, int iters, float* sink, hipStream_t stream) {
+    bsa::clear_error();
+    if (workgroups < 1 || workgroups > 1 << 20 || iters < 1 || !sink)
+        return bsa::fail(BSA_EINVAL, "workgroups %d, iters %d must be >= 1 (workgroups <= 2^20), sink non-NULL",
+                         workgroups, iters);
+    return hip_status(bsa::launch_mfma_probe(workgroups, iters, sink, stream), "mfma probe launch");
+}
+
 }  // extern "C"

@@ -42,6 +42,8 @@ hipError_t launch_slab_coverage(const double* cams, int n_cams, const int32_t* p
                                 const int32_t* frame_cam, const float* depth, const int32_t* h_cam,
                                 const double* h_geom, int n_h, float* coverage, void* ws, hipStream_t stream);
 
+hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, hipStream_t stream);
+
 hipError_t launch_attn(const AttnProblem& p, bool dense, hipStream_t stream);
 
 }  // namespace bsa

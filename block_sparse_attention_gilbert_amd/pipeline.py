@@ -170,6 +170,15 @@ class RoutedAttention:
             r = self.route_materialized(c, overlap=overlap, lam=lam, g_ref=g_ref, tau=tau, stream=stream,
                                         **materialize)
             return self._attend(r, nkb, k_hist, v_hist, stream, attn_events)
+        r = self.route(c, k_fixed=k_fixed, k_per_row=k_per_row, overlap=overlap, lam=lam, g_ref=g_ref, tau=tau,
+                       stream=stream)
+        return self._attend(r, nkb, k_hist, v_hist, stream, attn_events)
+
+    def route(self, c: int, *, k_fixed: Optional[int] = None, k_per_row: Optional[torch.Tensor] = None,
+              overlap: Optional[torch.Tensor] = None, lam=2.0, g_ref=0.2, tau=0.1, stream=None):
+        """Top-K routes of the already permuted queries over chunks 0..c."""
+        nkb = (c + 1) * self.nbc
+        k_hist = self.k_store[:, : nkb * self.block]
         tail = self.n_dense_tail_chunks * self.nbc
         kf = self.k_cap if k_fixed is None else k_fixed
         n_cand = nkb - tail
@@ -183,7 +192,7 @@ class RoutedAttention:
         self.workspace = r["workspace"]
         if self.use_kpool:
             self._kpool_valid = max(valid, n_cand)
-        return self._attend(r, nkb, k_hist, v_hist, stream, attn_events)
+        return r
 
     def route_materialized(self, c: int, *, coverage=None, eta_cov=0.9, k_cov=80, k_unc=150, mass=0.9,
                            ref_blocks=(0, 0), window: bool = True, overlap=None, lam=2.0, g_ref=0.2, tau=0.1,

@@ -508,6 +508,17 @@ int bsa_dense_attn(const void* q, const void* k, const void* v, void* o, float* 
                    const int32_t* q_block_len, const int32_t* kv_block_len, float scale,
                    hipStream_t stream);
 
+/*
+ * bsa_diag_mfma_bf16 -- diagnostic, not part of the method: `workgroups`
+ * workgroups of 4 waves each issue 4 * iters v_mfma_f32_32x32x16_bf16
+ * (32768 FLOP each) from registers, with no memory traffic, and write one
+ * float per thread to sink (device float32[workgroups * 256]).  Timing it
+ * gives the bf16 matrix rate the GPU delivers at its current clock, beside
+ * which the attention kernel's rate is read.
+ * Errors: BSA_EINVAL (workgroups outside [1, 2^20], iters < 1, NULL sink).
+ */
+int bsa_diag_mfma_bf16(int workgroups, int iters, float* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
