@@ -483,7 +483,7 @@ def read_traffic(per_launch_bytes):
 COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 
 
-def profile_attention(launches: int):
+def profile_attention(launches: int, expect_out=None):
     """Counter-collection mode: set up C4 at chunk 48, route once, then run
     ``launches`` block-sparse attention launches, two dense ones, and one
     plain 1 GiB device copy (the calibration kernel for the byte counters).  Prints nothing but a summary
@@ -507,7 +507,59 @@ def profile_attention(launches: int):
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
+    if expect_out:
+        # what the launches must issue: every listed block is ceil(valid / 32)
+        # sub-tiles of 32 keys per wave (an empty sub-tile is skipped), each
+        # 8 MFMAs for S and 8 for P V; an unlisted block costs nothing
+        import numpy as np
+        rp = r["row_ptr"].cpu().numpy().astype(np.int64)
+        ci = r["col_idx"].cpu().numpy().astype(np.int64)[: int(rp[-1])]
+        kvl = ra.kv_len[:nkb].cpu().numpy().astype(np.int64)
+        subs = -(-kvl // 32)
+        waves = ra.block // 32
+        with open(expect_out, "w") as f:
+            json.dump({"listed_blocks": int(rp[-1]), "rows": int(len(rp) - 1), "waves_per_row": waves,
+                       "listed_subtiles": int(subs[ci].sum()),
+                       "mfma_sparse_listed": int(subs[ci].sum()) * waves * 16,
+                       "mfma_dense_listed": int(len(rp) - 1) * int(subs.sum()) * waves * 16}, f, indent=1)
     print("profile-attention done: %d attention launches, one %d-byte copy" % (launches, COPY_BYTES), flush=True)
+
+
+def summarize_mfma(counter_csv: str, expect_json: str, out_path: str):
+    """Per-launch matrix-core counters of the attention launches (sparse and
+    dense) from one rocprofv3 --pmc CSV, against the MFMA count the lists
+    imply: a skipped block must cost no matrix work."""
+    import csv
+    per = {}
+    with open(counter_csv) as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            kind = "sparse" if "attn_bf16_kernel<128, 128, false>" in name else (
+                "dense" if "attn_bf16_kernel<128, 128, true>" in name else None)
+            if kind is None:
+                continue
+            key = (kind, row["Dispatch_Id"])
+            per.setdefault(key, {}).setdefault(row["Counter_Name"], 0.0)
+            per[key][row["Counter_Name"]] += float(row["Counter_Value"])
+    exp = json.load(open(expect_json))
+    out = {"kernel": "attn_bf16_kernel<128,128,*>", "workload": "C4 chunk 48", "expected": exp,
+           "attn_source_sha256_16": attn_source_hash()}
+    for kind in ("sparse", "dense"):
+        ds = [v for (k, _), v in per.items() if k == kind]
+        if not ds:
+            continue
+        avg = {c: sum(d.get(c, 0.0) for d in ds) / len(ds) for c in ds[0]}
+        out[kind] = {"launches": len(ds), "per_launch": avg}
+        if "SQ_INSTS_MFMA" in avg:
+            want = exp["mfma_%s_listed" % kind]
+            out[kind]["mfma_over_expected"] = avg["SQ_INSTS_MFMA"] / want
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg and avg["GRBM_GUI_ACTIVE"] > 0:
+            # busy cycles summed over the 1024 SIMDs, against the launch's
+            # GPU-busy cycles (summed over the 8 XCDs)
+            out[kind]["mfma_busy_fraction"] = (avg["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024) / (avg["GRBM_GUI_ACTIVE"] / 8)
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, out_path: str):
@@ -571,11 +623,18 @@ def main():
                     help="write a 1..C chunk rollout (append, route with the pooled-key cache, attend) to this JSONL file")
     ap.add_argument("--profile-attention", type=int, default=0, metavar="N",
                     help="counter mode: N attention launches + a 1 GiB copy, no JSON line")
+    ap.add_argument("--expect-out", default=None, metavar="JSON",
+                    help="counter mode: write the MFMA counts the launches must issue to this file")
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("COUNTER_CSV", "EXPECT_JSON", "OUT_JSON"),
+                    help="compare the MFMA instruction counters of the attention launches with the listed tiles")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                     help="write HBM bytes per attention launch from two rocprofv3 --pmc CSVs")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode (see the sharding notes)",
@@ -586,7 +645,7 @@ def main():
     import block_sparse_attention_gilbert_amd as bsa  # fails loudly if libbsa.so is missing
 
     if args.profile_attention:
-        profile_attention(args.profile_attention)
+        profile_attention(args.profile_attention, args.expect_out)
         return
 
     dev = "cuda:0"
