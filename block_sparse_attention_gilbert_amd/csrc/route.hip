@@ -609,40 +609,13 @@ topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int 
 // count; an exclusive scan turns the counts into row pointers, and a last
 // pass writes the set bits of each row, ascending, into its CSR list.
 
-// Largest K_unc: the ordered top-K_unc of a row is sorted in one wave's LDS.
+// Largest K_unc: the ordered top-K_unc of a row is ranked in one wave (at
+// most four entries per lane).
 constexpr int kMaxUnc = kMaxUncovered;
 
 __device__ __forceinline__ double key_value(unsigned long long key) {
     const unsigned long long b = (key & 0x8000000000000000ull) ? (key & 0x7fffffffffffffffull) : ~key;
     return __longlong_as_double((long long)b);
-}
-
-// Bitonic sort of 256 (key, index) pairs in LDS into selection order by one
-// wave; in each of the 36 stages a lane compare-exchanges two of the 128
-// disjoint pairs.
-__device__ __forceinline__ void wave_sort256_lds(unsigned long long* k, int* ix, int lane) {
-#pragma unroll 1
-    for (int size = 2; size <= kMaxUnc; size <<= 1) {
-#pragma unroll 1
-        for (int j = size >> 1; j > 0; j >>= 1) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int p = lane + 64 * s;
-                const int a = ((p & ~(j - 1)) << 1) | (p & (j - 1)), b = a + j;
-                const unsigned long long ka = k[a], kb = k[b];
-                const int ia = ix[a], ib = ix[b];
-                const bool up = (a & size) == 0;
-                if (up ? sel_before(kb, ib, ka, ia) : sel_before(ka, ia, kb, ib)) {
-                    k[a] = kb;
-                    ix[a] = ib;
-                    k[b] = ka;
-                    ix[b] = ia;
-                }
-            }
-            __builtin_amdgcn_wave_barrier();
-            __asm__ volatile("" ::: "memory");
-        }
-    }
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
@@ -662,7 +635,6 @@ materialize_kernel(const double* __restrict__ keys, int rows, int nqb, int nkb, 
     __shared__ int hist_all[kThreads / 64][256];
     __shared__ unsigned long long skey_all[kThreads / 64][kMaxUnc];
     __shared__ int sidx_all[kThreads / 64][kMaxUnc];
-    __shared__ double sp_all[kThreads / 64][kMaxUnc];
     __shared__ uint32_t bits_all[kThreads / 64][kMaxCandidates / 32];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = blockIdx.x * (kThreads / 64) + w;
@@ -671,7 +643,6 @@ materialize_kernel(const double* __restrict__ keys, int rows, int nqb, int nkb, 
     uint32_t* bits = bits_all[w];
     unsigned long long* skey = skey_all[w];
     int* sidx = sidx_all[w];
-    double* sp = sp_all[w];
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
     for (int x = lane; x < nwords; x += 64) bits[x] = 0u;
     __builtin_amdgcn_wave_barrier();
@@ -753,30 +724,60 @@ materialize_kernel(const double* __restrict__ keys, int rows, int nqb, int nkb, 
                 for (int m = 0; m < KPL; ++m)
                     if (key[m] != 0) z += exp(key_value(key[m]) - smax);
                 z = wave_sum_f64(z);
-                for (int e = ke + lane; e < kMaxUnc; e += 64) {
-                    skey[e] = 0;
-                    sidx[e] = 0x7fffffff;
+                // order the gathered ke keys by rank: an entry's rank is the
+                // number of entries before it in selection order (every lane
+                // compares its up to four entries with all ke of them)
+                __builtin_amdgcn_wave_barrier();
+                __asm__ volatile("" ::: "memory");
+                constexpr int kPer = kMaxUnc / 64;
+                unsigned long long mk[kPer];
+                int mi[kPer], rank[kPer];
+#pragma unroll
+                for (int u = 0; u < kPer; ++u) {
+                    const int e = lane + 64 * u;
+                    mk[u] = e < ke ? skey[e] : 0ull;
+                    mi[u] = e < ke ? sidx[e] : 0x7fffffff;
+                    rank[u] = 0;
+                }
+#pragma unroll 4
+                for (int f = 0; f < ke; ++f) {
+                    const unsigned long long kf = skey[f];
+                    const int jf = sidx[f];
+#pragma unroll
+                    for (int u = 0; u < kPer; ++u) rank[u] += sel_before(kf, jf, mk[u], mi[u]) ? 1 : 0;
                 }
                 __builtin_amdgcn_wave_barrier();
                 __asm__ volatile("" ::: "memory");
-                wave_sort256_lds(skey, sidx, lane);
-                for (int e = lane; e < ke; e += 64) sp[e] = exp(key_value(skey[e]) - smax) / z;
+                // p of each entry, in registers at its rank's lane: lane l,
+                // slot u holds p of the entry of rank l + 64 u
+#pragma unroll
+                for (int u = 0; u < kPer; ++u)
+                    if (lane + 64 * u < ke) {
+                        skey[rank[u]] = mk[u];
+                        sidx[rank[u]] = mi[u];
+                    }
                 __builtin_amdgcn_wave_barrier();
                 __asm__ volatile("" ::: "memory");
+                double pr[kPer];
+#pragma unroll
+                for (int u = 0; u < kPer; ++u) {
+                    const int e = lane + 64 * u;
+                    pr[u] = e < ke ? exp(key_value(skey[e]) - smax) / z : 0.0;
+                }
                 // shortest prefix, in selection order, whose running sum of p
-                // reaches the mass (all ke blocks if none does)
+                // reaches the mass (all ke blocks if none does): a sequential
+                // float64 sum, each term read from its lane
                 int take = ke;
-                if (lane == 0) {
-                    double csum = 0.0;
-                    for (int e = 0; e < ke; ++e) {
-                        csum += sp[e];
-                        if (csum >= mass) {
-                            take = e + 1;
-                            break;
-                        }
+                double csum = 0.0;
+#pragma unroll
+                for (int u = 0; u < kPer; ++u) {
+                    const int n_u = min(64, ke - 64 * u);
+                    const int lo = __double2loint(pr[u]), hi = __double2hiint(pr[u]);
+                    for (int l = 0; l < n_u && take == ke; ++l) {
+                        csum += __hiloint2double(__builtin_amdgcn_readlane(hi, l), __builtin_amdgcn_readlane(lo, l));
+                        if (csum >= mass) take = 64 * u + l + 1;
                     }
                 }
-                take = __shfl(take, 0);
                 for (int e = lane; e < take; e += 64) atomicOr(&bits[sidx[e] >> 5], 1u << (sidx[e] & 31));
             }
         }
@@ -944,8 +945,14 @@ hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* w
         BSA_TOPK(8);
     else if (n_cand <= 64 * 16)
         BSA_TOPK(16);
+    else if (n_cand <= 64 * 24)
+        BSA_TOPK(24);
     else if (n_cand <= 64 * 32)
         BSA_TOPK(32);
+    else if (n_cand <= 64 * 40)
+        BSA_TOPK(40);
+    else if (n_cand <= 64 * 48)
+        BSA_TOPK(48);
     else
         BSA_TOPK(64);
 #undef BSA_TOPK
@@ -972,8 +979,14 @@ hipError_t launch_materialize(const bsa_route_args* a, const bsa_materialize_arg
         BSA_MAT(8);
     else if (nkb <= 64 * 16)
         BSA_MAT(16);
+    else if (nkb <= 64 * 24)
+        BSA_MAT(24);
     else if (nkb <= 64 * 32)
         BSA_MAT(32);
+    else if (nkb <= 64 * 40)
+        BSA_MAT(40);
+    else if (nkb <= 64 * 48)
+        BSA_MAT(48);
     else
         BSA_MAT(64);
 #undef BSA_MAT
