@@ -24,7 +24,8 @@ each stage timed alone with its algorithmic bytes and GB/s, and the
 attention launch with L2 and MALL flushed before each call
 (``breakdown``), the bf16 matrix rate a register-only MFMA probe gets at
 the current clock (``mfma_probe``), dense attention through the same kernel
-(``dense``), the shader/memory clocks at start and end (``clocks``), and
+(``dense``), the shader/memory clocks at start and end (``clocks``), the
+ragged structured configuration C5 at chunk 48 (``c5``), and
 the step with the materialised route instead of the top-K
 (``materialized``: coverage-gated budgets, previous-chunk reservation,
 cumulative-mass prefix and the local window), its overlap and coverage
@@ -331,6 +332,50 @@ def tiles(chunk: int, reps: int, device: str, tile=(1, 8, 16)):
     return out
 
 
+def c5_config(reps: int, device: str):
+    """C5 at chunk 48 (ragged budgets K ~ U{8..143} over 47 history chunks of
+    74 blocks of 64, the current chunk's 74 blocks attended densely, a
+    structured field): the whole step and the attention launch, after the
+    history has been appended chunk by chunk."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from block_sparse_attention_gilbert_amd.pipeline import RoutedAttention
+
+    w = workloads.c5()
+    n_chunks = 48
+    ra = RoutedAttention(w.grid, w.heads, w.d, w.bs, n_chunks, device=device, k_cap=143, n_dense_tail_chunks=1)
+    for c in range(n_chunks - 1):
+        ra.append(w.k_raster[c].to(device), w.v_raster[c].to(device), c)
+    kpr = torch.from_numpy(w.k_per_row).to(device)
+    q_r, k_r, v_r = w.q_raster.to(device), w.k_raster[-1].to(device), w.v_raster[-1].to(device)
+    del w
+    for _ in range(30):
+        _, r = ra.step(q_r, k_r, v_r, n_chunks - 1, k_per_row=kpr)
+    torch.cuda.synchronize()
+    events = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        _, r = ra.step(q_r, k_r, v_r, n_chunks - 1, k_per_row=kpr, attn_events=events)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / reps
+    attn_ms = sum(a.elapsed_time(b) for a, b in events) / len(events)
+    q_len = ra.q_len.cpu().numpy()
+    k_len = ra.kv_len.cpu().numpy()
+    wc = work_counts(r["row_ptr"], r["col_idx"], q_len, k_len, ra.heads, ra.nbc, ra.block, ra.d)
+    out = {"workload": "C5 ragged structured, chunk 48, blocks of 64", "ms_per_step": round(ms_step, 4),
+           "attn_ms": round(attn_ms, 4), "listed_blocks": wc["pairs"], "effective_flop": wc["flop"],
+           "attn_effective_tflops": round(wc["flop"] / (attn_ms * 1e-3) / 1e12, 2),
+           "attn_alg_gbs": round(wc["alg_bytes"] / (attn_ms * 1e-3) / 1e9, 1),
+           "step_effective_tflops": round(wc["flop"] / (ms_step * 1e-3) / 1e12, 2)}
+    del ra, q_r, k_r, v_r
+    torch.cuda.empty_cache()
+    return out
+
+
 def geometry(st, reps: int):
     """Overlap and coverage of the current chunk's query blocks from frustum
     slabs (``workloads.geometry_inputs``: a camera path through a ray-cast
@@ -614,6 +659,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=40)
     ap.add_argument("--no-dense", action="store_true", help="skip timing dense attention at the same chunk")
+    ap.add_argument("--no-c5", action="store_true", help="skip timing the C5 (ragged, structured) configuration")
     ap.add_argument("--tiles", action="store_true",
                     help="also time the step with fixed 1 x 8 x 16 tile blocks at the same chunk")
     ap.add_argument("--no-materialized", action="store_true",
@@ -767,6 +813,8 @@ def main():
         out["materialized"] = materialized(st, max(1, min(args.steps, 10)), ov, cov)
     if args.tiles:
         out["tiles"] = tiles(args.chunk, max(1, min(args.steps, 10)), dev)
+    if not args.no_c5:
+        out["c5"] = c5_config(max(1, min(args.steps, 10)), dev)
     if args.sweep:
         sweep(st, args.sweep)
     if args.rollout:
