@@ -653,13 +653,15 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_path: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--chunk", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=40)
     ap.add_argument("--no-dense", action="store_true", help="skip timing dense attention at the same chunk")
     ap.add_argument("--no-c5", action="store_true", help="skip timing the C5 (ragged, structured) configuration")
+    ap.add_argument("--oracle-table", default=None, metavar="FILE",
+                    help="write the float64 oracle's host times beside the GPU's, config by config, to this JSONL file")
     ap.add_argument("--tiles", action="store_true",
                     help="also time the step with fixed 1 x 8 x 16 tile blocks at the same chunk")
     ap.add_argument("--no-materialized", action="store_true",
@@ -819,6 +821,8 @@ def main():
         sweep(st, args.sweep)
     if args.rollout:
         rollout(st, args.rollout)
+    if args.oracle_table:
+        oracle_table(st, args.oracle_table)
     out["clocks"] = {"start": clocks_start, "end": clocks()}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(st, args.cpu_heads)
@@ -851,6 +855,115 @@ def sweep(st, path):
                                 "dense_attn_ms": round(e0.elapsed_time(e1) / 3, 4)}) + "\n")
             f.flush()
             print("sweep chunk %d done" % c, file=sys.stderr, flush=True)
+
+
+def oracle_table(st, path):
+    """The float64 oracle timed on the host beside the GPU path, config by
+    config: C1, C2, C3 in full, C4 sparse at chunk 1, 2, 12, 24, 48 (two heads
+    timed, scaled to 40) and dense at chunk 1, 2, 12 (one head, scaled); the
+    GPU route + attention time of the same call beside each, and the ratio."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_gilbert_amd as bsa
+    import workloads
+    from oracle import attention as oatt
+    from oracle import route as oroute
+    from oracle.numerics import bf16_bits_to_f64
+
+    def f64(t):
+        t = t.contiguous()
+        return bf16_bits_to_f64(t.view(torch.int16).numpy()) if t.dtype == torch.bfloat16 else \
+            t.numpy().astype(np.float64)
+
+    def gpu_ms(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def oracle_s(w, heads, kpr, overlap=None, dense=False, nkb=None):
+        nkb = w.nkb if nkb is None else nkb
+        rows_k = nkb * w.bs
+        k_len = np.asarray(w.k_len)[:nkb]
+        tr = ta = 0.0
+        for h in heads:
+            q, k, v = f64(w.q[h]), f64(w.k[h][:rows_k]), f64(w.v[h][:rows_k])
+            t0 = time.perf_counter()
+            if dense:
+                oatt.dense_head(q, k, v, w.q_len, k_len, w.bs, w.scale)
+                ta += time.perf_counter() - t0
+                continue
+            r = oroute.route_head(q, k, w.q_len, k_len, w.bs, scale=w.scale, k_per_row=kpr, overlap=overlap,
+                                  lam=w.lam, tau=w.tau, g_ref=w.g_ref)
+            t1 = time.perf_counter()
+            oatt.block_sparse_head(q, k, v, w.q_len, k_len, w.bs, r["lists"], w.scale)
+            tr += t1 - t0
+            ta += time.perf_counter() - t1
+        return tr, ta
+
+    def gpu_call(w, dev_t, nkb, kf, overlap=None, dense=False):
+        q, k, v, ql, kl = dev_t
+        rows = nkb * w.bs
+        kh, vh, klh = k[:, :rows], v[:, :rows], kl[:nkb]
+        ov = None if overlap is None else torch.from_numpy(overlap).to(q.device)
+        if dense:
+            return lambda: bsa.dense_attn(q, kh, vh, block=w.bs, scale=w.scale, q_block_len=ql, kv_block_len=klh)
+        out = {}
+
+        def fn():
+            r = bsa.route_topk(q, kh, block=w.bs, nqb=w.nqb, nkb=nkb, scale=w.scale, q_block_len=ql,
+                               kv_block_len=klh, overlap=ov, lam=w.lam, g_ref=w.g_ref, tau=w.tau, k_fixed=kf,
+                               out=out.get("r"), workspace=(out.get("r") or {}).get("workspace"))
+            out["r"] = r
+            bsa.block_sparse_attn(q, kh, vh, r["row_ptr"], r["col_idx"], block=w.bs, scale=w.scale,
+                                  q_block_len=ql, kv_block_len=klh)
+        return fn
+
+    rows = []
+
+    def add(config, w, heads_timed, nkb, kf, overlap=None, dense=False, reps=1, dev_t=None):
+        dev = "cuda:0"
+        if dev_t is None:
+            dev_t = (w.q.to(dev), w.k.to(dev), w.v.to(dev),
+                     torch.from_numpy(np.asarray(w.q_len, dtype=np.int32)).to(dev),
+                     torch.from_numpy(np.asarray(w.k_len, dtype=np.int32)).to(dev))
+        g = gpu_ms(gpu_call(w, dev_t, nkb, kf, overlap, dense))
+        kpr = np.full(w.nqb, min(kf, nkb))
+        ts = [oracle_s(w, heads_timed, kpr, overlap, dense, nkb) for _ in range(reps)]
+        tr = statistics.median(t[0] for t in ts)
+        ta = statistics.median(t[1] for t in ts)
+        scale = w.heads / len(heads_timed)
+        total = (tr + ta) * scale
+        row = {"config": config, "kind": "dense" if dense else "route + block-sparse",
+               "heads_timed": len(heads_timed), "heads": w.heads, "oracle_route_s": round(tr, 3),
+               "oracle_attention_s": round(ta, 3), "oracle_total_s_all_heads": round(total, 3),
+               "scaled_from_heads": scale != 1, "gpu_ms": round(g, 4), "oracle_over_gpu": round(total * 1e3 / g, 1)}
+        rows.append(row)
+        print("oracle table:", json.dumps(row), file=sys.stderr, flush=True)
+
+    w1 = workloads.c1()
+    add("C1 tiny fp32", w1, [0], w1.nkb, 4, reps=5)
+    w2 = workloads.c2()
+    add("C2 Wan-1.3B-like", w2, list(range(w2.heads)), w2.nkb, 50)
+    w3 = workloads.c3()
+    add("C3 geometric bias", w3, list(range(w3.heads)), w3.nkb, 50, overlap=w3.overlap)
+    w4, ra = st["w"], st["ra"]
+    resident = (ra.q_blk, ra.k_store, ra.v_store, ra.q_len, ra.kv_len)   # the step left Q permuted in q_blk
+    for c in (1, 2, 12, 24, 48):
+        add("C4 chunk %d" % c, w4, [0, 39], 37 * c, 50, dev_t=resident)
+    for c in (1, 2, 12):
+        add("C4 chunk %d" % c, w4, [0], 37 * c, 50, dense=True, dev_t=resident)
+    with open(path, "w") as f:
+        for row in rows:
+            f.write(json.dumps(row) + "\n")
 
 
 def rollout(st, path, reps: int = 5):
