@@ -192,24 +192,21 @@ def _time_ms(fn, reps: int, warm: int = 10, between=None):
 def breakdown(st, reps: int):
     """Each stage of the step alone (median of ``reps`` calls), with its
     algorithmic bytes and the GB/s that gives: the Gilbert index, the three
-    forward permutations (Q, K, V), the router with the pooled-key cache,
-    the attention launch, the inverse permutation of O."""
+    forward permutations (Q and K with their block means, V), the router
+    over the pooled blocks, the attention launch, the inverse permutation
+    of O."""
     import torch
     w, ra = st["w"], st["ra"]
     cur = st["cur"]
-    ks, vs = ra.slot(cur)
     L, heads, d = 4680, w.heads, w.d
     raster = L * heads * d * 2
     blocked = ra.rows_c * heads * d * 2
 
-    def fwd():
-        ra.to_blocks(st["q_raster"], ra.q_blk)
-        ra.to_blocks(st["k_raster"], ks)
-        ra.to_blocks(st["v_raster"], vs)
+    def fwd():                                 # with the block means of Q and of the new chunk's K
+        ra.permute_inputs(st["q_raster"], st["k_raster"], st["v_raster"], cur)
 
-    def route():
-        ra.invalidate_kpool(cur * ra.nbc)      # as in the step: the new chunk's keys are pooled again
-        return ra.route(cur)
+    def route():                               # as in the step: every block's mean is already pooled
+        return ra.route(cur, qpool=ra.qbar)
 
     nkb = w.nkb
     k_hist, v_hist = ra.k_store[:, : nkb * w.bs], ra.v_store[:, : nkb * w.bs]
@@ -217,13 +214,14 @@ def breakdown(st, reps: int):
     torch.cuda.synchronize()
     wc = work_counts(r["row_ptr"], r["col_idx"], w.q_len, w.k_len, w.heads, w.nqb, w.bs, w.d)
     n_cand = nkb
-    route_bytes = (2 * raster                              # Q and the new chunk's K, read once
+    pooled = heads * w.nqb * d * 8                         # one chunk's block means (float64)
+    route_bytes = (pooled                                  # pooled queries read
                    + heads * n_cand * d * 8                # pooled keys (float64) read
                    + 2 * heads * w.nqb * n_cand * 8        # selection keys written and read
                    + 4 * (heads * w.nqb + 1 + int(r["row_ptr"][-1])))
     stages = {
         "gilbert_index": (lambda: ra._index(), 4 * 2 * L),
-        "forward_permutes": (fwd, 3 * (raster + blocked)),
+        "forward_permutes": (fwd, 3 * (raster + blocked) + 2 * pooled),
         "route": (route, route_bytes),
         "attention": (lambda: ra._attend(r, nkb, k_hist, v_hist, None, None), wc["alg_bytes"]),
         "inverse_permute": (lambda: ra.to_raster(ra.o_blk, ra.o_raster), raster + blocked),

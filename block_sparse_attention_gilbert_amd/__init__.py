@@ -60,6 +60,7 @@ class RouteArgs(ctypes.Structure):
         ("kpool", _p), ("kpool_valid_blocks", _i), ("kpool_head_blocks", _i),
         ("row_ptr", _p), ("col_idx", _p), ("col_capacity", _i64),
         ("fallback_counts", _p), ("sel_keys", _p),
+        ("qpool", _p), ("qpool_head_stride", _i64),
     ]
 
 
@@ -83,6 +84,8 @@ _lib.bsa_gilbert_index.restype = _i
 _lib.bsa_gilbert_index.argtypes = [_i, _i, _i, _p, _p, _p]
 _lib.bsa_gilbert_perm.restype = _i
 _lib.bsa_gilbert_perm.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i64, _i64, _i, _i, _p]
+_lib.bsa_gilbert_perm_pool.restype = _i
+_lib.bsa_gilbert_perm_pool.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i64, _i64, _i, _p, _i64, _p]
 _lib.bsa_gilbert_block_window.restype = _i
 _lib.bsa_gilbert_block_window.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p]
 _lib.bsa_route_materialize_workspace_size.restype = ctypes.c_size_t
@@ -114,12 +117,11 @@ _lib.bsa_block_sparse_attn.argtypes = _ATTN_COMMON + [_p, _p, _i64, _f, _p]
 _lib.bsa_dense_attn.restype = _i
 _lib.bsa_dense_attn.argtypes = _ATTN_COMMON + [_f, _p]
 
-EXPORTED = ("bsa_version", "bsa_strerror", "bsa_last_error_detail", "bsa_gilbert_index",
-            "bsa_gilbert_perm", "bsa_gilbert_block_window", "bsa_gilbert_tile_index", "bsa_tile_perm",
+EXPORTED = ("bsa_version", "bsa_strerror", "bsa_last_error_detail", "bsa_gilbert_index", "bsa_gilbert_perm",
+            "bsa_gilbert_perm_pool", "bsa_gilbert_block_window", "bsa_gilbert_tile_index", "bsa_tile_perm",
             "bsa_tile_block_window", "bsa_route_workspace_size", "bsa_route_topk",
-            "bsa_route_materialize_workspace_size", "bsa_route_materialize", "bsa_slab_overlap",
-            "bsa_slab_coverage", "bsa_slab_coverage_workspace_size", "bsa_block_sparse_attn", "bsa_dense_attn",
-            "bsa_diag_mfma_bf16")
+            "bsa_route_materialize_workspace_size", "bsa_route_materialize", "bsa_slab_overlap", "bsa_slab_coverage",
+            "bsa_slab_coverage_workspace_size", "bsa_block_sparse_attn", "bsa_dense_attn", "bsa_diag_mfma_bf16")
 
 
 class BsaError(RuntimeError):
@@ -224,6 +226,33 @@ def gilbert_perm(src: torch.Tensor, perm: torch.Tensor, *, block: int, inverse: 
     _check(_lib.bsa_gilbert_perm(_ptr(src), _ptr(dst), _ptr(perm), L_, heads, d, block, dst.stride(0), ghs, 1,
                                  _dtype_code(src), _stream(stream)))
     return dst
+
+
+def gilbert_perm_pool(src: torch.Tensor, perm: torch.Tensor, *, block: int, dst: Optional[torch.Tensor] = None,
+                      pool: Optional[torch.Tensor] = None, stream=None):
+    """Raster ``[L][heads][d]`` -> Gilbert ``[heads][n_blocks*block][d]``
+    like ``gilbert_perm``, plus the float64 block means of the valid rows
+    into ``pool`` ``[heads][>= n_blocks][d]`` (a head-strided view such as
+    a slice of a pooled-key cache is fine).  Returns ``(dst, pool)``."""
+    _need_gpu(src, perm, dst, pool)
+    perm = _i32(perm, "perm")
+    L_, heads, d = src.shape
+    if src.stride(2) != 1 or src.stride(1) != d:
+        raise ValueError("raster src must have contiguous [heads][d] per token")
+    nb = -(-L_ // block)
+    if dst is None:
+        dst = torch.empty((heads, nb * block, d), dtype=src.dtype, device=src.device)
+    _, drows, ghs = _heads_rows(dst, d)
+    if drows < nb * block:
+        raise ValueError("dst holds %d rows per head, %d needed" % (drows, nb * block))
+    if pool is None:
+        pool = torch.empty((heads, nb, d), dtype=torch.float64, device=src.device)
+    if pool.dtype != torch.float64 or pool.dim() != 3 or pool.shape[0] != heads or pool.shape[1] < nb \
+            or pool.shape[2] != d or pool.stride(2) != 1 or pool.stride(1) != d:
+        raise ValueError("pool must be float64 [heads][>= n_blocks][d] with contiguous blocks")
+    _check(_lib.bsa_gilbert_perm_pool(_ptr(src), _ptr(dst), _ptr(perm), L_, heads, d, block, src.stride(0), ghs,
+                                      _dtype_code(src), _ptr(pool), pool.stride(0), _stream(stream)))
+    return dst, pool
 
 
 def gilbert_block_window(perm: torch.Tensor, inv: torch.Tensor, grid, *, block: int, q_chunk: int,
@@ -382,7 +411,7 @@ def slab_coverage(cams, perm, grid, frame_cam, depth, h_slab_cam, h_slab_geom, *
 
 def _route_args(q, k, *, block, nqb, nkb, q_block_len, kv_block_len, scale, overlap, lam, g_ref, tau,
                 k_fixed, k_per_row, k_max, n_dense_tail_blocks, kpool, kpool_valid_blocks,
-                row_ptr, col_idx, fallback_counts, sel_keys):
+                row_ptr, col_idx, fallback_counts, sel_keys, qpool=None):
     d = q.shape[2]
     heads, _, qhs = _heads_rows(q, d)
     _, _, khs = _heads_rows(k, d)
@@ -415,6 +444,11 @@ def _route_args(q, k, *, block, nqb, nkb, q_block_len, kv_block_len, scale, over
         a.row_ptr, a.col_idx, a.col_capacity = row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel()
     a.fallback_counts = None if fallback_counts is None else fallback_counts.data_ptr()
     a.sel_keys = None if sel_keys is None else sel_keys.data_ptr()
+    if qpool is not None:
+        if qpool.dtype != torch.float64 or qpool.dim() != 3 or qpool.shape[2] != d or qpool.stride(2) != 1 \
+                or qpool.stride(1) != d or qpool.shape[0] != heads or qpool.shape[1] < nqb:
+            raise ValueError("qpool must be float64 [heads][>= nqb][d] with contiguous blocks")
+        a.qpool, a.qpool_head_stride = qpool.data_ptr(), qpool.stride(0)
     return a
 
 
@@ -427,13 +461,14 @@ def route_capacity(heads: int, nqb: int, nkb: int, k_cap: int, n_dense_tail_bloc
 def route_topk(q: torch.Tensor, k: torch.Tensor, *, block: int, nqb: int, nkb: int, scale: float,
                q_block_len=None, kv_block_len=None, overlap=None, lam: float = 2.0, g_ref: float = 0.2,
                tau: float = 0.1, k_fixed: int = 50, k_per_row=None, k_max: Optional[int] = None,
-               n_dense_tail_blocks: int = 0, kpool=None, kpool_valid_blocks: int = 0,
+               n_dense_tail_blocks: int = 0, kpool=None, kpool_valid_blocks: int = 0, qpool=None,
                want_keys: bool = False, out: Optional[dict] = None, workspace=None, stream=None):
     """Pool, score, fuse and select.  Returns a dict with ``row_ptr``,
     ``col_idx`` (capacity-sized; the first ``row_ptr[-1]`` entries are the
     lists), ``fallback_counts`` and optionally ``sel_keys``.  ``out`` and
-    ``workspace`` may be passed in to avoid allocations."""
-    _need_gpu(q, k, q_block_len, kv_block_len, overlap, k_per_row, kpool)
+    ``workspace`` may be passed in to avoid allocations.  ``qpool``: the
+    pooled queries (``gilbert_perm_pool``), so ``q`` is not pooled again."""
+    _need_gpu(q, k, q_block_len, kv_block_len, overlap, k_per_row, kpool, qpool)
     heads = q.shape[0]
     n_cand = nkb - n_dense_tail_blocks
     k_cap = k_max if k_per_row is not None else k_fixed
@@ -453,7 +488,7 @@ def route_topk(q: torch.Tensor, k: torch.Tensor, *, block: int, nqb: int, nkb: i
                     g_ref=g_ref, tau=tau, k_fixed=k_fixed, k_per_row=_i32(k_per_row, "k_per_row"), k_max=k_max,
                     n_dense_tail_blocks=n_dense_tail_blocks, kpool=kpool, kpool_valid_blocks=kpool_valid_blocks,
                     row_ptr=out["row_ptr"], col_idx=out["col_idx"], fallback_counts=out["fallback_counts"],
-                    sel_keys=out.get("sel_keys"))
+                    sel_keys=out.get("sel_keys"), qpool=qpool)
     need = _lib.bsa_route_workspace_size(ctypes.byref(a))
     if need == 0:
         _check(_lib.bsa_route_topk(ctypes.byref(a), None, 0, _stream(stream)))
@@ -501,14 +536,14 @@ def route_materialize(q: torch.Tensor, k: torch.Tensor, *, block: int, nqb: int,
                       q_block_len=None, kv_block_len=None, overlap=None, lam: float = 2.0, g_ref: float = 0.2,
                       tau: float = 0.1, coverage=None, eta_cov: float = 0.9, k_cov: int = 80, k_unc: int = 150,
                       mass: float = 0.9, prev_blocks=(0, 0), window=None, window_len=None, ref_blocks=(0, 0),
-                      kpool=None, kpool_valid_blocks: int = 0, want_keys: bool = False,
+                      kpool=None, kpool_valid_blocks: int = 0, qpool=None, want_keys: bool = False,
                       out: Optional[dict] = None, workspace=None, stream=None):
     """Materialised routes: coverage-gated budgets, the previous chunk's
     reservation, the cumulative-mass prefix, the local window and the
     reference blocks.  Returns a dict with ``row_ptr`` and ``col_idx``
     (capacity-sized; the first ``row_ptr[-1]`` entries are the lists) and
-    optionally ``sel_keys``."""
-    _need_gpu(q, k, q_block_len, kv_block_len, overlap, coverage, window, window_len, kpool)
+    optionally ``sel_keys``.  ``qpool`` as in ``route_topk``."""
+    _need_gpu(q, k, q_block_len, kv_block_len, overlap, coverage, window, window_len, kpool, qpool)
     heads = q.shape[0]
     dev = q.device
     wstride = 0 if window is None else window.stride(0)
@@ -524,7 +559,7 @@ def route_materialize(q: torch.Tensor, k: torch.Tensor, *, block: int, nqb: int,
                     kv_block_len=_i32(kv_block_len, "kv_block_len"), scale=scale, overlap=overlap, lam=lam,
                     g_ref=g_ref, tau=tau, k_fixed=0, k_per_row=None, k_max=0, n_dense_tail_blocks=0, kpool=kpool,
                     kpool_valid_blocks=kpool_valid_blocks, row_ptr=out["row_ptr"], col_idx=out["col_idx"],
-                    fallback_counts=None, sel_keys=out.get("sel_keys"))
+                    fallback_counts=None, sel_keys=out.get("sel_keys"), qpool=qpool)
     m = _materialize_args(coverage, eta_cov, k_cov, k_unc, mass, prev_blocks, window, window_len, ref_blocks)
     need = _lib.bsa_route_materialize_workspace_size(ctypes.byref(a), ctypes.byref(m))
     if need == 0:
@@ -607,8 +642,9 @@ def dense_attn(q, k, v, *, block: int, scale: Optional[float] = None, q_block_le
     return out, lse
 
 
-__all__ = ["gilbert_index", "gilbert_perm", "gilbert_block_window", "gilbert_tile_index", "tile_perm",
-           "tile_block_window", "tile_grid", "slab_overlap", "slab_coverage", "route_topk", "route_workspace_size",
-           "route_capacity", "route_materialize", "route_materialize_workspace_size", "materialize_capacity",
-           "MaterializeArgs", "block_sparse_attn", "dense_attn", "version", "library", "BsaError", "RouteArgs", "EXPORTED",
-           "BSA_OK", "BSA_EINVAL", "BSA_EUNSUPPORTED", "BSA_EWORKSPACE", "BSA_EHIP", "BSA_BF16", "BSA_F32"]
+__all__ = ["gilbert_index", "gilbert_perm", "gilbert_perm_pool", "gilbert_block_window", "gilbert_tile_index",
+           "tile_perm", "tile_block_window", "tile_grid", "slab_overlap", "slab_coverage", "route_topk",
+           "route_workspace_size", "route_capacity", "route_materialize", "route_materialize_workspace_size",
+           "materialize_capacity", "MaterializeArgs", "block_sparse_attn", "dense_attn", "version", "library",
+           "BsaError", "RouteArgs", "EXPORTED", "BSA_OK", "BSA_EINVAL", "BSA_EUNSUPPORTED", "BSA_EWORKSPACE",
+           "BSA_EHIP", "BSA_BF16", "BSA_F32"]

@@ -34,6 +34,18 @@ int bsa_gilbert_perm(const void* src, void* dst, const int32_t* perm, int L, int
                       "gilbert_perm launch");
 }
 
+int bsa_gilbert_perm_pool(const void* src, void* dst, const int32_t* perm, int L, int heads, int d, int block,
+                          int64_t raster_token_stride, int64_t gilbert_head_stride, int dtype, double* pool,
+                          int64_t pool_head_stride, hipStream_t stream) {
+    bsa::clear_error();
+    const int st = bsa::validate_gilbert_perm_pool(src, dst, perm, L, heads, d, block, raster_token_stride,
+                                                   gilbert_head_stride, dtype, pool, pool_head_stride);
+    if (st != BSA_OK) return st;
+    return hip_status(bsa::launch_gilbert_perm_pool(src, dst, perm, L, heads, d, block, raster_token_stride,
+                                                    gilbert_head_stride, dtype, pool, pool_head_stride, stream),
+                      "gilbert_perm_pool launch");
+}
+
 int bsa_route_topk(const bsa_route_args* args, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     bsa::clear_error();
     bsa::RouteLayout lay;

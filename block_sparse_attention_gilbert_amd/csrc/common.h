@@ -47,6 +47,9 @@ int validate_gilbert_index(int T, int H, int W, const int32_t* perm);
 int validate_gilbert_perm(const void* src, const void* dst, const int32_t* perm, int L, int heads,
                           int d, int block, int64_t raster_token_stride,
                           int64_t gilbert_head_stride, int inverse, int dtype);
+int validate_gilbert_perm_pool(const void* src, const void* dst, const int32_t* perm, int L, int heads, int d,
+                               int block, int64_t raster_token_stride, int64_t gilbert_head_stride, int dtype,
+                               const double* pool, int64_t pool_head_stride);
 int validate_attn(const AttnProblem& p, bool dense);
 int validate_route(const bsa_route_args* a, RouteLayout* lay);
 int validate_materialize(const bsa_route_args* a, const bsa_materialize_args* m, RouteLayout* lay);

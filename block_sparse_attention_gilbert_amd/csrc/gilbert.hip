@@ -84,6 +84,65 @@ gilbert_perm_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, cons
     }
 }
 
+// Forward permutation fused with the block means of the permuted rows.
+// One workgroup per (block, head): thread t copies 16-byte chunk t % chunks
+// of the block's rows t / chunks, + groups, ... (raster token perm[i] to
+// Gilbert row i; padding rows written as zeros) and sums what it copied in
+// float64.  The row groups of a wave are combined with shuffles, the four
+// waves through LDS in wave order, and the mean over the block's valid rows
+// goes to pool.  Sums of at most 128 bf16 values are exact in float64
+// unless their magnitudes span more than 2^37, so the mean equals the one
+// pooled from the permuted tensor by any summation order.
+// [Velox -- Methodology, Step 4: mean query and mean key vectors per block;
+//  Step 6: neighbouring regions contiguous in the block-padded layout]
+template <bool BF16>
+__global__ void __launch_bounds__(256)
+gilbert_perm_pool_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, const int32_t* __restrict__ perm,
+                         int L, int d, int block, int64_t raster_token_stride_c, int64_t gilbert_head_stride_c,
+                         double* __restrict__ pool, int64_t pool_head_stride) {
+    constexpr int CE = BF16 ? 8 : 4;  // elements per 16-byte chunk
+    __shared__ double part[4][128];
+    const int t = threadIdx.x, w = t >> 6;
+    const int b = blockIdx.x, h = blockIdx.y;
+    const int chunks = d / CE, groups = 256 / chunks;
+    const int ch = t % chunks, g = t / chunks;
+    const int64_t i0 = (int64_t)b * block;
+    const int valid = (int)(L - i0 < block ? L - i0 : block);
+    const int64_t hc = (int64_t)h * chunks + ch;
+    uint4* out = dst + h * gilbert_head_stride_c + i0 * chunks + ch;
+    double acc[CE];
+#pragma unroll
+    for (int e = 0; e < CE; ++e) acc[e] = 0.0;
+#pragma unroll 4
+    for (int k = g; k < block; k += groups) {
+        uint4 u = make_uint4(0u, 0u, 0u, 0u);
+        if (k < valid) u = src[(int64_t)perm[i0 + k] * raster_token_stride_c + hc];
+        out[(int64_t)k * chunks] = u;
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+        if (BF16) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += (double)__uint_as_float(wd[e] << 16);
+                acc[2 * e + 1] += (double)__uint_as_float(wd[e] & 0xFFFF0000u);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(wd[e]);
+        }
+    }
+    for (int off = chunks; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < CE; ++e) acc[e] += __shfl_xor(acc[e], off);
+    if ((t & 63) < chunks)
+#pragma unroll
+        for (int e = 0; e < CE; ++e) part[w][ch * CE + e] = acc[e];
+    __syncthreads();
+    if (t < d) {
+        const double sum = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
+        pool[h * pool_head_stride + (int64_t)b * d + t] = sum / (double)valid;
+    }
+}
+
 }  // namespace
 
 // Fixed 3-D tile layout: one thread per row of the tiled chunk.  Block b
@@ -248,6 +307,22 @@ hipError_t launch_gilbert_perm(const void* src, void* dst, const int32_t* perm, 
     else
         hipLaunchKernelGGL(gilbert_perm_kernel<false>, grid, dim3(256), 0, stream, static_cast<const uint4*>(src),
                            static_cast<uint4*>(dst), perm, L, heads, log2c, rows_total, rts_c, ghs_c);
+    return hipGetLastError();
+}
+
+hipError_t launch_gilbert_perm_pool(const void* src, void* dst, const int32_t* perm, int L, int heads, int d,
+                                    int block, int64_t raster_token_stride, int64_t gilbert_head_stride, int dtype,
+                                    double* pool, int64_t pool_head_stride, hipStream_t stream) {
+    const int chunk_elems = dtype == BSA_BF16 ? 8 : 4;
+    const dim3 grid((unsigned)((L + block - 1) / block), (unsigned)heads);
+    const int64_t rts_c = raster_token_stride / chunk_elems;
+    const int64_t ghs_c = gilbert_head_stride / chunk_elems;
+    if (dtype == BSA_BF16)
+        hipLaunchKernelGGL(gilbert_perm_pool_kernel<true>, grid, dim3(256), 0, stream, static_cast<const uint4*>(src),
+                           static_cast<uint4*>(dst), perm, L, d, block, rts_c, ghs_c, pool, pool_head_stride);
+    else
+        hipLaunchKernelGGL(gilbert_perm_pool_kernel<false>, grid, dim3(256), 0, stream, static_cast<const uint4*>(src),
+                           static_cast<uint4*>(dst), perm, L, d, block, rts_c, ghs_c, pool, pool_head_stride);
     return hipGetLastError();
 }
 

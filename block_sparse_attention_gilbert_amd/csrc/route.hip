@@ -150,7 +150,8 @@ __device__ __forceinline__ f64x4 load_f64x4(const double* p) {
 }
 
 __global__ void __launch_bounds__(kThreads)
-score_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar, int64_t kbar_head_blocks,
+score_kernel(const double* __restrict__ qbar, int64_t qbar_head_stride, const double* __restrict__ kbar,
+             int64_t kbar_head_blocks,
              int nqb, int n_cand, int d, double scale, const float* __restrict__ overlap, int64_t ors,
              double lambda, double g_ref, double tau, const float* __restrict__ coverage, double eta_cov,
              double* __restrict__ keys) {
@@ -175,7 +176,8 @@ score_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar, i
         for (int u = 0; u < kScoreTiles; ++u) {
             const int row = r0 + 16 * u + r;
             qa[k][u] = zero;
-            if (st < steps && row < nqb) qa[k][u] = load_f64x4(qbar + ((int64_t)h * nqb + row) * d + 16 * st + 4 * g);
+            if (st < steps && row < nqb)
+                qa[k][u] = load_f64x4(qbar + h * qbar_head_stride + (int64_t)row * d + 16 * st + 4 * g);
         }
     }
     f64x4 acc[kScoreJT][kScoreTiles];
@@ -318,84 +320,48 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
     return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
 }
 
-__device__ __forceinline__ unsigned long long shfl_u64(unsigned long long v, int src) {
-    const int lo = __shfl((int)(unsigned)v, src), hi = __shfl((int)(unsigned)(v >> 32), src);
-    return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
-}
-
 // (key, index) order of the selection: larger key first, lower index first
 // among equal keys.
 __device__ __forceinline__ bool sel_before(unsigned long long ka, int ia, unsigned long long kb, int ib) {
     return ka > kb || (ka == kb && ia < ib);
 }
 
-// Bitonic sort of 128 (key, index) pairs held two per lane (element lane and
-// element lane + 64) into selection order, across the wave.
-__device__ __forceinline__ void wave_sort128(unsigned long long& ka, int& ia, unsigned long long& kb, int& ib,
-                                             int lane) {
+// The k-th largest of the values held by a wave, N per lane (0 = none), by
+// bisection on the bits: the largest t with at least k values >= t, built
+// from the most significant bit down (0 when fewer than k values are
+// non-zero).  The count of each trial is a ballot, so the bound stays
+// wave-uniform and nothing moves between lanes.
+template <int N>
+__device__ __forceinline__ unsigned long long wave_kth_largest(const unsigned long long (&v)[N], int k) {
+    unsigned long long p = 0;
+    k = __builtin_amdgcn_readfirstlane(k);  // the same for every lane; keeps the bound scalar
 #pragma unroll
-    for (int k = 2; k <= 128; k <<= 1) {
+    for (int b = 63; b >= 0; --b) {
+        const unsigned long long t = p | (1ull << b);
+        int c = 0;
 #pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            if (j == 64) {
-                // pairs (lane, lane + 64); k == 128, so the lower keeps the first
-                if (sel_before(kb, ib, ka, ia)) {
-                    const unsigned long long tk = ka;
-                    const int ti = ia;
-                    ka = kb;
-                    ia = ib;
-                    kb = tk;
-                    ib = ti;
-                }
-            } else {
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    unsigned long long& kv = s ? kb : ka;
-                    int& iv = s ? ib : ia;
-                    const int e = lane + 64 * s;
-                    const unsigned long long ko = shfl_xor_u64(kv, j);
-                    const int io = __shfl_xor(iv, j);
-                    const bool first = (e & j) == 0, desc = (e & k) == 0;
-                    const bool mine_first = sel_before(kv, iv, ko, io);
-                    if (first == desc ? !mine_first : mine_first) {
-                        kv = ko;
-                        iv = io;
-                    }
-                }
-            }
-        }
+        for (int n = 0; n < N; ++n) c += __popcll(__ballot(v[n] >= t));
+        if (c >= k) p = t;
     }
-}
-
-// Bitonic sort of one value per lane, largest first.
-__device__ __forceinline__ unsigned long long wave_sort64_desc(unsigned long long v, int lane) {
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const unsigned long long o = shfl_xor_u64(v, j);
-            const bool first = (lane & j) == 0, desc = (lane & k) == 0;
-            const unsigned long long hi = v > o ? v : o, lo = v > o ? o : v;
-            v = first == desc ? hi : lo;
-        }
-    }
-    return v;
+    return p;
 }
 
 // Threshold of the top-ke selection over the keys of one row held by a
 // wave (lane l: keys of candidates l + 64 m; 0 = not a candidate): the
 // selected set is every key > prefix plus the first `need` keys == prefix
 // in ascending candidate order, which is the total order (key descending,
-// index ascending).  A fast path (below) handles most rows with ke <= 64
-// (a wave bitonic network over the lane maxima, then over the at most 128
-// keys at or above the ke-th largest of them); otherwise a
-// radix select over 8-bit digits (most significant first, a 256-bin
+// index ascending); prefix is the ke-th largest key and need = ke minus the
+// number of keys above it.  A fast path (below) handles most rows with
+// ke <= 64: the ke-th largest lane maximum bounds the ke-th largest key from
+// below, and when at most 128 keys reach that bound they are gathered two
+// per lane and the ke-th largest of them is found by bisection.  Otherwise
+// a radix select over 8-bit digits (most significant first, a 256-bin
 // histogram per wave in LDS) finds the ke-th largest key and how many keys
-// equal to it are needed.  `hist` is a 256-int and cand_key / cand_idx
-// 128-entry per-wave LDS scratch.
+// equal to it are needed.  `hist` is a 256-int and cand_key a 128-entry
+// per-wave LDS scratch.
 template <int KPL>
 __device__ __forceinline__ void select_threshold(const unsigned long long (&key)[KPL], int ke, int lane,
-                                                 int* hist, unsigned long long* cand_key, int* cand_idx,
+                                                 int* hist, unsigned long long* cand_key,
                                                  unsigned long long& prefix, int& need) {
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
     unsigned long long mask = 0;
@@ -403,53 +369,32 @@ __device__ __forceinline__ void select_threshold(const unsigned long long (&key)
     need = ke;
     bool found = false;
     if (ke > 0 && ke <= 64) {
-        // Fast path.  The ke-th largest lane maximum L is a lower bound of
-        // the ke-th largest key (ke lanes hold a key >= L), so every selected
-        // key is >= L.  When at most 128 keys are >= L, they are gathered,
-        // sorted in selection order, and the ke-th gives the threshold.
-        unsigned long long lm = 0;
+        // ke lanes hold a key >= L, so every selected key is >= L
+        unsigned long long lm[1] = {0};
 #pragma unroll
-        for (int m = 0; m < KPL; ++m) lm = key[m] > lm ? key[m] : lm;
-        const unsigned long long L = shfl_u64(wave_sort64_desc(lm, lane), ke - 1);
+        for (int m = 0; m < KPL; ++m) lm[0] = key[m] > lm[0] ? key[m] : lm[0];
+        const unsigned long long L = wave_kth_largest<1>(lm, ke);
+        unsigned long long* ck = cand_key;
         int c = 0;
 #pragma unroll
-        for (int m = 0; m < KPL; ++m) c += __popcll(__ballot(key[m] != 0 && key[m] >= L));
+        for (int m = 0; m < KPL; ++m) {
+            const bool cand = key[m] != 0 && key[m] >= L;
+            const unsigned long long b = __ballot(cand);
+            const int at = c + __popcll(b & lt_mask);
+            if (cand && at < 128) ck[at] = key[m];
+            c += __popcll(b);
+        }
         if (c <= 128) {
-            unsigned long long* ck = cand_key;
-            int* ci = cand_idx;
-            int pos = 0;
-#pragma unroll
-            for (int m = 0; m < KPL; ++m) {
-                const bool cand = key[m] != 0 && key[m] >= L;
-                const unsigned long long b = __ballot(cand);
-                if (cand) {
-                    const int at = pos + __popcll(b & lt_mask);
-                    ck[at] = key[m];
-                    ci[at] = lane + 64 * m;
-                }
-                pos += __popcll(b);
-            }
-            for (int e = c + lane; e < 128; e += 64) {
-                ck[e] = 0;
-                ci[e] = 0x7fffffff;
-            }
             __builtin_amdgcn_wave_barrier();
             __asm__ volatile("" ::: "memory");
-            unsigned long long ka = ck[lane], kb = ck[lane + 64];
-            int ia = ci[lane], ib = ci[lane + 64];
-            wave_sort128(ka, ia, kb, ib, lane);
-            const int p = ke - 1;
-            const unsigned long long kt = shfl_u64(p < 64 ? ka : kb, p & 63);
-            const int it = __shfl(p < 64 ? ia : ib, p & 63);
-            // threshold key and how many keys equal to it are taken (those
-            // with index <= it, in ascending index order)
-            int eq_take = 0;
-#pragma unroll
-            for (int m = 0; m < KPL; ++m) eq_take += __popcll(__ballot(key[m] == kt && lane + 64 * m <= it));
+            const unsigned long long two[2] = {lane < c ? ck[lane] : 0ull, lane + 64 < c ? ck[lane + 64] : 0ull};
+            const unsigned long long kt = wave_kth_largest<2>(two, ke);
             prefix = kt;
-            need = eq_take;
+            need = ke - __popcll(__ballot(two[0] > kt)) - __popcll(__ballot(two[1] > kt));
             found = true;
         }
+        __builtin_amdgcn_wave_barrier();
+        __asm__ volatile("" ::: "memory");
     }
     if (ke > 0 && !found) {
 #pragma unroll 1
@@ -500,7 +445,8 @@ __device__ __forceinline__ void select_threshold(const unsigned long long (&key)
 // One wave per (head, query block) row: the threshold of its top-K_eff,
 // then the selected indices in ascending order (ballot prefix counts),
 // followed by the dense tail.  grid = ceil(rows / 4), 4 waves per
-// workgroup, no barriers.
+// workgroup, no barriers.  The keys and the block lengths are loaded
+// together, so a row costs one memory round trip before the selection.
 template <int KPL>
 __global__ void __launch_bounds__(kThreads)
 topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int nkb, int block,
@@ -509,20 +455,28 @@ topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int 
             int32_t* __restrict__ zero_counts) {
     __shared__ int hist_all[kThreads / 64][256];
     __shared__ unsigned long long cand_key[kThreads / 64][128];
-    __shared__ int cand_idx[kThreads / 64][128];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // the wave index is the same for every lane: row, query block and budget stay scalar
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = blockIdx.x * (kThreads / 64) + w;
     if (r >= rows) return;
     const int i = r % nqb;
     const int vq = q_len ? q_len[i] : block;
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
-    bool vis[KPL];
+    const double* row = keys + (int64_t)r * n_cand;
+    // keys of the visible candidates (0: not a candidate)
+    unsigned long long key[KPL];
     int n_vis = 0;
 #pragma unroll
     for (int m = 0; m < KPL; ++m) {
         const int j = lane + 64 * m;
-        vis[m] = j < n_cand && (kv_len ? kv_len[j] : block) > 0;
-        n_vis += __popcll(__ballot(vis[m]));
+        double x = 0.0;
+        int v = 0;
+        if (j < n_cand) {
+            x = row[j];
+            v = kv_len ? kv_len[j] : block;
+        }
+        key[m] = v > 0 ? order_key(x) : 0ull;
+        n_vis += __popcll(__ballot(key[m] != 0));
     }
     int start, ke;
     if (k_fused >= 0) {
@@ -557,15 +511,10 @@ topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int 
     }
     if (vq <= 0) return;
     int* hist = hist_all[w];
-    const double* row = keys + (int64_t)r * n_cand;
-
-    unsigned long long key[KPL];
-#pragma unroll
-    for (int m = 0; m < KPL; ++m) key[m] = vis[m] ? order_key(row[lane + 64 * m]) : 0ull;
 
     unsigned long long prefix;
     int need;
-    select_threshold<KPL>(key, ke, lane, hist, cand_key[w], cand_idx[w], prefix, need);
+    select_threshold<KPL>(key, ke, lane, hist, cand_key[w], prefix, need);
     // ordered compaction: key > t, or key == t and among the first `need`
     int base = start, eq_seen = 0;
 #pragma unroll
@@ -680,7 +629,7 @@ materialize_kernel(const double* __restrict__ keys, int rows, int nqb, int nkb, 
         if (ke > 0) {
             unsigned long long prefix;
             int need;
-            select_threshold<KPL>(key, ke, lane, hist_all[w], skey, sidx, prefix, need);
+            select_threshold<KPL>(key, ke, lane, hist_all[w], skey, prefix, need);
             __builtin_amdgcn_wave_barrier();
             __asm__ volatile("" ::: "memory");
             // the selected keys in ascending block order: a well-covered row
@@ -871,7 +820,8 @@ namespace {
 void launch_pool_score(const bsa_route_args* a, const RouteLayout& lay, void* ws, const float* coverage,
                        double eta_cov, bool want_flags, hipStream_t stream) {
     char* w = static_cast<char*>(ws);
-    double* qbar = reinterpret_cast<double*>(w + lay.qbar);
+    const double* qbar = a->qpool ? a->qpool : reinterpret_cast<double*>(w + lay.qbar);
+    const int64_t qbar_head_stride = a->qpool ? a->qpool_head_stride : (int64_t)a->nqb * a->d;
     const int n_cand = lay.n_cand;
     double* kbar = lay.kbar_in_ws ? reinterpret_cast<double*>(w + lay.kbar) : a->kpool;
     const int64_t kbar_head_blocks = (!lay.kbar_in_ws && a->kpool_head_blocks > 0) ? a->kpool_head_blocks : n_cand;
@@ -879,15 +829,16 @@ void launch_pool_score(const bsa_route_args* a, const RouteLayout& lay, void* ws
     int32_t* flags = reinterpret_cast<int32_t*>(w + lay.flags);
     const bool bf16 = a->dtype == BSA_BF16;
 
-    // pooled queries
-    {
+    // pooled queries (unless the caller pooled them)
+    if (!a->qpool) {
+        double* qout = reinterpret_cast<double*>(w + lay.qbar);
         dim3 grid(a->nqb, a->heads);
         if (bf16)
             hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kThreads), 0, stream, a->q, a->q_head_stride, a->d,
-                               a->block, a->q_block_len, 0, a->nqb, qbar, (int64_t)a->nqb);
+                               a->block, a->q_block_len, 0, a->nqb, qout, (int64_t)a->nqb);
         else
             hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kThreads), 0, stream, a->q, a->q_head_stride, a->d,
-                               a->block, a->q_block_len, 0, a->nqb, qbar, (int64_t)a->nqb);
+                               a->block, a->q_block_len, 0, a->nqb, qout, (int64_t)a->nqb);
     }
     // pooled keys of the candidates not yet in the cache
     const int kb0 = a->kpool ? a->kpool_valid_blocks : 0;
@@ -908,7 +859,8 @@ void launch_pool_score(const bsa_route_args* a, const RouteLayout& lay, void* ws
     // selection keys
     if (n_cand > 0) {
         dim3 grid((n_cand + kScoreJ - 1) / kScoreJ, a->heads, (a->nqb + kScoreRows - 1) / kScoreRows);
-        hipLaunchKernelGGL(score_kernel, grid, dim3(kThreads), 0, stream, qbar, kbar, kbar_head_blocks, a->nqb,
+        hipLaunchKernelGGL(score_kernel, grid, dim3(kThreads), 0, stream, qbar, qbar_head_stride, kbar,
+                           kbar_head_blocks, a->nqb,
                            n_cand, a->d, a->scale, a->overlap, a->overlap_row_stride, a->lambda, a->g_ref, a->tau,
                            coverage, eta_cov, keys);
     }

@@ -65,6 +65,31 @@ int validate_gilbert_perm(const void* src, const void* dst, const int32_t* perm,
     return BSA_OK;
 }
 
+int validate_gilbert_perm_pool(const void* src, const void* dst, const int32_t* perm, int L, int heads, int d,
+                               int block, int64_t raster_token_stride, int64_t gilbert_head_stride, int dtype,
+                               const double* pool, int64_t pool_head_stride) {
+    const int st = validate_gilbert_perm(src, dst, perm, L, heads, d, block, raster_token_stride,
+                                         gilbert_head_stride, 0, dtype);
+    if (st != BSA_OK) return st;
+    if (!pool) return fail(BSA_EINVAL, "pool must be non-NULL");
+    if (heads > 65535) return fail(BSA_EINVAL, "heads = %d exceeds 65535", heads);
+    if (reinterpret_cast<uintptr_t>(pool) & 7u) return fail(BSA_EINVAL, "pool must be 8-byte aligned");
+    const int64_t nb = ceil_div(L, block);
+    if (pool_head_stride < nb * d)
+        return fail(BSA_EINVAL, "pool_head_stride %lld < n_blocks*d = %lld", (long long)pool_head_stride,
+                    (long long)(nb * d));
+    const int eb = dtype_bytes(dtype);
+    const char* pb = reinterpret_cast<const char*>(pool);
+    const int64_t pool_bytes = ((int64_t)(heads - 1) * pool_head_stride + nb * d) * (int64_t)sizeof(double);
+    const char* s = static_cast<const char*>(src);
+    const char* t = static_cast<const char*>(dst);
+    const int64_t raster_bytes = ((int64_t)(L - 1) * raster_token_stride + (int64_t)heads * d) * eb;
+    const int64_t gil_bytes = ((int64_t)(heads - 1) * gilbert_head_stride + nb * block * d) * eb;
+    if ((pb < s + raster_bytes && s < pb + pool_bytes) || (pb < t + gil_bytes && t < pb + pool_bytes))
+        return fail(BSA_EINVAL, "pool overlaps src or dst");
+    return BSA_OK;
+}
+
 int validate_attn(const AttnProblem& p, bool dense) {
     if (!p.q || !p.k || !p.v || !p.o) return fail(BSA_EINVAL, "q, k, v and o must be non-NULL");
     if (!dense && (!p.row_ptr || !p.col_idx)) return fail(BSA_EINVAL, "row_ptr and col_idx must be non-NULL");
@@ -116,7 +141,7 @@ int validate_route(const bsa_route_args* a, RouteLayout* lay) {
     if (a->struct_size != sizeof(bsa_route_args))
         return fail(BSA_EINVAL, "struct_size %zu != sizeof(bsa_route_args) %zu", a->struct_size,
                     sizeof(bsa_route_args));
-    if (!a->q || !a->k) return fail(BSA_EINVAL, "q and k must be non-NULL");
+    if ((!a->q && !a->qpool) || !a->k) return fail(BSA_EINVAL, "k and one of q, qpool must be non-NULL");
     if (!a->row_ptr || !a->col_idx) return fail(BSA_EINVAL, "row_ptr and col_idx must be non-NULL");
     if (a->dtype != BSA_BF16 && a->dtype != BSA_F32) return fail(BSA_EUNSUPPORTED, "dtype %d", a->dtype);
     if (!supported_dim(a->d)) return fail(BSA_EUNSUPPORTED, "d = %d (64 or 128)", a->d);
@@ -131,11 +156,16 @@ int validate_route(const bsa_route_args* a, RouteLayout* lay) {
                     kMaxCandidates);
     if ((int64_t)a->heads * a->nqb > (1 << 24)) return fail(BSA_EINVAL, "heads*nqb too large");
     const int64_t qrows = (int64_t)a->nqb * a->block, krows = (int64_t)a->nkb * a->block;
-    if (a->q_head_stride < qrows * a->d) return fail(BSA_EINVAL, "q_head_stride below nqb*block*d");
+    if (a->q && a->q_head_stride < qrows * a->d) return fail(BSA_EINVAL, "q_head_stride below nqb*block*d");
     if (a->k_head_stride < krows * a->d) return fail(BSA_EINVAL, "k_head_stride below nkb*block*d");
     const int eb = dtype_bytes(a->dtype);
     if (!aligned16(a->q) || !aligned16(a->k) || (a->q_head_stride * eb) % 16 || (a->k_head_stride * eb) % 16)
         return fail(BSA_EINVAL, "q/k pointers and head strides must be 16-byte aligned");
+    if (a->qpool) {
+        if (!aligned16(a->qpool) || a->qpool_head_stride % 2)
+            return fail(BSA_EINVAL, "qpool and its head stride must be 16-byte aligned");
+        if (a->qpool_head_stride < (int64_t)a->nqb * a->d) return fail(BSA_EINVAL, "qpool_head_stride below nqb*d");
+    }
     if (!(a->scale > 0.0) || a->scale > 1.0e300) return fail(BSA_EINVAL, "scale must be finite and > 0");
     if (a->overlap) {
         if (a->overlap_row_stride < n_cand) return fail(BSA_EINVAL, "overlap_row_stride below the candidate count");

@@ -39,7 +39,7 @@ from typing import Optional
 import torch
 
 from . import (_check, _lib, _ptr, _stream, block_sparse_attn, dense_attn, gilbert_block_window, gilbert_index,
-               gilbert_perm, gilbert_tile_index, materialize_capacity, route_capacity, route_materialize, route_topk,
+               gilbert_perm, gilbert_perm_pool, gilbert_tile_index, materialize_capacity, route_capacity, route_materialize, route_topk,
                tile_block_window, tile_perm)
 
 
@@ -102,6 +102,8 @@ class RoutedAttention:
         self.use_kpool = use_kpool
         self.kpool = torch.empty((heads, nkb_max, d), dtype=torch.float64, device=device) if use_kpool else None
         self._kpool_valid = 0
+        # pooled queries of the current chunk, written by the permutation
+        self.qbar = torch.empty((heads, self.nbc, d), dtype=torch.float64, device=device)
         # materialised routes: window rows of the current chunk, lists and
         # workspace (allocated on first use)
         self.window = torch.empty((self.nbc, 2 * self.nbc), dtype=torch.int32, device=device)
@@ -132,11 +134,31 @@ class RoutedAttention:
         return gilbert_perm(src, self.perm, block=self.block, inverse=True, dst=dst, stream=stream)
 
     def append(self, k_raster, v_raster, c: int, stream=None):
-        """Permute a chunk's raster K and V into slot ``c`` of the store."""
+        """Permute a chunk's raster K and V into slot ``c`` of the store; with
+        the pooled-key cache (curve blocks), the chunk's pooled keys are
+        written into it by the same pass."""
         ks, vs = self.slot(c)
-        self.invalidate_kpool(c * self.nbc)
-        self.to_blocks(k_raster, ks, stream)
+        b0 = c * self.nbc
+        self.invalidate_kpool(b0)
+        if self.use_kpool and self.tile is None:
+            gilbert_perm_pool(k_raster, self.perm, block=self.block, dst=ks, pool=self.kpool[:, b0:b0 + self.nbc],
+                              stream=stream)
+            if self._kpool_valid == b0:
+                self._kpool_valid = b0 + self.nbc
+        else:
+            self.to_blocks(k_raster, ks, stream)
         self.to_blocks(v_raster, vs, stream)
+
+    def permute_inputs(self, q_raster, k_raster, v_raster, c: int, stream=None):
+        """Append chunk ``c``'s K and V to the store and permute its queries
+        into ``q_blk``.  With curve blocks the queries' block means are
+        written by the same pass: returns them (``qbar``), else None."""
+        self.append(k_raster, v_raster, c, stream)
+        if self.tile is not None:
+            self.to_blocks(q_raster, self.q_blk, stream)
+            return None
+        gilbert_perm_pool(q_raster, self.perm, block=self.block, dst=self.q_blk, pool=self.qbar, stream=stream)
+        return self.qbar
 
     def step(self, q_raster, k_raster, v_raster, c: int, *, k_fixed: Optional[int] = None,
              k_per_row: Optional[torch.Tensor] = None, overlap: Optional[torch.Tensor] = None,
@@ -152,31 +174,33 @@ class RoutedAttention:
         materialised lists instead of a top-K."""
         if refresh_index:
             self._index(stream)
-        self.append(k_raster, v_raster, c, stream)
-        self.to_blocks(q_raster, self.q_blk, stream)
+        qpool = self.permute_inputs(q_raster, k_raster, v_raster, c, stream)
         r = self.route_and_attend(c, k_fixed=k_fixed, k_per_row=k_per_row, overlap=overlap, lam=lam, g_ref=g_ref,
-                                  tau=tau, materialize=materialize, stream=stream, attn_events=attn_events)
+                                  tau=tau, materialize=materialize, qpool=qpool, stream=stream,
+                                  attn_events=attn_events)
         self.to_raster(self.o_blk, self.o_raster, stream)
         return self.o_raster, r
 
     def route_and_attend(self, c: int, *, k_fixed: Optional[int] = None, k_per_row: Optional[torch.Tensor] = None,
                          overlap: Optional[torch.Tensor] = None, lam=2.0, g_ref=0.2, tau=0.1,
-                         materialize: Optional[dict] = None, stream=None, attn_events=None):
+                         materialize: Optional[dict] = None, qpool=None, stream=None, attn_events=None):
         """Route the already permuted queries over chunks 0..c of the store
-        and attend; the result stays in Gilbert layout (``o_blk``, ``lse``)."""
+        and attend; the result stays in Gilbert layout (``o_blk``, ``lse``).
+        ``qpool``: their pooled means, when already computed."""
         nkb = (c + 1) * self.nbc
         k_hist, v_hist = self.k_store[:, : nkb * self.block], self.v_store[:, : nkb * self.block]
         if materialize is not None:
-            r = self.route_materialized(c, overlap=overlap, lam=lam, g_ref=g_ref, tau=tau, stream=stream,
-                                        **materialize)
+            r = self.route_materialized(c, overlap=overlap, lam=lam, g_ref=g_ref, tau=tau, qpool=qpool,
+                                        stream=stream, **materialize)
             return self._attend(r, nkb, k_hist, v_hist, stream, attn_events)
         r = self.route(c, k_fixed=k_fixed, k_per_row=k_per_row, overlap=overlap, lam=lam, g_ref=g_ref, tau=tau,
-                       stream=stream)
+                       qpool=qpool, stream=stream)
         return self._attend(r, nkb, k_hist, v_hist, stream, attn_events)
 
     def route(self, c: int, *, k_fixed: Optional[int] = None, k_per_row: Optional[torch.Tensor] = None,
-              overlap: Optional[torch.Tensor] = None, lam=2.0, g_ref=0.2, tau=0.1, stream=None):
-        """Top-K routes of the already permuted queries over chunks 0..c."""
+              overlap: Optional[torch.Tensor] = None, lam=2.0, g_ref=0.2, tau=0.1, qpool=None, stream=None):
+        """Top-K routes of the already permuted queries over chunks 0..c
+        (``qpool``: their pooled means, when already computed)."""
         nkb = (c + 1) * self.nbc
         k_hist = self.k_store[:, : nkb * self.block]
         tail = self.n_dense_tail_chunks * self.nbc
@@ -187,7 +211,7 @@ class RoutedAttention:
                        q_block_len=self.q_len, kv_block_len=self.kv_len[:nkb], overlap=overlap, lam=lam,
                        g_ref=g_ref, tau=tau, k_fixed=kf, k_per_row=k_per_row,
                        k_max=self.k_cap if k_per_row is not None else None, n_dense_tail_blocks=tail,
-                       kpool=self.kpool, kpool_valid_blocks=valid if self.use_kpool else 0,
+                       kpool=self.kpool, kpool_valid_blocks=valid if self.use_kpool else 0, qpool=qpool,
                        out=self.route_out, workspace=self.workspace, stream=stream)
         self.workspace = r["workspace"]
         if self.use_kpool:
@@ -196,7 +220,7 @@ class RoutedAttention:
 
     def route_materialized(self, c: int, *, coverage=None, eta_cov=0.9, k_cov=80, k_unc=150, mass=0.9,
                            ref_blocks=(0, 0), window: bool = True, overlap=None, lam=2.0, g_ref=0.2, tau=0.1,
-                           stream=None):
+                           qpool=None, stream=None):
         """Materialised routes of the current queries over chunks 0..c:
         chunk c-1 is the reserved previous chunk; the local window of chunk
         c is rebuilt into the preallocated rows first."""
@@ -221,7 +245,7 @@ class RoutedAttention:
                               g_ref=g_ref, tau=tau, coverage=coverage, eta_cov=eta_cov, k_cov=k_cov, k_unc=k_unc,
                               mass=mass, prev_blocks=prev, window=self.window if window else None,
                               window_len=self.window_len if window else None, ref_blocks=ref_blocks,
-                              kpool=self.kpool, kpool_valid_blocks=valid if self.use_kpool else 0,
+                              kpool=self.kpool, kpool_valid_blocks=valid if self.use_kpool else 0, qpool=qpool,
                               out=self.mat_out, workspace=self.mat_workspace, stream=stream)
         self.mat_workspace = r["workspace"]
         if self.use_kpool:

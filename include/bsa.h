@@ -112,6 +112,30 @@ int bsa_gilbert_perm(const void* src, void* dst, const int32_t* perm, int L, int
                      int inverse, int dtype, hipStream_t stream);
 
 /*
+ * bsa_gilbert_perm_pool -- the forward permutation of bsa_gilbert_perm
+ * (inverse = 0) and, in the same pass, the mean of every block's valid
+ * rows, for the router's pooled queries or pooled-key cache.
+ * [Velox -- Methodology, Step 4 (mean query and mean key vectors per
+ *  block); Key Contributions 3; Methodology, Step 6]
+ *
+ * src, dst, perm, L, heads, d, block, raster_token_stride,
+ * gilbert_head_stride, dtype   as bsa_gilbert_perm with inverse = 0.
+ * pool           device float64: block b of head h (b < n_blocks =
+ *                ceil(L / block)) receives, at pool[h * pool_head_stride +
+ *                b * d + c], the mean over the block's valid rows (rows
+ *                i < L) of channel c, summed in float64 (the same value as
+ *                the router pools from dst).  pool may be a slice of a
+ *                larger cache (pool_head_stride >= n_blocks * d, in
+ *                elements); it must not overlap src or dst.
+ * Errors: those of bsa_gilbert_perm; BSA_EINVAL (pool NULL or not 8-byte
+ * aligned, pool_head_stride too small, heads > 65535, pool overlapping src
+ * or dst).
+ */
+int bsa_gilbert_perm_pool(const void* src, void* dst, const int32_t* perm, int L, int heads, int d, int block,
+                          int64_t raster_token_stride, int64_t gilbert_head_stride, int dtype, double* pool,
+                          int64_t pool_head_stride, hipStream_t stream);
+
+/*
  * Router arguments.  Set struct_size = sizeof(bsa_route_args).
  * [Velox -- Methodology, Step 4 (importance from mean query and mean key
  *  vectors; overlap above tau rescaled and applied as (1 + lambda * g_hat),
@@ -149,6 +173,11 @@ int bsa_gilbert_perm(const void* src, void* dst, const int32_t* perm, int L, int
  *  kpool_head_blocks  blocks per head of the cache (its head stride is
  *                 kpool_head_blocks*d); 0 means n_candidates.  Must be 0 or
  *                 >= n_candidates, so one cache can serve a growing history.
+ *  qpool          float64 pooled queries (NULL: pool q): entry (h, i, c) at
+ *                 qpool[h * qpool_head_stride + i * d + c] is the mean of
+ *                 query block i's valid rows, as bsa_gilbert_perm_pool
+ *                 writes it.  When given, q is not read and may be NULL.
+ *  qpool_head_stride  elements between heads of qpool (>= nqb*d).
  * Outputs (device):
  *  row_ptr        int32[heads*nqb + 1]; row r = h*nqb + i.
  *  col_idx        int32[col_capacity]; row r's list is col_idx[row_ptr[r] ..
@@ -200,6 +229,8 @@ typedef struct bsa_route_args {
     int64_t col_capacity;
     int32_t* fallback_counts;
     double* sel_keys;
+    const double* qpool;
+    int64_t qpool_head_stride;
 } bsa_route_args;
 
 /* Bytes of workspace bsa_route_topk needs for these arguments (0 if the

@@ -71,6 +71,22 @@ def test_gilbert_perm_rejects():
         == bsa.BSA_EINVAL
 
 
+def test_gilbert_perm_pool_rejects():
+    f = lib.bsa_gilbert_perm_pool
+    POOL = ctypes.c_void_p(0x40000000)
+    ok = (FAKE, FAKE2, FAKE, 4680, 40, 128, 128, 5120, 4736 * 128, 0)
+    assert f(*ok, None, 37 * 128, None) == bsa.BSA_EINVAL                     # no pool
+    assert f(*ok, POOL, 37 * 128 - 1, None) == bsa.BSA_EINVAL                 # pool head stride too small
+    assert "pool_head_stride" in lib.bsa_last_error_detail().decode()
+    assert f(*ok, ctypes.c_void_p(0x40000004), 37 * 128, None) == bsa.BSA_EINVAL   # misaligned pool
+    assert f(*ok, ctypes.c_void_p(0x20000000 + 4096), 37 * 128, None) == bsa.BSA_EINVAL   # pool inside dst
+    assert "overlaps" in lib.bsa_last_error_detail().decode()
+    assert f(FAKE, FAKE2, FAKE, 4680, 40, 96, 128, 5120, 4736 * 128, 0, POOL, 37 * 128, None) \
+        == bsa.BSA_EUNSUPPORTED                                               # the permutation's own checks
+    assert f(FAKE, FAKE2, FAKE, 4680, 70000, 128, 128, 70000 * 128, 4736 * 128, 0, POOL, 37 * 128, None) \
+        == bsa.BSA_EINVAL                                                     # heads beyond the grid
+
+
 def _attn(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, dtype=0, heads=40, d=128, block=128, nqb=37, nkb=1776,
              qhs=37 * 128 * 128, khs=1776 * 128 * 128, vhs=1776 * 128 * 128, ohs=37 * 128 * 128, ql=None,
@@ -140,6 +156,14 @@ def test_route_rejects_and_sizes():
                               None) == bsa.BSA_EINVAL
     assert lib.bsa_route_topk(ctypes.byref(_route_args(k_per_row=0x70000, k_max=-1)), FAKE, need, None) \
         == bsa.BSA_EINVAL
+    # pooled queries: q may then be NULL; the stride must cover the blocks
+    assert lib.bsa_route_topk(ctypes.byref(_route_args(q=None)), FAKE, need, None) == bsa.BSA_EINVAL
+    assert lib.bsa_route_topk(ctypes.byref(_route_args(q=None, qpool=0x90000, qpool_head_stride=37 * 128 - 2)),
+                              FAKE, need, None) == bsa.BSA_EINVAL
+    assert lib.bsa_route_topk(ctypes.byref(_route_args(qpool=0x90008, qpool_head_stride=37 * 128)), FAKE, need,
+                              None) == bsa.BSA_EINVAL
+    assert lib.bsa_route_topk(ctypes.byref(_route_args(q=None, qpool=0x90000, qpool_head_stride=37 * 128)),
+                              None, 0, None) == bsa.BSA_EWORKSPACE                # valid up to the workspace
     # kpool and sel_keys shrink the workspace
     small = lib.bsa_route_workspace_size(ctypes.byref(_route_args(kpool=0x60000, sel_keys=0x80000)))
     assert 0 < small < need

@@ -72,6 +72,57 @@ def test_permute_into_store_slot_and_token_stride():
     assert torch.equal(out[:, 1], k_raster) and torch.all(out[:, 0] == 0)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("block,d", [(128, 128), (64, 128), (64, 64), (128, 64)])
+def test_permute_pool_bitwise_and_exact_means(dtype, block, d):
+    """The fused pass writes the same bits as the plain permutation and the
+    oracle's block means of the permuted rows, exactly (ragged last block)."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    from oracle import route as oroute
+    T, H, W = 3, 30, 52
+    L, heads = T * H * W, 3
+    src = torch.randn((L, heads, d), generator=torch.Generator().manual_seed(12)).to(dtype)
+    perm, _ = bsa.gilbert_index(T, H, W, device=dev)
+    dst, pool = bsa.gilbert_perm_pool(src.to(dev), perm, block=block)
+    plain = bsa.gilbert_perm(src.to(dev), perm, block=block)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, plain)
+    ref = olay.permute_forward(f64(src), gilbert_order(T, H, W)[0], block)
+    lens = olay.chunk_block_lengths(L, block)
+    assert lens[-1] < block
+    for h in range(heads):
+        assert np.array_equal(pool[h].cpu().numpy(), oroute.pool_blocks(ref[h], lens, block)), h
+
+
+def test_permute_pool_into_cache_slice():
+    """K of one chunk into a store slot and its means into the matching
+    slice of a pooled-key cache (both head-strided views); the rest of the
+    store and of the cache is untouched, and a raster tensor with a wider
+    token stride is read correctly."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    from oracle import route as oroute
+    T, H, W = 3, 30, 52
+    L, heads, d, block = T * H * W, 4, 128, 128
+    nbc = -(-L // block)
+    fused = torch.randn((L, 3, heads, d), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(dev)
+    k_raster = fused[:, 1]
+    store = torch.full((heads, 3 * nbc * block, d), 7.0, dtype=torch.bfloat16, device=dev)
+    cache = torch.full((heads, 3 * nbc, d), -1.0, dtype=torch.float64, device=dev)
+    perm, _ = bsa.gilbert_index(T, H, W, device=dev)
+    slot = store[:, nbc * block: 2 * nbc * block]
+    bsa.gilbert_perm_pool(k_raster, perm, block=block, dst=slot, pool=cache[:, nbc: 2 * nbc])
+    torch.cuda.synchronize()
+    ref = olay.permute_forward(f64(k_raster), gilbert_order(T, H, W)[0], block)
+    assert np.array_equal(f64(slot), ref)
+    lens = olay.chunk_block_lengths(L, block)
+    for h in range(heads):
+        assert np.array_equal(cache[h, nbc: 2 * nbc].cpu().numpy(), oroute.pool_blocks(ref[h], lens, block))
+    assert torch.all(store[:, : nbc * block] == 7.0) and torch.all(store[:, 2 * nbc * block:] == 7.0)
+    assert torch.all(cache[:, :nbc] == -1.0) and torch.all(cache[:, 2 * nbc:] == -1.0)
+
+
 def test_index_large_grid():
     dev = need_gpu()
     import block_sparse_attention_gilbert_amd as bsa

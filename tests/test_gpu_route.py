@@ -126,6 +126,28 @@ def test_pooled_key_cache_incremental():
         assert np.array_equal(cache[h].cpu().numpy(), ref["kbar"])   # exact block means
 
 
+def test_routes_from_pooled_queries():
+    """Routing from the pooled queries of the fused permutation (q not
+    read) gives the lists of routing from the permuted queries."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    w = workloads.c4(c=3, heads=[0, 1])
+    perm, _ = bsa.gilbert_index(3, 30, 52, device=dev)
+    q_raster = bsa.gilbert_perm(w.q.to(dev), perm, block=128, inverse=True)
+    q_blk, qbar = bsa.gilbert_perm_pool(q_raster, perm, block=128)
+    ql = torch.from_numpy(w.q_len).to(dev)
+    kl = torch.from_numpy(w.k_len).to(dev)
+    kw = dict(block=128, nqb=37, nkb=w.nkb, scale=w.scale, q_block_len=ql, kv_block_len=kl, k_fixed=50)
+    r_q = bsa.route_topk(q_blk, w.k.to(dev), **kw)
+    lists_q = csr_lists(r_q["row_ptr"], r_q["col_idx"], w.heads, 37)
+    garbage = torch.full_like(q_blk, float("nan"))          # must not be read
+    r_p = bsa.route_topk(garbage, w.k.to(dev), qpool=qbar, **kw)
+    lists_p = csr_lists(r_p["row_ptr"], r_p["col_idx"], w.heads, 37)
+    for h in range(w.heads):
+        assert_lists_equal(lists_p[h], lists_q[h], "pooled queries head %d" % h)
+        assert_lists_equal(lists_p[h], _oracle_head(w, h)["lists"], "oracle head %d" % h)
+
+
 def test_pooled_key_cache_grows_with_history():
     """One cache with a fixed head stride serves a history that grows by a
     chunk per call: each call pools only the appended chunk."""
