@@ -193,8 +193,8 @@ def breakdown(st, reps: int):
     """Each stage of the step alone (median of ``reps`` calls), with its
     algorithmic bytes and the GB/s that gives: the Gilbert index, the three
     forward permutations (Q and K with their block means, V), the router
-    over the pooled blocks, the attention launch, the inverse permutation
-    of O."""
+    over the pooled blocks, the attention launch (its epilogue writes O in
+    raster order, so there is no separate inverse permutation)."""
     import torch
     w, ra = st["w"], st["ra"]
     cur = st["cur"]
@@ -223,8 +223,7 @@ def breakdown(st, reps: int):
         "gilbert_index": (lambda: ra._index(), 4 * 2 * L),
         "forward_permutes": (fwd, 3 * (raster + blocked) + 2 * pooled),
         "route": (route, route_bytes),
-        "attention": (lambda: ra._attend(r, nkb, k_hist, v_hist, None, None), wc["alg_bytes"]),
-        "inverse_permute": (lambda: ra.to_raster(ra.o_blk, ra.o_raster), raster + blocked),
+        "attention": (lambda: ra._attend(r, nkb, k_hist, v_hist, None, None, True), wc["alg_bytes"]),
     }
     out = {}
     for name, (fn, nbytes) in stages.items():
@@ -233,7 +232,8 @@ def breakdown(st, reps: int):
     # the same attention launch with L2 and the 256 MB MALL flushed before
     # each call (a 512 MB write, untimed, right before it)
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=ra.device)
-    ms = _time_ms(lambda: ra._attend(r, nkb, k_hist, v_hist, None, None), reps, between=lambda: scrub.fill_(1))
+    ms = _time_ms(lambda: ra._attend(r, nkb, k_hist, v_hist, None, None, True), reps,
+                  between=lambda: scrub.fill_(1))
     del scrub
     out["attention_cold_ms"] = round(ms, 4)
     return out
@@ -537,13 +537,11 @@ def profile_attention(launches: int, expect_out=None):
     run_step(st)
     torch.cuda.synchronize()
     # attention only, on the routed lists of the step above
-    from block_sparse_attention_gilbert_amd import block_sparse_attn
     nkb = ra.store_chunks * ra.nbc
     r = ra.route_out
-    for _ in range(launches):
-        block_sparse_attn(ra.q_blk, ra.k_store[:, : nkb * ra.block], ra.v_store[:, : nkb * ra.block], r["row_ptr"],
-                          r["col_idx"], block=ra.block, scale=ra.scale, q_block_len=ra.q_len,
-                          kv_block_len=ra.kv_len[:nkb], out=ra.o_blk, lse=ra.lse)
+    k_hist, v_hist = ra.k_store[:, : nkb * ra.block], ra.v_store[:, : nkb * ra.block]
+    for _ in range(launches):       # as in the step: output straight to raster order
+        ra._attend(r, nkb, k_hist, v_hist, None, None, out_raster=True)
     for _ in range(2):  # dense attention over the same history, for comparison counters
         ra.dense(st["cur"])
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
@@ -666,7 +664,8 @@ def main():
                     help="skip timing the slab geometry and the step with the materialised route")
     ap.add_argument("--sweep", default=None, help="write a chunk 1..C sparse/dense sweep to this JSONL file")
     ap.add_argument("--rollout", default=None,
-                    help="write a 1..C chunk rollout (append, route with the pooled-key cache, attend) to this JSONL file")
+                    help="write a 1..C chunk rollout (append, route with the pooled-key cache, attend) "
+                         "to this JSONL file")
     ap.add_argument("--profile-attention", type=int, default=0, metavar="N",
                     help="counter mode: N attention launches + a 1 GiB copy, no JSON line")
     ap.add_argument("--expect-out", default=None, metavar="JSON",

@@ -114,6 +114,9 @@ _lib.bsa_route_topk.argtypes = [ctypes.POINTER(RouteArgs), _p, ctypes.c_size_t, 
 _ATTN_COMMON = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p]
 _lib.bsa_block_sparse_attn.restype = _i
 _lib.bsa_block_sparse_attn.argtypes = _ATTN_COMMON + [_p, _p, _i64, _f, _p]
+_lib.bsa_block_sparse_attn_raster.restype = _i
+_lib.bsa_block_sparse_attn_raster.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _p, _i,
+                                              _i64, _p, _p, _p, _p, _i64, _f, _p]
 _lib.bsa_dense_attn.restype = _i
 _lib.bsa_dense_attn.argtypes = _ATTN_COMMON + [_f, _p]
 
@@ -121,7 +124,8 @@ EXPORTED = ("bsa_version", "bsa_strerror", "bsa_last_error_detail", "bsa_gilbert
             "bsa_gilbert_perm_pool", "bsa_gilbert_block_window", "bsa_gilbert_tile_index", "bsa_tile_perm",
             "bsa_tile_block_window", "bsa_route_workspace_size", "bsa_route_topk",
             "bsa_route_materialize_workspace_size", "bsa_route_materialize", "bsa_slab_overlap", "bsa_slab_coverage",
-            "bsa_slab_coverage_workspace_size", "bsa_block_sparse_attn", "bsa_dense_attn", "bsa_diag_mfma_bf16")
+            "bsa_slab_coverage_workspace_size", "bsa_block_sparse_attn", "bsa_block_sparse_attn_raster",
+            "bsa_dense_attn", "bsa_diag_mfma_bf16")
 
 
 class BsaError(RuntimeError):
@@ -629,6 +633,31 @@ def block_sparse_attn(q, k, v, row_ptr, col_idx, *, block: int, scale: Optional[
     return out, lse
 
 
+def block_sparse_attn_raster(q, k, v, row_ptr, col_idx, row_map, *, block: int, scale: Optional[float] = None,
+                             q_block_len=None, kv_block_len=None, out=None, tokens: Optional[int] = None, lse=None,
+                             nkb: Optional[int] = None, stream=None):
+    """``block_sparse_attn`` with the output written in raster token order:
+    query row g goes to token ``row_map[g]`` of ``out`` ``[tokens][heads][d]``
+    (negative entries: padding, not written).  ``tokens`` defaults to
+    ``row_map.numel()`` when ``out`` is allocated here.  Returns ``(O, LSE)``
+    (LSE in the blocked layout)."""
+    _need_gpu(row_ptr, col_idx, row_map, out)
+    d, heads, nqb, nkb_, qhs, khs, vhs, _, _, lse = _attn_prep(q, k, v, q, lse, block)
+    nkb = nkb_ if nkb is None else nkb
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    row_map = _i32(row_map, "row_map")
+    if out is None:
+        out = torch.empty((row_map.numel() if tokens is None else tokens, heads, d), dtype=q.dtype, device=q.device)
+    if out.dim() != 3 or out.shape[1] != heads or out.shape[2] != d or out.stride(2) != 1 or out.stride(1) != d:
+        raise ValueError("raster out must be [tokens][heads][d] with contiguous [heads][d] per token")
+    _check(_lib.bsa_block_sparse_attn_raster(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), heads, d, block, nqb, nkb, qhs, khs,
+        vhs, _ptr(row_map), row_map.numel(), out.stride(0), _ptr(_i32(q_block_len, "q_block_len")),
+        _ptr(_i32(kv_block_len, "kv_block_len")), _ptr(_i32(row_ptr, "row_ptr")), _ptr(_i32(col_idx, "col_idx")),
+        col_idx.numel(), scale, _stream(stream)))
+    return out, lse
+
+
 def dense_attn(q, k, v, *, block: int, scale: Optional[float] = None, q_block_len=None, kv_block_len=None,
                out=None, lse=None, nkb: Optional[int] = None, stream=None):
     """Dense attention over every KV block, through the same kernel."""
@@ -645,6 +674,6 @@ def dense_attn(q, k, v, *, block: int, scale: Optional[float] = None, q_block_le
 __all__ = ["gilbert_index", "gilbert_perm", "gilbert_perm_pool", "gilbert_block_window", "gilbert_tile_index",
            "tile_perm", "tile_block_window", "tile_grid", "slab_overlap", "slab_coverage", "route_topk",
            "route_workspace_size", "route_capacity", "route_materialize", "route_materialize_workspace_size",
-           "materialize_capacity", "MaterializeArgs", "block_sparse_attn", "dense_attn", "version", "library",
-           "BsaError", "RouteArgs", "EXPORTED", "BSA_OK", "BSA_EINVAL", "BSA_EUNSUPPORTED", "BSA_EWORKSPACE",
-           "BSA_EHIP", "BSA_BF16", "BSA_F32"]
+           "materialize_capacity", "MaterializeArgs", "block_sparse_attn", "block_sparse_attn_raster", "dense_attn",
+           "version", "library", "BsaError", "RouteArgs", "EXPORTED", "BSA_OK", "BSA_EINVAL", "BSA_EUNSUPPORTED",
+           "BSA_EWORKSPACE", "BSA_EHIP", "BSA_BF16", "BSA_F32"]

@@ -161,6 +161,24 @@ int bsa_block_sparse_attn(const void* q, const void* k, const void* v, void* o, 
     return hip_status(bsa::launch_attn(p, false, stream), "block_sparse_attn launch");
 }
 
+int bsa_block_sparse_attn_raster(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
+                                 int heads, int d, int block, int nqb, int nkb, int64_t q_head_stride,
+                                 int64_t k_head_stride, int64_t v_head_stride, const int32_t* o_row_map, int o_rows,
+                                 int64_t o_token_stride, const int32_t* q_block_len, const int32_t* kv_block_len,
+                                 const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len, float scale,
+                                 hipStream_t stream) {
+    bsa::clear_error();
+    // the blocked output stride is not used; the raster layout is checked below
+    bsa::AttnProblem p{q,      k,     v,    o,       lse,          dtype,        heads,   d,       block,
+                       nqb,    nkb,   q_head_stride, k_head_stride, v_head_stride, (int64_t)nqb * block * d,
+                       q_block_len, kv_block_len, row_ptr, col_idx, col_len, scale, o_row_map, o_rows,
+                       o_token_stride};
+    int st = bsa::validate_attn(p, false);
+    if (st == BSA_OK) st = bsa::validate_raster_out(p);
+    if (st != BSA_OK) return st;
+    return hip_status(bsa::launch_attn(p, false, stream), "block_sparse_attn_raster launch");
+}
+
 int bsa_dense_attn(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int heads, int d,
                    int block, int nqb, int nkb, int64_t q_head_stride, int64_t k_head_stride,
                    int64_t v_head_stride, int64_t o_head_stride, const int32_t* q_block_len,

@@ -27,6 +27,8 @@
 // exponentials with the scale folded in), in fp32.  Padded keys are masked
 // to -inf, padded query rows are written as zeros, an empty list gives zeros
 // and LSE = -inf.  Waves whose 32 query rows are all padding skip the math.
+// The output rows can also go straight to raster token order through a row
+// map (the inverse of the forward permutation, fused into the epilogue).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -54,7 +56,22 @@ struct AttnArgs {
     int64_t col_len;
     float scale;       // natural-log scale of the scores
     float scale_log2;  // scale * log2(e)
+    // raster output (o_map non-NULL): query row g = i*BLK + r of head h goes
+    // to o[o_map[g] * o_ts + h * D] when g < o_map_len and o_map[g] >= 0;
+    // other rows (padding) are not written
+    const int32_t* o_map;
+    int o_map_len;
+    int64_t o_ts;
 };
+
+// Output row of (head h, query row g): the head-major blocked row, or the
+// raster token row through the map (nullptr: a padding row, not written).
+template <typename T>
+__device__ __forceinline__ T* out_row(const AttnArgs& a, int h, int64_t g, int D) {
+    if (!a.o_map) return static_cast<T*>(a.o) + h * a.o_hs + g * D;
+    const int t = g < a.o_map_len ? a.o_map[g] : -1;
+    return t < 0 ? nullptr : static_cast<T*>(a.o) + (int64_t)t * a.o_ts + (int64_t)h * D;
+}
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -333,11 +350,13 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
     if (jk < 0) {
         // empty list: zeros and -inf, no copies in flight
         const int qrow = q0 + l32;
-        uint16_t* Orow = static_cast<uint16_t*>(a.o) + h * a.o_hs + ((int64_t)i * BLK + qrow) * D;
+        uint16_t* Orow = out_row<uint16_t>(a, h, (int64_t)i * BLK + qrow, D);
+        if (Orow)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) *reinterpret_cast<uint2*>(Orow + dt * 32 + 8 * g + 4 * hi) = make_uint2(0u, 0u);
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<uint2*>(Orow + dt * 32 + 8 * g + 4 * hi) = make_uint2(0u, 0u);
         if (a.lse && hi == 0) a.lse[(int64_t)h * a.nqb * BLK + (int64_t)i * BLK + qrow] = -INFINITY;
         return;
     }
@@ -688,20 +707,24 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
     const int qrow = q0 + l32;
     const bool live = active && valid_row && lt > 0.f;
     const float inv = live ? 1.f / lt : 0.f;
-    uint16_t* Orow = static_cast<uint16_t*>(a.o) + h * a.o_hs + ((int64_t)i * BLK + qrow) * D;
+    uint16_t* Orow = out_row<uint16_t>(a, h, (int64_t)i * BLK + qrow, D);
+    if (Orow) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int dv = dt * 32 + 8 * g + 4 * hi;
-            __bf16 v4[4];
+            for (int g = 0; g < 4; ++g) {
+                const int dv = dt * 32 + 8 * g + 4 * hi;
+                __bf16 v4[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) v4[c] = live ? (__bf16)(o[dt][4 * g + c] * inv) : (__bf16)0.f;
-            uint2 packed;
-            packed.x = (uint32_t)__builtin_bit_cast(uint16_t, v4[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v4[1]) << 16);
-            packed.y = (uint32_t)__builtin_bit_cast(uint16_t, v4[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v4[3]) << 16);
-            *reinterpret_cast<uint2*>(Orow + dv) = packed;
-        }
+                for (int c = 0; c < 4; ++c) v4[c] = live ? (__bf16)(o[dt][4 * g + c] * inv) : (__bf16)0.f;
+                uint2 packed;
+                packed.x = (uint32_t)__builtin_bit_cast(uint16_t, v4[0]) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, v4[1]) << 16);
+                packed.y = (uint32_t)__builtin_bit_cast(uint16_t, v4[2]) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, v4[3]) << 16);
+                *reinterpret_cast<uint2*>(Orow + dv) = packed;
+            }
+    }
     if (a.lse && hi == 0)
         a.lse[(int64_t)h * a.nqb * BLK + (int64_t)i * BLK + qrow] = live ? (ref + log2f(lt)) * kLn2 : -INFINITY;
 }
@@ -775,9 +798,10 @@ __global__ void __launch_bounds__(BLK * (D / 32)) attn_f32_kernel(AttnArgs a) {
     }
     const bool live = qi < vq && l > 0.f;
     const float inv = live ? 1.f / l : 0.f;
-    float* orow = static_cast<float*>(a.o) + h * a.o_hs + ((int64_t)i * BLK + qi) * D + part * 32;
+    float* orow = out_row<float>(a, h, (int64_t)i * BLK + qi, D);
+    if (orow)
 #pragma unroll
-    for (int c = 0; c < 32; ++c) orow[c] = live ? o[c] * inv : 0.f;
+        for (int c = 0; c < 32; ++c) orow[part * 32 + c] = live ? o[c] * inv : 0.f;
     if (a.lse && part == 0)
         a.lse[(int64_t)h * a.nqb * BLK + (int64_t)i * BLK + qi] = live ? m + logf(l) : -INFINITY;
 }
@@ -821,6 +845,9 @@ hipError_t launch_attn(const AttnProblem& p, bool dense, hipStream_t stream) {
     a.col_len = p.col_len;
     a.scale = p.scale;
     a.scale_log2 = p.scale * 1.44269504088896340736f;
+    a.o_map = p.o_map;
+    a.o_map_len = p.o_map_len;
+    a.o_ts = p.o_ts;
     const int total = p.heads * p.nqb;
     if (p.block == 128 && p.d == 128) return launch_typed<128, 128>(a, p.dtype, dense, total, stream);
     if (p.block == 128 && p.d == 64) return launch_typed<128, 64>(a, p.dtype, dense, total, stream);

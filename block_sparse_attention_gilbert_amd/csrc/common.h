@@ -34,6 +34,9 @@ struct AttnProblem {
     const int32_t* col_idx;  // NULL for dense
     int64_t col_len;
     float scale;
+    const int32_t* o_map;  // raster output: row map (NULL: blocked output)
+    int o_map_len;
+    int64_t o_ts;          // raster token stride of o, elements
 };
 
 // Workspace layout of the router (byte offsets, 256-byte aligned).
@@ -51,6 +54,7 @@ int validate_gilbert_perm_pool(const void* src, const void* dst, const int32_t* 
                                int block, int64_t raster_token_stride, int64_t gilbert_head_stride, int dtype,
                                const double* pool, int64_t pool_head_stride);
 int validate_attn(const AttnProblem& p, bool dense);
+int validate_raster_out(const AttnProblem& p);
 int validate_route(const bsa_route_args* a, RouteLayout* lay);
 int validate_materialize(const bsa_route_args* a, const bsa_materialize_args* m, RouteLayout* lay);
 int validate_block_window(const int32_t* perm, const int32_t* inv, int T, int H, int W, int block, int q_chunk,

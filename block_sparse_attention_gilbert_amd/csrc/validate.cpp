@@ -90,6 +90,17 @@ int validate_gilbert_perm_pool(const void* src, const void* dst, const int32_t* 
     return BSA_OK;
 }
 
+int validate_raster_out(const AttnProblem& p) {
+    if (!p.o_map) return fail(BSA_EINVAL, "o_row_map must be non-NULL");
+    if (p.o_map_len < 1 || (int64_t)p.o_map_len > (int64_t)p.nqb * p.block)
+        return fail(BSA_EINVAL, "o_rows %d outside [1, nqb*block]", p.o_map_len);
+    if (p.o_ts < (int64_t)p.heads * p.d)
+        return fail(BSA_EINVAL, "o_token_stride %lld < heads*d = %lld", (long long)p.o_ts,
+                    (long long)p.heads * p.d);
+    if ((p.o_ts * dtype_bytes(p.dtype)) % 16) return fail(BSA_EINVAL, "o_token_stride must be 16-byte aligned");
+    return BSA_OK;
+}
+
 int validate_attn(const AttnProblem& p, bool dense) {
     if (!p.q || !p.k || !p.v || !p.o) return fail(BSA_EINVAL, "q, k, v and o must be non-NULL");
     if (!dense && (!p.row_ptr || !p.col_idx)) return fail(BSA_EINVAL, "row_ptr and col_idx must be non-NULL");

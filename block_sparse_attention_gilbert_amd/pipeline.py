@@ -14,9 +14,11 @@ Per call (``RoutedAttention.step``):
    [Light Interaction -- abstract: 3-D block-sparse attention];
 2. Q, K, V of the current chunk, raster token-major ``[L][heads][d]``, are
    permuted into Gilbert head-major block-padded layout; K and V land in the
-   current chunk's slot of the KV store (the store grows by appending);
-3. the router pools, scores, fuses and selects over the visible history.
-   The pooled keys of the history are kept in a float64 cache across calls
+   current chunk's slot of the KV store (the store grows by appending).  The
+   permutation of Q and K also writes their block means (the pooled
+   queries, and the chunk's rows of the pooled-key cache);
+3. the router scores, fuses and selects over the visible history.  The
+   pooled keys of the history are kept in a float64 cache across calls
    (the store only grows by appending), so a call pools only the blocks
    appended or rewritten since the previous call.  The selection is either
    a top-K per row, or the materialised route (``materialize=``): coverage-
@@ -24,8 +26,8 @@ Per call (``RoutedAttention.step``):
    prefix, and the chunk's local window in Gilbert block order (built on
    the GPU for each call) plus reference blocks [Velox -- Methodology,
    Step 5];
-4. block-sparse attention over the selected blocks;
-5. O is permuted back to raster order.
+4. block-sparse attention over the selected blocks, whose epilogue writes
+   O straight back in raster token order (the inverse permutation).
 
 Nothing here computes on the host: each step is one or more HIP kernels of
 ``libbsa.so`` on the current stream.
@@ -38,9 +40,9 @@ from typing import Optional
 
 import torch
 
-from . import (_check, _lib, _ptr, _stream, block_sparse_attn, dense_attn, gilbert_block_window, gilbert_index,
-               gilbert_perm, gilbert_perm_pool, gilbert_tile_index, materialize_capacity, route_capacity, route_materialize, route_topk,
-               tile_block_window, tile_perm)
+from . import (_check, _lib, _ptr, _stream, block_sparse_attn, block_sparse_attn_raster, dense_attn,
+               gilbert_block_window, gilbert_index, gilbert_perm, gilbert_perm_pool, gilbert_tile_index,
+               materialize_capacity, route_capacity, route_materialize, route_topk, tile_block_window, tile_perm)
 
 
 def block_lengths(tokens: int, block: int, n_chunks: int = 1, device="cuda") -> torch.Tensor:
@@ -176,26 +178,28 @@ class RoutedAttention:
             self._index(stream)
         qpool = self.permute_inputs(q_raster, k_raster, v_raster, c, stream)
         r = self.route_and_attend(c, k_fixed=k_fixed, k_per_row=k_per_row, overlap=overlap, lam=lam, g_ref=g_ref,
-                                  tau=tau, materialize=materialize, qpool=qpool, stream=stream,
+                                  tau=tau, materialize=materialize, qpool=qpool, out_raster=True, stream=stream,
                                   attn_events=attn_events)
-        self.to_raster(self.o_blk, self.o_raster, stream)
         return self.o_raster, r
 
     def route_and_attend(self, c: int, *, k_fixed: Optional[int] = None, k_per_row: Optional[torch.Tensor] = None,
                          overlap: Optional[torch.Tensor] = None, lam=2.0, g_ref=0.2, tau=0.1,
-                         materialize: Optional[dict] = None, qpool=None, stream=None, attn_events=None):
+                         materialize: Optional[dict] = None, qpool=None, out_raster: bool = False, stream=None,
+                         attn_events=None):
         """Route the already permuted queries over chunks 0..c of the store
-        and attend; the result stays in Gilbert layout (``o_blk``, ``lse``).
-        ``qpool``: their pooled means, when already computed."""
+        and attend; the result stays in Gilbert layout (``o_blk``, ``lse``),
+        or with ``out_raster`` goes straight to ``o_raster`` (``o_blk`` is
+        then not written).  ``qpool``: their pooled means, when already
+        computed."""
         nkb = (c + 1) * self.nbc
         k_hist, v_hist = self.k_store[:, : nkb * self.block], self.v_store[:, : nkb * self.block]
         if materialize is not None:
             r = self.route_materialized(c, overlap=overlap, lam=lam, g_ref=g_ref, tau=tau, qpool=qpool,
                                         stream=stream, **materialize)
-            return self._attend(r, nkb, k_hist, v_hist, stream, attn_events)
-        r = self.route(c, k_fixed=k_fixed, k_per_row=k_per_row, overlap=overlap, lam=lam, g_ref=g_ref, tau=tau,
-                       qpool=qpool, stream=stream)
-        return self._attend(r, nkb, k_hist, v_hist, stream, attn_events)
+        else:
+            r = self.route(c, k_fixed=k_fixed, k_per_row=k_per_row, overlap=overlap, lam=lam, g_ref=g_ref, tau=tau,
+                           qpool=qpool, stream=stream)
+        return self._attend(r, nkb, k_hist, v_hist, stream, attn_events, out_raster)
 
     def route(self, c: int, *, k_fixed: Optional[int] = None, k_per_row: Optional[torch.Tensor] = None,
               overlap: Optional[torch.Tensor] = None, lam=2.0, g_ref=0.2, tau=0.1, qpool=None, stream=None):
@@ -252,13 +256,20 @@ class RoutedAttention:
             self._kpool_valid = max(valid, nkb)
         return r
 
-    def _attend(self, r, nkb, k_hist, v_hist, stream, attn_events):
+    def _attend(self, r, nkb, k_hist, v_hist, stream, attn_events, out_raster=False):
         if attn_events is not None:
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             ev[0].record(stream)
-        block_sparse_attn(self.q_blk, k_hist, v_hist, r["row_ptr"], r["col_idx"], block=self.block,
-                          scale=self.scale, q_block_len=self.q_len, kv_block_len=self.kv_len[:nkb],
-                          out=self.o_blk, lse=self.lse, stream=stream)
+        if out_raster:
+            # the inverse permutation in the kernel's epilogue: row g -> token row_map[g]
+            row_map = self.perm if self.tile is None else self.row_cell
+            block_sparse_attn_raster(self.q_blk, k_hist, v_hist, r["row_ptr"], r["col_idx"], row_map,
+                                     block=self.block, scale=self.scale, q_block_len=self.q_len,
+                                     kv_block_len=self.kv_len[:nkb], out=self.o_raster, lse=self.lse, stream=stream)
+        else:
+            block_sparse_attn(self.q_blk, k_hist, v_hist, r["row_ptr"], r["col_idx"], block=self.block,
+                              scale=self.scale, q_block_len=self.q_len, kv_block_len=self.kv_len[:nkb],
+                              out=self.o_blk, lse=self.lse, stream=stream)
         if attn_events is not None:
             ev[1].record(stream)
             attn_events.append(ev)

@@ -529,6 +529,37 @@ int bsa_block_sparse_attn(const void* q, const void* k, const void* v, void* o, 
                           hipStream_t stream);
 
 /*
+ * bsa_block_sparse_attn_raster -- bsa_block_sparse_attn with the output
+ * written straight into raster token order (the inverse permutation fused
+ * into the kernel's epilogue).
+ * [Velox -- Methodology, Step 6; Key Contributions 3 (Gilbert KV storage,
+ *  outputs returned in the caller's order)]
+ *
+ *  o_row_map      device int32[o_rows], o_rows <= nqb*block: query row g
+ *                 (of every head) goes to raster token o_row_map[g]; a
+ *                 negative entry marks a padding row, which is not written.
+ *                 For blocks that are runs of the curve this is the curve
+ *                 itself (perm of bsa_gilbert_index, o_rows = T*H*W); for
+ *                 fixed tiles it is the row map of bsa_gilbert_tile_index.
+ *                 Entries must be distinct and index tokens of o.
+ *  o              raster output in dtype: element (token t, head h, channel
+ *                 c) at o[t * o_token_stride + h * d + c]; tokens that no
+ *                 row maps to are left untouched.
+ * Every other argument, the lse layout (blocked, [heads][nqb*block]) and the
+ * values written are those of bsa_block_sparse_attn.
+ * Errors: those of bsa_block_sparse_attn; BSA_EINVAL (o_row_map NULL,
+ * o_rows outside [1, nqb*block], o_token_stride below heads*d or not a
+ * multiple of 16 bytes).
+ */
+int bsa_block_sparse_attn_raster(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int dtype, int heads, int d, int block, int nqb, int nkb,
+                                 int64_t q_head_stride, int64_t k_head_stride, int64_t v_head_stride,
+                                 const int32_t* o_row_map, int o_rows, int64_t o_token_stride,
+                                 const int32_t* q_block_len, const int32_t* kv_block_len,
+                                 const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
+                                 float scale, hipStream_t stream);
+
+/*
  * bsa_dense_attn -- the dense baseline: bsa_block_sparse_attn with every KV
  * block listed in ascending order, through the same kernel.
  * [Velox -- Main Findings: dense attention over all retained context]

@@ -115,6 +115,20 @@ def test_attention_rejects():
     assert d == bsa.BSA_EINVAL
 
 
+def test_raster_attention_rejects():
+    def f(o_map=FAKE, o_rows=4680, o_ts=40 * 128, d=128):
+        return lib.bsa_block_sparse_attn_raster(FAKE, FAKE, FAKE, FAKE2, None, 0, 40, d, 128, 37, 1776,
+                                                37 * 128 * 128, 1776 * 128 * 128, 1776 * 128 * 128, o_map, o_rows,
+                                                o_ts, None, None, FAKE, FAKE, 1480 * 50, ctypes.c_float(0.088), None)
+    assert f(o_map=None) == bsa.BSA_EINVAL
+    assert "o_row_map" in lib.bsa_last_error_detail().decode()
+    assert f(o_rows=0) == bsa.BSA_EINVAL
+    assert f(o_rows=37 * 128 + 1) == bsa.BSA_EINVAL
+    assert f(o_ts=40 * 128 - 8) == bsa.BSA_EINVAL
+    assert f(o_ts=40 * 128 + 4) == bsa.BSA_EINVAL           # 8 bytes: breaks 16-byte token rows
+    assert f(d=80) == bsa.BSA_EUNSUPPORTED                   # the attention checks come first
+
+
 def _route_args(**over):
     a = bsa.RouteArgs()
     a.struct_size = ctypes.sizeof(bsa.RouteArgs)

@@ -140,6 +140,56 @@ def test_deterministic_and_padding_inert():
     assert torch.equal(o1, o4) and torch.equal(l1, l4)
 
 
+def _raster_case(name):
+    """(workload, row map, token count): the Gilbert curve for the C4 layout
+    (ragged last block), a seeded shuffle for C1 (fp32), and a map with
+    padding rows (-1, as in the tile layout) over C2's rows."""
+    import block_sparse_attention_gilbert_amd as bsa
+    g = torch.Generator().manual_seed(31)
+    if name == "curve":
+        w = workloads.c4(c=2, heads=[3, 4])
+        perm, _ = bsa.gilbert_index(3, 30, 52, device="cuda")
+        return w, perm, 4680
+    if name == "shuffle":
+        w = workloads.c1()
+        n = int(w.q_len.sum())
+        return w, torch.randperm(n, generator=g).to(torch.int32), n
+    w = workloads.c2(heads=[0, 5])
+    rows = w.nqb * w.bs
+    m = torch.randperm(rows, generator=g).to(torch.int32)
+    m[torch.randperm(rows, generator=g)[: rows // 10]] = -1        # padding rows: not written
+    return w, m, rows
+
+
+@pytest.mark.parametrize("name", ["curve", "shuffle", "padding"])
+def test_raster_output_is_the_blocked_output_permuted(name):
+    """The raster-output launch writes row g's bits at token row_map[g]:
+    equal, bit for bit, to the blocked launch followed by the inverse
+    permutation; every mapped token is written, the others are untouched,
+    and the LSE is the blocked launch's."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    w, row_map, tokens = _raster_case(name)
+    row_map = row_map.to(dev)
+    q, k, v, ql, kl = _tensors(w, dev)
+    r = _route(w, dev, q, k, ql, kl)
+    args = dict(block=w.bs, scale=w.scale, q_block_len=ql, kv_block_len=kl, lse=True)
+    o_blk, l_blk = bsa.block_sparse_attn(q, k, v, r["row_ptr"], r["col_idx"], **args)
+    out = torch.full((tokens + 3, w.heads, w.d), 7.0, dtype=q.dtype, device=dev)
+    o_r, l_r = bsa.block_sparse_attn_raster(q, k, v, r["row_ptr"], r["col_idx"], row_map, out=out, **args)
+    torch.cuda.synchronize()
+    assert torch.equal(l_r, l_blk)
+    m = row_map.cpu().numpy()
+    g = np.nonzero(m >= 0)[0]
+    got = o_r.cpu()
+    ref = o_blk.cpu().transpose(0, 1)                     # [rows][heads][d]
+    assert torch.equal(got[torch.from_numpy(m[g]).long()], ref[torch.from_numpy(g).long()])
+    written = np.zeros(tokens + 3, dtype=bool)
+    written[m[g]] = True
+    assert torch.all(got[torch.from_numpy(~written)] == 7.0)
+    print(name, "rows mapped", len(g), "of", len(m))
+
+
 @pytest.mark.parametrize("block,d", [(64, 64), (64, 128), (128, 64)])
 def test_edge_cases_small(block, d):
     """Empty lists, out-of-range and negative indices (ignored), an empty KV

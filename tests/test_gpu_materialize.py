@@ -184,8 +184,11 @@ def test_pipeline_step_with_materialised_routes():
     k_r = bsa.gilbert_perm(ks, ra.perm, block=w.bs, inverse=True)
     v_r = bsa.gilbert_perm(vs, ra.perm, block=w.bs, inverse=True)
     mat = dict(coverage=torch.from_numpy(w.coverage).to(dev), k_cov=80, k_unc=150, mass=0.9, ref_blocks=(0, 3))
-    _, r = ra.step(q_r, k_r, v_r, c - 1, overlap=torch.from_numpy(w.overlap).to(dev), materialize=mat)
+    o_r, r = ra.step(q_r, k_r, v_r, c - 1, overlap=torch.from_numpy(w.overlap).to(dev), materialize=mat)
     torch.cuda.synchronize()
+    # the step writes O in raster order: Gilbert row g is token perm[g]
+    perm = ra.perm.cpu().numpy()
+    L = len(perm)
     got = csr_lists(r["row_ptr"], r["col_idx"], w.heads, w.nqb)
     win = om.block_window(gilbert_order(*workloads.CHUNK_GRID)[0], workloads.CHUNK_GRID, w.bs, c - 1)
     vmask = valid_rows(w.q_len, w.bs)
@@ -196,5 +199,7 @@ def test_pipeline_step_with_materialised_routes():
                                   ref_blocks=(0, 3), overlap=w.overlap, lam=w.lam, tau=w.tau, g_ref=w.g_ref)
         assert_lists_equal(got[hi], ref["lists"], "head %d" % hi)
         o_ref, _ = oatt.block_sparse_head(q, k, v, w.q_len, w.k_len, w.bs, ref["lists"], w.scale)
-        mx, mean = err_summary(f64(ra.o_blk[hi]), o_ref, vmask)
+        o_g = np.zeros_like(o_ref)
+        o_g[:L] = f64(o_r[:, hi, :])[perm]
+        mx, mean = err_summary(o_g, o_ref, vmask)
         assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (hi, mx, mean)
