@@ -326,59 +326,66 @@ __device__ __forceinline__ bool sel_before(unsigned long long ka, int ia, unsign
     return ka > kb || (ka == kb && ia < ib);
 }
 
-// The k-th largest of the values held by a wave, N per lane (0 = none), by
-// bisection on the bits: the largest t with at least k values >= t, built
-// from the most significant bit down (0 when fewer than k values are
-// non-zero).  The count of each trial is a ballot, so the bound stays
-// wave-uniform and nothing moves between lanes.
+// The k-th largest of 32-bit values held by a wave, N per lane, among
+// those whose flag is set, by bisection on the bits: the largest t with at
+// least k flagged values >= t, built from the most significant bit down (0
+// when fewer than k values are flagged).  The count of each trial is a
+// ballot, so the bound stays wave-uniform and nothing moves between lanes.
 template <int N>
-__device__ __forceinline__ unsigned long long wave_kth_largest(const unsigned long long (&v)[N], int k) {
-    unsigned long long p = 0;
+__device__ __forceinline__ uint32_t wave_kth_largest32(const uint32_t (&v)[N], const bool (&in)[N], int k) {
+    uint32_t p = 0;
     k = __builtin_amdgcn_readfirstlane(k);  // the same for every lane; keeps the bound scalar
 #pragma unroll
-    for (int b = 63; b >= 0; --b) {
-        const unsigned long long t = p | (1ull << b);
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t t = p | (1u << b);
         int c = 0;
 #pragma unroll
-        for (int n = 0; n < N; ++n) c += __popcll(__ballot(v[n] >= t));
+        for (int n = 0; n < N; ++n) c += __popcll(__ballot(in[n] && v[n] >= t));
         if (c >= k) p = t;
     }
     return p;
 }
+
+__device__ __forceinline__ uint32_t hi32(unsigned long long x) { return (uint32_t)(x >> 32); }
 
 // Threshold of the top-ke selection over the keys of one row held by a
 // wave (lane l: keys of candidates l + 64 m; 0 = not a candidate): the
 // selected set is every key > prefix plus the first `need` keys == prefix
 // in ascending candidate order, which is the total order (key descending,
 // index ascending); prefix is the ke-th largest key and need = ke minus the
-// number of keys above it.  A fast path (below) handles most rows with
-// ke <= 64: the ke-th largest lane maximum bounds the ke-th largest key from
-// below, and when at most 128 keys reach that bound they are gathered two
-// per lane and the ke-th largest of them is found by bisection.  Otherwise
-// a radix select over 8-bit digits (most significant first, a 256-bin
-// histogram per wave in LDS) finds the ke-th largest key and how many keys
-// equal to it are needed.  `hist` is a 256-int and cand_key a 128-entry
-// per-wave LDS scratch.
+// number of keys above it.  `all_eq` reports that every key equal to
+// prefix is selected (then no ranking among equal keys is needed).
+// A fast path (below) handles most rows with ke <= 64: the ke-th largest
+// high word of the lane maxima bounds the high word of the ke-th largest
+// key from below; when at most 128 keys reach that bound they are gathered
+// two per lane, and the ke-th largest of them is found by bisection on the
+// high words, then, only when several gathered keys share the deciding high
+// word, on their low words.  Otherwise a radix select over 8-bit digits
+// (most significant first, a 256-bin histogram per wave in LDS) finds the
+// ke-th largest key and how many keys equal to it are needed.  `hist` is a
+// 256-int and cand_key a 128-entry per-wave LDS scratch.
 template <int KPL>
 __device__ __forceinline__ void select_threshold(const unsigned long long (&key)[KPL], int ke, int lane,
                                                  int* hist, unsigned long long* cand_key,
-                                                 unsigned long long& prefix, int& need) {
+                                                 unsigned long long& prefix, int& need, bool& all_eq) {
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
     unsigned long long mask = 0;
     prefix = 0;
     need = ke;
+    all_eq = false;
     bool found = false;
     if (ke > 0 && ke <= 64) {
-        // ke lanes hold a key >= L, so every selected key is >= L
-        unsigned long long lm[1] = {0};
+        // ke lanes hold a key whose high word is >= Lh, so every selected key's is
+        uint32_t lmh[1] = {0};
+        const bool lane_in[1] = {true};
 #pragma unroll
-        for (int m = 0; m < KPL; ++m) lm[0] = key[m] > lm[0] ? key[m] : lm[0];
-        const unsigned long long L = wave_kth_largest<1>(lm, ke);
+        for (int m = 0; m < KPL; ++m) lmh[0] = hi32(key[m]) > lmh[0] ? hi32(key[m]) : lmh[0];
+        const uint32_t Lh = wave_kth_largest32<1>(lmh, lane_in, ke);
         unsigned long long* ck = cand_key;
         int c = 0;
 #pragma unroll
         for (int m = 0; m < KPL; ++m) {
-            const bool cand = key[m] != 0 && key[m] >= L;
+            const bool cand = key[m] != 0 && hi32(key[m]) >= Lh;
             const unsigned long long b = __ballot(cand);
             const int at = c + __popcll(b & lt_mask);
             if (cand && at < 128) ck[at] = key[m];
@@ -388,9 +395,25 @@ __device__ __forceinline__ void select_threshold(const unsigned long long (&key)
             __builtin_amdgcn_wave_barrier();
             __asm__ volatile("" ::: "memory");
             const unsigned long long two[2] = {lane < c ? ck[lane] : 0ull, lane + 64 < c ? ck[lane + 64] : 0ull};
-            const unsigned long long kt = wave_kth_largest<2>(two, ke);
-            prefix = kt;
-            need = ke - __popcll(__ballot(two[0] > kt)) - __popcll(__ballot(two[1] > kt));
+            const uint32_t th[2] = {hi32(two[0]), hi32(two[1])};
+            const bool nz[2] = {two[0] != 0, two[1] != 0};
+            const uint32_t ph = wave_kth_largest32<2>(th, nz, ke);
+            int above = 0, tied = 0;
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                above += __popcll(__ballot(nz[n] && th[n] > ph));
+                tied += __popcll(__ballot(nz[n] && th[n] == ph));
+            }
+            const int need_h = ke - above;  // 1 <= need_h <= tied
+            uint32_t pl = 0;
+            if (need_h < tied) {
+                const uint32_t tl[2] = {(uint32_t)two[0], (uint32_t)two[1]};
+                const bool in_h[2] = {nz[0] && th[0] == ph, nz[1] && th[1] == ph};
+                pl = wave_kth_largest32<2>(tl, in_h, need_h);
+            }
+            prefix = ((unsigned long long)ph << 32) | pl;
+            need = ke - __popcll(__ballot(two[0] > prefix)) - __popcll(__ballot(two[1] > prefix));
+            all_eq = need == __popcll(__ballot(two[0] == prefix)) + __popcll(__ballot(two[1] == prefix));
             found = true;
         }
         __builtin_amdgcn_wave_barrier();
@@ -514,20 +537,33 @@ topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int 
 
     unsigned long long prefix;
     int need;
-    select_threshold<KPL>(key, ke, lane, hist, cand_key[w], prefix, need);
+    bool all_eq;
+    select_threshold<KPL>(key, ke, lane, hist, cand_key[w], prefix, need, all_eq);
     // ordered compaction: key > t, or key == t and among the first `need`
-    int base = start, eq_seen = 0;
+    // (every key >= t when all the equal keys are taken)
+    int base = start;
+    if (ke > 0 && all_eq) {
 #pragma unroll
-    for (int m = 0; m < KPL; ++m) {
-        const bool gt = ke > 0 && key[m] > prefix;
-        const bool eq = ke > 0 && key[m] != 0 && key[m] == prefix;
-        const unsigned long long beq = __ballot(eq);
-        const int rank = eq_seen + __popcll(beq & lt_mask);
-        eq_seen += __popcll(beq);
-        const bool sel = gt || (eq && rank < need);
-        const unsigned long long bs = __ballot(sel);
-        if (sel) col_idx[base + __popcll(bs & lt_mask)] = lane + 64 * m;
-        base += __popcll(bs);
+        for (int m = 0; m < KPL; ++m) {
+            const bool sel = key[m] != 0 && key[m] >= prefix;
+            const unsigned long long bs = __ballot(sel);
+            if (sel) col_idx[base + __popcll(bs & lt_mask)] = lane + 64 * m;
+            base += __popcll(bs);
+        }
+    } else {
+        int eq_seen = 0;
+#pragma unroll
+        for (int m = 0; m < KPL; ++m) {
+            const bool gt = ke > 0 && key[m] > prefix;
+            const bool eq = ke > 0 && key[m] != 0 && key[m] == prefix;
+            const unsigned long long beq = __ballot(eq);
+            const int rank = eq_seen + __popcll(beq & lt_mask);
+            eq_seen += __popcll(beq);
+            const bool sel = gt || (eq && rank < need);
+            const unsigned long long bs = __ballot(sel);
+            if (sel) col_idx[base + __popcll(bs & lt_mask)] = lane + 64 * m;
+            base += __popcll(bs);
+        }
     }
     for (int j0 = n_cand; j0 < nkb; j0 += 64) {
         const int jb = j0 + lane;
@@ -629,7 +665,8 @@ materialize_kernel(const double* __restrict__ keys, int rows, int nqb, int nkb, 
         if (ke > 0) {
             unsigned long long prefix;
             int need;
-            select_threshold<KPL>(key, ke, lane, hist_all[w], skey, prefix, need);
+            bool all_eq;
+            select_threshold<KPL>(key, ke, lane, hist_all[w], skey, prefix, need, all_eq);
             __builtin_amdgcn_wave_barrier();
             __asm__ volatile("" ::: "memory");
             // the selected keys in ascending block order: a well-covered row
