@@ -603,6 +603,100 @@ def summarize_mfma(counter_csv: str, expect_json: str, out_path: str):
     print(json.dumps(out))
 
 
+def profile_step(steps: int):
+    """Counter-collection mode for the whole step: set up C4 at chunk 48, run
+    ``steps`` steps, then one plain 1 GiB device copy (the calibration kernel
+    for the byte counters).  Meant to run under rocprofv3."""
+    import torch
+    st = setup_c4(48, device="cuda:0")
+    for _ in range(steps):
+        run_step(st)
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print("profiled %d steps" % steps)
+
+
+def step_kernel_alg_bytes():
+    """Algorithmic bytes of each kernel of the C4 chunk-48 step (L = 4680
+    tokens, 40 heads, d 128, 37 query blocks, 1776 candidates, top-K 50):
+    what the kernel must read and write at least once."""
+    L, heads, d, nqb, n_cand, K = 4680, 40, 128, 37, 1776, 50
+    raster = L * heads * d * 2
+    blocked = nqb * 128 * heads * d * 2
+    pooled = heads * nqb * d * 8
+    keys = heads * nqb * n_cand * 8
+    lists = 4 * (heads * nqb + 1 + heads * nqb * K)
+    return {
+        "gilbert_index_kernel": (2 * 4 * L, "perm and inverse written"),
+        "gilbert_perm_pool_kernel": (raster + blocked + pooled, "raster read, blocked written, block means written"),
+        "gilbert_perm_kernel<false>": (raster + blocked, "raster read, blocked written"),
+        "score_kernel": (heads * n_cand * d * 8 + pooled + keys,
+                         "pooled keys and queries read, selection keys written"),
+        "topk_kernel": (keys + lists, "selection keys read, lists written"),
+    }
+
+
+def summarize_step_traffic(fetch_csv: str, write_csv: str, stats_csv: str, out_md: str):
+    """Per kernel of the step: HBM bytes from the FETCH_SIZE and WRITE_SIZE
+    counter runs (KiB per dispatch, each scaled by what it reads for the
+    plain 1 GiB copy), the kernel's mean duration from the kernel-trace
+    statistics of the same program, and the GB/s both give, beside the
+    kernel's algorithmic bytes."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name", counter) == counter:
+                    vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    dur = {}
+    with open(stats_csv) as f:
+        for row in csv.DictReader(f):
+            dur[row["Name"]] = float(row["AverageNs"])
+    cf = [v for k, vs in fetch.items() if "copy" in k for v in vs]
+    cw = [v for k, vs in write.items() if "copy" in k for v in vs]
+    f_factor = COPY_BYTES / (max(cf) * 1024.0)
+    w_factor = COPY_BYTES / (max(cw) * 1024.0)
+
+    def short(name):
+        tag = "(anonymous namespace)::"
+        n = name[name.index(tag) + len(tag):] if tag in name else name
+        return n[:n.index("(")] if "(" in n else n
+
+    alg = step_kernel_alg_bytes()
+    lines = ["| kernel | dispatches | mean duration (us) | HBM read (MB) | HBM written (MB) | HBM GB/s | "
+             "algorithmic MB | algorithmic GB/s | algorithmic bytes |", "|---|---|---|---|---|---|---|---|---|"]
+    for name in sorted(fetch, key=lambda n: -dur.get(n, 0.0)):
+        if "bsa::" not in name:
+            continue
+        sn = short(name)
+        fb = sum(fetch[name]) / len(fetch[name]) * 1024.0 * f_factor
+        wb = sum(write.get(name, [0.0])) / max(1, len(write.get(name, []))) * 1024.0 * w_factor
+        us = dur.get(name, 0.0) / 1e3
+        key = next((k for k in alg if sn.startswith(k)), None)
+        a, what = alg[key] if key else (None, "")
+        if sn.startswith("attn_bf16_kernel"):
+            what = "3.03 GB per launch (distinct selected K/V blocks once, Q, O, lists)"
+        elif sn.startswith("pool_kernel"):
+            what = "first step only: the full pool of the history (the cache starts empty)"
+        elif sn.startswith("gilbert_perm_kernel<true>"):
+            what = "set-up only: the raster inputs made from the blocked workload"
+        lines.append("| `%s` | %d | %.1f | %.1f | %.1f | %.0f | %s | %s | %s |" % (
+            sn, len(fetch[name]), us, fb / 1e6, wb / 1e6, (fb + wb) / (us * 1e3) if us else 0.0,
+            "%.1f" % (a / 1e6) if a else "-", "%.0f" % (a / (us * 1e3)) if a and us else "-", what))
+    text = "\n".join(lines) + "\n\nCounter scale factors (copy kernel): fetch %.3f, write %.3f.\n" % (f_factor, w_factor)
+    with open(out_md, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def summarize_counters(fetch_csv: str, write_csv: str, out_path: str):
     """Turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then WRITE_SIZE; KiB
     per dispatch) into HBM bytes per attention launch, each counter scaled by
@@ -672,9 +766,16 @@ def main():
                     help="counter mode: write the MFMA counts the launches must issue to this file")
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("COUNTER_CSV", "EXPECT_JSON", "OUT_JSON"),
                     help="compare the MFMA instruction counters of the attention launches with the listed tiles")
+    ap.add_argument("--profile-step", type=int, default=0, metavar="N",
+                    help="counter mode: N whole steps + a 1 GiB copy, no JSON line")
+    ap.add_argument("--summarize-step-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV", "OUT_MD"),
+                    help="per-kernel HBM bytes and GB/s of the step from counter and kernel-trace runs")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                     help="write HBM bytes per attention launch from two rocprofv3 --pmc CSVs")
     args = ap.parse_args()
+    if args.summarize_step_traffic:
+        summarize_step_traffic(*args.summarize_step_traffic)
+        return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return
@@ -689,6 +790,9 @@ def main():
     import torch
     import block_sparse_attention_gilbert_amd as bsa  # fails loudly if libbsa.so is missing
 
+    if args.profile_step:
+        profile_step(args.profile_step)
+        return
     if args.profile_attention:
         profile_attention(args.profile_attention, args.expect_out)
         return
