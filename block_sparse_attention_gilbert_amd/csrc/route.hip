@@ -348,76 +348,123 @@ __device__ __forceinline__ uint32_t wave_kth_largest32(const uint32_t (&v)[N], c
 
 __device__ __forceinline__ uint32_t hi32(unsigned long long x) { return (uint32_t)(x >> 32); }
 
+// Fast path of the top-ke threshold (see select_threshold) for ke <= 64 R:
+// the R largest high words of each lane hold ke values that are high words
+// of distinct keys, so the ke-th largest of them bounds the high word of
+// the ke-th largest key from below.  The keys that reach the bound are
+// gathered, G per lane (false when more than 64 G do), and the ke-th
+// largest of them is found by bisection on the high words, then, only when
+// several gathered keys share the deciding high word, on their low words.
+// `ck` is a 64 G-entry per-wave LDS scratch.
+template <int KPL, int R, int G>
+__device__ __forceinline__ bool select_fast(const unsigned long long (&key)[KPL], int ke, int lane,
+                                            unsigned long long* ck, unsigned long long& prefix, int& need,
+                                            bool& all_eq) {
+    const unsigned long long lt_mask = (1ull << lane) - 1ull;
+    uint32_t top[R];
+    bool lane_in[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        top[r] = 0;
+        lane_in[r] = true;
+    }
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+        uint32_t x = hi32(key[m]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t hi = top[r] > x ? top[r] : x;
+            x = top[r] > x ? x : top[r];
+            top[r] = hi;
+        }
+    }
+    const uint32_t lh = wave_kth_largest32<R>(top, lane_in, ke);
+    int c = 0;
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+        const bool cand = key[m] != 0 && hi32(key[m]) >= lh;
+        const unsigned long long b = __ballot(cand);
+        const int at = c + __popcll(b & lt_mask);
+        if (cand && at < 64 * G) ck[at] = key[m];
+        c += __popcll(b);
+    }
+    if (c > 64 * G) return false;
+    __builtin_amdgcn_wave_barrier();
+    __asm__ volatile("" ::: "memory");
+    unsigned long long kv[G];
+    uint32_t th[G];
+    bool nz[G];
+#pragma unroll
+    for (int n = 0; n < G; ++n) {
+        kv[n] = lane + 64 * n < c ? ck[lane + 64 * n] : 0ull;
+        th[n] = hi32(kv[n]);
+        nz[n] = kv[n] != 0;
+    }
+    const uint32_t ph = wave_kth_largest32<G>(th, nz, ke);
+    int above = 0, tied = 0;
+#pragma unroll
+    for (int n = 0; n < G; ++n) {
+        above += __popcll(__ballot(nz[n] && th[n] > ph));
+        tied += __popcll(__ballot(nz[n] && th[n] == ph));
+    }
+    const int need_h = ke - above;  // 1 <= need_h <= tied
+    uint32_t pl = 0;
+    if (need_h < tied) {
+        uint32_t tl[G];
+        bool in_h[G];
+#pragma unroll
+        for (int n = 0; n < G; ++n) {
+            tl[n] = (uint32_t)kv[n];
+            in_h[n] = nz[n] && th[n] == ph;
+        }
+        pl = wave_kth_largest32<G>(tl, in_h, need_h);
+    }
+    prefix = ((unsigned long long)ph << 32) | pl;
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int n = 0; n < G; ++n) {
+        gt += __popcll(__ballot(kv[n] > prefix));
+        eq += __popcll(__ballot(kv[n] == prefix));
+    }
+    need = ke - gt;
+    all_eq = need == eq;
+    __builtin_amdgcn_wave_barrier();
+    __asm__ volatile("" ::: "memory");
+    return true;
+}
+
+// Largest per-wave candidate scratch of the fast paths (entries).
+constexpr int kSelScratch = 64 * 8;
+
 // Threshold of the top-ke selection over the keys of one row held by a
 // wave (lane l: keys of candidates l + 64 m; 0 = not a candidate): the
 // selected set is every key > prefix plus the first `need` keys == prefix
 // in ascending candidate order, which is the total order (key descending,
 // index ascending); prefix is the ke-th largest key and need = ke minus the
 // number of keys above it.  `all_eq` reports that every key equal to
-// prefix is selected (then no ranking among equal keys is needed).
-// A fast path (below) handles most rows with ke <= 64: the ke-th largest
-// high word of the lane maxima bounds the high word of the ke-th largest
-// key from below; when at most 128 keys reach that bound they are gathered
-// two per lane, and the ke-th largest of them is found by bisection on the
-// high words, then, only when several gathered keys share the deciding high
-// word, on their low words.  Otherwise a radix select over 8-bit digits
+// prefix is selected (then no ranking among equal keys is needed).  The
+// fast path takes the lane top-2 bound for ke <= 64, top-4 for ke <= 128
+// and top-8 for ke <= 256; when it does not apply (more candidates reach
+// the bound than it gathers, or ke > 256), a radix select over 8-bit digits
 // (most significant first, a 256-bin histogram per wave in LDS) finds the
 // ke-th largest key and how many keys equal to it are needed.  `hist` is a
-// 256-int and cand_key a 128-entry per-wave LDS scratch.
+// 256-int and cand_key a kSelScratch-entry per-wave LDS scratch.
 template <int KPL>
 __device__ __forceinline__ void select_threshold(const unsigned long long (&key)[KPL], int ke, int lane,
                                                  int* hist, unsigned long long* cand_key,
                                                  unsigned long long& prefix, int& need, bool& all_eq) {
-    const unsigned long long lt_mask = (1ull << lane) - 1ull;
     unsigned long long mask = 0;
-    prefix = 0;
-    need = ke;
-    all_eq = false;
     bool found = false;
-    if (ke > 0 && ke <= 64) {
-        // ke lanes hold a key whose high word is >= Lh, so every selected key's is
-        uint32_t lmh[1] = {0};
-        const bool lane_in[1] = {true};
-#pragma unroll
-        for (int m = 0; m < KPL; ++m) lmh[0] = hi32(key[m]) > lmh[0] ? hi32(key[m]) : lmh[0];
-        const uint32_t Lh = wave_kth_largest32<1>(lmh, lane_in, ke);
-        unsigned long long* ck = cand_key;
-        int c = 0;
-#pragma unroll
-        for (int m = 0; m < KPL; ++m) {
-            const bool cand = key[m] != 0 && hi32(key[m]) >= Lh;
-            const unsigned long long b = __ballot(cand);
-            const int at = c + __popcll(b & lt_mask);
-            if (cand && at < 128) ck[at] = key[m];
-            c += __popcll(b);
-        }
-        if (c <= 128) {
-            __builtin_amdgcn_wave_barrier();
-            __asm__ volatile("" ::: "memory");
-            const unsigned long long two[2] = {lane < c ? ck[lane] : 0ull, lane + 64 < c ? ck[lane + 64] : 0ull};
-            const uint32_t th[2] = {hi32(two[0]), hi32(two[1])};
-            const bool nz[2] = {two[0] != 0, two[1] != 0};
-            const uint32_t ph = wave_kth_largest32<2>(th, nz, ke);
-            int above = 0, tied = 0;
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                above += __popcll(__ballot(nz[n] && th[n] > ph));
-                tied += __popcll(__ballot(nz[n] && th[n] == ph));
-            }
-            const int need_h = ke - above;  // 1 <= need_h <= tied
-            uint32_t pl = 0;
-            if (need_h < tied) {
-                const uint32_t tl[2] = {(uint32_t)two[0], (uint32_t)two[1]};
-                const bool in_h[2] = {nz[0] && th[0] == ph, nz[1] && th[1] == ph};
-                pl = wave_kth_largest32<2>(tl, in_h, need_h);
-            }
-            prefix = ((unsigned long long)ph << 32) | pl;
-            need = ke - __popcll(__ballot(two[0] > prefix)) - __popcll(__ballot(two[1] > prefix));
-            all_eq = need == __popcll(__ballot(two[0] == prefix)) + __popcll(__ballot(two[1] == prefix));
-            found = true;
-        }
-        __builtin_amdgcn_wave_barrier();
-        __asm__ volatile("" ::: "memory");
+    if (ke > 0 && ke <= 64)
+        found = select_fast<KPL, 2, 2>(key, ke, lane, cand_key, prefix, need, all_eq);
+    else if (ke > 64 && ke <= 128)
+        found = select_fast<KPL, 4, 4>(key, ke, lane, cand_key, prefix, need, all_eq);
+    else if (ke > 128 && ke <= 256)
+        found = select_fast<KPL, 8, 8>(key, ke, lane, cand_key, prefix, need, all_eq);
+    if (!found) {
+        prefix = 0;
+        need = ke;
+        all_eq = false;
     }
     if (ke > 0 && !found) {
 #pragma unroll 1
@@ -477,7 +524,7 @@ topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int 
             int32_t* __restrict__ row_ptr, const int32_t* __restrict__ keff, int32_t* __restrict__ col_idx,
             int32_t* __restrict__ zero_counts) {
     __shared__ int hist_all[kThreads / 64][256];
-    __shared__ unsigned long long cand_key[kThreads / 64][128];
+    __shared__ unsigned long long cand_key[kThreads / 64][kSelScratch];
     // the wave index is the same for every lane: row, query block and budget stay scalar
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = blockIdx.x * (kThreads / 64) + w;
@@ -621,6 +668,7 @@ materialize_kernel(const double* __restrict__ keys, int rows, int nqb, int nkb, 
     __shared__ unsigned long long skey_all[kThreads / 64][kMaxUnc];
     __shared__ int sidx_all[kThreads / 64][kMaxUnc];
     __shared__ uint32_t bits_all[kThreads / 64][kMaxCandidates / 32];
+    __shared__ unsigned long long cand_all[kThreads / 64][kSelScratch];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = blockIdx.x * (kThreads / 64) + w;
     if (r >= rows) return;
@@ -666,7 +714,7 @@ materialize_kernel(const double* __restrict__ keys, int rows, int nqb, int nkb, 
             unsigned long long prefix;
             int need;
             bool all_eq;
-            select_threshold<KPL>(key, ke, lane, hist_all[w], skey, prefix, need, all_eq);
+            select_threshold<KPL>(key, ke, lane, hist_all[w], cand_all[w], prefix, need, all_eq);
             __builtin_amdgcn_wave_barrier();
             __asm__ volatile("" ::: "memory");
             // the selected keys in ascending block order: a well-covered row
@@ -964,10 +1012,10 @@ hipError_t launch_materialize(const bsa_route_args* a, const bsa_materialize_arg
     hipLaunchKernelGGL(materialize_kernel<KPL>, grid, dim3(kThreads), 0, stream, keys, rows, a->nqb, nkb,        \
                        a->block, a->q_block_len, a->kv_block_len, m->coverage, m->eta_cov, m->k_cov, m->k_unc,  \
                        m->mass, pb, pe, m->window, m->window_len, m->window_stride, rb, re, nwords, bitmap, counts)
+    // no 16-key-per-lane instance: the register allocator spills that one
+    // to scratch, so rows of 513..1536 blocks take the 24-key instance
     if (nkb <= 64 * 8)
         BSA_MAT(8);
-    else if (nkb <= 64 * 16)
-        BSA_MAT(16);
     else if (nkb <= 64 * 24)
         BSA_MAT(24);
     else if (nkb <= 64 * 32)
