@@ -1,0 +1,62 @@
+"""The built library's device code, read from its own kernel metadata: no
+kernel spills to scratch memory (a spill turns register traffic into memory
+traffic), and the attention kernels keep the occupancy their design assumes
+(two workgroups per CU for the 128-row blocks: at most 256 registers per
+lane)."""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+import yaml
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "block_sparse_attention_gilbert_amd", "libbsa.so")
+LLVM = "/opt/rocm/llvm/bin"
+MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
+
+
+def _kernels(tmp_path):
+    """{kernel name: metadata fields} of every gfx950 code object in the library."""
+    tools = [shutil.which("objcopy"), os.path.join(LLVM, "clang-offload-bundler"), os.path.join(LLVM, "llvm-readelf")]
+    if not os.path.exists(LIB) or not all(t and os.path.exists(t) for t in tools):
+        pytest.skip("library or LLVM tools missing")
+    fat = tmp_path / "fatbin.bin"
+    subprocess.run([tools[0], "--dump-section", ".hip_fatbin=%s" % fat, LIB, str(tmp_path / "lib.copy")], check=True)
+    data = fat.read_bytes()
+    starts = [m.start() for m in re.finditer(re.escape(MAGIC), data)]
+    out = {}
+    for n, (a, b) in enumerate(zip(starts, starts[1:] + [len(data)])):
+        part = tmp_path / ("bundle%d.bin" % n)
+        part.write_bytes(data[a:b])
+        code = tmp_path / ("code%d.o" % n)
+        r = subprocess.run([tools[1], "--unbundle", "--type=o", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950",
+                            "--input=%s" % part, "--output=%s" % code], capture_output=True)
+        if r.returncode != 0 or not code.exists() or code.stat().st_size == 0:
+            continue
+        notes = subprocess.run([tools[2], "--notes", str(code)], capture_output=True, text=True).stdout
+        # the metadata is a YAML document: one list entry per kernel
+        text = notes[notes.index("amdhsa.kernels:"):] if "amdhsa.kernels:" in notes else ""
+        for entry in yaml.safe_load(text.split("\n...")[0]).get("amdhsa.kernels", []) if text else []:
+            out[entry[".name"]] = {k.lstrip("."): v for k, v in entry.items() if isinstance(v, int)}
+    return out
+
+
+def test_no_kernel_spills_to_scratch(tmp_path):
+    kernels = _kernels(tmp_path)
+    assert len(kernels) > 20, sorted(kernels)
+    spilled = {k: (v.get("private_segment_fixed_size"), v.get("vgpr_spill_count"))
+               for k, v in kernels.items()
+               if v.get("private_segment_fixed_size", 0) or v.get("vgpr_spill_count", 0)}
+    assert not spilled, spilled
+
+
+def test_attention_occupancy(tmp_path):
+    kernels = _kernels(tmp_path)
+    attn = {k: v for k, v in kernels.items() if "attn_bf16_kernelILi128" in k}
+    assert len(attn) == 4, sorted(attn)
+    for name, v in attn.items():
+        assert v["vgpr_count"] + v.get("agpr_count", 0) <= 256, (name, v)
+        assert v["group_segment_fixed_size"] <= 65536, (name, v)
