@@ -49,12 +49,14 @@ __host__ __device__ inline V3 gilbert_cell(int T, int H, int W, int64_t idx) {
         }
     }
     V3 p = {0, 0, 0};
-    int64_t i = idx;
+    // every count below is at most the grid's cell count, which the callers
+    // keep below 2^31, so the descent runs in 32-bit integers
+    int i = (int)idx;
 
     // three-dimensional levels
     for (;;) {
         const int la = vlen(a), lb = vlen(b), lc = vlen(c);
-        if (lb == 1 && lc == 1) return vadd(p, vmul(vunit(a), (int)i));
+        if (lb == 1 && lc == 1) return vadd(p, vmul(vunit(a), i));
         if (lc == 1) break;  // plane (a, b)
         if (lb == 1) {       // plane (a, c)
             b = c;
@@ -83,7 +85,7 @@ __host__ __device__ inline V3 gilbert_cell(int T, int H, int W, int64_t idx) {
                 break;
             }
             const V3 a2 = even_half(a);
-            const int64_t n1 = (int64_t)vlen(a2) * 4;
+            const int n1 = vlen(a2) * 4;
             if (i < n1) {
                 a = a2;
             } else {
@@ -95,7 +97,7 @@ __host__ __device__ inline V3 gilbert_cell(int T, int H, int W, int64_t idx) {
         }
         if (2 * la > 3 * (lb > lc ? lb : lc)) {
             const V3 a2 = even_half(a);
-            const int64_t n1 = (int64_t)vlen(a2) * lb * lc;
+            const int n1 = vlen(a2) * lb * lc;
             if (i < n1) {
                 a = a2;
             } else {
@@ -115,8 +117,8 @@ __host__ __device__ inline V3 gilbert_cell(int T, int H, int W, int64_t idx) {
         }
         const V3 a2 = even_half(a), L2 = even_half(L);
         const int lL = vlen(L), lO = vlen(O), lL2 = vlen(L2), la2 = vlen(a2);
-        const int64_t n1 = (int64_t)lL2 * la2 * lO;
-        const int64_t n2 = (int64_t)la * (lL - lL2) * lO;
+        const int n1 = lL2 * la2 * lO;
+        const int n2 = la * (lL - lL2) * lO;
         if (i < n1) {
             a = L2;
             b = a2;
@@ -139,11 +141,11 @@ __host__ __device__ inline V3 gilbert_cell(int T, int H, int W, int64_t idx) {
     // two-dimensional levels in the plane (a, b)
     for (;;) {
         const int la = vlen(a), lb = vlen(b);
-        if (lb == 1) return vadd(p, vmul(vunit(a), (int)i));
-        if (la == 1) return vadd(p, vmul(vunit(b), (int)i));
+        if (lb == 1) return vadd(p, vmul(vunit(a), i));
+        if (la == 1) return vadd(p, vmul(vunit(b), i));
         const V3 a2 = even_half(a), b2 = even_half(b);
         if (2 * la > 3 * lb) {
-            const int64_t n1 = (int64_t)vlen(a2) * lb;
+            const int n1 = vlen(a2) * lb;
             if (i < n1) {
                 a = a2;
             } else {
@@ -153,8 +155,8 @@ __host__ __device__ inline V3 gilbert_cell(int T, int H, int W, int64_t idx) {
             }
             continue;
         }
-        const int64_t n1 = (int64_t)vlen(b2) * vlen(a2);
-        const int64_t n2 = (int64_t)la * (lb - vlen(b2));
+        const int n1 = vlen(b2) * vlen(a2);
+        const int n2 = la * (lb - vlen(b2));
         if (i < n1) {
             a = b2;
             b = a2;
