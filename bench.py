@@ -84,6 +84,9 @@ def setup_c4(chunk: int = 48, heads=None, device="cuda:0"):
                          k_store=k_store, v_store=v_store)
     cur = chunk - 1
     ks, vs = ra.slot(cur)
+    # the step reads Q in raster order; the dense and sweep timings read the
+    # permuted copy, which stays as set here
+    ra.q_blk.copy_(w.q.to(device))
     q_raster = gilbert_perm(w.q.to(device), ra.perm, block=w.bs, inverse=True)
     k_raster = gilbert_perm(ks, ra.perm, block=w.bs, inverse=True)
     v_raster = gilbert_perm(vs, ra.perm, block=w.bs, inverse=True)
@@ -191,10 +194,11 @@ def _time_ms(fn, reps: int, warm: int = 10, between=None):
 
 def breakdown(st, reps: int):
     """Each stage of the step alone (median of ``reps`` calls), with its
-    algorithmic bytes and the GB/s that gives: the Gilbert index, the three
-    forward permutations (Q and K with their block means, V), the router
-    over the pooled blocks, the attention launch (its epilogue writes O in
-    raster order, so there is no separate inverse permutation)."""
+    algorithmic bytes and the GB/s that gives: the Gilbert index, the
+    forward passes (K with its block means and V into the store slot, the
+    block means of Q), the router over the pooled blocks, the attention
+    launch (reading Q and writing O in raster order, so neither is
+    permuted by a pass of its own)."""
     import torch
     w, ra = st["w"], st["ra"]
     cur = st["cur"]
@@ -202,8 +206,8 @@ def breakdown(st, reps: int):
     raster = L * heads * d * 2
     blocked = ra.rows_c * heads * d * 2
 
-    def fwd():                                 # with the block means of Q and of the new chunk's K
-        ra.permute_inputs(st["q_raster"], st["k_raster"], st["v_raster"], cur)
+    def fwd():                                 # as in the step: K and V permuted, Q only pooled
+        ra.permute_inputs(st["q_raster"], st["k_raster"], st["v_raster"], cur, q_blocks=False)
 
     def route():                               # as in the step: every block's mean is already pooled
         return ra.route(cur, qpool=ra.qbar)
@@ -221,9 +225,10 @@ def breakdown(st, reps: int):
                    + 4 * (heads * w.nqb + 1 + int(r["row_ptr"][-1])))
     stages = {
         "gilbert_index": (lambda: ra._index(), 4 * 2 * L),
-        "forward_permutes": (fwd, 3 * (raster + blocked) + 2 * pooled),
+        "forward_permutes": (fwd, 3 * raster + 2 * blocked + 2 * pooled),
         "route": (route, route_bytes),
-        "attention": (lambda: ra._attend(r, nkb, k_hist, v_hist, None, None, True), wc["alg_bytes"]),
+        "attention": (lambda: ra._attend(r, nkb, k_hist, v_hist, None, None, True, st["q_raster"]),
+                      wc["alg_bytes"]),
     }
     out = {}
     for name, (fn, nbytes) in stages.items():
@@ -232,7 +237,7 @@ def breakdown(st, reps: int):
     # the same attention launch with L2 and the 256 MB MALL flushed before
     # each call (a 512 MB write, untimed, right before it)
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=ra.device)
-    ms = _time_ms(lambda: ra._attend(r, nkb, k_hist, v_hist, None, None, True), reps,
+    ms = _time_ms(lambda: ra._attend(r, nkb, k_hist, v_hist, None, None, True, st["q_raster"]), reps,
                   between=lambda: scrub.fill_(1))
     del scrub
     out["attention_cold_ms"] = round(ms, 4)
@@ -540,8 +545,8 @@ def profile_attention(launches: int, expect_out=None):
     nkb = ra.store_chunks * ra.nbc
     r = ra.route_out
     k_hist, v_hist = ra.k_store[:, : nkb * ra.block], ra.v_store[:, : nkb * ra.block]
-    for _ in range(launches):       # as in the step: output straight to raster order
-        ra._attend(r, nkb, k_hist, v_hist, None, None, out_raster=True)
+    for _ in range(launches):       # as in the step: Q read and O written in raster order
+        ra._attend(r, nkb, k_hist, v_hist, None, None, out_raster=True, q_raster=st["q_raster"])
     for _ in range(2):  # dense attention over the same history, for comparison counters
         ra.dense(st["cur"])
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
@@ -630,7 +635,9 @@ def step_kernel_alg_bytes():
     lists = 4 * (heads * nqb + 1 + heads * nqb * K)
     return {
         "gilbert_index_kernel": (2 * 4 * L, "perm and inverse written"),
-        "gilbert_perm_pool_kernel": (raster + blocked + pooled, "raster read, blocked written, block means written"),
+        "gilbert_perm_pool_kernel": (raster + (blocked + 2 * pooled) // 2,
+                                     "mean of Q (raster read, block means written) and K (raster read, "
+                                     "blocked written, block means written)"),
         "gilbert_perm_kernel<false>": (raster + blocked, "raster read, blocked written"),
         "score_kernel": (heads * n_cand * d * 8 + pooled + keys,
                          "pooled keys and queries read, selection keys written"),
@@ -1057,7 +1064,7 @@ def oracle_table(st, path):
     w3 = workloads.c3()
     add("C3 geometric bias", w3, list(range(w3.heads)), w3.nkb, 50, overlap=w3.overlap)
     w4, ra = st["w"], st["ra"]
-    resident = (ra.q_blk, ra.k_store, ra.v_store, ra.q_len, ra.kv_len)   # the step left Q permuted in q_blk
+    resident = (ra.q_blk, ra.k_store, ra.v_store, ra.q_len, ra.kv_len)   # Q permuted in q_blk at set-up
     for c in (1, 2, 12, 24, 48):
         add("C4 chunk %d" % c, w4, [0, 39], 37 * c, 50, dev_t=resident)
     for c in (1, 2, 12):

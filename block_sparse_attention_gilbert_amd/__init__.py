@@ -115,8 +115,8 @@ _ATTN_COMMON = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i
 _lib.bsa_block_sparse_attn.restype = _i
 _lib.bsa_block_sparse_attn.argtypes = _ATTN_COMMON + [_p, _p, _i64, _f, _p]
 _lib.bsa_block_sparse_attn_raster.restype = _i
-_lib.bsa_block_sparse_attn_raster.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _p, _i,
-                                              _i64, _p, _p, _p, _p, _i64, _f, _p]
+_lib.bsa_block_sparse_attn_raster.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _p,
+                                              _i, _i64, _p, _p, _p, _p, _i64, _f, _p]
 _lib.bsa_dense_attn.restype = _i
 _lib.bsa_dense_attn.argtypes = _ATTN_COMMON + [_f, _p]
 
@@ -233,22 +233,28 @@ def gilbert_perm(src: torch.Tensor, perm: torch.Tensor, *, block: int, inverse: 
 
 
 def gilbert_perm_pool(src: torch.Tensor, perm: torch.Tensor, *, block: int, dst: Optional[torch.Tensor] = None,
-                      pool: Optional[torch.Tensor] = None, stream=None):
+                      pool: Optional[torch.Tensor] = None, pool_only: bool = False, stream=None):
     """Raster ``[L][heads][d]`` -> Gilbert ``[heads][n_blocks*block][d]``
     like ``gilbert_perm``, plus the float64 block means of the valid rows
     into ``pool`` ``[heads][>= n_blocks][d]`` (a head-strided view such as
-    a slice of a pooled-key cache is fine).  Returns ``(dst, pool)``."""
+    a slice of a pooled-key cache is fine).  ``pool_only``: the block means
+    alone (nothing permuted; ``dst`` is None).  Returns ``(dst, pool)``."""
     _need_gpu(src, perm, dst, pool)
     perm = _i32(perm, "perm")
     L_, heads, d = src.shape
     if src.stride(2) != 1 or src.stride(1) != d:
         raise ValueError("raster src must have contiguous [heads][d] per token")
     nb = -(-L_ // block)
-    if dst is None:
-        dst = torch.empty((heads, nb * block, d), dtype=src.dtype, device=src.device)
-    _, drows, ghs = _heads_rows(dst, d)
-    if drows < nb * block:
-        raise ValueError("dst holds %d rows per head, %d needed" % (drows, nb * block))
+    ghs = 0
+    if pool_only:
+        if dst is not None:
+            raise ValueError("pool_only takes no dst")
+    else:
+        if dst is None:
+            dst = torch.empty((heads, nb * block, d), dtype=src.dtype, device=src.device)
+        _, drows, ghs = _heads_rows(dst, d)
+        if drows < nb * block:
+            raise ValueError("dst holds %d rows per head, %d needed" % (drows, nb * block))
     if pool is None:
         pool = torch.empty((heads, nb, d), dtype=torch.float64, device=src.device)
     if pool.dtype != torch.float64 or pool.dim() != 3 or pool.shape[0] != heads or pool.shape[1] < nb \
@@ -635,26 +641,49 @@ def block_sparse_attn(q, k, v, row_ptr, col_idx, *, block: int, scale: Optional[
 
 def block_sparse_attn_raster(q, k, v, row_ptr, col_idx, row_map, *, block: int, scale: Optional[float] = None,
                              q_block_len=None, kv_block_len=None, out=None, tokens: Optional[int] = None, lse=None,
-                             nkb: Optional[int] = None, stream=None):
+                             nkb: Optional[int] = None, q_raster: bool = False, nqb: Optional[int] = None,
+                             stream=None):
     """``block_sparse_attn`` with the output written in raster token order:
     query row g goes to token ``row_map[g]`` of ``out`` ``[tokens][heads][d]``
-    (negative entries: padding, not written).  ``tokens`` defaults to
-    ``row_map.numel()`` when ``out`` is allocated here.  Returns ``(O, LSE)``
-    (LSE in the blocked layout)."""
+    (negative entries: padding, not written).  With ``q_raster`` the queries
+    are raster ``[tokens][heads][d]`` too, row g read from token
+    ``row_map[g]`` (``nqb`` query blocks: given, or the length of
+    ``q_block_len``).  ``tokens`` defaults to ``row_map.numel()`` when
+    ``out`` is allocated here.  Returns ``(O, LSE)`` (LSE in the blocked
+    layout)."""
     _need_gpu(row_ptr, col_idx, row_map, out)
-    d, heads, nqb, nkb_, qhs, khs, vhs, _, _, lse = _attn_prep(q, k, v, q, lse, block)
+    row_map = _i32(row_map, "row_map")
+    if q_raster:
+        _need_gpu(q, k, v, lse)
+        heads, d = k.shape[0], k.shape[2]
+        if q.dim() != 3 or q.shape[1] != heads or q.shape[2] != d or q.stride(2) != 1 or q.stride(1) != d:
+            raise ValueError("raster q must be [tokens][heads][d] with contiguous [heads][d] per token")
+        if nqb is None:
+            if q_block_len is None:
+                raise ValueError("raster q needs nqb or q_block_len")
+            nqb = q_block_len.numel()
+        _, krows, khs = _heads_rows(k, d)
+        _, vrows, vhs = _heads_rows(v, d)
+        if v.shape[0] != heads or vrows < krows or krows % block:
+            raise ValueError("k, v head counts / rows disagree")
+        nkb_, qs = krows // block, q.stride(0)
+        if lse is True:
+            lse = torch.empty((heads, nqb * block), dtype=torch.float32, device=q.device)
+        elif lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+            raise ValueError("lse must be a contiguous float32 tensor")
+    else:
+        d, heads, nqb, nkb_, qs, khs, vhs, _, _, lse = _attn_prep(q, k, v, q, lse, block)
     nkb = nkb_ if nkb is None else nkb
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    row_map = _i32(row_map, "row_map")
     if out is None:
         out = torch.empty((row_map.numel() if tokens is None else tokens, heads, d), dtype=q.dtype, device=q.device)
     if out.dim() != 3 or out.shape[1] != heads or out.shape[2] != d or out.stride(2) != 1 or out.stride(1) != d:
         raise ValueError("raster out must be [tokens][heads][d] with contiguous [heads][d] per token")
     _check(_lib.bsa_block_sparse_attn_raster(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), heads, d, block, nqb, nkb, qhs, khs,
-        vhs, _ptr(row_map), row_map.numel(), out.stride(0), _ptr(_i32(q_block_len, "q_block_len")),
-        _ptr(_i32(kv_block_len, "kv_block_len")), _ptr(_i32(row_ptr, "row_ptr")), _ptr(_i32(col_idx, "col_idx")),
-        col_idx.numel(), scale, _stream(stream)))
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), heads, d, block, nqb, nkb,
+        1 if q_raster else 0, qs, khs, vhs, _ptr(row_map), row_map.numel(), out.stride(0),
+        _ptr(_i32(q_block_len, "q_block_len")), _ptr(_i32(kv_block_len, "kv_block_len")),
+        _ptr(_i32(row_ptr, "row_ptr")), _ptr(_i32(col_idx, "col_idx")), col_idx.numel(), scale, _stream(stream)))
     return out, lse
 
 

@@ -162,17 +162,21 @@ int bsa_block_sparse_attn(const void* q, const void* k, const void* v, void* o, 
 }
 
 int bsa_block_sparse_attn_raster(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
-                                 int heads, int d, int block, int nqb, int nkb, int64_t q_head_stride,
-                                 int64_t k_head_stride, int64_t v_head_stride, const int32_t* o_row_map, int o_rows,
+                                 int heads, int d, int block, int nqb, int nkb, int q_raster, int64_t q_stride,
+                                 int64_t k_head_stride, int64_t v_head_stride, const int32_t* row_map, int rows,
                                  int64_t o_token_stride, const int32_t* q_block_len, const int32_t* kv_block_len,
                                  const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len, float scale,
                                  hipStream_t stream) {
     bsa::clear_error();
-    // the blocked output stride is not used; the raster layout is checked below
+    // the blocked strides of raster operands are not used; the raster
+    // layouts are checked below
+    const int64_t blocked = (int64_t)nqb * block * d;
+    const bool qr = q_raster == 1;
     bsa::AttnProblem p{q,      k,     v,    o,       lse,          dtype,        heads,   d,       block,
-                       nqb,    nkb,   q_head_stride, k_head_stride, v_head_stride, (int64_t)nqb * block * d,
-                       q_block_len, kv_block_len, row_ptr, col_idx, col_len, scale, o_row_map, o_rows,
-                       o_token_stride};
+                       nqb,    nkb,   qr ? blocked : q_stride, k_head_stride, v_head_stride, blocked,
+                       q_block_len, kv_block_len, row_ptr, col_idx, col_len, scale, row_map, rows,
+                       o_token_stride, qr ? row_map : nullptr, qr ? rows : 0, qr ? q_stride : 0};
+    if (q_raster != 0 && q_raster != 1) return bsa::fail(BSA_EINVAL, "q_raster = %d (0 or 1)", q_raster);
     int st = bsa::validate_attn(p, false);
     if (st == BSA_OK) st = bsa::validate_raster_out(p);
     if (st != BSA_OK) return st;

@@ -62,7 +62,22 @@ struct AttnArgs {
     const int32_t* o_map;
     int o_map_len;
     int64_t o_ts;
+    // raster queries (q_map non-NULL): query row g of head h is read from
+    // q[q_map[g] * q_ts + h * D]; rows past q_map_len or mapped to a
+    // negative entry (padding) read as zeros
+    const int32_t* q_map;
+    int q_map_len;
+    int64_t q_ts;
 };
+
+// Query row of (head h, query row g): the head-major blocked row, or the
+// raster token row through the map (nullptr: a padding row, read as zeros).
+template <typename T>
+__device__ __forceinline__ const T* in_row(const AttnArgs& a, int h, int64_t g, int D) {
+    if (!a.q_map) return static_cast<const T*>(a.q) + h * a.q_hs + g * D;
+    const int t = g < a.q_map_len ? a.q_map[g] : -1;
+    return t < 0 ? nullptr : static_cast<const T*>(a.q) + (int64_t)t * a.q_ts + (int64_t)h * D;
+}
 
 // Output row of (head h, query row g): the head-major blocked row, or the
 // raster token row through the map (nullptr: a padding row, not written).
@@ -315,16 +330,16 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
     const bool active = q0 < vq;
     const bool valid_row = q0 + l32 < vq;
 
-    const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + h * a.q_hs + (int64_t)i * BLK * D;
     const uint16_t* Kh = static_cast<const uint16_t*>(a.k) + h * a.k_hs;
     const uint16_t* Vh = static_cast<const uint16_t*>(a.v) + h * a.v_hs;
 
     // Q^T fragments (B operand of S^T = K Q^T), held for the whole walk
     bf16x8_t qf[KK];
     {
-        const uint16_t* qrow = Qb + (int64_t)(q0 + l32) * D + 8 * hi;
+        const uint16_t* qrow = in_row<uint16_t>(a, h, (int64_t)i * BLK + q0 + l32, D);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qf[kk] = lds_bf16x8(qrow + 16 * kk);
+        for (int kk = 0; kk < KK; ++kk)
+            qf[kk] = qrow ? lds_bf16x8(qrow + 8 * hi + 16 * kk) : bf16x8_t{};
     }
 
     int e0, e1;
@@ -743,11 +758,11 @@ __global__ void __launch_bounds__(BLK * (D / 32)) attn_f32_kernel(AttnArgs a) {
     map_item(a.heads * a.nqb, a.nqb, h, i);
     int vq = a.q_len ? a.q_len[i] : BLK;
     vq = vq < 0 ? 0 : (vq > BLK ? BLK : vq);
-    const float* qrow = static_cast<const float*>(a.q) + h * a.q_hs + ((int64_t)i * BLK + qi) * D + part * 32;
+    const float* qrow = in_row<float>(a, h, (int64_t)i * BLK + qi, D);
     float q[32], o[32];
 #pragma unroll
     for (int c = 0; c < 32; ++c) {
-        q[c] = qrow[c];
+        q[c] = qrow ? qrow[part * 32 + c] : 0.f;
         o[c] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
@@ -848,6 +863,9 @@ hipError_t launch_attn(const AttnProblem& p, bool dense, hipStream_t stream) {
     a.o_map = p.o_map;
     a.o_map_len = p.o_map_len;
     a.o_ts = p.o_ts;
+    a.q_map = p.q_map;
+    a.q_map_len = p.q_map_len;
+    a.q_ts = p.q_ts;
     const int total = p.heads * p.nqb;
     if (p.block == 128 && p.d == 128) return launch_typed<128, 128>(a, p.dtype, dense, total, stream);
     if (p.block == 128 && p.d == 64) return launch_typed<128, 64>(a, p.dtype, dense, total, stream);

@@ -37,6 +37,9 @@ struct AttnProblem {
     const int32_t* o_map;  // raster output: row map (NULL: blocked output)
     int o_map_len;
     int64_t o_ts;          // raster token stride of o, elements
+    const int32_t* q_map;  // raster queries: row map (NULL: blocked queries)
+    int q_map_len;
+    int64_t q_ts;          // raster token stride of q, elements
 };
 
 // Workspace layout of the router (byte offsets, 256-byte aligned).

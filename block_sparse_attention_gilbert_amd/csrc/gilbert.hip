@@ -84,7 +84,8 @@ gilbert_perm_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, cons
     }
 }
 
-// Forward permutation fused with the block means of the permuted rows.
+// Forward permutation fused with the block means of the permuted rows (dst
+// NULL: the block means only).
 // One workgroup per (block, head): thread t copies 16-byte chunk t % chunks
 // of the block's rows t / chunks, + groups, ... (raster token perm[i] to
 // Gilbert row i; padding rows written as zeros) and sums what it copied in
@@ -117,7 +118,7 @@ gilbert_perm_pool_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
     for (int k = g; k < block; k += groups) {
         uint4 u = make_uint4(0u, 0u, 0u, 0u);
         if (k < valid) u = src[(int64_t)perm[i0 + k] * raster_token_stride_c + hc];
-        out[(int64_t)k * chunks] = u;
+        if (dst) out[(int64_t)k * chunks] = u;
         const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
         if (BF16) {
 #pragma unroll

@@ -68,9 +68,22 @@ int validate_gilbert_perm(const void* src, const void* dst, const int32_t* perm,
 int validate_gilbert_perm_pool(const void* src, const void* dst, const int32_t* perm, int L, int heads, int d,
                                int block, int64_t raster_token_stride, int64_t gilbert_head_stride, int dtype,
                                const double* pool, int64_t pool_head_stride) {
-    const int st = validate_gilbert_perm(src, dst, perm, L, heads, d, block, raster_token_stride,
-                                         gilbert_head_stride, 0, dtype);
-    if (st != BSA_OK) return st;
+    if (dst) {
+        const int st = validate_gilbert_perm(src, dst, perm, L, heads, d, block, raster_token_stride,
+                                             gilbert_head_stride, 0, dtype);
+        if (st != BSA_OK) return st;
+    } else {  // block means only: the source side of the permutation's checks
+        if (!src || !perm) return fail(BSA_EINVAL, "src and perm must be non-NULL");
+        if (dtype != BSA_BF16 && dtype != BSA_F32) return fail(BSA_EUNSUPPORTED, "dtype %d", dtype);
+        if (!supported_dim(d)) return fail(BSA_EUNSUPPORTED, "d = %d (64 or 128)", d);
+        if (!supported_dim(block)) return fail(BSA_EUNSUPPORTED, "block = %d (64 or 128)", block);
+        if (L < 1 || heads < 1) return fail(BSA_EINVAL, "L = %d, heads = %d must be >= 1", L, heads);
+        if (raster_token_stride < (int64_t)heads * d)
+            return fail(BSA_EINVAL, "raster_token_stride %lld < heads*d = %lld", (long long)raster_token_stride,
+                        (long long)heads * d);
+        if (!aligned16(src) || (raster_token_stride * dtype_bytes(dtype)) % 16)
+            return fail(BSA_EINVAL, "src and its token stride must be 16-byte aligned");
+    }
     if (!pool) return fail(BSA_EINVAL, "pool must be non-NULL");
     if (heads > 65535) return fail(BSA_EINVAL, "heads = %d exceeds 65535", heads);
     if (reinterpret_cast<uintptr_t>(pool) & 7u) return fail(BSA_EINVAL, "pool must be 8-byte aligned");
@@ -85,19 +98,25 @@ int validate_gilbert_perm_pool(const void* src, const void* dst, const int32_t* 
     const char* t = static_cast<const char*>(dst);
     const int64_t raster_bytes = ((int64_t)(L - 1) * raster_token_stride + (int64_t)heads * d) * eb;
     const int64_t gil_bytes = ((int64_t)(heads - 1) * gilbert_head_stride + nb * block * d) * eb;
-    if ((pb < s + raster_bytes && s < pb + pool_bytes) || (pb < t + gil_bytes && t < pb + pool_bytes))
+    if ((pb < s + raster_bytes && s < pb + pool_bytes) || (t && pb < t + gil_bytes && t < pb + pool_bytes))
         return fail(BSA_EINVAL, "pool overlaps src or dst");
     return BSA_OK;
 }
 
 int validate_raster_out(const AttnProblem& p) {
-    if (!p.o_map) return fail(BSA_EINVAL, "o_row_map must be non-NULL");
+    if (!p.o_map) return fail(BSA_EINVAL, "row_map must be non-NULL");
     if (p.o_map_len < 1 || (int64_t)p.o_map_len > (int64_t)p.nqb * p.block)
-        return fail(BSA_EINVAL, "o_rows %d outside [1, nqb*block]", p.o_map_len);
+        return fail(BSA_EINVAL, "rows %d outside [1, nqb*block]", p.o_map_len);
     if (p.o_ts < (int64_t)p.heads * p.d)
         return fail(BSA_EINVAL, "o_token_stride %lld < heads*d = %lld", (long long)p.o_ts,
                     (long long)p.heads * p.d);
     if ((p.o_ts * dtype_bytes(p.dtype)) % 16) return fail(BSA_EINVAL, "o_token_stride must be 16-byte aligned");
+    if (p.q_map) {
+        if (p.q_ts < (int64_t)p.heads * p.d)
+            return fail(BSA_EINVAL, "raster q_stride %lld < heads*d = %lld", (long long)p.q_ts,
+                        (long long)p.heads * p.d);
+        if ((p.q_ts * dtype_bytes(p.dtype)) % 16) return fail(BSA_EINVAL, "raster q_stride must be 16-byte aligned");
+    }
     return BSA_OK;
 }
 

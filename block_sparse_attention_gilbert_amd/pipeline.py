@@ -12,11 +12,13 @@ Per call (``RoutedAttention.step``):
    are runs of ``block`` tokens along it, or, with ``tile=(tt, th, tw)``,
    fixed tt x th x tw tiles ordered by the Gilbert curve of the tile grid
    [Light Interaction -- abstract: 3-D block-sparse attention];
-2. Q, K, V of the current chunk, raster token-major ``[L][heads][d]``, are
-   permuted into Gilbert head-major block-padded layout; K and V land in the
-   current chunk's slot of the KV store (the store grows by appending).  The
-   permutation of Q and K also writes their block means (the pooled
-   queries, and the chunk's rows of the pooled-key cache);
+2. K and V of the current chunk, raster token-major ``[L][heads][d]``, are
+   permuted into Gilbert head-major block-padded layout in the current
+   chunk's slot of the KV store (the store grows by appending); the
+   permutation of K also writes its block means into the pooled-key cache.
+   Q is only read for its block means (the pooled queries): with blocks
+   that are runs of the curve the attention reads Q in raster order through
+   the curve; fixed tiles permute Q into ``q_blk``;
 3. the router scores, fuses and selects over the visible history.  The
    pooled keys of the history are kept in a float64 cache across calls
    (the store only grows by appending), so a call pools only the blocks
@@ -28,6 +30,10 @@ Per call (``RoutedAttention.step``):
    Step 5];
 4. block-sparse attention over the selected blocks, whose epilogue writes
    O straight back in raster token order (the inverse permutation).
+
+``q_blk`` therefore holds the permuted queries only where something put
+them there (fixed tiles, or the caller, e.g. before ``route_and_attend`` or
+``dense``).
 
 Nothing here computes on the host: each step is one or more HIP kernels of
 ``libbsa.so`` on the current stream.
@@ -151,15 +157,20 @@ class RoutedAttention:
             self.to_blocks(k_raster, ks, stream)
         self.to_blocks(v_raster, vs, stream)
 
-    def permute_inputs(self, q_raster, k_raster, v_raster, c: int, stream=None):
+    def permute_inputs(self, q_raster, k_raster, v_raster, c: int, stream=None, q_blocks: bool = True):
         """Append chunk ``c``'s K and V to the store and permute its queries
         into ``q_blk``.  With curve blocks the queries' block means are
-        written by the same pass: returns them (``qbar``), else None."""
+        written by the same pass: returns them (``qbar``), else None.
+        ``q_blocks=False`` (curve blocks only): the block means alone, the
+        queries stay in raster order (the attention reads them there)."""
         self.append(k_raster, v_raster, c, stream)
         if self.tile is not None:
             self.to_blocks(q_raster, self.q_blk, stream)
             return None
-        gilbert_perm_pool(q_raster, self.perm, block=self.block, dst=self.q_blk, pool=self.qbar, stream=stream)
+        if q_blocks:
+            gilbert_perm_pool(q_raster, self.perm, block=self.block, dst=self.q_blk, pool=self.qbar, stream=stream)
+        else:
+            gilbert_perm_pool(q_raster, self.perm, block=self.block, pool=self.qbar, pool_only=True, stream=stream)
         return self.qbar
 
     def step(self, q_raster, k_raster, v_raster, c: int, *, k_fixed: Optional[int] = None,
@@ -176,21 +187,26 @@ class RoutedAttention:
         materialised lists instead of a top-K."""
         if refresh_index:
             self._index(stream)
-        qpool = self.permute_inputs(q_raster, k_raster, v_raster, c, stream)
+        # curve blocks: Q stays raster (its block means taken in one read),
+        # the attention reads it and writes O through the curve
+        q_raster_in = q_raster if self.tile is None else None
+        qpool = self.permute_inputs(q_raster, k_raster, v_raster, c, stream, q_blocks=self.tile is not None)
         r = self.route_and_attend(c, k_fixed=k_fixed, k_per_row=k_per_row, overlap=overlap, lam=lam, g_ref=g_ref,
-                                  tau=tau, materialize=materialize, qpool=qpool, out_raster=True, stream=stream,
-                                  attn_events=attn_events)
+                                  tau=tau, materialize=materialize, qpool=qpool, out_raster=True,
+                                  q_raster=q_raster_in, stream=stream, attn_events=attn_events)
         return self.o_raster, r
 
     def route_and_attend(self, c: int, *, k_fixed: Optional[int] = None, k_per_row: Optional[torch.Tensor] = None,
                          overlap: Optional[torch.Tensor] = None, lam=2.0, g_ref=0.2, tau=0.1,
-                         materialize: Optional[dict] = None, qpool=None, out_raster: bool = False, stream=None,
-                         attn_events=None):
+                         materialize: Optional[dict] = None, qpool=None, out_raster: bool = False, q_raster=None,
+                         stream=None, attn_events=None):
         """Route the already permuted queries over chunks 0..c of the store
         and attend; the result stays in Gilbert layout (``o_blk``, ``lse``),
         or with ``out_raster`` goes straight to ``o_raster`` (``o_blk`` is
         then not written).  ``qpool``: their pooled means, when already
-        computed."""
+        computed; ``q_raster``: the queries in raster order, read by the
+        attention in place of ``q_blk`` (needs ``qpool`` and
+        ``out_raster``)."""
         nkb = (c + 1) * self.nbc
         k_hist, v_hist = self.k_store[:, : nkb * self.block], self.v_store[:, : nkb * self.block]
         if materialize is not None:
@@ -199,7 +215,7 @@ class RoutedAttention:
         else:
             r = self.route(c, k_fixed=k_fixed, k_per_row=k_per_row, overlap=overlap, lam=lam, g_ref=g_ref, tau=tau,
                            qpool=qpool, stream=stream)
-        return self._attend(r, nkb, k_hist, v_hist, stream, attn_events, out_raster)
+        return self._attend(r, nkb, k_hist, v_hist, stream, attn_events, out_raster, q_raster)
 
     def route(self, c: int, *, k_fixed: Optional[int] = None, k_per_row: Optional[torch.Tensor] = None,
               overlap: Optional[torch.Tensor] = None, lam=2.0, g_ref=0.2, tau=0.1, qpool=None, stream=None):
@@ -256,16 +272,18 @@ class RoutedAttention:
             self._kpool_valid = max(valid, nkb)
         return r
 
-    def _attend(self, r, nkb, k_hist, v_hist, stream, attn_events, out_raster=False):
+    def _attend(self, r, nkb, k_hist, v_hist, stream, attn_events, out_raster=False, q_raster=None):
         if attn_events is not None:
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             ev[0].record(stream)
         if out_raster:
-            # the inverse permutation in the kernel's epilogue: row g -> token row_map[g]
+            # the inverse permutation in the kernel's epilogue: row g -> token
+            # row_map[g] (and, for raster queries, the forward one in its loads)
             row_map = self.perm if self.tile is None else self.row_cell
-            block_sparse_attn_raster(self.q_blk, k_hist, v_hist, r["row_ptr"], r["col_idx"], row_map,
-                                     block=self.block, scale=self.scale, q_block_len=self.q_len,
-                                     kv_block_len=self.kv_len[:nkb], out=self.o_raster, lse=self.lse, stream=stream)
+            block_sparse_attn_raster(self.q_blk if q_raster is None else q_raster, k_hist, v_hist, r["row_ptr"],
+                                     r["col_idx"], row_map, block=self.block, scale=self.scale,
+                                     q_block_len=self.q_len, kv_block_len=self.kv_len[:nkb], out=self.o_raster,
+                                     lse=self.lse, q_raster=q_raster is not None, stream=stream)
         else:
             block_sparse_attn(self.q_blk, k_hist, v_hist, r["row_ptr"], r["col_idx"], block=self.block,
                               scale=self.scale, q_block_len=self.q_len, kv_block_len=self.kv_len[:nkb],

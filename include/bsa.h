@@ -119,7 +119,9 @@ int bsa_gilbert_perm(const void* src, void* dst, const int32_t* perm, int L, int
  *  block); Key Contributions 3; Methodology, Step 6]
  *
  * src, dst, perm, L, heads, d, block, raster_token_stride,
- * gilbert_head_stride, dtype   as bsa_gilbert_perm with inverse = 0.
+ * gilbert_head_stride, dtype   as bsa_gilbert_perm with inverse = 0;
+ *                dst may be NULL: then only the block means are written
+ *                (gilbert_head_stride is ignored).
  * pool           device float64: block b of head h (b < n_blocks =
  *                ceil(L / block)) receives, at pool[h * pool_head_stride +
  *                b * d + c], the mean over the block's valid rows (rows
@@ -127,9 +129,9 @@ int bsa_gilbert_perm(const void* src, void* dst, const int32_t* perm, int L, int
  *                the router pools from dst).  pool may be a slice of a
  *                larger cache (pool_head_stride >= n_blocks * d, in
  *                elements); it must not overlap src or dst.
- * Errors: those of bsa_gilbert_perm; BSA_EINVAL (pool NULL or not 8-byte
- * aligned, pool_head_stride too small, heads > 65535, pool overlapping src
- * or dst).
+ * Errors: those of bsa_gilbert_perm (its src-side checks without dst);
+ * BSA_EINVAL (pool NULL or not 8-byte aligned, pool_head_stride too small,
+ * heads > 65535, pool overlapping src or dst).
  */
 int bsa_gilbert_perm_pool(const void* src, void* dst, const int32_t* perm, int L, int heads, int d, int block,
                           int64_t raster_token_stride, int64_t gilbert_head_stride, int dtype, double* pool,
@@ -531,33 +533,43 @@ int bsa_block_sparse_attn(const void* q, const void* k, const void* v, void* o, 
 /*
  * bsa_block_sparse_attn_raster -- bsa_block_sparse_attn with the output
  * written straight into raster token order (the inverse permutation fused
- * into the kernel's epilogue).
+ * into the kernel's epilogue) and, optionally, the queries read from raster
+ * order too (the forward permutation of Q fused into its loads).
  * [Velox -- Methodology, Step 6; Key Contributions 3 (Gilbert KV storage,
  *  outputs returned in the caller's order)]
  *
- *  o_row_map      device int32[o_rows], o_rows <= nqb*block: query row g
- *                 (of every head) goes to raster token o_row_map[g]; a
- *                 negative entry marks a padding row, which is not written.
- *                 For blocks that are runs of the curve this is the curve
- *                 itself (perm of bsa_gilbert_index, o_rows = T*H*W); for
- *                 fixed tiles it is the row map of bsa_gilbert_tile_index.
- *                 Entries must be distinct and index tokens of o.
+ *  row_map        device int32[rows], rows <= nqb*block: query row g (of
+ *                 every head) is raster token row_map[g]; a negative entry
+ *                 marks a padding row, which is not written (and, for
+ *                 raster queries, reads as zeros).  For blocks that are
+ *                 runs of the curve this is the curve itself (perm of
+ *                 bsa_gilbert_index, rows = T*H*W); for fixed tiles it is
+ *                 the row map of bsa_gilbert_tile_index.  Entries must be
+ *                 distinct and index tokens of o (and of q).  Rows >= rows
+ *                 are padding.
+ *  q_raster       0: q is blocked [heads][nqb*block][d] with head stride
+ *                 q_stride (as bsa_block_sparse_attn); 1: q is raster,
+ *                 element (token t, head h, channel c) at
+ *                 q[t * q_stride + h * d + c], query row g reading token
+ *                 row_map[g].
  *  o              raster output in dtype: element (token t, head h, channel
  *                 c) at o[t * o_token_stride + h * d + c]; tokens that no
  *                 row maps to are left untouched.
  * Every other argument, the lse layout (blocked, [heads][nqb*block]) and the
- * values written are those of bsa_block_sparse_attn.
- * Errors: those of bsa_block_sparse_attn; BSA_EINVAL (o_row_map NULL,
- * o_rows outside [1, nqb*block], o_token_stride below heads*d or not a
- * multiple of 16 bytes).
+ * values written are those of bsa_block_sparse_attn (padding query rows
+ * must also be padding in q_block_len).
+ * Errors: those of bsa_block_sparse_attn; BSA_EINVAL (row_map NULL, rows
+ * outside [1, nqb*block], q_raster not 0 or 1, o_token_stride or a raster
+ * q_stride below heads*d or not a multiple of 16 bytes).
  */
 int bsa_block_sparse_attn_raster(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int dtype, int heads, int d, int block, int nqb, int nkb,
-                                 int64_t q_head_stride, int64_t k_head_stride, int64_t v_head_stride,
-                                 const int32_t* o_row_map, int o_rows, int64_t o_token_stride,
-                                 const int32_t* q_block_len, const int32_t* kv_block_len,
-                                 const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
-                                 float scale, hipStream_t stream);
+                                 int q_raster, int64_t q_stride, int64_t k_head_stride,
+                                 int64_t v_head_stride, const int32_t* row_map, int rows,
+                                 int64_t o_token_stride, const int32_t* q_block_len,
+                                 const int32_t* kv_block_len, const int32_t* row_ptr,
+                                 const int32_t* col_idx, int64_t col_len, float scale,
+                                 hipStream_t stream);
 
 /*
  * bsa_dense_attn -- the dense baseline: bsa_block_sparse_attn with every KV

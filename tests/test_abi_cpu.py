@@ -85,6 +85,12 @@ def test_gilbert_perm_pool_rejects():
         == bsa.BSA_EUNSUPPORTED                                               # the permutation's own checks
     assert f(FAKE, FAKE2, FAKE, 4680, 70000, 128, 128, 70000 * 128, 4736 * 128, 0, POOL, 37 * 128, None) \
         == bsa.BSA_EINVAL                                                     # heads beyond the grid
+    # block means only (no dst): the source-side checks still apply
+    assert f(FAKE, None, FAKE, 4680, 40, 128, 128, 100, 0, 0, POOL, 37 * 128, None) == bsa.BSA_EINVAL
+    assert f(None, None, FAKE, 4680, 40, 128, 128, 5120, 0, 0, POOL, 37 * 128, None) == bsa.BSA_EINVAL
+    assert f(FAKE, None, FAKE, 4680, 40, 96, 128, 5120, 0, 0, POOL, 37 * 128, None) == bsa.BSA_EUNSUPPORTED
+    assert f(FAKE, None, FAKE, 4680, 40, 128, 128, 5120, 0, 0, ctypes.c_void_p(0x10000 + 4096), 37 * 128,
+             None) == bsa.BSA_EINVAL                                          # pool inside src
 
 
 def _attn(**over):
@@ -116,17 +122,22 @@ def test_attention_rejects():
 
 
 def test_raster_attention_rejects():
-    def f(o_map=FAKE, o_rows=4680, o_ts=40 * 128, d=128):
-        return lib.bsa_block_sparse_attn_raster(FAKE, FAKE, FAKE, FAKE2, None, 0, 40, d, 128, 37, 1776,
-                                                37 * 128 * 128, 1776 * 128 * 128, 1776 * 128 * 128, o_map, o_rows,
-                                                o_ts, None, None, FAKE, FAKE, 1480 * 50, ctypes.c_float(0.088), None)
+    def f(o_map=FAKE, o_rows=4680, o_ts=40 * 128, d=128, q_raster=0, q_stride=37 * 128 * 128):
+        return lib.bsa_block_sparse_attn_raster(FAKE, FAKE, FAKE, FAKE2, None, 0, 40, d, 128, 37, 1776, q_raster,
+                                                q_stride, 1776 * 128 * 128, 1776 * 128 * 128, o_map, o_rows, o_ts,
+                                                None, None, FAKE, FAKE, 1480 * 50, ctypes.c_float(0.088), None)
     assert f(o_map=None) == bsa.BSA_EINVAL
-    assert "o_row_map" in lib.bsa_last_error_detail().decode()
+    assert "row_map" in lib.bsa_last_error_detail().decode()
     assert f(o_rows=0) == bsa.BSA_EINVAL
     assert f(o_rows=37 * 128 + 1) == bsa.BSA_EINVAL
     assert f(o_ts=40 * 128 - 8) == bsa.BSA_EINVAL
     assert f(o_ts=40 * 128 + 4) == bsa.BSA_EINVAL           # 8 bytes: breaks 16-byte token rows
     assert f(d=80) == bsa.BSA_EUNSUPPORTED                   # the attention checks come first
+    assert f(q_raster=2) == bsa.BSA_EINVAL
+    assert f(q_stride=37 * 128 * 128 - 8) == bsa.BSA_EINVAL  # blocked q: a head stride
+    assert f(q_raster=1, q_stride=40 * 128 - 8) == bsa.BSA_EINVAL     # raster q: a token stride
+    assert "q_stride" in lib.bsa_last_error_detail().decode()
+    assert f(q_raster=1, q_stride=40 * 128 + 4) == bsa.BSA_EINVAL
 
 
 def _route_args(**over):

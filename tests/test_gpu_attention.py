@@ -187,6 +187,22 @@ def test_raster_output_is_the_blocked_output_permuted(name):
     written = np.zeros(tokens + 3, dtype=bool)
     written[m[g]] = True
     assert torch.all(got[torch.from_numpy(~written)] == 7.0)
+    # the queries read in raster order through the same map: the same bits
+    # (rows the map leaves out read as zeros, as the blocked padding rows)
+    q_r = torch.full((tokens + 3, w.heads, w.d), 5.0, dtype=q.dtype, device=dev)
+    qb = q.transpose(0, 1)                                  # [rows][heads][d] view of the blocked queries
+    idx = torch.from_numpy(g).long().to(dev)
+    q_r[torch.from_numpy(m[g]).long().to(dev)] = qb[idx]
+    pad = torch.ones(q.shape[1], dtype=torch.bool, device=dev)
+    pad[idx] = False
+    q_zero = q.clone()
+    q_zero[:, pad] = 0                                      # unmapped rows read as zeros
+    o_z, l_z = bsa.block_sparse_attn_raster(q_zero, k, v, r["row_ptr"], r["col_idx"], row_map,
+                                            out=torch.full_like(out, 7.0), **args)
+    o_q, l_q = bsa.block_sparse_attn_raster(q_r, k, v, r["row_ptr"], r["col_idx"], row_map, q_raster=True,
+                                            nqb=w.nqb, out=torch.full_like(out, 7.0), **args)
+    torch.cuda.synchronize()
+    assert torch.equal(o_q, o_z) and torch.equal(l_q, l_z)
     print(name, "rows mapped", len(g), "of", len(m))
 
 

@@ -93,6 +93,10 @@ def test_permute_pool_bitwise_and_exact_means(dtype, block, d):
     assert lens[-1] < block
     for h in range(heads):
         assert np.array_equal(pool[h].cpu().numpy(), oroute.pool_blocks(ref[h], lens, block)), h
+    # the block means alone (nothing permuted): the same values
+    none, pool2 = bsa.gilbert_perm_pool(src.to(dev), perm, block=block, pool_only=True)
+    torch.cuda.synchronize()
+    assert none is None and torch.equal(pool2, pool)
 
 
 def test_permute_pool_into_cache_slice():
