@@ -940,29 +940,38 @@ def main():
 def sweep(st, path):
     """History-length sweep (chunk 1..C) of the routed call (route + sparse
     attention) and of dense attention, on the resident store; the queries
-    stay those of the last chunk."""
+    stay those of the last chunk.  All sparse timings come first (each chunk
+    warmed, then timed back to back), then all dense ones, so the heat of
+    the long dense launches does not lower the clock under the sparse ones."""
+    import statistics
+
     import torch
     ra = st["ra"]
+    sparse = {}
+    for c in range(1, ra.store_chunks + 1):
+        cur = c - 1
+        for _ in range(10):
+            ra.route_and_attend(cur)
+        ev = []
+        for _ in range(10):
+            ra.route_and_attend(cur, attn_events=ev)
+        torch.cuda.synchronize()
+        sparse[c] = statistics.median(a.elapsed_time(b) for a, b in ev)
+        print("sweep sparse chunk %d done" % c, file=sys.stderr, flush=True)
     with open(path, "w") as f:
         for c in range(1, ra.store_chunks + 1):
             cur = c - 1
-            ra.route_and_attend(cur)
-            torch.cuda.synchronize()
-            ev = []
-            for _ in range(5):
-                ra.route_and_attend(cur, attn_events=ev)
-            torch.cuda.synchronize()
-            sparse_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+            ra.dense(cur)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(3):
                 ra.dense(cur)
             e1.record()
             torch.cuda.synchronize()
-            f.write(json.dumps({"chunk": c, "sparse_attn_ms": round(sparse_ms, 4),
+            f.write(json.dumps({"chunk": c, "sparse_attn_ms": round(sparse[c], 4),
                                 "dense_attn_ms": round(e0.elapsed_time(e1) / 3, 4)}) + "\n")
             f.flush()
-            print("sweep chunk %d done" % c, file=sys.stderr, flush=True)
+            print("sweep dense chunk %d done" % c, file=sys.stderr, flush=True)
 
 
 def oracle_table(st, path):
