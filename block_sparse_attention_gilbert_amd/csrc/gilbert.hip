@@ -110,7 +110,7 @@ gilbert_perm_pool_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
     const int64_t i0 = (int64_t)b * block;
     const int valid = (int)(L - i0 < block ? L - i0 : block);
     const int64_t hc = (int64_t)h * chunks + ch;
-    uint4* out = dst + h * gilbert_head_stride_c + i0 * chunks + ch;
+    uint4* out = dst ? dst + h * gilbert_head_stride_c + i0 * chunks + ch : nullptr;
     double acc[CE];
 #pragma unroll
     for (int e = 0; e < CE; ++e) acc[e] = 0.0;
@@ -118,7 +118,7 @@ gilbert_perm_pool_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
     for (int k = g; k < block; k += groups) {
         uint4 u = make_uint4(0u, 0u, 0u, 0u);
         if (k < valid) u = src[(int64_t)perm[i0 + k] * raster_token_stride_c + hc];
-        if (dst) out[(int64_t)k * chunks] = u;
+        if (out) out[(int64_t)k * chunks] = u;
         const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
         if (BF16) {
 #pragma unroll
