@@ -1,5 +1,5 @@
 """Full-size parity in the benchmark's launch configuration: C4 at chunk 48
-(the headline workload) and C5 (48 ragged chunks), checked on sampled heads
+(the headline workload, routed and dense) and C5 (48 ragged chunks), checked on sampled heads
 (every route of those heads bit-exact) and sampled query rows (attention),
 plus size-independent properties on every head."""
 
@@ -13,7 +13,7 @@ from oracle import layout as olay
 from oracle import route as oroute
 from oracle.gilbert import gilbert_order
 
-from helpers import BF16_MAX_ABS, BF16_MEAN_ABS, assert_lists_equal, csr_lists, f64, need_gpu
+from helpers import BF16_MAX_ABS, BF16_MEAN_ABS, LSE_BF16, assert_lists_equal, csr_lists, f64, need_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -171,3 +171,28 @@ def test_c4_chunk48_fixed_tiles_sampled_heads():
         err = np.abs(f64(o_r[:, hi, :])[row_cell[rows]] - o_ref[rows])
         print("tiles head", h, "max", err.max(), "mean", err.mean(), flush=True)
         assert err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS
+
+
+def test_c4_chunk48_dense_sampled():
+    """Dense attention over the whole chunk-48 history (224,640 keys per
+    query) through the same kernel, as the bench times it: sampled rows of
+    two heads against the oracle's dense softmax, and LSE."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    heads = [4, 31]
+    w = workloads.c4(c=48, heads=heads)
+    ql = torch.from_numpy(w.q_len).to(dev)
+    kl = torch.from_numpy(w.k_len).to(dev)
+    o, lse = bsa.dense_attn(w.q.to(dev), w.k.to(dev), w.v.to(dev), block=128, scale=w.scale, q_block_len=ql,
+                            kv_block_len=kl, lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(21)
+    for hi, h in enumerate(heads):
+        rows = _sample_rows(rng, w.q_len, w.bs, n=16)
+        o_ref, l_ref = oatt.dense_head(f64(w.q[hi]), f64(w.k[hi]), f64(w.v[hi]), w.q_len, w.k_len, w.bs, w.scale,
+                                       rows=rows)
+        err = np.abs(f64(o[hi])[rows] - o_ref[rows])
+        lerr = np.abs(lse[hi].cpu().numpy().astype(np.float64)[rows] - l_ref[rows])
+        print("dense head", h, "max", err.max(), "mean", err.mean(), "lse", lerr.max(), flush=True)
+        assert err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS
+        assert lerr.max() <= LSE_BF16
