@@ -220,3 +220,26 @@ def test_route_maximum_candidates():
         bsa.route_topk(q.to(dev), torch.zeros((heads, (n_cand + 1) * bs, d), dtype=torch.bfloat16, device=dev),
                        block=bs, nqb=nqb, nkb=n_cand + 1, scale=0.125, k_fixed=5)
     assert err.value.code == bsa.BSA_EUNSUPPORTED
+
+
+def test_route_selection_paths():
+    """Every path of the threshold select against the oracle: budgets of up
+    to 64, 128 and 256 (the three fast-path widths), above 256 (the radix
+    select), and a query block whose keys all tie (all-zero queries: every
+    score is 0, so the fast path's candidate gather overflows and the radix
+    select takes the lowest indices)."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    rng = np.random.default_rng(77)
+    heads, d, bs, nqb, nkb = 2, 64, 64, 4, 1000
+    q = torch.from_numpy(rng.standard_normal((heads, nqb * bs, d)).astype(np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy(rng.standard_normal((heads, nkb * bs, d)).astype(np.float32)).to(torch.bfloat16)
+    q[:, 2 * bs:3 * bs] = 0                                # query block 2: every score ties
+    for K in (50, 100, 200, 300):
+        r = bsa.route_topk(q.to(dev), k.to(dev), block=bs, nqb=nqb, nkb=nkb, scale=0.125, k_fixed=K)
+        got = csr_lists(r["row_ptr"], r["col_idx"], heads, nqb)
+        for h in range(heads):
+            ref = oroute.route_head(f64(q[h]), f64(k[h]), [bs] * nqb, [bs] * nkb, bs, scale=0.125,
+                                    k_per_row=[K] * nqb)
+            assert_lists_equal(got[h], ref["lists"], "K=%d head %d" % (K, h))
+            assert np.array_equal(got[h][2], np.arange(K))  # ties: the lowest indices
