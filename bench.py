@@ -639,6 +639,9 @@ def step_kernel_alg_bytes():
                                      "mean of Q (raster read, block means written) and K (raster read, "
                                      "blocked written, block means written)"),
         "gilbert_perm_kernel<false>": (raster + blocked, "raster read, blocked written"),
+        "gilbert_perm_pool_batch_kernel": (3 * raster + 2 * blocked + 2 * pooled,
+                                           "Q, K and V raster read; K and V blocked written; block means "
+                                           "of Q and K written"),
         "score_kernel": (heads * n_cand * d * 8 + pooled + keys,
                          "pooled keys and queries read, selection keys written"),
         "topk_kernel": (keys + lists, "selection keys read, lists written"),
@@ -877,9 +880,10 @@ def main():
         "config": {"workload": "C4 growing-context 14B-like layer at chunk %d" % args.chunk,
                    "heads": w.heads, "head_dim": w.d, "block": w.bs, "query_tokens": 4680,
                    "kv_tokens": 4680 * args.chunk, "kv_blocks": w.nkb, "top_k": 50,
-                   "step": "gilbert_index + 3 forward permutes + route (pool Q and the new chunk's K, cached "
-                           "history pools; score all 1776 candidates; top-K) + block-sparse attention "
-                           "+ inverse permute", "parallelism": "single GPU"},
+                   "step": "gilbert_index + one launch permuting K and V into the store (K with its block "
+                           "means, Q block means only) + route (cached history pools; score all 1776 "
+                           "candidates; top-K) + block-sparse attention reading Q and writing O in raster "
+                           "order", "parallelism": "single GPU"},
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "attn": {"ms_per_call": round(attn_ms, 4),
                  "ms_median": round(attn_all[len(attn_all) // 2], 4),

@@ -76,6 +76,16 @@ class MaterializeArgs(ctypes.Structure):
     ]
 
 
+class PermJob(ctypes.Structure):
+    """Mirror of ``bsa_perm_job``."""
+    _fields_ = [
+        ("src", _p), ("dst", _p), ("raster_token_stride", _i64), ("gilbert_head_stride", _i64),
+        ("pool", _p), ("pool_head_stride", _i64),
+    ]
+
+
+MAX_PERM_JOBS = 4  # BSA_MAX_PERM_JOBS
+
 _lib.bsa_version.restype = _i
 _lib.bsa_strerror.restype = ctypes.c_char_p
 _lib.bsa_strerror.argtypes = [_i]
@@ -86,6 +96,8 @@ _lib.bsa_gilbert_perm.restype = _i
 _lib.bsa_gilbert_perm.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i64, _i64, _i, _i, _p]
 _lib.bsa_gilbert_perm_pool.restype = _i
 _lib.bsa_gilbert_perm_pool.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i64, _i64, _i, _p, _i64, _p]
+_lib.bsa_gilbert_perm_pool_batch.restype = _i
+_lib.bsa_gilbert_perm_pool_batch.argtypes = [ctypes.POINTER(PermJob), _i, _p, _i, _i, _i, _i, _i, _p]
 _lib.bsa_gilbert_block_window.restype = _i
 _lib.bsa_gilbert_block_window.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p]
 _lib.bsa_route_materialize_workspace_size.restype = ctypes.c_size_t
@@ -121,11 +133,11 @@ _lib.bsa_dense_attn.restype = _i
 _lib.bsa_dense_attn.argtypes = _ATTN_COMMON + [_f, _p]
 
 EXPORTED = ("bsa_version", "bsa_strerror", "bsa_last_error_detail", "bsa_gilbert_index", "bsa_gilbert_perm",
-            "bsa_gilbert_perm_pool", "bsa_gilbert_block_window", "bsa_gilbert_tile_index", "bsa_tile_perm",
-            "bsa_tile_block_window", "bsa_route_workspace_size", "bsa_route_topk",
-            "bsa_route_materialize_workspace_size", "bsa_route_materialize", "bsa_slab_overlap", "bsa_slab_coverage",
-            "bsa_slab_coverage_workspace_size", "bsa_block_sparse_attn", "bsa_block_sparse_attn_raster",
-            "bsa_dense_attn", "bsa_diag_mfma_bf16")
+            "bsa_gilbert_perm_pool", "bsa_gilbert_perm_pool_batch", "bsa_gilbert_block_window",
+            "bsa_gilbert_tile_index", "bsa_tile_perm", "bsa_tile_block_window", "bsa_route_workspace_size",
+            "bsa_route_topk", "bsa_route_materialize_workspace_size", "bsa_route_materialize", "bsa_slab_overlap",
+            "bsa_slab_coverage", "bsa_slab_coverage_workspace_size", "bsa_block_sparse_attn",
+            "bsa_block_sparse_attn_raster", "bsa_dense_attn", "bsa_diag_mfma_bf16")
 
 
 class BsaError(RuntimeError):
@@ -263,6 +275,46 @@ def gilbert_perm_pool(src: torch.Tensor, perm: torch.Tensor, *, block: int, dst:
     _check(_lib.bsa_gilbert_perm_pool(_ptr(src), _ptr(dst), _ptr(perm), L_, heads, d, block, src.stride(0), ghs,
                                       _dtype_code(src), _ptr(pool), pool.stride(0), _stream(stream)))
     return dst, pool
+
+
+def gilbert_perm_pool_batch(jobs, perm: torch.Tensor, *, block: int, stream=None):
+    """Several raster tensors of one chunk through one launch: ``jobs`` is a
+    list of ``(src, dst, pool)`` with ``src`` raster ``[L][heads][d]`` (the
+    same shape and dtype for every job), ``dst`` a Gilbert
+    ``[heads][>= n_blocks*block][d]`` view or None (block means only) and
+    ``pool`` a float64 ``[heads][>= n_blocks][d]`` view or None (the
+    permutation only); a job needs one of them.  Each job's results equal
+    ``gilbert_perm_pool`` (or ``gilbert_perm``) on it alone.  Returns
+    ``jobs``."""
+    if not 1 <= len(jobs) <= MAX_PERM_JOBS:
+        raise ValueError("1 to %d jobs, got %d" % (MAX_PERM_JOBS, len(jobs)))
+    _need_gpu(perm, *[t for job in jobs for t in job])
+    perm = _i32(perm, "perm")
+    shape, dtype = jobs[0][0].shape, jobs[0][0].dtype
+    L_, heads, d = shape
+    nb = -(-L_ // block)
+    arr = (PermJob * len(jobs))()
+    for z, (src, dst, pool) in enumerate(jobs):
+        if src.shape != shape or src.dtype != dtype:
+            raise ValueError("job %d: every src must have the shape and dtype of the first" % z)
+        if src.stride(2) != 1 or src.stride(1) != d:
+            raise ValueError("job %d: raster src must have contiguous [heads][d] per token" % z)
+        if dst is None and pool is None:
+            raise ValueError("job %d: needs a dst or a pool" % z)
+        ghs = 0
+        if dst is not None:
+            _, drows, ghs = _heads_rows(dst, d)
+            if drows < nb * block or dst.dtype != dtype:
+                raise ValueError("job %d: dst must be %s with >= %d rows per head" % (z, dtype, nb * block))
+        if pool is not None and (pool.dtype != torch.float64 or pool.dim() != 3 or pool.shape[0] != heads
+                                 or pool.shape[1] < nb or pool.shape[2] != d or pool.stride(2) != 1
+                                 or pool.stride(1) != d):
+            raise ValueError("job %d: pool must be float64 [heads][>= n_blocks][d] with contiguous blocks" % z)
+        arr[z] = PermJob(_ptr(src), _ptr(dst) if dst is not None else None, src.stride(0), ghs,
+                         _ptr(pool) if pool is not None else None, pool.stride(0) if pool is not None else 0)
+    _check(_lib.bsa_gilbert_perm_pool_batch(arr, len(jobs), _ptr(perm), L_, heads, d, block,
+                                            _dtype_code(jobs[0][0]), _stream(stream)))
+    return jobs
 
 
 def gilbert_block_window(perm: torch.Tensor, inv: torch.Tensor, grid, *, block: int, q_chunk: int,
@@ -700,9 +752,10 @@ def dense_attn(q, k, v, *, block: int, scale: Optional[float] = None, q_block_le
     return out, lse
 
 
-__all__ = ["gilbert_index", "gilbert_perm", "gilbert_perm_pool", "gilbert_block_window", "gilbert_tile_index",
-           "tile_perm", "tile_block_window", "tile_grid", "slab_overlap", "slab_coverage", "route_topk",
-           "route_workspace_size", "route_capacity", "route_materialize", "route_materialize_workspace_size",
-           "materialize_capacity", "MaterializeArgs", "block_sparse_attn", "block_sparse_attn_raster", "dense_attn",
-           "version", "library", "BsaError", "RouteArgs", "EXPORTED", "BSA_OK", "BSA_EINVAL", "BSA_EUNSUPPORTED",
-           "BSA_EWORKSPACE", "BSA_EHIP", "BSA_BF16", "BSA_F32"]
+__all__ = ["gilbert_index", "gilbert_perm", "gilbert_perm_pool", "gilbert_perm_pool_batch", "gilbert_block_window",
+           "gilbert_tile_index", "tile_perm", "tile_block_window", "tile_grid", "slab_overlap", "slab_coverage",
+           "route_topk", "route_workspace_size", "route_capacity", "route_materialize",
+           "route_materialize_workspace_size", "materialize_capacity", "MaterializeArgs", "block_sparse_attn",
+           "block_sparse_attn_raster", "dense_attn", "version", "library", "BsaError", "RouteArgs", "PermJob",
+           "MAX_PERM_JOBS", "EXPORTED", "BSA_OK", "BSA_EINVAL", "BSA_EUNSUPPORTED", "BSA_EWORKSPACE", "BSA_EHIP",
+           "BSA_BF16", "BSA_F32"]

@@ -46,6 +46,15 @@ int bsa_gilbert_perm_pool(const void* src, void* dst, const int32_t* perm, int L
                       "gilbert_perm_pool launch");
 }
 
+int bsa_gilbert_perm_pool_batch(const bsa_perm_job* jobs, int n_jobs, const int32_t* perm, int L, int heads, int d,
+                                int block, int dtype, hipStream_t stream) {
+    bsa::clear_error();
+    const int st = bsa::validate_gilbert_perm_pool_batch(jobs, n_jobs, perm, L, heads, d, block, dtype);
+    if (st != BSA_OK) return st;
+    return hip_status(bsa::launch_gilbert_perm_pool_batch(jobs, n_jobs, perm, L, heads, d, block, dtype, stream),
+                      "gilbert_perm_pool_batch launch");
+}
+
 int bsa_route_topk(const bsa_route_args* args, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     bsa::clear_error();
     bsa::RouteLayout lay;

@@ -56,6 +56,8 @@ int validate_gilbert_perm(const void* src, const void* dst, const int32_t* perm,
 int validate_gilbert_perm_pool(const void* src, const void* dst, const int32_t* perm, int L, int heads, int d,
                                int block, int64_t raster_token_stride, int64_t gilbert_head_stride, int dtype,
                                const double* pool, int64_t pool_head_stride);
+int validate_gilbert_perm_pool_batch(const bsa_perm_job* jobs, int n_jobs, const int32_t* perm, int L, int heads,
+                                     int d, int block, int dtype);
 int validate_attn(const AttnProblem& p, bool dense);
 int validate_raster_out(const AttnProblem& p);
 int validate_route(const bsa_route_args* a, RouteLayout* lay);

@@ -96,15 +96,14 @@ gilbert_perm_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, cons
 // pooled from the permuted tensor by any summation order.
 // [Velox -- Methodology, Step 4: mean query and mean key vectors per block;
 //  Step 6: neighbouring regions contiguous in the block-padded layout]
-template <bool BF16>
-__global__ void __launch_bounds__(256)
-gilbert_perm_pool_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, const int32_t* __restrict__ perm,
-                         int L, int d, int block, int64_t raster_token_stride_c, int64_t gilbert_head_stride_c,
-                         double* __restrict__ pool, int64_t pool_head_stride) {
+template <bool BF16, bool POOL>
+__device__ __forceinline__ void perm_pool_block(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                const int32_t* __restrict__ perm, int L, int d, int block, int b,
+                                                int h, int64_t raster_token_stride_c, int64_t gilbert_head_stride_c,
+                                                double* __restrict__ pool, int64_t pool_head_stride) {
     constexpr int CE = BF16 ? 8 : 4;  // elements per 16-byte chunk
     __shared__ double part[4][128];
     const int t = threadIdx.x, w = t >> 6;
-    const int b = blockIdx.x, h = blockIdx.y;
     const int chunks = d / CE, groups = 256 / chunks;
     const int ch = t % chunks, g = t / chunks;
     const int64_t i0 = (int64_t)b * block;
@@ -119,6 +118,7 @@ gilbert_perm_pool_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
         uint4 u = make_uint4(0u, 0u, 0u, 0u);
         if (k < valid) u = src[(int64_t)perm[i0 + k] * raster_token_stride_c + hc];
         if (out) out[(int64_t)k * chunks] = u;
+        if (!POOL) continue;
         const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
         if (BF16) {
 #pragma unroll
@@ -131,6 +131,7 @@ gilbert_perm_pool_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
             for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(wd[e]);
         }
     }
+    if (!POOL) return;
     for (int off = chunks; off < 64; off <<= 1)
 #pragma unroll
         for (int e = 0; e < CE; ++e) acc[e] += __shfl_xor(acc[e], off);
@@ -142,6 +143,50 @@ gilbert_perm_pool_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
         const double sum = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
         pool[h * pool_head_stride + (int64_t)b * d + t] = sum / (double)valid;
     }
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256)
+gilbert_perm_pool_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, const int32_t* __restrict__ perm,
+                         int L, int d, int block, int64_t raster_token_stride_c, int64_t gilbert_head_stride_c,
+                         double* __restrict__ pool, int64_t pool_head_stride) {
+    perm_pool_block<BF16, true>(src, dst, perm, L, d, block, blockIdx.x, blockIdx.y, raster_token_stride_c,
+                                gilbert_head_stride_c, pool, pool_head_stride);
+}
+
+// Several tensors of one chunk (Q, K, V) permuted and/or pooled by one
+// launch: grid.z picks the tensor, and each (block, head, tensor) workgroup
+// does what the single-tensor kernel above does, the block means skipped
+// where the tensor has no pool.  One launch instead of three keeps the copy
+// engines busy across the tensors' tails.
+constexpr int kMaxPermJobs = BSA_MAX_PERM_JOBS;
+
+struct PermJobs {
+    const uint4* src[kMaxPermJobs];
+    uint4* dst[kMaxPermJobs];
+    double* pool[kMaxPermJobs];
+    int64_t rts_c[kMaxPermJobs], ghs_c[kMaxPermJobs], phs[kMaxPermJobs];
+};
+
+// job z of the kernel argument (a select chain: indexing a by-value array
+// with a runtime index would copy it to scratch memory)
+template <class T>
+__device__ __forceinline__ T pick(const T (&v)[kMaxPermJobs], int z) {
+    static_assert(kMaxPermJobs == 4, "select chain covers four jobs");
+    return z == 0 ? v[0] : z == 1 ? v[1] : z == 2 ? v[2] : v[3];
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256)
+gilbert_perm_pool_batch_kernel(PermJobs j, const int32_t* __restrict__ perm, int L, int d, int block) {
+    const int z = blockIdx.z;
+    double* const pool = pick(j.pool, z);
+    if (pool)
+        perm_pool_block<BF16, true>(pick(j.src, z), pick(j.dst, z), perm, L, d, block, blockIdx.x, blockIdx.y,
+                                    pick(j.rts_c, z), pick(j.ghs_c, z), pool, pick(j.phs, z));
+    else
+        perm_pool_block<BF16, false>(pick(j.src, z), pick(j.dst, z), perm, L, d, block, blockIdx.x, blockIdx.y,
+                                     pick(j.rts_c, z), pick(j.ghs_c, z), nullptr, 0);
 }
 
 }  // namespace
@@ -324,6 +369,26 @@ hipError_t launch_gilbert_perm_pool(const void* src, void* dst, const int32_t* p
     else
         hipLaunchKernelGGL(gilbert_perm_pool_kernel<false>, grid, dim3(256), 0, stream, static_cast<const uint4*>(src),
                            static_cast<uint4*>(dst), perm, L, d, block, rts_c, ghs_c, pool, pool_head_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_gilbert_perm_pool_batch(const bsa_perm_job* jobs, int n_jobs, const int32_t* perm, int L,
+                                          int heads, int d, int block, int dtype, hipStream_t stream) {
+    const int chunk_elems = dtype == BSA_BF16 ? 8 : 4;
+    PermJobs j{};
+    for (int z = 0; z < n_jobs; ++z) {
+        j.src[z] = static_cast<const uint4*>(jobs[z].src);
+        j.dst[z] = static_cast<uint4*>(jobs[z].dst);
+        j.pool[z] = jobs[z].pool;
+        j.rts_c[z] = jobs[z].raster_token_stride / chunk_elems;
+        j.ghs_c[z] = jobs[z].gilbert_head_stride / chunk_elems;
+        j.phs[z] = jobs[z].pool_head_stride;
+    }
+    const dim3 grid((unsigned)((L + block - 1) / block), (unsigned)heads, (unsigned)n_jobs);
+    if (dtype == BSA_BF16)
+        hipLaunchKernelGGL(gilbert_perm_pool_batch_kernel<true>, grid, dim3(256), 0, stream, j, perm, L, d, block);
+    else
+        hipLaunchKernelGGL(gilbert_perm_pool_batch_kernel<false>, grid, dim3(256), 0, stream, j, perm, L, d, block);
     return hipGetLastError();
 }
 

@@ -18,6 +18,9 @@ hipError_t launch_gilbert_perm_pool(const void* src, void* dst, const int32_t* p
                                     int block, int64_t raster_token_stride, int64_t gilbert_head_stride, int dtype,
                                     double* pool, int64_t pool_head_stride, hipStream_t stream);
 
+hipError_t launch_gilbert_perm_pool_batch(const bsa_perm_job* jobs, int n_jobs, const int32_t* perm, int L,
+                                          int heads, int d, int block, int dtype, hipStream_t stream);
+
 hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* ws, hipStream_t stream);
 
 hipError_t launch_block_window(const int32_t* perm, const int32_t* inv, int T, int H, int W, int block, int q_chunk,

@@ -103,6 +103,49 @@ int validate_gilbert_perm_pool(const void* src, const void* dst, const int32_t* 
     return BSA_OK;
 }
 
+int validate_gilbert_perm_pool_batch(const bsa_perm_job* jobs, int n_jobs, const int32_t* perm, int L, int heads,
+                                     int d, int block, int dtype) {
+    if (!jobs) return fail(BSA_EINVAL, "jobs must be non-NULL");
+    if (n_jobs < 1 || n_jobs > BSA_MAX_PERM_JOBS)
+        return fail(BSA_EINVAL, "n_jobs = %d outside [1, %d]", n_jobs, BSA_MAX_PERM_JOBS);
+    if (heads > 65535) return fail(BSA_EINVAL, "heads = %d exceeds 65535", heads);
+    struct Range {
+        const char* p;
+        int64_t n;
+    };
+    Range src[BSA_MAX_PERM_JOBS], out[BSA_MAX_PERM_JOBS][2];
+    const int eb = dtype_bytes(dtype);
+    for (int z = 0; z < n_jobs; ++z) {
+        const bsa_perm_job& j = jobs[z];
+        if (!j.dst && !j.pool) return fail(BSA_EINVAL, "job %d has neither dst nor pool", z);
+        const int st = j.pool ? validate_gilbert_perm_pool(j.src, j.dst, perm, L, heads, d, block,
+                                                           j.raster_token_stride, j.gilbert_head_stride, dtype,
+                                                           j.pool, j.pool_head_stride)
+                              : validate_gilbert_perm(j.src, j.dst, perm, L, heads, d, block, j.raster_token_stride,
+                                                      j.gilbert_head_stride, 0, dtype);
+        if (st != BSA_OK) {
+            char why[sizeof(g_detail)];
+            snprintf(why, sizeof(why), "%s", g_detail);
+            return fail(st, "job %d: %s", z, why);
+        }
+        const int64_t nb = ceil_div(L, block);
+        src[z] = {static_cast<const char*>(j.src), ((int64_t)(L - 1) * j.raster_token_stride + (int64_t)heads * d) * eb};
+        out[z][0] = {static_cast<const char*>(j.dst),
+                     j.dst ? ((int64_t)(heads - 1) * j.gilbert_head_stride + nb * block * d) * eb : 0};
+        out[z][1] = {reinterpret_cast<const char*>(j.pool),
+                     j.pool ? ((int64_t)(heads - 1) * j.pool_head_stride + nb * d) * (int64_t)sizeof(double) : 0};
+    }
+    auto hit = [](const Range& a, const Range& b) { return a.n > 0 && b.n > 0 && a.p < b.p + b.n && b.p < a.p + a.n; };
+    for (int z = 0; z < n_jobs; ++z)
+        for (int y = 0; y < n_jobs; ++y) {
+            if (y == z) continue;
+            for (int o = 0; o < 2; ++o)
+                if (hit(out[z][o], src[y]) || hit(out[z][o], out[y][0]) || hit(out[z][o], out[y][1]))
+                    return fail(BSA_EINVAL, "job %d's %s overlaps job %d's buffers", z, o ? "pool" : "dst", y);
+        }
+    return BSA_OK;
+}
+
 int validate_raster_out(const AttnProblem& p) {
     if (!p.o_map) return fail(BSA_EINVAL, "row_map must be non-NULL");
     if (p.o_map_len < 1 || (int64_t)p.o_map_len > (int64_t)p.nqb * p.block)

@@ -18,7 +18,8 @@ Per call (``RoutedAttention.step``):
    permutation of K also writes its block means into the pooled-key cache.
    Q is only read for its block means (the pooled queries): with blocks
    that are runs of the curve the attention reads Q in raster order through
-   the curve; fixed tiles permute Q into ``q_blk``;
+   the curve; fixed tiles permute Q into ``q_blk``.  With curve blocks and
+   the pooled-key cache, Q, K and V go through one launch;
 3. the router scores, fuses and selects over the visible history.  The
    pooled keys of the history are kept in a float64 cache across calls
    (the store only grows by appending), so a call pools only the blocks
@@ -47,8 +48,9 @@ from typing import Optional
 import torch
 
 from . import (_check, _lib, _ptr, _stream, block_sparse_attn, block_sparse_attn_raster, dense_attn,
-               gilbert_block_window, gilbert_index, gilbert_perm, gilbert_perm_pool, gilbert_tile_index,
-               materialize_capacity, route_capacity, route_materialize, route_topk, tile_block_window, tile_perm)
+               gilbert_block_window, gilbert_index, gilbert_perm, gilbert_perm_pool, gilbert_perm_pool_batch,
+               gilbert_tile_index, materialize_capacity, route_capacity, route_materialize, route_topk,
+               tile_block_window, tile_perm)
 
 
 def block_lengths(tokens: int, block: int, n_chunks: int = 1, device="cuda") -> torch.Tensor:
@@ -163,6 +165,17 @@ class RoutedAttention:
         written by the same pass: returns them (``qbar``), else None.
         ``q_blocks=False`` (curve blocks only): the block means alone, the
         queries stay in raster order (the attention reads them there)."""
+        if self.tile is None and self.use_kpool:
+            # Q, K and V through one launch (the same bits as the three calls)
+            ks, vs = self.slot(c)
+            b0 = c * self.nbc
+            self.invalidate_kpool(b0)
+            gilbert_perm_pool_batch([(q_raster, self.q_blk if q_blocks else None, self.qbar),
+                                     (k_raster, ks, self.kpool[:, b0:b0 + self.nbc]), (v_raster, vs, None)],
+                                    self.perm, block=self.block, stream=stream)
+            if self._kpool_valid == b0:
+                self._kpool_valid = b0 + self.nbc
+            return self.qbar
         self.append(k_raster, v_raster, c, stream)
         if self.tile is not None:
             self.to_blocks(q_raster, self.q_blk, stream)

@@ -138,6 +138,42 @@ int bsa_gilbert_perm_pool(const void* src, void* dst, const int32_t* perm, int L
                           int64_t pool_head_stride, hipStream_t stream);
 
 /*
+ * bsa_gilbert_perm_pool_batch -- bsa_gilbert_perm_pool over several tensors
+ * of one chunk that share its curve (say Q, K and V) in a single launch.
+ * [Velox -- Methodology, Step 4 (mean query and mean key vectors per
+ *  block); Key Contributions 3; Methodology, Step 6]
+ *
+ * jobs           host array of n_jobs descriptions (1 <= n_jobs <=
+ *                BSA_MAX_PERM_JOBS), read during the call only.  Job z
+ *                moves jobs[z].src (raster, jobs[z].raster_token_stride) as
+ *                bsa_gilbert_perm_pool does with its own dst (Gilbert
+ *                slot, jobs[z].gilbert_head_stride; NULL = block means
+ *                only) and pool (jobs[z].pool_head_stride; NULL = the
+ *                permutation only, as bsa_gilbert_perm with inverse = 0).
+ *                A job needs a dst or a pool.
+ * perm, L, heads, d, block, dtype   shared by every job, as in
+ *                bsa_gilbert_perm_pool.
+ * The results are bitwise those of the single-tensor calls.  No job's dst or
+ * pool may overlap any job's src, dst or pool.
+ * Errors: those of bsa_gilbert_perm_pool for each job; BSA_EINVAL (jobs
+ * NULL, n_jobs out of range, a job with neither dst nor pool, overlap
+ * between jobs).
+ */
+#define BSA_MAX_PERM_JOBS 4
+
+typedef struct bsa_perm_job {
+    const void* src;
+    void* dst;
+    int64_t raster_token_stride;
+    int64_t gilbert_head_stride;
+    double* pool;
+    int64_t pool_head_stride;
+} bsa_perm_job;
+
+int bsa_gilbert_perm_pool_batch(const bsa_perm_job* jobs, int n_jobs, const int32_t* perm, int L, int heads, int d,
+                                int block, int dtype, hipStream_t stream);
+
+/*
  * Router arguments.  Set struct_size = sizeof(bsa_route_args).
  * [Velox -- Methodology, Step 4 (importance from mean query and mean key
  *  vectors; overlap above tau rescaled and applied as (1 + lambda * g_hat),

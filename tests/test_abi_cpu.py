@@ -93,6 +93,37 @@ def test_gilbert_perm_pool_rejects():
              None) == bsa.BSA_EINVAL                                          # pool inside src
 
 
+def test_gilbert_perm_pool_batch_rejects():
+    f = lib.bsa_gilbert_perm_pool_batch
+    J = bsa.PermJob
+    # Q pooled only, K permuted and pooled, V permuted only: distinct buffers
+    q, k, v = 0x100000000, 0x200000000, 0x300000000
+    kd, vd, qp, kp = 0x400000000, 0x500000000, 0x600000000, 0x700000000
+    jobs = (J * 4)(J(q, None, 5120, 0, qp, 37 * 128), J(k, kd, 5120, 4736 * 128, kp, 37 * 128),
+                   J(v, vd, 5120, 4736 * 128, None, 0), J(v, None, 5120, 0, None, 0))
+    args = (FAKE, 4680, 40, 128, 128, 0, None)
+    assert f(None, 3, *args) == bsa.BSA_EINVAL                                # no jobs
+    assert f(jobs, 0, *args) == bsa.BSA_EINVAL                                # too few
+    assert f(jobs, bsa.MAX_PERM_JOBS + 1, *args) == bsa.BSA_EINVAL            # too many
+    assert f(jobs, 4, *args) == bsa.BSA_EINVAL                                # job 3: neither dst nor pool
+    assert "job 3" in lib.bsa_last_error_detail().decode()
+    assert f(jobs, 3, FAKE, 4680, 70000, 128, 128, 0, None) == bsa.BSA_EINVAL  # heads beyond the grid
+    assert f(jobs, 3, FAKE, 4680, 40, 96, 128, 0, None) == bsa.BSA_EUNSUPPORTED
+    assert f(jobs, 3, None, 4680, 40, 128, 128, 0, None) == bsa.BSA_EINVAL   # no perm
+    # a job's own checks, reported with its index
+    bad = (J * 2)(J(q, None, 5120, 0, qp, 37 * 128), J(k, kd, 5120, 4736 * 128, kp, 37 * 128 - 1))
+    assert f(bad, 2, *args) == bsa.BSA_EINVAL
+    detail = lib.bsa_last_error_detail().decode()
+    assert "job 1" in detail and "pool_head_stride" in detail
+    # across jobs: K's slot inside V's slot, a pool inside another job's src,
+    # two jobs sharing a pool
+    for a, b in ((J(k, kd, 5120, 4736 * 128, kp, 37 * 128), J(v, kd + 4096, 5120, 4736 * 128, None, 0)),
+                 (J(q, None, 5120, 0, k + 4096, 37 * 128), J(k, kd, 5120, 4736 * 128, None, 0)),
+                 (J(q, None, 5120, 0, qp, 37 * 128), J(k, None, 5120, 0, qp, 37 * 128))):
+        assert f((J * 2)(a, b), 2, *args) == bsa.BSA_EINVAL
+        assert "overlaps" in lib.bsa_last_error_detail().decode()
+
+
 def _attn(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, dtype=0, heads=40, d=128, block=128, nqb=37, nkb=1776,
              qhs=37 * 128 * 128, khs=1776 * 128 * 128, vhs=1776 * 128 * 128, ohs=37 * 128 * 128, ql=None,

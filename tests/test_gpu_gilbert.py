@@ -127,6 +127,49 @@ def test_permute_pool_into_cache_slice():
     assert torch.all(cache[:, :nbc] == -1.0) and torch.all(cache[:, 2 * nbc:] == -1.0)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("block,d", [(128, 128), (64, 64)])
+def test_permute_pool_batch(dtype, block, d):
+    """Q (block means only), K (store slot + cache slice) and V (store slot,
+    no means) of one chunk through one launch: every output equals the
+    oracle's, bitwise, and the stores and cache outside the slots are
+    untouched."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    from oracle import route as oroute
+    T, H, W = 3, 30, 52
+    L, heads = T * H * W, 5
+    nbc = -(-L // block)
+    fused = torch.randn((L, 3, heads, d), generator=torch.Generator().manual_seed(21)).to(dtype).to(dev)
+    q, k, v = fused[:, 0], fused[:, 1], fused[:, 2]
+    k_store = torch.full((heads, 3 * nbc * block, d), 7.0, dtype=dtype, device=dev)
+    v_store = torch.full((heads, 3 * nbc * block, d), 5.0, dtype=dtype, device=dev)
+    cache = torch.full((heads, 3 * nbc, d), -1.0, dtype=torch.float64, device=dev)
+    qbar = torch.full((heads, nbc, d), -2.0, dtype=torch.float64, device=dev)
+    perm, _ = bsa.gilbert_index(T, H, W, device=dev)
+    ks, vs = k_store[:, nbc * block: 2 * nbc * block], v_store[:, nbc * block: 2 * nbc * block]
+    bsa.gilbert_perm_pool_batch([(q, None, qbar), (k, ks, cache[:, nbc: 2 * nbc]), (v, vs, None)], perm,
+                                block=block)
+    torch.cuda.synchronize()
+    order = gilbert_order(T, H, W)[0]
+    lens = olay.chunk_block_lengths(L, block)
+    refs = [olay.permute_forward(f64(x), order, block) for x in (q, k, v)]
+    assert np.array_equal(f64(ks), refs[1]) and np.array_equal(f64(vs), refs[2])
+    for h in range(heads):
+        assert np.array_equal(qbar[h].cpu().numpy(), oroute.pool_blocks(refs[0][h], lens, block)), h
+        assert np.array_equal(cache[h, nbc: 2 * nbc].cpu().numpy(), oroute.pool_blocks(refs[1][h], lens, block)), h
+    for store, fill in ((k_store, 7.0), (v_store, 5.0)):
+        assert torch.all(store[:, : nbc * block] == fill) and torch.all(store[:, 2 * nbc * block:] == fill)
+    assert torch.all(cache[:, :nbc] == -1.0) and torch.all(cache[:, 2 * nbc:] == -1.0)
+    # one job alone, and the single-tensor entry on the same input: the same bits
+    dst1, pool1 = bsa.gilbert_perm_pool(k, perm, block=block)
+    ks2 = torch.empty_like(dst1)
+    pool2 = torch.empty_like(pool1)
+    bsa.gilbert_perm_pool_batch([(k, ks2, pool2)], perm, block=block)
+    torch.cuda.synchronize()
+    assert torch.equal(ks2, dst1) and torch.equal(pool2, pool1)
+
+
 def test_index_large_grid():
     dev = need_gpu()
     import block_sparse_attention_gilbert_amd as bsa
