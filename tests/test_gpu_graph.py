@@ -80,3 +80,11 @@ def test_step_equals_the_stage_by_stage_chain():
     assert torch.equal(r_step["col_idx"][:n], r_chain["col_idx"][:n])
     assert torch.equal(o_step, o_chain)
     assert torch.equal(ra.lse, rb.lse)
+    # the step without the pooled-key cache (separate passes over Q, K and V,
+    # the router pooling the whole history): the same bits again
+    rc = mk()
+    rc.use_kpool = False
+    o_nc, r_nc = rc.step(q_r, k_r, v_r, 3)
+    torch.cuda.synchronize()
+    assert torch.equal(r_nc["col_idx"][:n], r_chain["col_idx"][:n])
+    assert torch.equal(o_nc, o_step) and torch.equal(rc.lse, ra.lse)
