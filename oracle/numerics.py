@@ -1,4 +1,5 @@
-"""Exact conversions of stored inputs to float64.
+"""Exact conversions of stored inputs to float64 (test infrastructure: only
+the tests, the smoke check and the benchmark's CPU baseline use the oracle).
 
 The oracle sees the values exactly as stored on the device: a bf16 value is
 the top 16 bits of an IEEE binary32, so widening its bit pattern by 16 zero
@@ -20,13 +21,3 @@ def f32_to_f64(x: np.ndarray) -> np.ndarray:
     """float64 values of a binary32 array (exact)."""
     return np.asarray(x, dtype=np.float32).astype(np.float64)
 
-
-def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float64 values to bf16 (round to nearest, ties to even) and
-    return the bit patterns as uint16.  Used only to state what a bf16 output
-    rounding can contribute to an error bound."""
-    f = np.asarray(x, dtype=np.float64).astype(np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-    return r.astype(np.uint16)
