@@ -662,16 +662,43 @@ def _attn_prep(q, k, v, out, lse, block):
     _, vrows, vhs = _heads_rows(v, d)
     if k.shape[0] != heads or v.shape[0] != heads or vrows < krows:
         raise ValueError("q, k, v head counts / rows disagree")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must have q's dtype (%s), got %s and %s" % (q.dtype, k.dtype, v.dtype))
     if qrows % block or krows % block:
         raise ValueError("row counts must be multiples of the block size")
     if out is None:
         out = torch.empty((heads, qrows, d), dtype=q.dtype, device=q.device)
-    _, _, ohs = _heads_rows(out, d)
-    if lse is True:
-        lse = torch.empty((heads, qrows), dtype=torch.float32, device=q.device)
-    elif lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 tensor")
+    _, orows, ohs = _heads_rows(out, d)
+    if out.dtype != q.dtype:
+        raise ValueError("out must have q's dtype (%s), got %s" % (q.dtype, out.dtype))
+    if out.shape[0] != heads or orows < qrows:
+        raise ValueError("out must hold %d heads x %d rows" % (heads, qrows))
+    lse = _lse_arg(lse, heads, qrows, q.device)
     return d, heads, qrows // block, krows // block, qhs, khs, vhs, out, ohs, lse
+
+
+def _lse_arg(lse, heads, qrows, device):
+    if lse is True:
+        return torch.empty((heads, qrows), dtype=torch.float32, device=device)
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 tensor")
+        if lse.numel() < heads * qrows:
+            raise ValueError("lse holds %d values, heads*nqb*block = %d needed" % (lse.numel(), heads * qrows))
+    return lse
+
+
+def _attn_sizes(heads, nqb, nkb, nkb_rows, q_block_len, kv_block_len, row_ptr=None):
+    """Sizes the C ABI cannot see: every device array must cover what the
+    kernels read from it."""
+    if nkb < 1 or nkb > nkb_rows:
+        raise ValueError("nkb = %d outside [1, %d] (the KV rows / block)" % (nkb, nkb_rows))
+    if q_block_len is not None and q_block_len.numel() < nqb:
+        raise ValueError("q_block_len holds %d entries, nqb = %d needed" % (q_block_len.numel(), nqb))
+    if kv_block_len is not None and kv_block_len.numel() < nkb:
+        raise ValueError("kv_block_len holds %d entries, nkb = %d needed" % (kv_block_len.numel(), nkb))
+    if row_ptr is not None and row_ptr.numel() < heads * nqb + 1:
+        raise ValueError("row_ptr holds %d entries, heads*nqb+1 = %d needed" % (row_ptr.numel(), heads * nqb + 1))
 
 
 def block_sparse_attn(q, k, v, row_ptr, col_idx, *, block: int, scale: Optional[float] = None,
@@ -682,6 +709,7 @@ def block_sparse_attn(q, k, v, row_ptr, col_idx, *, block: int, scale: Optional[
     _need_gpu(row_ptr, col_idx)
     d, heads, nqb, nkb_, qhs, khs, vhs, out, ohs, lse = _attn_prep(q, k, v, out, lse, block)
     nkb = nkb_ if nkb is None else nkb
+    _attn_sizes(heads, nqb, nkb, nkb_, q_block_len, kv_block_len, row_ptr)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(_lib.bsa_block_sparse_attn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), heads, d, block, nqb, nkb, qhs, khs,
@@ -718,19 +746,21 @@ def block_sparse_attn_raster(q, k, v, row_ptr, col_idx, row_map, *, block: int, 
         _, vrows, vhs = _heads_rows(v, d)
         if v.shape[0] != heads or vrows < krows or krows % block:
             raise ValueError("k, v head counts / rows disagree")
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise ValueError("k and v must have q's dtype (%s), got %s and %s" % (q.dtype, k.dtype, v.dtype))
         nkb_, qs = krows // block, q.stride(0)
-        if lse is True:
-            lse = torch.empty((heads, nqb * block), dtype=torch.float32, device=q.device)
-        elif lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-            raise ValueError("lse must be a contiguous float32 tensor")
+        lse = _lse_arg(lse, heads, nqb * block, q.device)
     else:
         d, heads, nqb, nkb_, qs, khs, vhs, _, _, lse = _attn_prep(q, k, v, q, lse, block)
     nkb = nkb_ if nkb is None else nkb
+    _attn_sizes(heads, nqb, nkb, nkb_, q_block_len, kv_block_len, row_ptr)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     if out is None:
         out = torch.empty((row_map.numel() if tokens is None else tokens, heads, d), dtype=q.dtype, device=q.device)
     if out.dim() != 3 or out.shape[1] != heads or out.shape[2] != d or out.stride(2) != 1 or out.stride(1) != d:
         raise ValueError("raster out must be [tokens][heads][d] with contiguous [heads][d] per token")
+    if out.dtype != q.dtype:
+        raise ValueError("out must have q's dtype (%s), got %s" % (q.dtype, out.dtype))
     _check(_lib.bsa_block_sparse_attn_raster(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), heads, d, block, nqb, nkb,
         1 if q_raster else 0, qs, khs, vhs, _ptr(row_map), row_map.numel(), out.stride(0),
@@ -744,6 +774,7 @@ def dense_attn(q, k, v, *, block: int, scale: Optional[float] = None, q_block_le
     """Dense attention over every KV block, through the same kernel."""
     d, heads, nqb, nkb_, qhs, khs, vhs, out, ohs, lse = _attn_prep(q, k, v, out, lse, block)
     nkb = nkb_ if nkb is None else nkb
+    _attn_sizes(heads, nqb, nkb, nkb_, q_block_len, kv_block_len)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(_lib.bsa_dense_attn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), heads, d, block, nqb, nkb, qhs, khs,

@@ -244,3 +244,53 @@ def test_edge_cases_small(block, d):
             assert np.all(both_inf | (np.abs(lg - l_ref) <= 1e-4))
         # head 0 block 1 has an empty list: zeros and -inf
         assert torch.all(o[0, block: 2 * block] == 0) and torch.all(torch.isneginf(lse[0, block:2 * block]))
+
+
+def test_wrapper_rejects_short_or_mistyped_arrays():
+    """The binding checks what the C ABI cannot see (device array lengths,
+    operand dtypes, nkb against the KV rows) and raises ValueError before
+    anything is launched."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    heads, nqb, nkb, bs, d = 2, 3, 5, 64, 64
+    q = torch.zeros((heads, nqb * bs, d), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros((heads, nkb * bs, d), dtype=torch.bfloat16, device=dev)
+    v = torch.zeros_like(k)
+    rp = torch.zeros(heads * nqb + 1, dtype=torch.int32, device=dev)
+    ci = torch.zeros(1, dtype=torch.int32, device=dev)
+    i32 = lambda n: torch.full((n,), bs, dtype=torch.int32, device=dev)
+    cases = [
+        dict(lse=torch.empty(heads * nqb * bs - 1, dtype=torch.float32, device=dev)),
+        dict(q_block_len=i32(nqb - 1)),
+        dict(kv_block_len=i32(nkb - 1)),
+        dict(nkb=nkb + 1),
+        dict(nkb=0),
+        dict(out=torch.empty((heads, nqb * bs, d), dtype=torch.float32, device=dev)),
+        dict(out=torch.empty((heads, nqb * bs - bs, d), dtype=torch.bfloat16, device=dev)),
+    ]
+    for kw in cases:
+        with pytest.raises(ValueError):
+            bsa.block_sparse_attn(q, k, v, rp, ci, block=bs, **kw)
+    with pytest.raises(ValueError):
+        bsa.block_sparse_attn(q, k, v, rp[:-1], ci, block=bs)
+    with pytest.raises(ValueError):
+        bsa.block_sparse_attn(q, k.float(), v, rp, ci, block=bs)
+    with pytest.raises(ValueError):
+        bsa.block_sparse_attn(q, k, v.float(), rp, ci, block=bs)
+    with pytest.raises(ValueError):
+        bsa.dense_attn(q, k, v, block=bs, kv_block_len=i32(nkb - 1))
+    with pytest.raises(ValueError):
+        bsa.dense_attn(q, k, v, block=bs, lse=torch.empty(7, dtype=torch.float32, device=dev))
+    row_map = torch.arange(nqb * bs, dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError):
+        bsa.block_sparse_attn_raster(q, k, v, rp, ci, row_map, block=bs, q_block_len=i32(nqb - 1))
+    q_r = torch.zeros((nqb * bs, heads, d), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        bsa.block_sparse_attn_raster(q_r, k.float(), v, rp, ci, row_map, block=bs, q_raster=True, nqb=nqb)
+    with pytest.raises(ValueError):
+        bsa.block_sparse_attn_raster(q_r, k, v, rp, ci, row_map, block=bs, q_raster=True, nqb=nqb,
+                                     lse=torch.empty(5, dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):
+        bsa.block_sparse_attn_raster(q_r, k, v, rp, ci, row_map, block=bs, q_raster=True, nqb=nqb,
+                                     out=torch.empty((nqb * bs, heads, d), dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
