@@ -11,7 +11,7 @@ Entry points (same names as the C ABI, without the ``bsa_`` prefix):
 ``gilbert_index``, ``gilbert_perm``, ``gilbert_block_window``,
 ``gilbert_tile_index``, ``tile_perm``, ``tile_block_window``,
 ``slab_overlap``, ``slab_coverage``, ``route_topk`` (with
-``route_workspace_size``), ``route_materialize`` (with
+``route_workspace_size``), ``route_topk_static`` (no workspace), ``route_materialize`` (with
 ``route_materialize_workspace_size``), ``block_sparse_attn``,
 ``dense_attn``.
 """
@@ -123,6 +123,8 @@ _lib.bsa_route_workspace_size.restype = ctypes.c_size_t
 _lib.bsa_route_workspace_size.argtypes = [ctypes.POINTER(RouteArgs)]
 _lib.bsa_route_topk.restype = _i
 _lib.bsa_route_topk.argtypes = [ctypes.POINTER(RouteArgs), _p, ctypes.c_size_t, _p]
+_lib.bsa_route_topk_static.restype = _i
+_lib.bsa_route_topk_static.argtypes = [ctypes.POINTER(RouteArgs), _p]
 _ATTN_COMMON = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p]
 _lib.bsa_block_sparse_attn.restype = _i
 _lib.bsa_block_sparse_attn.argtypes = _ATTN_COMMON + [_p, _p, _i64, _f, _p]
@@ -135,7 +137,7 @@ _lib.bsa_dense_attn.argtypes = _ATTN_COMMON + [_f, _p]
 EXPORTED = ("bsa_version", "bsa_strerror", "bsa_last_error_detail", "bsa_gilbert_index", "bsa_gilbert_perm",
             "bsa_gilbert_perm_pool", "bsa_gilbert_perm_pool_batch", "bsa_gilbert_block_window",
             "bsa_gilbert_tile_index", "bsa_tile_perm", "bsa_tile_block_window", "bsa_route_workspace_size",
-            "bsa_route_topk", "bsa_route_materialize_workspace_size", "bsa_route_materialize", "bsa_slab_overlap",
+            "bsa_route_topk", "bsa_route_topk_static", "bsa_route_materialize_workspace_size", "bsa_route_materialize", "bsa_slab_overlap",
             "bsa_slab_coverage", "bsa_slab_coverage_workspace_size", "bsa_block_sparse_attn",
             "bsa_block_sparse_attn_raster", "bsa_dense_attn", "bsa_diag_mfma_bf16")
 
@@ -520,16 +522,9 @@ def route_capacity(heads: int, nqb: int, nkb: int, k_cap: int, n_dense_tail_bloc
     return heads * nqb * (min(k_cap, n_cand) + n_dense_tail_blocks)
 
 
-def route_topk(q: torch.Tensor, k: torch.Tensor, *, block: int, nqb: int, nkb: int, scale: float,
-               q_block_len=None, kv_block_len=None, overlap=None, lam: float = 2.0, g_ref: float = 0.2,
-               tau: float = 0.1, k_fixed: int = 50, k_per_row=None, k_max: Optional[int] = None,
-               n_dense_tail_blocks: int = 0, kpool=None, kpool_valid_blocks: int = 0, qpool=None,
-               want_keys: bool = False, out: Optional[dict] = None, workspace=None, stream=None):
-    """Pool, score, fuse and select.  Returns a dict with ``row_ptr``,
-    ``col_idx`` (capacity-sized; the first ``row_ptr[-1]`` entries are the
-    lists), ``fallback_counts`` and optionally ``sel_keys``.  ``out`` and
-    ``workspace`` may be passed in to avoid allocations.  ``qpool``: the
-    pooled queries (``gilbert_perm_pool``), so ``q`` is not pooled again."""
+def _route_topk_args(q, k, *, block, nqb, nkb, scale, q_block_len, kv_block_len, overlap, lam, g_ref, tau,
+                     k_fixed, k_per_row, k_max, n_dense_tail_blocks, kpool, kpool_valid_blocks, qpool, want_keys,
+                     out):
     _need_gpu(q, k, q_block_len, kv_block_len, overlap, k_per_row, kpool, qpool)
     heads = q.shape[0]
     n_cand = nkb - n_dense_tail_blocks
@@ -551,13 +546,56 @@ def route_topk(q: torch.Tensor, k: torch.Tensor, *, block: int, nqb: int, nkb: i
                     n_dense_tail_blocks=n_dense_tail_blocks, kpool=kpool, kpool_valid_blocks=kpool_valid_blocks,
                     row_ptr=out["row_ptr"], col_idx=out["col_idx"], fallback_counts=out["fallback_counts"],
                     sel_keys=out.get("sel_keys"), qpool=qpool)
+    return a, out
+
+
+def route_topk(q: torch.Tensor, k: torch.Tensor, *, block: int, nqb: int, nkb: int, scale: float,
+               q_block_len=None, kv_block_len=None, overlap=None, lam: float = 2.0, g_ref: float = 0.2,
+               tau: float = 0.1, k_fixed: int = 50, k_per_row=None, k_max: Optional[int] = None,
+               n_dense_tail_blocks: int = 0, kpool=None, kpool_valid_blocks: int = 0, qpool=None,
+               want_keys: bool = False, out: Optional[dict] = None, workspace=None, stream=None):
+    """Pool, score, fuse and select.  Returns a dict with ``row_ptr``,
+    ``col_idx`` (capacity-sized; the first ``row_ptr[-1]`` entries are the
+    lists), ``fallback_counts`` and optionally ``sel_keys``.  ``out`` and
+    ``workspace`` may be passed in to avoid allocations.  ``qpool``: the
+    pooled queries (``gilbert_perm_pool``), so ``q`` is not pooled again."""
+    a, out = _route_topk_args(q, k, block=block, nqb=nqb, nkb=nkb, scale=scale, q_block_len=q_block_len,
+                              kv_block_len=kv_block_len, overlap=overlap, lam=lam, g_ref=g_ref, tau=tau,
+                              k_fixed=k_fixed, k_per_row=k_per_row, k_max=k_max,
+                              n_dense_tail_blocks=n_dense_tail_blocks, kpool=kpool,
+                              kpool_valid_blocks=kpool_valid_blocks, qpool=qpool, want_keys=want_keys, out=out)
     need = _lib.bsa_route_workspace_size(ctypes.byref(a))
     if need == 0:
         _check(_lib.bsa_route_topk(ctypes.byref(a), None, 0, _stream(stream)))
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     out["workspace"] = workspace
     _check(_lib.bsa_route_topk(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+ROUTE_STATIC_SCRATCH_BYTES = 32 << 20  # BSA_ROUTE_STATIC_SCRATCH_BYTES
+
+
+def route_topk_static(q: torch.Tensor, k: torch.Tensor, *, block: int, nqb: int, nkb: int, scale: float,
+                      out: dict, q_block_len=None, kv_block_len=None, overlap=None, lam: float = 2.0,
+                      g_ref: float = 0.2, tau: float = 0.1, k_fixed: int = 50, k_per_row=None,
+                      k_max: Optional[int] = None, n_dense_tail_blocks: int = 0, kpool=None,
+                      kpool_valid_blocks: int = 0, qpool=None, stream=None):
+    """``route_topk`` through ``bsa_route_topk_static``: the library's fixed
+    per-GPU scratch instead of a workspace, so the call allocates nothing.
+    ``out`` (``row_ptr``, ``col_idx``, ``fallback_counts`` and optionally
+    ``sel_keys``) is required.  Calls that overlap on one GPU race on the
+    shared scratch."""
+    for name in ("row_ptr", "col_idx", "fallback_counts"):
+        if out.get(name) is None:
+            raise ValueError("out[%r] is required" % name)
+    a, out = _route_topk_args(q, k, block=block, nqb=nqb, nkb=nkb, scale=scale, q_block_len=q_block_len,
+                              kv_block_len=kv_block_len, overlap=overlap, lam=lam, g_ref=g_ref, tau=tau,
+                              k_fixed=k_fixed, k_per_row=k_per_row, k_max=k_max,
+                              n_dense_tail_blocks=n_dense_tail_blocks, kpool=kpool,
+                              kpool_valid_blocks=kpool_valid_blocks, qpool=qpool, want_keys=False, out=out)
+    _check(_lib.bsa_route_topk_static(ctypes.byref(a), _stream(stream)))
     return out
 
 
@@ -785,7 +823,7 @@ def dense_attn(q, k, v, *, block: int, scale: Optional[float] = None, q_block_le
 
 __all__ = ["gilbert_index", "gilbert_perm", "gilbert_perm_pool", "gilbert_perm_pool_batch", "gilbert_block_window",
            "gilbert_tile_index", "tile_perm", "tile_block_window", "tile_grid", "slab_overlap", "slab_coverage",
-           "route_topk", "route_workspace_size", "route_capacity", "route_materialize",
+           "route_topk", "route_topk_static", "ROUTE_STATIC_SCRATCH_BYTES", "route_workspace_size", "route_capacity", "route_materialize",
            "route_materialize_workspace_size", "materialize_capacity", "MaterializeArgs", "block_sparse_attn",
            "block_sparse_attn_raster", "dense_attn", "version", "library", "BsaError", "RouteArgs", "PermJob",
            "MAX_PERM_JOBS", "EXPORTED", "BSA_OK", "BSA_EINVAL", "BSA_EUNSUPPORTED", "BSA_EWORKSPACE", "BSA_EHIP",

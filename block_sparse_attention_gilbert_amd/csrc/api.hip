@@ -68,6 +68,22 @@ int bsa_route_topk(const bsa_route_args* args, void* workspace, size_t workspace
     return hip_status(bsa::launch_route(args, lay, workspace, stream), "route launch");
 }
 
+int bsa_route_topk_static(const bsa_route_args* args, hipStream_t stream) {
+    bsa::clear_error();
+    bsa::RouteLayout lay;
+    const int st = bsa::validate_route(args, &lay);
+    if (st != BSA_OK) return st;
+    if (lay.total > (size_t)BSA_ROUTE_STATIC_SCRATCH_BYTES)
+        return bsa::fail(BSA_EWORKSPACE,
+                         "these arguments need %zu bytes of scratch; the static scratch holds %zu (pass kpool and "
+                         "sel_keys to shrink the need, or call bsa_route_topk with a workspace)",
+                         lay.total, (size_t)BSA_ROUTE_STATIC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    const int rs = hip_status(bsa::static_route_scratch(&ws), "static scratch lookup");
+    if (rs != BSA_OK) return rs;
+    return hip_status(bsa::launch_route(args, lay, ws, stream), "route launch");
+}
+
 int bsa_gilbert_block_window(const int32_t* perm, const int32_t* inv, int T, int H, int W, int block, int q_chunk,
                              int32_t* window, int32_t* window_len, int window_stride, hipStream_t stream) {
     bsa::clear_error();

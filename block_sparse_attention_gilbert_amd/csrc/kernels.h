@@ -23,6 +23,10 @@ hipError_t launch_gilbert_perm_pool_batch(const bsa_perm_job* jobs, int n_jobs, 
 
 hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* ws, hipStream_t stream);
 
+// Device address of the router's fixed scratch (BSA_ROUTE_STATIC_SCRATCH_BYTES)
+// on the current device, looked up once per device.
+hipError_t static_route_scratch(void** ptr);
+
 hipError_t launch_block_window(const int32_t* perm, const int32_t* inv, int T, int H, int W, int block, int q_chunk,
                                int32_t* window, int32_t* window_len, int stride, hipStream_t stream);
 

@@ -19,7 +19,16 @@
 // index ascending).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kernels.h"
+
+// Fixed device scratch of bsa_route_topk_static (callers that cannot
+// allocate): one copy per GPU, held from the library's load to the end of
+// the process.  Host code never passes `scratch` itself to a kernel (in host
+// code the name is a host-side stand-in, not a device address); it uses the
+// address hipGetSymbolAddress returns on each device.
+static __device__ __align__(256) unsigned char scratch[BSA_ROUTE_STATIC_SCRATCH_BYTES];
 
 namespace bsa {
 namespace {
@@ -1031,6 +1040,31 @@ hipError_t launch_materialize(const bsa_route_args* a, const bsa_materialize_arg
     hipLaunchKernelGGL(emit_lists_kernel, grid, dim3(kThreads), 0, stream, bitmap, rows, nwords, a->row_ptr,
                        a->col_idx);
     return hipGetLastError();
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null until looked up)
+
+}  // namespace
+
+hipError_t static_route_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace bsa

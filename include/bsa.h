@@ -30,7 +30,8 @@
  *   otherwise.  The library never allocates or frees; scratch memory is a
  *   caller buffer sized by the matching *_workspace_size function.  The
  *   library holds no mutable global state and is safe to call from several
- *   threads on different streams.
+ *   threads on different streams; the one exception is the fixed scratch
+ *   of bsa_route_topk_static, which its own comment describes.
  * - Tensor pointers must be 16-byte aligned and head strides must keep every
  *   row 16-byte aligned.
  * - Results are deterministic: identical inputs give bitwise identical
@@ -285,6 +286,28 @@ size_t bsa_route_workspace_size(const bsa_route_args* args);
  */
 int bsa_route_topk(const bsa_route_args* args, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
+
+/*
+ * bsa_route_topk_static -- bsa_route_topk with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The scratch is a
+ * fixed array of BSA_ROUTE_STATIC_SCRATCH_BYTES inside the library, one
+ * copy per GPU, held from the library's load to the end of the process; its
+ * device address is looked up on the first call on each device (the
+ * caller's current device, which must be the one stream belongs to).  The
+ * call itself allocates nothing.
+ * Results are bitwise those of bsa_route_topk with the same arguments.
+ * Calls that overlap in time on one GPU (different streams, or different
+ * host threads) share that scratch and race: serialise them.  Nothing in
+ * the scratch has to start at zero; each call writes what it reads.
+ * Errors: those of bsa_route_topk; BSA_EWORKSPACE when
+ * bsa_route_workspace_size(args) exceeds BSA_ROUTE_STATIC_SCRATCH_BYTES
+ * (passing kpool and sel_keys leaves only the pooled queries, list lengths
+ * and row flags in the scratch); BSA_EHIP if the address lookup fails.
+ */
+#define BSA_ROUTE_STATIC_SCRATCH_BYTES (32u << 20)
+
+int bsa_route_topk_static(const bsa_route_args* args, hipStream_t stream);
 
 /*
  * bsa_gilbert_block_window -- the local window of every query block of one

@@ -225,6 +225,22 @@ def test_route_rejects_and_sizes():
     assert 0 < small < need
 
 
+def test_route_static_rejects_on_the_host():
+    # the static-scratch router validates like bsa_route_topk, then refuses
+    # arguments whose workspace exceeds its fixed scratch (nothing enqueued)
+    assert bsa.ROUTE_STATIC_SCRATCH_BYTES == 32 << 20
+    f = lib.bsa_route_topk_static
+    assert f(ctypes.byref(_route_args(struct_size=8)), None) == bsa.BSA_EINVAL
+    assert f(ctypes.byref(_route_args(nkb=5000)), None) == bsa.BSA_EUNSUPPORTED
+    big = _route_args()   # chunk 48 without a pooled-key cache: ~95 MB of scratch
+    assert lib.bsa_route_workspace_size(ctypes.byref(big)) > bsa.ROUTE_STATIC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), None) == bsa.BSA_EWORKSPACE
+    assert "static scratch" in lib.bsa_last_error_detail().decode()
+    # with the cache the same problem fits
+    fits = _route_args(kpool=0x60000)
+    assert 0 < lib.bsa_route_workspace_size(ctypes.byref(fits)) <= bsa.ROUTE_STATIC_SCRATCH_BYTES
+
+
 def _mat_args(**over):
     m = bsa.MaterializeArgs()
     m.struct_size = ctypes.sizeof(bsa.MaterializeArgs)
