@@ -514,10 +514,15 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s2], o[dt], 0, 0, 0);
             }
     };
-    // scale raw scores into logits relative to ref and take the pair max;
-    // then move ref (rare, wave-uniform branch) where the sub-tile's maximum
-    // passes it by more than the slack, or first sets it
-    float mx = -INFINITY;
+    // scale raw scores into logits relative to ref and take this lane's
+    // maximum (half of its query's keys); then move ref (rare, wave-uniform
+    // branch) where the sub-tile's maximum passes it by more than the slack,
+    // or first sets it.  The common path compares each lane's own maximum
+    // with its query's threshold thr_l (+inf for padded rows): a query needs
+    // a move exactly when one of its two lanes passes, so the cross-lane
+    // maximum is only taken on the rare path.
+    float m3l = -INFINITY;
+    float thr_l = valid_row ? -INFINITY : INFINITY;
     auto logits_scale = [&](const f32x16_t& s) __attribute__((always_inline)) {
         float m3 = -INFINITY;
 #pragma unroll
@@ -525,16 +530,18 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
             xc[r] = fmaf(s[r], c2, -ref);
             m3 = fmaxf(m3, xc[r]);
         }
-        mx = max_halves(m3);
+        m3l = m3;
     };
     auto logits_check = [&]() __attribute__((always_inline)) {
-        const float thr = ref_set ? kRescaleSlack : -INFINITY;
-        const bool need = valid_row & (mx > thr);
-        if (__any(need)) {
+        if (__any(m3l > thr_l)) {
+            const float mx = max_halves(m3l);
+            const float thr = ref_set ? kRescaleSlack : -INFINITY;
+            const bool need = valid_row & (mx > thr);
             const float shift = need ? mx : 0.f;
             const float alpha = (need && ref_set) ? __builtin_amdgcn_exp2f(-shift) : 1.0f;
             ref += shift;
             ref_set = ref_set || need;
+            thr_l = valid_row ? (ref_set ? kRescaleSlack : -INFINITY) : INFINITY;
             l *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
@@ -661,7 +668,7 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         });
         __asm__ volatile("" ::"v"(ls), "v"(m3));
         l += ls;
-        mx = max_halves(m3);
+        m3l = m3;
         logits_check();
     };
     auto step = [&](auto K_) __attribute__((always_inline)) -> bool {

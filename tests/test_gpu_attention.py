@@ -241,7 +241,7 @@ def test_edge_cases_small(block, d):
             assert np.all(og[~vmask] == 0.0)
             lg = lse[h].cpu().numpy().astype(np.float64)
             both_inf = np.isneginf(lg) & np.isneginf(l_ref)
-            assert np.all(both_inf | (np.abs(lg - l_ref) <= 1e-4))
+            assert np.all(both_inf | (np.abs(lg - l_ref) <= (LSE_BF16 if dtype == torch.bfloat16 else 1e-4)))
         # head 0 block 1 has an empty list: zeros and -inf
         assert torch.all(o[0, block: 2 * block] == 0) and torch.all(torch.isneginf(lse[0, block:2 * block]))
 

@@ -2,7 +2,7 @@
 kernel spills to scratch memory (a spill turns register traffic into memory
 traffic), and the attention kernels keep the occupancy their design assumes
 (two workgroups per CU for the 128-row blocks: at most 256 registers per
-lane)."""
+lane and half of the CU's 160 KB of LDS each)."""
 
 import os
 import re
@@ -59,4 +59,4 @@ def test_attention_occupancy(tmp_path):
     assert len(attn) == 4, sorted(attn)
     for name, v in attn.items():
         assert v["vgpr_count"] + v.get("agpr_count", 0) <= 256, (name, v)
-        assert v["group_segment_fixed_size"] <= 65536, (name, v)
+        assert v["group_segment_fixed_size"] <= 160 * 1024 // 2, (name, v)
