@@ -226,7 +226,7 @@ score_kernel(const double* __restrict__ qbar, int64_t qbar_head_stride, const do
             double kap = sum[e] * scale;
             // the geometric bias applies to well-covered query blocks only
             // (all of them when no coverage is given)
-            if (overlap && (!coverage || (double)coverage[i] >= eta_cov))
+            if (overlap && (!coverage || coverage[i] >= (float)eta_cov))
                 kap += overlap_bias((double)overlap[(int64_t)i * ors + jc], lambda, g_ref, tau);
             keys[((int64_t)h * nqb + i) * n_cand + jc] = kap;
         }
@@ -691,7 +691,7 @@ materialize_kernel(const double* __restrict__ keys, int rows, int nqb, int nkb, 
     __asm__ volatile("" ::: "memory");
     const int vq = q_len ? q_len[i] : block;
     if (vq > 0) {
-        const bool covered = !coverage || (double)coverage[i] >= eta_cov;
+        const bool covered = !coverage || coverage[i] >= (float)eta_cov;
         const double* row = keys + (int64_t)r * nkb;
         // keys of the visible blocks (0: not a candidate); a well-covered row
         // sets the bits of the visible reserved blocks instead

@@ -409,7 +409,10 @@ int bsa_tile_block_window(const int32_t* row_cell, const int32_t* cell_row, int 
  *
  *  coverage       device float32[nqb] (NULL: every query block is well
  *                 covered); shared by all heads.  Query block i is well
- *                 covered when coverage[i] >= eta_cov.
+ *                 covered when coverage[i] >= eta_cov, compared in
+ *                 float32 (eta_cov rounded to float32): for a coverage
+ *                 that is a ratio of token counts this is the exact
+ *                 decision (72 of 80 tokens is covered at eta_cov = 0.9).
  *  k_cov          budget of a well-covered row (reserved blocks count
  *                 towards it).
  *  k_unc          cap of a poorly covered row's prefix, 0 .. 256.

@@ -24,7 +24,12 @@ Pages [Velox: Spatial Memory Makes World Models Efficient]:
 Readings where the pages are silent:
 
 * coverage is given per query block (one vector shared by all heads, like
-  the overlap); a block is well covered when coverage >= eta_cov;
+  the overlap); a block is well covered when coverage >= eta_cov.  The
+  coverage reaches the library as float32, so this decision is taken in
+  float32 (coverage and eta_cov both rounded to float32): for a coverage
+  that is a ratio k/n of token counts (n <= 2^16) that decides exactly as
+  the exact ratio against eta_cov does, e.g. 72 of 80 tokens is covered at
+  0.9, where a float64 comparison of float32(0.9) with 0.9 would not be;
 * the cumulative-mass threshold is not given; it is a parameter (0.9 by
   default) on the unbiased distribution p = softmax(s) of the row, ordered
   by (p descending, block index ascending); the prefix is the shortest one
@@ -128,7 +133,7 @@ def materialize_head(q, k, q_len, k_len, bs, *, scale, coverage, eta_cov=0.9, k_
     kb = np.where(visible[:, None], kbar, 0.0)
     qb = np.where((q_len > 0)[:, None], qbar, 0.0)
     s = (qb @ kb.T) * scale
-    covered = np.asarray(coverage, dtype=np.float64) >= eta_cov
+    covered = np.asarray(coverage, dtype=np.float64).astype(np.float32) >= np.float32(eta_cov)
     # the geometric fusion applies to the well-covered rows only
     ov = None
     if overlap is not None:

@@ -163,10 +163,11 @@ def test_slabs_to_materialised_routes():
     _ulp_equal(ov.cpu().numpy(), ref_ov)
     assert np.array_equal(cov.cpu().numpy(), ref_cov.astype(np.float32))
     win = om.block_window(order, g["grid"], w.bs, c - 1)
-    print("covered query blocks: %d of %d" % (int((ref_cov.astype(np.float32) >= 0.9).sum()), w.nqb))
+    print("covered query blocks: %d of %d" % (int((ref_cov.astype(np.float32) >= np.float32(0.9)).sum()), w.nqb))
     for hi in range(w.heads):
+        # the oracle's own float64 coverage (it takes the decision in float32)
         ref = om.materialize_head(f64(w.q[hi]), f64(w.k[hi]), w.q_len, w.k_len, w.bs, scale=w.scale,
-                                  coverage=ref_cov.astype(np.float32), k_cov=80, k_unc=150, mass=0.9,
+                                  coverage=ref_cov, k_cov=80, k_unc=150, mass=0.9,
                                   prev_blocks=prev, windows=win, overlap=ref_ov.astype(np.float32),
                                   lam=w.lam, tau=w.tau, g_ref=w.g_ref)
         assert_lists_equal(got[hi], ref["lists"], "head %d" % hi)

@@ -203,3 +203,36 @@ def test_pipeline_step_with_materialised_routes():
         o_g[:L] = f64(o_r[:, hi, :])[perm]
         mx, mean = err_summary(o_g, o_ref, vmask)
         assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (hi, mx, mean)
+
+
+def test_materialize_coverage_at_the_threshold():
+    """Query blocks of 80 valid tokens with 72 and 71 of them covered, and
+    float32 0.9 and the float32 just below it: the first two are well
+    covered (reservation + top-K fill), the others take the mass prefix, on
+    the GPU as in the oracle (both decide in float32)."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    rng = np.random.default_rng(21)
+    heads, nqb, nkb, block, d = 2, 4, 24, 128, 128
+    q_len = np.array([80, 80, 80, 80], dtype=np.int32)
+    k_len = np.full(nkb, block, dtype=np.int32)
+    q = torch.zeros((heads, nqb * block, d), dtype=torch.bfloat16)
+    k = torch.from_numpy(rng.standard_normal((heads, nkb * block, d)).astype(np.float32)).to(torch.bfloat16)
+    for i in range(nqb):
+        q[:, i * block: i * block + 80] = torch.from_numpy(
+            rng.standard_normal((heads, 80, d)).astype(np.float32)).to(torch.bfloat16)
+    cov = np.array([72 / 80, 0.9, np.nextafter(np.float32(0.9), np.float32(0)), 71 / 80], dtype=np.float32)
+    ov = rng.beta(0.5, 2.0, size=(nqb, nkb)).astype(np.float32)
+    r = bsa.route_materialize(q.to(dev), k.to(dev), block=block, nqb=nqb, nkb=nkb, scale=d ** -0.5,
+                              q_block_len=torch.from_numpy(q_len).to(dev), kv_block_len=torch.from_numpy(k_len).to(dev),
+                              overlap=torch.from_numpy(ov).to(dev), coverage=torch.from_numpy(cov).to(dev),
+                              prev_blocks=(16, 20), k_cov=8, k_unc=6, mass=0.5)
+    torch.cuda.synchronize()
+    got = csr_lists(r["row_ptr"], r["col_idx"], heads, nqb)
+    for h in range(heads):
+        ref = om.materialize_head(f64(q[h]), f64(k[h]), q_len, k_len, block, scale=d ** -0.5, coverage=cov,
+                                  k_cov=8, k_unc=6, mass=0.5, prev_blocks=(16, 20), overlap=ov)
+        assert ref["covered"].tolist() == [True, True, False, False]
+        assert_lists_equal(got[h], ref["lists"], "head %d" % h)
+        for i in (0, 1):
+            assert {16, 17, 18, 19} <= set(got[h][i].tolist())

@@ -150,3 +150,32 @@ def test_empty_query_block_gets_an_empty_list():
     r = om.materialize_head(q, k, q_len, k_len, bs, scale=0.25, coverage=np.ones(4), k_cov=3,
                             ref_blocks=(0, 3))
     assert r["lists"][2].size == 0 and r["lists"][0].size > 0
+
+
+def test_float32_coverage_decision_is_exact_for_token_ratios():
+    """The well-covered decision is taken in float32 (the coverage's storage
+    type): for every ratio k/n of covered tokens (n <= 128) and thresholds
+    read as exact fractions, it agrees with the exact rational comparison,
+    so a block with exactly 90 % of its tokens covered is well covered."""
+    from fractions import Fraction
+    for num, den in [(9, 10), (1, 2), (3, 4), (19, 20), (2, 3)]:
+        eta = num / den
+        for n in range(1, 129):
+            for k in range(n + 1):
+                f32 = np.float32(k / n) >= np.float32(eta)
+                assert f32 == (Fraction(k, n) >= Fraction(num, den)), (k, n, eta)
+    # the float64 comparison of a float32-stored 0.9 would call 72/80 poorly covered
+    assert float(np.float32(72 / 80)) < 0.9
+
+
+def test_coverage_at_the_threshold():
+    q, k, q_len, k_len, bs = _tiny(seed=6)
+    cov = np.array([72 / 80, np.float32(0.9), np.nextafter(np.float32(0.9), np.float32(0)), 71 / 80])
+    r = om.materialize_head(q, k, q_len, k_len, bs, scale=0.25, coverage=cov, k_cov=6, k_unc=5, mass=0.6,
+                            prev_blocks=(8, 11))
+    assert r["covered"].tolist() == [True, True, False, False]
+    r32 = om.materialize_head(q, k, q_len, k_len, bs, scale=0.25, coverage=cov.astype(np.float32), k_cov=6,
+                              k_unc=5, mass=0.6, prev_blocks=(8, 11))
+    assert r32["covered"].tolist() == [True, True, False, False]
+    for a, b in zip(r["lists"], r32["lists"]):
+        assert np.array_equal(a, b)
