@@ -42,10 +42,14 @@ struct AttnProblem {
     int64_t q_ts;          // raster token stride of q, elements
 };
 
-// Workspace layout of the router (byte offsets, 256-byte aligned).
+// Workspace layout of the router (byte offsets, 256-byte aligned).  Rows
+// with more than kSegCandidates candidates are selected in two levels: the
+// top-K of each segment of kSegCandidates candidates (n_seg segments, at
+// most seg_cap pairs each: order keys at seg_key, candidate indices at
+// seg_idx, counts at seg_cnt), then the top-K over those pairs.
 struct RouteLayout {
-    size_t qbar, kbar, keys, keff, flags, bitmap, counts, total;
-    int n_cand;
+    size_t qbar, kbar, keys, keff, flags, bitmap, counts, seg_key, seg_idx, seg_cnt, total;
+    int n_cand, n_seg, seg_cap;
     bool kbar_in_ws, keys_in_ws;
 };
 
@@ -66,8 +70,14 @@ int validate_block_window(const int32_t* perm, const int32_t* inv, int T, int H,
                           const int32_t* window, const int32_t* window_len, int window_stride);
 size_t route_layout(const bsa_route_args* a, RouteLayout* lay);
 
-// Largest candidate count the in-LDS top-K sort handles.
-constexpr int kMaxCandidates = 4096;
+// Candidates one wave selects over (64 lanes x 64 keys in registers).
+constexpr int kSegCandidates = 4096;
+// Largest candidate count of the router (16 segments; the second level
+// needs segments x min(K cap, kSegCandidates) <= kSegCandidates).
+constexpr int kMaxCandidates = 16 * kSegCandidates;
+// Largest KV block count of the route materialisation (one LDS bitmap bit
+// per block and row).
+constexpr int kMaxMaterializeBlocks = 4096;
 int validate_tile_index(int T, int H, int W, int tt, int th, int tw, const int32_t* row_cell, const int32_t* block_len);
 int validate_tile_perm(const void* src, const void* dst, const int32_t* row_cell, int n_rows, int L, int heads, int d,
                        int64_t raster_token_stride, int64_t tiled_head_stride, int inverse, int dtype);

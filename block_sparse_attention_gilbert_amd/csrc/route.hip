@@ -634,6 +634,138 @@ topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int 
     }
 }
 
+// First level of the selection for rows with more than kSegCandidates
+// candidates: one wave per (row, segment of kSegCandidates candidates)
+// keeps the segment's top min(K_eff, visible) under the same total order
+// (key descending, index ascending) and writes them, ascending by index, as
+// (order key, candidate index) pairs at slot (row, segment) of the
+// workspace, with their count.  A row's top K_eff is among the union of its
+// segments' top K_eff.
+__global__ void __launch_bounds__(kThreads)
+topk_segment_kernel(const double* __restrict__ keys, int rows, int n_cand, int n_seg, int block,
+                    const int32_t* __restrict__ kv_len, const int32_t* __restrict__ keff, int seg_cap,
+                    unsigned long long* __restrict__ seg_key, int32_t* __restrict__ seg_idx,
+                    int32_t* __restrict__ seg_cnt) {
+    constexpr int KPL = kSegCandidates / 64;
+    __shared__ int hist_all[kThreads / 64][256];
+    __shared__ unsigned long long cand_key[kThreads / 64][kSelScratch];
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int u = blockIdx.x * (kThreads / 64) + w;
+    if (u >= rows * n_seg) return;
+    const int r = u / n_seg, sg = u % n_seg;
+    const int j0 = sg * kSegCandidates;
+    const unsigned long long lt_mask = (1ull << lane) - 1ull;
+    const double* row = keys + (int64_t)r * n_cand;
+    unsigned long long key[KPL];
+    int n_vis = 0;
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+        const int j = j0 + lane + 64 * m;
+        double x = 0.0;
+        int v = 0;
+        if (j < n_cand) {
+            x = row[j];
+            v = kv_len ? kv_len[j] : block;
+        }
+        key[m] = v > 0 ? order_key(x) : 0ull;
+        n_vis += __popcll(__ballot(key[m] != 0));
+    }
+    int ke = keff[r];
+    ke = ke < n_vis ? ke : n_vis;
+    ke = ke < seg_cap ? ke : seg_cap;
+    if (lane == 0) seg_cnt[u] = ke;
+    if (ke <= 0) return;
+    unsigned long long prefix;
+    int need;
+    bool all_eq;
+    select_threshold<KPL>(key, ke, lane, hist_all[w], cand_key[w], prefix, need, all_eq);
+    const int64_t base0 = (int64_t)u * seg_cap;
+    int base = 0, eq_seen = 0;
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+        const bool gt = key[m] > prefix;
+        const bool eq = key[m] != 0 && key[m] == prefix;
+        const unsigned long long beq = __ballot(eq);
+        const int rank = eq_seen + __popcll(beq & lt_mask);
+        eq_seen += __popcll(beq);
+        const bool sel = gt || (eq && (all_eq || rank < need));
+        const unsigned long long bs = __ballot(sel);
+        if (sel) {
+            const int64_t at = base0 + base + __popcll(bs & lt_mask);
+            seg_key[at] = key[m];
+            seg_idx[at] = j0 + lane + 64 * m;
+        }
+        base += __popcll(bs);
+    }
+}
+
+// Second level: one wave per row selects its top K_eff among its segments'
+// pairs (entry p = segment * seg_cap + e, e < the segment's count; lane l
+// holds entries l + 64 m, i.e. ascending candidate index) and writes their
+// indices, ascending, after row_ptr[r], then the dense tail.
+template <int KPL>
+__global__ void __launch_bounds__(kThreads)
+topk_merge_kernel(const unsigned long long* __restrict__ seg_key, const int32_t* __restrict__ seg_idx,
+                  const int32_t* __restrict__ seg_cnt, int rows, int nqb, int nkb, int n_cand, int n_seg,
+                  int seg_cap, int block, const int32_t* __restrict__ q_len, const int32_t* __restrict__ kv_len,
+                  const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ keff,
+                  int32_t* __restrict__ col_idx) {
+    __shared__ int hist_all[kThreads / 64][256];
+    __shared__ unsigned long long cand_key[kThreads / 64][kSelScratch];
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = blockIdx.x * (kThreads / 64) + w;
+    if (r >= rows) return;
+    const int i = r % nqb;
+    const int vq = q_len ? q_len[i] : block;
+    if (vq <= 0) return;
+    const unsigned long long lt_mask = (1ull << lane) - 1ull;
+    const int M = n_seg * seg_cap;
+    const int64_t base0 = (int64_t)r * M;
+    unsigned long long key[KPL];
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+        const int p = lane + 64 * m;
+        unsigned long long k = 0ull;
+        if (p < M) {
+            const int sg = p / seg_cap, e = p - sg * seg_cap;
+            if (e < seg_cnt[(int64_t)r * n_seg + sg]) k = seg_key[base0 + p];
+        }
+        key[m] = k;
+    }
+    const int ke = keff[r];
+    int base = row_ptr[r];
+    if (ke > 0) {
+        unsigned long long prefix;
+        int need;
+        bool all_eq;
+        select_threshold<KPL>(key, ke, lane, hist_all[w], cand_key[w], prefix, need, all_eq);
+        int eq_seen = 0;
+#pragma unroll
+        for (int m = 0; m < KPL; ++m) {
+            const bool gt = key[m] > prefix;
+            const bool eq = key[m] != 0 && key[m] == prefix;
+            const unsigned long long beq = __ballot(eq);
+            const int rank = eq_seen + __popcll(beq & lt_mask);
+            eq_seen += __popcll(beq);
+            const bool sel = gt || (eq && (all_eq || rank < need));
+            const unsigned long long bs = __ballot(sel);
+            if (sel) col_idx[base + __popcll(bs & lt_mask)] = seg_idx[base0 + lane + 64 * m];
+            base += __popcll(bs);
+        }
+    }
+    for (int j0 = n_cand; j0 < nkb; j0 += 64) {
+        const int jb = j0 + lane;
+        bool take = false;
+        if (jb < nkb) {
+            const int v = kv_len ? kv_len[jb] : block;
+            take = v > 0;
+        }
+        const unsigned long long bt = __ballot(take);
+        if (take) col_idx[base + __popcll(bt & lt_mask)] = jb;
+        base += __popcll(bt);
+    }
+}
+
 // ------------------------------------------------------------------------
 // Route materialisation.
 // [Velox: Spatial Memory Makes World Models Efficient -- Methodology,
@@ -676,7 +808,7 @@ materialize_kernel(const double* __restrict__ keys, int rows, int nqb, int nkb, 
     __shared__ int hist_all[kThreads / 64][256];
     __shared__ unsigned long long skey_all[kThreads / 64][kMaxUnc];
     __shared__ int sidx_all[kThreads / 64][kMaxUnc];
-    __shared__ uint32_t bits_all[kThreads / 64][kMaxCandidates / 32];
+    __shared__ uint32_t bits_all[kThreads / 64][kMaxMaterializeBlocks / 32];
     __shared__ unsigned long long cand_all[kThreads / 64][kSelScratch];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = blockIdx.x * (kThreads / 64) + w;
@@ -974,13 +1106,42 @@ hipError_t launch_route(const bsa_route_args* a, const RouteLayout& lay, void* w
     // 5. list lengths and row pointers: with one fixed budget (and no
     // overlap rows to count) the selection kernel derives them itself and
     // writes the (zero) fallback counts
-    const bool fused = !a->k_per_row && !want_flags && a->nqb <= 4096;
+    const bool two_level = lay.n_seg > 1;
+    const bool fused = !a->k_per_row && !want_flags && a->nqb <= 4096 && !two_level;
     if (!fused)
         hipLaunchKernelGGL(rowptr_kernel, dim3(1), dim3(1024), 0, stream, a->heads, a->nqb, a->nkb, n_cand, a->block,
                            a->q_block_len, a->kv_block_len, a->k_per_row ? 0 : a->k_fixed, a->k_per_row,
                            a->k_max, want_flags ? flags : nullptr, a->row_ptr, keff, a->fallback_counts);
-    // 6. selection: one wave per row
     const int rows = a->heads * a->nqb;
+    if (two_level) {
+        // 6'. selection in two levels: each segment's top-K, then the top-K
+        // over those
+        char* wb = static_cast<char*>(ws);
+        auto* seg_key = reinterpret_cast<unsigned long long*>(wb + lay.seg_key);
+        auto* seg_idx = reinterpret_cast<int32_t*>(wb + lay.seg_idx);
+        auto* seg_cnt = reinterpret_cast<int32_t*>(wb + lay.seg_cnt);
+        const int units = rows * lay.n_seg;
+        hipLaunchKernelGGL(topk_segment_kernel, dim3((units + kThreads / 64 - 1) / (kThreads / 64)), dim3(kThreads),
+                           0, stream, keys, rows, n_cand, lay.n_seg, a->block, a->kv_block_len, keff, lay.seg_cap,
+                           seg_key, seg_idx, seg_cnt);
+        const dim3 mgrid((rows + kThreads / 64 - 1) / (kThreads / 64));
+        const int M = lay.n_seg * lay.seg_cap;
+#define BSA_MERGE(KPL)                                                                                          \
+    hipLaunchKernelGGL(topk_merge_kernel<KPL>, mgrid, dim3(kThreads), 0, stream, seg_key, seg_idx, seg_cnt, rows, \
+                       a->nqb, a->nkb, n_cand, lay.n_seg, lay.seg_cap, a->block, a->q_block_len, a->kv_block_len, \
+                       a->row_ptr, keff, a->col_idx)
+        if (M <= 64 * 8)
+            BSA_MERGE(8);
+        else if (M <= 64 * 16)
+            BSA_MERGE(16);
+        else if (M <= 64 * 32)
+            BSA_MERGE(32);
+        else
+            BSA_MERGE(64);
+#undef BSA_MERGE
+        return hipGetLastError();
+    }
+    // 6. selection: one wave per row
     const int k_fused = fused ? a->k_fixed : -1;
     const dim3 grid((rows + kThreads / 64 - 1) / (kThreads / 64));
 #define BSA_TOPK(KPL)                                                                                       \

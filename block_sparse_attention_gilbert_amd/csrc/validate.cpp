@@ -205,6 +205,21 @@ size_t route_layout(const bsa_route_args* a, RouteLayout* lay) {
     lay->flags = off;
     off = align256(off + sizeof(int32_t) * ((size_t)a->nqb + 8));
     lay->bitmap = lay->counts = off;
+    // two-level selection: the segments' top-K pairs
+    lay->n_seg = n_cand > kSegCandidates ? (int)ceil_div(n_cand, kSegCandidates) : 1;
+    int kcap = a->k_per_row ? a->k_max : a->k_fixed;
+    kcap = kcap < 0 ? 0 : (kcap > kSegCandidates ? kSegCandidates : kcap);
+    lay->seg_cap = lay->n_seg > 1 ? kcap : 0;
+    lay->seg_key = lay->seg_idx = lay->seg_cnt = off;
+    if (lay->n_seg > 1) {
+        const size_t pairs = (size_t)a->heads * a->nqb * lay->n_seg * (size_t)lay->seg_cap;
+        lay->seg_key = off;
+        off = align256(off + sizeof(unsigned long long) * pairs);
+        lay->seg_idx = off;
+        off = align256(off + sizeof(int32_t) * pairs);
+        lay->seg_cnt = off;
+        off = align256(off + sizeof(int32_t) * (size_t)a->heads * a->nqb * lay->n_seg);
+    }
     lay->total = off;
     return off;
 }
@@ -225,8 +240,7 @@ int validate_route(const bsa_route_args* a, RouteLayout* lay) {
         return fail(BSA_EINVAL, "n_dense_tail_blocks %d outside [0, nkb]", a->n_dense_tail_blocks);
     const int n_cand = a->nkb - a->n_dense_tail_blocks;
     if (n_cand > kMaxCandidates)
-        return fail(BSA_EUNSUPPORTED, "%d candidate blocks exceed the in-LDS selection limit %d", n_cand,
-                    kMaxCandidates);
+        return fail(BSA_EUNSUPPORTED, "%d candidate blocks exceed the selection limit %d", n_cand, kMaxCandidates);
     if ((int64_t)a->heads * a->nqb > (1 << 24)) return fail(BSA_EINVAL, "heads*nqb too large");
     const int64_t qrows = (int64_t)a->nqb * a->block, krows = (int64_t)a->nkb * a->block;
     if (a->q && a->q_head_stride < qrows * a->d) return fail(BSA_EINVAL, "q_head_stride below nqb*block*d");
@@ -259,6 +273,10 @@ int validate_route(const bsa_route_args* a, RouteLayout* lay) {
         return fail(BSA_EINVAL, "kpool_valid_blocks %d outside [0, %d]", a->kpool_valid_blocks, n_cand);
     if (a->kpool && a->kpool_head_blocks != 0 && a->kpool_head_blocks < n_cand)
         return fail(BSA_EINVAL, "kpool_head_blocks %d below the candidate count %d", a->kpool_head_blocks, n_cand);
+    if (n_cand > kSegCandidates && ceil_div(n_cand, kSegCandidates) * (int64_t)kcap > kSegCandidates)
+        return fail(BSA_EUNSUPPORTED,
+                    "%d candidates in %lld segments with a budget cap of %d: segments x cap must be <= %d", n_cand,
+                    (long long)ceil_div(n_cand, kSegCandidates), kcap, kSegCandidates);
     const int64_t need = (int64_t)a->heads * a->nqb * ((int64_t)kcap + a->n_dense_tail_blocks);
     if (a->col_capacity < need)
         return fail(BSA_EINVAL, "col_capacity %lld < heads*nqb*(k cap + dense tail) = %lld",
@@ -279,6 +297,9 @@ int validate_materialize(const bsa_route_args* a, const bsa_materialize_args* m,
             return fail(BSA_EINVAL, "n_dense_tail_blocks must be 0: every KV block is a candidate");
         if (a->fallback_counts) return fail(BSA_EINVAL, "fallback_counts must be NULL (not produced)");
     }
+    if (a->nkb > kMaxMaterializeBlocks)
+        return fail(BSA_EUNSUPPORTED, "%d KV blocks exceed the materialisation limit %d", a->nkb,
+                    kMaxMaterializeBlocks);
     // the router's own checks, with the top-K budget out of the way
     bsa_route_args base = *a;
     base.k_fixed = 0;

@@ -280,9 +280,14 @@ size_t bsa_route_workspace_size(const bsa_route_args* args);
  * bsa_route_topk -- pool, score, fuse and select; see bsa_route_args.
  * workspace: device memory of at least bsa_route_workspace_size(args) bytes,
  * 256-byte aligned, owned by the caller, not read before it is written.
+ * Rows of up to 4096 candidates are selected by one wave each; longer
+ * rows in segments of 4096 candidates, whose top-K are merged into the
+ * row's top-K (the same lists, bit for bit).
  * Errors: BSA_EINVAL (arguments; col_capacity below
  * heads*nqb*(min(k cap, candidates) + n_dense_tail_blocks)),
- * BSA_EUNSUPPORTED, BSA_EWORKSPACE.
+ * BSA_EUNSUPPORTED (more than 65536 candidates, or more than 4096
+ * candidates with ceil(candidates / 4096) * min(k cap, candidates) above
+ * 4096; d, block or dtype), BSA_EWORKSPACE.
  */
 int bsa_route_topk(const bsa_route_args* args, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);

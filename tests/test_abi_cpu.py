@@ -199,7 +199,18 @@ def test_route_rejects_and_sizes():
     assert lib.bsa_route_workspace_size(ctypes.byref(bad)) == 0
     assert lib.bsa_route_topk(ctypes.byref(_route_args(col_capacity=1480 * 50 - 1)), FAKE, need, None) \
         == bsa.BSA_EINVAL
-    assert lib.bsa_route_topk(ctypes.byref(_route_args(nkb=5000)), FAKE, need, None) == bsa.BSA_EUNSUPPORTED
+    assert lib.bsa_route_topk(ctypes.byref(_route_args(nkb=70000)), FAKE, need, None) == bsa.BSA_EUNSUPPORTED
+    # more than 4096 candidates: selected in segments of 4096 whose top-K
+    # pairs are merged, which needs segments x budget cap <= 4096
+    seg = _route_args(nkb=20000, k_head_stride=20000 * 128 * 128)
+    need_seg = lib.bsa_route_workspace_size(ctypes.byref(seg))
+    # the segments' pairs: 5 segments x 50 (8-byte key + 4-byte index) per row
+    assert need_seg >= 8 * (40 * 37 * 128 + 40 * 20000 * 128 + 40 * 37 * 20000) + 12 * 1480 * 5 * 50
+    assert lib.bsa_route_topk(ctypes.byref(seg), None, 0, None) == bsa.BSA_EWORKSPACE   # valid up to the workspace
+    big_k = _route_args(nkb=20000, k_head_stride=20000 * 128 * 128, k_fixed=1000, k_max=1000,
+                        col_capacity=1480 * 1000)
+    assert lib.bsa_route_topk(ctypes.byref(big_k), FAKE, 1 << 40, None) == bsa.BSA_EUNSUPPORTED
+    assert "segments" in lib.bsa_last_error_detail().decode()
     assert lib.bsa_route_topk(ctypes.byref(_route_args(n_dense_tail_blocks=2000)), FAKE, need, None) \
         == bsa.BSA_EINVAL
     assert lib.bsa_route_topk(ctypes.byref(_route_args(overlap=0x50000, overlap_row_stride=10)), FAKE, need,
@@ -231,7 +242,7 @@ def test_route_static_rejects_on_the_host():
     assert bsa.ROUTE_STATIC_SCRATCH_BYTES == 32 << 20
     f = lib.bsa_route_topk_static
     assert f(ctypes.byref(_route_args(struct_size=8)), None) == bsa.BSA_EINVAL
-    assert f(ctypes.byref(_route_args(nkb=5000)), None) == bsa.BSA_EUNSUPPORTED
+    assert f(ctypes.byref(_route_args(nkb=70000)), None) == bsa.BSA_EUNSUPPORTED
     big = _route_args()   # chunk 48 without a pooled-key cache: ~95 MB of scratch
     assert lib.bsa_route_workspace_size(ctypes.byref(big)) > bsa.ROUTE_STATIC_SCRATCH_BYTES
     assert f(ctypes.byref(big), None) == bsa.BSA_EWORKSPACE

@@ -198,8 +198,9 @@ def test_route_edge_cases():
 
 
 def test_route_maximum_candidates():
-    """4096 candidates (the largest the selection supports) with per-row
-    budgets up to 143 and a dense tail, against the oracle."""
+    """4096 candidates (the most one wave selects over) with per-row budgets
+    up to 143 and a dense tail, and 4097 (a second segment of one
+    candidate), against the oracle."""
     dev = need_gpu()
     import block_sparse_attention_gilbert_amd as bsa
     rng = np.random.default_rng(4096)
@@ -216,10 +217,17 @@ def test_route_maximum_candidates():
         ref = oroute.route_head(f64(q[h]), f64(k[h]), [bs] * nqb, [bs] * nkb, bs, scale=0.125,
                                 k_per_row=kpr[h * nqb:(h + 1) * nqb], n_dense_tail=tail)
         assert_lists_equal(got[h], ref["lists"], "max candidates head %d" % h)
-    with pytest.raises(bsa.BsaError) as err:  # one candidate more than the selection handles
-        bsa.route_topk(q.to(dev), torch.zeros((heads, (n_cand + 1) * bs, d), dtype=torch.bfloat16, device=dev),
-                       block=bs, nqb=nqb, nkb=n_cand + 1, scale=0.125, k_fixed=5)
-    assert err.value.code == bsa.BSA_EUNSUPPORTED
+    # one candidate more: two segments, the second holding a single block
+    # that is the best of every row
+    k2 = torch.cat([k, torch.zeros((heads, bs, d), dtype=torch.bfloat16)], dim=1)
+    k2[:, n_cand * bs:] = q[:, :bs].float().mean(dim=1, keepdim=True).mul(50).to(torch.bfloat16)
+    r2 = bsa.route_topk(q.to(dev), k2.to(dev), block=bs, nqb=nqb, nkb=n_cand + 1, scale=0.125, k_fixed=5)
+    got2 = csr_lists(r2["row_ptr"], r2["col_idx"], heads, nqb)
+    for h in range(heads):
+        ref = oroute.route_head(f64(q[h]), f64(k2[h]), [bs] * nqb, [bs] * (n_cand + 1), bs, scale=0.125,
+                                k_per_row=np.full(nqb, 5))
+        assert_lists_equal(got2[h], ref["lists"], "4097 candidates head %d" % h)
+    assert n_cand in got2[0][0].tolist()
 
 
 def test_route_selection_paths():
@@ -243,3 +251,75 @@ def test_route_selection_paths():
                                     k_per_row=[K] * nqb)
             assert_lists_equal(got[h], ref["lists"], "K=%d head %d" % (K, h))
             assert np.array_equal(got[h][2], np.arange(K))  # ties: the lowest indices
+
+
+def _long_history(seed, heads, d, bs, n_chunks, nbc_tokens=4680):
+    """Q of one chunk and K of a long history (per-chunk padded blocks), N(0,1)
+    plus N(0, 0.5^2) per-block offsets, bf16 (input recipe of the growing
+    context, without its V)."""
+    rng = np.random.default_rng(seed)
+    q_len = workloads.block_lengths(nbc_tokens, bs)
+    k_len = np.tile(q_len, n_chunks).astype(np.int32)
+
+    def blocked(lens):
+        x = rng.standard_normal((heads, len(lens), bs, d), dtype=np.float32)
+        x += rng.standard_normal((heads, len(lens), 1, d), dtype=np.float32) * np.float32(0.5)
+        x[:, np.arange(bs)[None, :] >= lens[:, None]] = 0.0
+        return torch.from_numpy(x.reshape(heads, len(lens) * bs, d)).to(torch.bfloat16)
+
+    return blocked(q_len), blocked(k_len), q_len, k_len
+
+
+@pytest.mark.parametrize("d,bs,n_chunks,heads", [(128, 128, 170, 1), (64, 64, 90, 2)])
+def test_routes_beyond_one_wave_of_candidates(d, bs, n_chunks, heads):
+    """More than 4096 candidates (6290 and 6660): selected in segments of 4096
+    whose top-K are merged; lists bit-exact against the oracle for a fixed
+    budget and for per-row budgets up to 256."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    q, k, q_len, k_len = _long_history(31 + d, heads, d, bs, n_chunks)
+    nqb, nkb = len(q_len), len(k_len)
+    assert nkb > 6000
+    scale = d ** -0.5
+    kpr = np.random.default_rng(5).integers(1, 257, size=heads * nqb).astype(np.int32)
+    kw = dict(block=bs, nqb=nqb, nkb=nkb, scale=scale, q_block_len=torch.from_numpy(q_len).to(dev),
+              kv_block_len=torch.from_numpy(k_len).to(dev))
+    print("routing %d candidates" % nkb, flush=True)
+    r_fix = bsa.route_topk(q.to(dev), k.to(dev), k_fixed=50, **kw)
+    r_var = bsa.route_topk(q.to(dev), k.to(dev), k_per_row=torch.from_numpy(kpr).to(dev), k_max=256, **kw)
+    torch.cuda.synchronize()
+    g_fix = csr_lists(r_fix["row_ptr"], r_fix["col_idx"], heads, nqb)
+    g_var = csr_lists(r_var["row_ptr"], r_var["col_idx"], heads, nqb)
+    for h in range(heads):
+        qh, kh = f64(q[h]), f64(k[h])
+        ref = oroute.route_head(qh, kh, q_len, k_len, bs, scale=scale, k_per_row=np.full(nqb, 50))
+        assert_lists_equal(g_fix[h], ref["lists"], "fixed budget head %d" % h)
+        ref = oroute.route_head(qh, kh, q_len, k_len, bs, scale=scale, k_per_row=kpr[h * nqb:(h + 1) * nqb])
+        assert_lists_equal(g_var[h], ref["lists"], "per-row budgets head %d" % h)
+
+
+def test_routes_beyond_one_wave_ties_across_segments():
+    """Exact ties between blocks of different segments (the same K rows copied
+    into a block of a later segment): the lower index wins, as in the
+    oracle, also when the budget cuts between the copies."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    q, k, q_len, k_len = _long_history(47, 1, 64, 64, 70)
+    nqb, nkb = len(q_len), len(k_len)
+    assert 4240 < nkb     # two segments: 4096 + the rest
+    k = k.clone()
+    # copy the 40 blocks a row likes best into blocks past the first segment
+    qh, kh = f64(q[0]), f64(k[0])
+    best = np.argsort(-oroute.route_head(qh, kh, q_len, k_len, 64, scale=0.125,
+                                         k_per_row=np.full(nqb, 40))["kappa"][3])[:40]
+    dst = np.arange(4200, 4200 + 40)
+    for a, b in zip(best, dst):
+        k[0, b * 64:(b + 1) * 64] = k[0, a * 64:(a + 1) * 64]
+        k_len[b] = k_len[a]
+    for kf in (20, 40, 60):
+        r = bsa.route_topk(q.to(dev), k.to(dev), block=64, nqb=nqb, nkb=nkb, scale=0.125, k_fixed=kf,
+                           q_block_len=torch.from_numpy(q_len).to(dev), kv_block_len=torch.from_numpy(k_len).to(dev))
+        torch.cuda.synchronize()
+        got = csr_lists(r["row_ptr"], r["col_idx"], 1, nqb)
+        ref = oroute.route_head(qh, f64(k[0]), q_len, k_len, 64, scale=0.125, k_per_row=np.full(nqb, kf))
+        assert_lists_equal(got[0], ref["lists"], "ties, budget %d" % kf)
