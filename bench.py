@@ -11,7 +11,8 @@ Inputs are seeded synthetic tensors (``workloads.c4``), resident in HBM
 before timing starts.
 
 One step is one attention call of the chunked model, the whole hot path:
-Gilbert index of the chunk grid; permutation of the current chunk's raster
+(the Gilbert index of the chunk grid is computed once per grid shape and
+kept; it is timed alone in the breakdown) permutation of the current chunk's raster
 Q, K, V into Gilbert head-major blocks (K, V into the store's newest slot);
 routing (mean-pool Q and the K blocks appended since the previous call --
 the pooled history keys are cached across calls, as the store only grows by
@@ -25,7 +26,8 @@ attention launch with L2 and MALL flushed before each call
 (``breakdown``), the bf16 matrix rate a register-only MFMA probe gets at
 the current clock (``mfma_probe``), dense attention through the same kernel
 (``dense``), the shader/memory clocks at start and end (``clocks``), the
-ragged structured configuration C5 at chunk 48 (``c5``), and
+ragged structured configuration C5 at chunk 48 (``c5``), the attention of
+the Wan-1.3B-like layer C2 with its matrix-core roofline (``c2``), and
 the step with the materialised route instead of the top-K
 (``materialized``: coverage-gated budgets, previous-chunk reservation,
 cumulative-mass prefix and the local window), its overlap and coverage
@@ -57,6 +59,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "block-sparse attn effective TFLOP/s + ms/call at chunk 48; % bf16 MFMA peak"
+SETTLE_MS = 400.0              # steady GPU load run before the warm-up steps (clock ramp after set-up)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_c4_chunk48_traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_gilbert_amd", "csrc", "attn.hip")
 
@@ -375,6 +378,60 @@ def c5_config(reps: int, device: str):
            "attn_alg_gbs": round(wc["alg_bytes"] / (attn_ms * 1e-3) / 1e9, 1),
            "step_effective_tflops": round(wc["flop"] / (ms_step * 1e-3) / 1e12, 2)}
     del ra, q_r, k_r, v_r
+    torch.cuda.empty_cache()
+    return out
+
+
+def c2_config(reps: int, device: str):
+    """C2 (the Wan-1.3B-like layer: 12 heads, 37 query blocks of 128, 143
+    history blocks, top-K 50, bf16): routed once, then the attention launch
+    timed alone (median of ``reps``), its effective TFLOP/s and its
+    roofline.  Every query block of a head reuses the same 143 history
+    blocks (112 MB of K and V for the 12 heads), about 1300 FLOP per
+    algorithmic byte: the launch is bound by the matrix cores, not HBM."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from block_sparse_attention_gilbert_amd import block_sparse_attn, route_topk
+
+    w = workloads.c2()
+    q, k, v = w.q.to(device), w.k.to(device), w.v.to(device)
+    ql = torch.from_numpy(w.q_len.astype(np.int32)).to(device)
+    kl = torch.from_numpy(w.k_len.astype(np.int32)).to(device)
+    r = route_topk(q, k, block=w.bs, nqb=w.nqb, nkb=w.nkb, scale=w.scale, q_block_len=ql, kv_block_len=kl,
+                   k_fixed=50)
+    out_t = torch.empty_like(q)
+
+    def call():
+        block_sparse_attn(q, k, v, r["row_ptr"], r["col_idx"], block=w.bs, scale=w.scale, q_block_len=ql,
+                          kv_block_len=kl, out=out_t)
+
+    for _ in range(max(20, reps)):
+        call()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = statistics.median(a.elapsed_time(b) for a, b in evs)
+    wc = work_counts(r["row_ptr"], r["col_idx"], w.q_len, w.k_len, w.heads, w.nqb, w.bs, w.d)
+    tflops = wc["flop"] / (ms * 1e-3) / 1e12
+    intensity = wc["flop"] / wc["alg_bytes"]
+    out = {"workload": "C2 Wan-1.3B-like layer (12 heads, 143 history blocks, top-K 50)", "attn_ms": round(ms, 4),
+           "effective_flop": wc["flop"], "attn_effective_tflops": round(tflops, 2),
+           "pct_bf16_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+           "roofline": {"bound": "mfma" if intensity * PEAK_HBM_GBS / 1e3 > PEAK_BF16_TFLOPS else "hbm",
+                        "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                        "intensity_flop_per_byte": round(intensity, 1), "alg_bytes_per_launch": wc["alg_bytes"]}}
+    del q, k, v, out_t, r
     torch.cuda.empty_cache()
     return out
 
@@ -760,6 +817,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=40)
     ap.add_argument("--no-dense", action="store_true", help="skip timing dense attention at the same chunk")
     ap.add_argument("--no-c5", action="store_true", help="skip timing the C5 (ragged, structured) configuration")
+    ap.add_argument("--no-c2", action="store_true", help="skip timing the C2 (Wan-1.3B-like layer) attention")
     ap.add_argument("--oracle-table", default=None, metavar="FILE",
                     help="write the float64 oracle's host times beside the GPU's, config by config, to this JSONL file")
     ap.add_argument("--tiles", action="store_true",
@@ -825,6 +883,21 @@ def main():
     torch.cuda.synchronize()
     assert torch.equal(ks_before, ra.slot(st["cur"])[0]), "forward permutation did not reproduce the store slot"
     del ks_before
+    # settle: after set-up (uploads, allocations, host work) the GPU's clock
+    # takes a few hundred milliseconds of steady load to come back up, which
+    # a short warm-up would leave inside the timed region; a fixed settle
+    # phase of steps runs first, so the steady state does not depend on
+    # --warmup
+    settle_ms, settle_steps = 0.0, 0
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    while settle_ms < SETTLE_MS and settle_steps < 5000:
+        s0.record()
+        for _ in range(50):
+            run_step(st)
+        s1.record()
+        torch.cuda.synchronize()
+        settle_ms += s0.elapsed_time(s1)
+        settle_steps += 50
     for _ in range(args.warmup):
         run_step(st)
     torch.cuda.synchronize()
@@ -880,10 +953,12 @@ def main():
         "config": {"workload": "C4 growing-context 14B-like layer at chunk %d" % args.chunk,
                    "heads": w.heads, "head_dim": w.d, "block": w.bs, "query_tokens": 4680,
                    "kv_tokens": 4680 * args.chunk, "kv_blocks": w.nkb, "top_k": 50,
-                   "step": "gilbert_index + one launch permuting K and V into the store (K with its block "
-                           "means, Q block means only) + route (cached history pools; score all 1776 "
-                           "candidates; top-K) + block-sparse attention reading Q and writing O in raster "
-                           "order", "parallelism": "single GPU"},
+                   "step": "one launch permuting K and V into the store (K with its block means, Q block "
+                           "means only) + route (cached history pools; score all 1776 candidates; top-K) + "
+                           "block-sparse attention reading Q and writing O in raster order; the Gilbert index "
+                           "is computed once per grid shape (timed alone in breakdown)",
+                   "parallelism": "single GPU"},
+        "settle": {"steps": settle_steps, "ms": round(settle_ms, 1)},
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "attn": {"ms_per_call": round(attn_ms, 4),
                  "ms_median": round(attn_all[len(attn_all) // 2], 4),
@@ -929,6 +1004,8 @@ def main():
         out["tiles"] = tiles(args.chunk, max(1, min(args.steps, 10)), dev)
     if not args.no_c5:
         out["c5"] = c5_config(max(1, min(args.steps, 10)), dev)
+    if not args.no_c2:
+        out["c2"] = c2_config(max(10, min(args.steps, 50)), dev)
     if args.sweep:
         sweep(st, args.sweep)
     if args.rollout:

@@ -8,7 +8,7 @@ Steps 4-6; Key Contributions 3]
 
 Per call (``RoutedAttention.step``):
 
-1. the chunk's Gilbert order (recomputed into preallocated buffers); blocks
+1. the chunk's Gilbert order (computed once per grid shape and kept); blocks
    are runs of ``block`` tokens along it, or, with ``tile=(tt, th, tw)``,
    fixed tt x th x tw tiles ordered by the Gilbert curve of the tile grid
    [Light Interaction -- abstract: 3-D block-sparse attention];
@@ -188,7 +188,7 @@ class RoutedAttention:
 
     def step(self, q_raster, k_raster, v_raster, c: int, *, k_fixed: Optional[int] = None,
              k_per_row: Optional[torch.Tensor] = None, overlap: Optional[torch.Tensor] = None,
-             lam=2.0, g_ref=0.2, tau=0.1, materialize: Optional[dict] = None, refresh_index: bool = True,
+             lam=2.0, g_ref=0.2, tau=0.1, materialize: Optional[dict] = None, refresh_index: bool = False,
              stream=None, attn_events=None):
         """One attention call for chunk ``c`` (0-based) over chunks 0..c.
         Returns ``(o_raster, route_out)``.  ``attn_events``: optional list
@@ -197,7 +197,9 @@ class RoutedAttention:
         keyword arguments of ``route_materialize`` (``coverage``,
         ``eta_cov``, ``k_cov``, ``k_unc``, ``mass``, ``ref_blocks``; plus
         ``window=False`` to leave the local window out) to route with the
-        materialised lists instead of a top-K."""
+        materialised lists instead of a top-K.  The chunk's Gilbert order is
+        fixed by its grid: it is computed when the object is built and kept;
+        ``refresh_index`` recomputes it into the same buffers first."""
         if refresh_index:
             self._index(stream)
         # curve blocks: Q stays raster (its block means taken in one read),
