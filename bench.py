@@ -628,6 +628,98 @@ def profile_attention(launches: int, expect_out=None):
     print("profile-attention done: %d attention launches, one %d-byte copy" % (launches, COPY_BYTES), flush=True)
 
 
+def coloured_visit_order(row_ptr, col_idx, heads: int, nqb: int):
+    """Measurement experiment (host side, not part of the path): the same
+    lists, each row visited in a co-scheduled order.  Per head, every
+    selected block gets one slot (blocks with more selectors first, each
+    the smallest slot free in all its selectors), and each row visits its
+    blocks by slot, so the query blocks that share a block reach it at the
+    same list position.  Returns the reordered col_idx (row_ptr unchanged)."""
+    import numpy as np
+    rp = row_ptr.cpu().numpy().astype(np.int64)
+    ci = col_idx.cpu().numpy().astype(np.int64)
+    out = ci.copy()
+    for h in range(heads):
+        rows = [ci[rp[h * nqb + i]:rp[h * nqb + i + 1]] for i in range(nqb)]
+        sel = {}
+        for i, row in enumerate(rows):
+            for b in row.tolist():
+                sel.setdefault(b, []).append(i)
+        used = [0] * nqb
+        slot = {}
+        for b in sorted(sel, key=lambda x: (-len(sel[x]), x)):
+            busy = 0
+            for i in sel[b]:
+                busy |= used[i]
+            sl = 0
+            while busy >> sl & 1:
+                sl += 1
+            slot[b] = sl
+            for i in sel[b]:
+                used[i] |= 1 << sl
+        for i, row in enumerate(rows):
+            r0 = rp[h * nqb + i]
+            out[r0:r0 + len(row)] = sorted(row.tolist(), key=lambda x: (slot[x], x))
+    return torch_int32(out)
+
+
+def torch_int32(a):
+    import torch
+    return torch.from_numpy(a.astype("int32"))
+
+
+def visit_order_experiment(order: str, launches: int, timing: bool):
+    """C4 at chunk 48: the step's lists visited in ascending order (as the
+    router writes them) or in the co-scheduled order of
+    ``coloured_visit_order``; ``launches`` attention launches (for counter
+    runs), or with ``timing`` both orders timed in alternation (median of
+    their launch times) and the largest output difference between them."""
+    import statistics
+
+    import torch
+    st = setup_c4(48, device="cuda:0")
+    ra = st["ra"]
+    for _ in range(20):
+        run_step(st)
+    torch.cuda.synchronize()
+    nkb = ra.store_chunks * ra.nbc
+    r = ra.route_out
+    k_hist, v_hist = ra.k_store[:, : nkb * ra.block], ra.v_store[:, : nkb * ra.block]
+    n = int(r["row_ptr"][-1].item())
+    cols = {"ascending": r["col_idx"][:n].clone(),
+            "coloured": coloured_visit_order(r["row_ptr"], r["col_idx"][:n], ra.heads, ra.nbc).to("cuda:0")}
+
+    def launch(name, out):
+        from block_sparse_attention_gilbert_amd import block_sparse_attn
+        block_sparse_attn(ra.q_blk, k_hist, v_hist, r["row_ptr"], cols[name], block=ra.block, scale=ra.scale,
+                          q_block_len=ra.q_len, kv_block_len=ra.kv_len[:nkb], out=out, lse=ra.lse)
+
+    if not timing:
+        for _ in range(launches):
+            launch(order, ra.o_blk)
+        torch.cuda.synchronize()
+        print("visit-order %s: %d launches" % (order, launches), flush=True)
+        return
+    outs = {k: torch.empty_like(ra.o_blk) for k in cols}
+    times = {k: [] for k in cols}
+    for _ in range(8):
+        for k in cols:
+            for _ in range(3):
+                launch(k, outs[k])
+            evs = []
+            for _ in range(15):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                launch(k, outs[k])
+                e1.record()
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            times[k] += [a.elapsed_time(b) for a, b in evs]
+    diff = float((outs["coloured"].float() - outs["ascending"].float()).abs().max())
+    print(json.dumps({k: round(statistics.median(v), 4) for k, v in times.items()} | {"max_abs_diff": diff}),
+          flush=True)
+
+
 def summarize_mfma(counter_csv: str, expect_json: str, out_path: str):
     """Per-launch matrix-core counters of the attention launches (sparse and
     dense) from one rocprofv3 --pmc CSV, against the MFMA count the lists
@@ -807,6 +899,49 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_path: str):
     print(json.dumps(out))
 
 
+def summarize_pipe(csvs, out_path: str):
+    """Per-launch averages of the pipeline counters of the attention launches
+    (block-sparse and dense) from rocprofv3 --pmc CSVs of bench.py
+    --profile-attention, with the derived rates: matrix cores busy, vector
+    issue busy, LDS busy and bank-conflict share, L2 hit rate.  Counters of
+    the SQ block are per-SIMD aggregates (the VALU and wait ones in units of
+    4 cycles); GRBM_GUI_ACTIVE is summed over the 8 XCDs."""
+    import csv
+
+    vals = {}
+    for path in csvs:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                name = row["Kernel_Name"]
+                kind = ("sparse" if "attn_bf16_kernel<128, 128, false>" in name else
+                        "dense" if "attn_bf16_kernel<128, 128, true>" in name else None)
+                if kind is None:
+                    continue
+                vals.setdefault(kind, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    simds, cus = 1024, 256
+    out = {"kernel": "attn_bf16_kernel<128,128>", "workload": "C4 chunk 48",
+           "attn_source_sha256_16": attn_source_hash()}
+    for kind, c in vals.items():
+        avg = {k: sum(v) / len(v) for k, v in c.items()}
+        d = {"counters_per_launch": avg}
+        cyc = avg.get("GRBM_GUI_ACTIVE", 0.0) / 8.0     # per XCD: the launch's GPU cycles
+        if cyc:
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                d["mfma_busy"] = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / cyc
+            if "SQ_ACTIVE_INST_VALU" in avg:
+                d["valu_issue_busy"] = 4.0 * avg["SQ_ACTIVE_INST_VALU"] / simds / cyc
+            if "SQ_LDS_IDX_ACTIVE" in avg:
+                d["lds_busy"] = avg["SQ_LDS_IDX_ACTIVE"] / cus / cyc
+        if avg.get("SQ_LDS_IDX_ACTIVE"):
+            d["lds_bank_conflict_share"] = avg.get("SQ_LDS_BANK_CONFLICT", 0.0) / avg["SQ_LDS_IDX_ACTIVE"]
+        if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg:
+            d["l2_hit_rate"] = avg["TCC_HIT_sum"] / max(1.0, avg["TCC_HIT_sum"] + avg["TCC_MISS_sum"])
+        out[kind] = d
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -834,13 +969,23 @@ def main():
                     help="counter mode: write the MFMA counts the launches must issue to this file")
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("COUNTER_CSV", "EXPECT_JSON", "OUT_JSON"),
                     help="compare the MFMA instruction counters of the attention launches with the listed tiles")
+    ap.add_argument("--visit-order", default=None, choices=["ascending", "coloured", "ab"],
+                    help="experiment: the attention launch on the step's lists in ascending or co-scheduled "
+                         "visit order (N launches, --visit-order-launches), or both timed in alternation (ab)")
+    ap.add_argument("--visit-order-launches", type=int, default=5)
     ap.add_argument("--profile-step", type=int, default=0, metavar="N",
                     help="counter mode: N whole steps + a 1 GiB copy, no JSON line")
     ap.add_argument("--summarize-step-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV", "OUT_MD"),
                     help="per-kernel HBM bytes and GB/s of the step from counter and kernel-trace runs")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                     help="write HBM bytes per attention launch from two rocprofv3 --pmc CSVs")
+    ap.add_argument("--summarize-pipe", nargs="+", metavar="CSV",
+                    help="pipeline counters of the attention launches (matrix, vector, LDS, L2) from rocprofv3 "
+                         "--pmc CSVs of --profile-attention; the last argument is the output JSON")
     args = ap.parse_args()
+    if args.summarize_pipe:
+        summarize_pipe(args.summarize_pipe[:-1], args.summarize_pipe[-1])
+        return
     if args.summarize_step_traffic:
         summarize_step_traffic(*args.summarize_step_traffic)
         return
@@ -863,6 +1008,9 @@ def main():
         return
     if args.profile_attention:
         profile_attention(args.profile_attention, args.expect_out)
+        return
+    if args.visit_order:
+        visit_order_experiment(args.visit_order, args.visit_order_launches, args.visit_order == "ab")
         return
 
     dev = "cuda:0"
