@@ -338,12 +338,11 @@ def tiles(chunk: int, reps: int, device: str, tile=(1, 8, 16)):
     return out
 
 
-def c5_config(reps: int, device: str):
+def setup_c5(device: str):
     """C5 at chunk 48 (ragged budgets K ~ U{8..143} over 47 history chunks of
     74 blocks of 64, the current chunk's 74 blocks attended densely, a
-    structured field): the whole step and the attention launch, after the
-    history has been appended chunk by chunk."""
-    import numpy as np
+    structured field): the pipeline with the history appended chunk by
+    chunk, and the current chunk's inputs on the device."""
     import torch
 
     import workloads
@@ -356,7 +355,15 @@ def c5_config(reps: int, device: str):
         ra.append(w.k_raster[c].to(device), w.v_raster[c].to(device), c)
     kpr = torch.from_numpy(w.k_per_row).to(device)
     q_r, k_r, v_r = w.q_raster.to(device), w.k_raster[-1].to(device), w.v_raster[-1].to(device)
-    del w
+    return ra, kpr, q_r, k_r, v_r, n_chunks
+
+
+def c5_config(reps: int, device: str):
+    """C5 at chunk 48: the whole step and the attention launch (HIP events
+    on the step's stream)."""
+    import torch
+
+    ra, kpr, q_r, k_r, v_r, n_chunks = setup_c5(device)
     for _ in range(30):
         _, r = ra.step(q_r, k_r, v_r, n_chunks - 1, k_per_row=kpr)
     torch.cuda.synchronize()
@@ -626,6 +633,98 @@ def profile_attention(launches: int, expect_out=None):
                        "mfma_sparse_listed": int(subs[ci].sum()) * waves * 16,
                        "mfma_dense_listed": int(len(rp) - 1) * int(subs.sum()) * waves * 16}, f, indent=1)
     print("profile-attention done: %d attention launches, one %d-byte copy" % (launches, COPY_BYTES), flush=True)
+
+
+def profile_c5(launches: int):
+    """Counter-collection mode for C5 at chunk 48: one step (it routes the
+    chunk), a settle phase, then ``launches`` attention launches on its lists
+    exactly as the step makes them (Q read and O written in raster order),
+    then one plain 1 GiB device copy (the calibration kernel for the byte
+    counters).
+    Prints a one-line summary of the lists; meant to run under rocprofv3
+    --pmc."""
+    import torch
+
+    ra, kpr, q_r, k_r, v_r, n_chunks = setup_c5("cuda:0")
+    _, r = ra.step(q_r, k_r, v_r, n_chunks - 1, k_per_row=kpr)
+    torch.cuda.synchronize()
+    nkb = n_chunks * ra.nbc
+    k_hist, v_hist = ra.k_store[:, : nkb * ra.block], ra.v_store[:, : nkb * ra.block]
+    # settle: the same launches for SETTLE_MS of GPU time first (the clock
+    # ramps after set-up), so the counted ones run at the steady clock
+    settle_ms, settle_n = 0.0, 0
+    while settle_ms < SETTLE_MS and settle_n < 2000:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            ra._attend(r, nkb, k_hist, v_hist, None, None, out_raster=True, q_raster=q_r)
+        e1.record()
+        torch.cuda.synchronize()
+        settle_ms += e0.elapsed_time(e1)
+        settle_n += 20
+    for _ in range(launches):
+        ra._attend(r, nkb, k_hist, v_hist, None, None, out_raster=True, q_raster=q_r)
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    rp = r["row_ptr"].cpu()
+    lens = (rp[1:] - rp[:-1]).float()
+    print("profile-c5 done: %d settle + %d attention launches on %d listed blocks (per row: mean %.1f, min %d, "
+          "max %d), one %d-byte copy" % (settle_n, launches, int(rp[-1]), float(lens.mean()), int(lens.min()),
+                                         int(lens.max()), COPY_BYTES), flush=True)
+
+
+def summarize_launch_counters(csvs, kernel: str, launches: int, workload: str, out_path: str):
+    """Per-launch counters of the last ``launches`` dispatches of ``kernel``
+    (a substring of its name) in rocprofv3 --pmc CSVs, with the byte
+    counters (FETCH_SIZE, WRITE_SIZE; KiB) scaled by what they read for the
+    1 GiB copy, and the derived rates: matrix cores busy, vector issue busy,
+    L2 hit rate, resident waves per SIMD.  Counters of the SQ block are
+    per-SIMD aggregates (the VALU, wave and wait ones in units of 4 cycles);
+    GRBM_GUI_ACTIVE is summed over the 8 XCDs."""
+    import csv
+
+    per = {}      # counter -> dispatch -> value (summed over the CSV's rows of that dispatch)
+    copy = {}
+    for path in csvs:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                name, cn = row["Kernel_Name"], row["Counter_Name"]
+                disp = int(row.get("Dispatch_Id") or row.get("Correlation_Id") or 0)
+                v = float(row["Counter_Value"])
+                if kernel in name:
+                    per.setdefault(cn, {}).setdefault(disp, 0.0)
+                    per[cn][disp] += v
+                elif "copy" in name.lower():
+                    copy.setdefault(cn, {}).setdefault(disp, 0.0)
+                    copy[cn][disp] += v
+    avg = {}
+    for cn, d in per.items():
+        last = sorted(d)[-launches:]
+        avg[cn] = sum(d[k] for k in last) / len(last)
+    out = {"kernel": kernel, "workload": workload, "attn_source_sha256_16": attn_source_hash(),
+           "launches": launches, "counters_per_launch": avg}
+    for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+        if cn in avg and cn in copy:
+            scale = COPY_BYTES / (max(copy[cn].values()) * 1024.0)
+            out[cn.lower() + "_bytes_per_launch"] = avg[cn] * 1024.0 * scale
+            out[cn.lower() + "_copy_scale"] = scale
+    cyc = avg.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+    simds = 1024
+    if cyc:
+        out["gpu_cycles"] = cyc
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            out["mfma_busy"] = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / cyc
+        if "SQ_ACTIVE_INST_VALU" in avg:
+            out["valu_issue_busy"] = 4.0 * avg["SQ_ACTIVE_INST_VALU"] / simds / cyc
+        if "SQ_WAVE_CYCLES" in avg:     # quad-cycles, like the VALU counter
+            out["waves_per_simd"] = 4.0 * avg["SQ_WAVE_CYCLES"] / simds / cyc
+    if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg:
+        out["l2_hit_rate"] = avg["TCC_HIT_sum"] / max(1.0, avg["TCC_HIT_sum"] + avg["TCC_MISS_sum"])
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def coloured_visit_order(row_ptr, col_idx, heads: int, nqb: int):
@@ -973,6 +1072,11 @@ def main():
                     help="experiment: the attention launch on the step's lists in ascending or co-scheduled "
                          "visit order (N launches, --visit-order-launches), or both timed in alternation (ab)")
     ap.add_argument("--visit-order-launches", type=int, default=5)
+    ap.add_argument("--profile-c5", type=int, default=0, metavar="N",
+                    help="counter mode: C5 at chunk 48, one step, N attention launches + a 1 GiB copy, no JSON line")
+    ap.add_argument("--summarize-launch-counters", nargs="+", metavar="ARG",
+                    help="KERNEL LAUNCHES WORKLOAD CSV... OUT_JSON: per-launch counters of the last LAUNCHES "
+                         "dispatches of KERNEL in rocprofv3 --pmc CSVs")
     ap.add_argument("--profile-step", type=int, default=0, metavar="N",
                     help="counter mode: N whole steps + a 1 GiB copy, no JSON line")
     ap.add_argument("--summarize-step-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV", "OUT_MD"),
@@ -983,6 +1087,10 @@ def main():
                     help="pipeline counters of the attention launches (matrix, vector, LDS, L2) from rocprofv3 "
                          "--pmc CSVs of --profile-attention; the last argument is the output JSON")
     args = ap.parse_args()
+    if args.summarize_launch_counters:
+        a = args.summarize_launch_counters
+        summarize_launch_counters(a[3:-1], a[0], int(a[1]), a[2], a[-1])
+        return
     if args.summarize_pipe:
         summarize_pipe(args.summarize_pipe[:-1], args.summarize_pipe[-1])
         return
@@ -1008,6 +1116,9 @@ def main():
         return
     if args.profile_attention:
         profile_attention(args.profile_attention, args.expect_out)
+        return
+    if args.profile_c5:
+        profile_c5(args.profile_c5)
         return
     if args.visit_order:
         visit_order_experiment(args.visit_order, args.visit_order_launches, args.visit_order == "ab")
