@@ -101,6 +101,59 @@ __device__ __forceinline__ void map_item(int total, int nqb, int& h, int& i) {
     i = item % nqb;
 }
 
+// Workgroup -> item for routed lists: the XCD runs of map_item, but inside
+// a run the query blocks of one head (in windows of at most 128) start
+// longest list first, ties to the lower index.  The workgroups that share
+// an XCD at any time then walk lists of similar length and reach the blocks
+// they have in common (notably a dense tail at the end of every list) at
+// similar times, while those blocks are still in that XCD's L2; the longest
+// lists also no longer start last.  The order is a permutation of the
+// window (strict order on (length, index)), found by every wave alone from
+// the window's row pointers: rank = number of items ahead of it.
+__device__ __forceinline__ int longest_first_item(const int32_t* row_ptr, int64_t col_len, int total, int nqb) {
+    constexpr int kWin = 128;
+    const int b = blockIdx.x;
+    const int per = total / 8;
+    if (b >= per * 8) return b;
+    const int run = (b % 8) * per, item0 = run + b / 8;
+    const int hs = item0 / nqb * nqb;
+    const int lo = run > hs ? run : hs;
+    const int hi = run + per < hs + nqb ? run + per : hs + nqb;
+    const int ws = lo + (item0 - lo) / kWin * kWin;
+    const int n = hi - ws < kWin ? hi - ws : kWin;
+    const int r = item0 - ws;
+    const int lane = threadIdx.x & 63;
+    // key: length (clamped to 2^24 - 1) above the inverted window index, so
+    // a larger key goes first and keys are distinct
+    uint32_t key[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const int t = lane + 64 * w;
+        uint32_t len = 0;
+        if (t < n) {
+            int e0 = row_ptr[ws + t], e1 = row_ptr[ws + t + 1];
+            e0 = e0 < 0 ? 0 : e0;
+            e1 = e1 > col_len ? (int)col_len : e1;
+            len = e1 > e0 ? (uint32_t)(e1 - e0) : 0u;
+            len = len < (1u << 24) ? len : (1u << 24) - 1u;
+        }
+        key[w] = (len << 7) | (uint32_t)(kWin - 1 - t);
+    }
+    int rank[2] = {0, 0};
+    for (int k = 0; k < n; ++k) {
+        const uint32_t kk = k < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)key[0], k)
+                                   : (uint32_t)__builtin_amdgcn_readlane((int)key[1], k - 64);
+        rank[0] += kk > key[0];
+        rank[1] += kk > key[1];
+    }
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const uint64_t m = __ballot(lane + 64 * w < n && rank[w] == r);
+        if (m) return __builtin_amdgcn_readfirstlane(ws + 64 * w + __builtin_ctzll(m));
+    }
+    return item0;  // unreachable: the ranks are a permutation of [0, n)
+}
+
 __device__ __forceinline__ bf16x8_t lds_bf16x8(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
 }
@@ -284,18 +337,39 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
+// Compile-time loop that stops at the first f(integral_constant<int, I>)
+// returning false; true when every call did.
+template <int B, int E, class F>
+__device__ __forceinline__ bool static_all(F&& f) {
+    if constexpr (B < E) {
+        if (!f(std::integral_constant<int, B>())) return false;
+        return static_all<B + 1, E>(f);
+    }
+    return true;
+}
+
+constexpr int gcd_c(int x, int y) { return y == 0 ? x : gcd_c(y, x % y); }
+constexpr int lcm3(int x, int y, int z) {
+    const int xy = x / gcd_c(x, y) * y;
+    return xy / gcd_c(xy, z) * z;
+}
+
 // Scheduling fence: the compiler keeps the instruction order across it.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Workgroup of BLK/32 waves, one (head, query block); wave w owns query rows
 // 32w .. 32w+31 and every key.  Keys stream in sub-tiles of kSubKeys: slot t
 // is sub-tile t % SUBS of the t / SUBS-th listed block.  K and V have rings
-// of four 32-key sub-tiles each (2 x 32 KB at d = 128, so two workgroups
-// share a CU and overlap each other's softmax with their matrix work).
+// of RK and RV 32-key sub-tiles, sized so that every SIMD holds at least
+// two waves, whose softmax and matrix work then overlap each other: the
+// 128-row workgroup (four waves) keeps four of each (2 x 32 KB at d = 128,
+// two workgroups per CU); the 64-row one (two waves) keeps three K and two
+// V sub-tiles at d = 128 (40 KB, four workgroups per CU: with four of each,
+// only two would fit, one wave per SIMD), four of each at d = 64 (32 KB).
 //
 // Iteration t, after one barrier:
-//   copies      K of slot t+4 and V of slot t+3 are issued into the buffers
-//               freed by iteration t-1 (three sub-tiles of each in flight);
+//   copies      V of slot t+RV-1, then K of slot t+RK, are issued into the
+//               buffers freed by iteration t-1;
 //   phase A     S(t+1) = K(t+1) Q^T on the matrix cores while the vector
 //               units exponentiate slot t's scores into bf16 P(t);
 //   phase B     O^T += V(t)^T P(t)^T on the matrix cores while the vector
@@ -311,11 +385,18 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
     constexpr int SUBE = kSubKeys * D;     // elements of a K or V sub-tile
     constexpr int SUBS = BLK / kSubKeys;   // sub-tiles per block
     constexpr int NI = kSubKeys * D * 2 / 1024 / NW;  // copy instructions per wave per sub-tile
-    constexpr int LAG = 3 / SUBS;          // blocks between the K-copy cursor and slot t+1
+    constexpr bool kSmallRing = BLK == 64 && D == 128;
+    constexpr int RK = kSmallRing ? 3 : 4, RV = kSmallRing ? 2 : 4;  // K and V ring depths
+    constexpr int LAG = (RK - 1) / SUBS;   // blocks between the K-copy cursor and slot t+1
+    constexpr int U = lcm3(RK, RV, SUBS);  // unroll period: every ring index a constant
     static_assert(kSubKeys * D * 2 % (1024 * NW) == 0, "sub-tile copy must split evenly over the waves");
-    static_assert(4 % SUBS == 0, "the four-slot unroll must hold whole blocks");
-    __shared__ __attribute__((aligned(1024))) uint16_t kb0[SUBE], kb1[SUBE], kb2[SUBE], kb3[SUBE];
-    __shared__ __attribute__((aligned(1024))) uint16_t vb0[SUBE], vb1[SUBE], vb2[SUBE], vb3[SUBE];
+    static_assert(LAG <= 1, "the cursor history is two blocks deep");
+    static_assert(RK >= RV && RK - RV < SUBS, "the V copy of a new block must find it at the K-copy cursor");
+    // one LDS object per buffer: the compiler then tracks each buffer's
+    // copies on their own (a read of one waits only for that buffer's)
+    __shared__ __attribute__((aligned(1024))) uint16_t kb0[SUBE], kb1[SUBE], kb2[SUBE], kb3[RK > 3 ? SUBE : 1];
+    __shared__ __attribute__((aligned(1024))) uint16_t vb0[SUBE], vb1[SUBE], vb2[RV > 2 ? SUBE : 1],
+        vb3[RV > 3 ? SUBE : 1];
     uint16_t* const KB[4] = {kb0, kb1, kb2, kb3};
     uint16_t* const VB[4] = {vb0, vb1, vb2, vb3};
 
@@ -323,7 +404,13 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, l32 = lane & 31, g16 = lane & 15;
     int h, i;
-    map_item(a.heads * a.nqb, a.nqb, h, i);
+    if (DENSE) {
+        map_item(a.heads * a.nqb, a.nqb, h, i);
+    } else {
+        const int item = longest_first_item(a.row_ptr, a.col_len, a.heads * a.nqb, a.nqb);
+        h = item / a.nqb;
+        i = item % a.nqb;
+    }
     int vq = a.q_len ? a.q_len[i] : BLK;
     vq = vq < 0 ? 0 : (vq > BLK ? BLK : vq);
     const int q0 = wave * 32;
@@ -413,18 +500,18 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
                           VB[buf], wave);
     };
 
-    // prologue: K of slots 0..3, V of slots 0..2
+    // prologue: K of slots 0..RK-1, V of slots 0..RV-2
     list.prefetch1();
     list.prefetch2();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < RK; ++s) {
         if (s > 0 && s % SUBS == 0) {
             k_advance();
             list.prefetch1();
             list.prefetch2();
         }
         issue_k(s, s % SUBS);
-        if (s < 3) {
+        if (s < RV - 1) {
             if (s % SUBS == 0) {
                 jv = h0j;
                 vvk = h0v;
@@ -553,7 +640,7 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
     };
 
     // slot 0: wait for its K copy, scores, first reference
-    wait_vmcnt<6 * NI>();
+    wait_vmcnt<(RK + RV - 2) * NI>();
     lds_barrier();
     wait_lgkmcnt0();
     int cvk = LAG == 0 ? h0v : h1v;  // valid keys of the block of slot t+1
@@ -564,10 +651,11 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         logits_check();
     }
 
-    // Iteration t (K = t % 4): the body reads K slot t+1 from buffer
-    // (K+1) % 4 and V slot t from buffer K, and refills buffer K with K slot
-    // t+4 and buffer (K+3) % 4 with V slot t+3.  Returns false when slot t+1
-    // does not exist; slot t is then finished by the tail.
+    // Iteration t (K = t % U): the body reads K slot t+1 from buffer
+    // (K+1) % RK and V slot t from buffer K % RV; V slot t+RV-1 refills V
+    // buffer (K+RV-1) % RV and K slot t+RK refills K buffer K % RK.  Returns
+    // false when slot t+1 does not exist; slot t is then finished by the
+    // tail.
     // One iteration's math, in fenced segments so that each matrix
     // instruction is issued beside vector work that does not depend on it:
     //   phase A  KK segments, each: K fragment read three ahead, two V reads,
@@ -671,56 +759,50 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         m3l = m3;
         logits_check();
     };
-    auto step = [&](auto K_) __attribute__((always_inline)) -> bool {
-        constexpr int K = decltype(K_)::value;
-        constexpr int SUB_K = (K + 4) % SUBS, SUB_V = (K + 3) % SUBS, SUB_N = (K + 1) % SUBS;
-        wait_vmcnt<4 * NI>();
-        lds_barrier();
-        wait_lgkmcnt0();  // the list prefetches of the previous iteration
-        if (SUB_K == 0) k_advance();
-        issue_k(K, SUB_K);
-        if (SUB_V == 0) {
-            jv = h0j;
-            vvk = h0v;
-        }
-        issue_v((K + 3) % 4, SUB_V);
-        if (SUB_N == 0) {
-            cvk = LAG == 0 ? h0v : h1v;
-            if (LAG == 0 ? h0end : h1end) return false;
-        }
-        if (active) body(KB[(K + 1) % 4], VB[K], cvk - SUB_N * kSubKeys);
-        // the next block's list entry, two loads on two iterations
-        if (SUB_K == 0) list.prefetch1();
-        if (SUB_V == 0) list.prefetch2();
-        return true;
-    };
+    // Copies still in flight when iteration t starts: those issued after
+    // the later of K slot t+1 (second copy of iteration t+1-RK) and V slot
+    // t (first copy of iteration t+1-RV); the prologue's order keeps the
+    // first iterations within the same count.
+    constexpr int kLastK = 2 * (1 - RK) + 1, kLastV = 2 * (1 - RV);
+    constexpr int kInFlight = -1 - (kLastK > kLastV ? kLastK : kLastV);
     auto tail = [&](auto K_) __attribute__((always_inline)) {
         constexpr int K = decltype(K_)::value;
         if (active) {
             s16x4_t vr[2][DT][2];
-            load_v(VB[K], vr);
+            load_v(VB[K % RV], vr);
             bf16x8_t pf[2];
             exp_p(pf);
             pv(vr, pf);
         }
     };
-    for (;;) {
-        if (!step(std::integral_constant<int, 0>())) {
-            tail(std::integral_constant<int, 0>());
-            break;
+    auto step = [&](auto K_) __attribute__((always_inline)) -> bool {
+        constexpr int K = decltype(K_)::value;
+        constexpr int SUB_K = (K + RK) % SUBS, SUB_V = (K + RV - 1) % SUBS, SUB_N = (K + 1) % SUBS;
+        wait_vmcnt<kInFlight * NI>();
+        lds_barrier();
+        wait_lgkmcnt0();  // the list prefetches of the previous iteration
+        if (SUB_V == 0) {  // V's new block is the K-copy cursor's current one
+            jv = h0j;
+            vvk = h0v;
         }
-        if (!step(std::integral_constant<int, 1>())) {
-            tail(std::integral_constant<int, 1>());
-            break;
+        issue_v((K + RV - 1) % RV, SUB_V);
+        if (SUB_K == 0) k_advance();
+        issue_k(K % RK, SUB_K);
+        if (SUB_N == 0) {
+            cvk = LAG == 0 ? h0v : h1v;
+            if (LAG == 0 ? h0end : h1end) {
+                tail(K_);
+                return false;
+            }
         }
-        if (!step(std::integral_constant<int, 2>())) {
-            tail(std::integral_constant<int, 2>());
-            break;
-        }
-        if (!step(std::integral_constant<int, 3>())) {
-            tail(std::integral_constant<int, 3>());
-            break;
-        }
+        if (active) body(KB[(K + 1) % RK], VB[K % RV], cvk - SUB_N * kSubKeys);
+        // the next block's list entry, two loads on the two iterations after
+        // the K-copy cursor moved
+        if (SUB_K == 0) list.prefetch1();
+        if ((K + RK - 1) % SUBS == 0) list.prefetch2();
+        return true;
+    };
+    while (static_all<0, U>(step)) {
     }
     wait_vmcnt<0>();  // the copies past the end must land before the LDS is released
 

@@ -246,6 +246,47 @@ def test_edge_cases_small(block, d):
         assert torch.all(o[0, block: 2 * block] == 0) and torch.all(torch.isneginf(lse[0, block:2 * block]))
 
 
+@pytest.mark.parametrize("block", [64, 128])
+def test_ragged_lengths_every_item_once(block):
+    """Lists of widely different lengths (0 to nkb) over more than 128 query
+    blocks per head and 3 heads (450 items: the per-XCD runs of 56 items cut
+    heads apart, two items fall outside the runs, windows of 128 split a
+    head): the workgroups take the items longest list first, and every
+    (head, query block) must still be computed exactly once."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    rng = np.random.default_rng(7 + block)
+    heads, nqb, nkb, d = 3, 150, 10, 128
+    q = torch.from_numpy(rng.standard_normal((heads, nqb * block, d)).astype(np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy(rng.standard_normal((heads, nkb * block, d)).astype(np.float32)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((heads, nkb * block, d)).astype(np.float32)).to(torch.bfloat16)
+    q_len = np.full(nqb, block, dtype=np.int32)
+    q_len[-1] = 5
+    k_len = np.full(nkb, block, dtype=np.int32)
+    k_len[3] = 17
+    raw = [sorted(rng.choice(nkb, size=int(rng.integers(0, nkb + 1)), replace=False).tolist())
+           for _ in range(heads * nqb)]
+    row_ptr = np.cumsum([0] + [len(x) for x in raw]).astype(np.int32)
+    col = np.concatenate([np.asarray(x, dtype=np.int32) for x in raw if x])
+    o = torch.full((heads, nqb * block, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    o, lse = bsa.block_sparse_attn(q.to(dev), k.to(dev), v.to(dev), torch.from_numpy(row_ptr).to(dev),
+                                   torch.from_numpy(col).to(dev), block=block, scale=0.09,
+                                   q_block_len=torch.from_numpy(q_len).to(dev),
+                                   kv_block_len=torch.from_numpy(k_len).to(dev), out=o, lse=True)
+    torch.cuda.synchronize()
+    vmask = valid_rows(q_len, block)
+    for h in range(heads):
+        lists = raw[h * nqb:(h + 1) * nqb]
+        o_ref, l_ref = oatt.block_sparse_head(f64(q[h]), f64(k[h]), f64(v[h]), q_len, k_len, block, lists, 0.09)
+        og = f64(o[h])
+        mx, mean = err_summary(og, o_ref, vmask)
+        assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (h, mx, mean)
+        assert np.all(og[~vmask] == 0.0)
+        lg = lse[h].cpu().numpy().astype(np.float64)
+        both_inf = np.isneginf(lg) & np.isneginf(l_ref)
+        assert np.all(both_inf | (np.abs(lg - l_ref) <= LSE_BF16)), h
+
+
 def test_wrapper_rejects_short_or_mistyped_arrays():
     """The binding checks what the C ABI cannot see (device array lengths,
     operand dtypes, nkb against the KV rows) and raises ValueError before
