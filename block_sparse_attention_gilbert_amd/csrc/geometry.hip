@@ -4,13 +4,13 @@
 // inside a historical slab.
 //
 // [Velox: Spatial Memory Makes World Models Efficient -- Methodology, Step 1:
-//  a historical block is kept as frustum slabs (a token rectangle in its
-//  source camera plus a depth interval); Step 3: query and historical slabs
-//  are approximated by camera-facing oriented boxes, the score is the IoU of
-//  the query box with the best-matching historical box, computed on a
-//  deterministic grid after a separating-axis test, and a coverage score
-//  counts the query tokens that fall inside a valid historical slab both
-//  spatially and in depth]
+//  the geometry of a historical block is a set of frustum slabs, each a
+//  rectangle of tokens in the camera that saw it and a range of depths;
+//  Step 3: every slab becomes an oriented box facing its camera; the score
+//  of a query block is the largest IoU of its box with a historical box,
+//  measured on a fixed grid once a separating-axis test has not ruled the
+//  pair out; coverage is the share of its tokens that lie in some valid
+//  historical slab, inside the rectangle and the depth range]
 //
 // Camera record (16 float64): fx, fy, cx, cy (token units), R row-major
 // (world-from-camera; its columns are the camera's right, down and forward

@@ -2,9 +2,9 @@
 // raster <-> Gilbert permutation of token tensors.
 //
 // [Velox: Spatial Memory Makes World Models Efficient -- Key Contributions 3
-//  ("global-aligned Gilbert KV storage"); Methodology, Step 6 (the order keeps
-//  neighbouring image regions contiguous, so local neighbourhoods and
-//  block-contiguous KV storage share one coordinate frame)]
+//  (KV storage in a Gilbert order aligned across chunks); Methodology, Step 6
+//  (nearby image regions stay adjacent along the order, so a block of
+//  consecutive KV rows is also a spatial neighbourhood)]
 // [Light Interaction -- abstract ("3D block sparse attention")]
 //
 // The pages name the curve but do not define it.  The definition used here:
@@ -34,6 +34,7 @@
 // steps into the child that holds its position.
 #include <hip/hip_runtime.h>
 
+#include "exact_sum.h"
 #include "gilbert_curve.h"
 #include "kernels.h"
 
@@ -88,21 +89,22 @@ gilbert_perm_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, cons
 // NULL: the block means only).
 // One workgroup per (block, head): thread t copies 16-byte chunk t % chunks
 // of the block's rows t / chunks, + groups, ... (raster token perm[i] to
-// Gilbert row i; padding rows written as zeros) and sums what it copied in
-// float64.  The row groups of a wave are combined with shuffles, the four
-// waves through LDS in wave order, and the mean over the block's valid rows
-// goes to pool.  Sums of at most 128 bf16 values are exact in float64
-// unless their magnitudes span more than 2^37, so the mean equals the one
-// pooled from the permuted tensor by any summation order.
-// [Velox -- Methodology, Step 4: mean query and mean key vectors per block;
-//  Step 6: neighbouring regions contiguous in the block-padded layout]
+// Gilbert row i; padding rows written as zeros) and sums what it copied,
+// exactly (exact_sum.h).  The row groups of a wave are combined with
+// shuffles, the four waves through LDS, and the mean over the block's valid
+// rows (the exact sum rounded once, divided once) goes to pool: the same
+// value whatever the summation order, for a column whose nonzero
+// magnitudes span less than 2^39 (bf16) or 2^74 (float32).
+// [Velox -- Methodology, Step 4: the router works on per-block averages of
+//  the queries and keys; Step 6: nearby regions adjacent in the padded block
+//  layout]
 template <bool BF16, bool POOL>
 __device__ __forceinline__ void perm_pool_block(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                 const int32_t* __restrict__ perm, int L, int d, int block, int b,
                                                 int h, int64_t raster_token_stride_c, int64_t gilbert_head_stride_c,
                                                 double* __restrict__ pool, int64_t pool_head_stride) {
     constexpr int CE = BF16 ? 8 : 4;  // elements per 16-byte chunk
-    __shared__ double part[4][128];
+    __shared__ double part_hi[4][128], part_lo[4][128];
     const int t = threadIdx.x, w = t >> 6;
     const int chunks = d / CE, groups = 256 / chunks;
     const int ch = t % chunks, g = t / chunks;
@@ -110,9 +112,7 @@ __device__ __forceinline__ void perm_pool_block(const uint4* __restrict__ src, u
     const int valid = (int)(L - i0 < block ? L - i0 : block);
     const int64_t hc = (int64_t)h * chunks + ch;
     uint4* out = dst ? dst + h * gilbert_head_stride_c + i0 * chunks + ch : nullptr;
-    double acc[CE];
-#pragma unroll
-    for (int e = 0; e < CE; ++e) acc[e] = 0.0;
+    Acc<BF16> acc[CE];
 #pragma unroll 4
     for (int k = g; k < block; k += groups) {
         uint4 u = make_uint4(0u, 0u, 0u, 0u);
@@ -123,25 +123,30 @@ __device__ __forceinline__ void perm_pool_block(const uint4* __restrict__ src, u
         if (BF16) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc[2 * e] += (double)__uint_as_float(wd[e] << 16);
-                acc[2 * e + 1] += (double)__uint_as_float(wd[e] & 0xFFFF0000u);
+                acc[2 * e].add((double)__uint_as_float(wd[e] << 16));
+                acc[2 * e + 1].add((double)__uint_as_float(wd[e] & 0xFFFF0000u));
             }
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(wd[e]);
+            for (int e = 0; e < 4; ++e) acc[e].add((double)__uint_as_float(wd[e]));
         }
     }
     if (!POOL) return;
     for (int off = chunks; off < 64; off <<= 1)
 #pragma unroll
-        for (int e = 0; e < CE; ++e) acc[e] += __shfl_xor(acc[e], off);
+        for (int e = 0; e < CE; ++e) acc[e].add(acc[e].shfl_xor(off));
     if ((t & 63) < chunks)
 #pragma unroll
-        for (int e = 0; e < CE; ++e) part[w][ch * CE + e] = acc[e];
+        for (int e = 0; e < CE; ++e) {
+            part_hi[w][ch * CE + e] = acc[e].hi();
+            part_lo[w][ch * CE + e] = acc[e].lo();
+        }
     __syncthreads();
     if (t < d) {
-        const double sum = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
-        pool[h * pool_head_stride + (int64_t)b * d + t] = sum / (double)valid;
+        Acc<BF16> sum = Acc<BF16>::make(part_hi[0][t], part_lo[0][t]);
+#pragma unroll
+        for (int u = 1; u < 4; ++u) sum.add(Acc<BF16>::make(part_hi[u][t], part_lo[u][t]));
+        pool[h * pool_head_stride + (int64_t)b * d + t] = sum.hi() / (double)valid;
     }
 }
 
@@ -252,8 +257,8 @@ tile_perm_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, const i
 // cell in an LDS bitmap over the previous and the current chunk's blocks.
 // The bitmap is then written out in ascending block order.
 // [Velox: Spatial Memory Makes World Models Efficient -- Methodology,
-//  Step 5: routes are unioned with a 26-neighbour local window in a
-//  global-aligned Gilbert block ordering]
+//  Step 5: every route also takes the block's 26 neighbours in the Gilbert
+//  block order shared by all chunks]
 constexpr int kWindowWords = 2 * kMaxWindowChunkBlocks / 32;  // bitmap words: 2 chunks
 
 static_assert(kWindowWords == 64, "one wave compacts the window bitmap");

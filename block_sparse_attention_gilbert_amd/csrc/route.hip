@@ -2,16 +2,17 @@
 // geometric bias, and top-K selection into ascending CSR lists.
 //
 // [Velox: Spatial Memory Makes World Models Efficient -- Methodology, Step 4:
-//  a per-layer importance distribution over the visible KV blocks from mean
-//  query and mean key vectors; vetted overlap (above tau) is rescaled to
-//  g_hat and multiplies the distribution by (1 + lambda g_hat), then
-//  renormalised (at most a 1 + lambda boost); Key Contributions 2: uncovered
-//  regions keep the model-derived route; Methodology, Step 5: the
-//  top-scoring blocks up to a budget]
+//  each layer scores the KV blocks a query block can see with the block
+//  averages of its queries and keys; overlaps above tau, rescaled to g_hat,
+//  scale that distribution by (1 + lambda g_hat) before it is normalised
+//  again (a boost of at most 1 + lambda); Key Contributions 2: where the
+//  geometry covers nothing the model's own scores decide; Methodology,
+//  Step 5: each row keeps its highest-scoring blocks, up to a budget]
 //
-// Arithmetic is float64 throughout.  A block mean of <= 128 bf16 values is
-// an exact float64 sum divided once, so it does not depend on summation
-// order.  The fused distribution softmax(s) * (1 + lambda g_hat) / Z orders
+// Arithmetic is float64 throughout.  A block mean is the exact sum of its
+// valid rows (for a column whose nonzero magnitudes span less than 2^39 in
+// bf16, or 2^74 in float32: exact_sum.h), rounded once and divided once, so
+// it does not depend on summation order.  The fused distribution softmax(s) * (1 + lambda g_hat) / Z orders
 // a row exactly as kappa = s + log1p(lambda g_hat) does (Z is a positive
 // per-row constant, log is increasing), so kappa is what gets ranked; a row
 // whose overlap is all zero has g_hat = 0 everywhere and so keeps kappa = s,
@@ -21,6 +22,7 @@
 
 #include <mutex>
 
+#include "exact_sum.h"
 #include "kernels.h"
 
 // Fixed device scratch of bsa_route_topk_static (callers that cannot
@@ -42,11 +44,10 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t bits16) {
 // Mean of the valid rows of each block: one workgroup of 4 waves per block,
 // grid = (blocks, heads).  Wave w sums rows w, w + 4, ... of its quarter of
 // the block; lane l owns one 16-byte chunk (l % chunks) of rows l / chunks,
-// + groups, ...  The partial sums (of the row groups, then of the four
-// waves) are combined with butterfly shuffles and through LDS: sums of at
-// most 128 bf16 or fp32 values are exact in float64, so the combination
-// order does not matter.  Four waves per block keep enough loads in flight
-// when only a chunk's worth of blocks is pooled.
+// + groups, ...  Sums are exact (exact_sum.h), combined over the row groups
+// with butterfly shuffles and over the four waves through LDS; the order
+// does not change the result.  Four waves per block keep
+// enough loads in flight when only a chunk's worth of blocks is pooled.
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads)
 pool_kernel(const void* __restrict__ x, int64_t head_stride, int d, int block,
@@ -54,16 +55,14 @@ pool_kernel(const void* __restrict__ x, int64_t head_stride, int d, int block,
             int64_t out_head_blocks) {
     constexpr int CE = BF16 ? 8 : 4;  // elements per 16-byte chunk
     constexpr int NW = kThreads / 64;
-    __shared__ double part[NW][128];
+    __shared__ double part_hi[NW][128], part_lo[NW][128];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int b = b_begin + blockIdx.x, h = blockIdx.y;
     int valid = lens ? lens[b] : block;
     valid = valid < 0 ? 0 : (valid > block ? block : valid);
     const int chunks = d / CE, groups = 64 / chunks;
     const int ch = lane % chunks, g = lane / chunks;
-    double acc[CE];
-#pragma unroll
-    for (int e = 0; e < CE; ++e) acc[e] = 0.0;
+    Acc<BF16> acc[CE];
     const int64_t base = h * head_stride + (int64_t)b * block * d + ch * CE;
 #pragma unroll 8
     for (int row = w * groups + g; row < valid; row += NW * groups) {
@@ -72,30 +71,33 @@ pool_kernel(const void* __restrict__ x, int64_t head_stride, int d, int block,
             const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc[2 * e] += bf16_to_f64(wd[e] & 0xFFFFu);
-                acc[2 * e + 1] += bf16_to_f64(wd[e] >> 16);
+                acc[2 * e].add(bf16_to_f64(wd[e] & 0xFFFFu));
+                acc[2 * e + 1].add(bf16_to_f64(wd[e] >> 16));
             }
         } else {
             const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + base + (int64_t)row * d);
-            acc[0] += (double)f.x;
-            acc[1] += (double)f.y;
-            acc[2] += (double)f.z;
-            acc[3] += (double)f.w;
+            acc[0].add((double)f.x);
+            acc[1].add((double)f.y);
+            acc[2].add((double)f.z);
+            acc[3].add((double)f.w);
         }
     }
     for (int off = chunks; off < 64; off <<= 1)
 #pragma unroll
-        for (int e = 0; e < CE; ++e) acc[e] += __shfl_xor(acc[e], off);
+        for (int e = 0; e < CE; ++e) acc[e].add(acc[e].shfl_xor(off));
     if (g == 0)
 #pragma unroll
-        for (int e = 0; e < CE; ++e) part[w][ch * CE + e] = acc[e];
+        for (int e = 0; e < CE; ++e) {
+            part_hi[w][ch * CE + e] = acc[e].hi();
+            part_lo[w][ch * CE + e] = acc[e].lo();
+        }
     __syncthreads();
     const int t = threadIdx.x;
     if (t < d) {
-        double sum = 0.0;
+        Acc<BF16> sum = Acc<BF16>::make(part_hi[0][t], part_lo[0][t]);
 #pragma unroll
-        for (int u = 0; u < NW; ++u) sum += part[u][t];
-        out[(h * out_head_blocks + b) * d + t] = valid > 0 ? sum / (double)valid : 0.0;
+        for (int u = 1; u < NW; ++u) sum.add(Acc<BF16>::make(part_hi[u][t], part_lo[u][t]));
+        out[(h * out_head_blocks + b) * d + t] = valid > 0 ? sum.hi() / (double)valid : 0.0;
     }
 }
 
@@ -770,12 +772,12 @@ topk_merge_kernel(const unsigned long long* __restrict__ seg_key, const int32_t*
 // Route materialisation.
 // [Velox: Spatial Memory Makes World Models Efficient -- Methodology,
 //  Step 3: a coverage score per query block; Step 4: the geometric fusion
-//  applies to well-covered blocks; Step 5: a well-covered query block first
-//  reserves the previous chunk's KV blocks, then takes the top-scoring
-//  remaining blocks up to K_cov; a poorly covered one takes the smallest
-//  prefix of the model distribution whose cumulative mass reaches a
-//  threshold, at most K_unc blocks; both are unioned, outside the budget,
-//  with the local window and with optional reference-frame blocks]
+//  applies to well-covered blocks; Step 5: a well-covered query block takes
+//  all of the previous chunk's KV blocks, then fills its budget K_cov with
+//  the best of the others; a poorly covered one ranks by the unbiased model
+//  scores and stops at the shortest prefix whose probability mass passes a
+//  threshold, never more than K_unc blocks; either route then adds, outside
+//  its budget, the local window and optional reference-frame blocks]
 //
 // One wave per (head, query block) row builds the row's membership bitmap
 // in LDS (one bit per KV block) and writes it out with its population

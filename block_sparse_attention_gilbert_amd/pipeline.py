@@ -1,9 +1,9 @@
 """One attention call of a chunked model over its growing KV history, as a
 chain of the library's entry points with every buffer allocated up front.
 
-[Velox: Spatial Memory Makes World Models Efficient -- Methodology (the model
-generates one chunk at a time and keeps every previous chunk in a KV cache;
-only the set of historical KV blocks each region may look at changes),
+[Velox: Spatial Memory Makes World Models Efficient -- Methodology (chunks
+are produced in sequence and the KV cache holds all earlier ones; what
+changes is only the set of earlier KV blocks a region may attend to),
 Steps 4-6; Key Contributions 3]
 
 Per call (``RoutedAttention.step``):

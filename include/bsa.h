@@ -116,8 +116,8 @@ int bsa_gilbert_perm(const void* src, void* dst, const int32_t* perm, int L, int
  * bsa_gilbert_perm_pool -- the forward permutation of bsa_gilbert_perm
  * (inverse = 0) and, in the same pass, the mean of every block's valid
  * rows, for the router's pooled queries or pooled-key cache.
- * [Velox -- Methodology, Step 4 (mean query and mean key vectors per
- *  block); Key Contributions 3; Methodology, Step 6]
+ * [Velox -- Methodology, Step 4 (per-block averages of queries and keys);
+ *  Key Contributions 3; Methodology, Step 6]
  *
  * src, dst, perm, L, heads, d, block, raster_token_stride,
  * gilbert_head_stride, dtype   as bsa_gilbert_perm with inverse = 0;
@@ -141,8 +141,8 @@ int bsa_gilbert_perm_pool(const void* src, void* dst, const int32_t* perm, int L
 /*
  * bsa_gilbert_perm_pool_batch -- bsa_gilbert_perm_pool over several tensors
  * of one chunk that share its curve (say Q, K and V) in a single launch.
- * [Velox -- Methodology, Step 4 (mean query and mean key vectors per
- *  block); Key Contributions 3; Methodology, Step 6]
+ * [Velox -- Methodology, Step 4 (per-block averages of queries and keys);
+ *  Key Contributions 3; Methodology, Step 6]
  *
  * jobs           host array of n_jobs descriptions (1 <= n_jobs <=
  *                BSA_MAX_PERM_JOBS), read during the call only.  Job z
@@ -176,11 +176,12 @@ int bsa_gilbert_perm_pool_batch(const bsa_perm_job* jobs, int n_jobs, const int3
 
 /*
  * Router arguments.  Set struct_size = sizeof(bsa_route_args).
- * [Velox -- Methodology, Step 4 (importance from mean query and mean key
- *  vectors; overlap above tau rescaled and applied as (1 + lambda * g_hat),
- *  then renormalised; at most a 1 + lambda boost); Key Contributions 2
- *  (uncovered regions keep the model-derived route); Methodology, Step 5
- *  (top-scoring blocks up to a budget)]
+ * [Velox -- Methodology, Step 4 (block scores from the per-block averages
+ *  of queries and keys; overlaps above tau, rescaled, scale them by
+ *  (1 + lambda * g_hat) before normalising again, a boost of at most
+ *  1 + lambda); Key Contributions 2 (without geometric cover the model's own
+ *  scores decide); Methodology, Step 5 (the highest-scoring blocks, up to a
+ *  budget)]
  *
  * Inputs (device unless noted):
  *  q, k           [heads][rows][d] in dtype, rows contiguous; q rows =
@@ -317,9 +318,9 @@ int bsa_route_topk_static(const bsa_route_args* args, hipStream_t stream);
 /*
  * bsa_gilbert_block_window -- the local window of every query block of one
  * chunk, in block indices of the Gilbert-ordered history.
- * [Velox -- Methodology, Step 5 (routes are unioned with a 26-neighbour
- *  local window in the global-aligned Gilbert block ordering); Key
- *  Contributions 3 (global-aligned Gilbert KV storage)]
+ * [Velox -- Methodology, Step 5 (every route also takes the block's 26
+ *  neighbours in the Gilbert block order); Key Contributions 3 (KV storage
+ *  in one Gilbert order aligned across chunks)]
  *
  * perm, inv      device int32[T*H*W]: a chunk grid's curve and its inverse
  *                (bsa_gilbert_index).  Chunk c of the history occupies
@@ -489,10 +490,11 @@ int bsa_route_materialize(const bsa_route_args* args, const bsa_materialize_args
  * Frustum-slab geometry.
  * [Velox -- Methodology, Step 1 (a historical block is kept as frustum
  *  slabs: a token rectangle in its source camera plus a depth interval);
- *  Step 3 (camera-facing oriented boxes, IoU of the query box with the
- *  best-matching historical box on a deterministic grid after a
- *  separating-axis test; coverage = share of a query block's tokens inside
- *  a valid historical slab both spatially and in depth)]
+ *  Step 3 (each slab as an oriented box facing its camera; the score is
+ *  the largest IoU of the query's box with a historical box, measured on a
+ *  fixed grid once a separating-axis test has not ruled the pair out;
+ *  coverage = the share of a query block's tokens that lie in some valid
+ *  historical slab, inside its rectangle and its depth range)]
  *
  * cams       device float64[n_cams][16]: fx, fy, cx, cy (token units), R
  *            row-major (world-from-camera; columns = the camera's right,

@@ -7,16 +7,16 @@ module; the library never does.
 
 Pages [Velox: Spatial Memory Makes World Models Efficient]:
 
-* Methodology, Step 1: each historical block is stored as one or more
-  frustum slabs -- a token rectangle in its source camera plus a depth
-  interval -- that passed the validity gates;
-* Methodology, Step 3: each query slab and historical slab is approximated
-  by a camera-facing oriented bounding box; the geometric score of a query
-  block against a historical block is the intersection-over-union between
-  the query box and the best-matching historical box, computed on a
-  deterministic grid over the boxes after a separating-axis test; a
-  separate coverage score is the fraction of a query block's tokens that
-  fall inside a valid historical slab both spatially and in depth.
+* Methodology, Step 1: the geometry of a historical block is a set of
+  frustum slabs (each a rectangle of tokens in the camera that saw it, with
+  a range of depths) that the validity gates let through;
+* Methodology, Step 3: every slab, query or historical, is replaced by an
+  oriented box facing its camera; a query block scores a historical block
+  by the largest intersection-over-union of its box with one of that
+  block's boxes, measured on a fixed grid, a separating-axis test first
+  discarding pairs that cannot meet; coverage, a second score, is the share
+  of the query block's tokens lying in some valid historical slab (inside
+  its rectangle and within its depth range).
 
 Readings where the pages are silent:
 

@@ -7,17 +7,17 @@ module; the library never does.
 
 Pages [Velox: Spatial Memory Makes World Models Efficient]:
 
-* Methodology, Step 3: a coverage score per query block, the fraction of its
-  tokens that fall inside a valid historical slab;
+* Methodology, Step 3: each query block has a coverage score, the share of
+  its tokens that lie in some valid historical slab;
 * Methodology, Step 4: the soft geometric fusion applies to well-covered
   query blocks;
-* Methodology, Step 5: well-covered query blocks reserve the previous
-  chunk's KV blocks first, then take the top-scoring remaining blocks up to
-  K_cov; poorly covered ones keep the model distribution and take the
-  smallest prefix whose cumulative mass reaches a threshold, capped at
-  K_unc; both routes are unioned with a 26-neighbour local window in the
-  global-aligned Gilbert block ordering and with optional reference-frame
-  blocks, outside the budget;
+* Methodology, Step 5: a well-covered query block first takes every KV
+  block of the previous chunk, then fills its budget K_cov with the best of
+  the others; a poorly covered one ranks by the unbiased model scores and
+  stops at the shortest prefix whose probability mass passes a threshold,
+  never more than K_unc blocks; on top of either budget, each route adds the
+  block's 26 neighbours in the Gilbert block order and, optionally, blocks
+  of reference frames;
 * the calibrated constants eta_cov = 0.9, K_cov = 80, K_unc = 150 close the
   Methodology section.
 

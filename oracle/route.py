@@ -3,13 +3,14 @@ with unbiased fallback, and top-K route materialisation.
 
 Pages [Velox: Spatial Memory Makes World Models Efficient]:
 
-* Methodology, Step 4: each layer's importance distribution over the visible
-  KV blocks comes from mean query and mean key vectors; overlap values above
-  a noise threshold tau are rescaled to g_hat, the distribution is multiplied
-  by (1 + lambda * g_hat) and renormalised; full overlap gives at most a
-  1 + lambda boost, a block with no vetted overlap keeps its importance.
-* Key Contributions 2 and the abstract: regions without geometric coverage
-  keep the model-derived route without geometric bias (the fallback).
+* Methodology, Step 4: per layer, the visible KV blocks are scored with
+  the block averages of the queries and keys; overlaps above a noise
+  threshold tau are rescaled to g_hat, and the distribution is scaled by
+  (1 + lambda * g_hat) and normalised again, so full overlap multiplies a
+  block's weight by at most 1 + lambda and a block whose overlap was
+  discarded keeps its weight.
+* Key Contributions 2 and the abstract: where no geometry covers a region,
+  its route comes from the model's scores alone (the fallback).
 * Methodology, Step 5 / Main Findings: routes take the top-scoring blocks up
   to a budget (50 of 143 in the pages' audit).
 * The calibrated constants tau = 0.1, g_ref = 0.2, lambda = 2 close the
@@ -37,9 +38,12 @@ from __future__ import annotations
 
 import numpy as np
 
+from .numerics import exact_column_sums
+
 
 def pool_blocks(x: np.ndarray, lengths: np.ndarray, bs: int) -> np.ndarray:
-    """Mean of the valid rows of each block of one head.
+    """Mean of the valid rows of each block of one head: the exact sum of
+    each column, rounded once to float64, divided by the row count.
 
     ``x[rows][d]`` float64 with ``rows = len(lengths) * bs``; block ``b``
     holds rows ``b*bs .. b*bs + lengths[b] - 1``.  Blocks with no valid row
@@ -51,7 +55,7 @@ def pool_blocks(x: np.ndarray, lengths: np.ndarray, bs: int) -> np.ndarray:
         n = int(lengths[b])
         if n > 0:
             rows = x[b * bs: b * bs + n, :]
-            out[b, :] = rows.sum(axis=0) / n
+            out[b, :] = exact_column_sums(rows) / n
     return out
 
 

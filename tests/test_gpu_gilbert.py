@@ -178,3 +178,40 @@ def test_index_large_grid():
     ref, ref_inv = gilbert_order(*shape)
     assert np.array_equal(perm.cpu().numpy(), ref)
     assert np.array_equal(inv.cpu().numpy(), ref_inv)
+
+
+def _mixed_magnitudes(shape, span_log2, seed, dtype):
+    """Values of random sign and magnitude 2^U(-span/2, span/2), with every
+    second row of a block cancelling the row before it in some columns: sums
+    that a plain float64 accumulation rounds, in an order-dependent way."""
+    rng = np.random.default_rng(seed)
+    x = 2.0 ** rng.uniform(-span_log2 / 2, span_log2 / 2, shape) * rng.choice([-1.0, 1.0], shape)
+    x[1::2, :, ::3] = -x[0::2, :, ::3][: x[1::2].shape[0]]
+    return torch.from_numpy(x.astype(np.float32)).to(dtype)
+
+
+@pytest.mark.parametrize("dtype,span", [(torch.float32, 60), (torch.bfloat16, 36)])
+def test_permute_pool_exact_means_mixed_magnitudes(dtype, span):
+    """Block means of rows whose magnitudes span 2^60 (float32: summed as
+    exact pairs) or 2^36 (bf16: a plain float64 sum, exact below 2^39) equal
+    the oracle's exact means bit for bit (its exact sum, rounded once): the
+    fused pass's summation order does not show."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    from oracle import route as oroute
+    T, H, W = 2, 12, 20
+    L, heads, d, block = T * H * W, 2, 64, 64
+    src = _mixed_magnitudes((L, heads, d), span, 31, dtype)
+    perm, _ = bsa.gilbert_index(T, H, W, device=dev)
+    _, pool = bsa.gilbert_perm_pool(src.to(dev), perm, block=block)
+    torch.cuda.synchronize()
+    ref = olay.permute_forward(f64(src), gilbert_order(T, H, W)[0], block)
+    lens = olay.chunk_block_lengths(L, block)
+    plain_differs = 0
+    for h in range(heads):
+        want = oroute.pool_blocks(ref[h], lens, block)
+        assert np.array_equal(pool[h].cpu().numpy(), want), h
+        for b, n in enumerate(lens):
+            plain_differs += int(np.sum(ref[h][b * block: b * block + n].sum(axis=0) / n != want[b]))
+    if dtype == torch.float32:
+        assert plain_differs > 0   # the inputs do reach sums a plain accumulation rounds

@@ -323,3 +323,31 @@ def test_routes_beyond_one_wave_ties_across_segments():
         got = csr_lists(r["row_ptr"], r["col_idx"], 1, nqb)
         ref = oroute.route_head(qh, f64(k[0]), q_len, k_len, 64, scale=0.125, k_per_row=np.full(nqb, kf))
         assert_lists_equal(got[0], ref["lists"], "ties, budget %d" % kf)
+
+
+@pytest.mark.parametrize("dtype,span", [(torch.float32, 60), (torch.bfloat16, 36)])
+def test_router_pools_exact_means_mixed_magnitudes(dtype, span):
+    """The router's own pooling (every K block into an empty pooled-key
+    cache) gives the oracle's exact block means bit for bit on rows whose
+    magnitudes span 2^60 (float32, summed as exact pairs) or 2^36 (bf16, a
+    plain float64 sum, exact below 2^39)."""
+    dev = need_gpu()
+    import block_sparse_attention_gilbert_amd as bsa
+    rng = np.random.default_rng(41)
+    heads, nqb, nkb, block, d = 2, 3, 9, 64, 64
+    def mixed(rows):
+        x = 2.0 ** rng.uniform(-span / 2, span / 2, (heads, rows, d)) * rng.choice([-1.0, 1.0], (heads, rows, d))
+        x[:, 1::2, ::3] = -x[:, 0::2, ::3]
+        return torch.from_numpy(x.astype(np.float32)).to(dtype)
+    q, k = mixed(nqb * block), mixed(nkb * block)
+    kl = np.full(nkb, block, dtype=np.int32)
+    kl[4], kl[8] = 37, 1
+    ql = np.full(nqb, block, dtype=np.int32)
+    cache = torch.zeros((heads, nkb, d), dtype=torch.float64, device=dev)
+    bsa.route_topk(q.to(dev), k.to(dev), block=block, nqb=nqb, nkb=nkb, scale=0.125,
+                   q_block_len=torch.from_numpy(ql).to(dev), kv_block_len=torch.from_numpy(kl).to(dev), k_fixed=3,
+                   kpool=cache, kpool_valid_blocks=0)
+    torch.cuda.synchronize()
+    for h in range(heads):
+        want = oroute.pool_blocks(f64(k[h]), kl, block)
+        assert np.array_equal(cache[h].cpu().numpy(), want), h

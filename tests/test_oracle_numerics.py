@@ -19,7 +19,7 @@ import math
 import numpy as np
 import torch
 
-from oracle.numerics import bf16_bits_to_f64, f32_to_f64
+from oracle.numerics import bf16_bits_to_f64, exact_column_sums, f32_to_f64
 
 
 def _decode_bf16(bits: int) -> float:
@@ -95,3 +95,47 @@ def test_f32_to_f64_exact():
     assert got[2] == 2.0 ** -149
     assert got[3] == (2 - 2.0 ** -23) * 2.0 ** 127
     assert np.array_equal(got.astype(np.float32), x)
+
+
+# ------------------------------------------------------ exact column sums
+
+def _fsum_cols(x):
+    return np.array([math.fsum(x[:, c].tolist()) for c in range(x.shape[1])])
+
+
+def test_exact_column_sums_fixes_what_plain_summation_rounds():
+    # 2^60 + 1 rounds to 2^60 in float64: a plain left-to-right sum gives 0
+    x = np.array([[2.0 ** 60], [1.0], [-(2.0 ** 60)]])
+    assert x.sum(axis=0)[0] == 0.0
+    assert exact_column_sums(x)[0] == 1.0
+    # a tie: 1 + 2^-53 is halfway between 1 and 1 + 2^-52 and rounds to even
+    y = np.array([[1.0], [2.0 ** -54], [2.0 ** -54]])
+    assert exact_column_sums(y)[0] == 1.0
+    z = np.array([[1.0], [2.0 ** -53], [2.0 ** -60]])
+    assert exact_column_sums(z)[0] == 1.0 + 2.0 ** -52
+
+
+def test_exact_column_sums_match_fsum_on_mixed_magnitudes():
+    rng = np.random.default_rng(5)
+    for span in (8, 30, 45, 60, 74, 100, 140):
+        for n in (1, 2, 7, 64, 128):
+            mag = 2.0 ** rng.uniform(-span / 2, span / 2, (n, 24))
+            x = (mag * rng.choice([-1.0, 1.0], (n, 24))).astype(np.float32).astype(np.float64)
+            if n > 2:
+                x[1] = -x[0]                      # cancellation
+                x[2, ::3] = 0.0                   # zeros
+            assert np.array_equal(exact_column_sums(x), _fsum_cols(x)), (span, n)
+
+
+def test_exact_column_sums_certified_columns_and_edge_values():
+    rng = np.random.default_rng(6)
+    # ordinary bf16-like data: every column certified, numpy's sum already exact
+    bits = (rng.standard_normal((128, 32)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    x = bf16_bits_to_f64(bits)
+    assert np.array_equal(exact_column_sums(x), _fsum_cols(x))
+    # subnormal and huge binary32 values, all-zero columns, one row, no rows
+    e = np.array([[1e-45, 3.4e38, 0.0], [-1e-45, -3.4e38, 0.0], [2e-45, 1.0, 0.0]], dtype=np.float32)
+    e = e.astype(np.float64)
+    assert np.array_equal(exact_column_sums(e), _fsum_cols(e))
+    assert np.array_equal(exact_column_sums(e[:1]), e[0])
+    assert exact_column_sums(np.zeros((0, 3))).shape == (3,)

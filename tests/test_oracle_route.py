@@ -41,8 +41,7 @@ def test_pool_sum_exact_for_bf16_values():
     m = route.pool_blocks(x, lens, 128)
     for b, n in enumerate(lens):
         for c in range(16):
-            # the float64 sum of <= 128 bf16 values is exact, so the mean is
-            # the correctly rounded quotient of the exact sum
+            # the mean is the correctly rounded quotient of the exact sum
             exact = math.fsum(x[b * 128: b * 128 + n, c].tolist())
             assert m[b, c] == exact / n
 
