@@ -16,6 +16,38 @@ thread_local char g_detail[512] = {0};
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool supported_dim(int x) { return x == 64 || x == 128; }
+
+// No device buffer reaches 2^48 bytes (256 TiB); extents above it are
+// rejected, which also keeps every kernel's int64 element offset in range.
+constexpr int64_t kMaxBytes = int64_t(1) << 48;
+
+// (n * stride + tail) elements of eb bytes, in bytes: false when an operand
+// is negative or the result overflows or exceeds kMaxBytes.
+bool extent(int64_t n, int64_t stride, int64_t tail, int eb, int64_t& bytes) {
+    int64_t x;
+    if (n < 0 || stride < 0 || tail < 0) return false;
+    if (__builtin_mul_overflow(n, stride, &x) || __builtin_add_overflow(x, tail, &x) ||
+        __builtin_mul_overflow(x, (int64_t)eb, &x) || x > kMaxBytes)
+        return false;
+    bytes = x;
+    return true;
+}
+
+// T x H x W grid cells fit in 2^31-1 (overflow-checked product)
+bool cells_fit(int T, int H, int W) {
+    int64_t x;
+    return !__builtin_mul_overflow((int64_t)T, (int64_t)H, &x) && !__builtin_mul_overflow(x, (int64_t)W, &x) &&
+           x <= INT32_MAX;
+}
+
+// a stride of eb-byte elements keeps 16-byte alignment (eb is 2, 4 or 8)
+bool stride16(int64_t stride, int eb) { return stride % (16 / eb) == 0; }
+
+// [a, a + na) and [b, b + nb) share a byte (address arithmetic unsigned)
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
 }  // namespace
 
 int fail(int code, const char* fmt, ...) {
@@ -32,7 +64,7 @@ const char* last_detail() { return g_detail; }
 
 int validate_gilbert_index(int T, int H, int W, const int32_t* perm) {
     if (T < 1 || H < 1 || W < 1) return fail(BSA_EINVAL, "grid %d x %d x %d: dimensions must be >= 1", T, H, W);
-    if ((int64_t)T * H * W > INT32_MAX) return fail(BSA_EINVAL, "grid %d x %d x %d exceeds 2^31-1 cells", T, H, W);
+    if (!cells_fit(T, H, W)) return fail(BSA_EINVAL, "grid %d x %d x %d exceeds 2^31-1 cells", T, H, W);
     if (!perm) return fail(BSA_EINVAL, "perm is NULL");
     return BSA_OK;
 }
@@ -54,14 +86,14 @@ int validate_gilbert_perm(const void* src, const void* dst, const int32_t* perm,
         return fail(BSA_EINVAL, "gilbert_head_stride %lld < n_blocks*block*d = %lld",
                     (long long)gilbert_head_stride, (long long)(rows * d));
     const int eb = dtype_bytes(dtype);
-    if (!aligned16(src) || !aligned16(dst) || (raster_token_stride * eb) % 16 || (gilbert_head_stride * eb) % 16)
+    if (!aligned16(src) || !aligned16(dst) || !stride16(raster_token_stride, eb) || !stride16(gilbert_head_stride, eb))
         return fail(BSA_EINVAL, "pointers and strides must be 16-byte aligned");
-    const char* s = static_cast<const char*>(src);
-    const char* t = static_cast<const char*>(dst);
-    const int64_t raster_bytes = ((int64_t)(L - 1) * raster_token_stride + (int64_t)heads * d) * eb;
-    const int64_t gil_bytes = ((int64_t)(heads - 1) * gilbert_head_stride + rows * d) * eb;
+    int64_t raster_bytes, gil_bytes;
+    if (!extent(L - 1, raster_token_stride, (int64_t)heads * d, eb, raster_bytes) ||
+        !extent(heads - 1, gilbert_head_stride, rows * d, eb, gil_bytes))
+        return fail(BSA_EINVAL, "tensor extent exceeds 2^48 bytes");
     const int64_t sb = inverse ? gil_bytes : raster_bytes, tb = inverse ? raster_bytes : gil_bytes;
-    if (s < t + tb && t < s + sb) return fail(BSA_EINVAL, "src and dst overlap");
+    if (overlap(src, sb, dst, tb)) return fail(BSA_EINVAL, "src and dst overlap");
     return BSA_OK;
 }
 
@@ -81,7 +113,7 @@ int validate_gilbert_perm_pool(const void* src, const void* dst, const int32_t* 
         if (raster_token_stride < (int64_t)heads * d)
             return fail(BSA_EINVAL, "raster_token_stride %lld < heads*d = %lld", (long long)raster_token_stride,
                         (long long)heads * d);
-        if (!aligned16(src) || (raster_token_stride * dtype_bytes(dtype)) % 16)
+        if (!aligned16(src) || !stride16(raster_token_stride, dtype_bytes(dtype)))
             return fail(BSA_EINVAL, "src and its token stride must be 16-byte aligned");
     }
     if (!pool) return fail(BSA_EINVAL, "pool must be non-NULL");
@@ -92,13 +124,12 @@ int validate_gilbert_perm_pool(const void* src, const void* dst, const int32_t* 
         return fail(BSA_EINVAL, "pool_head_stride %lld < n_blocks*d = %lld", (long long)pool_head_stride,
                     (long long)(nb * d));
     const int eb = dtype_bytes(dtype);
-    const char* pb = reinterpret_cast<const char*>(pool);
-    const int64_t pool_bytes = ((int64_t)(heads - 1) * pool_head_stride + nb * d) * (int64_t)sizeof(double);
-    const char* s = static_cast<const char*>(src);
-    const char* t = static_cast<const char*>(dst);
-    const int64_t raster_bytes = ((int64_t)(L - 1) * raster_token_stride + (int64_t)heads * d) * eb;
-    const int64_t gil_bytes = ((int64_t)(heads - 1) * gilbert_head_stride + nb * block * d) * eb;
-    if ((pb < s + raster_bytes && s < pb + pool_bytes) || (t && pb < t + gil_bytes && t < pb + pool_bytes))
+    int64_t pool_bytes, raster_bytes, gil_bytes = 0;
+    if (!extent(heads - 1, pool_head_stride, nb * d, (int)sizeof(double), pool_bytes) ||
+        !extent(L - 1, raster_token_stride, (int64_t)heads * d, eb, raster_bytes) ||
+        (dst && !extent(heads - 1, gilbert_head_stride, nb * block * d, eb, gil_bytes)))
+        return fail(BSA_EINVAL, "tensor extent exceeds 2^48 bytes");
+    if (overlap(pool, pool_bytes, src, raster_bytes) || overlap(pool, pool_bytes, dst, gil_bytes))
         return fail(BSA_EINVAL, "pool overlaps src or dst");
     return BSA_OK;
 }
@@ -128,6 +159,7 @@ int validate_gilbert_perm_pool_batch(const bsa_perm_job* jobs, int n_jobs, const
             snprintf(why, sizeof(why), "%s", g_detail);
             return fail(st, "job %d: %s", z, why);
         }
+        // every extent below was checked by the job's own validation
         const int64_t nb = ceil_div(L, block);
         src[z] = {static_cast<const char*>(j.src), ((int64_t)(L - 1) * j.raster_token_stride + (int64_t)heads * d) * eb};
         out[z][0] = {static_cast<const char*>(j.dst),
@@ -135,7 +167,7 @@ int validate_gilbert_perm_pool_batch(const bsa_perm_job* jobs, int n_jobs, const
         out[z][1] = {reinterpret_cast<const char*>(j.pool),
                      j.pool ? ((int64_t)(heads - 1) * j.pool_head_stride + nb * d) * (int64_t)sizeof(double) : 0};
     }
-    auto hit = [](const Range& a, const Range& b) { return a.n > 0 && b.n > 0 && a.p < b.p + b.n && b.p < a.p + a.n; };
+    auto hit = [](const Range& a, const Range& b) { return overlap(a.p, a.n, b.p, b.n); };
     for (int z = 0; z < n_jobs; ++z)
         for (int y = 0; y < n_jobs; ++y) {
             if (y == z) continue;
@@ -153,12 +185,18 @@ int validate_raster_out(const AttnProblem& p) {
     if (p.o_ts < (int64_t)p.heads * p.d)
         return fail(BSA_EINVAL, "o_token_stride %lld < heads*d = %lld", (long long)p.o_ts,
                     (long long)p.heads * p.d);
-    if ((p.o_ts * dtype_bytes(p.dtype)) % 16) return fail(BSA_EINVAL, "o_token_stride must be 16-byte aligned");
+    const int eb = dtype_bytes(p.dtype);
+    int64_t bytes;
+    if (!stride16(p.o_ts, eb)) return fail(BSA_EINVAL, "o_token_stride must be 16-byte aligned");
+    if (!extent(p.o_map_len - 1, p.o_ts, (int64_t)p.heads * p.d, eb, bytes))
+        return fail(BSA_EINVAL, "raster output extent exceeds 2^48 bytes");
     if (p.q_map) {
         if (p.q_ts < (int64_t)p.heads * p.d)
             return fail(BSA_EINVAL, "raster q_stride %lld < heads*d = %lld", (long long)p.q_ts,
                         (long long)p.heads * p.d);
-        if ((p.q_ts * dtype_bytes(p.dtype)) % 16) return fail(BSA_EINVAL, "raster q_stride must be 16-byte aligned");
+        if (!stride16(p.q_ts, eb)) return fail(BSA_EINVAL, "raster q_stride must be 16-byte aligned");
+        if (!extent(p.q_map_len > 0 ? p.q_map_len - 1 : 0, p.q_ts, (int64_t)p.heads * p.d, eb, bytes))
+            return fail(BSA_EINVAL, "raster query extent exceeds 2^48 bytes");
     }
     return BSA_OK;
 }
@@ -179,9 +217,13 @@ int validate_attn(const AttnProblem& p, bool dense) {
     if (p.k_hs < krows * p.d || p.v_hs < krows * p.d)
         return fail(BSA_EINVAL, "k/v head stride below nkb*block*d = %lld", (long long)(krows * p.d));
     const int eb = dtype_bytes(p.dtype);
-    if (!aligned16(p.q) || !aligned16(p.k) || !aligned16(p.v) || !aligned16(p.o) || (p.q_hs * eb) % 16 ||
-        (p.k_hs * eb) % 16 || (p.v_hs * eb) % 16 || (p.o_hs * eb) % 16)
+    if (!aligned16(p.q) || !aligned16(p.k) || !aligned16(p.v) || !aligned16(p.o) || !stride16(p.q_hs, eb) ||
+        !stride16(p.k_hs, eb) || !stride16(p.v_hs, eb) || !stride16(p.o_hs, eb))
         return fail(BSA_EINVAL, "tensor pointers and head strides must be 16-byte aligned");
+    int64_t bytes;
+    if (!extent(p.heads - 1, p.q_hs, qrows * p.d, eb, bytes) || !extent(p.heads - 1, p.o_hs, qrows * p.d, eb, bytes) ||
+        !extent(p.heads - 1, p.k_hs, krows * p.d, eb, bytes) || !extent(p.heads - 1, p.v_hs, krows * p.d, eb, bytes))
+        return fail(BSA_EINVAL, "tensor extent exceeds 2^48 bytes");
     if (!(p.scale > 0.0f) || p.scale > 3.0e38f) return fail(BSA_EINVAL, "scale must be finite and > 0");
     return BSA_OK;
 }
@@ -246,12 +288,18 @@ int validate_route(const bsa_route_args* a, RouteLayout* lay) {
     if (a->q && a->q_head_stride < qrows * a->d) return fail(BSA_EINVAL, "q_head_stride below nqb*block*d");
     if (a->k_head_stride < krows * a->d) return fail(BSA_EINVAL, "k_head_stride below nkb*block*d");
     const int eb = dtype_bytes(a->dtype);
-    if (!aligned16(a->q) || !aligned16(a->k) || (a->q_head_stride * eb) % 16 || (a->k_head_stride * eb) % 16)
+    if (!aligned16(a->q) || !aligned16(a->k) || !stride16(a->q_head_stride, eb) || !stride16(a->k_head_stride, eb))
         return fail(BSA_EINVAL, "q/k pointers and head strides must be 16-byte aligned");
+    int64_t bytes;
+    if ((a->q && !extent(a->heads - 1, a->q_head_stride, qrows * a->d, eb, bytes)) ||
+        !extent(a->heads - 1, a->k_head_stride, krows * a->d, eb, bytes))
+        return fail(BSA_EINVAL, "q/k extent exceeds 2^48 bytes");
     if (a->qpool) {
         if (!aligned16(a->qpool) || a->qpool_head_stride % 2)
             return fail(BSA_EINVAL, "qpool and its head stride must be 16-byte aligned");
         if (a->qpool_head_stride < (int64_t)a->nqb * a->d) return fail(BSA_EINVAL, "qpool_head_stride below nqb*d");
+        if (!extent(a->heads - 1, a->qpool_head_stride, (int64_t)a->nqb * a->d, 8, bytes))
+            return fail(BSA_EINVAL, "qpool extent exceeds 2^48 bytes");
     }
     if (!(a->scale > 0.0) || a->scale > 1.0e300) return fail(BSA_EINVAL, "scale must be finite and > 0");
     if (a->overlap) {
@@ -344,8 +392,8 @@ int validate_materialize(const bsa_route_args* a, const bsa_materialize_args* m,
 int validate_block_window(const int32_t* perm, const int32_t* inv, int T, int H, int W, int block, int q_chunk,
                           const int32_t* window, const int32_t* window_len, int window_stride) {
     if (T < 1 || H < 1 || W < 1) return fail(BSA_EINVAL, "grid %d x %d x %d: dimensions must be >= 1", T, H, W);
+    if (!cells_fit(T, H, W)) return fail(BSA_EINVAL, "grid %d x %d x %d exceeds 2^31-1 cells", T, H, W);
     const int64_t L = (int64_t)T * H * W;
-    if (L > INT32_MAX) return fail(BSA_EINVAL, "grid %d x %d x %d exceeds 2^31-1 cells", T, H, W);
     if (!perm || !inv || !window || !window_len)
         return fail(BSA_EINVAL, "perm, inv, window and window_len must be non-NULL");
     if (block < 1) return fail(BSA_EINVAL, "block %d < 1", block);
@@ -363,9 +411,13 @@ int validate_tile_index(int T, int H, int W, int tt, int th, int tw, const int32
     if (T < 1 || H < 1 || W < 1) return fail(BSA_EINVAL, "grid %d x %d x %d: dimensions must be >= 1", T, H, W);
     if (tt < 1 || th < 1 || tw < 1) return fail(BSA_EINVAL, "tile %d x %d x %d: dimensions must be >= 1", tt, th, tw);
     if (!row_cell || !block_len) return fail(BSA_EINVAL, "row_cell and block_len must be non-NULL");
-    const int64_t rows = ceil_div(T, tt) * ceil_div(H, th) * ceil_div(W, tw) * ((int64_t)tt * th * tw);
-    if (rows > INT32_MAX || (int64_t)T * H * W > INT32_MAX)
-        return fail(BSA_EINVAL, "tiled rows or cells exceed 2^31-1");
+    if (!cells_fit(T, H, W)) return fail(BSA_EINVAL, "grid cells exceed 2^31-1");
+    // padded rows = (tiles along each axis) x (cells per tile), overflow-checked
+    const int64_t f[6] = {ceil_div(T, tt), ceil_div(H, th), ceil_div(W, tw), tt, th, tw};
+    int64_t rows = 1;
+    for (int64_t x : f)
+        if (__builtin_mul_overflow(rows, x, &rows) || rows > INT32_MAX)
+            return fail(BSA_EINVAL, "tiled rows exceed 2^31-1");
     return BSA_OK;
 }
 
@@ -384,14 +436,14 @@ int validate_tile_perm(const void* src, const void* dst, const int32_t* row_cell
         return fail(BSA_EINVAL, "tiled_head_stride %lld < n_rows*d = %lld", (long long)tiled_head_stride,
                     (long long)n_rows * d);
     const int eb = dtype_bytes(dtype);
-    if (!aligned16(src) || !aligned16(dst) || (raster_token_stride * eb) % 16 || (tiled_head_stride * eb) % 16)
+    if (!aligned16(src) || !aligned16(dst) || !stride16(raster_token_stride, eb) || !stride16(tiled_head_stride, eb))
         return fail(BSA_EINVAL, "pointers and strides must be 16-byte aligned");
-    const char* s = static_cast<const char*>(src);
-    const char* t = static_cast<const char*>(dst);
-    const int64_t raster_bytes = ((int64_t)(L - 1) * raster_token_stride + (int64_t)heads * d) * eb;
-    const int64_t tiled_bytes = ((int64_t)(heads - 1) * tiled_head_stride + (int64_t)n_rows * d) * eb;
+    int64_t raster_bytes, tiled_bytes;
+    if (!extent(L - 1, raster_token_stride, (int64_t)heads * d, eb, raster_bytes) ||
+        !extent(heads - 1, tiled_head_stride, (int64_t)n_rows * d, eb, tiled_bytes))
+        return fail(BSA_EINVAL, "tensor extent exceeds 2^48 bytes");
     const int64_t sb = inverse ? tiled_bytes : raster_bytes, tb = inverse ? raster_bytes : tiled_bytes;
-    if (s < t + tb && t < s + sb) return fail(BSA_EINVAL, "src and dst overlap");
+    if (overlap(src, sb, dst, tb)) return fail(BSA_EINVAL, "src and dst overlap");
     return BSA_OK;
 }
 
@@ -399,7 +451,7 @@ int validate_tile_block_window(const int32_t* row_cell, const int32_t* cell_row,
                                int block, int q_chunk, const int32_t* window, const int32_t* window_len,
                                int window_stride) {
     if (T < 1 || H < 1 || W < 1) return fail(BSA_EINVAL, "grid %d x %d x %d: dimensions must be >= 1", T, H, W);
-    if ((int64_t)T * H * W > INT32_MAX) return fail(BSA_EINVAL, "grid exceeds 2^31-1 cells");
+    if (!cells_fit(T, H, W)) return fail(BSA_EINVAL, "grid exceeds 2^31-1 cells");
     if (!row_cell || !cell_row || !window || !window_len)
         return fail(BSA_EINVAL, "row_cell, cell_row, window and window_len must be non-NULL");
     if (block < 1 || n_rows < 1 || n_rows % block)
@@ -434,7 +486,7 @@ int validate_slab_coverage(const double* cams, int n_cams, const int32_t* perm, 
                            int n_h, const float* coverage) {
     if (!cams || n_cams < 1) return fail(BSA_EINVAL, "cams must be non-NULL with n_cams >= 1");
     if (T < 1 || H < 1 || W < 1) return fail(BSA_EINVAL, "grid %d x %d x %d: dimensions must be >= 1", T, H, W);
-    if ((int64_t)T * H * W > INT32_MAX) return fail(BSA_EINVAL, "grid exceeds 2^31-1 cells");
+    if (!cells_fit(T, H, W)) return fail(BSA_EINVAL, "grid exceeds 2^31-1 cells");
     if (block < 1) return fail(BSA_EINVAL, "block %d < 1", block);
     if (!perm || !frame_cam || !depth || !coverage)
         return fail(BSA_EINVAL, "perm, frame_cam, depth and coverage must be non-NULL");
@@ -476,7 +528,7 @@ size_t bsa_route_materialize_workspace_size(const bsa_route_args* args, const bs
 }
 
 size_t bsa_slab_coverage_workspace_size(int T, int H, int W) {
-    if (T < 1 || H < 1 || W < 1 || (int64_t)T * H * W > INT32_MAX) return 0;
+    if (T < 1 || H < 1 || W < 1 || !bsa::cells_fit(T, H, W)) return 0;
     return sizeof(uint32_t) * (size_t)bsa::ceil_div((int64_t)T * H * W, 32);
 }
 
