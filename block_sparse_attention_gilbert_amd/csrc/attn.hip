@@ -207,18 +207,43 @@ __device__ __forceinline__ uint32_t dma_lane_offset(int n, int wave, int lane) {
     return (uint32_t)(row * D + c * 8) * 2u;
 }
 
+// Instruction n's lane offset equals instruction 0's plus n * NW KB when
+// the NW * RPI rows that one instruction round covers are a whole number of
+// swizzle periods (16 rows for K, 4 for V at d = 128).
+template <int D, int NW>
+constexpr bool dma_lane_offset_step() {
+    return D == 128 && (NW * (64 / (D / 8))) % 16 == 0;
+}
+
 // Issue the copies of one sub-tile: NI wave-instructions; buffer resource =
 // the block, bounded to its valid rows; scalar offset = the sub-tile, vector
 // offset = the lane's.  The bound applies to the whole offset (scalar +
 // vector): rows past it are not fetched and land in LDS as zeros.
-template <int NI, int NW>
+template <int NI, int NW, bool FORM_AT_USE = false>
 __device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t rsrc, uint32_t sub_off, const uint32_t* voff,
                                           uint16_t* lds_tile, int wave) {
+    if constexpr (FORM_AT_USE) {
+        // For a kernel short of registers: the LDS destination is formed
+        // here from one wave-uniform base that passes through an empty asm
+        // (otherwise the compiler keeps every (buffer, instruction) address
+        // of the unrolled loop live in scalar registers), and instruction n
+        // reuses the lane offset of instruction 0 with n * NW * 1 KB more in
+        // the scalar offset (see dma_lane_offset_step).
+        constexpr uint32_t kStep = (uint32_t)NW * 1024u;
+        uint32_t base = (uint32_t)(uintptr_t)(lds_u16_t*)lds_tile + (uint32_t)wave * 1024u;
+        __asm__ volatile("" : "+s"(base));
 #pragma unroll
-    for (int n = 0; n < NI; ++n)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc, (__attribute__((address_space(3))) void*)((lds_u16_t*)lds_tile + (n * NW + wave) * 512), 16,
-            voff[n], sub_off, 0, 0);
+        for (int n = 0; n < NI; ++n)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)(uintptr_t)(base + n * kStep), 16, voff[0],
+                sub_off + n * kStep, 0, 0);
+    } else {
+#pragma unroll
+        for (int n = 0; n < NI; ++n)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)((lds_u16_t*)lds_tile + (n * NW + wave) * 512), 16,
+                voff[n], sub_off, 0, 0);
+    }
 }
 
 // Raw buffer (no stride) over nbytes from base; 0x00020000 = 32-bit data
@@ -284,11 +309,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // during the LDS reads would force every LDS wait to lgkmcnt(0), since
 // scalar loads complete out of order.  Out-of-range entries take a slow
 // path with direct loads.
-template <int BLK, bool DENSE>
+//
+// With PIPE2 (a new block every iteration) the block index is loaded one
+// entry further ahead (pj2), so that the two loads issued after a next()
+// by prefetch_both() -- the key count of the next entry and the index of
+// the one after -- do not depend on each other.
+template <int BLK, bool DENSE, bool PIPE2 = false>
 struct ListReader {
     const_i32_t* col;
     const_i32_t* kvl;
-    int e, e1, nkb, pj, pv;
+    int e, e1, nkb, pj, pv, pj2 = 0;
     __device__ __forceinline__ int keys(int v) const {
         return __builtin_amdgcn_readfirstlane(v < 0 ? 0 : (v > BLK ? BLK : v));
     }
@@ -301,6 +331,13 @@ struct ListReader {
         nkb = nkb_;
         pj = DENSE ? e : (e < e1 ? col[e] : 0);
         pv = kvl ? kvl[clamp_j(pj)] : BLK;
+        if (PIPE2) pj2 = DENSE ? e + 1 : (e + 1 < e1 ? col[e + 1] : 0);
+    }
+    // PIPE2: after a next(), the entry now at e and the index of e + 1
+    __device__ __forceinline__ void prefetch_both() {
+        pv = kvl ? kvl[clamp_j(pj2)] : BLK;
+        pj = pj2;
+        pj2 = DENSE ? e + 1 : col[e + 1 < e1 ? e + 1 : e1 - 1];
     }
     __device__ __forceinline__ void prefetch1() {
         pj = DENSE ? e : col[e < e1 ? e : e1 - 1];
@@ -323,6 +360,7 @@ struct ListReader {
                     break;
                 }
             }
+            if (PIPE2) pj2 = col[e < e1 ? e : e1 - 1];  // the entry at e, for prefetch_both
         }
         return j;
     }
@@ -336,6 +374,11 @@ __device__ __forceinline__ void static_for(F&& f) {
         static_for<B + 1, E>(f);
     }
 }
+
+// Waves that share each 32-row query tile, each taking its own 32 keys of
+// every slot: 2 for the 64-row, d-128 workgroup (four waves instead of two,
+// so two workgroups per CU give each SIMD two waves), 1 otherwise.
+constexpr int attn_key_split(int blk, int d) { return blk == 64 && d == 128 ? 2 : 1; }
 
 // Compile-time loop that stops at the first f(integral_constant<int, I>)
 // returning false; true when every call did.
@@ -357,15 +400,20 @@ constexpr int lcm3(int x, int y, int z) {
 // Scheduling fence: the compiler keeps the instruction order across it.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// Workgroup of BLK/32 waves, one (head, query block); wave w owns query rows
-// 32w .. 32w+31 and every key.  Keys stream in sub-tiles of kSubKeys: slot t
-// is sub-tile t % SUBS of the t / SUBS-th listed block.  K and V have rings
-// of RK and RV 32-key sub-tiles, sized so that every SIMD holds at least
-// two waves, whose softmax and matrix work then overlap each other: the
-// 128-row workgroup (four waves) keeps four of each (2 x 32 KB at d = 128,
-// two workgroups per CU); the 64-row one (two waves) keeps three K and two
-// V sub-tiles at d = 128 (40 KB, four workgroups per CU: with four of each,
-// only two would fit, one wave per SIMD), four of each at d = 64 (32 KB).
+// Workgroup of BLK/32 query tiles of 32 rows, one (head, query block).
+// Keys stream in slots of SLOTK keys: slot t is slot t % SUBS of the
+// t / SUBS-th listed block.  K and V have rings of RK and RV slots, sized so
+// that every SIMD holds two waves, whose softmax and matrix work then
+// overlap each other:
+//  - 128 rows: four waves, one per query tile, 32-key slots, rings of four
+//    K and four V slots (2 x 32 KB at d = 128, two workgroups per CU);
+//  - 64 rows at d = 128: four waves, two per query tile, each taking its
+//    own 32 keys of every 64-key slot (one slot = one block), rings of two
+//    K and two V slots (64 KB, two workgroups per CU).  The two waves of a
+//    tile keep separate softmax states, merged at the end.  A two-wave
+//    workgroup with the same 64 KB would leave one wave per SIMD; with a
+//    smaller ring (four per CU) twice the workgroups share each XCD's L2;
+//  - d = 64: 32-key slots, four of each (32 KB).
 //
 // Iteration t, after one barrier:
 //   copies      V of slot t+RV-1, then K of slot t+RK, are issued into the
@@ -379,19 +427,22 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // passes it by more than kRescaleSlack (a rare, wave-uniform branch), so
 // p <= 2^slack and each query's arithmetic depends on its own scores only.
 template <int BLK, int D, bool DENSE>
-__global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
-    constexpr int NW = BLK / 32;  // waves
+__global__ void __launch_bounds__(BLK * 2 * attn_key_split(BLK, D), 2) attn_bf16_kernel(AttnArgs a) {
+    constexpr int KS = attn_key_split(BLK, D);  // waves per query tile, one key share each
+    constexpr int NWQ = BLK / 32;               // query tiles (32 rows each)
+    constexpr int NW = NWQ * KS;                // waves
     constexpr int DT = D / 32, KK = D / 16;
-    constexpr int SUBE = kSubKeys * D;     // elements of a K or V sub-tile
-    constexpr int SUBS = BLK / kSubKeys;   // sub-tiles per block
-    constexpr int NI = kSubKeys * D * 2 / 1024 / NW;  // copy instructions per wave per sub-tile
-    constexpr bool kSmallRing = BLK == 64 && D == 128;
-    constexpr int RK = kSmallRing ? 3 : 4, RV = kSmallRing ? 2 : 4;  // K and V ring depths
-    constexpr int LAG = (RK - 1) / SUBS;   // blocks between the K-copy cursor and slot t+1
-    constexpr int U = lcm3(RK, RV, SUBS);  // unroll period: every ring index a constant
-    static_assert(kSubKeys * D * 2 % (1024 * NW) == 0, "sub-tile copy must split evenly over the waves");
-    static_assert(LAG <= 1, "the cursor history is two blocks deep");
-    static_assert(RK >= RV && RK - RV < SUBS, "the V copy of a new block must find it at the K-copy cursor");
+    constexpr int SLOTK = kSubKeys * KS;        // keys per slot (one pipeline stage)
+    constexpr int SUBE = SLOTK * D;             // elements of a K or V slot buffer
+    constexpr int SUBS = BLK / SLOTK;           // slots per block
+    constexpr int NI = SLOTK * D * 2 / 1024 / NW;  // copy instructions per wave per slot
+    constexpr int RK = KS == 2 ? 2 : 4, RV = KS == 2 ? 2 : 4;  // K and V ring depths (slots)
+    constexpr int LAG = (RK - 1) / SUBS;        // blocks between the K-copy cursor and slot t+1
+    constexpr int VLAG = (RK - RV) / SUBS;      // blocks between it and a V copy that opens a block
+    constexpr int HD = LAG + 1;                 // depth of the cursor history
+    constexpr int U = lcm3(RK, RV, SUBS);       // unroll period: every ring index a constant
+    static_assert(SLOTK * D * 2 % (1024 * NW) == 0, "slot copy must split evenly over the waves");
+    static_assert(RK >= RV && LAG <= 2 && VLAG <= LAG, "cursor history");
     // one LDS object per buffer: the compiler then tracks each buffer's
     // copies on their own (a read of one waits only for that buffer's)
     __shared__ __attribute__((aligned(1024))) uint16_t kb0[SUBE], kb1[SUBE], kb2[SUBE], kb3[RK > 3 ? SUBE : 1];
@@ -402,6 +453,8 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ks = KS == 1 ? 0 : wave / NWQ;                    // this wave's key share of a slot
+    const int ksoff = ks * kSubKeys * D * 2;                    // bytes to its 32 keys in a slot buffer
     const int hi = lane >> 5, l32 = lane & 31, g16 = lane & 15;
     int h, i;
     if (DENSE) {
@@ -413,7 +466,7 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
     }
     int vq = a.q_len ? a.q_len[i] : BLK;
     vq = vq < 0 ? 0 : (vq > BLK ? BLK : vq);
-    const int q0 = wave * 32;
+    const int q0 = (wave % NWQ) * 32;
     const bool active = q0 < vq;
     const bool valid_row = q0 + l32 < vq;
 
@@ -441,7 +494,7 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         e0 = e0 < 0 ? 0 : e0;
         e1 = e1 > a.col_len ? (int)a.col_len : e1;
     }
-    ListReader<BLK, DENSE> list;
+    ListReader<BLK, DENSE, SUBS == 1> list;
     list.init((const_i32_t*)a.col_idx, (const_i32_t*)a.kv_len, e0, e1, a.nkb);
 
     // K-copy cursor: block jk; the blocks it has entered are published to a
@@ -462,59 +515,71 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         if (a.lse && hi == 0) a.lse[(int64_t)h * a.nqb * BLK + (int64_t)i * BLK + qrow] = -INFINITY;
         return;
     }
-    int h0j = jk, h1v = 0;
-    int h0end = 0, h1end = 1;  // ints, not bools: kept in scalar registers
+    // history: [0] = the K-copy cursor's block, [d] = d blocks before it:
+    // its index and valid keys, -1 keys past the end of the list (ints, kept
+    // in scalar registers)
+    int hj[HD], hv[HD];
+    hj[0] = jk, hv[0] = h0v;
+#pragma unroll
+    for (int d = 1; d < HD; ++d) hj[d] = jk, hv[d] = -1;
     auto k_advance = [&]() __attribute__((always_inline)) {
-        h1v = h0v;
-        h1end = h0end;
+#pragma unroll
+        for (int d = HD - 1; d > 0; --d) hj[d] = hj[d - 1], hv[d] = hv[d - 1];
         int nv = 0;
-        const int nj = h0end ? -1 : list.next(nv);
+        const int nj = hv[0] < 0 ? -1 : list.next(nv);
         if (nj >= 0) {
             jk = nj;
-            h0v = nv;
+            hv[0] = nv;
         } else {
-            h0end = 1;  // copies past the end fetch nothing (never computed)
-            h0v = 0;
+            hv[0] = -1;  // copies past the end fetch nothing (never computed)
         }
-        h0j = jk;
+        hj[0] = jk;
+    };
+    // the list's next entry: two loads (see ListReader)
+    auto prefetch_all = [&]() __attribute__((always_inline)) {
+        if constexpr (SUBS == 1) {
+            list.prefetch_both();
+        } else {
+            list.prefetch1();
+            list.prefetch2();
+        }
     };
     int kvk = 0, vvk = 0;  // valid keys of the blocks being copied (0 past the end)
     int jv = jk;
 
+    static_assert(KS == 1 || dma_lane_offset_step<D, NW>(), "copy offsets of the key-split kernel");
     uint32_t koffs[NI], voffs[NI];
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
         koffs[n] = dma_lane_offset<D, NW, false>(n, wave, lane);
         voffs[n] = dma_lane_offset<D, NW, true>(n, wave, lane);
     }
-    constexpr uint32_t kSubBytes = kSubKeys * D * 2;
-    // copies of one sub-tile, bounded to the block's valid rows: padded rows
+    constexpr uint32_t kSubBytes = SLOTK * D * 2;
+    // copies of one slot, bounded to the block's valid rows: padded rows
     // and copies past the end of the list (0 valid keys) fetch nothing
     auto issue_k = [&](int buf, int sub) __attribute__((always_inline)) {
-        kvk = h0v;
-        dma_issue<NI, NW>(block_rsrc(Kh + (int64_t)jk * BLK * D, (uint32_t)kvk * (D * 2)), sub * kSubBytes, koffs,
+        kvk = hv[0] < 0 ? 0 : hv[0];
+        dma_issue<NI, NW, KS == 2>(block_rsrc(Kh + (int64_t)jk * BLK * D, (uint32_t)kvk * (D * 2)), sub * kSubBytes, koffs,
                           KB[buf], wave);
     };
     auto issue_v = [&](int buf, int sub) __attribute__((always_inline)) {
-        dma_issue<NI, NW>(block_rsrc(Vh + (int64_t)jv * BLK * D, (uint32_t)vvk * (D * 2)), sub * kSubBytes, voffs,
+        dma_issue<NI, NW, KS == 2>(block_rsrc(Vh + (int64_t)jv * BLK * D, (uint32_t)vvk * (D * 2)), sub * kSubBytes, voffs,
                           VB[buf], wave);
     };
 
     // prologue: K of slots 0..RK-1, V of slots 0..RV-2
-    list.prefetch1();
-    list.prefetch2();
+    prefetch_all();
 #pragma unroll
     for (int s = 0; s < RK; ++s) {
         if (s > 0 && s % SUBS == 0) {
             k_advance();
-            list.prefetch1();
-            list.prefetch2();
+            prefetch_all();
         }
         issue_k(s, s % SUBS);
         if (s < RV - 1) {
-            if (s % SUBS == 0) {
-                jv = h0j;
-                vvk = h0v;
+            if (s % SUBS == 0) {  // the V copy follows the K copy of its slot
+                jv = hj[0];
+                vvk = hv[0] < 0 ? 0 : hv[0];
             }
             issue_v(s, s % SUBS);
         }
@@ -524,7 +589,7 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
     const int kr = key_of_row(l32);
     int koff[KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) koff[kk] = tile_off<D, false>(kr, 2 * kk + hi);
+    for (int kk = 0; kk < KK; ++kk) koff[kk] = tile_off<D, false>(kr, 2 * kk + hi) + ksoff;
     int voff[DT][2];
     {
         const int j4 = g16 >> 2, r4 = g16 & 3, g2 = (lane >> 4) & 1;
@@ -534,7 +599,7 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
             for (int h4 = 0; h4 < 2; ++h4) {
                 const int row = 8 * hi + 4 * h4 + j4;  // + 16*s2
                 const int col = dt * 32 + 16 * g2 + 4 * r4;
-                voff[dt][h4] = tile_off<D, true>(row, col >> 3) + ((col >> 2) & 1) * 8;
+                voff[dt][h4] = tile_off<D, true>(row, col >> 3) + ((col >> 2) & 1) * 8 + ksoff;
             }
     }
 
@@ -643,10 +708,11 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
     wait_vmcnt<(RK + RV - 2) * NI>();
     lds_barrier();
     wait_lgkmcnt0();
-    int cvk = LAG == 0 ? h0v : h1v;  // valid keys of the block of slot t+1
+    int cvk = hv[LAG];  // valid keys of the block of slot t+1
     if (active) {
         f32x16_t s = scores(KB[0]);
-        if (cvk < kSubKeys) mask(s, cvk);
+        const int nv0 = cvk - ks * kSubKeys;
+        if (nv0 < kSubKeys) mask(s, nv0);
         logits_scale(s);
         logits_check();
     }
@@ -666,7 +732,7 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
     // Between the phases, keys >= nv of slot t+1 are masked (a rare,
     // wave-uniform branch: only a block's last, partly valid sub-tiles).
     auto body = [&](const uint16_t* kbuf, const uint16_t* vbuf, int nv) __attribute__((always_inline)) {
-        constexpr int KD = 3;                       // K fragment read distance
+        constexpr int KD = KS == 2 ? 2 : 3;         // K fragment read distance (registers)
         constexpr int VPS = 4 * DT / KK;            // V reads per phase-A segment
         constexpr int NA = 16 + 4;                  // list A: 16 exp2, 4 packs of P[0..7]
         constexpr int NB = 4 + 16 + 24;              // list B
@@ -781,30 +847,71 @@ __global__ void __launch_bounds__(BLK * 2, 2) attn_bf16_kernel(AttnArgs a) {
         wait_vmcnt<kInFlight * NI>();
         lds_barrier();
         wait_lgkmcnt0();  // the list prefetches of the previous iteration
-        if (SUB_V == 0) {  // V's new block is the K-copy cursor's current one
-            jv = h0j;
-            vvk = h0v;
+        if (SUB_V == 0) {  // V's new block: VLAG blocks behind the K-copy cursor
+            jv = hj[VLAG];
+            vvk = hv[VLAG] < 0 ? 0 : hv[VLAG];
         }
         issue_v((K + RV - 1) % RV, SUB_V);
         if (SUB_K == 0) k_advance();
         issue_k(K % RK, SUB_K);
         if (SUB_N == 0) {
-            cvk = LAG == 0 ? h0v : h1v;
-            if (LAG == 0 ? h0end : h1end) {
+            cvk = hv[LAG];
+            if (cvk < 0) {
                 tail(K_);
                 return false;
             }
         }
-        if (active) body(KB[(K + 1) % RK], VB[K % RV], cvk - SUB_N * kSubKeys);
-        // the next block's list entry, two loads on the two iterations after
-        // the K-copy cursor moved
-        if (SUB_K == 0) list.prefetch1();
-        if ((K + RK - 1) % SUBS == 0) list.prefetch2();
+        if (active)
+            body(KB[(K + 1) % RK], VB[K % RV], cvk - SUB_N * SLOTK - ks * kSubKeys);
+        // the next block's list entry: two loads, on the two iterations
+        // after the K-copy cursor moved (both on that one with one slot per
+        // block, where the reader keeps the indices a further entry ahead)
+        if constexpr (SUBS == 1) {
+            list.prefetch_both();
+        } else {
+            if (SUB_K == 0) list.prefetch1();
+            if ((K + RK - 1) % SUBS == 0) list.prefetch2();
+        }
         return true;
     };
     while (static_all<0, U>(step)) {
     }
     wait_vmcnt<0>();  // the copies past the end must land before the LDS is released
+
+    if constexpr (KS == 2) {
+        // The two key shares of each query tile meet: the second wave's
+        // (reference, row sums, O) go through LDS (the ring, now free: O of
+        // query tile w into K buffer w, its sums and reference into V buffer
+        // w) and the first wave rescales both to the larger reference.  A
+        // reference never set (no valid key seen) counts as -inf: its O and
+        // sums are exact zeros.
+        static_assert(NWQ == 2 && RV >= 2 && DT * 16 * 64 * 4 <= SUBE * 2, "merge buffers");
+        const bool w0 = wave % NWQ == 0;
+        float* xo = reinterpret_cast<float*>(w0 ? KB[0] : KB[1]);
+        float* xs = reinterpret_cast<float*>(w0 ? VB[0] : VB[1]);
+        __syncthreads();  // every wave's ring reads are done
+        if (ks == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xo[(dt * 16 + r) * 64 + lane] = o[dt][r];
+            xs[lane] = l;
+            xs[64 + lane] = ref_set ? ref : -INFINITY;
+        }
+        __syncthreads();
+        if (ks == 1) return;
+        const float r1 = ref_set ? ref : -INFINITY, r2 = xs[64 + lane];
+        const float mr = fmaxf(r1, r2);
+        if (mr > -INFINITY) {
+            const float a1 = __builtin_amdgcn_exp2f(r1 - mr), a2 = __builtin_amdgcn_exp2f(r2 - mr);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] = o[dt][r] * a1 + xo[(dt * 16 + r) * 64 + lane] * a2;
+            l = l * a1 + xs[lane] * a2;
+            ref = mr;
+        }
+    }
 
     // epilogue
     const float lt = add_halves(l);
@@ -914,9 +1021,11 @@ template <int BLK, int D>
 hipError_t launch_typed(const AttnArgs& args, int dtype, bool dense, int total, hipStream_t stream) {
     if (dtype == BSA_BF16) {
         if (dense)
-            hipLaunchKernelGGL((attn_bf16_kernel<BLK, D, true>), dim3(total), dim3(BLK * 2), 0, stream, args);
+            hipLaunchKernelGGL((attn_bf16_kernel<BLK, D, true>), dim3(total), dim3(BLK * 2 * attn_key_split(BLK, D)), 0,
+                               stream, args);
         else
-            hipLaunchKernelGGL((attn_bf16_kernel<BLK, D, false>), dim3(total), dim3(BLK * 2), 0, stream, args);
+            hipLaunchKernelGGL((attn_bf16_kernel<BLK, D, false>), dim3(total), dim3(BLK * 2 * attn_key_split(BLK, D)),
+                               0, stream, args);
     } else {
         if (dense)
             hipLaunchKernelGGL((attn_f32_kernel<BLK, D, true>), dim3(total), dim3(BLK * (D / 32)), 0, stream, args);

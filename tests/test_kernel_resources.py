@@ -2,8 +2,8 @@
 kernel spills to scratch memory (a spill turns register traffic into memory
 traffic), and the attention kernels keep the occupancy their design assumes
 (two workgroups per CU for the 128-row blocks: at most 256 registers per
-lane and half of the CU's 160 KB of LDS each; four per CU for the 64-row
-blocks at d = 128: a quarter of the LDS each)."""
+lane and half of the CU's 160 KB of LDS each; the same for the four-wave
+64-row workgroups at d = 128)."""
 
 import os
 import re
@@ -64,12 +64,14 @@ def test_attention_occupancy(tmp_path):
 
 
 def test_attention_64_row_occupancy(tmp_path):
-    """The 64-row, d-128 workgroup (two waves) holds a 40 KB ring so that four
-    share a CU, two waves per SIMD: at most 256 registers per lane and a
-    quarter of the 160 KB of LDS each."""
+    """The 64-row, d-128 workgroup has four waves (two per 32-row query
+    tile, each with half of every 64-key slot) and a 64 KB ring, so that two
+    share a CU with two waves per SIMD: at most 256 registers per lane and
+    half of the 160 KB of LDS each."""
     kernels = _kernels(tmp_path)
     attn = {k: v for k, v in kernels.items() if "attn_bf16_kernelILi64ELi128" in k}
     assert len(attn) == 2, sorted(attn)
     for name, v in attn.items():
         assert v["vgpr_count"] + v.get("agpr_count", 0) <= 256, (name, v)
-        assert v["group_segment_fixed_size"] <= 160 * 1024 // 4, (name, v)
+        assert v["group_segment_fixed_size"] <= 160 * 1024 // 2, (name, v)
+        assert v.get("max_flat_workgroup_size", 256) == 256, (name, v)
