@@ -618,20 +618,24 @@ def profile_attention(launches: int, expect_out=None):
     dst.copy_(src)
     torch.cuda.synchronize()
     if expect_out:
-        # what the launches must issue: every listed block is ceil(valid / 32)
-        # sub-tiles of 32 keys per wave (an empty sub-tile is skipped), each
-        # 8 MFMAs for S and 8 for P V; an unlisted block costs nothing
+        # what the launches must issue: every listed block is block / 32
+        # sub-tiles of 32 keys (a partly valid block is masked, not cut), each
+        # 8 MFMAs for S and 8 for P V in every wave whose 32 query rows are not
+        # all padding (the others skip the math); an unlisted block costs
+        # nothing
         import numpy as np
         rp = r["row_ptr"].cpu().numpy().astype(np.int64)
-        ci = r["col_idx"].cpu().numpy().astype(np.int64)[: int(rp[-1])]
-        kvl = ra.kv_len[:nkb].cpu().numpy().astype(np.int64)
-        subs = -(-kvl // 32)
-        waves = ra.block // 32
+        ql = ra.q_len.cpu().numpy().astype(np.int64)
+        nqb = len(ql)
+        waves_q = -(-np.clip(ql, 0, ra.block) // 32)          # active waves per query block
+        listed = rp[1:] - rp[:-1]                              # per (head, query block) row
+        active = np.tile(waves_q, len(listed) // nqb)
+        subs = ra.block // 32
         with open(expect_out, "w") as f:
-            json.dump({"listed_blocks": int(rp[-1]), "rows": int(len(rp) - 1), "waves_per_row": waves,
-                       "listed_subtiles": int(subs[ci].sum()),
-                       "mfma_sparse_listed": int(subs[ci].sum()) * waves * 16,
-                       "mfma_dense_listed": int(len(rp) - 1) * int(subs.sum()) * waves * 16}, f, indent=1)
+            json.dump({"listed_blocks": int(rp[-1]), "rows": int(len(rp) - 1), "subtiles_per_block": subs,
+                       "active_wave_rows": int(active.sum()),
+                       "mfma_sparse_listed": int((active * listed).sum()) * subs * 16,
+                       "mfma_dense_listed": int(active.sum()) * nkb * subs * 16}, f, indent=1)
     print("profile-attention done: %d attention launches, one %d-byte copy" % (launches, COPY_BYTES), flush=True)
 
 
