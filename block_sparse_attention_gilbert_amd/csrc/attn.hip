@@ -789,6 +789,7 @@ __global__ void __launch_bounds__(BLK * 2 * attn_key_split(BLK, D), 2) attn_bf16
 #pragma unroll
         for (int r = 0; r < 16; ++r) sn[r] = 0.f;
         // phase A (a few exponentials first, to cover the first K read)
+        __builtin_amdgcn_s_setprio(0);
         constexpr int NA0 = 4;
 #pragma unroll
         for (int n = 0; n < KD; ++n) rdk(n);
@@ -810,7 +811,13 @@ __global__ void __launch_bounds__(BLK * 2 * attn_key_split(BLK, D), 2) attn_bf16
                          "v"(p[14]), "v"(p[15]));
         __asm__ volatile("" ::"v"(pf[0]));
         if (nv < kSubKeys) mask(sn, nv);
-        // phase B
+        // phase B at a raised issue priority, kept through the end of the
+        // iteration (the workgroup barrier and the next copies) until phase A:
+        // the wave that is finishing its stage issues first, so the barrier
+        // every wave of the workgroup waits at is reached sooner (the sparse
+        // and dense launches take 3-6 % less time, A/B in one process; the
+        // priority within phase A or only across the barrier gains nothing)
+        __builtin_amdgcn_s_setprio(2);
         static_for<0, KK>([&](auto N_) __attribute__((always_inline)) {
             constexpr int n = decltype(N_)::value;
             constexpr int s2 = n / DT, dt = n % DT;
