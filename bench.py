@@ -595,24 +595,29 @@ def read_traffic(per_launch_bytes):
 COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 
 
-def profile_attention(launches: int, expect_out=None):
-    """Counter-collection mode: set up C4 at chunk 48, route once, then run
-    ``launches`` block-sparse attention launches, two dense ones, and one
-    plain 1 GiB device copy (the calibration kernel for the byte counters).  Prints nothing but a summary
-    line; meant to run under rocprofv3 --pmc."""
+def profile_attention(launches: int, expect_out=None, chunk: int = 48):
+    """Counter-collection mode: set up C4 at chunk 48, route once (over the
+    first ``chunk`` chunks of the store when ``chunk`` < 48: the chunk sweep's
+    workload at that history length), then run ``launches`` block-sparse
+    attention launches, two dense ones over the same history, and one plain
+    1 GiB device copy (the calibration kernel for the byte counters).  Prints
+    nothing but a summary line; meant to run under rocprofv3 --pmc."""
     import torch
     st = setup_c4(48, device="cuda:0")
     ra = st["ra"]
     run_step(st)
     torch.cuda.synchronize()
-    # attention only, on the routed lists of the step above
-    nkb = ra.store_chunks * ra.nbc
-    r = ra.route_out
+    if not 1 <= chunk <= ra.store_chunks:
+        raise ValueError("chunk must be 1..%d" % ra.store_chunks)
+    # attention only, on the routed lists of the step above (or of a route
+    # over the first `chunk` chunks, with the same queries)
+    nkb = chunk * ra.nbc
+    r = ra.route_out if chunk == ra.store_chunks else ra.route(chunk - 1, qpool=ra.qbar)
     k_hist, v_hist = ra.k_store[:, : nkb * ra.block], ra.v_store[:, : nkb * ra.block]
     for _ in range(launches):       # as in the step: Q read and O written in raster order
         ra._attend(r, nkb, k_hist, v_hist, None, None, out_raster=True, q_raster=st["q_raster"])
     for _ in range(2):  # dense attention over the same history, for comparison counters
-        ra.dense(st["cur"])
+        ra.dense(chunk - 1)
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -1002,7 +1007,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_path: str):
     print(json.dumps(out))
 
 
-def summarize_pipe(csvs, out_path: str):
+def summarize_pipe(csvs, out_path: str, chunk: int = 48):
     """Per-launch averages of the pipeline counters of the attention launches
     (block-sparse and dense) from rocprofv3 --pmc CSVs of bench.py
     --profile-attention, with the derived rates: matrix cores busy, vector
@@ -1022,7 +1027,7 @@ def summarize_pipe(csvs, out_path: str):
                     continue
                 vals.setdefault(kind, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
     simds, cus = 1024, 256
-    out = {"kernel": "attn_bf16_kernel<128,128>", "workload": "C4 chunk 48",
+    out = {"kernel": "attn_bf16_kernel<128,128>", "workload": "C4 chunk %d" % chunk,
            "attn_source_sha256_16": attn_source_hash()}
     for kind, c in vals.items():
         avg = {k: sum(v) / len(v) for k, v in c.items()}
@@ -1050,7 +1055,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--chunk", type=int, default=48)
+    ap.add_argument("--chunk", type=int, default=48,
+                    help="C4 history length in chunks (1..48); with --profile-attention and --summarize-pipe: "
+                         "the 48-chunk store routed over its first C chunks (the chunk sweep's workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=40)
     ap.add_argument("--no-dense", action="store_true", help="skip timing dense attention at the same chunk")
@@ -1096,7 +1103,7 @@ def main():
         summarize_launch_counters(a[3:-1], a[0], int(a[1]), a[2], a[-1])
         return
     if args.summarize_pipe:
-        summarize_pipe(args.summarize_pipe[:-1], args.summarize_pipe[-1])
+        summarize_pipe(args.summarize_pipe[:-1], args.summarize_pipe[-1], args.chunk)
         return
     if args.summarize_step_traffic:
         summarize_step_traffic(*args.summarize_step_traffic)
@@ -1119,7 +1126,7 @@ def main():
         profile_step(args.profile_step)
         return
     if args.profile_attention:
-        profile_attention(args.profile_attention, args.expect_out)
+        profile_attention(args.profile_attention, args.expect_out, args.chunk)
         return
     if args.profile_c5:
         profile_c5(args.profile_c5)
