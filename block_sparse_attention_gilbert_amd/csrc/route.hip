@@ -235,18 +235,44 @@ score_kernel(const double* __restrict__ qbar, int64_t qbar_head_stride, const do
     }
 }
 
-__device__ __forceinline__ int block_sum_1024(int v, int* sh) {
-    const int t = threadIdx.x;
+// Integer sums and scans over a 1024-thread workgroup: within each wave by
+// shuffles, across the 16 waves through a 16-int LDS array (two barriers).
+// Integer addition is exact, so the order does not matter.
+__device__ __forceinline__ int block_sum_1024(int v, int* sh16) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    __syncthreads();  // sh16 free (the previous use has been read)
+    if (lane == 0) sh16[w] = v;
     __syncthreads();
-    sh[t] = v;
-    __syncthreads();
-    for (int off = 512; off > 0; off >>= 1) {
-        if (t < off) sh[t] += sh[t + off];
-        __syncthreads();
-    }
-    const int r = sh[0];
-    __syncthreads();
+    int r = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r += sh16[i];
     return r;
+}
+
+// Exclusive prefix sum of v over the workgroup's threads in thread order;
+// *total receives the sum of all of them.
+__device__ __forceinline__ int block_excl_scan_1024(int v, int* sh16, int* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int up = __shfl_up(incl, off);
+        if (lane >= off) incl += up;
+    }
+    __syncthreads();  // sh16 free
+    if (lane == 63) sh16[w] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int x = sh16[i];
+        before += i < w ? x : 0;
+        all += x;
+    }
+    *total = all;
+    return before + incl - v;
 }
 
 // Single workgroup: per-row list lengths, the exclusive prefix sum into
@@ -256,7 +282,7 @@ rowptr_kernel(int heads, int nqb, int nkb, int n_cand, int block, const int32_t*
               const int32_t* __restrict__ kv_len, int k_fixed, const int32_t* __restrict__ k_per_row,
               int k_max, const int32_t* __restrict__ flags, int32_t* __restrict__ row_ptr,
               int32_t* __restrict__ keff, int32_t* __restrict__ fallback_counts) {
-    __shared__ int sh[1024];
+    __shared__ int sh[16];
     const int t = threadIdx.x;
     int c_vis = 0, c_tail = 0;
     for (int j = t; j < nkb; j += 1024) {
@@ -287,17 +313,10 @@ rowptr_kernel(int heads, int nqb, int nkb, int n_cand, int block, const int32_t*
             keff[r] = ke;
             tot = vq > 0 ? ke + n_tail : 0;
         }
-        __syncthreads();
-        sh[t] = tot;
-        __syncthreads();
-        for (int off = 1; off < 1024; off <<= 1) {
-            const int add = t >= off ? sh[t - off] : 0;
-            __syncthreads();
-            sh[t] += add;
-            __syncthreads();
-        }
-        if (r < rows) row_ptr[r] = carry + sh[t] - tot;
-        carry += sh[1023];
+        int chunk_total;
+        const int excl = block_excl_scan_1024(tot, sh, &chunk_total);
+        if (r < rows) row_ptr[r] = carry + excl;
+        carry += chunk_total;
     }
     if (t == 0) row_ptr[rows] = carry;
     if (fallback_counts) {
@@ -987,23 +1006,16 @@ materialize_kernel(const double* __restrict__ keys, int rows, int nqb, int nkb, 
 // Single workgroup: exclusive prefix sum of the row counts into row_ptr.
 __global__ void __launch_bounds__(1024)
 scan_counts_kernel(const int32_t* __restrict__ counts, int rows, int32_t* __restrict__ row_ptr) {
-    __shared__ int sh[1024];
+    __shared__ int sh[16];
     const int t = threadIdx.x;
     int carry = 0;
     for (int base = 0; base < rows; base += 1024) {
         const int r = base + t;
         const int v = r < rows ? counts[r] : 0;
-        __syncthreads();
-        sh[t] = v;
-        __syncthreads();
-        for (int off = 1; off < 1024; off <<= 1) {
-            const int add = t >= off ? sh[t - off] : 0;
-            __syncthreads();
-            sh[t] += add;
-            __syncthreads();
-        }
-        if (r < rows) row_ptr[r] = carry + sh[t] - v;
-        carry += sh[1023];
+        int chunk_total;
+        const int excl = block_excl_scan_1024(v, sh, &chunk_total);
+        if (r < rows) row_ptr[r] = carry + excl;
+        carry += chunk_total;
     }
     if (t == 0) row_ptr[rows] = carry;
 }
