@@ -542,13 +542,18 @@ __device__ __forceinline__ void select_threshold(const unsigned long long (&key)
     }
 }
 
+// Three waves per SIMD (at most 168 registers; the compiler fits every
+// instance without spilling): one wave per row spends most of its time in
+// short dependent ballot chains, so more rows in flight per SIMD is what
+// shortens the launch (C5, 2960 rows of 3478 candidates: 2 -> 3 waves per
+// SIMD takes the router from 187 to 156 us, the same lists).
 // One wave per (head, query block) row: the threshold of its top-K_eff,
 // then the selected indices in ascending order (ballot prefix counts),
 // followed by the dense tail.  grid = ceil(rows / 4), 4 waves per
 // workgroup, no barriers.  The keys and the block lengths are loaded
 // together, so a row costs one memory round trip before the selection.
 template <int KPL>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, 3)
 topk_kernel(const double* __restrict__ keys, int rows, int nqb, int n_cand, int nkb, int block,
             const int32_t* __restrict__ q_len, const int32_t* __restrict__ kv_len, int k_fused,
             int32_t* __restrict__ row_ptr, const int32_t* __restrict__ keff, int32_t* __restrict__ col_idx,
@@ -725,7 +730,7 @@ topk_segment_kernel(const double* __restrict__ keys, int rows, int n_cand, int n
 // holds entries l + 64 m, i.e. ascending candidate index) and writes their
 // indices, ascending, after row_ptr[r], then the dense tail.
 template <int KPL>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, 3)
 topk_merge_kernel(const unsigned long long* __restrict__ seg_key, const int32_t* __restrict__ seg_idx,
                   const int32_t* __restrict__ seg_cnt, int rows, int nqb, int nkb, int n_cand, int n_seg,
                   int seg_cap, int block, const int32_t* __restrict__ q_len, const int32_t* __restrict__ kv_len,
