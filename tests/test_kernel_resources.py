@@ -75,3 +75,15 @@ def test_attention_64_row_occupancy(tmp_path):
         assert v["vgpr_count"] + v.get("agpr_count", 0) <= 256, (name, v)
         assert v["group_segment_fixed_size"] <= 160 * 1024 // 2, (name, v)
         assert v.get("max_flat_workgroup_size", 256) == 256, (name, v)
+
+
+def test_topk_occupancy(tmp_path):
+    """The per-row top-K kernels run one wave per row and spend most of a
+    wave's time in short dependent ballot chains, so they are built for
+    three waves per SIMD: at most 168 registers per lane in every
+    instance (and no spill, checked above)."""
+    kernels = _kernels(tmp_path)
+    topk = {k: v for k, v in kernels.items() if "topk_kernelILi" in k}
+    assert len(topk) >= 4, sorted(topk)
+    for name, v in topk.items():
+        assert v["vgpr_count"] + v.get("agpr_count", 0) <= 168, (name, v)
