@@ -545,7 +545,7 @@ __device__ __forceinline__ void select_threshold(const unsigned long long (&key)
 // Three waves per SIMD (at most 168 registers; the compiler fits every
 // instance without spilling): one wave per row spends most of its time in
 // short dependent ballot chains, so more rows in flight per SIMD is what
-// shortens the launch (C5, 2960 rows of 3478 candidates: 2 -> 3 waves per
+// shortens the launch (2960 rows of 3478 candidates, blocks of 64: 2 -> 3 waves per
 // SIMD takes the router from 187 to 156 us, the same lists).
 // One wave per (head, query block) row: the threshold of its top-K_eff,
 // then the selected indices in ascending order (ballot prefix counts),
